@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Throughput of batched draft verification on one MI355X.
+
+Default workload: the heavy-load batch -- B=512 requests, K=8, budgets
+2..8 (mean 4), V=151,936, bf16 target and drafter logits, T=1 -- verified
+back to back with a fresh Philox seed per step, inputs resident in HBM.
+
+Prints one JSON line: verified draft tokens/s (sum of budgets per step over
+the step time), the roofline of the verify kernel (algorithmic HBM bytes per
+launch over its measured duration, against the 8 TB/s HBM peak), and the
+fp64 CPU oracle's rate on a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload heavy] [--no-cpu-baseline]
+  python bench.py --copy-probe GIB   # plain copies of a known size (counter scale)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E peak, GB/s
+KERNEL_SRC = os.path.join(ROOT, "draft_verify_sampling_spec_amd", "csrc", "spec_verify.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_kernel_heavy_traffic.json")
+WORKLOAD_INDEX = {"tiny": 1, "qwen3": 2, "ragged": 3, "gemma": 4, "heavy": 5}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(budgets, K, V, elem_bytes, greedy):
+    """HBM bytes the method must move once per step: every budgeted logit row
+    read once (k_b+1 target rows, k_b drafter rows; greedy reads no drafter
+    rows), drafted tokens and budgets read, tokens and counts written."""
+    ksum = int(sum(int(k) for k in budgets))
+    B = len(budgets)
+    rows = ksum + B if greedy else 2 * ksum + B
+    return rows * V * elem_bytes + 4 * (B * K + B) + 4 * (B * (K + 1) + B), rows
+
+
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(bytes_per_launch_expected):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, seed, n_requests):
+    """The fp64 oracle, as it stands, on the first n_requests of the batch."""
+    import numpy as np
+    import torch
+    from oracle import verify as ov
+
+    def bits(x):
+        return x.cpu().view(torch.int16).numpy().view(np.uint16)
+
+    budgets = inp["budgets"].cpu().numpy()
+    tokens = inp["tokens"].cpu().numpy()
+    T = inp["temperature"]
+    rows = [(bits(inp["target"][b, : int(budgets[b]) + 1]), bits(inp["draft"][b, : int(budgets[b])]))
+            for b in range(n_requests)]
+    t0 = time.perf_counter()
+    verified = 0
+    for b in range(n_requests):
+        kb = int(budgets[b])
+        zt = ov.decode_bf16(rows[b][0])
+        zd = ov.decode_bf16(rows[b][1])
+        ov.verify_request(b, zt, zd, tokens[b, :kb], T, seed)
+        verified += kb
+    dt = time.perf_counter() - t0
+    return verified / dt, dt
+
+
+def copy_probe(gib):
+    import torch
+    n = int(gib * (1 << 30))
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="heavy", choices=sorted(WORKLOAD_INDEX))
+    ap.add_argument("--temperature", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-requests", type=int, default=512)
+    ap.add_argument("--copy-probe", type=float, default=None)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from draft_verify_sampling_spec_amd import SpecVerify
+    from workloads import make_inputs, philox_seed
+
+    if args.copy_probe is not None:
+        copy_probe(args.copy_probe)
+        return
+
+    dev = torch.device("cuda:0")
+    log(f"[bench] drawing workload {args.workload} on {torch.cuda.get_device_name(dev)}")
+    inp = make_inputs(args.workload, device=dev)
+    w = inp["workload"]
+    T = inp["temperature"] if args.temperature is None else args.temperature
+    greedy = T == 0.0
+    t, x, k = inp["target"], inp["tokens"], inp["budgets"]
+    d = inp["draft"] if not greedy else None
+    B, K1, V = t.shape
+    K = K1 - 1
+    elem = t.element_size()
+    sv = SpecVerify(dev, max_batch=B, max_k=K, vocab=V, dtype=t.dtype)
+    out_t = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    out_n = torch.empty(B, dtype=torch.int32, device=dev)
+    widx = WORKLOAD_INDEX[args.workload]
+
+    budgets = k.cpu().tolist()
+    alg_bytes, rows = algorithmic_bytes(budgets, K, V, elem, greedy)
+    verified_per_step = int(sum(budgets))
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for s in range(args.warmup):
+        sv.run(t, d, x, k, T, philox_seed(widx, s), out_t, out_n, want_probs=False)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    accepted = torch.zeros((), dtype=torch.int64, device=dev)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        starts[s].record(stream)
+        sv.run(t, d, x, k, T, philox_seed(widx, 1_000_000 + s), out_t, out_n,
+               want_probs=False)
+        ends[s].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    accepted += out_n.sum()
+    kernel_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    kernel_ms.sort()
+    mean_kernel_ms = sum(kernel_ms) / len(kernel_ms)
+    ms_per_step = elapsed * 1e3 / args.steps
+    if sv.status() != 0:
+        log("[bench] device status flags set")
+        sys.exit(1)
+
+    achieved = alg_bytes / (mean_kernel_ms * 1e-3) / 1e9
+    traffic = load_traffic(alg_bytes)
+    result = {
+        "metric": "verified draft tokens/s + achieved HBM GB/s (% peak), B=512 V=151936 bf16",
+        "value": verified_per_step / (ms_per_step * 1e-3),
+        "unit": "verified draft tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if elem == 2 else "f32",
+        "data": "synthetic (seeded; see workloads/)",
+        "config": {
+            "workload": f"{w.name}: {w.summary}",
+            "B": B, "K": K, "V": V, "temperature": T,
+            "verified_draft_tokens_per_step": verified_per_step,
+            "logit_rows_per_step": rows,
+            "accepted_last_step": int(accepted.item()),
+        },
+        "hbm_gbs": achieved,
+        "hbm_frac_of_peak": achieved / HBM_PEAK_GBS,
+        "kernel_ms": {"mean": mean_kernel_ms, "median": kernel_ms[len(kernel_ms) // 2],
+                      "p5": kernel_ms[int(0.05 * (len(kernel_ms) - 1))],
+                      "p95": kernel_ms[int(0.95 * (len(kernel_ms) - 1))]},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "kernel": "verify_kernel<bf16, sampled>" if not greedy else "verify_kernel<bf16, greedy>",
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline and not greedy and args.workload == "heavy":
+        n_req = min(args.cpu_requests, B)
+        log(f"[bench] cpu baseline: oracle on {n_req} requests")
+        rate, dt = cpu_baseline(inp, philox_seed(widx, 0), n_req)
+        result["cpu_baseline"] = {
+            "value": rate, "unit": "verified draft tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n_req} of the {B} requests of one heavy step "
+                      f"({dt:.1f} s of fp64 NumPy, one process, one thread)",
+        }
+    print(json.dumps(result), flush=True)
+    sv.close()
+
+
+if __name__ == "__main__":
+    main()

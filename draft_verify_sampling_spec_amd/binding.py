@@ -1,0 +1,253 @@
+"""ctypes binding of ``libspec_verify.so`` (argument marshalling only).
+
+Every function of the C ABI (include/spec_verify.h) is exposed under its own
+name; ``SpecVerify`` wraps a context for torch tensors. Tensors are passed as
+raw device pointers and the current torch stream as the HIP stream; all work
+runs in the library's kernels. There is no fallback: if the library is not
+built, ``load()`` raises.
+
+torch is imported before the library is opened so that the library binds to
+the HIP runtime torch already loaded (one runtime per process).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+SV_OK = 0
+SV_ERR_NULL = -1
+SV_ERR_ARG = -2
+SV_ERR_DTYPE = -3
+SV_ERR_ALIGN = -4
+SV_ERR_HIP = -5
+SV_ERR_NOMEM = -6
+SV_ERR_STATE = -7
+
+SV_DTYPE_F32 = 0
+SV_DTYPE_BF16 = 1
+
+SV_FLAG_BAD_BUDGET = 0x1
+SV_FLAG_BAD_TOKEN = 0x2
+
+SV_MAX_BATCH = 16384
+SV_MAX_K = 32
+SV_MAX_VOCAB = 1 << 20
+
+EXPORTED = (
+    "spec_verify_init",
+    "spec_verify_run",
+    "spec_verify_check_args",
+    "spec_verify_status",
+    "spec_verify_philox_words",
+    "spec_verify_free",
+    "spec_verify_strerror",
+    "spec_verify_chunks",
+)
+
+_lib = None
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+
+
+def _declare(lib):
+    lib.spec_verify_init.argtypes = [ctypes.POINTER(_vp), _i, _i, _i, _i, _i]
+    lib.spec_verify_init.restype = _i
+    lib.spec_verify_run.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, ctypes.c_float,
+                                    ctypes.c_uint64, _vp, _vp, _vp, _vp, _vp]
+    lib.spec_verify_run.restype = _i
+    lib.spec_verify_check_args.argtypes = [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i,
+                                           ctypes.c_float, _vp, _vp, _vp, _vp]
+    lib.spec_verify_check_args.restype = _i
+    lib.spec_verify_status.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint32)]
+    lib.spec_verify_status.restype = _i
+    lib.spec_verify_philox_words.argtypes = [ctypes.c_uint64, _i, _i, _vp, _vp]
+    lib.spec_verify_philox_words.restype = _i
+    lib.spec_verify_free.argtypes = [_vp]
+    lib.spec_verify_free.restype = None
+    lib.spec_verify_strerror.argtypes = [_i]
+    lib.spec_verify_strerror.restype = ctypes.c_char_p
+    lib.spec_verify_chunks.argtypes = [_i, _i]
+    lib.spec_verify_chunks.restype = _i
+
+
+def load(path: str | None = None):
+    """Open the built library (once per process)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; run `python -m draft_verify_sampling_spec_amd.build`")
+    lib = ctypes.CDLL(path)
+    _declare(lib)
+    _lib = lib
+    return lib
+
+
+# ---- the C functions under their own names ------------------------------------
+
+def spec_verify_strerror(code: int) -> str:
+    return load().spec_verify_strerror(int(code)).decode()
+
+
+def spec_verify_chunks(vocab: int, dtype: int) -> int:
+    return load().spec_verify_chunks(int(vocab), int(dtype))
+
+
+def spec_verify_check_args(max_batch, max_k, vocab, dtype, target, draft, tokens, budgets,
+                           B, K, temperature, out_tokens, out_num_accepted,
+                           out_p_draft=None, out_q_draft=None) -> int:
+    """Host-only argument check; pointer arguments are ints (addresses) or None."""
+    return load().spec_verify_check_args(
+        max_batch, max_k, vocab, dtype, target, draft, tokens, budgets, B, K,
+        ctypes.c_float(temperature), out_tokens, out_num_accepted, out_p_draft, out_q_draft)
+
+
+def spec_verify_init(device: int, max_batch: int, max_k: int, vocab: int, dtype: int):
+    """Returns (status, ctx handle or None)."""
+    ctx = _vp()
+    rc = load().spec_verify_init(ctypes.byref(ctx), device, max_batch, max_k, vocab, dtype)
+    return rc, (ctx.value if rc == SV_OK else None)
+
+
+def spec_verify_run(ctx, target, draft, tokens, budgets, B, K, temperature, seed,
+                    out_tokens, out_num_accepted, out_p_draft, out_q_draft, stream) -> int:
+    return load().spec_verify_run(ctx, target, draft, tokens, budgets, B, K,
+                                  ctypes.c_float(temperature), ctypes.c_uint64(seed),
+                                  out_tokens, out_num_accepted, out_p_draft, out_q_draft,
+                                  stream)
+
+
+def spec_verify_status(ctx):
+    """Returns (status, flags)."""
+    flags = ctypes.c_uint32(0)
+    rc = load().spec_verify_status(ctx, ctypes.byref(flags))
+    return rc, flags.value
+
+
+def spec_verify_philox_words(seed: int, B: int, P: int, out_words, stream) -> int:
+    return load().spec_verify_philox_words(ctypes.c_uint64(seed), B, P, out_words, stream)
+
+
+def spec_verify_free(ctx) -> None:
+    load().spec_verify_free(ctx)
+
+
+# ---- torch convenience ----------------------------------------------------------
+
+def _check(rc: int, what: str):
+    if rc != SV_OK:
+        raise RuntimeError(f"{what}: {spec_verify_strerror(rc)} ({rc})")
+
+
+def _stream_handle(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+_DTYPES = {torch.float32: SV_DTYPE_F32, torch.bfloat16: SV_DTYPE_BF16}
+
+
+class SpecVerify:
+    """A verify context bound to one device, vocabulary and logit dtype."""
+
+    def __init__(self, device, max_batch: int, max_k: int, vocab: int,
+                 dtype: torch.dtype = torch.bfloat16):
+        if dtype not in _DTYPES:
+            raise ValueError(f"logits must be float32 or bfloat16, not {dtype}")
+        self.device = torch.device(device)
+        if self.device.type != "cuda":
+            raise ValueError("SpecVerify needs a GPU device")
+        self.max_batch, self.max_k, self.vocab, self.dtype = max_batch, max_k, vocab, dtype
+        idx = self.device.index if self.device.index is not None else torch.cuda.current_device()
+        rc, ctx = spec_verify_init(idx, max_batch, max_k, vocab, _DTYPES[dtype])
+        _check(rc, "spec_verify_init")
+        self._ctx = ctx
+
+    def close(self):
+        if getattr(self, "_ctx", None):
+            spec_verify_free(self._ctx)
+            self._ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _tensor(self, t, name, dtype, shape):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device != self.device and not (t.device.type == "cuda" and self.device.index is None):
+            raise ValueError(f"{name} is on {t.device}, context on {self.device}")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        return t.data_ptr()
+
+    def run(self, target, draft, tokens, budgets, temperature: float, seed: int,
+            out_tokens=None, out_num_accepted=None, out_p=None, out_q=None,
+            want_probs: bool = True, stream=None):
+        """Verify a batch. Returns (tokens [B,K+1], n_accepted [B], p_x, q_x).
+
+        p_x/q_x are None unless ``want_probs`` (or output buffers are given).
+        Enqueued on ``stream`` (default: the current torch stream), not waited for.
+        """
+        if target.dim() != 3:
+            raise ValueError("target logits must be [B, K+1, V]")
+        B, K1, V = target.shape
+        K = K1 - 1
+        if V != self.vocab:
+            raise ValueError(f"vocabulary {V} != context vocabulary {self.vocab}")
+        temperature = float(temperature)
+        if not math.isfinite(temperature) or temperature < 0:
+            raise ValueError("temperature must be finite and >= 0")
+        t_ptr = self._tensor(target, "target", self.dtype, (B, K + 1, V))
+        d_ptr = None
+        if draft is not None:
+            d_ptr = self._tensor(draft, "draft", self.dtype, (B, K, V))
+        elif temperature > 0 and K > 0:
+            raise ValueError("sampled verification needs drafter logits")
+        x_ptr = self._tensor(tokens, "tokens", torch.int32, (B, K))
+        k_ptr = self._tensor(budgets, "budgets", torch.int32, (B,))
+        dev = target.device
+        if out_tokens is None:
+            out_tokens = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+        if out_num_accepted is None:
+            out_num_accepted = torch.empty(B, dtype=torch.int32, device=dev)
+        if want_probs and out_p is None:
+            out_p = torch.empty(B, K, dtype=torch.float32, device=dev)
+        if want_probs and out_q is None:
+            out_q = torch.empty(B, K, dtype=torch.float32, device=dev)
+        ot = self._tensor(out_tokens, "out_tokens", torch.int32, (B, K + 1))
+        on = self._tensor(out_num_accepted, "out_num_accepted", torch.int32, (B,))
+        op = self._tensor(out_p, "out_p", torch.float32, (B, K)) if out_p is not None else None
+        oq = self._tensor(out_q, "out_q", torch.float32, (B, K)) if out_q is not None else None
+        s = stream.cuda_stream if stream is not None else _stream_handle(dev)
+        rc = spec_verify_run(self._ctx, t_ptr, d_ptr, x_ptr, k_ptr, B, K, temperature,
+                             int(seed) & 0xFFFFFFFFFFFFFFFF, ot, on, op, oq, s)
+        _check(rc, "spec_verify_run")
+        return out_tokens, out_num_accepted, out_p, out_q
+
+    def status(self) -> int:
+        rc, flags = spec_verify_status(self._ctx)
+        _check(rc, "spec_verify_status")
+        return flags
+
+
+def philox_words(seed: int, B: int, P: int, device="cuda") -> torch.Tensor:
+    """The device generator's blocks for counters (b, i, 0, 0): [B, P, 4] int64."""
+    out = torch.empty(B * P * 4, dtype=torch.int32, device=device)
+    rc = spec_verify_philox_words(int(seed) & 0xFFFFFFFFFFFFFFFF, B, P, out.data_ptr(),
+                                  _stream_handle(out.device))
+    _check(rc, "spec_verify_philox_words")
+    return out.view(B, P, 4).to(torch.int64) & 0xFFFFFFFF

@@ -1,0 +1,69 @@
+"""Build the HIP library in-tree with hipcc for gfx950.
+
+``python -m draft_verify_sampling_spec_amd.build`` (or ``build_library()``)
+compiles ``csrc/spec_verify.hip`` into ``libspec_verify.so`` next to this file.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+SRC = os.path.join(PKG_DIR, "csrc", "spec_verify.hip")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libspec_verify.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
+
+
+def compile_command(out: str = LIB_PATH) -> list:
+    return [
+        hipcc(),
+        f"--offload-arch={ARCH}",
+        "-O3",
+        "-std=c++17",
+        "-fPIC",
+        "-shared",
+        # Floating-point expressions are evaluated as written (no FMA
+        # contraction), so identical expressions give identical values.
+        "-ffp-contract=off",
+        # Keep the compiler from emitting packed fp32 VALU instructions.
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall",
+        "-I", INCLUDE,
+        SRC,
+        "-o", out,
+    ]
+
+
+def build_library(verbose: bool = True) -> str:
+    """Compile the library (always; the output is replaced atomically)."""
+    tmp = LIB_PATH + ".tmp"
+    cmd = compile_command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    if verbose and res.stderr.strip():
+        # Warnings (the host pass does not know the packed-fp32 feature flag).
+        lines = [l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l]
+        if any(l.strip() for l in lines):
+            sys.stderr.write("\n".join(lines) + "\n")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    build_library()

@@ -1,0 +1,180 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X (gfx950) batched draft-verification
+ * library.
+ *
+ * The operation. For every request b of a batch, a drafter has proposed
+ * up to K tokens x_0..x_{K-1}; the target model has scored the whole block
+ * in one pass, giving K+1 logit rows (one per drafted position plus the
+ * position after the block). Of the K drafted tokens only the first k_b (the
+ * request's verify budget) are checked. The library decides which drafted
+ * tokens survive and draws the one token that follows them:
+ *
+ *   - Greedy verification (temperature == 0), as described in
+ *     "Speculative decoding becomes standard: DSpark and multi-token
+ *     drafters", section "Why draft-and-verify does not change the output",
+ *     paragraph 1: keep drafted tokens while they equal the target's most
+ *     likely token (lowest index among equal maxima), and at the first
+ *     mismatch emit the target's own token; if all k_b agree, emit the
+ *     target's token at position k_b.
+ *   - Sampled verification (temperature T > 0), same section, paragraph 2
+ *     (the rule of Leviathan, Kalman and Matias): with p_i = softmax(z_t/T)
+ *     and q_i = softmax(z_d/T) over the full vocabulary, drafted token x_i
+ *     survives when u < min(1, p_i(x_i)/q_i(x_i)); at the first rejection j
+ *     the token is drawn from the renormalised residual max(0, p_j - q_j);
+ *     if all k_b survive, a bonus token is drawn from p_{k_b}. Draws are
+ *     inverse-CDF in vocabulary order.
+ *   - Per-request budgets k_b (0 <= k_b <= K) model the confidence-driven
+ *     scheduler of the same page, section "What DSpark adds", paragraph 2.
+ *
+ * Random numbers: Philox4x32-10 (Salmon et al., SC'11) with key = seed
+ * (low word, high word) and counter = (b, i, 0, 0) for position i of request
+ * b; output word 0 gives the acceptance uniform of position i, word 1 its
+ * sampling uniform, each as (word >> 8) * 2^-24.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensors are caller-owned device memory; the library never frees
+ *     or retains them past a call. The library owns only the context and its
+ *     device workspace.
+ *   - Work is enqueued on the caller's HIP stream (hipStream_t passed as
+ *     void*, NULL = default stream) and the call returns without waiting.
+ *   - Return values are sv_status codes; nothing is thrown across the ABI.
+ *     Argument errors are detected on the host before anything is enqueued.
+ *     Errors only visible on the device (a budget outside [0, K], a drafted
+ *     token outside [0, V)) set bits of a device status word read by
+ *     spec_verify_status; the kernels never read out of bounds because of
+ *     them.
+ *   - One context serves one stream at a time: calls that overlap in time
+ *     on the same context race on its workspace.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct spec_verify_ctx spec_verify_ctx;
+
+/* Storage type of the logit tensors. */
+enum sv_dtype {
+    SV_DTYPE_F32 = 0,   /* IEEE fp32 */
+    SV_DTYPE_BF16 = 1   /* bfloat16: the upper 16 bits of an fp32 */
+};
+
+/* Return codes. */
+enum sv_status {
+    SV_OK = 0,
+    SV_ERR_NULL = -1,    /* a required pointer is NULL */
+    SV_ERR_ARG = -2,     /* a scalar argument is out of range */
+    SV_ERR_DTYPE = -3,   /* unknown storage type */
+    SV_ERR_ALIGN = -4,   /* a pointer is not aligned to its element size */
+    SV_ERR_HIP = -5,     /* the HIP runtime reported an error */
+    SV_ERR_NOMEM = -6,   /* device workspace allocation failed */
+    SV_ERR_STATE = -7    /* NULL or already freed context */
+};
+
+/* Bits of the device status word (spec_verify_status). */
+#define SV_FLAG_BAD_BUDGET 0x1u /* a budget was outside [0, K]; it was clamped */
+#define SV_FLAG_BAD_TOKEN  0x2u /* a checked drafted token was outside [0, V);
+                                   it was treated as rejected, its p and q as 0 */
+
+/* Library limits. */
+#define SV_MAX_BATCH 16384
+#define SV_MAX_K 32
+#define SV_MAX_VOCAB (1 << 20)
+
+/*
+ * spec_verify_init -- create a context for one device and one problem shape.
+ *   out        receives the context (set to NULL on failure).
+ *   device     HIP device ordinal.
+ *   max_batch  largest B a run will pass, 1..SV_MAX_BATCH.
+ *   max_k      largest K a run will pass, 0..SV_MAX_K.
+ *   vocab      V, the vocabulary size of every run, 1..SV_MAX_VOCAB.
+ *   dtype      sv_dtype of the logits of every run.
+ * Allocates and zeroes the device workspace (per-row partial statistics,
+ * per-request counters, work-queue counters, status word). Synchronous.
+ * Errors: SV_ERR_NULL, SV_ERR_ARG, SV_ERR_DTYPE, SV_ERR_HIP, SV_ERR_NOMEM.
+ */
+int spec_verify_init(spec_verify_ctx** out, int device, int max_batch, int max_k,
+                     int vocab, int dtype);
+
+/*
+ * spec_verify_run -- verify one batch (stream-ordered, no host sync).
+ *   target_logits     [B, K+1, V] row-major, storage ctx dtype (device).
+ *   draft_logits      [B, K, V] row-major, same storage (device); may be
+ *                     NULL when temperature == 0 (never read then).
+ *   draft_tokens      int32 [B, K] drafted token ids (device); entries at
+ *                     positions >= budgets[b] are never read.
+ *   budgets           int32 [B] verify budgets k_b, 0 <= k_b <= K (device).
+ *   B, K              batch size (0..max_batch; 0 is a no-op) and block
+ *                     width (0..max_k).
+ *   temperature       0 = greedy; > 0 = sampled; must be finite.
+ *   seed              Philox key of this call.
+ *   out_tokens        int32 [B, K+1]: x_0..x_{j-1}, then the drawn token,
+ *                     then -1 padding (device).
+ *   out_num_accepted  int32 [B]: j, the number of drafted tokens kept.
+ *   out_p_draft       float [B, K] or NULL: p_i(x_i) for i < k_b, NaN for
+ *                     i >= k_b and in greedy mode (device).
+ *   out_q_draft       float [B, K] or NULL: q_i(x_i), same layout.
+ *   stream            hipStream_t or NULL.
+ * Pointers must be aligned to their element size; a 16-byte aligned logit
+ * base with V * sizeof(element) a multiple of 16 takes the vector-load path
+ * for every row. Rows b*(K+1)+i beyond i = k_b are never read.
+ * Errors (host-detected, nothing enqueued): SV_ERR_STATE, SV_ERR_NULL,
+ * SV_ERR_ARG, SV_ERR_ALIGN; SV_ERR_HIP if the launch fails.
+ */
+int spec_verify_run(spec_verify_ctx* ctx, const void* target_logits,
+                    const void* draft_logits, const int32_t* draft_tokens,
+                    const int32_t* budgets, int B, int K, float temperature,
+                    uint64_t seed, int32_t* out_tokens, int32_t* out_num_accepted,
+                    float* out_p_draft, float* out_q_draft, void* stream);
+
+/*
+ * spec_verify_check_args -- the host-side argument check of spec_verify_run
+ * for a context created with (max_batch, max_k, vocab, dtype), without a
+ * context or a device. Pointers are only tested for NULL and alignment,
+ * never dereferenced. Returns SV_OK or the code spec_verify_run would return.
+ */
+int spec_verify_check_args(int max_batch, int max_k, int vocab, int dtype,
+                           const void* target_logits, const void* draft_logits,
+                           const void* draft_tokens, const void* budgets, int B,
+                           int K, float temperature, const void* out_tokens,
+                           const void* out_num_accepted, const void* out_p_draft,
+                           const void* out_q_draft);
+
+/*
+ * spec_verify_status -- wait for the device, return and clear the status
+ * word (SV_FLAG_* bits accumulated by runs since the last call).
+ * Errors: SV_ERR_STATE, SV_ERR_NULL, SV_ERR_HIP.
+ */
+int spec_verify_status(spec_verify_ctx* ctx, uint32_t* flags);
+
+/*
+ * spec_verify_philox_words -- write the Philox4x32-10 blocks the verifier
+ * uses: out_words[(b*P + i)*4 + w] = word w of the block with key = seed and
+ * counter = (b, i, 0, 0), for b < B, i < P (device buffer of 4*B*P uint32).
+ * Stream-ordered. For checking the device generator against other
+ * implementations. Errors: SV_ERR_NULL, SV_ERR_ARG, SV_ERR_HIP.
+ */
+int spec_verify_philox_words(uint64_t seed, int B, int P, uint32_t* out_words,
+                             void* stream);
+
+/* spec_verify_free -- release the context (NULL-safe, idempotent on NULL).
+ * Waits for the device before freeing the workspace. */
+void spec_verify_free(spec_verify_ctx* ctx);
+
+/* spec_verify_strerror -- static text for an sv_status code. */
+const char* spec_verify_strerror(int code);
+
+/* spec_verify_chunks -- number of vocabulary chunks a row is split into for
+ * (vocab, dtype), or a negative sv_status on bad arguments. Host only. */
+int spec_verify_chunks(int vocab, int dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

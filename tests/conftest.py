@@ -23,3 +23,10 @@ def gpu_lib():
         pytest.fail("GPU test collected on a machine without a GPU")
     from draft_verify_sampling_spec_amd import binding
     return binding.load()
+
+
+def pytest_sessionstart(session):
+    """Build the HIP library once if this checkout has none yet."""
+    from draft_verify_sampling_spec_amd import build
+    if not os.path.exists(build.LIB_PATH):
+        build.build_library(verbose=False)

@@ -46,17 +46,22 @@ def check_probabilities(gpu_p, ora_p, budgets):
     return bad
 
 
-def compare_sampled(gpu_tokens, gpu_n, ora):
-    """Compare sampled outputs with the oracle, excusing near-ties.
+def padded(tokens, K):
+    out = [int(t) for t in tokens] + [-1] * (K + 1 - len(tokens))
+    return out
+
+
+def compare_sampled(gpu_tokens, gpu_n, decisions, K):
+    """Compare sampled outputs with the oracle's decisions, excusing near-ties.
 
     Returns (n_excused, unexcused) where unexcused lists the requests whose
     first diverging decision was not within the near-tie band.
     """
     excused, unexcused = 0, []
-    for n, d in enumerate(ora.decisions):
+    for n, d in enumerate(decisions):
         g_n = int(gpu_n[n])
         g_tok = [int(t) for t in gpu_tokens[n]]
-        o_tok = [int(t) for t in ora.tokens[n]]
+        o_tok = padded(d.tokens, K)
         if g_n == d.n_accepted and g_tok == o_tok:
             continue
         if g_n != d.n_accepted:
@@ -67,7 +72,7 @@ def compare_sampled(gpu_tokens, gpu_n, ora):
             else:
                 unexcused.append((n, "accept", i, g_n, d.n_accepted, margin))
             continue
-        # Same acceptance path: only the sample can differ.
+        # Same acceptance path: only the drawn token can differ.
         if d.cdf_margin < NEAR_TIE:
             excused += 1
         else:

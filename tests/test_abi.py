@@ -1,0 +1,139 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and its host-side argument checks return the documented
+codes. No kernel is launched here."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from draft_verify_sampling_spec_amd import binding as sb
+from draft_verify_sampling_spec_amd.build import LIB_PATH
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "spec_verify.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_verify_[a-z_]+)\s*\(", text)))
+
+
+def _declared_constants():
+    text = open(HEADER).read()
+    out = dict(re.findall(r"#define\s+(SV_[A-Z_]+)\s+([0-9][0-9a-fA-Fx]*)u?\s", text))
+    for name, val in re.findall(r"\b(SV_[A-Z_0-9]+)\s*=\s*(-?\d+)", text):
+        out[name] = val
+    return out
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(LIB_PATH)
+    declared = _declared_functions()
+    assert declared, "no functions parsed from the header"
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(sb.EXPORTED)
+
+
+def test_binding_constants_match_header():
+    consts = _declared_constants()
+    for name, val in consts.items():
+        if hasattr(sb, name):
+            v = int(val, 0) if not val.startswith("(") else None
+            assert getattr(sb, name) == v, name
+    assert sb.SV_MAX_VOCAB == 1 << 20
+
+
+def test_strerror_covers_every_code():
+    for code in range(0, -8, -1):
+        assert sb.spec_verify_strerror(code) != "unknown status code"
+    assert sb.spec_verify_strerror(42) == "unknown status code"
+
+
+def test_chunk_count():
+    assert sb.spec_verify_chunks(151936, sb.SV_DTYPE_BF16) == 10
+    assert sb.spec_verify_chunks(262144, sb.SV_DTYPE_BF16) == 16
+    assert sb.spec_verify_chunks(151936, sb.SV_DTYPE_F32) == 19
+    assert sb.spec_verify_chunks(32, sb.SV_DTYPE_F32) == 1
+    assert sb.spec_verify_chunks(0, sb.SV_DTYPE_F32) == sb.SV_ERR_ARG
+    assert sb.spec_verify_chunks(32, 7) == sb.SV_ERR_DTYPE
+
+
+A = 0x10000  # a 16-byte aligned fake address (never dereferenced)
+
+
+def _check(**kw):
+    args = dict(max_batch=8, max_k=4, vocab=1000, dtype=sb.SV_DTYPE_BF16, target=A,
+                draft=A, tokens=A, budgets=A, B=8, K=4, temperature=1.0, out_tokens=A,
+                out_num_accepted=A, out_p_draft=None, out_q_draft=None)
+    args.update(kw)
+    return sb.spec_verify_check_args(**args)
+
+
+def test_check_args_accepts_valid_calls():
+    assert _check() == sb.SV_OK
+    assert _check(temperature=0.0, draft=None) == sb.SV_OK          # greedy needs no drafter
+    assert _check(B=0, target=None, budgets=None) == sb.SV_OK      # empty batch is a no-op
+    assert _check(K=0, draft=None, tokens=None) == sb.SV_OK         # bonus-only requests
+    assert _check(out_p_draft=A, out_q_draft=A) == sb.SV_OK
+    assert _check(dtype=sb.SV_DTYPE_F32, target=A + 4, draft=A + 8) == sb.SV_OK
+
+
+@pytest.mark.parametrize("kw, code", [
+    (dict(B=9), sb.SV_ERR_ARG),
+    (dict(B=-1), sb.SV_ERR_ARG),
+    (dict(K=5), sb.SV_ERR_ARG),
+    (dict(K=-1), sb.SV_ERR_ARG),
+    (dict(temperature=-0.5), sb.SV_ERR_ARG),
+    (dict(temperature=math.nan), sb.SV_ERR_ARG),
+    (dict(temperature=math.inf), sb.SV_ERR_ARG),
+    (dict(dtype=2), sb.SV_ERR_DTYPE),
+    (dict(max_batch=0), sb.SV_ERR_ARG),
+    (dict(max_batch=sb.SV_MAX_BATCH + 1, B=1), sb.SV_ERR_ARG),
+    (dict(max_k=sb.SV_MAX_K + 1), sb.SV_ERR_ARG),
+    (dict(vocab=0), sb.SV_ERR_ARG),
+    (dict(vocab=sb.SV_MAX_VOCAB + 1), sb.SV_ERR_ARG),
+    (dict(target=None), sb.SV_ERR_NULL),
+    (dict(draft=None), sb.SV_ERR_NULL),
+    (dict(tokens=None), sb.SV_ERR_NULL),
+    (dict(budgets=None), sb.SV_ERR_NULL),
+    (dict(out_tokens=None), sb.SV_ERR_NULL),
+    (dict(out_num_accepted=None), sb.SV_ERR_NULL),
+    (dict(target=A + 1), sb.SV_ERR_ALIGN),
+    (dict(draft=A + 3), sb.SV_ERR_ALIGN),
+    (dict(dtype=sb.SV_DTYPE_F32, target=A + 2), sb.SV_ERR_ALIGN),
+    (dict(tokens=A + 2), sb.SV_ERR_ALIGN),
+    (dict(budgets=A + 1), sb.SV_ERR_ALIGN),
+    (dict(out_tokens=A + 2), sb.SV_ERR_ALIGN),
+    (dict(out_p_draft=A + 2), sb.SV_ERR_ALIGN),
+])
+def test_check_args_rejects(kw, code):
+    assert _check(**kw) == code
+
+
+def test_null_context_paths_do_not_touch_a_device():
+    lib = sb.load()
+    assert sb.spec_verify_run(None, A, A, A, A, 1, 1, 1.0, 0, A, A, None, None, None) \
+        == sb.SV_ERR_STATE
+    rc, _ = sb.spec_verify_status(None)
+    assert rc == sb.SV_ERR_STATE
+    sb.spec_verify_free(None)                         # NULL-safe
+    out = ctypes.c_void_p()
+    assert lib.spec_verify_init(None, 0, 8, 4, 1000, 1) == sb.SV_ERR_NULL
+    assert lib.spec_verify_init(ctypes.byref(out), 0, 8, 4, 1000, 9) == sb.SV_ERR_DTYPE
+    assert lib.spec_verify_init(ctypes.byref(out), 0, 0, 4, 1000, 1) == sb.SV_ERR_ARG
+    assert lib.spec_verify_init(ctypes.byref(out), -1, 8, 4, 1000, 1) == sb.SV_ERR_ARG
+    assert out.value is None
+    assert sb.spec_verify_philox_words(0, -1, 1, None, None) == sb.SV_ERR_ARG
+    assert sb.spec_verify_philox_words(0, 0, 5, None, None) == sb.SV_OK
+
+
+def test_init_without_a_device_fails_cleanly():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    rc, ctx = sb.spec_verify_init(0, 8, 4, 1000, sb.SV_DTYPE_BF16)
+    assert rc == sb.SV_ERR_HIP and ctx is None

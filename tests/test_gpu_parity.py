@@ -1,0 +1,350 @@
+"""GPU parity of the HIP library against the fp64 CPU oracle.
+
+Every call goes through the C ABI (ctypes binding). Inputs are the seeded
+synthetic workloads; the oracle reads back the exact tensors the library was
+given. Bar (see tests/helpers.py): greedy outputs bit-exact; p_i(x_i), q_i(x_i)
+within 1e-5 relative; sampled decisions identical except first divergences
+inside the 1e-6 near-tie band, which are counted and printed.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+from scipy import special, stats
+
+from draft_verify_sampling_spec_amd import SpecVerify, binding, philox_words
+from oracle import philox
+from oracle import verify as ov
+from tests.helpers import check_probabilities, compare_sampled, padded, to_oracle
+from workloads import make_inputs, philox_seed
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _run(inp, seed, sv=None, temperature=None):
+    T = inp["temperature"] if temperature is None else temperature
+    t = inp["target"].to(DEV)
+    d = inp["draft"].to(DEV) if T > 0 else None
+    x = inp["tokens"].to(DEV)
+    k = inp["budgets"].to(DEV)
+    B, K1, V = t.shape
+    own = sv is None
+    if own:
+        sv = SpecVerify(DEV, max_batch=max(B, 1), max_k=K1 - 1, vocab=V, dtype=t.dtype)
+    toks, nacc, p, q = sv.run(t, d, x, k, T, seed)
+    torch.cuda.synchronize()
+    flags = sv.status()
+    out = (toks.cpu().numpy(), nacc.cpu().numpy(), p.cpu().numpy(), q.cpu().numpy(), flags)
+    if own:
+        sv.close()
+    return out
+
+
+def _oracle(inp, seed, requests=None, temperature=None):
+    """Oracle decisions for the given requests (global indices keep their counters)."""
+    T = inp["temperature"] if temperature is None else temperature
+    budgets = inp["budgets"].cpu().numpy()
+    tokens = inp["tokens"].cpu().numpy()
+    reqs = range(len(budgets)) if requests is None else requests
+    out = []
+    for b in reqs:
+        k = int(budgets[b])
+        zt, fmt = to_oracle(inp["target"][b, : k + 1])
+        zt = ov.as_f64_rows(zt, fmt)
+        zd = None
+        if T > 0:
+            zd, _ = to_oracle(inp["draft"][b, :k])
+            zd = ov.as_f64_rows(zd, fmt)
+        out.append(ov.verify_request(int(b), zt, zd, tokens[b, :k], float(T), seed))
+    return out
+
+
+def _assert_parity(inp, seed, gpu, decisions, requests=None, temperature=None, tag=""):
+    T = inp["temperature"] if temperature is None else temperature
+    toks, nacc, p, q, flags = gpu
+    assert flags == 0, f"device status flags {flags:#x}"
+    K = inp["tokens"].shape[1]
+    reqs = np.arange(len(toks)) if requests is None else np.asarray(requests)
+    budgets = inp["budgets"].cpu().numpy()[reqs]
+    g_tok, g_n = toks[reqs], nacc[reqs]
+    if T == 0:
+        for n, d in enumerate(decisions):
+            assert int(g_n[n]) == d.n_accepted, (tag, int(reqs[n]))
+            assert list(g_tok[n]) == padded(d.tokens, K), (tag, int(reqs[n]))
+        assert np.all(np.isnan(p[reqs])) and np.all(np.isnan(q[reqs]))
+        return 0
+    ora_p = np.full((len(reqs), K), np.nan)
+    ora_q = np.full((len(reqs), K), np.nan)
+    for n, d in enumerate(decisions):
+        ora_p[n, : len(d.p_x)] = d.p_x
+        ora_q[n, : len(d.q_x)] = d.q_x
+    bad_p = check_probabilities(p[reqs], ora_p, budgets)
+    bad_q = check_probabilities(q[reqs], ora_q, budgets)
+    assert not bad_p, (tag, "p_x", bad_p[:5])
+    assert not bad_q, (tag, "q_x", bad_q[:5])
+    for n, kb in enumerate(budgets):                 # padding beyond the budget
+        assert np.all(np.isnan(p[reqs[n], kb:])) and np.all(np.isnan(q[reqs[n], kb:]))
+    excused, unexcused = compare_sampled(g_tok, g_n, decisions, K)
+    _log(f"[{tag}] requests={len(decisions)} excused near-ties={excused} "
+         f"unexcused={len(unexcused)}")
+    assert not unexcused, (tag, unexcused[:5])
+    return excused
+
+
+# ------------------------------------------------------------------ Philox ---
+
+@pytest.mark.parametrize("seed", [0, 2**64 - 1, (5 << 32) | 17, 0x0123456789ABCDEF])
+def test_device_philox_matches_oracle(seed):
+    B, P = 1000, 9
+    got = philox_words(seed, B, P, DEV).cpu().numpy().astype(np.uint64)
+    k0, k1 = philox.seed_key(seed)
+    bb, ii = np.meshgrid(np.arange(B, dtype=np.uint64), np.arange(P, dtype=np.uint64),
+                         indexing="ij")
+    ref = np.stack(philox.philox4x32_np(bb, ii, 0, 0, k0, k1), axis=-1)
+    assert np.array_equal(got, ref)
+
+
+# -------------------------------------------------------------------- tiny ---
+
+def test_tiny_greedy_bit_exact():
+    inp = make_inputs("tiny", B=64, variant="greedy", temperature=0.0)
+    gpu = _run(inp, 1)
+    _assert_parity(inp, 1, gpu, _oracle(inp, 1), tag="tiny-greedy")
+
+
+def test_tiny_q_equal_p_accepts_all():
+    inp = make_inputs("tiny", B=2000, variant="q_eq_p")
+    seed = philox_seed(1, 7)
+    gpu = _run(inp, seed)
+    assert np.all(gpu[1] == 4)
+    _assert_parity(inp, seed, gpu, _oracle(inp, seed), tag="tiny-q=p")
+
+
+@pytest.mark.parametrize("variant", ["sampled", "adversarial"])
+def test_tiny_sampled_parity_and_exactness(variant):
+    """20,000 trials (one context-free target, drafted tokens drawn from the
+    drafter) in two calls of 10,000 with different seeds: oracle parity for
+    every trial and a per-position chi-square of the library's emitted tokens
+    against the target's softmax."""
+    full = make_inputs("tiny", B=20000, variant=variant)
+    emitted = [[] for _ in range(5)]
+    for call in range(2):
+        part = {n: full[n][call * 10000:(call + 1) * 10000]
+                for n in ("target", "draft", "tokens", "budgets")}
+        part["temperature"] = full["temperature"]
+        seed = philox_seed(1, 1000 + call)
+        gpu = _run(part, seed)
+        _assert_parity(part, seed, gpu, _oracle(part, seed), tag=f"tiny-{variant}-{call}")
+        toks, nacc = gpu[0], gpu[1]
+        for i in range(5):
+            emitted[i].append(toks[nacc >= i, i])
+    zt = full["target"][0].double().numpy()
+    for i in range(5):
+        e = np.concatenate(emitted[i])
+        if e.size < 500:
+            continue
+        obs = np.bincount(e, minlength=32).astype(float)
+        exp = special.softmax(zt[i]) * obs.sum()
+        keep = exp >= 5
+        obs_m = np.append(obs[keep], obs[~keep].sum())
+        exp_m = np.append(exp[keep], exp[~keep].sum())
+        if exp_m[-1] < 5:
+            obs_m[-2] += obs_m[-1]
+            exp_m[-2] += exp_m[-1]
+            obs_m, exp_m = obs_m[:-1], exp_m[:-1]
+        assert stats.chisquare(obs_m, exp_m).pvalue > 1e-3, (variant, i)
+
+
+# ------------------------------------------------------------ full configs ---
+
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_qwen3_shaped_fp32(T):
+    inp = make_inputs("qwen3", device=DEV)
+    seed = philox_seed(2, 3)
+    gpu = _run(inp, seed, temperature=T)
+    _assert_parity(inp, seed, gpu, _oracle(inp, seed, temperature=T), temperature=T,
+                   tag=f"qwen3-T{T}")
+
+
+def test_ragged_moderate_bf16():
+    inp = make_inputs("ragged", device=DEV)
+    seed = philox_seed(3, 1)
+    gpu = _run(inp, seed)
+    _assert_parity(inp, seed, gpu, _oracle(inp, seed), tag="ragged")
+
+
+def test_gemma_shaped_bf16():
+    inp = make_inputs("gemma", device=DEV)
+    seed = philox_seed(4, 1)
+    gpu = _run(inp, seed)
+    reqs = list(range(0, 128, 2))
+    _assert_parity(inp, seed, gpu, _oracle(inp, seed, reqs), requests=reqs, tag="gemma")
+
+
+@pytest.fixture(scope="module")
+def heavy():
+    return make_inputs("heavy", device=DEV)
+
+
+def test_heavy_sampled_full_launch(heavy):
+    """The benchmark's workload and launch: oracle on a sample of requests,
+    structural checks on all of them."""
+    seed = philox_seed(5, 0)
+    gpu = _run(heavy, seed)
+    toks, nacc = gpu[0], gpu[1]
+    budgets = heavy["budgets"].cpu().numpy()
+    drafted = heavy["tokens"].cpu().numpy()
+    V = heavy["target"].shape[2]
+    for b in range(len(budgets)):
+        j = int(nacc[b])
+        assert 0 <= j <= budgets[b]
+        assert list(toks[b, :j]) == list(drafted[b, :j])
+        assert 0 <= toks[b, j] < V
+        assert np.all(toks[b, j + 1:] == -1)
+    reqs = list(range(0, 512, 21))
+    _assert_parity(heavy, seed, gpu, _oracle(heavy, seed, reqs), requests=reqs, tag="heavy")
+
+
+def test_heavy_greedy_every_request(heavy):
+    seed = philox_seed(5, 1)
+    gpu = _run(heavy, seed, temperature=0.0)
+    _assert_parity(heavy, seed, gpu, _oracle(heavy, seed, temperature=0.0), temperature=0.0,
+                   tag="heavy-greedy")
+
+
+# -------------------------------------------------------------- edge cases ---
+
+def _edge_inputs(B, K, V, dtype, budgets, seed, masks=False, ties=False):
+    g = torch.Generator().manual_seed(seed)
+    zt = 2.0 * torch.randn(B, K + 1, V, generator=g)
+    zd = zt[:, :K] + 0.7 * torch.randn(B, K, V, generator=g)
+    if ties:
+        zt = torch.round(zt)
+    if masks:
+        m = torch.rand(B, K + 1, V, generator=g) < 0.3
+        zt[m] = -float("inf")
+        zt[..., 0] = 0.0                       # keep every row finite somewhere
+        md = torch.rand(B, K, V, generator=g) < 0.3
+        zd[md] = -float("inf")
+        zd[..., 1 % V] = 0.0
+    t = zt.to(dtype)
+    d = zd.to(dtype)
+    x = torch.argmax(d.float(), dim=-1).to(torch.int32)
+    k = torch.tensor(budgets, dtype=torch.int32)
+    return {"target": t, "draft": d, "tokens": x, "budgets": k}
+
+
+EDGE = [
+    # B, K, V, dtype, budgets
+    (1, 0, 1, torch.float32, [0]),
+    (3, 2, 3, torch.bfloat16, [0, 1, 2]),
+    (37, 3, 1003, torch.bfloat16, None),          # rows not 16-byte aligned
+    (37, 3, 1003, torch.float32, None),
+    (9, 8, 16392, torch.bfloat16, None),           # two chunks, ragged tail
+    (5, 4, 40003, torch.bfloat16, None),           # several chunks, misaligned rows
+    (5, 4, 40003, torch.float32, None),
+    (64, 1, 2048, torch.bfloat16, None),           # exactly one sampling tile
+]
+
+
+@pytest.mark.parametrize("B,K,V,dtype,budgets", EDGE)
+@pytest.mark.parametrize("T", [0.0, 0.7])
+@pytest.mark.parametrize("masks", [False, True])
+def test_edge_shapes(B, K, V, dtype, budgets, T, masks):
+    if budgets is None:
+        budgets = [(b * 7) % (K + 1) for b in range(B)]
+    inp = _edge_inputs(B, K, V, dtype, budgets, seed=B * 1000 + V, masks=masks, ties=(T == 0))
+    inp["temperature"] = T
+    seed = 0xABCDEF00 + B + V
+    _log(f"edge B={B} K={K} V={V} {dtype} T={T} masks={masks}")
+    gpu = _run(inp, seed, temperature=T)
+    _assert_parity(inp, seed, gpu, _oracle(inp, seed, temperature=T), temperature=T,
+                   tag=f"edge-{B}-{K}-{V}")
+
+
+def test_empty_batch_is_a_no_op():
+    sv = SpecVerify(DEV, max_batch=4, max_k=2, vocab=64, dtype=torch.float32)
+    t = torch.zeros(0, 3, 64, device=DEV)
+    d = torch.zeros(0, 2, 64, device=DEV)
+    x = torch.zeros(0, 2, dtype=torch.int32, device=DEV)
+    k = torch.zeros(0, dtype=torch.int32, device=DEV)
+    toks, nacc, p, q = sv.run(t, d, x, k, 1.0, 1)
+    torch.cuda.synchronize()
+    assert toks.shape == (0, 3) and sv.status() == 0
+    sv.close()
+
+
+def test_bad_budget_and_token_set_status_flags():
+    B, K, V = 6, 3, 500
+    inp = _edge_inputs(B, K, V, torch.bfloat16, [3, 3, 3, 3, 3, 3], seed=9)
+    inp["temperature"] = 1.0
+    bad = inp["budgets"].clone()
+    bad[1] = 7                                     # > K: clamped to K
+    bad[2] = -2                                    # < 0: clamped to 0
+    sv = SpecVerify(DEV, max_batch=B, max_k=K, vocab=V, dtype=torch.bfloat16)
+    t, d = inp["target"].to(DEV), inp["draft"].to(DEV)
+    toks, nacc, _, _ = sv.run(t, d, inp["tokens"].to(DEV), bad.to(DEV), 1.0, 5)
+    torch.cuda.synchronize()
+    assert sv.status() == binding.SV_FLAG_BAD_BUDGET
+    assert sv.status() == 0                        # reading clears it
+    clamped = dict(inp)
+    clamped["budgets"] = torch.tensor([3, 3, 0, 3, 3, 3], dtype=torch.int32)
+    decisions = _oracle(clamped, 5)
+    gpu = (toks.cpu().numpy(), nacc.cpu().numpy(), None, None, 0)
+    excused, unexcused = compare_sampled(gpu[0], gpu[1], decisions, K)
+    assert not unexcused
+    # A drafted token outside [0, V) is rejected and flagged.
+    xbad = inp["tokens"].clone()
+    xbad[4, 0] = V + 5
+    toks, nacc, p, q = sv.run(t, d, xbad.to(DEV), inp["budgets"].to(DEV), 1.0, 5)
+    torch.cuda.synchronize()
+    assert sv.status() == binding.SV_FLAG_BAD_TOKEN
+    assert int(nacc[4]) == 0 and float(p[4, 0]) == 0.0 and float(q[4, 0]) == 0.0
+    assert 0 <= int(toks[4, 0]) < V
+    sv.close()
+
+
+def test_repeat_calls_reuse_workspace_and_are_deterministic():
+    inp = make_inputs("ragged", device=DEV)
+    t, d, x, k = (inp[n].to(DEV) for n in ("target", "draft", "tokens", "budgets"))
+    sv = SpecVerify(DEV, max_batch=64, max_k=6, vocab=t.shape[2], dtype=t.dtype)
+    outs = []
+    for _ in range(3):
+        toks, nacc, p, q = sv.run(t, d, x, k, 0.8, 42)
+        outs.append((toks.clone(), nacc.clone(), p.clone(), q.clone()))
+    # A smaller batch through the same context, then the full one again.
+    sub = {n: inp[n][:17] for n in ("target", "draft", "tokens", "budgets")}
+    sub["temperature"] = 0.8
+    toks_s, nacc_s, _, _ = sv.run(t[:17].contiguous(), d[:17].contiguous(), x[:17].contiguous(),
+                                  k[:17].contiguous(), 0.8, 42)
+    toks, nacc, p, q = sv.run(t, d, x, k, 0.8, 42)
+    outs.append((toks, nacc, p, q))
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert torch.equal(a.nan_to_num(-7.0), b.nan_to_num(-7.0))
+    assert torch.equal(toks_s, outs[0][0][:17]) and torch.equal(nacc_s, outs[0][1][:17])
+    assert sv.status() == 0
+    sv.close()
+
+
+def test_runs_on_a_non_default_stream():
+    inp = make_inputs("tiny", B=256, variant="sampled")
+    s = torch.cuda.Stream(DEV)
+    t, d, x, k = (inp[n].to(DEV) for n in ("target", "draft", "tokens", "budgets"))
+    torch.cuda.synchronize()
+    sv = SpecVerify(DEV, max_batch=256, max_k=4, vocab=32, dtype=torch.float32)
+    with torch.cuda.stream(s):
+        toks, nacc, p, q = sv.run(t, d, x, k, 1.0, 11)
+    s.synchronize()
+    ref = _oracle(inp, 11)
+    excused, unexcused = compare_sampled(toks.cpu().numpy(), nacc.cpu().numpy(), ref, 4)
+    assert not unexcused
+    sv.close()
