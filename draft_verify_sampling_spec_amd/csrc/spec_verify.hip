@@ -7,27 +7,38 @@
 // per-request verify budgets of section "What DSpark adds", paragraph 2.
 // The ABI and its conventions are documented in include/spec_verify.h.
 //
-// Design (one fused, persistent kernel per call):
-//  * Work unit = one vocabulary chunk of one logit row of one request. Every
-//    chunk has the same size, so units balance perfectly; units are numbered
-//    request-major (target row 0, drafter row 0, target row 1, ...), and
-//    workgroups pull them from eight queues, one per XCD (workgroup w starts
-//    on queue w % 8, the XCD the dispatcher places it on, and steals from the
-//    others once its own is empty).
-//  * A unit's rows are streamed with 16-byte loads, every load of the unit in
-//    flight at once (8 per lane), reduced in registers: row max, then the sum
-//    of 2^((z - max) * log2(e)/T) (sampled) or the (max, lowest index) pair
-//    (greedy). The chunk's partial result goes to the workspace.
-//  * Each request counts its finished units. The workgroup that finishes the
-//    last one (release/acquire on the counter, no waiting anywhere) merges
-//    the partials, takes the accept decisions and the first-reject scan in one
-//    wave, then draws the residual / bonus token with the whole workgroup: a
-//    pass computing per-tile masses into LDS, a scan over tiles, and an
-//    element-level scan of the one tile holding the threshold. Because the
-//    request's units were processed moments earlier, the re-read row pair is
-//    served by the caches rather than HBM.
-//  * Counters clean themselves: the last arriver of a request zeroes its
-//    counter, the last workgroup to exit zeroes the queues.
+// Design: one persistent kernel per call, every logit byte read from HBM once.
+//  * Work unit = vocabulary chunk c of position i of request b: the chunk of
+//    target row i and, for a drafted position, the same chunk of drafter row
+//    i. Every chunk has the same size (448 data lanes x 4 sixteen-byte loads
+//    per row). Units are numbered request-major, position-major, chunk-minor,
+//    so the C chunks of one position (a "team") are consecutive.
+//  * The grid is exactly the resident workgroups; workgroup w takes units
+//    w, w + G, w + 2G, ... (G = grid size >= C, so two units of one
+//    workgroup never share a team).
+//  * A workgroup is 8 waves. Waves 1-7 stream data: 16-byte loads of a unit
+//    into registers, all in flight at once, reduced to the chunk's max and
+//    sum of 2^((z - max) log2(e)/T) (sampled) or (max, lowest index)
+//    (greedy). Wave 0 is the control wave: it publishes the partials with
+//    device-scope stores, counts the team's arrivals (the last arriver leads
+//    the team: merges the chunks, takes the accept decision, publishes the
+//    normalisers) and waits on other teams, so that no data wave ever waits
+//    on a synchronisation load behind its own prefetched loads.
+//  * The unit's data then waits in a per-lane LDS slot while the workgroup
+//    streams its next unit; then the control wave reads the parked team's
+//    decision. Only for the request's earliest rejected position do the
+//    members turn the parked chunk into its residual mass max(0, p - q); the
+//    last of them scans the residual CDF over chunks, and the data waves
+//    re-read just the one chunk holding the threshold for the element-level
+//    scan. The bonus draw works the same way on the target row alone.
+//  * Per request, the team that completes last writes the outputs.
+//  * Waiting: a workgroup waits for a team only after arriving at it, and
+//    while it holds just the unit after it, which lies G >= C units further
+//    on; by induction on the unit index every unit arrives. The wait is
+//    still bounded (status flag on expiry) so the kernel always drains.
+//  * Synchronisation uses device-scope relaxed atomics plus s_waitcnt, never
+//    release/acquire fences (those write back and invalidate the whole L2).
+//  * Counters clean themselves: each is zeroed by its last user.
 
 #include <hip/hip_runtime.h>
 
@@ -35,20 +46,45 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "spec_verify.h"
 
 namespace {
 
-constexpr int kThreads = 256;                 // workgroup size (4 waves)
-constexpr int kWaves = kThreads / 64;
-constexpr int kGroupsPerThread = 8;           // 16-byte loads per lane per unit
-constexpr int kTileElems = kThreads * 8;      // elements per sampling tile
-constexpr int kTilesPerPass = 4;              // tiles whose loads are in flight together
-constexpr int kNumQueues = 8;                 // one per XCD
-constexpr int kCounterStride = 32;            // 128 bytes between counters
-constexpr int kExitCounter = kNumQueues;      // index (in strides) of the exit counter
-constexpr int kCounterWords = (kNumQueues + 1) * kCounterStride;
+// The wave count is a multiple of 4 so that every SIMD of a CU holds the same
+// number of waves of each workgroup: with 5 waves, the hardware reserves two
+// wave slots per SIMD for each workgroup, and fewer workgroups fit than the
+// occupancy query reports.
+constexpr int kWaves = 8;                      // wave 0: control; waves 1-7: data
+constexpr int kThreads = kWaves * 64;
+constexpr int kDataWaves = kWaves - 1;
+constexpr int kDataThreads = kDataWaves * 64;
+constexpr int kG = 4;                          // 16-byte groups per data lane per row of a unit
+constexpr int kScanElems = kDataThreads * 8;   // elements per scan sub-tile
+constexpr int kMaxSub = 4;                     // sub-tiles per chunk (chunk <= 8192 elements)
+constexpr int kTeamWords = 32;                 // words per team record (128 bytes)
+constexpr int kReqStride = 16;                 // words between request records (64 bytes)
+constexpr unsigned kNoReject = 0x7F7F7F7Fu;    // "no rejection yet" (memset pattern)
+constexpr unsigned kSpinLimit = 1u << 20;      // bounded wait, about 0.1 s
+
+// Team record words.
+constexpr int TW_ARRIVE = 0;    // units of the team that published their partials
+constexpr int TW_PHASE = 1;     // (call epoch << 2) | PH_* bits once the leader has published
+constexpr int TW_ST = 2;        // double S_t (words 2-3)
+constexpr int TW_SD = 4;        // double S_d (words 4-5)
+constexpr int TW_MT = 6;        // float M_t
+constexpr int TW_MD = 7;        // float M_d
+constexpr int TW_ARRIVE2 = 8;   // units that published their residual mass
+constexpr unsigned PH_READY = 1u;
+constexpr unsigned PH_RESIDUAL = 2u;
+
+// Partial record of one unit (four 64-bit words):
+//   [0] sampled: (M_t bits << 32) | M_d bits    greedy: (max bits << 32) | index
+//   [1] S_t = sum over the chunk of 2^((z_t - M_t) c)   (double)
+//   [2] S_d (double)
+//   [3] residual mass of the chunk once the normalisers are known (double)
+constexpr int kPartWords = 4;
 
 // Philox4x32 constants (Salmon et al., SC'11): round multipliers and the key
 // increments applied between rounds.
@@ -59,38 +95,63 @@ constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
 
 constexpr double kLog2e = 1.4426950408889634073599246810019;
 
-// Partial result of one chunk of one row.
-//   sampled: m = chunk max, s = sum over the chunk of 2^((z - m) * c)
-//   greedy:  m = chunk max, idx = lowest index attaining it
-struct Partial {
-    float m;
-    int idx;
-    double s;
-};
-static_assert(sizeof(Partial) == 16, "Partial layout");
-
 struct Params {
-    const void* target;       // [B, K+1, V]
-    const void* draft;        // [B, K, V] (sampled mode)
-    const int32_t* tokens;    // [B, K]
-    const int32_t* budgets;   // [B]
-    int32_t* out_tokens;      // [B, K+1]
-    int32_t* out_nacc;        // [B]
-    float* out_p;             // [B, K] or null
-    float* out_q;             // [B, K] or null
-    Partial* partials;        // [B, slots, C]
-    int* arrive;              // [B]
-    unsigned* counters;       // kCounterWords
-    unsigned* status;         // 1 word
+    const void* target;            // [B, K+1, V]
+    const void* draft;             // [B, K, V] (sampled mode)
+    const int32_t* tokens;         // [B, K]
+    const int32_t* budgets;        // [B]
+    int32_t* out_tokens;           // [B, K+1]
+    int32_t* out_nacc;             // [B]
+    float* out_p;                  // [B, K] or null
+    float* out_q;                  // [B, K] or null
+    unsigned long long* part;      // [B*(K+1)*C][kPartWords]
+    unsigned* team;                // [B*(K+1)][kTeamWords]
+    unsigned long long* result;    // [B*(K+1)]: (accepted << 32) | drawn token
+    unsigned* req_count;           // [B][kReqStride]: teams completed
+    unsigned* req_first;           // [B][kReqStride]: first rejected position
+    unsigned* status;              // 1 word
     int B, K, V;
-    int C;                    // chunks per row
-    int CE;                   // elements per chunk (a multiple of the 16-byte group)
-    int slots;                // rows per request held in the partial layout (2K+1 or K+1)
-    int tiles;                // ceil(V / kTileElems)
-    float c32;                // log2(e) / T
+    int C;                         // chunks per row
+    int CE;                        // elements per chunk
+    float c32;                     // log2(e) / T
     double c64;
     uint32_t key0, key1;
+    unsigned epoch;                // call number (30 bits, never 0): tags phase words
 };
+
+// ------------------------------------------------------------- atomics --
+
+__device__ __forceinline__ void st32(unsigned* p, unsigned v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned ld32(unsigned* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st64(unsigned long long* p, unsigned long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long ld64(unsigned long long* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned add32(unsigned* p, unsigned v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave issued has completed, so that
+// device-scope stores above are visible before the counter update below.
+// The signal fences only stop the compiler from moving memory operations
+// across the wait; they emit no instruction.
+__device__ __forceinline__ void drain() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ unsigned long long as_u64(double d) {
+    return (unsigned long long)__double_as_longlong(d);
+}
+__device__ __forceinline__ double as_f64(unsigned long long u) {
+    return __longlong_as_double((long long)u);
+}
 
 // ----------------------------------------------------------------- Philox --
 
@@ -152,11 +213,21 @@ template <> struct Elem<uint16_t> {   // bfloat16 bit patterns
     }
 };
 
-// Load the group of elements [e, e + W) of a row; elements at or beyond `n`
-// read as -inf. `vec_ok` says 16-byte loads are legal for this row segment.
 template <typename E>
+__device__ __forceinline__ uint4 neg_group() {
+    return make_uint4(Elem<E>::kNegInfWord, Elem<E>::kNegInfWord, Elem<E>::kNegInfWord,
+                      Elem<E>::kNegInfWord);
+}
+
+// Load the group of elements [e, e + W) of a row segment of n elements;
+// elements at or beyond n read as -inf. `vec_ok`: 16-byte loads are legal.
+template <typename E, bool kVec = false>
 __device__ __forceinline__ uint4 load_group(const E* base, int e, int n, bool vec_ok) {
     constexpr int W = Elem<E>::W;
+    if (kVec) {
+        // Caller guarantees 16-byte alignment and that n is a multiple of W.
+        return e < n ? *reinterpret_cast<const uint4*>(base + e) : neg_group<E>();
+    }
     if (vec_ok && e + W <= n) {
         return *reinterpret_cast<const uint4*>(base + e);
     }
@@ -170,6 +241,40 @@ __device__ __forceinline__ uint4 load_group(const E* base, int e, int n, bool ve
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bool aligned16(const void* p) {
+    return (reinterpret_cast<uintptr_t>(p) & 15) == 0;
+}
+
+// --------------------------------------------------------- shared memory --
+
+struct Shared {
+    float red_m[kWaves][2];          // block max of (target, drafter)
+    double red_s[kWaves][2];         // block sums
+    float red_f[kWaves];
+    int red_i[kWaves];
+    double red_d[kWaves];
+    double scan_ws[kMaxSub * kDataWaves];
+    int leader;
+    int leader2;
+    unsigned phase;
+    float nmt, nmd;                  // normalisers of the team being finished
+    double nst, nsd;
+    // chunk scan hand-off (control wave -> data waves)
+    int scan_chunk;
+    int scan_residual;               // 1: residual p - q; 0: target row alone
+    double scan_thr;                 // threshold relative to the chunk start
+    int sub_star;
+    double sub_base;
+    // deferred draws, run by the data waves at the start of the next round
+    int pend_bonus;
+    int bonus_b, bonus_k, bonus_tr, bonus_chunk;
+    float bonus_mt, bonus_ist;
+    double bonus_thr;
+    int pend_resid;
+    int resid_b, resid_i, resid_k, resid_tr;
+    float resid_mt, resid_md, resid_ist, resid_isd;
+};
 
 // ------------------------------------------------------ block reductions --
 
@@ -199,159 +304,134 @@ __device__ __forceinline__ bool better_arg(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
 }
 
-// --------------------------------------------------------- shared memory --
-
-struct Shared {
-    float red_f[kWaves];
-    int red_i[kWaves];
-    double red_d[kWaves];
-    int unit;               // next unit of this workgroup (-1: none)
-    int last;               // this workgroup finished the last unit of a request
-    int last_b;
-    // decision -> sampler hand-off
-    int j, k, mode;         // mode 0: residual, 1: bonus (target row only)
-    float mt, md;
-    float inv_st, inv_sd;
-    double u;
-    double R;
-    int tile_star;
-    double base;
-};
-
-// Units per request for budget k.
-__device__ __forceinline__ int units_of(int k, int C, bool greedy) {
-    return (greedy ? (k + 1) : (2 * k + 1)) * C;
-}
-
-// ------------------------------------------------------------ work queue --
-
-// Thread 0 only. `q` counts the queues this workgroup found empty.
-__device__ int fetch_unit(unsigned* counters, int U, int home, int& q) {
-    while (q < kNumQueues) {
-        const int qi = (home + q) % kNumQueues;
-        const int lo = (int)(((long long)U * qi) / kNumQueues);
-        const int hi = (int)(((long long)U * (qi + 1)) / kNumQueues);
-        const unsigned idx = __hip_atomic_fetch_add(&counters[qi * kCounterStride], 1u,
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((long long)idx < (long long)(hi - lo)) return lo + (int)idx;
-        ++q;
+// Block-wide max of two values (every thread gets both results). The control
+// wave contributes -inf.
+__device__ __forceinline__ float2 block_max2(Shared& sh, float a, float b) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    a = wave_max(a);
+    b = wave_max(b);
+    if (lane == 0) {
+        sh.red_m[wave][0] = a;
+        sh.red_m[wave][1] = b;
     }
-    return -1;
+    __syncthreads();
+    float ra = sh.red_m[0][0], rb = sh.red_m[0][1];
+    #pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+        ra = fmaxf(ra, sh.red_m[w][0]);
+        rb = fmaxf(rb, sh.red_m[w][1]);
+    }
+    return make_float2(ra, rb);
 }
 
-// -------------------------------------------------------- sampling pass --
+// Block-wide sums of two doubles (every thread gets both results). Callers
+// separate consecutive uses by at least one other barrier.
+__device__ __forceinline__ double2 block_sum2(Shared& sh, double a, double b) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    a = wave_sum(a);
+    b = wave_sum(b);
+    if (lane == 0) {
+        sh.red_s[wave][0] = a;
+        sh.red_s[wave][1] = b;
+    }
+    __syncthreads();
+    double ra = sh.red_s[0][0], rb = sh.red_s[0][1];
+    #pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+        ra += sh.red_s[w][0];
+        rb += sh.red_s[w][1];
+    }
+    return make_double2(ra, rb);
+}
 
-// Unnormalised-free residual (or bonus) mass of the 8 elements starting at e.
-template <typename E>
-__device__ __forceinline__ void tile_mass(const E* rt, const E* rd, int e, int V, bool vt,
-                                          bool vd, float mt, float inv_st, float md,
-                                          float inv_sd, float c, float r[8]) {
+// ------------------------------------------------------- mass and scans --
+
+// Sampling mass of the 8 elements [e, e + 8) of a chunk of n elements:
+// residual max(0, p - q) when rd is given, else p. p = 2^((z_t - mt) c) / S_t.
+template <typename E, bool kVec>
+__device__ __forceinline__ void mass8(const E* rt, const E* rd, int e, int n, bool vt, bool vd,
+                                      float mt, float ist, float md, float isd, float c,
+                                      float r[8]) {
     constexpr int W = Elem<E>::W;
     #pragma unroll
     for (int h = 0; h < 8 / W; ++h) {
-        const uint4 gt = load_group<E>(rt, e + h * W, V, vt);
-        float pt[W];
-        #pragma unroll
-        for (int k = 0; k < W; ++k) pt[k] = fast_exp2((Elem<E>::at(gt, k) - mt) * c) * inv_st;
+        const uint4 gt = load_group<E, kVec>(rt, e + h * W, n, vt);
         if (rd != nullptr) {
-            const uint4 gd = load_group<E>(rd, e + h * W, V, vd);
+            const uint4 gd = load_group<E, kVec>(rd, e + h * W, n, vd);
             #pragma unroll
             for (int k = 0; k < W; ++k) {
-                const float qd = fast_exp2((Elem<E>::at(gd, k) - md) * c) * inv_sd;
-                r[h * W + k] = fmaxf(0.0f, pt[k] - qd);
+                const float p = fast_exp2((Elem<E>::at(gt, k) - mt) * c) * ist;
+                const float q = fast_exp2((Elem<E>::at(gd, k) - md) * c) * isd;
+                r[h * W + k] = fmaxf(0.0f, p - q);
             }
         } else {
             #pragma unroll
-            for (int k = 0; k < W; ++k) r[h * W + k] = pt[k];
+            for (int k = 0; k < W; ++k) r[h * W + k] = fast_exp2((Elem<E>::at(gt, k) - mt) * c) * ist;
         }
     }
 }
 
-// Inverse-CDF draw from the mass of the row (pair) described in `sh`:
-// y = smallest v with (running mass up to v) > u * (total mass), zero-mass
-// tokens excluded. Whole workgroup; returns y in every thread.
-template <typename E>
-__device__ int sample_row(const Params& P, Shared& sh, double* tile_sums, const E* rt,
-                          const E* rd) {
+// Element-level inverse CDF inside one chunk (whole workgroup; the data
+// waves hold the elements): returns the offset in the chunk of the smallest
+// element whose running mass (from the chunk start) exceeds thr, zero-mass
+// elements excluded; if rounding leaves no crossing, the last positive-mass
+// element; -1 if the chunk has no mass.
+template <typename E, bool kVec>
+__device__ int chunk_scan(Shared& sh, const E* rt, const E* rd, int n, float mt, float ist,
+                          float md, float isd, float c, double thr) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int V = P.V, tiles = P.tiles;
-    const bool vt = (reinterpret_cast<uintptr_t>(rt) & 15) == 0;
-    const bool vd = rd != nullptr && (reinterpret_cast<uintptr_t>(rd) & 15) == 0;
-    const float mt = sh.mt, md = sh.md, inv_st = sh.inv_st, inv_sd = sh.inv_sd;
-    const float c = P.c32;
-
-    // Pass 1: mass of every (tile, wave) segment.
-    for (int t0 = 0; t0 < tiles; t0 += kTilesPerPass) {
-        float r[kTilesPerPass][8];
-        #pragma unroll
-        for (int a = 0; a < kTilesPerPass; ++a) {
-            const int e = (t0 + a) * kTileElems + tid * 8;
-            if (t0 + a < tiles) {
-                tile_mass<E>(rt, rd, e, V, vt, vd, mt, inv_st, md, inv_sd, c, r[a]);
-            }
+    const bool data = wave > 0;
+    const int dt = tid - 64;                       // data thread index
+    const bool vt = aligned16(rt);
+    const bool vd = rd != nullptr && aligned16(rd);
+    const int nsub = (n + kScanElems - 1) / kScanElems;
+    for (int s = 0; s < nsub; ++s) {
+        float ls = 0.0f;
+        if (data) {
+            float r[8];
+            mass8<E, kVec>(rt, rd, s * kScanElems + dt * 8, n, vt, vd, mt, ist, md, isd, c, r);
+            #pragma unroll
+            for (int k = 0; k < 8; ++k) ls += r[k];
         }
-        #pragma unroll
-        for (int a = 0; a < kTilesPerPass; ++a) {
-            if (t0 + a < tiles) {
-                float ls = 0.0f;
-                #pragma unroll
-                for (int k = 0; k < 8; ++k) ls += r[a][k];
-                const double ws = wave_sum((double)ls);
-                if (lane == 0) tile_sums[(t0 + a) * kWaves + wave] = ws;
-            }
-        }
+        const double ws = wave_sum((double)ls);
+        if (data && lane == 0) sh.scan_ws[s * kDataWaves + wave - 1] = ws;
     }
     __syncthreads();
-
-    // Pass 2 (wave 0): total mass, threshold, and the tile holding it.
-    if (wave == 0) {
-        const int per = (tiles + 63) / 64;
-        const int a0 = min(lane * per, tiles), a1 = min(a0 + per, tiles);
-        double acc = 0.0;
-        for (int t = a0; t < a1; ++t) {
-            const double* ts = tile_sums + t * kWaves;
-            acc += ((ts[0] + ts[1]) + ts[2]) + ts[3];
-        }
-        const double incl = wave_incl_scan(acc, lane);
-        const double prev = __shfl_up(incl, 1, 64);
-        const double R = __shfl(incl, 63, 64);
-        const double thr = sh.u * R;
-        const unsigned long long hit = __ballot(incl > thr);
-        const int lane_star = hit ? (__ffsll((long long)hit) - 1) : 63;
-        if (lane == lane_star) {
-            double base = lane ? prev : 0.0;
-            int found = -1, last_pos = -1;
-            double base_last = 0.0;
-            for (int t = a0; t < a1; ++t) {
-                const double* ts = tile_sums + t * kWaves;
-                const double tt = ((ts[0] + ts[1]) + ts[2]) + ts[3];
-                if (tt > 0.0) {
-                    last_pos = t;
-                    base_last = base;
-                }
-                if (tt > 0.0 && base + tt > thr) {
-                    found = t;
+    if (tid == 0) {
+        double acc = 0.0, acc_last = 0.0;
+        int star = -1, last = -1;
+        for (int s = 0; s < nsub; ++s) {
+            const double* ws = sh.scan_ws + s * kDataWaves;
+            double tot = ws[0];
+            for (int w = 1; w < kDataWaves; ++w) tot += ws[w];
+            if (tot > 0.0) {
+                last = s;
+                acc_last = acc;
+                if (acc + tot > thr) {
+                    star = s;
                     break;
                 }
-                base += tt;
             }
-            if (found < 0) {          // rounding left the crossing past this lane's tiles
-                found = last_pos;
-                base = base_last;
-            }
-            sh.tile_star = found;
-            sh.base = base;
-            sh.R = R;
+            acc += tot;
         }
+        if (star < 0) {
+            star = last;
+            acc = acc_last;
+        }
+        sh.sub_star = star;
+        sh.sub_base = acc;
     }
     __syncthreads();
-    if (!(sh.R > 0.0) || sh.tile_star < 0) return -1;   // no mass at all
-
-    // Pass 3: element-level scan of the chosen tile.
-    const int ts = sh.tile_star;
-    const int e = ts * kTileElems + tid * 8;
+    const int s = sh.sub_star;
+    if (s < 0) {
+        __syncthreads();
+        return -1;
+    }
+    const int e = s * kScanElems + dt * 8;
     float r[8];
-    tile_mass<E>(rt, rd, e, V, vt, vd, mt, inv_st, md, inv_sd, c, r);
+    #pragma unroll
+    for (int k = 0; k < 8; ++k) r[k] = 0.0f;
+    if (data) mass8<E, kVec>(rt, rd, e, n, vt, vd, mt, ist, md, isd, c, r);
     double pre[8];
     double run = 0.0;
     #pragma unroll
@@ -359,33 +439,28 @@ __device__ int sample_row(const Params& P, Shared& sh, double* tile_sums, const 
         run += (double)r[k];
         pre[k] = run;
     }
-    // Block exclusive scan of the per-thread totals.
-    double incl = wave_incl_scan(run, lane);
+    const double incl = wave_incl_scan(run, lane);
     if (lane == 63) sh.red_d[wave] = incl;
     __syncthreads();
-    double excl = incl - run;
-    {
-        // Use the exact lane-exclusive value rather than incl - run.
-        const double up = __shfl_up(incl, 1, 64);
-        excl = lane ? up : 0.0;
-    }
-    for (int w = 0; w < wave; ++w) excl += sh.red_d[w];
-    const double thr = sh.u * sh.R - sh.base;
+    const double up = __shfl_up(incl, 1, 64);
+    double excl = lane ? up : 0.0;
+    for (int w = 1; w < wave; ++w) excl += sh.red_d[w];
+    const double t = thr - sh.sub_base;
     int cand = INT_MAX, last_pos = -1;
-    #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        if (r[k] > 0.0f) {
-            last_pos = e + k;
-            if (cand == INT_MAX && excl + pre[k] > thr) cand = e + k;
+    if (data) {
+        #pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (r[k] > 0.0f) {
+                last_pos = e + k;
+                if (cand == INT_MAX && excl + pre[k] > t) cand = e + k;
+            }
         }
     }
-    // Block min of candidates, block max of last positive index.
     #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         cand = min(cand, __shfl_xor(cand, off, 64));
         last_pos = max(last_pos, __shfl_xor(last_pos, off, 64));
     }
-    __syncthreads();
     if (lane == 0) {
         sh.red_i[wave] = cand;
         sh.red_f[wave] = __int_as_float(last_pos);
@@ -401,21 +476,684 @@ __device__ int sample_row(const Params& P, Shared& sh, double* tile_sums, const 
     return y != INT_MAX ? y : lp;
 }
 
+// Wave 0: find the chunk where the running mass over chunks 0..C-1 first
+// exceeds thr. mass(cc) gives chunk cc's mass. Returns (chunk, mass before it)
+// in every lane; chunk -1 if there is no mass.
+template <typename F>
+__device__ void chunk_crossing(int C, double thr, F mass, int& chunk, double& base) {
+    const int lane = threadIdx.x & 63;
+    const int per = (C + 63) / 64;
+    const int a0 = min(lane * per, C), a1 = min(a0 + per, C);
+    double acc = 0.0;
+    for (int cc = a0; cc < a1; ++cc) acc += mass(cc);
+    const double incl = wave_incl_scan(acc, lane);
+    const double prev = __shfl_up(incl, 1, 64);
+    const unsigned long long hit = __ballot(incl > thr);
+    const int lane_star = hit ? (__ffsll((long long)hit) - 1) : 63;
+    chunk = -1;
+    base = 0.0;
+    if (lane == lane_star) {
+        double b = lane ? prev : 0.0;
+        int found = -1, last = -1;
+        double b_last = 0.0;
+        for (int cc = a0; cc < a1; ++cc) {
+            const double m = mass(cc);
+            if (m > 0.0) {
+                last = cc;
+                b_last = b;
+                if (b + m > thr) {
+                    found = cc;
+                    break;
+                }
+            }
+            b += m;
+        }
+        if (found < 0) {
+            found = last;
+            b = b_last;
+        }
+        chunk = found;
+        base = b;
+    }
+    chunk = __shfl(chunk, lane_star, 64);
+    base = __shfl(base, lane_star, 64);
+}
+
+// ------------------------------------------------------ request outputs --
+
+// Control lane: team (b, i) is complete (its result word is stored). The team
+// completing last for request b writes the request's outputs and resets the
+// request's counters for the next call.
+template <bool kGreedy>
+__device__ void team_complete(const Params& P, int b, int k) {
+    drain();
+    const unsigned old = add32(&P.req_count[b * kReqStride], 1u);
+    if (old != (unsigned)k) return;
+    const unsigned fr = ld32(&P.req_first[b * kReqStride]);
+    const int j = fr < (unsigned)k ? (int)fr : k;
+    const int y = (int)(unsigned)ld64(&P.result[(size_t)b * (P.K + 1) + j]);
+    const int K = P.K;
+    P.out_nacc[b] = j;
+    for (int t = 0; t <= K; ++t) {
+        int32_t v = -1;
+        if (t < j) v = P.tokens[(size_t)b * K + t];
+        else if (t == j) v = y;
+        P.out_tokens[(size_t)b * (K + 1) + t] = v;
+    }
+    for (int t = kGreedy ? 0 : k; t < K; ++t) {
+        if (P.out_p) P.out_p[(size_t)b * K + t] = NAN;
+        if (P.out_q) P.out_q[(size_t)b * K + t] = NAN;
+    }
+    // Every unit of every team of this request has arrived: reset the teams'
+    // counters (phase words carry the call epoch and need no reset).
+    for (int t = 0; t <= k; ++t) {
+        unsigned* tw = P.team + ((size_t)b * (K + 1) + t) * kTeamWords;
+        st32(tw + TW_ARRIVE, 0u);
+        st32(tw + TW_ARRIVE2, 0u);
+    }
+    st32(&P.req_count[b * kReqStride], 0u);
+    st32(&P.req_first[b * kReqStride], kNoReject);
+}
+
+// ------------------------------------------------------------ leader work --
+
+// Control wave, greedy: merge the chunk argmaxes of target row i, decide,
+// complete the team.
+__device__ void leader_greedy(const Params& P, int b, int i, int k, int tr) {
+    const int lane = threadIdx.x & 63;
+    const int C = P.C;
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    for (int cc = lane; cc < C; cc += 64) {
+        const unsigned long long w = ld64(&P.part[((size_t)tr * C + cc) * kPartWords]);
+        const float v = __uint_as_float((unsigned)(w >> 32));
+        const int idx = (int)(unsigned)w;
+        if (better_arg(v, idx, bv, bi)) {
+            bv = v;
+            bi = idx;
+        }
+    }
+    #pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, 64);
+        const int oi = __shfl_xor(bi, off, 64);
+        if (better_arg(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+        }
+    }
+    if (lane == 0) {
+        const int best = bi == INT_MAX ? 0 : bi;      // an all -inf row: index 0
+        bool accept = true;
+        if (i < k) {
+            const int x = P.tokens[(size_t)b * P.K + i];
+            const bool valid = x >= 0 && x < P.V;
+            if (!valid) atomicOr(P.status, SV_FLAG_BAD_TOKEN);
+            accept = valid && x == best;
+            if (!accept) {
+                __hip_atomic_fetch_min(&P.req_first[b * kReqStride], (unsigned)i,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        st64(&P.result[tr], ((unsigned long long)(accept ? 1u : 0u) << 32) | (unsigned)best);
+        team_complete<true>(P, b, k);
+    }
+}
+
+// Control wave, sampled: merge the chunk statistics of target (and drafter)
+// row i; for a drafted position take the accept decision and publish the
+// normalisers; for the bonus position locate the chunk of the bonus draw and
+// leave its element scan to the data waves (pend_bonus).
+template <typename E>
+__device__ void leader_sampled(const Params& P, Shared& sh, int b, int i, int k, int tr) {
+    const int lane = threadIdx.x & 63;
+    const int C = P.C;
+    const int K = P.K;
+    const E* target = static_cast<const E*>(P.target);
+    const E* draft = static_cast<const E*>(P.draft);
+    const unsigned long long* part = P.part + (size_t)tr * C * kPartWords;
+    // Merge: M = max of chunk maxima, S = sum of S_c 2^((M_c - M) c).
+    float mt = -INFINITY, md = -INFINITY;
+    for (int cc = lane; cc < C; cc += 64) {
+        const unsigned long long w = ld64(const_cast<unsigned long long*>(&part[cc * kPartWords]));
+        mt = fmaxf(mt, __uint_as_float((unsigned)(w >> 32)));
+        md = fmaxf(md, __uint_as_float((unsigned)w));
+    }
+    mt = wave_max(mt);
+    md = wave_max(md);
+    double st = 0.0, sd = 0.0;
+    for (int cc = lane; cc < C; cc += 64) {
+        unsigned long long* pw = const_cast<unsigned long long*>(&part[cc * kPartWords]);
+        const unsigned long long w = ld64(pw);
+        const double s1 = as_f64(ld64(pw + 1));
+        const double s2 = as_f64(ld64(pw + 2));
+        const float m1 = __uint_as_float((unsigned)(w >> 32));
+        const float m2 = __uint_as_float((unsigned)w);
+        if (s1 > 0.0) st += s1 * exp2(((double)m1 - (double)mt) * P.c64);
+        if (s2 > 0.0) sd += s2 * exp2(((double)m2 - (double)md) * P.c64);
+    }
+    st = wave_sum(st);
+    sd = wave_sum(sd);
+    if (i < k) {
+        if (lane == 0) {
+            const int x = P.tokens[(size_t)b * K + i];
+            const bool valid = x >= 0 && x < P.V;
+            if (!valid) atomicOr(P.status, SV_FLAG_BAD_TOKEN);
+            double px = 0.0, qx = 0.0;
+            if (valid) {
+                const float zt = Elem<E>::one(target + ((size_t)b * (K + 1) + i) * (size_t)P.V + x);
+                const float zd = Elem<E>::one(draft + ((size_t)b * K + i) * (size_t)P.V + x);
+                px = exp2(((double)zt - (double)mt) * P.c64) / st;
+                qx = exp2(((double)zd - (double)md) * P.c64) / sd;
+            }
+            const uint4 rw = philox4x32_10((uint32_t)b, (uint32_t)i, 0u, 0u, P.key0, P.key1);
+            const bool accept = word_to_uniform(rw.x) * qx < px;
+            if (P.out_p) P.out_p[(size_t)b * K + i] = (float)px;
+            if (P.out_q) P.out_q[(size_t)b * K + i] = (float)qx;
+            bool residual = false;
+            if (!accept) {
+                const unsigned old = __hip_atomic_fetch_min(
+                    &P.req_first[b * kReqStride], (unsigned)i, __ATOMIC_RELAXED,
+                    __HIP_MEMORY_SCOPE_AGENT);
+                residual = (unsigned)i < old;          // earliest rejection so far
+            }
+            unsigned* tw = P.team + (size_t)tr * kTeamWords;
+            st64(reinterpret_cast<unsigned long long*>(tw + TW_ST), as_u64(st));
+            st64(reinterpret_cast<unsigned long long*>(tw + TW_SD), as_u64(sd));
+            st32(tw + TW_MT, __float_as_uint(mt));
+            st32(tw + TW_MD, __float_as_uint(md));
+            drain();
+            st32(tw + TW_PHASE, (P.epoch << 2) | PH_READY | (residual ? PH_RESIDUAL : 0u));
+            if (!residual) {
+                st64(&P.result[tr], ((unsigned long long)(accept ? 1u : 0u) << 32) | 0xFFFFFFFFull);
+                team_complete<false>(P, b, k);
+            }
+        }
+        return;
+    }
+    // Bonus position: needed only if nothing was rejected so far.
+    unsigned fr = 0;
+    if (lane == 0) fr = ld32(&P.req_first[b * kReqStride]);
+    fr = __shfl(fr, 0, 64);
+    int go = 0;
+    if (fr == kNoReject && st > 0.0) {
+        const uint4 rw = philox4x32_10((uint32_t)b, (uint32_t)k, 0u, 0u, P.key0, P.key1);
+        const double u = word_to_uniform(rw.y);
+        const double inv = 1.0 / st;
+        auto mass = [&](int cc) -> double {
+            unsigned long long* pw = const_cast<unsigned long long*>(&part[cc * kPartWords]);
+            const double s1 = as_f64(ld64(pw + 1));
+            const float m1 = __uint_as_float((unsigned)(ld64(pw) >> 32));
+            return s1 > 0.0 ? s1 * exp2(((double)m1 - (double)mt) * P.c64) * inv : 0.0;
+        };
+        double total = 0.0;
+        for (int cc = lane; cc < C; cc += 64) total += mass(cc);
+        total = wave_sum(total);
+        int chunk;
+        double base;
+        chunk_crossing(C, u * total, mass, chunk, base);
+        if (chunk >= 0) {
+            go = 1;
+            if (lane == 0) {
+                sh.bonus_b = b;
+                sh.bonus_k = k;
+                sh.bonus_tr = tr;
+                sh.bonus_chunk = chunk;
+                sh.bonus_mt = mt;
+                sh.bonus_ist = (float)inv;
+                sh.bonus_thr = u * total - base;
+            }
+        }
+    }
+    if (lane == 0) {
+        sh.pend_bonus = go;
+        if (!go) {
+            st64(&P.result[tr], (1ull << 32) | 0xFFFFFFFFull);
+            team_complete<false>(P, b, k);
+        }
+    }
+}
+
+// Control wave: all chunks of a residual team published their residual mass;
+// scan the residual CDF over chunks and leave the element scan of the chunk
+// holding the threshold to the data waves (pend_resid).
+template <typename E>
+__device__ void residual_locate(const Params& P, Shared& sh, int b, int i, int k, int tr,
+                                double st, float mt, float md, float ist, float isd) {
+    const int lane = threadIdx.x & 63;
+    const int C = P.C;
+    const unsigned long long* part = P.part + (size_t)tr * C * kPartWords;
+    const uint4 rw = philox4x32_10((uint32_t)b, (uint32_t)i, 0u, 0u, P.key0, P.key1);
+    const double u_s = word_to_uniform(rw.y);
+    auto rmass = [&](int cc) -> double {
+        const double v = as_f64(ld64(const_cast<unsigned long long*>(&part[cc * kPartWords + 3])));
+        return v > 0.0 ? v : 0.0;
+    };
+    double total = 0.0;
+    for (int cc = lane; cc < C; cc += 64) total += rmass(cc);
+    total = wave_sum(total);
+    int chunk = -1;
+    double base = 0.0;
+    int residual = 1;
+    if (total > 0.0) chunk_crossing(C, u_s * total, rmass, chunk, base);
+    if (chunk < 0) {
+        // The residual kept no mass (rounding only): draw from p_i.
+        residual = 0;
+        const double inv = 1.0 / st;
+        auto pmass = [&](int cc) -> double {
+            unsigned long long* pw = const_cast<unsigned long long*>(&part[cc * kPartWords]);
+            const double s1 = as_f64(ld64(pw + 1));
+            const float m1 = __uint_as_float((unsigned)(ld64(pw) >> 32));
+            return s1 > 0.0 ? s1 * exp2(((double)m1 - (double)mt) * P.c64) * inv : 0.0;
+        };
+        total = 0.0;
+        for (int cc = lane; cc < C; cc += 64) total += pmass(cc);
+        total = wave_sum(total);
+        chunk_crossing(C, u_s * total, pmass, chunk, base);
+    }
+    if (lane == 0) {
+        sh.pend_resid = 1;
+        sh.resid_b = b;
+        sh.resid_i = i;
+        sh.resid_k = k;
+        sh.resid_tr = tr;
+        sh.resid_mt = mt;
+        sh.resid_md = md;
+        sh.resid_ist = ist;
+        sh.resid_isd = isd;
+        sh.scan_chunk = chunk;
+        sh.scan_residual = residual;
+        sh.scan_thr = u_s * total - base;
+    }
+}
+
 // ---------------------------------------------------------- main kernel --
 
-template <typename E, bool kGreedy>
-__global__ __launch_bounds__(kThreads) void verify_kernel(Params P) {
+// Coordinates of a work unit (uniform across the workgroup).
+struct Unit {
+    int u;         // unit index, -1: none
+    int b, i, k, c;
+    int tr;        // team record index b * (K + 1) + i
+    int e0, n;     // chunk start and length (elements)
+    bool has_d;    // drafted position in sampled mode: the drafter row is read too
+};
+
+__device__ __forceinline__ Unit decode_unit(const Params& P, const int* off, int u, int U,
+                                            bool greedy) {
+    Unit d;
+    d.u = u < U ? u : -1;
+    d.b = d.i = d.k = d.c = d.tr = d.e0 = d.n = 0;
+    d.has_d = false;
+    if (d.u < 0) return d;
+    int lo_b = 0, hi_b = P.B;                      // largest b with off[b] <= u
+    while (hi_b - lo_b > 1) {
+        const int mid = (lo_b + hi_b) >> 1;
+        if (off[mid] <= u) lo_b = mid; else hi_b = mid;
+    }
+    d.b = lo_b;
+    const int local = u - off[d.b];
+    d.k = (off[d.b + 1] - off[d.b]) / P.C - 1;
+    d.i = local / P.C;
+    d.c = local - d.i * P.C;
+    d.tr = d.b * (P.K + 1) + d.i;
+    d.e0 = d.c * P.CE;
+    d.n = min(P.CE, P.V - d.e0);
+    d.has_d = !greedy && d.i < d.k;
+    return d;
+}
+
+// Data waves: issue the 16-byte loads of a unit into registers (no wait).
+template <typename E, bool kVec>
+__device__ __forceinline__ void issue_loads(const Params& P, const Unit& d, int dt,
+                                            uint4 (&gt)[kG], uint4 (&gd)[kG]) {
+    constexpr int W = Elem<E>::W;
+    const E* target = static_cast<const E*>(P.target);
+    const E* draft = static_cast<const E*>(P.draft);
+    const E* bt = target + ((size_t)d.b * (P.K + 1) + d.i) * (size_t)P.V + d.e0;
+    const E* bd = d.has_d ? draft + ((size_t)d.b * P.K + d.i) * (size_t)P.V + d.e0 : nullptr;
+    const bool vt = aligned16(bt);
+    const bool vd = d.has_d && aligned16(bd);
+    #pragma unroll
+    for (int j = 0; j < kG; ++j) {
+        const int e = (dt + j * kDataThreads) * W;
+        gt[j] = e < d.n ? load_group<E, kVec>(bt, e, d.n, vt) : neg_group<E>();
+        gd[j] = (d.has_d && e < d.n) ? load_group<E, kVec>(bd, e, d.n, vd) : neg_group<E>();
+    }
+}
+
+// Block-wide (max, lowest index) merge; every thread gets the result.
+__device__ __forceinline__ void block_argmax(Shared& sh, float& bv, int& bi) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    #pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (better_arg(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+        }
+    }
+    if (lane == 0) {
+        sh.red_f[wave] = bv;
+        sh.red_i[wave] = bi;
+    }
+    __syncthreads();
+    #pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        if (better_arg(sh.red_f[w], sh.red_i[w], bv, bi)) {
+            bv = sh.red_f[w];
+            bi = sh.red_i[w];
+        }
+    }
+}
+
+// Deferred draws left by the previous round (whole workgroup): the element
+// scan of the one chunk that holds the bonus or the residual threshold. The
+// control wave's lane 0 stores the result and completes the team.
+template <typename E, bool kVec, bool kCtrl>
+__device__ __forceinline__ void pending_draws(const Params& P, Shared& sh) {
+    const int K = P.K;
+    if (sh.pend_bonus) {
+        const E* target = static_cast<const E*>(P.target);
+        const int chunk = sh.bonus_chunk;
+        const int e0 = chunk * P.CE;
+        const int n = min(P.CE, P.V - e0);
+        const E* rt = target + ((size_t)sh.bonus_b * (K + 1) + sh.bonus_k) * (size_t)P.V + e0;
+        const int o = chunk_scan<E, kVec>(sh, rt, nullptr, n, sh.bonus_mt, sh.bonus_ist, 0.0f,
+                                          0.0f, P.c32, sh.bonus_thr);
+        if (kCtrl && threadIdx.x == 0) {
+            const int y = o < 0 ? 0 : e0 + o;
+            st64(&P.result[sh.bonus_tr], (1ull << 32) | (unsigned)y);
+            team_complete<false>(P, sh.bonus_b, sh.bonus_k);
+            sh.pend_bonus = 0;
+        }
+        __syncthreads();
+    }
+    if (sh.pend_resid) {
+        const E* target = static_cast<const E*>(P.target);
+        const E* draft = static_cast<const E*>(P.draft);
+        const int chunk = sh.scan_chunk;
+        int y = 0;
+        if (chunk >= 0) {
+            const int e0 = chunk * P.CE;
+            const int n = min(P.CE, P.V - e0);
+            const E* rt = target + ((size_t)sh.resid_b * (K + 1) + sh.resid_i) * (size_t)P.V + e0;
+            const E* rd = sh.scan_residual
+                              ? draft + ((size_t)sh.resid_b * K + sh.resid_i) * (size_t)P.V + e0
+                              : nullptr;
+            const int o = chunk_scan<E, kVec>(sh, rt, rd, n, sh.resid_mt, sh.resid_ist,
+                                              sh.resid_md, sh.resid_isd, P.c32, sh.scan_thr);
+            y = o < 0 ? 0 : e0 + o;
+        }
+        if (kCtrl && threadIdx.x == 0) {
+            st64(&P.result[sh.resid_tr], (unsigned)y);
+            team_complete<false>(P, sh.resid_b, sh.resid_k);
+            sh.pend_resid = 0;
+        }
+        __syncthreads();
+    }
+}
+
+// Control wave: the loop of a workgroup's control wave. It mirrors the data
+// waves' loop barrier for barrier (every branch below depends only on values
+// the whole workgroup shares), contributes neutral values to the block
+// reductions, and does all synchronisation with other workgroups.
+template <typename E, bool kGreedy, bool kVec>
+__device__ __forceinline__ void control_loop(const Params& P, Shared& sh, const int* off) {
+    const int lane = threadIdx.x & 63;
+    const int C = P.C;
+    const int U = off[P.B];
+    const int G = gridDim.x;
+    const unsigned ep = P.epoch & 0x3FFFFFFFu;
+    Unit cur = decode_unit(P, off, blockIdx.x, U, kGreedy);
+    Unit prev;
+    prev.u = -1;
+    for (;;) {
+        // Read the parked unit's team phase early; the draws below hide the latency.
+        unsigned ph = 0;
+        if (lane == 0 && prev.u >= 0) ph = ld32(P.team + (size_t)prev.tr * kTeamWords + TW_PHASE);
+
+        pending_draws<E, kVec, true>(P, sh);
+
+        if (prev.u >= 0) {
+            // Wait for the parked unit's team decision.
+            if (lane == 0) {
+                unsigned* tw = P.team + (size_t)prev.tr * kTeamWords;
+                for (unsigned it = 0; (ph >> 2) != ep && it < kSpinLimit; ++it) {
+                    __builtin_amdgcn_s_sleep(2);
+                    ph = ld32(tw + TW_PHASE);
+                }
+                if ((ph >> 2) != ep) {
+                    atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);
+                    ph = PH_READY;
+                }
+                sh.phase = ph;
+                if (ph & PH_RESIDUAL) {
+                    sh.nst = as_f64(ld64(reinterpret_cast<unsigned long long*>(tw + TW_ST)));
+                    sh.nsd = as_f64(ld64(reinterpret_cast<unsigned long long*>(tw + TW_SD)));
+                    sh.nmt = __uint_as_float(ld32(tw + TW_MT));
+                    sh.nmd = __uint_as_float(ld32(tw + TW_MD));
+                }
+            }
+            __syncthreads();
+            if (sh.phase & PH_RESIDUAL) {
+                // The request's earliest rejection: publish the parked chunk's
+                // residual mass; the last chunk to do so locates the draw.
+                const double2 R = block_sum2(sh, 0.0, 0.0);
+                int last = 0;
+                if (lane == 0) {
+                    st64(P.part + ((size_t)prev.tr * C + prev.c) * kPartWords + 3, as_u64(R.x));
+                    drain();
+                    const unsigned old = add32(&P.team[(size_t)prev.tr * kTeamWords + TW_ARRIVE2], 1u);
+                    last = old == (unsigned)C - 1;
+                }
+                last = __shfl(last, 0, 64);
+                if (last) {
+                    const float ist = (float)(1.0 / sh.nst), isd = (float)(1.0 / sh.nsd);
+                    residual_locate<E>(P, sh, prev.b, prev.i, prev.k, prev.tr, sh.nst, sh.nmt,
+                                       sh.nmd, ist, isd);
+                }
+            }
+            prev.u = -1;
+        }
+
+        if (cur.u < 0) {
+            __syncthreads();
+            if (sh.pend_bonus || sh.pend_resid) continue;
+            break;
+        }
+
+        // The current unit's chunk statistics (the data waves hold the data).
+        unsigned long long w0;
+        double s_t = 0.0, s_d = 0.0;
+        if (kGreedy) {
+            float bv = -INFINITY;
+            int bi = INT_MAX;
+            block_argmax(sh, bv, bi);
+            w0 = ((unsigned long long)__float_as_uint(bv) << 32) | (unsigned)bi;
+        } else {
+            const float2 M = block_max2(sh, -INFINITY, -INFINITY);
+            const double2 S = block_sum2(sh, 0.0, 0.0);
+            s_t = S.x;
+            s_d = S.y;
+            w0 = ((unsigned long long)__float_as_uint(M.x) << 32) | __float_as_uint(M.y);
+        }
+
+        // Publish, arrive; the last arrival of a team leads it.
+        int lead = 0;
+        if (lane == 0) {
+            unsigned long long* pw = P.part + ((size_t)cur.tr * C + cur.c) * kPartWords;
+            st64(pw, w0);
+            if (!kGreedy) {
+                st64(pw + 1, as_u64(s_t));
+                st64(pw + 2, as_u64(s_d));
+            }
+            drain();
+            const unsigned old = add32(&P.team[(size_t)cur.tr * kTeamWords + TW_ARRIVE], 1u);
+            lead = old == (unsigned)C - 1;
+        }
+        lead = __shfl(lead, 0, 64);
+        if (lead) {
+            if (kGreedy) {
+                leader_greedy(P, cur.b, cur.i, cur.k, cur.tr);
+            } else {
+                leader_sampled<E>(P, sh, cur.b, cur.i, cur.k, cur.tr);
+            }
+        }
+        __syncthreads();
+        if (cur.has_d) prev = cur;
+        cur = decode_unit(P, off, cur.u + G, U, kGreedy);
+    }
+}
+
+// Data waves: stream units through registers, reduce them, park them in LDS.
+template <typename E, bool kGreedy, bool kVec>
+__device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int* off,
+                                          uint4* stash) {
+    constexpr int W = Elem<E>::W;
+    const int dt = threadIdx.x - 64;               // data thread index
+    const int U = off[P.B];
+    const int G = gridDim.x;
+    const float cs = P.c32;
+
+    uint4 gt[kG], gd[kG];
+    Unit cur = decode_unit(P, off, blockIdx.x, U, kGreedy);
+    if (cur.u >= 0) issue_loads<E, kVec>(P, cur, dt, gt, gd);
+    bool have_prev = false;
+
+    for (;;) {
+        pending_draws<E, kVec, false>(P, sh);
+
+        if (have_prev) {
+            __syncthreads();                       // the control wave has the parked team's phase
+            if (sh.phase & PH_RESIDUAL) {
+                const float mt = sh.nmt, md = sh.nmd;
+                const float ist = (float)(1.0 / sh.nst), isd = (float)(1.0 / sh.nsd);
+                float lr = 0.0f;
+                #pragma unroll 1
+                for (int j = 0; j < kG; ++j) {
+                    // Each lane reads back only the groups it parked itself.
+                    const uint4 a = stash[(0 * kG + j) * kDataThreads + dt];
+                    const uint4 d = stash[(1 * kG + j) * kDataThreads + dt];
+                    float r[W];
+                    #pragma unroll
+                    for (int kk = 0; kk < W; ++kk) {
+                        const float pv = fast_exp2((Elem<E>::at(a, kk) - mt) * cs) * ist;
+                        const float qv = fast_exp2((Elem<E>::at(d, kk) - md) * cs) * isd;
+                        r[kk] = fmaxf(0.0f, pv - qv);
+                    }
+                    #pragma unroll
+                    for (int h = W / 2; h > 0; h >>= 1) {
+                        #pragma unroll
+                        for (int kk = 0; kk < h; ++kk) r[kk] += r[kk + h];
+                    }
+                    lr += r[0];
+                }
+                (void)block_sum2(sh, (double)lr, 0.0);
+            }
+            have_prev = false;
+        }
+
+        if (cur.u < 0) {
+            __syncthreads();
+            if (sh.pend_bonus || sh.pend_resid) continue;
+            break;
+        }
+
+        // Reduce the current unit to its chunk statistics.
+        if (kGreedy) {
+            float bv = -INFINITY;
+            int bi = INT_MAX;
+            #pragma unroll
+            for (int j = 0; j < kG; ++j) {
+                #pragma unroll
+                for (int kk = 0; kk < W; ++kk) {
+                    const float v = Elem<E>::at(gt[j], kk);
+                    if (v > bv) {                  // a lane's elements go up in index order
+                        bv = v;
+                        bi = cur.e0 + (dt + j * kDataThreads) * W + kk;
+                    }
+                }
+            }
+            block_argmax(sh, bv, bi);
+        } else {
+            float mt = -INFINITY, md = -INFINITY;
+            #pragma unroll
+            for (int j = 0; j < kG; ++j) {
+                #pragma unroll
+                for (int kk = 0; kk < W; ++kk) {
+                    mt = fmaxf(mt, Elem<E>::at(gt[j], kk));
+                    md = fmaxf(md, Elem<E>::at(gd[j], kk));
+                }
+            }
+            // Opaque raw registers: the exp pass converts them again rather
+            // than keeping every converted float alive across the barrier.
+            #pragma unroll
+            for (int j = 0; j < kG; ++j) {
+                asm volatile("" : "+v"(gt[j].x), "+v"(gt[j].y), "+v"(gt[j].z), "+v"(gt[j].w));
+                asm volatile("" : "+v"(gd[j].x), "+v"(gd[j].y), "+v"(gd[j].z), "+v"(gd[j].w));
+            }
+            const float2 M = block_max2(sh, mt, md);
+            float lt = 0.0f, ld = 0.0f;
+            if (M.x != -INFINITY) {
+                #pragma unroll
+                for (int j = 0; j < kG; ++j) {
+                    float e[W];
+                    #pragma unroll
+                    for (int kk = 0; kk < W; ++kk) e[kk] = fast_exp2((Elem<E>::at(gt[j], kk) - M.x) * cs);
+                    #pragma unroll
+                    for (int h = W / 2; h > 0; h >>= 1) {
+                        #pragma unroll
+                        for (int kk = 0; kk < h; ++kk) e[kk] += e[kk + h];
+                    }
+                    lt += e[0];
+                }
+            }
+            if (cur.has_d && M.y != -INFINITY) {
+                #pragma unroll
+                for (int j = 0; j < kG; ++j) {
+                    float e[W];
+                    #pragma unroll
+                    for (int kk = 0; kk < W; ++kk) e[kk] = fast_exp2((Elem<E>::at(gd[j], kk) - M.y) * cs);
+                    #pragma unroll
+                    for (int h = W / 2; h > 0; h >>= 1) {
+                        #pragma unroll
+                        for (int kk = 0; kk < h; ++kk) e[kk] += e[kk + h];
+                    }
+                    ld += e[0];
+                }
+            }
+            (void)block_sum2(sh, (double)lt, (double)ld);
+        }
+
+        // Park the unit, start streaming the next one.
+        const Unit nxt = decode_unit(P, off, cur.u + G, U, kGreedy);
+        if (cur.has_d) {
+            #pragma unroll
+            for (int j = 0; j < kG; ++j) {
+                stash[(0 * kG + j) * kDataThreads + dt] = gt[j];
+                stash[(1 * kG + j) * kDataThreads + dt] = gd[j];
+            }
+        }
+        if (nxt.u >= 0) issue_loads<E, kVec>(P, nxt, dt, gt, gd);
+        __syncthreads();                           // the control wave has published and led
+        if (cur.has_d) have_prev = true;
+        cur = nxt;
+    }
+}
+
+template <typename E, bool kGreedy, bool kVec>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void verify_kernel(Params P) {
     extern __shared__ __align__(16) unsigned char dyn_smem[];
     __shared__ Shared sh;
-    // Dynamic LDS: per-(tile, wave) sampling masses, then request unit offsets.
-    double* tile_sums = reinterpret_cast<double*>(dyn_smem);
-    int* off = reinterpret_cast<int*>(dyn_smem + (kGreedy ? 0 : (size_t)P.tiles * kWaves * 8));
+    // Dynamic LDS: the parked unit (sampled mode), then request unit offsets.
+    uint4* stash = reinterpret_cast<uint4*>(dyn_smem);
+    int* off = reinterpret_cast<int*>(dyn_smem + (kGreedy ? 0 : (size_t)2 * kG * kDataThreads * 16));
 
-    constexpr int W = Elem<E>::W;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int B = P.B, K = P.K, V = P.V, C = P.C;
+    const int B = P.B, K = P.K, C = P.C;
 
-    // Prologue: every workgroup scans the budgets into unit offsets.
+    // Prologue: every workgroup scans the budgets into per-request unit offsets.
     {
         const int per = (B + kThreads - 1) / kThreads;
         const int b0 = min(tid * per, B), b1 = min(b0 + per, B);
@@ -427,10 +1165,9 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(Params P) {
                 bad = true;
                 k = k < 0 ? 0 : K;
             }
-            local += units_of(k, C, kGreedy);
+            local += (k + 1) * C;
         }
         if (bad && blockIdx.x == 0) atomicOr(P.status, SV_FLAG_BAD_BUDGET);
-        // Block exclusive scan of `local`.
         int incl = local;
         #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -445,289 +1182,26 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(Params P) {
             off[b] = run;
             int k = P.budgets[b];
             k = k < 0 ? 0 : (k > K ? K : k);
-            run += units_of(k, C, kGreedy);
+            run += (k + 1) * C;
         }
         if (tid == kThreads - 1) off[B] = run;
-        __syncthreads();
-    }
-    const int U = off[B];
-    const int home = blockIdx.x % kNumQueues;
-    int qpos = 0;                                   // thread 0's queue cursor
-
-    if (tid == 0) sh.unit = fetch_unit(P.counters, U, home, qpos);
-    __syncthreads();
-
-    const E* target = static_cast<const E*>(P.target);
-    const E* draft = static_cast<const E*>(P.draft);
-
-    for (;;) {
-        const int u = sh.unit;
-        if (u < 0) break;
-        // Decode the unit: request b (largest b with off[b] <= u), row slot, chunk.
-        int lo = 0, hi = B;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (off[mid] <= u) lo = mid; else hi = mid;
-        }
-        const int b = lo;
-        const int local = u - off[b];
-        const int slot = local / C;
-        const int chunk = local - slot * C;
-        const int n_units = off[b + 1] - off[b];
-        const E* row;
-        if (kGreedy) {
-            row = target + ((size_t)b * (K + 1) + slot) * (size_t)V;
-        } else if (slot & 1) {
-            row = draft + ((size_t)b * K + (slot >> 1)) * (size_t)V;
-        } else {
-            row = target + ((size_t)b * (K + 1) + (slot >> 1)) * (size_t)V;
-        }
-        const int e0 = chunk * P.CE;
-        const int n = min(P.CE, V - e0);
-        const E* base = row + e0;
-        const bool vec_ok = (reinterpret_cast<uintptr_t>(base) & 15) == 0;
-        const int ngroups = (n + W - 1) / W;
-
-        int next = -1;
-        if (tid == 0) next = fetch_unit(P.counters, U, home, qpos);
-
-        uint4 g[kGroupsPerThread];
-        #pragma unroll
-        for (int j = 0; j < kGroupsPerThread; ++j) {
-            const int gi = tid + j * kThreads;
-            if (gi < ngroups) {
-                g[j] = load_group<E>(base, gi * W, n, vec_ok);
-            } else {
-                g[j] = make_uint4(Elem<E>::kNegInfWord, Elem<E>::kNegInfWord,
-                                  Elem<E>::kNegInfWord, Elem<E>::kNegInfWord);
-            }
-        }
-
-        Partial part;
-        if (kGreedy) {
-            float bv = -INFINITY;
-            int bi = INT_MAX;
-            #pragma unroll
-            for (int j = 0; j < kGroupsPerThread; ++j) {
-                #pragma unroll
-                for (int k = 0; k < W; ++k) {
-                    const float v = Elem<E>::at(g[j], k);
-                    const int idx = e0 + (tid + j * kThreads) * W + k;
-                    if (v > bv) {           // groups and lanes go up in index order
-                        bv = v;
-                        bi = idx;
-                    }
-                }
-            }
-            #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                const float ov = __shfl_xor(bv, o, 64);
-                const int oi = __shfl_xor(bi, o, 64);
-                if (better_arg(ov, oi, bv, bi)) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
-            if (lane == 0) {
-                sh.red_f[wave] = bv;
-                sh.red_i[wave] = bi;
-            }
-            __syncthreads();
-            if (tid == 0) {
-                for (int w = 1; w < kWaves; ++w) {
-                    if (better_arg(sh.red_f[w], sh.red_i[w], bv, bi)) {
-                        bv = sh.red_f[w];
-                        bi = sh.red_i[w];
-                    }
-                }
-                part.m = bv;
-                part.idx = bi;
-                part.s = 0.0;
-            }
-        } else {
-            float m = -INFINITY;
-            #pragma unroll
-            for (int j = 0; j < kGroupsPerThread; ++j) {
-                #pragma unroll
-                for (int k = 0; k < W; ++k) m = fmaxf(m, Elem<E>::at(g[j], k));
-            }
-            m = wave_max(m);
-            if (lane == 0) sh.red_f[wave] = m;
-            __syncthreads();
-            float M = sh.red_f[0];
-            #pragma unroll
-            for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh.red_f[w]);
-            float ls = 0.0f;
-            if (M != -INFINITY) {
-                const float c = P.c32;
-                #pragma unroll
-                for (int j = 0; j < kGroupsPerThread; ++j) {
-                    float e[W];
-                    #pragma unroll
-                    for (int k = 0; k < W; ++k) e[k] = fast_exp2((Elem<E>::at(g[j], k) - M) * c);
-                    // pairwise sum of the group
-                    #pragma unroll
-                    for (int h = W / 2; h > 0; h >>= 1) {
-                        #pragma unroll
-                        for (int k = 0; k < h; ++k) e[k] += e[k + h];
-                    }
-                    ls += e[0];
-                }
-            }
-            const double ws = wave_sum((double)ls);
-            if (lane == 0) sh.red_d[wave] = ws;
-            __syncthreads();
-            if (tid == 0) {
-                part.m = M;
-                part.idx = 0;
-                part.s = ((sh.red_d[0] + sh.red_d[1]) + sh.red_d[2]) + sh.red_d[3];
-            }
-        }
-
         if (tid == 0) {
-            P.partials[((size_t)b * P.slots + slot) * C + chunk] = part;
-            const int old = __hip_atomic_fetch_add(&P.arrive[b], 1, __ATOMIC_RELEASE,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-            const bool last = old == n_units - 1;
-            if (last) {
-                __hip_atomic_store(&P.arrive[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            sh.last = last;
-            sh.last_b = b;
-            sh.unit = next;
+            sh.pend_bonus = 0;
+            sh.pend_resid = 0;
         }
         __syncthreads();
-
-        if (sh.last) {
-            // This workgroup finished request b: decide and sample.
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            const int k = kGreedy ? n_units / C - 1 : (n_units / C - 1) / 2;
-            if (wave == 0) {
-                const int i = lane;
-                bool accept = true;          // lanes beyond the budget never reject
-                int best = 0;
-                double mt = 0.0, st = 1.0, md = 0.0, sd = 1.0;
-                if (i <= k) {
-                    const Partial* pt = P.partials + ((size_t)b * P.slots + (kGreedy ? i : 2 * i)) * C;
-                    if (kGreedy) {
-                        float bv = pt[0].m;
-                        int bi = pt[0].idx;
-                        for (int cc = 1; cc < C; ++cc) {
-                            if (better_arg(pt[cc].m, pt[cc].idx, bv, bi)) {
-                                bv = pt[cc].m;
-                                bi = pt[cc].idx;
-                            }
-                        }
-                        best = bi == INT_MAX ? 0 : bi;      // an all -inf row: index 0
-                    } else {
-                        float M = pt[0].m;
-                        for (int cc = 1; cc < C; ++cc) M = fmaxf(M, pt[cc].m);
-                        double S = 0.0;
-                        for (int cc = 0; cc < C; ++cc) {
-                            if (pt[cc].s > 0.0) S += pt[cc].s * exp2(((double)pt[cc].m - (double)M) * P.c64);
-                        }
-                        mt = M;
-                        st = S;
-                        if (i < k) {
-                            const Partial* pd = P.partials + ((size_t)b * P.slots + 2 * i + 1) * C;
-                            float Md = pd[0].m;
-                            for (int cc = 1; cc < C; ++cc) Md = fmaxf(Md, pd[cc].m);
-                            double Sd = 0.0;
-                            for (int cc = 0; cc < C; ++cc) {
-                                if (pd[cc].s > 0.0) Sd += pd[cc].s * exp2(((double)pd[cc].m - (double)Md) * P.c64);
-                            }
-                            md = Md;
-                            sd = Sd;
-                        }
-                    }
-                }
-                if (i < k) {
-                    const int x = P.tokens[(size_t)b * K + i];
-                    const bool valid = x >= 0 && x < V;
-                    if (!valid) atomicOr(P.status, SV_FLAG_BAD_TOKEN);
-                    if (kGreedy) {
-                        accept = valid && x == best;
-                    } else {
-                        double px = 0.0, qx = 0.0;
-                        if (valid) {
-                            const float zt = Elem<E>::one(target + ((size_t)b * (K + 1) + i) * (size_t)V + x);
-                            const float zd = Elem<E>::one(draft + ((size_t)b * K + i) * (size_t)V + x);
-                            px = exp2(((double)zt - mt) * P.c64) / st;
-                            qx = exp2(((double)zd - md) * P.c64) / sd;
-                        }
-                        const uint4 rw = philox4x32_10((uint32_t)b, (uint32_t)i, 0u, 0u, P.key0, P.key1);
-                        const double ua = word_to_uniform(rw.x);
-                        accept = ua * qx < px;
-                        if (P.out_p) P.out_p[(size_t)b * K + i] = (float)px;
-                        if (P.out_q) P.out_q[(size_t)b * K + i] = (float)qx;
-                    }
-                } else if (i < K) {
-                    if (P.out_p) P.out_p[(size_t)b * K + i] = NAN;
-                    if (P.out_q) P.out_q[(size_t)b * K + i] = NAN;
-                }
-                if (kGreedy && i < K && i < k) {
-                    if (P.out_p) P.out_p[(size_t)b * K + i] = NAN;
-                    if (P.out_q) P.out_q[(size_t)b * K + i] = NAN;
-                }
-                const unsigned long long rej = __ballot(!accept);
-                const int j = rej ? (__ffsll((long long)rej) - 1) : k;
-                // Emitted tokens other than the drawn one.
-                if (i <= K && i != j) {
-                    int32_t v = -1;
-                    if (i < j) v = P.tokens[(size_t)b * K + i];
-                    P.out_tokens[(size_t)b * (K + 1) + i] = v;
-                }
-                if (i == 0) P.out_nacc[b] = j;
-                if (kGreedy) {
-                    const int yj = __shfl(best, j, 64);
-                    if (i == 0) P.out_tokens[(size_t)b * (K + 1) + j] = yj;
-                } else {
-                    const double mtj = __shfl(mt, j, 64), stj = __shfl(st, j, 64);
-                    const double mdj = __shfl(md, j, 64), sdj = __shfl(sd, j, 64);
-                    if (i == 0) {
-                        sh.j = j;
-                        sh.k = k;
-                        sh.mode = j < k ? 0 : 1;
-                        sh.mt = (float)mtj;
-                        sh.inv_st = (float)(1.0 / stj);
-                        sh.md = (float)mdj;
-                        sh.inv_sd = (float)(1.0 / sdj);
-                        const uint4 rw = philox4x32_10((uint32_t)b, (uint32_t)j, 0u, 0u, P.key0, P.key1);
-                        sh.u = word_to_uniform(rw.y);
-                    }
-                }
-            }
-            __syncthreads();
-            if (!kGreedy) {
-                const int j = sh.j;
-                const E* rt = target + ((size_t)b * (K + 1) + j) * (size_t)V;
-                const E* rd = sh.mode == 0 ? draft + ((size_t)b * K + j) * (size_t)V : nullptr;
-                int y = sample_row<E>(P, sh, tile_sums, rt, rd);
-                if (y < 0 && rd != nullptr) {
-                    // The residual kept no mass (rounding only): draw from p_j.
-                    y = sample_row<E>(P, sh, tile_sums, rt, nullptr);
-                }
-                if (tid == 0) P.out_tokens[(size_t)b * (K + 1) + j] = y < 0 ? 0 : y;
-                __syncthreads();
-            }
-        }
     }
 
-    // Exit: the last workgroup out resets the queues for the next call.
-    if (tid == 0) {
-        const unsigned old = __hip_atomic_fetch_add(&P.counters[kExitCounter * kCounterStride], 1u,
-                                                    __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        if (old == gridDim.x - 1) {
-            for (int q = 0; q < kNumQueues; ++q) {
-                __hip_atomic_store(&P.counters[q * kCounterStride], 0u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
-            __hip_atomic_store(&P.counters[kExitCounter * kCounterStride], 0u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
+    // Wave specialisation: the branch is uniform per wave, and the two loops
+    // execute the same sequence of barriers.
+    if (__builtin_amdgcn_readfirstlane(wave) == 0) {
+        control_loop<E, kGreedy, kVec>(P, sh, off);
+    } else {
+        data_loop<E, kGreedy, kVec>(P, sh, off, stash);
     }
 }
 
+// Philox blocks as the verifier draws them, for checking the generator.
 __global__ void philox_words_kernel(uint32_t k0, uint32_t k1, int B, int P, uint32_t* out) {
     const long long n = (long long)B * P;
     for (long long t = blockIdx.x * (long long)blockDim.x + threadIdx.x; t < n;
@@ -745,20 +1219,17 @@ __global__ void philox_words_kernel(uint32_t k0, uint32_t k1, int B, int P, uint
 
 constexpr uint32_t kMagic = 0x53505643u;   // live context marker
 
+int elems_per_group(int dtype) { return dtype == SV_DTYPE_BF16 ? 8 : 4; }
+
+int chunk_elems(int dtype) { return kDataThreads * kG * elems_per_group(dtype); }
+
 int chunks_for(int vocab, int dtype) {
-    const int w = dtype == SV_DTYPE_BF16 ? 8 : 4;
-    const int per_unit = kThreads * kGroupsPerThread * w;
-    return (vocab + per_unit - 1) / per_unit;
+    const int ce = chunk_elems(dtype);
+    return (vocab + ce - 1) / ce;
 }
 
-int chunk_elems(int vocab, int dtype, int C) {
-    const int w = dtype == SV_DTYPE_BF16 ? 8 : 4;
-    const int ce = (vocab + C - 1) / C;
-    return (ce + w - 1) / w * w;
-}
-
-size_t dyn_smem_bytes(int B, int tiles, bool greedy) {
-    return (greedy ? 0 : (size_t)tiles * kWaves * sizeof(double)) + (size_t)(B + 1) * sizeof(int);
+size_t dyn_smem_bytes(int B, bool greedy) {
+    return (greedy ? 0 : (size_t)2 * kG * kDataThreads * 16) + (size_t)(B + 1) * sizeof(int);
 }
 
 }  // namespace
@@ -766,38 +1237,49 @@ size_t dyn_smem_bytes(int B, int tiles, bool greedy) {
 struct spec_verify_ctx {
     uint32_t magic;
     int device, max_batch, max_k, vocab, dtype;
-    int C, CE, tiles;
+    int C, CE;
     int cus;
     void* ws;
-    Partial* partials;
-    int* arrive;
-    unsigned* counters;
+    unsigned long long* part;
+    unsigned* team;
+    unsigned long long* result;
+    unsigned* req_count;
+    unsigned* req_first;
     unsigned* status;
+    unsigned calls;                // calls made so far (phase-word epochs)
+    // occupancy cache: dynamic LDS bytes -> resident workgroups per CU, per kernel
+    size_t occ_smem[8];
+    int occ_val[8];
 };
 
 namespace {
 
-template <typename E, bool G>
-int occupancy_of(size_t smem) {
+template <typename E, bool G, bool Vv>
+int occupancy_of(spec_verify_ctx* ctx, int slot, size_t smem) {
+    if (ctx->occ_smem[slot] == smem && ctx->occ_val[slot] > 0) return ctx->occ_val[slot];
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, verify_kernel<E, G>, kThreads, smem) !=
-        hipSuccess) {
-        return 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, verify_kernel<E, G, Vv>, kThreads, smem) !=
+            hipSuccess ||
+        n < 1) {
+        n = 1;
     }
-    return n > 0 ? n : 1;
+    ctx->occ_smem[slot] = smem;
+    ctx->occ_val[slot] = n;
+    return n;
 }
 
-template <typename E, bool G>
-hipError_t launch(const spec_verify_ctx* ctx, const Params& p, hipStream_t stream) {
-    const size_t smem = dyn_smem_bytes(p.B, p.tiles, G);
-    const int occ = occupancy_of<E, G>(smem);
-    long long max_units = (long long)p.B * p.slots * p.C;
-    long long grid = (long long)ctx->cus * occ;
-    if (grid > max_units) grid = max_units;
-    if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((verify_kernel<E, G>), dim3((unsigned)grid), dim3(kThreads), smem, stream,
+// Launch shape: every workgroup resident (grid = CUs x occupancy); the
+// schedule needs at least as many workgroups as a team has members.
+template <typename E, bool G, bool Vv>
+int launch(spec_verify_ctx* ctx, Params& p, hipStream_t stream) {
+    const int slot = (std::is_same<E, uint16_t>::value ? 4 : 0) + (G ? 2 : 0) + (Vv ? 1 : 0);
+    const size_t smem = dyn_smem_bytes(p.B, G);
+    const int occ = occupancy_of<E, G, Vv>(ctx, slot, smem);
+    const long long grid = (long long)ctx->cus * occ;
+    if (grid < (long long)p.C) return SV_ERR_ARG;   // a team would not fit
+    hipLaunchKernelGGL((verify_kernel<E, G, Vv>), dim3((unsigned)grid), dim3(kThreads), smem, stream,
                        p);
-    return hipGetLastError();
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
 bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -878,29 +1360,40 @@ int spec_verify_init(spec_verify_ctx** out, int device, int max_batch, int max_k
     c->vocab = vocab;
     c->dtype = dtype;
     c->C = chunks_for(vocab, dtype);
-    c->CE = chunk_elems(vocab, dtype, c->C);
-    c->tiles = (vocab + kTileElems - 1) / kTileElems;
+    c->CE = chunk_elems(dtype);
     int rc = SV_OK;
     if (hipDeviceGetAttribute(&c->cus, hipDeviceAttributeMultiprocessorCount, device) !=
         hipSuccess) {
         rc = SV_ERR_HIP;
     }
-    const size_t slots = 2 * (size_t)max_k + 1;
-    const size_t part_bytes = (size_t)max_batch * slots * c->C * sizeof(Partial);
-    const size_t arrive_bytes = ((size_t)max_batch * sizeof(int) + 255) / 256 * 256;
-    const size_t counter_bytes = (size_t)kCounterWords * sizeof(unsigned);
-    const size_t total = part_bytes + arrive_bytes + counter_bytes + 256;
+    auto round256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t teams = (size_t)max_batch * (max_k + 1);
+    const size_t part_bytes = round256(teams * c->C * kPartWords * 8);
+    const size_t team_bytes = round256(teams * kTeamWords * 4);
+    const size_t result_bytes = round256(teams * 8);
+    const size_t req_bytes = round256((size_t)max_batch * kReqStride * 4);
+    const size_t total = part_bytes + team_bytes + result_bytes + 2 * req_bytes + 256;
     if (rc == SV_OK && hipMalloc(&c->ws, total) != hipSuccess) {
         c->ws = nullptr;
         rc = SV_ERR_NOMEM;
     }
     if (rc == SV_OK) {
         unsigned char* w = static_cast<unsigned char*>(c->ws);
-        c->partials = reinterpret_cast<Partial*>(w);
-        c->arrive = reinterpret_cast<int*>(w + part_bytes);
-        c->counters = reinterpret_cast<unsigned*>(w + part_bytes + arrive_bytes);
-        c->status = reinterpret_cast<unsigned*>(w + part_bytes + arrive_bytes + counter_bytes);
-        if (hipMemset(c->ws, 0, total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        size_t o = 0;
+        c->part = reinterpret_cast<unsigned long long*>(w + o);
+        o += part_bytes;
+        c->team = reinterpret_cast<unsigned*>(w + o);
+        o += team_bytes;
+        c->result = reinterpret_cast<unsigned long long*>(w + o);
+        o += result_bytes;
+        c->req_count = reinterpret_cast<unsigned*>(w + o);
+        o += req_bytes;
+        c->req_first = reinterpret_cast<unsigned*>(w + o);
+        o += req_bytes;
+        c->status = reinterpret_cast<unsigned*>(w + o);
+        if (hipMemset(c->ws, 0, total) != hipSuccess ||
+            hipMemset(c->req_first, 0x7F, req_bytes) != hipSuccess ||
+            hipDeviceSynchronize() != hipSuccess) {
             rc = SV_ERR_HIP;
         }
     }
@@ -939,34 +1432,49 @@ int spec_verify_run(spec_verify_ctx* ctx, const void* target_logits, const void*
     p.out_nacc = out_num_accepted;
     p.out_p = out_p_draft;
     p.out_q = out_q_draft;
-    p.partials = ctx->partials;
-    p.arrive = ctx->arrive;
-    p.counters = ctx->counters;
+    p.part = ctx->part;
+    p.team = ctx->team;
+    p.result = ctx->result;
+    p.req_count = ctx->req_count;
+    p.req_first = ctx->req_first;
     p.status = ctx->status;
     p.B = B;
     p.K = K;
     p.V = ctx->vocab;
     p.C = ctx->C;
     p.CE = ctx->CE;
-    p.slots = greedy ? K + 1 : 2 * K + 1;
-    p.tiles = ctx->tiles;
     p.c64 = greedy ? 0.0 : kLog2e / (double)temperature;
     p.c32 = (float)p.c64;
     p.key0 = (uint32_t)(seed & 0xFFFFFFFFu);
     p.key1 = (uint32_t)(seed >> 32);
+    ctx->calls = ctx->calls % 0x3FFFFFFFu + 1u;     // 1 .. 2^30 - 1, never 0
+    p.epoch = ctx->calls;
 
     int prev = -1;
     if (hipGetDevice(&prev) != hipSuccess) return SV_ERR_HIP;
     if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return SV_ERR_HIP;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
+    int r;
+    // Vector-only loads when every row starts on a 16-byte boundary.
+    const size_t es = ctx->dtype == SV_DTYPE_BF16 ? 2 : 4;
+    const bool vec = aligned_to(target_logits, 16) &&
+                     (greedy || K == 0 || aligned_to(draft_logits, 16)) &&
+                     ((size_t)ctx->vocab * es) % 16 == 0;
     if (ctx->dtype == SV_DTYPE_BF16) {
-        e = greedy ? launch<uint16_t, true>(ctx, p, s) : launch<uint16_t, false>(ctx, p, s);
+        if (vec) {
+            r = greedy ? launch<uint16_t, true, true>(ctx, p, s) : launch<uint16_t, false, true>(ctx, p, s);
+        } else {
+            r = greedy ? launch<uint16_t, true, false>(ctx, p, s) : launch<uint16_t, false, false>(ctx, p, s);
+        }
     } else {
-        e = greedy ? launch<float, true>(ctx, p, s) : launch<float, false>(ctx, p, s);
+        if (vec) {
+            r = greedy ? launch<float, true, true>(ctx, p, s) : launch<float, false, true>(ctx, p, s);
+        } else {
+            r = greedy ? launch<float, true, false>(ctx, p, s) : launch<float, false, false>(ctx, p, s);
+        }
     }
     if (prev != ctx->device) (void)hipSetDevice(prev);
-    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+    return r;
 }
 
 int spec_verify_status(spec_verify_ctx* ctx, uint32_t* flags) {

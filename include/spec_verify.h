@@ -80,6 +80,11 @@ enum sv_status {
 #define SV_FLAG_BAD_BUDGET 0x1u /* a budget was outside [0, K]; it was clamped */
 #define SV_FLAG_BAD_TOKEN  0x2u /* a checked drafted token was outside [0, V);
                                    it was treated as rejected, its p and q as 0 */
+#define SV_FLAG_SYNC_TIMEOUT 0x4u /* a workgroup gave up waiting for the other
+                                   chunks of a row pair (bounded wait); the
+                                   outputs of that call are not valid. Only
+                                   possible if the device could not keep the
+                                   launch's workgroups resident. */
 
 /* Library limits. */
 #define SV_MAX_BATCH 16384
@@ -94,8 +99,8 @@ enum sv_status {
  *   max_k      largest K a run will pass, 0..SV_MAX_K.
  *   vocab      V, the vocabulary size of every run, 1..SV_MAX_VOCAB.
  *   dtype      sv_dtype of the logits of every run.
- * Allocates and zeroes the device workspace (per-row partial statistics,
- * per-request counters, work-queue counters, status word). Synchronous.
+ * Allocates and zeroes the device workspace (per-chunk partial statistics,
+ * per-row team records, per-request counters, status word). Synchronous.
  * Errors: SV_ERR_NULL, SV_ERR_ARG, SV_ERR_DTYPE, SV_ERR_HIP, SV_ERR_NOMEM.
  */
 int spec_verify_init(spec_verify_ctx** out, int device, int max_batch, int max_k,

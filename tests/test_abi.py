@@ -54,9 +54,13 @@ def test_strerror_covers_every_code():
 
 
 def test_chunk_count():
-    assert sb.spec_verify_chunks(151936, sb.SV_DTYPE_BF16) == 10
-    assert sb.spec_verify_chunks(262144, sb.SV_DTYPE_BF16) == 16
-    assert sb.spec_verify_chunks(151936, sb.SV_DTYPE_F32) == 19
+    # A chunk is 256 lanes x 4 sixteen-byte loads: 8192 bf16 or 4096 fp32 values.
+    # a chunk is 448 lanes x 4 sixteen-byte groups: 14336 bf16 or 7168 fp32
+    assert sb.spec_verify_chunks(151936, sb.SV_DTYPE_BF16) == 11
+    assert sb.spec_verify_chunks(262144, sb.SV_DTYPE_BF16) == 19
+    assert sb.spec_verify_chunks(151936, sb.SV_DTYPE_F32) == 22
+    assert sb.spec_verify_chunks(14336, sb.SV_DTYPE_BF16) == 1
+    assert sb.spec_verify_chunks(14337, sb.SV_DTYPE_BF16) == 2
     assert sb.spec_verify_chunks(32, sb.SV_DTYPE_F32) == 1
     assert sb.spec_verify_chunks(0, sb.SV_DTYPE_F32) == sb.SV_ERR_ARG
     assert sb.spec_verify_chunks(32, 7) == sb.SV_ERR_DTYPE
