@@ -17,28 +17,39 @@
 //    w, w + G, w + 2G, ... (G = grid size >= C, so two units of one
 //    workgroup never share a team).
 //  * A workgroup is 8 waves. Waves 1-7 stream data: 16-byte loads of a unit
-//    into registers, all in flight at once, reduced to the chunk's max and
+//    into registers, all in flight at once, reduced per wave to the max and
 //    sum of 2^((z - max) log2(e)/T) (sampled) or (max, lowest index)
-//    (greedy). Wave 0 is the control wave: it publishes the partials with
-//    device-scope stores, counts the team's arrivals (the last arriver leads
-//    the team: merges the chunks, takes the accept decision, publishes the
-//    normalisers) and waits on other teams, so that no data wave ever waits
-//    on a synchronisation load behind its own prefetched loads.
-//  * The unit's data then waits in a per-lane LDS slot while the workgroup
-//    streams its next unit; then the control wave reads the parked team's
-//    decision. Only for the request's earliest rejected position do the
-//    members turn the parked chunk into its residual mass max(0, p - q); the
-//    last of them scans the residual CDF over chunks, and the data waves
-//    re-read just the one chunk holding the threshold for the element-level
-//    scan. The bonus draw works the same way on the target row alone.
+//    (greedy), posted to LDS. Wave 0 is the control wave: it merges the
+//    waves' statistics and publishes the chunk's partial record. The two
+//    kinds of waves exchange tagged LDS messages, with no workgroup barrier
+//    in the streaming loop.
+//  * Sampled mode: every record word carries the call's epoch, so a record
+//    is complete when all its words carry it. Every member of a team reads
+//    the C records of its team once they are complete and takes the team's
+//    accept decision itself (the same deterministic merge in every member);
+//    no election and no counter sits between a chunk's statistics and its
+//    team's decision. Meanwhile the drafted unit's data waits in a per-lane
+//    LDS slot; on a rejection each member turns its parked chunk into its
+//    residual mass max(0, p - q) and publishes it.
+//  * The member holding chunk 0 keeps the books: p(x), q(x), the decision
+//    word, and, for a rejection or a bonus position, a draw queued to the end
+//    of its loop. There, once the earlier positions of the request are
+//    decided, the draw is made only for the request's first rejection (or
+//    the bonus position when none): residual CDF over chunks from the
+//    published masses, then the whole workgroup re-reads the one chunk that
+//    holds the threshold for the element-level scan.
+//  * Greedy mode: the last arriver of a team (device-scope counter) merges
+//    the chunk argmaxes and decides; no data is parked.
 //  * Per request, the team that completes last writes the outputs.
-//  * Waiting: a workgroup waits for a team only after arriving at it, and
-//    while it holds just the unit after it, which lies G >= C units further
-//    on; by induction on the unit index every unit arrives. The wait is
-//    still bounded (status flag on expiry) so the kernel always drains.
-//  * Synchronisation uses device-scope relaxed atomics plus s_waitcnt, never
-//    release/acquire fences (those write back and invalidate the whole L2).
-//  * Counters clean themselves: each is zeroed by its last user.
+//  * Waiting: inside the loop a workgroup waits only for the records of a
+//    team it has already published to, and never while it holds an
+//    unpublished unit; by induction on the unit index every record gets
+//    written. Waits at the end of the loop depend only on work done inside
+//    loops. Every wait is bounded (status flag on expiry) so the kernel
+//    always drains.
+//  * Synchronisation uses device-scope relaxed atomics (plus s_waitcnt where
+//    a counter orders earlier stores), never release/acquire fences: those
+//    write back and invalidate the whole L2.
 
 #include <hip/hip_runtime.h>
 
@@ -62,29 +73,29 @@ constexpr int kDataWaves = kWaves - 1;
 constexpr int kDataThreads = kDataWaves * 64;
 constexpr int kG = 4;                          // 16-byte groups per data lane per row of a unit
 constexpr int kScanElems = kDataThreads * 8;   // elements per scan sub-tile
-constexpr int kMaxSub = 4;                     // sub-tiles per chunk (chunk <= 8192 elements)
+constexpr int kMaxSub = 4;                     // sub-tiles per chunk
 constexpr int kTeamWords = 32;                 // words per team record (128 bytes)
-constexpr int kReqStride = 16;                 // words between request records (64 bytes)
-constexpr unsigned kNoReject = 0x7F7F7F7Fu;    // "no rejection yet" (memset pattern)
-constexpr unsigned kSpinLimit = 1u << 20;      // bounded wait, about 0.1 s
+constexpr int kReqStride = 16;                 // words between request counters (64 bytes)
+constexpr unsigned kSpinLimit = 1u << 20;      // bounded device-scope wait (~1 s)
+constexpr unsigned kLdsSpinLimit = 1u << 26;   // bounded LDS mailbox wait (~3 s)
 
 // Team record words.
-constexpr int TW_ARRIVE = 0;    // units of the team that published their partials
-constexpr int TW_PHASE = 1;     // (call epoch << 2) | PH_* bits once the leader has published
-constexpr int TW_ST = 2;        // double S_t (words 2-3)
-constexpr int TW_SD = 4;        // double S_d (words 4-5)
-constexpr int TW_MT = 6;        // float M_t
-constexpr int TW_MD = 7;        // float M_d
-constexpr int TW_ARRIVE2 = 8;   // units that published their residual mass
-constexpr unsigned PH_READY = 1u;
-constexpr unsigned PH_RESIDUAL = 2u;
+constexpr int TW_ARRIVE = 0;    // greedy: units of the team that published their argmax
+constexpr int TW_DEC = 2;       // 64-bit decision: (epoch << 32) | accepted (words 2-3)
 
-// Partial record of one unit (four 64-bit words):
-//   [0] sampled: (M_t bits << 32) | M_d bits    greedy: (max bits << 32) | index
-//   [1] S_t = sum over the chunk of 2^((z_t - M_t) c)   (double)
-//   [2] S_d (double)
-//   [3] residual mass of the chunk once the normalisers are known (double)
-constexpr int kPartWords = 4;
+// Unit record: 8 64-bit words.
+//   sampled: word f = (value bits << 32) | epoch for the fp32 values
+//            R_MT max of z_t, R_MD max of z_d, R_ST sum of 2^((z_t - M_t) c),
+//            R_SD likewise, R_RES residual mass once the team has rejected
+//   greedy:  word 0 = (max bits << 32) | lowest index of the max
+constexpr int kRecWords = 8;
+constexpr int R_MT = 0, R_MD = 1, R_ST = 2, R_SD = 3, R_RES = 4;
+constexpr int kStatWords = 4;   // words R_MT..R_SD make a record complete
+constexpr int kMaxChunks = 192; // chunks per row the team merge supports
+
+// Decision posted to the data waves for a parked unit.
+constexpr unsigned PH_ACCEPT = 1u;
+constexpr unsigned PH_REJECT = 2u;              // data waves: publish the residual mass
 
 // Philox4x32 constants (Salmon et al., SC'11): round multipliers and the key
 // increments applied between rounds.
@@ -104,19 +115,20 @@ struct Params {
     int32_t* out_nacc;             // [B]
     float* out_p;                  // [B, K] or null
     float* out_q;                  // [B, K] or null
-    unsigned long long* part;      // [B*(K+1)*C][kPartWords]
+    unsigned long long* rec;       // [B*(K+1)*C][kRecWords]
     unsigned* team;                // [B*(K+1)][kTeamWords]
-    unsigned long long* result;    // [B*(K+1)]: (accepted << 32) | drawn token
+    unsigned* result;              // [B*(K+1)]: drawn token of the team
     unsigned* req_count;           // [B][kReqStride]: teams completed
-    unsigned* req_first;           // [B][kReqStride]: first rejected position
+    int* tasks;                    // [G][task_cap]: deferred draws, 2 * team + is_bonus
     unsigned* status;              // 1 word
     int B, K, V;
     int C;                         // chunks per row
     int CE;                        // elements per chunk
+    int task_cap;                  // task list entries per workgroup
     float c32;                     // log2(e) / T
     double c64;
     uint32_t key0, key1;
-    unsigned epoch;                // call number (30 bits, never 0): tags phase words
+    unsigned epoch;                // call number (never 0): tags record and decision words
 };
 
 // ------------------------------------------------------------- atomics --
@@ -151,6 +163,17 @@ __device__ __forceinline__ unsigned long long as_u64(double d) {
 }
 __device__ __forceinline__ double as_f64(unsigned long long u) {
     return __longlong_as_double((long long)u);
+}
+
+// Epoch-tagged 32-bit value.
+__device__ __forceinline__ unsigned long long tagged(float v, unsigned ep) {
+    return ((unsigned long long)__float_as_uint(v) << 32) | ep;
+}
+__device__ __forceinline__ float tag_val(unsigned long long w) {
+    return __uint_as_float((unsigned)(w >> 32));
+}
+__device__ __forceinline__ bool tag_ok(unsigned long long w, unsigned ep) {
+    return (unsigned)w == ep;
 }
 
 // ----------------------------------------------------------------- Philox --
@@ -248,35 +271,77 @@ __device__ __forceinline__ bool aligned16(const void* p) {
 
 // --------------------------------------------------------- shared memory --
 
+// Workgroup-local state. The streaming loop has no workgroup barrier: the
+// data waves and the control wave exchange tagged messages through these
+// mailboxes (a tag is written after its payload; LDS operations of one wave
+// complete in order, so a reader that sees the tag sees the payload).
 struct Shared {
-    float red_m[kWaves][2];          // block max of (target, drafter)
-    double red_s[kWaves][2];         // block sums
+    // Data wave -> control wave: a unit's per-wave statistics, by round parity.
+    //   sampled: (max, sum of 2^((z - max) c)) of the target and drafter parts
+    //   greedy:  (max, lowest index of the max) of the target part
+    float st_mt[2][kDataWaves];
+    float st_md[2][kDataWaves];
+    double st_st[2][kDataWaves];
+    double st_sd[2][kDataWaves];
+    int st_idx[2][kDataWaves];
+    int st_tag[2][kDataWaves];                   // round + 1
+    int st_done[2];                              // control wave: round + 1 of the slot it read last
+    // Control wave -> data waves: the parked unit's decision and the team's
+    // normalisers, posted in round r (tag r) into slot r & 1.
+    unsigned ph_val[2];
+    float ph_mt[2], ph_md[2], ph_ist[2], ph_isd[2];
+    int ph_tag[2];
+    // Data wave -> control wave: the parked chunk's residual mass (tag: round).
+    double rs_val[kDataWaves];
+    int rs_tag[kDataWaves];
+    // Set once a bounded wait expired: every later wait returns at once.
+    int abort_wait;
+    // End of the loop: deferred draws of this workgroup and the one at hand.
+    int ntasks;
+    int tk_draw;                                 // 1: scan tk_chunk
+    int tk_chunk, tk_mode;                       // mode: 0 target row, 1 residual
+    double tk_thr;
+    float tk_mt, tk_md, tk_ist, tk_isd;
+    // Block-wide scan scratch (deferred draws only, under barriers).
+    double scan_ws[kMaxSub * kDataWaves];
+    double red_d[kWaves];
     float red_f[kWaves];
     int red_i[kWaves];
-    double red_d[kWaves];
-    double scan_ws[kMaxSub * kDataWaves];
-    int leader;
-    int leader2;
-    unsigned phase;
-    float nmt, nmd;                  // normalisers of the team being finished
-    double nst, nsd;
-    // chunk scan hand-off (control wave -> data waves)
-    int scan_chunk;
-    int scan_residual;               // 1: residual p - q; 0: target row alone
-    double scan_thr;                 // threshold relative to the chunk start
     int sub_star;
     double sub_base;
-    // deferred draws, run by the data waves at the start of the next round
-    int pend_bonus;
-    int bonus_b, bonus_k, bonus_tr, bonus_chunk;
-    float bonus_mt, bonus_ist;
-    double bonus_thr;
-    int pend_resid;
-    int resid_b, resid_i, resid_k, resid_tr;
-    float resid_mt, resid_md, resid_ist, resid_isd;
 };
 
-// ------------------------------------------------------ block reductions --
+// Relaxed workgroup-scope accesses for the mailboxes.
+__device__ __forceinline__ void lds_put(int* p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ int lds_get(int* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// Compiler-only ordering point between a payload and its tag.
+__device__ __forceinline__ void order() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
+
+// Record a synchronisation time-out: the status word gets the flag, later
+// waits of the workgroup return at once, and the kernel runs to its end with
+// outputs that are not valid.
+__device__ __forceinline__ void give_up(const Params& P, Shared& sh) {
+    atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);
+    lds_put(&sh.abort_wait, 1);
+}
+
+// Poll an LDS tag until it equals want (bounded).
+__device__ __forceinline__ void lds_wait(const Params& P, Shared& sh, int* tag, int want) {
+    for (unsigned it = 0; lds_get(tag) != want; ++it) {
+        if (it >= kLdsSpinLimit || lds_get(&sh.abort_wait)) {
+            give_up(P, sh);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    order();
+}
+
+// ------------------------------------------------------ wave reductions --
 
 __device__ __forceinline__ float wave_max(float v) {
     #pragma unroll
@@ -302,46 +367,6 @@ __device__ __forceinline__ double wave_incl_scan(double v, int lane) {
 
 __device__ __forceinline__ bool better_arg(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
-}
-
-// Block-wide max of two values (every thread gets both results). The control
-// wave contributes -inf.
-__device__ __forceinline__ float2 block_max2(Shared& sh, float a, float b) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    a = wave_max(a);
-    b = wave_max(b);
-    if (lane == 0) {
-        sh.red_m[wave][0] = a;
-        sh.red_m[wave][1] = b;
-    }
-    __syncthreads();
-    float ra = sh.red_m[0][0], rb = sh.red_m[0][1];
-    #pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
-        ra = fmaxf(ra, sh.red_m[w][0]);
-        rb = fmaxf(rb, sh.red_m[w][1]);
-    }
-    return make_float2(ra, rb);
-}
-
-// Block-wide sums of two doubles (every thread gets both results). Callers
-// separate consecutive uses by at least one other barrier.
-__device__ __forceinline__ double2 block_sum2(Shared& sh, double a, double b) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    a = wave_sum(a);
-    b = wave_sum(b);
-    if (lane == 0) {
-        sh.red_s[wave][0] = a;
-        sh.red_s[wave][1] = b;
-    }
-    __syncthreads();
-    double ra = sh.red_s[0][0], rb = sh.red_s[0][1];
-    #pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
-        ra += sh.red_s[w][0];
-        rb += sh.red_s[w][1];
-    }
-    return make_double2(ra, rb);
 }
 
 // ------------------------------------------------------- mass and scans --
@@ -521,18 +546,29 @@ __device__ void chunk_crossing(int C, double thr, F mass, int& chunk, double& ba
 
 // ------------------------------------------------------ request outputs --
 
-// Control lane: team (b, i) is complete (its result word is stored). The team
-// completing last for request b writes the request's outputs and resets the
-// request's counters for the next call.
+__device__ __forceinline__ unsigned long long* dec_word(const Params& P, int tr) {
+    return reinterpret_cast<unsigned long long*>(P.team + (size_t)tr * kTeamWords + TW_DEC);
+}
+
+// Control lane: team tr = (b, i) of a request with budget k is complete (its
+// decision and, if it drew one, its token are stored). The team completing
+// last for request b writes the request's outputs: j = the first rejected
+// position (k if none), the token drawn by team j.
 template <bool kGreedy>
 __device__ void team_complete(const Params& P, int b, int k) {
     drain();
     const unsigned old = add32(&P.req_count[b * kReqStride], 1u);
     if (old != (unsigned)k) return;
-    const unsigned fr = ld32(&P.req_first[b * kReqStride]);
-    const int j = fr < (unsigned)k ? (int)fr : k;
-    const int y = (int)(unsigned)ld64(&P.result[(size_t)b * (P.K + 1) + j]);
     const int K = P.K;
+    const int tr0 = b * (K + 1);
+    int j = k;
+    for (int t = 0; t < k; ++t) {
+        if ((ld64(dec_word(P, tr0 + t)) & 1ull) == 0) {
+            j = t;
+            break;
+        }
+    }
+    const int y = (int)ld32(&P.result[tr0 + j]);
     P.out_nacc[b] = j;
     for (int t = 0; t <= K; ++t) {
         int32_t v = -1;
@@ -544,18 +580,15 @@ __device__ void team_complete(const Params& P, int b, int k) {
         if (P.out_p) P.out_p[(size_t)b * K + t] = NAN;
         if (P.out_q) P.out_q[(size_t)b * K + t] = NAN;
     }
-    // Every unit of every team of this request has arrived: reset the teams'
-    // counters (phase words carry the call epoch and need no reset).
-    for (int t = 0; t <= k; ++t) {
-        unsigned* tw = P.team + ((size_t)b * (K + 1) + t) * kTeamWords;
-        st32(tw + TW_ARRIVE, 0u);
-        st32(tw + TW_ARRIVE2, 0u);
+    // Every unit of the request has been counted: reset the counters for the
+    // next call (tagged words carry the call epoch and need no reset).
+    if (kGreedy) {
+        for (int t = 0; t <= k; ++t) st32(P.team + (size_t)(tr0 + t) * kTeamWords + TW_ARRIVE, 0u);
     }
     st32(&P.req_count[b * kReqStride], 0u);
-    st32(&P.req_first[b * kReqStride], kNoReject);
 }
 
-// ------------------------------------------------------------ leader work --
+// ------------------------------------------------------------ greedy leader --
 
 // Control wave, greedy: merge the chunk argmaxes of target row i, decide,
 // complete the team.
@@ -565,7 +598,7 @@ __device__ void leader_greedy(const Params& P, int b, int i, int k, int tr) {
     float bv = -INFINITY;
     int bi = INT_MAX;
     for (int cc = lane; cc < C; cc += 64) {
-        const unsigned long long w = ld64(&P.part[((size_t)tr * C + cc) * kPartWords]);
+        const unsigned long long w = ld64(&P.rec[((size_t)tr * C + cc) * kRecWords]);
         const float v = __uint_as_float((unsigned)(w >> 32));
         const int idx = (int)(unsigned)w;
         if (better_arg(v, idx, bv, bi)) {
@@ -590,181 +623,88 @@ __device__ void leader_greedy(const Params& P, int b, int i, int k, int tr) {
             const bool valid = x >= 0 && x < P.V;
             if (!valid) atomicOr(P.status, SV_FLAG_BAD_TOKEN);
             accept = valid && x == best;
-            if (!accept) {
-                __hip_atomic_fetch_min(&P.req_first[b * kReqStride], (unsigned)i,
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
         }
-        st64(&P.result[tr], ((unsigned long long)(accept ? 1u : 0u) << 32) | (unsigned)best);
+        st32(&P.result[tr], (unsigned)best);
+        st64(dec_word(P, tr), ((unsigned long long)P.epoch << 32) | (accept ? 1u : 0u));
         team_complete<true>(P, b, k);
     }
 }
 
-// Control wave, sampled: merge the chunk statistics of target (and drafter)
-// row i; for a drafted position take the accept decision and publish the
-// normalisers; for the bonus position locate the chunk of the bonus draw and
-// leave its element scan to the data waves (pend_bonus).
-template <typename E>
-__device__ void leader_sampled(const Params& P, Shared& sh, int b, int i, int k, int tr) {
+// ----------------------------------------------------- sampled team merge --
+
+// Team-wide normalisers (identical in every workgroup that computes them:
+// same inputs, same lanes, same reduction order).
+struct TeamStats {
+    float mt, md;      // max of the target / drafter row
+    double st, sd;     // sum of 2^((z - max) c) over the row
+};
+
+// Control wave: wait until the C records of team tr are complete (bounded),
+// then merge them: M = max of chunk maxima, S = sum of S_c 2^((M_c - M) c).
+// Lane l holds chunks l, l + 64, l + 128 (C <= kMaxChunks).
+__device__ TeamStats merge_team(const Params& P, Shared& sh, int tr) {
     const int lane = threadIdx.x & 63;
     const int C = P.C;
-    const int K = P.K;
-    const E* target = static_cast<const E*>(P.target);
-    const E* draft = static_cast<const E*>(P.draft);
-    const unsigned long long* part = P.part + (size_t)tr * C * kPartWords;
-    // Merge: M = max of chunk maxima, S = sum of S_c 2^((M_c - M) c).
+    const unsigned ep = P.epoch;
+    unsigned long long* rec = P.rec + (size_t)tr * C * kRecWords;
+    constexpr int Q = kMaxChunks / 64;
+    unsigned long long w[Q][kStatWords];
+    for (unsigned it = 0;; ++it) {
+        bool ok = true;
+        #pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int cc = lane + 64 * q;
+            #pragma unroll
+            for (int f = 0; f < kStatWords; ++f) {
+                w[q][f] = cc < C ? ld64(rec + cc * kRecWords + f) : (unsigned long long)ep;
+            }
+        }
+        #pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            #pragma unroll
+            for (int f = 0; f < kStatWords; ++f) ok = ok && tag_ok(w[q][f], ep);
+        }
+        if (__ballot(!ok) == 0) break;
+        if (it >= kSpinLimit || lds_get(&sh.abort_wait)) {
+            if (lane == 0) give_up(P, sh);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
     float mt = -INFINITY, md = -INFINITY;
-    for (int cc = lane; cc < C; cc += 64) {
-        const unsigned long long w = ld64(const_cast<unsigned long long*>(&part[cc * kPartWords]));
-        mt = fmaxf(mt, __uint_as_float((unsigned)(w >> 32)));
-        md = fmaxf(md, __uint_as_float((unsigned)w));
+    #pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        if (lane + 64 * q < C) {
+            mt = fmaxf(mt, tag_val(w[q][R_MT]));
+            md = fmaxf(md, tag_val(w[q][R_MD]));
+        }
     }
     mt = wave_max(mt);
     md = wave_max(md);
     double st = 0.0, sd = 0.0;
-    for (int cc = lane; cc < C; cc += 64) {
-        unsigned long long* pw = const_cast<unsigned long long*>(&part[cc * kPartWords]);
-        const unsigned long long w = ld64(pw);
-        const double s1 = as_f64(ld64(pw + 1));
-        const double s2 = as_f64(ld64(pw + 2));
-        const float m1 = __uint_as_float((unsigned)(w >> 32));
-        const float m2 = __uint_as_float((unsigned)w);
-        if (s1 > 0.0) st += s1 * exp2(((double)m1 - (double)mt) * P.c64);
-        if (s2 > 0.0) sd += s2 * exp2(((double)m2 - (double)md) * P.c64);
-    }
-    st = wave_sum(st);
-    sd = wave_sum(sd);
-    if (i < k) {
-        if (lane == 0) {
-            const int x = P.tokens[(size_t)b * K + i];
-            const bool valid = x >= 0 && x < P.V;
-            if (!valid) atomicOr(P.status, SV_FLAG_BAD_TOKEN);
-            double px = 0.0, qx = 0.0;
-            if (valid) {
-                const float zt = Elem<E>::one(target + ((size_t)b * (K + 1) + i) * (size_t)P.V + x);
-                const float zd = Elem<E>::one(draft + ((size_t)b * K + i) * (size_t)P.V + x);
-                px = exp2(((double)zt - (double)mt) * P.c64) / st;
-                qx = exp2(((double)zd - (double)md) * P.c64) / sd;
-            }
-            const uint4 rw = philox4x32_10((uint32_t)b, (uint32_t)i, 0u, 0u, P.key0, P.key1);
-            const bool accept = word_to_uniform(rw.x) * qx < px;
-            if (P.out_p) P.out_p[(size_t)b * K + i] = (float)px;
-            if (P.out_q) P.out_q[(size_t)b * K + i] = (float)qx;
-            bool residual = false;
-            if (!accept) {
-                const unsigned old = __hip_atomic_fetch_min(
-                    &P.req_first[b * kReqStride], (unsigned)i, __ATOMIC_RELAXED,
-                    __HIP_MEMORY_SCOPE_AGENT);
-                residual = (unsigned)i < old;          // earliest rejection so far
-            }
-            unsigned* tw = P.team + (size_t)tr * kTeamWords;
-            st64(reinterpret_cast<unsigned long long*>(tw + TW_ST), as_u64(st));
-            st64(reinterpret_cast<unsigned long long*>(tw + TW_SD), as_u64(sd));
-            st32(tw + TW_MT, __float_as_uint(mt));
-            st32(tw + TW_MD, __float_as_uint(md));
-            drain();
-            st32(tw + TW_PHASE, (P.epoch << 2) | PH_READY | (residual ? PH_RESIDUAL : 0u));
-            if (!residual) {
-                st64(&P.result[tr], ((unsigned long long)(accept ? 1u : 0u) << 32) | 0xFFFFFFFFull);
-                team_complete<false>(P, b, k);
-            }
-        }
-        return;
-    }
-    // Bonus position: needed only if nothing was rejected so far.
-    unsigned fr = 0;
-    if (lane == 0) fr = ld32(&P.req_first[b * kReqStride]);
-    fr = __shfl(fr, 0, 64);
-    int go = 0;
-    if (fr == kNoReject && st > 0.0) {
-        const uint4 rw = philox4x32_10((uint32_t)b, (uint32_t)k, 0u, 0u, P.key0, P.key1);
-        const double u = word_to_uniform(rw.y);
-        const double inv = 1.0 / st;
-        auto mass = [&](int cc) -> double {
-            unsigned long long* pw = const_cast<unsigned long long*>(&part[cc * kPartWords]);
-            const double s1 = as_f64(ld64(pw + 1));
-            const float m1 = __uint_as_float((unsigned)(ld64(pw) >> 32));
-            return s1 > 0.0 ? s1 * exp2(((double)m1 - (double)mt) * P.c64) * inv : 0.0;
-        };
-        double total = 0.0;
-        for (int cc = lane; cc < C; cc += 64) total += mass(cc);
-        total = wave_sum(total);
-        int chunk;
-        double base;
-        chunk_crossing(C, u * total, mass, chunk, base);
-        if (chunk >= 0) {
-            go = 1;
-            if (lane == 0) {
-                sh.bonus_b = b;
-                sh.bonus_k = k;
-                sh.bonus_tr = tr;
-                sh.bonus_chunk = chunk;
-                sh.bonus_mt = mt;
-                sh.bonus_ist = (float)inv;
-                sh.bonus_thr = u * total - base;
-            }
+    #pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        if (lane + 64 * q < C) {
+            const float s1 = tag_val(w[q][R_ST]), s2 = tag_val(w[q][R_SD]);
+            if (s1 > 0.0f) st += (double)s1 * exp2(((double)tag_val(w[q][R_MT]) - (double)mt) * P.c64);
+            if (s2 > 0.0f) sd += (double)s2 * exp2(((double)tag_val(w[q][R_MD]) - (double)md) * P.c64);
         }
     }
-    if (lane == 0) {
-        sh.pend_bonus = go;
-        if (!go) {
-            st64(&P.result[tr], (1ull << 32) | 0xFFFFFFFFull);
-            team_complete<false>(P, b, k);
-        }
-    }
+    TeamStats t;
+    t.mt = mt;
+    t.md = md;
+    t.st = wave_sum(st);
+    t.sd = wave_sum(sd);
+    return t;
 }
 
-// Control wave: all chunks of a residual team published their residual mass;
-// scan the residual CDF over chunks and leave the element scan of the chunk
-// holding the threshold to the data waves (pend_resid).
-template <typename E>
-__device__ void residual_locate(const Params& P, Shared& sh, int b, int i, int k, int tr,
-                                double st, float mt, float md, float ist, float isd) {
-    const int lane = threadIdx.x & 63;
-    const int C = P.C;
-    const unsigned long long* part = P.part + (size_t)tr * C * kPartWords;
-    const uint4 rw = philox4x32_10((uint32_t)b, (uint32_t)i, 0u, 0u, P.key0, P.key1);
-    const double u_s = word_to_uniform(rw.y);
-    auto rmass = [&](int cc) -> double {
-        const double v = as_f64(ld64(const_cast<unsigned long long*>(&part[cc * kPartWords + 3])));
-        return v > 0.0 ? v : 0.0;
-    };
-    double total = 0.0;
-    for (int cc = lane; cc < C; cc += 64) total += rmass(cc);
-    total = wave_sum(total);
-    int chunk = -1;
-    double base = 0.0;
-    int residual = 1;
-    if (total > 0.0) chunk_crossing(C, u_s * total, rmass, chunk, base);
-    if (chunk < 0) {
-        // The residual kept no mass (rounding only): draw from p_i.
-        residual = 0;
-        const double inv = 1.0 / st;
-        auto pmass = [&](int cc) -> double {
-            unsigned long long* pw = const_cast<unsigned long long*>(&part[cc * kPartWords]);
-            const double s1 = as_f64(ld64(pw + 1));
-            const float m1 = __uint_as_float((unsigned)(ld64(pw) >> 32));
-            return s1 > 0.0 ? s1 * exp2(((double)m1 - (double)mt) * P.c64) * inv : 0.0;
-        };
-        total = 0.0;
-        for (int cc = lane; cc < C; cc += 64) total += pmass(cc);
-        total = wave_sum(total);
-        chunk_crossing(C, u_s * total, pmass, chunk, base);
+// Control wave: queue a deferred draw (team tr; bonus or rejection).
+__device__ __forceinline__ void add_task(const Params& P, int tr, bool bonus, int& ntasks) {
+    if ((threadIdx.x & 63) == 0 && ntasks < P.task_cap) {
+        st32(reinterpret_cast<unsigned*>(P.tasks) + (size_t)blockIdx.x * P.task_cap + ntasks,
+             (unsigned)(2 * tr + (bonus ? 1 : 0)));
     }
-    if (lane == 0) {
-        sh.pend_resid = 1;
-        sh.resid_b = b;
-        sh.resid_i = i;
-        sh.resid_k = k;
-        sh.resid_tr = tr;
-        sh.resid_mt = mt;
-        sh.resid_md = md;
-        sh.resid_ist = ist;
-        sh.resid_isd = isd;
-        sh.scan_chunk = chunk;
-        sh.scan_residual = residual;
-        sh.scan_thr = u_s * total - base;
-    }
+    ++ntasks;
 }
 
 // ---------------------------------------------------------- main kernel --
@@ -821,196 +761,178 @@ __device__ __forceinline__ void issue_loads(const Params& P, const Unit& d, int 
     }
 }
 
-// Block-wide (max, lowest index) merge; every thread gets the result.
-__device__ __forceinline__ void block_argmax(Shared& sh, float& bv, int& bi) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (better_arg(ov, oi, bv, bi)) {
-            bv = ov;
-            bi = oi;
-        }
-    }
-    if (lane == 0) {
-        sh.red_f[wave] = bv;
-        sh.red_i[wave] = bi;
-    }
-    __syncthreads();
-    #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        if (better_arg(sh.red_f[w], sh.red_i[w], bv, bi)) {
-            bv = sh.red_f[w];
-            bi = sh.red_i[w];
-        }
-    }
-}
-
-// Deferred draws left by the previous round (whole workgroup): the element
-// scan of the one chunk that holds the bonus or the residual threshold. The
-// control wave's lane 0 stores the result and completes the team.
-template <typename E, bool kVec, bool kCtrl>
-__device__ __forceinline__ void pending_draws(const Params& P, Shared& sh) {
-    const int K = P.K;
-    if (sh.pend_bonus) {
-        const E* target = static_cast<const E*>(P.target);
-        const int chunk = sh.bonus_chunk;
-        const int e0 = chunk * P.CE;
-        const int n = min(P.CE, P.V - e0);
-        const E* rt = target + ((size_t)sh.bonus_b * (K + 1) + sh.bonus_k) * (size_t)P.V + e0;
-        const int o = chunk_scan<E, kVec>(sh, rt, nullptr, n, sh.bonus_mt, sh.bonus_ist, 0.0f,
-                                          0.0f, P.c32, sh.bonus_thr);
-        if (kCtrl && threadIdx.x == 0) {
-            const int y = o < 0 ? 0 : e0 + o;
-            st64(&P.result[sh.bonus_tr], (1ull << 32) | (unsigned)y);
-            team_complete<false>(P, sh.bonus_b, sh.bonus_k);
-            sh.pend_bonus = 0;
-        }
-        __syncthreads();
-    }
-    if (sh.pend_resid) {
-        const E* target = static_cast<const E*>(P.target);
-        const E* draft = static_cast<const E*>(P.draft);
-        const int chunk = sh.scan_chunk;
-        int y = 0;
-        if (chunk >= 0) {
-            const int e0 = chunk * P.CE;
-            const int n = min(P.CE, P.V - e0);
-            const E* rt = target + ((size_t)sh.resid_b * (K + 1) + sh.resid_i) * (size_t)P.V + e0;
-            const E* rd = sh.scan_residual
-                              ? draft + ((size_t)sh.resid_b * K + sh.resid_i) * (size_t)P.V + e0
-                              : nullptr;
-            const int o = chunk_scan<E, kVec>(sh, rt, rd, n, sh.resid_mt, sh.resid_ist,
-                                              sh.resid_md, sh.resid_isd, P.c32, sh.scan_thr);
-            y = o < 0 ? 0 : e0 + o;
-        }
-        if (kCtrl && threadIdx.x == 0) {
-            st64(&P.result[sh.resid_tr], (unsigned)y);
-            team_complete<false>(P, sh.resid_b, sh.resid_k);
-            sh.pend_resid = 0;
-        }
-        __syncthreads();
-    }
-}
-
-// Control wave: the loop of a workgroup's control wave. It mirrors the data
-// waves' loop barrier for barrier (every branch below depends only on values
-// the whole workgroup shares), contributes neutral values to the block
-// reductions, and does all synchronisation with other workgroups.
-template <typename E, bool kGreedy, bool kVec>
-__device__ __forceinline__ void control_loop(const Params& P, Shared& sh, const int* off) {
+// Control wave: collect the data waves' statistics of the unit of round r,
+// merge them and publish the unit's record. Greedy: count the arrival and
+// lead the team if last. Sampled: queue the bonus draw from the chunk-0
+// member of a bonus position.
+template <typename E, bool kGreedy>
+__device__ __forceinline__ void control_unit(const Params& P, Shared& sh, const Unit& cur, int r,
+                                             int& ntasks) {
     const int lane = threadIdx.x & 63;
     const int C = P.C;
-    const int U = off[P.B];
-    const int G = gridDim.x;
-    const unsigned ep = P.epoch & 0x3FFFFFFFu;
-    Unit cur = decode_unit(P, off, blockIdx.x, U, kGreedy);
-    Unit prev;
-    prev.u = -1;
-    for (;;) {
-        // Read the parked unit's team phase early; the draws below hide the latency.
-        unsigned ph = 0;
-        if (lane == 0 && prev.u >= 0) ph = ld32(P.team + (size_t)prev.tr * kTeamWords + TW_PHASE);
-
-        pending_draws<E, kVec, true>(P, sh);
-
-        if (prev.u >= 0) {
-            // Wait for the parked unit's team decision.
-            if (lane == 0) {
-                unsigned* tw = P.team + (size_t)prev.tr * kTeamWords;
-                for (unsigned it = 0; (ph >> 2) != ep && it < kSpinLimit; ++it) {
-                    __builtin_amdgcn_s_sleep(2);
-                    ph = ld32(tw + TW_PHASE);
-                }
-                if ((ph >> 2) != ep) {
-                    atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);
-                    ph = PH_READY;
-                }
-                sh.phase = ph;
-                if (ph & PH_RESIDUAL) {
-                    sh.nst = as_f64(ld64(reinterpret_cast<unsigned long long*>(tw + TW_ST)));
-                    sh.nsd = as_f64(ld64(reinterpret_cast<unsigned long long*>(tw + TW_SD)));
-                    sh.nmt = __uint_as_float(ld32(tw + TW_MT));
-                    sh.nmd = __uint_as_float(ld32(tw + TW_MD));
-                }
+    const int slot = r & 1;
+    if (lane < kDataWaves) lds_wait(P, sh, &sh.st_tag[slot][lane], r + 1);
+    unsigned long long* rec = P.rec + ((size_t)cur.tr * C + cur.c) * kRecWords;
+    if (kGreedy) {
+        float bv = -INFINITY;
+        int bi = INT_MAX;
+        if (lane < kDataWaves) {
+            bv = sh.st_mt[slot][lane];
+            bi = sh.st_idx[slot][lane];
+        }
+        order();
+        if (lane == 0) lds_put(&sh.st_done[slot], r + 1);
+        #pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float ov = __shfl_xor(bv, o, 64);
+            const int oi = __shfl_xor(bi, o, 64);
+            if (better_arg(ov, oi, bv, bi)) {
+                bv = ov;
+                bi = oi;
             }
-            __syncthreads();
-            if (sh.phase & PH_RESIDUAL) {
-                // The request's earliest rejection: publish the parked chunk's
-                // residual mass; the last chunk to do so locates the draw.
-                const double2 R = block_sum2(sh, 0.0, 0.0);
-                int last = 0;
-                if (lane == 0) {
-                    st64(P.part + ((size_t)prev.tr * C + prev.c) * kPartWords + 3, as_u64(R.x));
-                    drain();
-                    const unsigned old = add32(&P.team[(size_t)prev.tr * kTeamWords + TW_ARRIVE2], 1u);
-                    last = old == (unsigned)C - 1;
-                }
-                last = __shfl(last, 0, 64);
-                if (last) {
-                    const float ist = (float)(1.0 / sh.nst), isd = (float)(1.0 / sh.nsd);
-                    residual_locate<E>(P, sh, prev.b, prev.i, prev.k, prev.tr, sh.nst, sh.nmt,
-                                       sh.nmd, ist, isd);
-                }
-            }
-            prev.u = -1;
         }
-
-        if (cur.u < 0) {
-            __syncthreads();
-            if (sh.pend_bonus || sh.pend_resid) continue;
-            break;
-        }
-
-        // The current unit's chunk statistics (the data waves hold the data).
-        unsigned long long w0;
-        double s_t = 0.0, s_d = 0.0;
-        if (kGreedy) {
-            float bv = -INFINITY;
-            int bi = INT_MAX;
-            block_argmax(sh, bv, bi);
-            w0 = ((unsigned long long)__float_as_uint(bv) << 32) | (unsigned)bi;
-        } else {
-            const float2 M = block_max2(sh, -INFINITY, -INFINITY);
-            const double2 S = block_sum2(sh, 0.0, 0.0);
-            s_t = S.x;
-            s_d = S.y;
-            w0 = ((unsigned long long)__float_as_uint(M.x) << 32) | __float_as_uint(M.y);
-        }
-
-        // Publish, arrive; the last arrival of a team leads it.
         int lead = 0;
         if (lane == 0) {
-            unsigned long long* pw = P.part + ((size_t)cur.tr * C + cur.c) * kPartWords;
-            st64(pw, w0);
-            if (!kGreedy) {
-                st64(pw + 1, as_u64(s_t));
-                st64(pw + 2, as_u64(s_d));
-            }
+            st64(rec, ((unsigned long long)__float_as_uint(bv) << 32) | (unsigned)bi);
             drain();
             const unsigned old = add32(&P.team[(size_t)cur.tr * kTeamWords + TW_ARRIVE], 1u);
             lead = old == (unsigned)C - 1;
         }
         lead = __shfl(lead, 0, 64);
-        if (lead) {
-            if (kGreedy) {
-                leader_greedy(P, cur.b, cur.i, cur.k, cur.tr);
-            } else {
-                leader_sampled<E>(P, sh, cur.b, cur.i, cur.k, cur.tr);
-            }
+        if (lead) leader_greedy(P, cur.b, cur.i, cur.k, cur.tr);
+    } else {
+        float mt = -INFINITY, md = -INFINITY;
+        double a = 0.0, d = 0.0;
+        if (lane < kDataWaves) {
+            mt = sh.st_mt[slot][lane];
+            md = sh.st_md[slot][lane];
+            a = sh.st_st[slot][lane];
+            d = sh.st_sd[slot][lane];
         }
-        __syncthreads();
-        if (cur.has_d) prev = cur;
-        cur = decode_unit(P, off, cur.u + G, U, kGreedy);
+        order();
+        if (lane == 0) lds_put(&sh.st_done[slot], r + 1);
+        const float Mt = wave_max(mt), Md = wave_max(md);
+        // Rescale each wave's sum from its own maximum to the chunk maximum.
+        if (a > 0.0) a *= (double)fast_exp2((mt - Mt) * P.c32);
+        if (d > 0.0) d *= (double)fast_exp2((md - Md) * P.c32);
+        const double St = wave_sum(a), Sd = wave_sum(d);
+        if (lane == 0) {
+            const unsigned ep = P.epoch;
+            st64(rec + R_MT, tagged(Mt, ep));
+            st64(rec + R_MD, tagged(Md, ep));
+            st64(rec + R_ST, tagged((float)St, ep));
+            st64(rec + R_SD, tagged((float)Sd, ep));
+        }
+        if (cur.i == cur.k && cur.c == 0) add_task(P, cur.tr, true, ntasks);
     }
 }
 
-// Data waves: stream units through registers, reduce them, park them in LDS.
+// Control wave, sampled: the parked unit of round r - 1 (drafted position i
+// of request b, drafted token x loaded a round earlier). Wait for its team's
+// records, take the team's decision, post it to the data waves; on a
+// rejection that may be the request's first, collect and publish the chunk's
+// residual mass. The chunk-0 member also writes p(x), q(x) and the decision
+// word, and completes the team or queues its draw.
+template <typename E>
+__device__ __forceinline__ void control_parked(const Params& P, Shared& sh, const Unit& prev, int x,
+                                               int r, int& ntasks) {
+    const int lane = threadIdx.x & 63;
+    const int K = P.K;
+    const int slot = r & 1;
+    const unsigned ep = P.epoch;
+    const E* target = static_cast<const E*>(P.target);
+    const E* draft = static_cast<const E*>(P.draft);
+    // Issued before the records are awaited: the drafted token's logits and
+    // the decisions of the request's earlier positions known so far.
+    const bool valid = x >= 0 && x < P.V;
+    float zt = 0.0f, zd = 0.0f;
+    if (valid) {
+        zt = Elem<E>::one(target + ((size_t)prev.b * (K + 1) + prev.i) * (size_t)P.V + x);
+        zd = Elem<E>::one(draft + ((size_t)prev.b * K + prev.i) * (size_t)P.V + x);
+    }
+    unsigned long long dprev = 0;
+    if (lane < prev.i) dprev = ld64(dec_word(P, prev.b * (K + 1) + lane));
+    const TeamStats ts = merge_team(P, sh, prev.tr);
+    double px = 0.0, qx = 0.0;
+    if (valid) {
+        px = exp2(((double)zt - (double)ts.mt) * P.c64) / ts.st;
+        qx = exp2(((double)zd - (double)ts.md) * P.c64) / ts.sd;
+    }
+    const uint4 rw = philox4x32_10((uint32_t)prev.b, (uint32_t)prev.i, 0u, 0u, P.key0, P.key1);
+    const bool accept = word_to_uniform(rw.x) * qx < px;
+    // An earlier position already known to be rejected: no draw will be
+    // needed for this one, whatever its decision.
+    const bool later = __ballot(lane < prev.i && (unsigned)(dprev >> 32) == ep &&
+                                (dprev & 1ull) == 0) != 0;
+    const bool residual = !accept && !later;
+    const float ist = (float)(1.0 / ts.st), isd = (float)(1.0 / ts.sd);
+    if (lane == 0) {
+        sh.ph_val[slot] = residual ? PH_REJECT : PH_ACCEPT;
+        sh.ph_mt[slot] = ts.mt;
+        sh.ph_md[slot] = ts.md;
+        sh.ph_ist[slot] = ist;
+        sh.ph_isd[slot] = isd;
+        order();
+        lds_put(&sh.ph_tag[slot], r);
+    }
+    const bool books = prev.c == 0;
+    if (books && lane == 0) {
+        if (!valid) atomicOr(P.status, SV_FLAG_BAD_TOKEN);
+        if (P.out_p) P.out_p[(size_t)prev.b * K + prev.i] = (float)px;
+        if (P.out_q) P.out_q[(size_t)prev.b * K + prev.i] = (float)qx;
+        st64(dec_word(P, prev.tr), ((unsigned long long)ep << 32) | (accept ? 1u : 0u));
+        if (!residual) team_complete<false>(P, prev.b, prev.k);
+    }
+    if (!residual) return;
+    if (books) add_task(P, prev.tr, false, ntasks);
+    // Residual mass of the parked chunk: one partial per data wave.
+    double v = 0.0;
+    if (lane < kDataWaves) {
+        lds_wait(P, sh, &sh.rs_tag[lane], r);
+        v = sh.rs_val[lane];
+    }
+    v = wave_sum(v);
+    if (lane == 0) {
+        st64(P.rec + ((size_t)prev.tr * P.C + prev.c) * kRecWords + R_RES,
+             tagged((float)v, ep));
+    }
+}
+
+// The control wave's loop. Round r: the parked unit of round r - 1 (its
+// team's decision, started as soon as that unit is published), then the unit
+// of round r (publish).
+template <typename E, bool kGreedy, bool kVec>
+__device__ __forceinline__ int control_loop(const Params& P, Shared& sh, const int* off) {
+    const int U = off[P.B];
+    const int G = gridDim.x;
+    Unit cur = decode_unit(P, off, blockIdx.x, U, kGreedy);
+    Unit prev;
+    prev.u = -1;
+    int x_prev = 0;
+    int ntasks = 0;
+    for (int r = 0; cur.u >= 0 || prev.u >= 0; ++r) {
+        if (!kGreedy && prev.u >= 0) control_parked<E>(P, sh, prev, x_prev, r, ntasks);
+        prev.u = -1;
+        if (cur.u >= 0) {
+            control_unit<E, kGreedy>(P, sh, cur, r, ntasks);
+            if (cur.has_d) {
+                prev = cur;
+                x_prev = P.tokens[(size_t)cur.b * P.K + cur.i];   // used next round
+            }
+            cur = decode_unit(P, off, cur.u + G, U, kGreedy);
+        }
+    }
+    return ntasks;
+}
+
+// The data waves' loop: stream units through registers, post per-wave
+// statistics, park drafted units in LDS until their team has decided.
 template <typename E, bool kGreedy, bool kVec>
 __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int* off,
                                           uint4* stash) {
     constexpr int W = Elem<E>::W;
+    const int lane = threadIdx.x & 63;
+    const int dw = (threadIdx.x >> 6) - 1;         // data wave index
     const int dt = threadIdx.x - 64;               // data thread index
     const int U = off[P.B];
     const int G = gridDim.x;
@@ -1020,47 +942,47 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
     Unit cur = decode_unit(P, off, blockIdx.x, U, kGreedy);
     if (cur.u >= 0) issue_loads<E, kVec>(P, cur, dt, gt, gd);
     bool have_prev = false;
+    int r = 0;
 
-    for (;;) {
-        pending_draws<E, kVec, false>(P, sh);
-
-        if (have_prev) {
-            __syncthreads();                       // the control wave has the parked team's phase
-            if (sh.phase & PH_RESIDUAL) {
-                const float mt = sh.nmt, md = sh.nmd;
-                const float ist = (float)(1.0 / sh.nst), isd = (float)(1.0 / sh.nsd);
-                float lr = 0.0f;
-                #pragma unroll 1
-                for (int j = 0; j < kG; ++j) {
-                    // Each lane reads back only the groups it parked itself.
-                    const uint4 a = stash[(0 * kG + j) * kDataThreads + dt];
-                    const uint4 d = stash[(1 * kG + j) * kDataThreads + dt];
-                    float r[W];
-                    #pragma unroll
-                    for (int kk = 0; kk < W; ++kk) {
-                        const float pv = fast_exp2((Elem<E>::at(a, kk) - mt) * cs) * ist;
-                        const float qv = fast_exp2((Elem<E>::at(d, kk) - md) * cs) * isd;
-                        r[kk] = fmaxf(0.0f, pv - qv);
-                    }
-                    #pragma unroll
-                    for (int h = W / 2; h > 0; h >>= 1) {
-                        #pragma unroll
-                        for (int kk = 0; kk < h; ++kk) r[kk] += r[kk + h];
-                    }
-                    lr += r[0];
-                }
-                (void)block_sum2(sh, (double)lr, 0.0);
+    // The parked unit of round rr - 1: wait for its team's decision; on a
+    // rejection, post this wave's part of the chunk's residual mass.
+    auto finish_parked = [&](int rr) {
+        const int slot = rr & 1;
+        lds_wait(P, sh, &sh.ph_tag[slot], rr);
+        if (sh.ph_val[slot] != PH_REJECT) return;
+        const float mt = sh.ph_mt[slot], md = sh.ph_md[slot];
+        const float ist = sh.ph_ist[slot], isd = sh.ph_isd[slot];
+        float lr = 0.0f;
+        #pragma unroll 1
+        for (int j = 0; j < kG; ++j) {
+            // Each lane reads back only the groups it parked itself.
+            const uint4 a = stash[(0 * kG + j) * kDataThreads + dt];
+            const uint4 d = stash[(1 * kG + j) * kDataThreads + dt];
+            float m8[W];
+            #pragma unroll
+            for (int kk = 0; kk < W; ++kk) {
+                const float pv = fast_exp2((Elem<E>::at(a, kk) - mt) * cs) * ist;
+                const float qv = fast_exp2((Elem<E>::at(d, kk) - md) * cs) * isd;
+                m8[kk] = fmaxf(0.0f, pv - qv);
             }
-            have_prev = false;
+            #pragma unroll
+            for (int h = W / 2; h > 0; h >>= 1) {
+                #pragma unroll
+                for (int kk = 0; kk < h; ++kk) m8[kk] += m8[kk + h];
+            }
+            lr += m8[0];
         }
-
-        if (cur.u < 0) {
-            __syncthreads();
-            if (sh.pend_bonus || sh.pend_resid) continue;
-            break;
+        const double v = wave_sum((double)lr);
+        if (lane == 0) {
+            sh.rs_val[dw] = v;
+            order();
+            lds_put(&sh.rs_tag[dw], rr);
         }
+    };
 
-        // Reduce the current unit to its chunk statistics.
+    for (; cur.u >= 0; ++r) {
+        const int slot = r & 1;
+        // Per-wave statistics of the unit of round r.
         if (kGreedy) {
             float bv = -INFINITY;
             int bi = INT_MAX;
@@ -1075,7 +997,22 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
                     }
                 }
             }
-            block_argmax(sh, bv, bi);
+            #pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const float ov = __shfl_xor(bv, o, 64);
+                const int oi = __shfl_xor(bi, o, 64);
+                if (better_arg(ov, oi, bv, bi)) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+            if (lane == 0) {
+                if (r >= 2) lds_wait(P, sh, &sh.st_done[slot], r - 1);
+                sh.st_mt[slot][dw] = bv;
+                sh.st_idx[slot][dw] = bi;
+                order();
+                lds_put(&sh.st_tag[slot][dw], r + 1);
+            }
         } else {
             float mt = -INFINITY, md = -INFINITY;
             #pragma unroll
@@ -1087,20 +1024,21 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
                 }
             }
             // Opaque raw registers: the exp pass converts them again rather
-            // than keeping every converted float alive across the barrier.
+            // than keeping every converted float alive across the reduction.
             #pragma unroll
             for (int j = 0; j < kG; ++j) {
                 asm volatile("" : "+v"(gt[j].x), "+v"(gt[j].y), "+v"(gt[j].z), "+v"(gt[j].w));
                 asm volatile("" : "+v"(gd[j].x), "+v"(gd[j].y), "+v"(gd[j].z), "+v"(gd[j].w));
             }
-            const float2 M = block_max2(sh, mt, md);
+            mt = wave_max(mt);
+            md = wave_max(md);
             float lt = 0.0f, ld = 0.0f;
-            if (M.x != -INFINITY) {
+            if (mt != -INFINITY) {
                 #pragma unroll
                 for (int j = 0; j < kG; ++j) {
                     float e[W];
                     #pragma unroll
-                    for (int kk = 0; kk < W; ++kk) e[kk] = fast_exp2((Elem<E>::at(gt[j], kk) - M.x) * cs);
+                    for (int kk = 0; kk < W; ++kk) e[kk] = fast_exp2((Elem<E>::at(gt[j], kk) - mt) * cs);
                     #pragma unroll
                     for (int h = W / 2; h > 0; h >>= 1) {
                         #pragma unroll
@@ -1109,12 +1047,12 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
                     lt += e[0];
                 }
             }
-            if (cur.has_d && M.y != -INFINITY) {
+            if (cur.has_d && md != -INFINITY) {
                 #pragma unroll
                 for (int j = 0; j < kG; ++j) {
                     float e[W];
                     #pragma unroll
-                    for (int kk = 0; kk < W; ++kk) e[kk] = fast_exp2((Elem<E>::at(gd[j], kk) - M.y) * cs);
+                    for (int kk = 0; kk < W; ++kk) e[kk] = fast_exp2((Elem<E>::at(gd[j], kk) - md) * cs);
                     #pragma unroll
                     for (int h = W / 2; h > 0; h >>= 1) {
                         #pragma unroll
@@ -1123,8 +1061,21 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
                     ld += e[0];
                 }
             }
-            (void)block_sum2(sh, (double)lt, (double)ld);
+            const double st = wave_sum((double)lt);
+            const double sd = wave_sum((double)ld);
+            if (lane == 0) {
+                if (r >= 2) lds_wait(P, sh, &sh.st_done[slot], r - 1);
+                sh.st_mt[slot][dw] = mt;
+                sh.st_md[slot][dw] = md;
+                sh.st_st[slot][dw] = st;
+                sh.st_sd[slot][dw] = sd;
+                order();
+                lds_put(&sh.st_tag[slot][dw], r + 1);
+            }
         }
+
+        // The stash is free once the previous parked unit is done with.
+        if (have_prev) finish_parked(r);
 
         // Park the unit, start streaming the next one.
         const Unit nxt = decode_unit(P, off, cur.u + G, U, kGreedy);
@@ -1136,14 +1087,150 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
             }
         }
         if (nxt.u >= 0) issue_loads<E, kVec>(P, nxt, dt, gt, gd);
-        __syncthreads();                           // the control wave has published and led
-        if (cur.has_d) have_prev = true;
+        have_prev = cur.has_d;
         cur = nxt;
+    }
+    if (have_prev) finish_parked(r);
+}
+
+// Control wave: prepare deferred draw number t of this workgroup (team
+// b, i): wait until the earlier positions of the request are decided; draw
+// only if none of them rejected (i is the request's first rejection, or the
+// bonus position with no rejection). Locate the chunk that holds the
+// threshold and leave its element scan to the whole workgroup.
+__device__ void task_prepare(const Params& P, Shared& sh, int task) {
+    const int lane = threadIdx.x & 63;
+    const int K = P.K, C = P.C;
+    const unsigned ep = P.epoch;
+    const int tr = task >> 1;
+    const bool bonus = task & 1;
+    const int b = tr / (K + 1), i = tr - b * (K + 1);
+    // Earlier positions (lane t polls position t): done once every position
+    // before the first known rejection is decided, or all are decided.
+    bool first = true;
+    for (unsigned it = 0;; ++it) {
+        unsigned long long d = 0;
+        if (lane < i) d = ld64(dec_word(P, b * (K + 1) + lane));
+        const bool known = lane >= i || (unsigned)(d >> 32) == ep;
+        const unsigned long long rej = __ballot(lane < i && known && (d & 1ull) == 0);
+        const unsigned long long unknown = __ballot(!known);
+        if (rej != 0) {
+            const unsigned long long below = (rej & (~rej + 1)) - 1;   // lanes below the first rejection
+            if ((unknown & below) == 0) {
+                first = false;
+                break;
+            }
+        } else if (unknown == 0) {
+            break;
+        }
+        if (it >= kSpinLimit || lds_get(&sh.abort_wait)) {
+            if (lane == 0) give_up(P, sh);
+            first = false;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+    int draw = 0, chunk = -1, mode = 0;
+    double thr = 0.0;
+    TeamStats ts;
+    ts.mt = ts.md = 0.0f;
+    ts.st = ts.sd = 1.0;
+    if (first) {
+        ts = merge_team(P, sh, tr);
+        unsigned long long* rec = P.rec + (size_t)tr * C * kRecWords;
+        const uint4 rw = philox4x32_10((uint32_t)b, (uint32_t)i, 0u, 0u, P.key0, P.key1);
+        const double u = word_to_uniform(rw.y);
+        double total = 0.0, base = 0.0;
+        if (!bonus) {
+            // Residual masses: all C members publish theirs.
+            for (unsigned it = 0;; ++it) {
+                bool ok = true;
+                for (int cc = lane; cc < C; cc += 64) ok = ok && tag_ok(ld64(rec + cc * kRecWords + R_RES), ep);
+                if (__ballot(!ok) == 0) break;
+                if (it >= kSpinLimit || lds_get(&sh.abort_wait)) {
+                    if (lane == 0) give_up(P, sh);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            auto rmass = [&](int cc) -> double {
+                const float v = tag_val(ld64(rec + cc * kRecWords + R_RES));
+                return v > 0.0f ? (double)v : 0.0;
+            };
+            for (int cc = lane; cc < C; cc += 64) total += rmass(cc);
+            total = wave_sum(total);
+            if (total > 0.0) {
+                chunk_crossing(C, u * total, rmass, chunk, base);
+                mode = 1;
+            }
+        }
+        if (chunk < 0 && ts.st > 0.0) {
+            // Bonus draw, or a residual without mass (rounding only): from p_i.
+            mode = 0;
+            const double inv = 1.0 / ts.st;
+            auto pmass = [&](int cc) -> double {
+                const float s1 = tag_val(ld64(rec + cc * kRecWords + R_ST));
+                const float m1 = tag_val(ld64(rec + cc * kRecWords + R_MT));
+                return s1 > 0.0f ? (double)s1 * exp2(((double)m1 - (double)ts.mt) * P.c64) * inv : 0.0;
+            };
+            total = 0.0;
+            for (int cc = lane; cc < C; cc += 64) total += pmass(cc);
+            total = wave_sum(total);
+            chunk_crossing(C, u * total, pmass, chunk, base);
+        }
+        draw = 1;
+        thr = u * total - base;
+    }
+    if (lane == 0) {
+        sh.tk_draw = draw;
+        sh.tk_chunk = chunk;
+        sh.tk_mode = mode;
+        sh.tk_thr = thr;
+        sh.tk_mt = ts.mt;
+        sh.tk_md = ts.md;
+        sh.tk_ist = (float)(1.0 / ts.st);
+        sh.tk_isd = (float)(1.0 / ts.sd);
+    }
+}
+
+// Deferred draws of this workgroup (whole workgroup, under barriers).
+template <typename E, bool kVec>
+__device__ __forceinline__ void run_tasks(const Params& P, Shared& sh) {
+    const int K = P.K;
+    const int nt = min(sh.ntasks, P.task_cap);
+    const E* target = static_cast<const E*>(P.target);
+    const E* draft = static_cast<const E*>(P.draft);
+    unsigned* list = reinterpret_cast<unsigned*>(P.tasks) + (size_t)blockIdx.x * P.task_cap;
+    for (int t = 0; t < nt; ++t) {
+        const int task = (int)ld32(list + t);
+        if (threadIdx.x < 64) task_prepare(P, sh, task);
+        __syncthreads();
+        const int tr = task >> 1;
+        const int b = tr / (K + 1), i = tr - b * (K + 1);
+        int y = 0;
+        if (sh.tk_draw && sh.tk_chunk >= 0) {
+            const int e0 = sh.tk_chunk * P.CE;
+            const int n = min(P.CE, P.V - e0);
+            const E* rt = target + ((size_t)b * (K + 1) + i) * (size_t)P.V + e0;
+            const E* rd = sh.tk_mode == 1 ? draft + ((size_t)b * K + i) * (size_t)P.V + e0 : nullptr;
+            const int o = chunk_scan<E, kVec>(sh, rt, rd, n, sh.tk_mt, sh.tk_ist, sh.tk_md,
+                                              sh.tk_isd, P.c32, sh.tk_thr);
+            y = o < 0 ? 0 : e0 + o;
+        }
+        if (threadIdx.x == 0) {
+            // The request's budget, clamped as in the prologue.
+            int k = P.budgets[b];
+            k = k < 0 ? 0 : (k > K ? K : k);
+            if (sh.tk_draw) st32(&P.result[tr], (unsigned)y);
+            team_complete<false>(P, b, k);
+        }
+        __syncthreads();
     }
 }
 
 template <typename E, bool kGreedy, bool kVec>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void verify_kernel(Params P) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void verify_kernel(Params P) {
     extern __shared__ __align__(16) unsigned char dyn_smem[];
     __shared__ Shared sh;
     // Dynamic LDS: the parked unit (sampled mode), then request unit offsets.
@@ -1153,7 +1240,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int B = P.B, K = P.K, C = P.C;
 
-    // Prologue: every workgroup scans the budgets into per-request unit offsets.
+    // Prologue: every workgroup scans the budgets into per-request unit
+    // offsets, and clears the mailbox tags.
     {
         const int per = (B + kThreads - 1) / kThreads;
         const int b0 = min(tid * per, B), b1 = min(b0 + per, B);
@@ -1175,6 +1263,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             if (lane >= o) incl += v;
         }
         if (lane == 63) sh.red_i[wave] = incl;
+        if (tid < 2 * kDataWaves) (&sh.st_tag[0][0])[tid] = 0;
+        if (tid < kDataWaves) sh.rs_tag[tid] = -1;
+        if (tid < 2) {
+            sh.ph_tag[tid] = -1;
+            sh.st_done[tid] = 0;
+        }
+        if (tid == 0) sh.abort_wait = 0;
         __syncthreads();
         int run = incl - local;
         for (int w = 0; w < wave; ++w) run += sh.red_i[w];
@@ -1185,20 +1280,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             run += (k + 1) * C;
         }
         if (tid == kThreads - 1) off[B] = run;
-        if (tid == 0) {
-            sh.pend_bonus = 0;
-            sh.pend_resid = 0;
-        }
         __syncthreads();
     }
 
-    // Wave specialisation: the branch is uniform per wave, and the two loops
-    // execute the same sequence of barriers.
+    // Wave specialisation (the branch is uniform per wave). No barrier
+    // until both loops are done.
     if (__builtin_amdgcn_readfirstlane(wave) == 0) {
-        control_loop<E, kGreedy, kVec>(P, sh, off);
+        const int nt = control_loop<E, kGreedy, kVec>(P, sh, off);
+        if (lane == 0) sh.ntasks = nt;
+        drain();                                   // task list entries are written
     } else {
         data_loop<E, kGreedy, kVec>(P, sh, off, stash);
     }
+    __syncthreads();
+    if (!kGreedy) run_tasks<E, kVec>(P, sh);
 }
 
 // Philox blocks as the verifier draws them, for checking the generator.
@@ -1240,12 +1335,13 @@ struct spec_verify_ctx {
     int C, CE;
     int cus;
     void* ws;
-    unsigned long long* part;
+    unsigned long long* rec;
     unsigned* team;
-    unsigned long long* result;
+    unsigned* result;
     unsigned* req_count;
-    unsigned* req_first;
     unsigned* status;
+    int* tasks;
+    size_t task_words;             // entries of the task lists' region
     unsigned calls;                // calls made so far (phase-word epochs)
     // occupancy cache: dynamic LDS bytes -> resident workgroups per CU, per kernel
     size_t occ_smem[8];
@@ -1277,6 +1373,12 @@ int launch(spec_verify_ctx* ctx, Params& p, hipStream_t stream) {
     const int occ = occupancy_of<E, G, Vv>(ctx, slot, smem);
     const long long grid = (long long)ctx->cus * occ;
     if (grid < (long long)p.C) return SV_ERR_ARG;   // a team would not fit
+    // Task lists: at most two deferred draws per round of a workgroup.
+    const long long units = (long long)p.B * (p.K + 1) * p.C;
+    const long long cap = 2 * ((units + grid - 1) / grid) + 2;
+    if (cap > INT_MAX || (size_t)(grid * cap) > ctx->task_words) return SV_ERR_ARG;
+    p.tasks = ctx->tasks;
+    p.task_cap = (int)cap;
     hipLaunchKernelGGL((verify_kernel<E, G, Vv>), dim3((unsigned)grid), dim3(kThreads), smem, stream,
                        p);
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
@@ -1346,6 +1448,7 @@ int spec_verify_init(spec_verify_ctx** out, int device, int max_batch, int max_k
         max_k > SV_MAX_K || vocab < 1 || vocab > SV_MAX_VOCAB) {
         return SV_ERR_ARG;
     }
+    if (chunks_for(vocab, dtype) > kMaxChunks) return SV_ERR_ARG;   // not reachable for legal V
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || device >= ndev) return SV_ERR_HIP;
     int prev = -1;
@@ -1368,11 +1471,15 @@ int spec_verify_init(spec_verify_ctx** out, int device, int max_batch, int max_k
     }
     auto round256 = [](size_t x) { return (x + 255) / 256 * 256; };
     const size_t teams = (size_t)max_batch * (max_k + 1);
-    const size_t part_bytes = round256(teams * c->C * kPartWords * 8);
+    const size_t rec_bytes = round256(teams * c->C * kRecWords * 8);
     const size_t team_bytes = round256(teams * kTeamWords * 4);
-    const size_t result_bytes = round256(teams * 8);
+    const size_t result_bytes = round256(teams * 4);
     const size_t req_bytes = round256((size_t)max_batch * kReqStride * 4);
-    const size_t total = part_bytes + team_bytes + result_bytes + 2 * req_bytes + 256;
+    // Task lists: 2 entries per unit plus 4 per workgroup bound every launch
+    // (at most 4 resident workgroups per CU of 8 waves; 16 allowed for).
+    c->task_words = 2 * teams * (size_t)c->C + 4 * (size_t)c->cus * 16;
+    const size_t task_bytes = round256(c->task_words * 4);
+    const size_t total = rec_bytes + team_bytes + result_bytes + req_bytes + task_bytes + 256;
     if (rc == SV_OK && hipMalloc(&c->ws, total) != hipSuccess) {
         c->ws = nullptr;
         rc = SV_ERR_NOMEM;
@@ -1380,20 +1487,18 @@ int spec_verify_init(spec_verify_ctx** out, int device, int max_batch, int max_k
     if (rc == SV_OK) {
         unsigned char* w = static_cast<unsigned char*>(c->ws);
         size_t o = 0;
-        c->part = reinterpret_cast<unsigned long long*>(w + o);
-        o += part_bytes;
+        c->rec = reinterpret_cast<unsigned long long*>(w + o);
+        o += rec_bytes;
         c->team = reinterpret_cast<unsigned*>(w + o);
         o += team_bytes;
-        c->result = reinterpret_cast<unsigned long long*>(w + o);
+        c->result = reinterpret_cast<unsigned*>(w + o);
         o += result_bytes;
         c->req_count = reinterpret_cast<unsigned*>(w + o);
         o += req_bytes;
-        c->req_first = reinterpret_cast<unsigned*>(w + o);
-        o += req_bytes;
+        c->tasks = reinterpret_cast<int*>(w + o);
+        o += task_bytes;
         c->status = reinterpret_cast<unsigned*>(w + o);
-        if (hipMemset(c->ws, 0, total) != hipSuccess ||
-            hipMemset(c->req_first, 0x7F, req_bytes) != hipSuccess ||
-            hipDeviceSynchronize() != hipSuccess) {
+        if (hipMemset(c->ws, 0, total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
             rc = SV_ERR_HIP;
         }
     }
@@ -1432,11 +1537,10 @@ int spec_verify_run(spec_verify_ctx* ctx, const void* target_logits, const void*
     p.out_nacc = out_num_accepted;
     p.out_p = out_p_draft;
     p.out_q = out_q_draft;
-    p.part = ctx->part;
+    p.rec = ctx->rec;
     p.team = ctx->team;
     p.result = ctx->result;
     p.req_count = ctx->req_count;
-    p.req_first = ctx->req_first;
     p.status = ctx->status;
     p.B = B;
     p.K = K;
@@ -1447,7 +1551,7 @@ int spec_verify_run(spec_verify_ctx* ctx, const void* target_logits, const void*
     p.c32 = (float)p.c64;
     p.key0 = (uint32_t)(seed & 0xFFFFFFFFu);
     p.key1 = (uint32_t)(seed >> 32);
-    ctx->calls = ctx->calls % 0x3FFFFFFFu + 1u;     // 1 .. 2^30 - 1, never 0
+    ctx->calls = ctx->calls % 0xFFFFFFFFu + 1u;     // 1 .. 2^32 - 1, never 0
     p.epoch = ctx->calls;
 
     int prev = -1;
