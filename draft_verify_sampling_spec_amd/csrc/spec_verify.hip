@@ -7,7 +7,9 @@
 // per-request verify budgets of section "What DSpark adds", paragraph 2.
 // The ABI and its conventions are documented in include/spec_verify.h.
 //
-// Design: one persistent kernel per call, every logit byte read from HBM once.
+// Design: one persistent kernel per call; every logit byte is read from HBM
+// once by the streaming loop, and only the rows of each request's first
+// rejected position are read a second time.
 //  * Work unit = vocabulary chunk c of position i of request b: the chunk of
 //    target row i and, for a drafted position, the same chunk of drafter row
 //    i. Every chunk has the same size (448 data lanes x 4 sixteen-byte loads
@@ -17,36 +19,33 @@
 //    w, w + G, w + 2G, ... (G = grid size >= C, so two units of one
 //    workgroup never share a team).
 //  * A workgroup is 8 waves. Waves 1-7 stream data: 16-byte loads of a unit
-//    into registers, all in flight at once, reduced per wave to the max and
-//    sum of 2^((z - max) log2(e)/T) (sampled) or (max, lowest index)
-//    (greedy), posted to LDS. Wave 0 is the control wave: it merges the
-//    waves' statistics and publishes the chunk's partial record. The two
-//    kinds of waves exchange tagged LDS messages, with no workgroup barrier
-//    in the streaming loop.
-//  * Sampled mode: every record word carries the call's epoch, so a record
-//    is complete when all its words carry it. Every member of a team reads
-//    the C records of its team once they are complete and takes the team's
-//    accept decision itself (the same deterministic merge in every member);
-//    no election and no counter sits between a chunk's statistics and its
-//    team's decision. Meanwhile the drafted unit's data waits in a per-lane
-//    LDS slot; on a rejection each member turns its parked chunk into its
-//    residual mass max(0, p - q) and publishes it.
-//  * The member holding chunk 0 keeps the books: p(x), q(x), the decision
-//    word, and, for a rejection or a bonus position, a draw queued to the end
-//    of its loop. There, once the earlier positions of the request are
-//    decided, the draw is made only for the request's first rejection (or
-//    the bonus position when none): residual CDF over chunks from the
-//    published masses, then the whole workgroup re-reads the one chunk that
-//    holds the threshold for the element-level scan.
-//  * Greedy mode: the last arriver of a team (device-scope counter) merges
-//    the chunk argmaxes and decides; no data is parked.
+//    into registers, reduced per wave to the max and sum of
+//    2^((z - max) log2(e)/T) (sampled) or (max, lowest index) (greedy),
+//    posted to LDS; then the next unit's loads go out. They never wait on
+//    another workgroup. Wave 0 is the control wave: it merges the waves'
+//    statistics and publishes the chunk's record; the two kinds of waves
+//    exchange tagged LDS messages, with no workgroup barrier in the loop.
+//  * Every record word carries the call's epoch, so a record is complete when
+//    all its words carry it. The workgroup holding chunk 0 of a team reads
+//    the team's C records once complete (a poll issued one round later, so
+//    its latency overlaps the next unit) and decides: greedy, the row's
+//    first argmax; sampled, p(x), q(x) and the accept test. It writes the
+//    decision word and completes the team, or queues a draw for after the
+//    loop (a rejection, or the bonus position).
+//  * After the loop (barriers allowed): each queued draw is settled -- a
+//    rejection draws only if it is its request's first, the bonus position
+//    only if nothing was rejected; the members of each first rejection
+//    re-read their chunk and publish its residual mass max(0, p - q) with the
+//    team's normalisers; the draw's owner scans the residual CDF over chunks,
+//    then the whole workgroup re-reads the one chunk that holds the threshold
+//    for the element-level scan.
 //  * Per request, the team that completes last writes the outputs.
-//  * Waiting: inside the loop a workgroup waits only for the records of a
-//    team it has already published to, and never while it holds an
-//    unpublished unit; by induction on the unit index every record gets
-//    written. Waits at the end of the loop depend only on work done inside
-//    loops. Every wait is bounded (status flag on expiry) so the kernel
-//    always drains.
+//  * Waiting: in the loop only the control wave waits on other workgroups,
+//    for the records of units they publish in the same pass, and a unit is
+//    published without waiting for anything but this workgroup's data waves.
+//    After the loop, each step waits only on earlier steps (or the loops) of
+//    other workgroups. Every wait is bounded (status flag on expiry) so the
+//    kernel always drains.
 //  * Synchronisation uses device-scope relaxed atomics (plus s_waitcnt where
 //    a counter orders earlier stores), never release/acquire fences: those
 //    write back and invalidate the whole L2.
@@ -63,15 +62,16 @@
 
 namespace {
 
-// The wave count is a multiple of 4 so that every SIMD of a CU holds the same
-// number of waves of each workgroup: with 5 waves, the hardware reserves two
-// wave slots per SIMD for each workgroup, and fewer workgroups fit than the
-// occupancy query reports.
+// The wave count is a multiple of 4 so that every SIMD holds the same number
+// of a workgroup's waves (with 5 waves, the hardware reserves two wave slots
+// per SIMD per workgroup and fewer workgroups fit than the occupancy query
+// reports).
 constexpr int kWaves = 8;                      // wave 0: control; waves 1-7: data
 constexpr int kThreads = kWaves * 64;
 constexpr int kDataWaves = kWaves - 1;
 constexpr int kDataThreads = kDataWaves * 64;
 constexpr int kG = 4;                          // 16-byte groups per data lane per row of a unit
+constexpr int kLaunchBatch = 8192;             // requests per launch (unit offsets live in LDS)
 constexpr int kScanElems = kDataThreads * 8;   // elements per scan sub-tile
 constexpr int kMaxSub = 4;                     // sub-tiles per chunk
 constexpr int kTeamWords = 32;                 // words per team record (128 bytes)
@@ -80,22 +80,19 @@ constexpr unsigned kSpinLimit = 1u << 20;      // bounded device-scope wait (~1 
 constexpr unsigned kLdsSpinLimit = 1u << 26;   // bounded LDS mailbox wait (~3 s)
 
 // Team record words.
-constexpr int TW_ARRIVE = 0;    // greedy: units of the team that published their argmax
 constexpr int TW_DEC = 2;       // 64-bit decision: (epoch << 32) | accepted (words 2-3)
+constexpr int TW_DRAW = 4;      // 64-bit: (epoch << 32) | 1 if the team's deferred draw is made
 
 // Unit record: 8 64-bit words.
 //   sampled: word f = (value bits << 32) | epoch for the fp32 values
 //            R_MT max of z_t, R_MD max of z_d, R_ST sum of 2^((z_t - M_t) c),
 //            R_SD likewise, R_RES residual mass once the team has rejected
-//   greedy:  word 0 = (max bits << 32) | lowest index of the max
+//   greedy:  word R_MT = (max bits << 32) | epoch, word R_MD = (lowest index
+//            of the max << 32) | epoch
 constexpr int kRecWords = 8;
 constexpr int R_MT = 0, R_MD = 1, R_ST = 2, R_SD = 3, R_RES = 4;
 constexpr int kStatWords = 4;   // words R_MT..R_SD make a record complete
 constexpr int kMaxChunks = 192; // chunks per row the team merge supports
-
-// Decision posted to the data waves for a parked unit.
-constexpr unsigned PH_ACCEPT = 1u;
-constexpr unsigned PH_REJECT = 2u;              // data waves: publish the residual mass
 
 // Philox4x32 constants (Salmon et al., SC'11): round multipliers and the key
 // increments applied between rounds.
@@ -122,6 +119,7 @@ struct Params {
     int* tasks;                    // [G][task_cap]: deferred draws, 2 * team + is_bonus
     unsigned* status;              // 1 word
     int B, K, V;
+    int bbase;                     // index of request 0 of this launch in the caller's batch
     int C;                         // chunks per row
     int CE;                        // elements per chunk
     int task_cap;                  // task list entries per workgroup
@@ -286,23 +284,21 @@ struct Shared {
     int st_idx[2][kDataWaves];
     int st_tag[2][kDataWaves];                   // round + 1
     int st_done[2];                              // control wave: round + 1 of the slot it read last
-    // Control wave -> data waves: the parked unit's decision and the team's
-    // normalisers, posted in round r (tag r) into slot r & 1.
-    unsigned ph_val[2];
-    float ph_mt[2], ph_md[2], ph_ist[2], ph_isd[2];
-    int ph_tag[2];
-    // Data wave -> control wave: the parked chunk's residual mass (tag: round).
-    double rs_val[kDataWaves];
-    int rs_tag[kDataWaves];
     // Set once a bounded wait expired: every later wait returns at once.
     int abort_wait;
-    // End of the loop: deferred draws of this workgroup and the one at hand.
+    // After the loop: deferred draws of this workgroup and the one at hand.
     int ntasks;
     int tk_draw;                                 // 1: scan tk_chunk
     int tk_chunk, tk_mode;                       // mode: 0 target row, 1 residual
     double tk_thr;
     float tk_mt, tk_md, tk_ist, tk_isd;
-    // Block-wide scan scratch (deferred draws only, under barriers).
+    // After the loop: chunks of first rejections to re-read for their
+    // residual mass (round indices of this workgroup), and the one at hand.
+    int rr_n;
+    int rr_round[64];
+    int rr_b, rr_i, rr_c, rr_tr;
+    float rr_mt, rr_md, rr_ist, rr_isd;
+    // Block-wide scratch (after the loop only, under barriers).
     double scan_ws[kMaxSub * kDataWaves];
     double red_d[kWaves];
     float red_f[kWaves];
@@ -580,30 +576,127 @@ __device__ void team_complete(const Params& P, int b, int k) {
         if (P.out_p) P.out_p[(size_t)b * K + t] = NAN;
         if (P.out_q) P.out_q[(size_t)b * K + t] = NAN;
     }
-    // Every unit of the request has been counted: reset the counters for the
+    // Every team of the request has been counted: reset the counter for the
     // next call (tagged words carry the call epoch and need no reset).
-    if (kGreedy) {
-        for (int t = 0; t <= k; ++t) st32(P.team + (size_t)(tr0 + t) * kTeamWords + TW_ARRIVE, 0u);
-    }
     st32(&P.req_count[b * kReqStride], 0u);
 }
 
-// ------------------------------------------------------------ greedy leader --
+// ----------------------------------------------------------- team records --
 
-// Control wave, greedy: merge the chunk argmaxes of target row i, decide,
-// complete the team.
-__device__ void leader_greedy(const Params& P, int b, int i, int k, int tr) {
+// Record words a team's decision needs per chunk: sampled R_MT..R_SD,
+// greedy R_MT (max) and R_MD (index).
+template <bool kGreedy>
+__device__ __forceinline__ constexpr int rec_words() { return kGreedy ? 2 : kStatWords; }
+
+// A team's C records as one control-wave load: lane l holds chunks l, l + 64,
+// l + 128 (C <= kMaxChunks).
+struct TeamPoll {
+    unsigned long long w[kMaxChunks / 64][kStatWords];
+};
+
+template <bool kGreedy>
+__device__ __forceinline__ void poll_issue(const Params& P, int tr, TeamPoll& pl) {
+    const int lane = threadIdx.x & 63;
+    const int C = P.C;
+    unsigned long long* rec = P.rec + (size_t)tr * C * kRecWords;
+    #pragma unroll
+    for (int q = 0; q < kMaxChunks / 64; ++q) {
+        const int cc = lane + 64 * q;
+        #pragma unroll
+        for (int f = 0; f < rec_words<kGreedy>(); ++f) {
+            pl.w[q][f] = cc < C ? ld64(rec + cc * kRecWords + f) : (unsigned long long)P.epoch;
+        }
+    }
+}
+
+// True when every record word of the team carries this call's epoch.
+template <bool kGreedy>
+__device__ __forceinline__ bool poll_complete(const Params& P, const TeamPoll& pl) {
+    bool ok = true;
+    #pragma unroll
+    for (int q = 0; q < kMaxChunks / 64; ++q) {
+        #pragma unroll
+        for (int f = 0; f < rec_words<kGreedy>(); ++f) ok = ok && tag_ok(pl.w[q][f], P.epoch);
+    }
+    return __ballot(!ok) == 0;
+}
+
+// Poll until complete (bounded).
+template <bool kGreedy>
+__device__ void poll_wait(const Params& P, Shared& sh, int tr, TeamPoll& pl) {
+    for (unsigned it = 0;; ++it) {
+        poll_issue<kGreedy>(P, tr, pl);
+        if (poll_complete<kGreedy>(P, pl)) break;
+        if (it >= kSpinLimit || lds_get(&sh.abort_wait)) {
+            if ((threadIdx.x & 63) == 0) give_up(P, sh);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// Team-wide normalisers (identical in every workgroup that computes them:
+// same inputs, same lanes, same reduction order).
+struct TeamStats {
+    float mt, md;      // max of the target / drafter row
+    double st, sd;     // sum of 2^((z - max) c) over the row
+};
+
+// Merge complete sampled records: M = max of chunk maxima,
+// S = sum of S_c 2^((M_c - M) c).
+__device__ TeamStats team_stats(const Params& P, const TeamPoll& pl) {
+    const int lane = threadIdx.x & 63;
+    const int C = P.C;
+    float mt = -INFINITY, md = -INFINITY;
+    #pragma unroll
+    for (int q = 0; q < kMaxChunks / 64; ++q) {
+        if (lane + 64 * q < C) {
+            mt = fmaxf(mt, tag_val(pl.w[q][R_MT]));
+            md = fmaxf(md, tag_val(pl.w[q][R_MD]));
+        }
+    }
+    mt = wave_max(mt);
+    md = wave_max(md);
+    double st = 0.0, sd = 0.0;
+    #pragma unroll
+    for (int q = 0; q < kMaxChunks / 64; ++q) {
+        if (lane + 64 * q < C) {
+            const float s1 = tag_val(pl.w[q][R_ST]), s2 = tag_val(pl.w[q][R_SD]);
+            if (s1 > 0.0f) st += (double)s1 * exp2(((double)tag_val(pl.w[q][R_MT]) - (double)mt) * P.c64);
+            if (s2 > 0.0f) sd += (double)s2 * exp2(((double)tag_val(pl.w[q][R_MD]) - (double)md) * P.c64);
+        }
+    }
+    TeamStats t;
+    t.mt = mt;
+    t.md = md;
+    t.st = wave_sum(st);
+    t.sd = wave_sum(sd);
+    return t;
+}
+
+// Blocking wait and merge (deferred draws).
+__device__ TeamStats merge_team(const Params& P, Shared& sh, int tr) {
+    TeamPoll pl;
+    poll_wait<false>(P, sh, tr, pl);
+    return team_stats(P, pl);
+}
+
+// Control wave, greedy: complete records of team tr (position i of request
+// b with budget k): the row's first argmax; the decision; complete the team.
+__device__ void decide_greedy(const Params& P, const TeamPoll& pl, int b, int i, int k, int tr) {
     const int lane = threadIdx.x & 63;
     const int C = P.C;
     float bv = -INFINITY;
     int bi = INT_MAX;
-    for (int cc = lane; cc < C; cc += 64) {
-        const unsigned long long w = ld64(&P.rec[((size_t)tr * C + cc) * kRecWords]);
-        const float v = __uint_as_float((unsigned)(w >> 32));
-        const int idx = (int)(unsigned)w;
-        if (better_arg(v, idx, bv, bi)) {
-            bv = v;
-            bi = idx;
+    #pragma unroll
+    for (int q = 0; q < kMaxChunks / 64; ++q) {
+        if (lane + 64 * q < C) {
+            const float v = tag_val(pl.w[q][R_MT]);
+            const int idx = (int)(unsigned)(pl.w[q][R_MD] >> 32);
+            if (better_arg(v, idx, bv, bi)) {
+                bv = v;
+                bi = idx;
+            }
         }
     }
     #pragma unroll
@@ -628,74 +721,6 @@ __device__ void leader_greedy(const Params& P, int b, int i, int k, int tr) {
         st64(dec_word(P, tr), ((unsigned long long)P.epoch << 32) | (accept ? 1u : 0u));
         team_complete<true>(P, b, k);
     }
-}
-
-// ----------------------------------------------------- sampled team merge --
-
-// Team-wide normalisers (identical in every workgroup that computes them:
-// same inputs, same lanes, same reduction order).
-struct TeamStats {
-    float mt, md;      // max of the target / drafter row
-    double st, sd;     // sum of 2^((z - max) c) over the row
-};
-
-// Control wave: wait until the C records of team tr are complete (bounded),
-// then merge them: M = max of chunk maxima, S = sum of S_c 2^((M_c - M) c).
-// Lane l holds chunks l, l + 64, l + 128 (C <= kMaxChunks).
-__device__ TeamStats merge_team(const Params& P, Shared& sh, int tr) {
-    const int lane = threadIdx.x & 63;
-    const int C = P.C;
-    const unsigned ep = P.epoch;
-    unsigned long long* rec = P.rec + (size_t)tr * C * kRecWords;
-    constexpr int Q = kMaxChunks / 64;
-    unsigned long long w[Q][kStatWords];
-    for (unsigned it = 0;; ++it) {
-        bool ok = true;
-        #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const int cc = lane + 64 * q;
-            #pragma unroll
-            for (int f = 0; f < kStatWords; ++f) {
-                w[q][f] = cc < C ? ld64(rec + cc * kRecWords + f) : (unsigned long long)ep;
-            }
-        }
-        #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            #pragma unroll
-            for (int f = 0; f < kStatWords; ++f) ok = ok && tag_ok(w[q][f], ep);
-        }
-        if (__ballot(!ok) == 0) break;
-        if (it >= kSpinLimit || lds_get(&sh.abort_wait)) {
-            if (lane == 0) give_up(P, sh);
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-    }
-    float mt = -INFINITY, md = -INFINITY;
-    #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        if (lane + 64 * q < C) {
-            mt = fmaxf(mt, tag_val(w[q][R_MT]));
-            md = fmaxf(md, tag_val(w[q][R_MD]));
-        }
-    }
-    mt = wave_max(mt);
-    md = wave_max(md);
-    double st = 0.0, sd = 0.0;
-    #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        if (lane + 64 * q < C) {
-            const float s1 = tag_val(w[q][R_ST]), s2 = tag_val(w[q][R_SD]);
-            if (s1 > 0.0f) st += (double)s1 * exp2(((double)tag_val(w[q][R_MT]) - (double)mt) * P.c64);
-            if (s2 > 0.0f) sd += (double)s2 * exp2(((double)tag_val(w[q][R_MD]) - (double)md) * P.c64);
-        }
-    }
-    TeamStats t;
-    t.mt = mt;
-    t.md = md;
-    t.st = wave_sum(st);
-    t.sd = wave_sum(sd);
-    return t;
 }
 
 // Control wave: queue a deferred draw (team tr; bonus or rejection).
@@ -762,15 +787,15 @@ __device__ __forceinline__ void issue_loads(const Params& P, const Unit& d, int 
 }
 
 // Control wave: collect the data waves' statistics of the unit of round r,
-// merge them and publish the unit's record. Greedy: count the arrival and
-// lead the team if last. Sampled: queue the bonus draw from the chunk-0
-// member of a bonus position.
+// merge them and publish the unit's record (epoch-tagged words, no wait).
+// Sampled: the chunk-0 member of a bonus position queues the bonus draw.
 template <typename E, bool kGreedy>
 __device__ __forceinline__ void control_unit(const Params& P, Shared& sh, const Unit& cur, int r,
                                              int& ntasks) {
     const int lane = threadIdx.x & 63;
     const int C = P.C;
     const int slot = r & 1;
+    const unsigned ep = P.epoch;
     if (lane < kDataWaves) lds_wait(P, sh, &sh.st_tag[slot][lane], r + 1);
     unsigned long long* rec = P.rec + ((size_t)cur.tr * C + cur.c) * kRecWords;
     if (kGreedy) {
@@ -791,15 +816,10 @@ __device__ __forceinline__ void control_unit(const Params& P, Shared& sh, const 
                 bi = oi;
             }
         }
-        int lead = 0;
         if (lane == 0) {
-            st64(rec, ((unsigned long long)__float_as_uint(bv) << 32) | (unsigned)bi);
-            drain();
-            const unsigned old = add32(&P.team[(size_t)cur.tr * kTeamWords + TW_ARRIVE], 1u);
-            lead = old == (unsigned)C - 1;
+            st64(rec + R_MT, tagged(bv, ep));
+            st64(rec + R_MD, ((unsigned long long)(unsigned)bi << 32) | ep);
         }
-        lead = __shfl(lead, 0, 64);
-        if (lead) leader_greedy(P, cur.b, cur.i, cur.k, cur.tr);
     } else {
         float mt = -INFINITY, md = -INFINITY;
         double a = 0.0, d = 0.0;
@@ -817,7 +837,6 @@ __device__ __forceinline__ void control_unit(const Params& P, Shared& sh, const 
         if (d > 0.0) d *= (double)fast_exp2((md - Md) * P.c32);
         const double St = wave_sum(a), Sd = wave_sum(d);
         if (lane == 0) {
-            const unsigned ep = P.epoch;
             st64(rec + R_MT, tagged(Mt, ep));
             st64(rec + R_MD, tagged(Md, ep));
             st64(rec + R_ST, tagged((float)St, ep));
@@ -827,109 +846,128 @@ __device__ __forceinline__ void control_unit(const Params& P, Shared& sh, const 
     }
 }
 
-// Control wave, sampled: the parked unit of round r - 1 (drafted position i
-// of request b, drafted token x loaded a round earlier). Wait for its team's
-// records, take the team's decision, post it to the data waves; on a
-// rejection that may be the request's first, collect and publish the chunk's
-// residual mass. The chunk-0 member also writes p(x), q(x) and the decision
-// word, and completes the team or queues its draw.
-template <typename E>
-__device__ __forceinline__ void control_parked(const Params& P, Shared& sh, const Unit& prev, int x,
-                                               int r, int& ntasks) {
-    const int lane = threadIdx.x & 63;
-    const int K = P.K;
-    const int slot = r & 1;
-    const unsigned ep = P.epoch;
-    const E* target = static_cast<const E*>(P.target);
-    const E* draft = static_cast<const E*>(P.draft);
-    // Issued before the records are awaited: the drafted token's logits and
-    // the decisions of the request's earlier positions known so far.
-    const bool valid = x >= 0 && x < P.V;
-    float zt = 0.0f, zd = 0.0f;
-    if (valid) {
-        zt = Elem<E>::one(target + ((size_t)prev.b * (K + 1) + prev.i) * (size_t)P.V + x);
-        zd = Elem<E>::one(draft + ((size_t)prev.b * K + prev.i) * (size_t)P.V + x);
+// A chunk-0 unit whose team decision this workgroup owes, with what the
+// decision needs besides the records (loaded when its poll is issued).
+struct Owed {
+    Unit u;
+    int x;              // drafted token (sampled)
+    float zt, zd;       // the drafted token's logits (sampled)
+};
+
+template <typename E, bool kGreedy>
+__device__ __forceinline__ void owed_issue(const Params& P, Owed& o, TeamPoll& pl) {
+    if (!kGreedy) {
+        const int K = P.K;
+        const E* target = static_cast<const E*>(P.target);
+        const E* draft = static_cast<const E*>(P.draft);
+        o.zt = o.zd = 0.0f;
+        if (o.x >= 0 && o.x < P.V) {
+            o.zt = Elem<E>::one(target + ((size_t)o.u.b * (K + 1) + o.u.i) * (size_t)P.V + o.x);
+            o.zd = Elem<E>::one(draft + ((size_t)o.u.b * K + o.u.i) * (size_t)P.V + o.x);
+        }
     }
-    unsigned long long dprev = 0;
-    if (lane < prev.i) dprev = ld64(dec_word(P, prev.b * (K + 1) + lane));
-    const TeamStats ts = merge_team(P, sh, prev.tr);
-    double px = 0.0, qx = 0.0;
-    if (valid) {
-        px = exp2(((double)zt - (double)ts.mt) * P.c64) / ts.st;
-        qx = exp2(((double)zd - (double)ts.md) * P.c64) / ts.sd;
-    }
-    const uint4 rw = philox4x32_10((uint32_t)prev.b, (uint32_t)prev.i, 0u, 0u, P.key0, P.key1);
-    const bool accept = word_to_uniform(rw.x) * qx < px;
-    // An earlier position already known to be rejected: no draw will be
-    // needed for this one, whatever its decision.
-    const bool later = __ballot(lane < prev.i && (unsigned)(dprev >> 32) == ep &&
-                                (dprev & 1ull) == 0) != 0;
-    const bool residual = !accept && !later;
-    const float ist = (float)(1.0 / ts.st), isd = (float)(1.0 / ts.sd);
-    if (lane == 0) {
-        sh.ph_val[slot] = residual ? PH_REJECT : PH_ACCEPT;
-        sh.ph_mt[slot] = ts.mt;
-        sh.ph_md[slot] = ts.md;
-        sh.ph_ist[slot] = ist;
-        sh.ph_isd[slot] = isd;
-        order();
-        lds_put(&sh.ph_tag[slot], r);
-    }
-    const bool books = prev.c == 0;
-    if (books && lane == 0) {
-        if (!valid) atomicOr(P.status, SV_FLAG_BAD_TOKEN);
-        if (P.out_p) P.out_p[(size_t)prev.b * K + prev.i] = (float)px;
-        if (P.out_q) P.out_q[(size_t)prev.b * K + prev.i] = (float)qx;
-        st64(dec_word(P, prev.tr), ((unsigned long long)ep << 32) | (accept ? 1u : 0u));
-        if (!residual) team_complete<false>(P, prev.b, prev.k);
-    }
-    if (!residual) return;
-    if (books) add_task(P, prev.tr, false, ntasks);
-    // Residual mass of the parked chunk: one partial per data wave.
-    double v = 0.0;
-    if (lane < kDataWaves) {
-        lds_wait(P, sh, &sh.rs_tag[lane], r);
-        v = sh.rs_val[lane];
-    }
-    v = wave_sum(v);
-    if (lane == 0) {
-        st64(P.rec + ((size_t)prev.tr * P.C + prev.c) * kRecWords + R_RES,
-             tagged((float)v, ep));
-    }
+    poll_issue<kGreedy>(P, o.u.tr, pl);
 }
 
-// The control wave's loop. Round r: the parked unit of round r - 1 (its
-// team's decision, started as soon as that unit is published), then the unit
-// of round r (publish).
+// Control wave: decide an owed team from its complete records. Greedy:
+// argmax, decision, completion. Sampled (a drafted position): p(x), q(x), the
+// accept decision, the decision word; an accepted team is complete, a
+// rejected one gets a deferred draw (made only if it is the request's first
+// rejection).
+template <bool kGreedy>
+__device__ __forceinline__ void owed_decide(const Params& P, const Owed& o, const TeamPoll& pl,
+                                            int& ntasks) {
+    const Unit& u = o.u;
+    if (kGreedy) {
+        decide_greedy(P, pl, u.b, u.i, u.k, u.tr);
+        return;
+    }
+    const int lane = threadIdx.x & 63;
+    const int K = P.K;
+    const TeamStats ts = team_stats(P, pl);
+    const bool valid = o.x >= 0 && o.x < P.V;
+    double px = 0.0, qx = 0.0;
+    if (valid) {
+        px = exp2(((double)o.zt - (double)ts.mt) * P.c64) / ts.st;
+        qx = exp2(((double)o.zd - (double)ts.md) * P.c64) / ts.sd;
+    }
+    const uint4 rw = philox4x32_10((uint32_t)(P.bbase + u.b), (uint32_t)u.i, 0u, 0u, P.key0, P.key1);
+    const bool accept = word_to_uniform(rw.x) * qx < px;
+    if (lane == 0) {
+        if (!valid) atomicOr(P.status, SV_FLAG_BAD_TOKEN);
+        if (P.out_p) P.out_p[(size_t)u.b * K + u.i] = (float)px;
+        if (P.out_q) P.out_q[(size_t)u.b * K + u.i] = (float)qx;
+        st64(dec_word(P, u.tr), ((unsigned long long)P.epoch << 32) | (accept ? 1u : 0u));
+        if (accept) team_complete<false>(P, u.b, u.k);
+    }
+    if (!accept) add_task(P, u.tr, false, ntasks);
+}
+
+// The control wave's loop, round r:
+//  A. a decision still owed for the unit of round r - 2 (its team was
+//     incomplete when last polled): wait for the records and decide;
+//  B. poll the team of the chunk-0 unit of round r - 1; decide if complete;
+//  C. the unit of round r: statistics from the data waves, publish;
+//  D. the unit of round r - 1 still undecided: poll again, decide if
+//     complete, else it is owed (A of the next round).
+// Nothing the data waves do waits on a decision.
 template <typename E, bool kGreedy, bool kVec>
 __device__ __forceinline__ int control_loop(const Params& P, Shared& sh, const int* off) {
     const int U = off[P.B];
     const int G = gridDim.x;
     Unit cur = decode_unit(P, off, blockIdx.x, U, kGreedy);
-    Unit prev;
-    prev.u = -1;
-    int x_prev = 0;
+    Owed prev, owed;
+    prev.u.u = -1;
+    owed.u.u = -1;
     int ntasks = 0;
-    for (int r = 0; cur.u >= 0 || prev.u >= 0; ++r) {
-        if (!kGreedy && prev.u >= 0) control_parked<E>(P, sh, prev, x_prev, r, ntasks);
-        prev.u = -1;
+    TeamPoll pl;
+    for (int r = 0; cur.u >= 0 || prev.u.u >= 0 || owed.u.u >= 0; ++r) {
+        // A.
+        if (owed.u.u >= 0) {
+            owed_issue<E, kGreedy>(P, owed, pl);
+            if (!poll_complete<kGreedy>(P, pl)) poll_wait<kGreedy>(P, sh, owed.u.tr, pl);
+            owed_decide<kGreedy>(P, owed, pl, ntasks);
+            owed.u.u = -1;
+        }
+        // B.
+        bool pending = false;
+        if (prev.u.u >= 0) {
+            owed_issue<E, kGreedy>(P, prev, pl);
+            if (poll_complete<kGreedy>(P, pl)) {
+                owed_decide<kGreedy>(P, prev, pl, ntasks);
+            } else {
+                pending = true;
+            }
+        }
+        // C.
+        Owed next;
+        next.u.u = -1;
         if (cur.u >= 0) {
             control_unit<E, kGreedy>(P, sh, cur, r, ntasks);
-            if (cur.has_d) {
-                prev = cur;
-                x_prev = P.tokens[(size_t)cur.b * P.K + cur.i];   // used next round
+            if (cur.c == 0 && (kGreedy || cur.has_d)) {
+                next.u = cur;
+                next.x = kGreedy ? 0 : P.tokens[(size_t)cur.b * P.K + cur.i];
             }
             cur = decode_unit(P, off, cur.u + G, U, kGreedy);
         }
+        // D.
+        if (pending) {
+            poll_issue<kGreedy>(P, prev.u.tr, pl);
+            if (poll_complete<kGreedy>(P, pl)) {
+                owed_decide<kGreedy>(P, prev, pl, ntasks);
+            } else {
+                owed = prev;
+            }
+        }
+        prev = next;
     }
     return ntasks;
 }
 
 // The data waves' loop: stream units through registers, post per-wave
-// statistics, park drafted units in LDS until their team has decided.
+// statistics to the control wave, load the next unit.
 template <typename E, bool kGreedy, bool kVec>
-__device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int* off,
-                                          uint4* stash) {
+__device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int* off) {
     constexpr int W = Elem<E>::W;
     const int lane = threadIdx.x & 63;
     const int dw = (threadIdx.x >> 6) - 1;         // data wave index
@@ -941,48 +979,9 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
     uint4 gt[kG], gd[kG];
     Unit cur = decode_unit(P, off, blockIdx.x, U, kGreedy);
     if (cur.u >= 0) issue_loads<E, kVec>(P, cur, dt, gt, gd);
-    bool have_prev = false;
-    int r = 0;
-
-    // The parked unit of round rr - 1: wait for its team's decision; on a
-    // rejection, post this wave's part of the chunk's residual mass.
-    auto finish_parked = [&](int rr) {
-        const int slot = rr & 1;
-        lds_wait(P, sh, &sh.ph_tag[slot], rr);
-        if (sh.ph_val[slot] != PH_REJECT) return;
-        const float mt = sh.ph_mt[slot], md = sh.ph_md[slot];
-        const float ist = sh.ph_ist[slot], isd = sh.ph_isd[slot];
-        float lr = 0.0f;
-        #pragma unroll 1
-        for (int j = 0; j < kG; ++j) {
-            // Each lane reads back only the groups it parked itself.
-            const uint4 a = stash[(0 * kG + j) * kDataThreads + dt];
-            const uint4 d = stash[(1 * kG + j) * kDataThreads + dt];
-            float m8[W];
-            #pragma unroll
-            for (int kk = 0; kk < W; ++kk) {
-                const float pv = fast_exp2((Elem<E>::at(a, kk) - mt) * cs) * ist;
-                const float qv = fast_exp2((Elem<E>::at(d, kk) - md) * cs) * isd;
-                m8[kk] = fmaxf(0.0f, pv - qv);
-            }
-            #pragma unroll
-            for (int h = W / 2; h > 0; h >>= 1) {
-                #pragma unroll
-                for (int kk = 0; kk < h; ++kk) m8[kk] += m8[kk + h];
-            }
-            lr += m8[0];
-        }
-        const double v = wave_sum((double)lr);
-        if (lane == 0) {
-            sh.rs_val[dw] = v;
-            order();
-            lds_put(&sh.rs_tag[dw], rr);
-        }
-    };
-
-    for (; cur.u >= 0; ++r) {
+    for (int r = 0; cur.u >= 0; ++r) {
         const int slot = r & 1;
-        // Per-wave statistics of the unit of round r.
+        const Unit nxt = decode_unit(P, off, cur.u + G, U, kGreedy);
         if (kGreedy) {
             float bv = -INFINITY;
             int bi = INT_MAX;
@@ -997,6 +996,7 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
                     }
                 }
             }
+            if (nxt.u >= 0) issue_loads<E, kVec>(P, nxt, dt, gt, gd);
             #pragma unroll
             for (int o = 32; o > 0; o >>= 1) {
                 const float ov = __shfl_xor(bv, o, 64);
@@ -1061,6 +1061,8 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
                     ld += e[0];
                 }
             }
+            // The unit's data is consumed: stream the next one.
+            if (nxt.u >= 0) issue_loads<E, kVec>(P, nxt, dt, gt, gd);
             const double st = wave_sum((double)lt);
             const double sd = wave_sum((double)ld);
             if (lane == 0) {
@@ -1073,41 +1075,20 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
                 lds_put(&sh.st_tag[slot][dw], r + 1);
             }
         }
-
-        // The stash is free once the previous parked unit is done with.
-        if (have_prev) finish_parked(r);
-
-        // Park the unit, start streaming the next one.
-        const Unit nxt = decode_unit(P, off, cur.u + G, U, kGreedy);
-        if (cur.has_d) {
-            #pragma unroll
-            for (int j = 0; j < kG; ++j) {
-                stash[(0 * kG + j) * kDataThreads + dt] = gt[j];
-                stash[(1 * kG + j) * kDataThreads + dt] = gd[j];
-            }
-        }
-        if (nxt.u >= 0) issue_loads<E, kVec>(P, nxt, dt, gt, gd);
-        have_prev = cur.has_d;
         cur = nxt;
     }
-    if (have_prev) finish_parked(r);
 }
 
-// Control wave: prepare deferred draw number t of this workgroup (team
-// b, i): wait until the earlier positions of the request are decided; draw
-// only if none of them rejected (i is the request's first rejection, or the
-// bonus position with no rejection). Locate the chunk that holds the
-// threshold and leave its element scan to the whole workgroup.
-__device__ void task_prepare(const Params& P, Shared& sh, int task) {
+// ------------------------------------------------------- after the loop --
+
+// Control wave: are positions 0 .. i-1 of request b all accepted? Waits
+// (bounded) until the decisions that settle it are known: lane t polls
+// position t; done once every position before the first known rejection is
+// decided, or all are decided.
+__device__ bool earlier_accepted(const Params& P, Shared& sh, int b, int i) {
     const int lane = threadIdx.x & 63;
-    const int K = P.K, C = P.C;
+    const int K = P.K;
     const unsigned ep = P.epoch;
-    const int tr = task >> 1;
-    const bool bonus = task & 1;
-    const int b = tr / (K + 1), i = tr - b * (K + 1);
-    // Earlier positions (lane t polls position t): done once every position
-    // before the first known rejection is decided, or all are decided.
-    bool first = true;
     for (unsigned it = 0;; ++it) {
         unsigned long long d = 0;
         if (lane < i) d = ld64(dec_word(P, b * (K + 1) + lane));
@@ -1116,33 +1097,168 @@ __device__ void task_prepare(const Params& P, Shared& sh, int task) {
         const unsigned long long unknown = __ballot(!known);
         if (rej != 0) {
             const unsigned long long below = (rej & (~rej + 1)) - 1;   // lanes below the first rejection
-            if ((unknown & below) == 0) {
-                first = false;
-                break;
-            }
+            if ((unknown & below) == 0) return false;
         } else if (unknown == 0) {
-            break;
+            return true;
         }
         if (it >= kSpinLimit || lds_get(&sh.abort_wait)) {
             if (lane == 0) give_up(P, sh);
-            first = false;
-            break;
+            return false;
         }
         __builtin_amdgcn_s_sleep(2);
     }
-    int draw = 0, chunk = -1, mode = 0;
+}
+
+__device__ __forceinline__ unsigned long long* draw_word(const Params& P, int tr) {
+    return reinterpret_cast<unsigned long long*>(P.team + (size_t)tr * kTeamWords + TW_DRAW);
+}
+
+// Control wave, step 1: settle this workgroup's deferred draws. A rejected
+// position draws only if it is the request's first rejection; the bonus
+// position only if every drafted position was accepted. The answer goes to
+// the team's draw word, which the chunk members read in step 2.
+__device__ void settle_tasks(const Params& P, Shared& sh, int nt) {
+    const int K = P.K;
+    unsigned* list = reinterpret_cast<unsigned*>(P.tasks) + (size_t)blockIdx.x * P.task_cap;
+    for (int t = 0; t < nt; ++t) {
+        const int task = (int)ld32(list + t);
+        const int tr = task >> 1;
+        const int b = tr / (K + 1), i = tr - b * (K + 1);
+        const bool draw = earlier_accepted(P, sh, b, i);
+        if ((threadIdx.x & 63) == 0) {
+            st64(draw_word(P, tr), ((unsigned long long)P.epoch << 32) | (draw ? 1u : 0u));
+        }
+    }
+}
+
+// Control wave, step 2: which of this workgroup's drafted units (rounds
+// base .. base+63, lane = round - base) belong to a request's first
+// rejection? Those chunks are re-read for their residual mass.
+template <bool kGreedy>
+__device__ void scan_members(const Params& P, Shared& sh, const int* off, int base) {
+    const int lane = threadIdx.x & 63;
+    const int U = off[P.B];
+    const unsigned ep = P.epoch;
+    const Unit u = decode_unit(P, off, blockIdx.x + (base + lane) * gridDim.x, U, kGreedy);
+    bool need = false;
+    if (u.u >= 0 && u.has_d) {
+        bool settled = false;
+        for (unsigned it = 0; !settled; ++it) {
+            const unsigned long long d = ld64(dec_word(P, u.tr));
+            if ((unsigned)(d >> 32) == ep) {
+                if (d & 1ull) {
+                    settled = true;                            // accepted: no residual
+                } else {
+                    const unsigned long long w = ld64(draw_word(P, u.tr));
+                    if ((unsigned)(w >> 32) == ep) {
+                        settled = true;
+                        need = (w & 1ull) != 0;
+                    }
+                }
+            }
+            if (!settled) {
+                if (it >= kSpinLimit || lds_get(&sh.abort_wait)) {
+                    give_up(P, sh);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+    }
+    const unsigned long long m = __ballot(need);
+    if (need) sh.rr_round[__popcll(m & ((1ull << lane) - 1))] = base + lane;
+    if (lane == 0) sh.rr_n = __popcll(m);
+}
+
+// Whole workgroup, step 3: re-read the chunk of one first-rejection unit and
+// publish its residual mass sum max(0, p - q) with the team's normalisers.
+template <typename E, bool kVec>
+__device__ void reread_residual(const Params& P, Shared& sh, const int* off, int round) {
+    constexpr int W = Elem<E>::W;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int U = off[P.B];
+    if (wave == 0) {
+        const Unit u = decode_unit(P, off, blockIdx.x + round * gridDim.x, U, false);
+        const TeamStats ts = merge_team(P, sh, u.tr);
+        if (lane == 0) {
+            sh.rr_b = u.b;
+            sh.rr_i = u.i;
+            sh.rr_c = u.c;
+            sh.rr_tr = u.tr;
+            sh.rr_mt = ts.mt;
+            sh.rr_md = ts.md;
+            sh.rr_ist = (float)(1.0 / ts.st);
+            sh.rr_isd = (float)(1.0 / ts.sd);
+        }
+    }
+    __syncthreads();
+    float lr = 0.0f;
+    if (wave > 0) {
+        Unit u;
+        u.b = sh.rr_b;
+        u.i = sh.rr_i;
+        u.c = sh.rr_c;
+        u.e0 = u.c * P.CE;
+        u.n = min(P.CE, P.V - u.e0);
+        u.has_d = true;
+        uint4 gt[kG], gd[kG];
+        issue_loads<E, kVec>(P, u, tid - 64, gt, gd);
+        const float mt = sh.rr_mt, md = sh.rr_md, ist = sh.rr_ist, isd = sh.rr_isd;
+        const float cs = P.c32;
+        #pragma unroll
+        for (int j = 0; j < kG; ++j) {
+            float m8[W];
+            #pragma unroll
+            for (int kk = 0; kk < W; ++kk) {
+                const float pv = fast_exp2((Elem<E>::at(gt[j], kk) - mt) * cs) * ist;
+                const float qv = fast_exp2((Elem<E>::at(gd[j], kk) - md) * cs) * isd;
+                m8[kk] = fmaxf(0.0f, pv - qv);
+            }
+            #pragma unroll
+            for (int h = W / 2; h > 0; h >>= 1) {
+                #pragma unroll
+                for (int kk = 0; kk < h; ++kk) m8[kk] += m8[kk + h];
+            }
+            lr += m8[0];
+        }
+    }
+    const double v = wave_sum((double)lr);
+    if (lane == 0) sh.red_d[wave] = v;
+    __syncthreads();
+    if (tid == 0) {
+        double tot = 0.0;
+        for (int w = 1; w < kWaves; ++w) tot += sh.red_d[w];
+        st64(P.rec + ((size_t)sh.rr_tr * P.C + sh.rr_c) * kRecWords + R_RES,
+             tagged((float)tot, P.epoch));
+    }
+    __syncthreads();
+}
+
+// Control wave, step 4 (one deferred draw): if the draw is to be made, locate
+// the chunk holding the threshold -- over the residual masses of the team's
+// chunks for a first rejection, over p for the bonus position (or a residual
+// without mass) -- and leave its element scan to the whole workgroup.
+__device__ void task_prepare(const Params& P, Shared& sh, int task) {
+    const int lane = threadIdx.x & 63;
+    const int K = P.K, C = P.C;
+    const unsigned ep = P.epoch;
+    const int tr = task >> 1;
+    const bool bonus = task & 1;
+    const int b = tr / (K + 1), i = tr - b * (K + 1);
+    const bool draw = (ld64(draw_word(P, tr)) & 1ull) != 0;      // written by this workgroup
+    int chunk = -1, mode = 0;
     double thr = 0.0;
     TeamStats ts;
     ts.mt = ts.md = 0.0f;
     ts.st = ts.sd = 1.0;
-    if (first) {
+    if (draw) {
         ts = merge_team(P, sh, tr);
         unsigned long long* rec = P.rec + (size_t)tr * C * kRecWords;
-        const uint4 rw = philox4x32_10((uint32_t)b, (uint32_t)i, 0u, 0u, P.key0, P.key1);
+        const uint4 rw = philox4x32_10((uint32_t)(P.bbase + b), (uint32_t)i, 0u, 0u, P.key0, P.key1);
         const double u = word_to_uniform(rw.y);
         double total = 0.0, base = 0.0;
         if (!bonus) {
-            // Residual masses: all C members publish theirs.
+            // Residual masses: every chunk member publishes its own.
             for (unsigned it = 0;; ++it) {
                 bool ok = true;
                 for (int cc = lane; cc < C; cc += 64) ok = ok && tag_ok(ld64(rec + cc * kRecWords + R_RES), ep);
@@ -1178,7 +1294,6 @@ __device__ void task_prepare(const Params& P, Shared& sh, int task) {
             total = wave_sum(total);
             chunk_crossing(C, u * total, pmass, chunk, base);
         }
-        draw = 1;
         thr = u * total - base;
     }
     if (lane == 0) {
@@ -1193,17 +1308,34 @@ __device__ void task_prepare(const Params& P, Shared& sh, int task) {
     }
 }
 
-// Deferred draws of this workgroup (whole workgroup, under barriers).
+// After both loops (whole workgroup, under barriers): settle the deferred
+// draws, re-read the chunks of first rejections for their residual mass,
+// then make the draws. Each step waits only on earlier steps of other
+// workgroups (or on their loops), so no wait is circular.
 template <typename E, bool kVec>
-__device__ __forceinline__ void run_tasks(const Params& P, Shared& sh) {
+__device__ void after_loop(const Params& P, Shared& sh, const int* off) {
     const int K = P.K;
+    const int tid = threadIdx.x, wave = tid >> 6;
     const int nt = min(sh.ntasks, P.task_cap);
+    const int U = off[P.B];
+    const int rounds = (int)blockIdx.x < U ? (U - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+    // 1.
+    if (wave == 0) settle_tasks(P, sh, nt);
+    // 2 and 3, 64 rounds at a time.
+    for (int base = 0; base < rounds; base += 64) {
+        if (wave == 0) scan_members<false>(P, sh, off, base);
+        __syncthreads();
+        const int n = sh.rr_n;
+        for (int j = 0; j < n; ++j) reread_residual<E, kVec>(P, sh, off, sh.rr_round[j]);
+        __syncthreads();
+    }
+    // 4.
     const E* target = static_cast<const E*>(P.target);
     const E* draft = static_cast<const E*>(P.draft);
     unsigned* list = reinterpret_cast<unsigned*>(P.tasks) + (size_t)blockIdx.x * P.task_cap;
     for (int t = 0; t < nt; ++t) {
         const int task = (int)ld32(list + t);
-        if (threadIdx.x < 64) task_prepare(P, sh, task);
+        if (wave == 0) task_prepare(P, sh, task);
         __syncthreads();
         const int tr = task >> 1;
         const int b = tr / (K + 1), i = tr - b * (K + 1);
@@ -1217,7 +1349,7 @@ __device__ __forceinline__ void run_tasks(const Params& P, Shared& sh) {
                                               sh.tk_isd, P.c32, sh.tk_thr);
             y = o < 0 ? 0 : e0 + o;
         }
-        if (threadIdx.x == 0) {
+        if (tid == 0) {
             // The request's budget, clamped as in the prologue.
             int k = P.budgets[b];
             k = k < 0 ? 0 : (k > K ? K : k);
@@ -1233,9 +1365,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void verify_kernel(Params P) {
     extern __shared__ __align__(16) unsigned char dyn_smem[];
     __shared__ Shared sh;
-    // Dynamic LDS: the parked unit (sampled mode), then request unit offsets.
-    uint4* stash = reinterpret_cast<uint4*>(dyn_smem);
-    int* off = reinterpret_cast<int*>(dyn_smem + (kGreedy ? 0 : (size_t)2 * kG * kDataThreads * 16));
+    int* off = reinterpret_cast<int*>(dyn_smem);   // request unit offsets [B + 1]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int B = P.B, K = P.K, C = P.C;
@@ -1264,11 +1394,7 @@ void verify_kernel(Params P) {
         }
         if (lane == 63) sh.red_i[wave] = incl;
         if (tid < 2 * kDataWaves) (&sh.st_tag[0][0])[tid] = 0;
-        if (tid < kDataWaves) sh.rs_tag[tid] = -1;
-        if (tid < 2) {
-            sh.ph_tag[tid] = -1;
-            sh.st_done[tid] = 0;
-        }
+        if (tid < 2) sh.st_done[tid] = 0;
         if (tid == 0) sh.abort_wait = 0;
         __syncthreads();
         int run = incl - local;
@@ -1290,10 +1416,10 @@ void verify_kernel(Params P) {
         if (lane == 0) sh.ntasks = nt;
         drain();                                   // task list entries are written
     } else {
-        data_loop<E, kGreedy, kVec>(P, sh, off, stash);
+        data_loop<E, kGreedy, kVec>(P, sh, off);
     }
     __syncthreads();
-    if (!kGreedy) run_tasks<E, kVec>(P, sh);
+    if (!kGreedy) after_loop<E, kVec>(P, sh, off);
 }
 
 // Philox blocks as the verifier draws them, for checking the generator.
@@ -1324,7 +1450,8 @@ int chunks_for(int vocab, int dtype) {
 }
 
 size_t dyn_smem_bytes(int B, bool greedy) {
-    return (greedy ? 0 : (size_t)2 * kG * kDataThreads * 16) + (size_t)(B + 1) * sizeof(int);
+    (void)greedy;
+    return (size_t)(B + 1) * sizeof(int);
 }
 
 }  // namespace
@@ -1551,30 +1678,48 @@ int spec_verify_run(spec_verify_ctx* ctx, const void* target_logits, const void*
     p.c32 = (float)p.c64;
     p.key0 = (uint32_t)(seed & 0xFFFFFFFFu);
     p.key1 = (uint32_t)(seed >> 32);
-    ctx->calls = ctx->calls % 0xFFFFFFFFu + 1u;     // 1 .. 2^32 - 1, never 0
-    p.epoch = ctx->calls;
 
     int prev = -1;
     if (hipGetDevice(&prev) != hipSuccess) return SV_ERR_HIP;
     if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return SV_ERR_HIP;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    int r;
+    int r = SV_OK;
     // Vector-only loads when every row starts on a 16-byte boundary.
     const size_t es = ctx->dtype == SV_DTYPE_BF16 ? 2 : 4;
     const bool vec = aligned_to(target_logits, 16) &&
                      (greedy || K == 0 || aligned_to(draft_logits, 16)) &&
                      ((size_t)ctx->vocab * es) % 16 == 0;
-    if (ctx->dtype == SV_DTYPE_BF16) {
-        if (vec) {
-            r = greedy ? launch<uint16_t, true, true>(ctx, p, s) : launch<uint16_t, false, true>(ctx, p, s);
+    // Batches beyond kLaunchBatch requests run as consecutive launches on the
+    // stream (each launch keeps its request table in LDS); the workspace is
+    // reused, and the Philox counter keeps the caller's request index.
+    const size_t V = (size_t)ctx->vocab;
+    for (int b0 = 0; b0 < B && r == SV_OK; b0 += kLaunchBatch) {
+        Params q = p;
+        q.B = B - b0 < kLaunchBatch ? B - b0 : kLaunchBatch;
+        q.bbase = b0;
+        q.target = static_cast<const unsigned char*>(target_logits) + (size_t)b0 * (K + 1) * V * es;
+        q.draft = greedy ? nullptr
+                         : static_cast<const unsigned char*>(draft_logits) + (size_t)b0 * K * V * es;
+        q.tokens = draft_tokens ? draft_tokens + (size_t)b0 * K : nullptr;
+        q.budgets = budgets + b0;
+        q.out_tokens = out_tokens + (size_t)b0 * (K + 1);
+        q.out_nacc = out_num_accepted + b0;
+        q.out_p = out_p_draft ? out_p_draft + (size_t)b0 * K : nullptr;
+        q.out_q = out_q_draft ? out_q_draft + (size_t)b0 * K : nullptr;
+        ctx->calls = ctx->calls % 0xFFFFFFFFu + 1u;     // 1 .. 2^32 - 1, never 0
+        q.epoch = ctx->calls;
+        if (ctx->dtype == SV_DTYPE_BF16) {
+            if (vec) {
+                r = greedy ? launch<uint16_t, true, true>(ctx, q, s) : launch<uint16_t, false, true>(ctx, q, s);
+            } else {
+                r = greedy ? launch<uint16_t, true, false>(ctx, q, s) : launch<uint16_t, false, false>(ctx, q, s);
+            }
         } else {
-            r = greedy ? launch<uint16_t, true, false>(ctx, p, s) : launch<uint16_t, false, false>(ctx, p, s);
-        }
-    } else {
-        if (vec) {
-            r = greedy ? launch<float, true, true>(ctx, p, s) : launch<float, false, true>(ctx, p, s);
-        } else {
-            r = greedy ? launch<float, true, false>(ctx, p, s) : launch<float, false, false>(ctx, p, s);
+            if (vec) {
+                r = greedy ? launch<float, true, true>(ctx, q, s) : launch<float, false, true>(ctx, q, s);
+            } else {
+                r = greedy ? launch<float, true, false>(ctx, q, s) : launch<float, false, false>(ctx, q, s);
+            }
         }
     }
     if (prev != ctx->device) (void)hipSetDevice(prev);
