@@ -8,17 +8,17 @@
 // The ABI and its conventions are documented in include/spec_verify.h.
 //
 // Design: one persistent kernel per call; every logit byte is read from HBM
-// once by the streaming loop, and only the rows of each request's first
-// rejected position are read a second time.
+// once, and only the rows of each request's first rejected position are read
+// a second time (interleaved into the same stream).
 //  * Work unit = vocabulary chunk c of position i of request b: the chunk of
 //    target row i and, for a drafted position, the same chunk of drafter row
-//    i. Every chunk has the same size (448 data lanes x 4 sixteen-byte loads
+//    i. Every chunk has the same size (960 data lanes x 4 sixteen-byte loads
 //    per row). Units are numbered request-major, position-major, chunk-minor,
 //    so the C chunks of one position (a "team") are consecutive.
 //  * The grid is exactly the resident workgroups; workgroup w takes units
 //    w, w + G, w + 2G, ... (G = grid size >= C, so two units of one
 //    workgroup never share a team).
-//  * A workgroup is 8 waves. Waves 1-7 stream data: 16-byte loads of a unit
+//  * One workgroup of 16 waves per CU. Waves 1-15 stream data: 16-byte loads of a unit
 //    into registers, reduced per wave to the max and sum of
 //    2^((z - max) log2(e)/T) (sampled) or (max, lowest index) (greedy),
 //    posted to LDS; then the next unit's loads go out. They never wait on
@@ -32,20 +32,26 @@
 //    first argmax; sampled, p(x), q(x) and the accept test. It writes the
 //    decision word and completes the team, or queues a draw for after the
 //    loop (a rejection, or the bonus position).
-//  * After the loop (barriers allowed): each queued draw is settled -- a
-//    rejection draws only if it is its request's first, the bonus position
-//    only if nothing was rejected; the members of each first rejection
-//    re-read their chunk and publish its residual mass max(0, p - q) with the
-//    team's normalisers; the draw's owner scans the residual CDF over chunks,
-//    then the whole workgroup re-reads the one chunk that holds the threshold
-//    for the element-level scan.
+//  * First rejections: the control wave keeps its drafted units in a ring
+//    until the decisions of their request's positions tell whether the unit
+//    belongs to the request's first rejection. Such a chunk becomes a re-read
+//    job, planned into the data waves' stream like a regular unit: the data
+//    waves re-load it and reduce it to its residual mass max(0, p - q) with
+//    the team's normalisers, which the control wave publishes. The control
+//    wave plans every round a few rounds ahead (regular unit, job, or end).
+//  * After the loop (barriers allowed): chunks of first rejections the loop
+//    did not get to are re-read; then each queued draw is made only for its
+//    request's first rejection (or the bonus position when none): the owner
+//    scans the residual CDF over chunks, and the whole workgroup re-reads the
+//    one chunk that holds the threshold for the element-level scan.
 //  * Per request, the team that completes last writes the outputs.
 //  * Waiting: in the loop only the control wave waits on other workgroups,
-//    for the records of units they publish in the same pass, and a unit is
-//    published without waiting for anything but this workgroup's data waves.
-//    After the loop, each step waits only on earlier steps (or the loops) of
-//    other workgroups. Every wait is bounded (status flag on expiry) so the
-//    kernel always drains.
+//    and only for an owed decision: the records of a team whose units all
+//    precede the unit it publishes next (G >= C), so by induction on the unit
+//    index every record gets written. Pending first-rejection checks never
+//    wait. After the loop, re-reads wait only on decisions (taken in loops)
+//    and draws only on residual masses (published in loops or re-reads).
+//    Every wait is bounded (status flag on expiry) so the kernel drains.
 //  * Synchronisation uses device-scope relaxed atomics (plus s_waitcnt where
 //    a counter orders earlier stores), never release/acquire fences: those
 //    write back and invalidate the whole L2.
@@ -66,12 +72,19 @@ namespace {
 // of a workgroup's waves (with 5 waves, the hardware reserves two wave slots
 // per SIMD per workgroup and fewer workgroups fit than the occupancy query
 // reports).
-constexpr int kWaves = 8;                      // wave 0: control; waves 1-7: data
+constexpr int kWaves = 16;                     // wave 0: control; waves 1-15: data
 constexpr int kThreads = kWaves * 64;
 constexpr int kDataWaves = kWaves - 1;
 constexpr int kDataThreads = kDataWaves * 64;
 constexpr int kG = 4;                          // 16-byte groups per data lane per row of a unit
 constexpr int kLaunchBatch = 8192;             // requests per launch (unit offsets live in LDS)
+constexpr int kPlanLead = 4;                   // rounds the control wave plans ahead
+constexpr int kPlanSlots = 8;                  // plan ring (> kPlanLead + 1)
+constexpr int kPendSlots = 16;                 // drafted units awaiting first-rejection status
+constexpr int kJobSlots = 8;                   // re-read jobs ready to plan
+constexpr int kFirstSlots = 8;                 // first rejections whose normalisers are to load
+constexpr int kOwedSlots = 8;                  // chunk-0 units whose decision is owed
+constexpr int PL_END = 0, PL_UNIT = 1, PL_JOB = 2;
 constexpr int kScanElems = kDataThreads * 8;   // elements per scan sub-tile
 constexpr int kMaxSub = 4;                     // sub-tiles per chunk
 constexpr int kTeamWords = 32;                 // words per team record (128 bytes)
@@ -81,7 +94,6 @@ constexpr unsigned kLdsSpinLimit = 1u << 26;   // bounded LDS mailbox wait (~3 s
 
 // Team record words.
 constexpr int TW_DEC = 2;       // 64-bit decision: (epoch << 32) | accepted (words 2-3)
-constexpr int TW_DRAW = 4;      // 64-bit: (epoch << 32) | 1 if the team's deferred draw is made
 
 // Unit record: 8 64-bit words.
 //   sampled: word f = (value bits << 32) | epoch for the fp32 values
@@ -92,7 +104,6 @@ constexpr int TW_DRAW = 4;      // 64-bit: (epoch << 32) | 1 if the team's defer
 constexpr int kRecWords = 8;
 constexpr int R_MT = 0, R_MD = 1, R_ST = 2, R_SD = 3, R_RES = 4;
 constexpr int kStatWords = 4;   // words R_MT..R_SD make a record complete
-constexpr int kMaxChunks = 192; // chunks per row the team merge supports
 
 // Philox4x32 constants (Salmon et al., SC'11): round multipliers and the key
 // increments applied between rounds.
@@ -156,12 +167,6 @@ __device__ __forceinline__ void drain() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-__device__ __forceinline__ unsigned long long as_u64(double d) {
-    return (unsigned long long)__double_as_longlong(d);
-}
-__device__ __forceinline__ double as_f64(unsigned long long u) {
-    return __longlong_as_double((long long)u);
-}
 
 // Epoch-tagged 32-bit value.
 __device__ __forceinline__ unsigned long long tagged(float v, unsigned ep) {
@@ -274,9 +279,18 @@ __device__ __forceinline__ bool aligned16(const void* p) {
 // mailboxes (a tag is written after its payload; LDS operations of one wave
 // complete in order, so a reader that sees the tag sees the payload).
 struct Shared {
-    // Data wave -> control wave: a unit's per-wave statistics, by round parity.
-    //   sampled: (max, sum of 2^((z - max) c)) of the target and drafter parts
-    //   greedy:  (max, lowest index of the max) of the target part
+    // Control wave -> data waves: the plan of data round q, written kPlanLead
+    // rounds ahead into slot q % kPlanSlots: a regular unit (the next one of
+    // the workgroup's sequence), a re-read job (a chunk of a first rejection,
+    // with its team's normalisers), or the end of the loop.
+    int pl_tag[kPlanSlots];
+    int pl_kind[kPlanSlots];
+    int pl_u[kPlanSlots];
+    float pl_mt[kPlanSlots], pl_md[kPlanSlots], pl_ist[kPlanSlots], pl_isd[kPlanSlots];
+    // Data wave -> control wave: a round's per-wave results, by round parity.
+    //   regular, sampled: (max, sum of 2^((z - max) c)) of the target and
+    //                     drafter parts; greedy: (max, lowest index of the max)
+    //   job: the part's residual mass in st_st
     float st_mt[2][kDataWaves];
     float st_md[2][kDataWaves];
     double st_st[2][kDataWaves];
@@ -284,6 +298,14 @@ struct Shared {
     int st_idx[2][kDataWaves];
     int st_tag[2][kDataWaves];                   // round + 1
     int st_done[2];                              // control wave: round + 1 of the slot it read last
+    // Control wave only (rings): drafted units whose first-rejection status
+    // is not known yet, first rejections whose normalisers are to be loaded,
+    // chunk-0 units whose decision is owed, and re-read jobs ready to plan.
+    int pd_u[kPendSlots];
+    int fr_u[kFirstSlots];
+    int ow_u[kOwedSlots], ow_x[kOwedSlots];
+    int jq_u[kJobSlots];
+    float jq_mt[kJobSlots], jq_md[kJobSlots], jq_ist[kJobSlots], jq_isd[kJobSlots];
     // Set once a bounded wait expired: every later wait returns at once.
     int abort_wait;
     // After the loop: deferred draws of this workgroup and the one at hand.
@@ -292,8 +314,8 @@ struct Shared {
     int tk_chunk, tk_mode;                       // mode: 0 target row, 1 residual
     double tk_thr;
     float tk_mt, tk_md, tk_ist, tk_isd;
-    // After the loop: chunks of first rejections to re-read for their
-    // residual mass (round indices of this workgroup), and the one at hand.
+    // After the loop: chunks of first rejections still to re-read (round
+    // indices of this workgroup), and the one at hand.
     int rr_n;
     int rr_round[64];
     int rr_b, rr_i, rr_c, rr_tr;
@@ -588,35 +610,41 @@ __device__ void team_complete(const Params& P, int b, int k) {
 template <bool kGreedy>
 __device__ __forceinline__ constexpr int rec_words() { return kGreedy ? 2 : kStatWords; }
 
-// A team's C records as one control-wave load: lane l holds chunks l, l + 64,
-// l + 128 (C <= kMaxChunks).
+// A team's C records as one control-wave load: lane l holds chunk l in
+// registers; chunks 64 and up (vocabularies of more than 64 chunks) are read
+// again where they are needed.
 struct TeamPoll {
-    unsigned long long w[kMaxChunks / 64][kStatWords];
+    unsigned long long w[kStatWords];
+    int tr;
 };
+
+__device__ __forceinline__ unsigned long long* team_rec(const Params& P, int tr) {
+    return P.rec + (size_t)tr * P.C * kRecWords;
+}
 
 template <bool kGreedy>
 __device__ __forceinline__ void poll_issue(const Params& P, int tr, TeamPoll& pl) {
     const int lane = threadIdx.x & 63;
-    const int C = P.C;
-    unsigned long long* rec = P.rec + (size_t)tr * C * kRecWords;
+    unsigned long long* rec = team_rec(P, tr);
+    pl.tr = tr;
     #pragma unroll
-    for (int q = 0; q < kMaxChunks / 64; ++q) {
-        const int cc = lane + 64 * q;
-        #pragma unroll
-        for (int f = 0; f < rec_words<kGreedy>(); ++f) {
-            pl.w[q][f] = cc < C ? ld64(rec + cc * kRecWords + f) : (unsigned long long)P.epoch;
-        }
+    for (int f = 0; f < rec_words<kGreedy>(); ++f) {
+        pl.w[f] = lane < P.C ? ld64(rec + lane * kRecWords + f) : (unsigned long long)P.epoch;
     }
 }
 
 // True when every record word of the team carries this call's epoch.
 template <bool kGreedy>
 __device__ __forceinline__ bool poll_complete(const Params& P, const TeamPoll& pl) {
+    const int lane = threadIdx.x & 63;
     bool ok = true;
     #pragma unroll
-    for (int q = 0; q < kMaxChunks / 64; ++q) {
-        #pragma unroll
-        for (int f = 0; f < rec_words<kGreedy>(); ++f) ok = ok && tag_ok(pl.w[q][f], P.epoch);
+    for (int f = 0; f < rec_words<kGreedy>(); ++f) ok = ok && tag_ok(pl.w[f], P.epoch);
+    if (P.C > 64) {
+        unsigned long long* rec = team_rec(P, pl.tr);
+        for (int cc = lane + 64; cc < P.C; cc += 64) {
+            for (int f = 0; f < rec_words<kGreedy>(); ++f) ok = ok && tag_ok(ld64(rec + cc * kRecWords + f), P.epoch);
+        }
     }
     return __ballot(!ok) == 0;
 }
@@ -647,24 +675,27 @@ struct TeamStats {
 __device__ TeamStats team_stats(const Params& P, const TeamPoll& pl) {
     const int lane = threadIdx.x & 63;
     const int C = P.C;
+    unsigned long long* rec = team_rec(P, pl.tr);
     float mt = -INFINITY, md = -INFINITY;
-    #pragma unroll
-    for (int q = 0; q < kMaxChunks / 64; ++q) {
-        if (lane + 64 * q < C) {
-            mt = fmaxf(mt, tag_val(pl.w[q][R_MT]));
-            md = fmaxf(md, tag_val(pl.w[q][R_MD]));
-        }
+    if (lane < C) {
+        mt = tag_val(pl.w[R_MT]);
+        md = tag_val(pl.w[R_MD]);
+    }
+    for (int cc = lane + 64; cc < C; cc += 64) {
+        mt = fmaxf(mt, tag_val(ld64(rec + cc * kRecWords + R_MT)));
+        md = fmaxf(md, tag_val(ld64(rec + cc * kRecWords + R_MD)));
     }
     mt = wave_max(mt);
     md = wave_max(md);
     double st = 0.0, sd = 0.0;
-    #pragma unroll
-    for (int q = 0; q < kMaxChunks / 64; ++q) {
-        if (lane + 64 * q < C) {
-            const float s1 = tag_val(pl.w[q][R_ST]), s2 = tag_val(pl.w[q][R_SD]);
-            if (s1 > 0.0f) st += (double)s1 * exp2(((double)tag_val(pl.w[q][R_MT]) - (double)mt) * P.c64);
-            if (s2 > 0.0f) sd += (double)s2 * exp2(((double)tag_val(pl.w[q][R_MD]) - (double)md) * P.c64);
-        }
+    auto add = [&](float m1, float m2, float s1, float s2) {
+        if (s1 > 0.0f) st += (double)s1 * exp2(((double)m1 - (double)mt) * P.c64);
+        if (s2 > 0.0f) sd += (double)s2 * exp2(((double)m2 - (double)md) * P.c64);
+    };
+    if (lane < C) add(tag_val(pl.w[R_MT]), tag_val(pl.w[R_MD]), tag_val(pl.w[R_ST]), tag_val(pl.w[R_SD]));
+    for (int cc = lane + 64; cc < C; cc += 64) {
+        add(tag_val(ld64(rec + cc * kRecWords + R_MT)), tag_val(ld64(rec + cc * kRecWords + R_MD)),
+            tag_val(ld64(rec + cc * kRecWords + R_ST)), tag_val(ld64(rec + cc * kRecWords + R_SD)));
     }
     TeamStats t;
     t.mt = mt;
@@ -674,7 +705,7 @@ __device__ TeamStats team_stats(const Params& P, const TeamPoll& pl) {
     return t;
 }
 
-// Blocking wait and merge (deferred draws).
+// Blocking wait and merge.
 __device__ TeamStats merge_team(const Params& P, Shared& sh, int tr) {
     TeamPoll pl;
     poll_wait<false>(P, sh, tr, pl);
@@ -686,18 +717,20 @@ __device__ TeamStats merge_team(const Params& P, Shared& sh, int tr) {
 __device__ void decide_greedy(const Params& P, const TeamPoll& pl, int b, int i, int k, int tr) {
     const int lane = threadIdx.x & 63;
     const int C = P.C;
+    unsigned long long* rec = team_rec(P, tr);
     float bv = -INFINITY;
     int bi = INT_MAX;
-    #pragma unroll
-    for (int q = 0; q < kMaxChunks / 64; ++q) {
-        if (lane + 64 * q < C) {
-            const float v = tag_val(pl.w[q][R_MT]);
-            const int idx = (int)(unsigned)(pl.w[q][R_MD] >> 32);
-            if (better_arg(v, idx, bv, bi)) {
-                bv = v;
-                bi = idx;
-            }
+    auto take = [&](unsigned long long wm, unsigned long long wi) {
+        const float v = tag_val(wm);
+        const int idx = (int)(unsigned)(wi >> 32);
+        if (better_arg(v, idx, bv, bi)) {
+            bv = v;
+            bi = idx;
         }
+    };
+    if (lane < C) take(pl.w[R_MT], pl.w[R_MD]);
+    for (int cc = lane + 64; cc < C; cc += 64) {
+        take(ld64(rec + cc * kRecWords + R_MT), ld64(rec + cc * kRecWords + R_MD));
     }
     #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
@@ -903,69 +936,252 @@ __device__ __forceinline__ void owed_decide(const Params& P, const Owed& o, cons
     if (!accept) add_task(P, u.tr, false, ntasks);
 }
 
-// The control wave's loop, round r:
-//  A. a decision still owed for the unit of round r - 2 (its team was
-//     incomplete when last polled): wait for the records and decide;
-//  B. poll the team of the chunk-0 unit of round r - 1; decide if complete;
-//  C. the unit of round r: statistics from the data waves, publish;
-//  D. the unit of round r - 1 still undecided: poll again, decide if
-//     complete, else it is owed (A of the next round).
-// Nothing the data waves do waits on a decision.
+// -------------------------------------------------------------- planning --
+
+// Decision words of up to two positions' prefixes, one per half-wave: lanes
+// 0..31 read positions 0..i of request b (first candidate), lanes 32..63 the
+// second candidate's. Issued in one round, read in the same round after the
+// mailbox work.
+__device__ __forceinline__ unsigned long long prefix_issue(const Params& P, int b, int i, bool valid,
+                                                           int half) {
+    const int lane = threadIdx.x & 63;
+    const int t = lane - 32 * half;
+    if (valid && t >= 0 && t < 32 && t <= i) return ld64(dec_word(P, b * (P.K + 1) + t));
+    return 0;
+}
+
+// First-rejection status from a half-wave's loaded decision words (see
+// prefix_issue): 1 = position i rejected and every earlier one accepted,
+// 0 = not, -1 = not known yet.
+__device__ __forceinline__ int prefix_status(const Params& P, unsigned long long d, int i, int half) {
+    const int lane = threadIdx.x & 63;
+    const int t = lane - 32 * half;
+    const bool mine = t >= 0 && t < 32 && t <= i;
+    const bool known = !mine || (unsigned)(d >> 32) == P.epoch;
+    const unsigned long long rej = __ballot(mine && known && (d & 1ull) == 0) >> (32 * half);
+    const unsigned long long unknown = (__ballot(!known) >> (32 * half)) & 0xFFFFFFFFull;
+    if (rej != 0) {
+        const unsigned long long low = rej & (~rej + 1);
+        if ((unknown & (low - 1)) != 0) return -1;
+        return low == (1ull << i) ? 1 : 0;
+    }
+    return unknown == 0 ? 0 : -1;
+}
+
+// Control wave state of the streaming loop (uniform).
+struct CtrlState {
+    int next_unit;          // next regular unit of this workgroup's sequence
+    int planned;            // rounds planned so far (plans 0 .. planned-1 exist)
+    int end_round;          // round planned as the end (INT_MAX: not yet)
+    int pd_head, pd_tail;   // pending ring: drafted units awaiting first-rejection status
+    int fr_head, fr_tail;   // first-rejection ring: units whose team stats are to be loaded
+    int jq_head, jq_tail;   // job ring: re-read jobs ready to plan
+    int ow_head, ow_tail;   // owed ring: chunk-0 units whose team was incomplete when polled
+};
+
+// Control wave: write the plan of the next round: a ready re-read job, else
+// the next regular unit, else the end.
+__device__ __forceinline__ void plan_next(const Params& P, Shared& sh, CtrlState& cs, int U) {
+    const int q = cs.planned++;
+    const int slot = q % kPlanSlots;
+    int kind;
+    if (cs.jq_head != cs.jq_tail) {
+        kind = PL_JOB;
+        const int j = cs.jq_head++ % kJobSlots;
+        if ((threadIdx.x & 63) == 0) {
+            sh.pl_u[slot] = sh.jq_u[j];
+            sh.pl_mt[slot] = sh.jq_mt[j];
+            sh.pl_md[slot] = sh.jq_md[j];
+            sh.pl_ist[slot] = sh.jq_ist[j];
+            sh.pl_isd[slot] = sh.jq_isd[j];
+        }
+    } else if (cs.next_unit < U) {
+        kind = PL_UNIT;
+        if ((threadIdx.x & 63) == 0) sh.pl_u[slot] = cs.next_unit;
+        cs.next_unit += gridDim.x;
+    } else {
+        kind = PL_END;
+        cs.end_round = q;
+    }
+    if ((threadIdx.x & 63) == 0) {
+        sh.pl_kind[slot] = kind;
+        order();
+        lds_put(&sh.pl_tag[slot], q);
+    }
+}
+
+// Push/pop helpers of the LDS rings (the control wave owns them; indices
+// live in registers, uniform).
+__device__ __forceinline__ void ring_put(int* ring, int slots, int& tail, int v) {
+    if ((threadIdx.x & 63) == 0) ring[tail % slots] = v;
+    ++tail;
+}
+
+// The control wave's loop. Every round issues all of its device-scope loads
+// first, does the mailbox work while they are in flight, then reads them:
+//  P. plan round r + kPlanLead (the data waves read it at the end of round
+//     r + kPlanLead - 1, by which time this write is always done);
+//  1. issue: the team records of the chunk-0 unit consumed last round and of
+//     the oldest owed one (decisions), the decision words of the two oldest
+//     pending drafted units' request prefixes (first-rejection status), and
+//     the team records of the oldest first rejection (its normalisers);
+//  2. the data waves' results of round r: a regular unit's statistics are
+//     merged and published (a chunk-0 unit is decided next round, a drafted
+//     unit joins the pending ring); a job's residual mass is published;
+//  3. read what step 1 loaded: decide complete teams (an incomplete one is
+//     owed), settle pending units in order (a first rejection goes to the
+//     first-rejection ring), turn a loaded first rejection into a job.
+// After the last round, owed decisions are waited for. Nothing the data
+// waves do waits on a decision.
 template <typename E, bool kGreedy, bool kVec>
 __device__ __forceinline__ int control_loop(const Params& P, Shared& sh, const int* off) {
     const int U = off[P.B];
-    const int G = gridDim.x;
-    Unit cur = decode_unit(P, off, blockIdx.x, U, kGreedy);
-    Owed prev, owed;
-    prev.u.u = -1;
-    owed.u.u = -1;
+    CtrlState cs;
+    cs.next_unit = blockIdx.x;
+    cs.planned = 0;
+    cs.end_round = INT_MAX;
+    cs.pd_head = cs.pd_tail = 0;
+    cs.fr_head = cs.fr_tail = 0;
+    cs.jq_head = cs.jq_tail = 0;
+    cs.ow_head = cs.ow_tail = 0;
+    for (int q = 0; q < kPlanLead && cs.end_round == INT_MAX; ++q) plan_next(P, sh, cs, U);
+    Owed fresh;                      // chunk-0 unit consumed last round, to decide now
+    fresh.u.u = -1;
     int ntasks = 0;
-    TeamPoll pl;
-    for (int r = 0; cur.u >= 0 || prev.u.u >= 0 || owed.u.u >= 0; ++r) {
-        // A.
-        if (owed.u.u >= 0) {
-            owed_issue<E, kGreedy>(P, owed, pl);
-            if (!poll_complete<kGreedy>(P, pl)) poll_wait<kGreedy>(P, sh, owed.u.tr, pl);
-            owed_decide<kGreedy>(P, owed, pl, ntasks);
-            owed.u.u = -1;
+    TeamPoll pa, pb, pc;
+    for (int r = 0; r < cs.end_round; ++r) {
+        // P.
+        if (cs.end_round == INT_MAX && r + kPlanLead == cs.planned) plan_next(P, sh, cs, U);
+        // 1.
+        const bool have_a = fresh.u.u >= 0;
+        if (have_a) owed_issue<E, kGreedy>(P, fresh, pa);
+        Owed old;
+        old.u.u = -1;
+        if (cs.ow_head != cs.ow_tail) {
+            const int j = cs.ow_head % kOwedSlots;
+            old.u = decode_unit(P, off, sh.ow_u[j], U, kGreedy);
+            old.x = sh.ow_x[j];
+            owed_issue<E, kGreedy>(P, old, pb);
         }
-        // B.
-        bool pending = false;
-        if (prev.u.u >= 0) {
-            owed_issue<E, kGreedy>(P, prev, pl);
-            if (poll_complete<kGreedy>(P, pl)) {
-                owed_decide<kGreedy>(P, prev, pl, ntasks);
-            } else {
-                pending = true;
-            }
+        Unit c0, c1;
+        c0.u = c1.u = -1;
+        unsigned long long dw = 0;
+        if (!kGreedy) {
+            if (cs.pd_head != cs.pd_tail) c0 = decode_unit(P, off, sh.pd_u[cs.pd_head % kPendSlots], U, false);
+            if (cs.pd_tail - cs.pd_head >= 2)
+                c1 = decode_unit(P, off, sh.pd_u[(cs.pd_head + 1) % kPendSlots], U, false);
+            dw = prefix_issue(P, c0.b, c0.i, c0.u >= 0, 0) | prefix_issue(P, c1.b, c1.i, c1.u >= 0, 1);
         }
-        // C.
+        Unit fj;
+        fj.u = -1;
+        if (!kGreedy && cs.fr_head != cs.fr_tail && cs.jq_tail - cs.jq_head < kJobSlots) {
+            fj = decode_unit(P, off, sh.fr_u[cs.fr_head % kFirstSlots], U, false);
+            poll_issue<false>(P, fj.tr, pc);
+        }
+        // 2.
         Owed next;
         next.u.u = -1;
-        if (cur.u >= 0) {
-            control_unit<E, kGreedy>(P, sh, cur, r, ntasks);
-            if (cur.c == 0 && (kGreedy || cur.has_d)) {
-                next.u = cur;
-                next.x = kGreedy ? 0 : P.tokens[(size_t)cur.b * P.K + cur.i];
-            }
-            cur = decode_unit(P, off, cur.u + G, U, kGreedy);
-        }
-        // D.
-        if (pending) {
-            poll_issue<kGreedy>(P, prev.u.tr, pl);
-            if (poll_complete<kGreedy>(P, pl)) {
-                owed_decide<kGreedy>(P, prev, pl, ntasks);
+        {
+            const int slot = r % kPlanSlots;
+            const int kind = sh.pl_kind[slot];
+            const Unit cur = decode_unit(P, off, sh.pl_u[slot], U, kGreedy);
+            if (kind == PL_UNIT) {
+                control_unit<E, kGreedy>(P, sh, cur, r, ntasks);
+                if (cur.c == 0 && (kGreedy || cur.has_d)) {
+                    next.u = cur;
+                    next.x = kGreedy ? 0 : P.tokens[(size_t)cur.b * P.K + cur.i];
+                }
+                if (!kGreedy && cur.has_d) {
+                    if (cs.pd_tail - cs.pd_head >= kPendSlots) ++cs.pd_head;   // oldest left to after the loop
+                    ring_put(sh.pd_u, kPendSlots, cs.pd_tail, cur.u);
+                }
             } else {
-                owed = prev;
+                // A job's residual mass: one partial per data wave.
+                const int lane = threadIdx.x & 63;
+                const int rs = r & 1;
+                double v = 0.0;
+                if (lane < kDataWaves) {
+                    lds_wait(P, sh, &sh.st_tag[rs][lane], r + 1);
+                    v = sh.st_st[rs][lane];
+                }
+                order();
+                if (lane == 0) lds_put(&sh.st_done[rs], r + 1);
+                v = wave_sum(v);
+                if (lane == 0) {
+                    st64(P.rec + ((size_t)cur.tr * P.C + cur.c) * kRecWords + R_RES,
+                         tagged((float)v, P.epoch));
+                }
             }
         }
-        prev = next;
+        // 3.
+        if (have_a) {
+            if (poll_complete<kGreedy>(P, pa)) {
+                owed_decide<kGreedy>(P, fresh, pa, ntasks);
+            } else if (cs.ow_tail - cs.ow_head < kOwedSlots) {
+                if ((threadIdx.x & 63) == 0) sh.ow_x[cs.ow_tail % kOwedSlots] = fresh.x;
+                ring_put(sh.ow_u, kOwedSlots, cs.ow_tail, fresh.u.u);
+            } else {
+                poll_wait<kGreedy>(P, sh, fresh.u.tr, pa);   // ring full: wait (rare)
+                owed_decide<kGreedy>(P, fresh, pa, ntasks);
+            }
+        }
+        if (old.u.u >= 0 && poll_complete<kGreedy>(P, pb)) {
+            owed_decide<kGreedy>(P, old, pb, ntasks);
+            ++cs.ow_head;
+        }
+        fresh = next;
+        if (!kGreedy) {
+            if (c0.u >= 0) {
+                const int s0 = prefix_status(P, dw, c0.i, 0);
+                if (s0 >= 0) {
+                    ++cs.pd_head;
+                    if (s0 == 1 && cs.fr_tail - cs.fr_head < kFirstSlots) ring_put(sh.fr_u, kFirstSlots, cs.fr_tail, c0.u);
+                    if (c1.u >= 0) {
+                        const int s1 = prefix_status(P, dw, c1.i, 1);
+                        if (s1 >= 0) {
+                            ++cs.pd_head;
+                            if (s1 == 1 && cs.fr_tail - cs.fr_head < kFirstSlots) ring_put(sh.fr_u, kFirstSlots, cs.fr_tail, c1.u);
+                        }
+                    }
+                }
+            }
+            if (fj.u >= 0 && poll_complete<false>(P, pc)) {
+                const TeamStats ts = team_stats(P, pc);
+                const int j = cs.jq_tail++ % kJobSlots;
+                if ((threadIdx.x & 63) == 0) {
+                    sh.jq_u[j] = fj.u;
+                    sh.jq_mt[j] = ts.mt;
+                    sh.jq_md[j] = ts.md;
+                    sh.jq_ist[j] = (float)(1.0 / ts.st);
+                    sh.jq_isd[j] = (float)(1.0 / ts.sd);
+                }
+                ++cs.fr_head;
+            }
+        }
+    }
+    // Decisions still owed: wait for their records.
+    TeamPoll pl;
+    if (fresh.u.u >= 0) {
+        poll_wait<kGreedy>(P, sh, fresh.u.tr, pl);
+        owed_issue<E, kGreedy>(P, fresh, pl);
+        owed_decide<kGreedy>(P, fresh, pl, ntasks);
+    }
+    while (cs.ow_head != cs.ow_tail) {
+        const int j = cs.ow_head % kOwedSlots;
+        Owed o;
+        o.u = decode_unit(P, off, sh.ow_u[j], U, kGreedy);
+        o.x = sh.ow_x[j];
+        poll_wait<kGreedy>(P, sh, o.u.tr, pl);
+        owed_issue<E, kGreedy>(P, o, pl);
+        owed_decide<kGreedy>(P, o, pl, ntasks);
+        ++cs.ow_head;
     }
     return ntasks;
 }
 
-// The data waves' loop: stream units through registers, post per-wave
-// statistics to the control wave, load the next unit.
+// The data waves' loop: each round reads its plan, reduces the unit in
+// registers (or, for a job, its residual mass), issues the loads of the next
+// planned round, and posts its results to the control wave.
 template <typename E, bool kGreedy, bool kVec>
 __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int* off) {
     constexpr int W = Elem<E>::W;
@@ -973,16 +1189,56 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
     const int dw = (threadIdx.x >> 6) - 1;         // data wave index
     const int dt = threadIdx.x - 64;               // data thread index
     const int U = off[P.B];
-    const int G = gridDim.x;
     const float cs = P.c32;
 
+    // The plan of round q (the control wave wrote it long before).
+    auto read_plan = [&](int q, Unit& u, int& kind) __attribute__((always_inline)) {
+        const int slot = q % kPlanSlots;
+        lds_wait(P, sh, &sh.pl_tag[slot], q);
+        kind = sh.pl_kind[slot];
+        u = decode_unit(P, off, kind == PL_END ? U : sh.pl_u[slot], U, kGreedy);
+        if (kind == PL_JOB) u.has_d = true;
+    };
+
     uint4 gt[kG], gd[kG];
-    Unit cur = decode_unit(P, off, blockIdx.x, U, kGreedy);
-    if (cur.u >= 0) issue_loads<E, kVec>(P, cur, dt, gt, gd);
-    for (int r = 0; cur.u >= 0; ++r) {
+    Unit cur;
+    int kind;
+    read_plan(0, cur, kind);
+    if (kind == PL_END) return;
+    issue_loads<E, kVec>(P, cur, dt, gt, gd);
+    for (int r = 0;; ++r) {
         const int slot = r & 1;
-        const Unit nxt = decode_unit(P, off, cur.u + G, U, kGreedy);
-        if (kGreedy) {
+        const int ps = r % kPlanSlots;
+        Unit nxt;
+        int nkind;
+        double post_a = 0.0, post_b = 0.0;
+        float post_mt = -INFINITY, post_md = -INFINITY;
+        int post_idx = INT_MAX;
+        if (!kGreedy && kind == PL_JOB) {
+            // Residual mass of the chunk with the team's normalisers.
+            const float mt = sh.pl_mt[ps], md = sh.pl_md[ps];
+            const float ist = sh.pl_ist[ps], isd = sh.pl_isd[ps];
+            float lr = 0.0f;
+            #pragma unroll
+            for (int j = 0; j < kG; ++j) {
+                float m8[W];
+                #pragma unroll
+                for (int kk = 0; kk < W; ++kk) {
+                    const float pv = fast_exp2((Elem<E>::at(gt[j], kk) - mt) * cs) * ist;
+                    const float qv = fast_exp2((Elem<E>::at(gd[j], kk) - md) * cs) * isd;
+                    m8[kk] = fmaxf(0.0f, pv - qv);
+                }
+                #pragma unroll
+                for (int h = W / 2; h > 0; h >>= 1) {
+                    #pragma unroll
+                    for (int kk = 0; kk < h; ++kk) m8[kk] += m8[kk + h];
+                }
+                lr += m8[0];
+            }
+            read_plan(r + 1, nxt, nkind);
+            if (nkind != PL_END) issue_loads<E, kVec>(P, nxt, dt, gt, gd);
+            post_a = wave_sum((double)lr);
+        } else if (kGreedy) {
             float bv = -INFINITY;
             int bi = INT_MAX;
             #pragma unroll
@@ -996,7 +1252,8 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
                     }
                 }
             }
-            if (nxt.u >= 0) issue_loads<E, kVec>(P, nxt, dt, gt, gd);
+            read_plan(r + 1, nxt, nkind);
+            if (nkind != PL_END) issue_loads<E, kVec>(P, nxt, dt, gt, gd);
             #pragma unroll
             for (int o = 32; o > 0; o >>= 1) {
                 const float ov = __shfl_xor(bv, o, 64);
@@ -1006,13 +1263,8 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
                     bi = oi;
                 }
             }
-            if (lane == 0) {
-                if (r >= 2) lds_wait(P, sh, &sh.st_done[slot], r - 1);
-                sh.st_mt[slot][dw] = bv;
-                sh.st_idx[slot][dw] = bi;
-                order();
-                lds_put(&sh.st_tag[slot][dw], r + 1);
-            }
+            post_mt = bv;
+            post_idx = bi;
         } else {
             float mt = -INFINITY, md = -INFINITY;
             #pragma unroll
@@ -1062,20 +1314,26 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
                 }
             }
             // The unit's data is consumed: stream the next one.
-            if (nxt.u >= 0) issue_loads<E, kVec>(P, nxt, dt, gt, gd);
-            const double st = wave_sum((double)lt);
-            const double sd = wave_sum((double)ld);
-            if (lane == 0) {
-                if (r >= 2) lds_wait(P, sh, &sh.st_done[slot], r - 1);
-                sh.st_mt[slot][dw] = mt;
-                sh.st_md[slot][dw] = md;
-                sh.st_st[slot][dw] = st;
-                sh.st_sd[slot][dw] = sd;
-                order();
-                lds_put(&sh.st_tag[slot][dw], r + 1);
-            }
+            read_plan(r + 1, nxt, nkind);
+            if (nkind != PL_END) issue_loads<E, kVec>(P, nxt, dt, gt, gd);
+            post_a = wave_sum((double)lt);
+            post_b = wave_sum((double)ld);
+            post_mt = mt;
+            post_md = md;
         }
+        if (lane == 0) {
+            if (r >= 2) lds_wait(P, sh, &sh.st_done[slot], r - 1);
+            sh.st_mt[slot][dw] = post_mt;
+            sh.st_md[slot][dw] = post_md;
+            sh.st_st[slot][dw] = post_a;
+            sh.st_sd[slot][dw] = post_b;
+            sh.st_idx[slot][dw] = post_idx;
+            order();
+            lds_put(&sh.st_tag[slot][dw], r + 1);
+        }
+        if (nkind == PL_END) break;
         cur = nxt;
+        kind = nkind;
     }
 }
 
@@ -1109,31 +1367,9 @@ __device__ bool earlier_accepted(const Params& P, Shared& sh, int b, int i) {
     }
 }
 
-__device__ __forceinline__ unsigned long long* draw_word(const Params& P, int tr) {
-    return reinterpret_cast<unsigned long long*>(P.team + (size_t)tr * kTeamWords + TW_DRAW);
-}
-
-// Control wave, step 1: settle this workgroup's deferred draws. A rejected
-// position draws only if it is the request's first rejection; the bonus
-// position only if every drafted position was accepted. The answer goes to
-// the team's draw word, which the chunk members read in step 2.
-__device__ void settle_tasks(const Params& P, Shared& sh, int nt) {
-    const int K = P.K;
-    unsigned* list = reinterpret_cast<unsigned*>(P.tasks) + (size_t)blockIdx.x * P.task_cap;
-    for (int t = 0; t < nt; ++t) {
-        const int task = (int)ld32(list + t);
-        const int tr = task >> 1;
-        const int b = tr / (K + 1), i = tr - b * (K + 1);
-        const bool draw = earlier_accepted(P, sh, b, i);
-        if ((threadIdx.x & 63) == 0) {
-            st64(draw_word(P, tr), ((unsigned long long)P.epoch << 32) | (draw ? 1u : 0u));
-        }
-    }
-}
-
-// Control wave, step 2: which of this workgroup's drafted units (rounds
-// base .. base+63, lane = round - base) belong to a request's first
-// rejection? Those chunks are re-read for their residual mass.
+// Control wave: which of this workgroup's drafted units (rounds base ..
+// base+63 of its regular sequence, lane = round - base) are chunks of a
+// request's first rejection whose residual mass is not published yet?
 template <bool kGreedy>
 __device__ void scan_members(const Params& P, Shared& sh, const int* off, int base) {
     const int lane = threadIdx.x & 63;
@@ -1142,21 +1378,31 @@ __device__ void scan_members(const Params& P, Shared& sh, const int* off, int ba
     const Unit u = decode_unit(P, off, blockIdx.x + (base + lane) * gridDim.x, U, kGreedy);
     bool need = false;
     if (u.u >= 0 && u.has_d) {
-        bool settled = false;
-        for (unsigned it = 0; !settled; ++it) {
-            const unsigned long long d = ld64(dec_word(P, u.tr));
-            if ((unsigned)(d >> 32) == ep) {
-                if (d & 1ull) {
-                    settled = true;                            // accepted: no residual
-                } else {
-                    const unsigned long long w = ld64(draw_word(P, u.tr));
-                    if ((unsigned)(w >> 32) == ep) {
-                        settled = true;
-                        need = (w & 1ull) != 0;
+        const unsigned long long rw =
+            ld64(P.rec + ((size_t)u.tr * P.C + u.c) * kRecWords + R_RES);
+        if (!tag_ok(rw, ep)) {
+            // Position u.i is the first rejection iff it is rejected and every
+            // earlier position accepted (bounded wait for their decisions).
+            const int K = P.K;
+            for (unsigned it = 0;; ++it) {
+                int status = -1;                           // -1 unknown, 0 not first, 1 first
+                for (int t = 0; t <= u.i; ++t) {
+                    const unsigned long long d = ld64(dec_word(P, u.b * (K + 1) + t));
+                    if ((unsigned)(d >> 32) != ep) {
+                        status = -1;
+                        break;
                     }
+                    const bool rej = (d & 1ull) == 0;
+                    if (t < u.i && rej) {
+                        status = 0;
+                        break;
+                    }
+                    if (t == u.i) status = rej ? 1 : 0;
                 }
-            }
-            if (!settled) {
+                if (status >= 0) {
+                    need = status == 1;
+                    break;
+                }
                 if (it >= kSpinLimit || lds_get(&sh.abort_wait)) {
                     give_up(P, sh);
                     break;
@@ -1245,7 +1491,9 @@ __device__ void task_prepare(const Params& P, Shared& sh, int task) {
     const int tr = task >> 1;
     const bool bonus = task & 1;
     const int b = tr / (K + 1), i = tr - b * (K + 1);
-    const bool draw = (ld64(draw_word(P, tr)) & 1ull) != 0;      // written by this workgroup
+    // A rejection draws only as its request's first; the bonus position
+    // only if every drafted position was accepted.
+    const bool draw = earlier_accepted(P, sh, b, i);
     int chunk = -1, mode = 0;
     double thr = 0.0;
     TeamStats ts;
@@ -1308,10 +1556,11 @@ __device__ void task_prepare(const Params& P, Shared& sh, int task) {
     }
 }
 
-// After both loops (whole workgroup, under barriers): settle the deferred
-// draws, re-read the chunks of first rejections for their residual mass,
-// then make the draws. Each step waits only on earlier steps of other
-// workgroups (or on their loops), so no wait is circular.
+// After both loops (whole workgroup, under barriers): re-read the chunks of
+// first rejections whose residual mass the loop did not publish, then make
+// this workgroup's draws. The re-reads wait only on decisions (taken in the
+// loops); the draws wait on residual masses (published in the loops or by
+// the re-reads), so no wait is circular.
 template <typename E, bool kVec>
 __device__ void after_loop(const Params& P, Shared& sh, const int* off) {
     const int K = P.K;
@@ -1319,9 +1568,7 @@ __device__ void after_loop(const Params& P, Shared& sh, const int* off) {
     const int nt = min(sh.ntasks, P.task_cap);
     const int U = off[P.B];
     const int rounds = (int)blockIdx.x < U ? (U - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
-    // 1.
-    if (wave == 0) settle_tasks(P, sh, nt);
-    // 2 and 3, 64 rounds at a time.
+    // Re-reads, 64 rounds of the regular sequence at a time.
     for (int base = 0; base < rounds; base += 64) {
         if (wave == 0) scan_members<false>(P, sh, off, base);
         __syncthreads();
@@ -1329,7 +1576,7 @@ __device__ void after_loop(const Params& P, Shared& sh, const int* off) {
         for (int j = 0; j < n; ++j) reread_residual<E, kVec>(P, sh, off, sh.rr_round[j]);
         __syncthreads();
     }
-    // 4.
+    // Draws.
     const E* target = static_cast<const E*>(P.target);
     const E* draft = static_cast<const E*>(P.draft);
     unsigned* list = reinterpret_cast<unsigned*>(P.tasks) + (size_t)blockIdx.x * P.task_cap;
@@ -1395,6 +1642,7 @@ void verify_kernel(Params P) {
         if (lane == 63) sh.red_i[wave] = incl;
         if (tid < 2 * kDataWaves) (&sh.st_tag[0][0])[tid] = 0;
         if (tid < 2) sh.st_done[tid] = 0;
+        if (tid < kPlanSlots) sh.pl_tag[tid] = -1;
         if (tid == 0) sh.abort_wait = 0;
         __syncthreads();
         int run = incl - local;
@@ -1575,7 +1823,6 @@ int spec_verify_init(spec_verify_ctx** out, int device, int max_batch, int max_k
         max_k > SV_MAX_K || vocab < 1 || vocab > SV_MAX_VOCAB) {
         return SV_ERR_ARG;
     }
-    if (chunks_for(vocab, dtype) > kMaxChunks) return SV_ERR_ARG;   // not reachable for legal V
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || device >= ndev) return SV_ERR_HIP;
     int prev = -1;

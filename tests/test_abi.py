@@ -55,12 +55,12 @@ def test_strerror_covers_every_code():
 
 def test_chunk_count():
     # A chunk is 256 lanes x 4 sixteen-byte loads: 8192 bf16 or 4096 fp32 values.
-    # a chunk is 448 lanes x 4 sixteen-byte groups: 14336 bf16 or 7168 fp32
-    assert sb.spec_verify_chunks(151936, sb.SV_DTYPE_BF16) == 11
-    assert sb.spec_verify_chunks(262144, sb.SV_DTYPE_BF16) == 19
-    assert sb.spec_verify_chunks(151936, sb.SV_DTYPE_F32) == 22
-    assert sb.spec_verify_chunks(14336, sb.SV_DTYPE_BF16) == 1
-    assert sb.spec_verify_chunks(14337, sb.SV_DTYPE_BF16) == 2
+    # a chunk is 960 lanes x 4 sixteen-byte groups: 30720 bf16 or 15360 fp32
+    assert sb.spec_verify_chunks(151936, sb.SV_DTYPE_BF16) == 5
+    assert sb.spec_verify_chunks(262144, sb.SV_DTYPE_BF16) == 9
+    assert sb.spec_verify_chunks(151936, sb.SV_DTYPE_F32) == 10
+    assert sb.spec_verify_chunks(30720, sb.SV_DTYPE_BF16) == 1
+    assert sb.spec_verify_chunks(30721, sb.SV_DTYPE_BF16) == 2
     assert sb.spec_verify_chunks(32, sb.SV_DTYPE_F32) == 1
     assert sb.spec_verify_chunks(0, sb.SV_DTYPE_F32) == sb.SV_ERR_ARG
     assert sb.spec_verify_chunks(32, 7) == sb.SV_ERR_DTYPE
