@@ -285,7 +285,7 @@ struct Shared {
     // with its team's normalisers), or the end of the loop.
     int pl_tag[kPlanSlots];
     int pl_kind[kPlanSlots];
-    int pl_u[kPlanSlots];
+    int pl_u[kPlanSlots], pl_b[kPlanSlots];      // unit and its request
     float pl_mt[kPlanSlots], pl_md[kPlanSlots], pl_ist[kPlanSlots], pl_isd[kPlanSlots];
     // Data wave -> control wave: a round's per-wave results, by round parity.
     //   regular, sampled: (max, sum of 2^((z - max) c)) of the target and
@@ -301,10 +301,13 @@ struct Shared {
     // Control wave only (rings): drafted units whose first-rejection status
     // is not known yet, first rejections whose normalisers are to be loaded,
     // chunk-0 units whose decision is owed, and re-read jobs ready to plan.
-    int pd_u[kPendSlots];
-    int fr_u[kFirstSlots];
-    int ow_u[kOwedSlots], ow_x[kOwedSlots];
-    int jq_u[kJobSlots];
+    int pd_u[kPendSlots], pd_b[kPendSlots];
+    int fr_u[kFirstSlots], fr_b[kFirstSlots];
+    int ow_u[kOwedSlots], ow_b[kOwedSlots], ow_x[kOwedSlots];
+    int jq_u[kJobSlots], jq_b[kJobSlots];
+    // Control wave only: requests of the next 64 units of the regular
+    // sequence (decoded 64 at a time, one per lane).
+    int seq_b[64];
     float jq_mt[kJobSlots], jq_md[kJobSlots], jq_ist[kJobSlots], jq_isd[kJobSlots];
     // Set once a bounded wait expired: every later wait returns at once.
     int abort_wait;
@@ -800,6 +803,37 @@ __device__ __forceinline__ Unit decode_unit(const Params& P, const int* off, int
     return d;
 }
 
+// The request of unit u: largest b with off[b] <= u (binary search).
+__device__ __forceinline__ int request_of(const Params& P, const int* off, int u) {
+    int lo_b = 0, hi_b = P.B;
+    while (hi_b - lo_b > 1) {
+        const int mid = (lo_b + hi_b) >> 1;
+        if (off[mid] <= u) lo_b = mid; else hi_b = mid;
+    }
+    return lo_b;
+}
+
+// The coordinates of unit u of request b (two independent LDS reads; no
+// search). u < 0 gives the empty unit.
+__device__ __forceinline__ Unit unit_from(const Params& P, const int* off, int u, int b, bool greedy) {
+    Unit d;
+    d.u = u;
+    d.b = d.i = d.k = d.c = d.tr = d.e0 = d.n = 0;
+    d.has_d = false;
+    if (u < 0) return d;
+    d.b = b;
+    const int o0 = off[b], o1 = off[b + 1];
+    const int local = u - o0;
+    d.k = (o1 - o0) / P.C - 1;
+    d.i = local / P.C;
+    d.c = local - d.i * P.C;
+    d.tr = b * (P.K + 1) + d.i;
+    d.e0 = d.c * P.CE;
+    d.n = min(P.CE, P.V - d.e0);
+    d.has_d = !greedy && d.i < d.k;
+    return d;
+}
+
 // Data waves: issue the 16-byte loads of a unit into registers (no wait).
 template <typename E, bool kVec>
 __device__ __forceinline__ void issue_loads(const Params& P, const Unit& d, int dt,
@@ -977,11 +1011,13 @@ struct CtrlState {
     int fr_head, fr_tail;   // first-rejection ring: units whose team stats are to be loaded
     int jq_head, jq_tail;   // job ring: re-read jobs ready to plan
     int ow_head, ow_tail;   // owed ring: chunk-0 units whose team was incomplete when polled
+    int seq_n;              // regular units planned so far
 };
 
 // Control wave: write the plan of the next round: a ready re-read job, else
 // the next regular unit, else the end.
-__device__ __forceinline__ void plan_next(const Params& P, Shared& sh, CtrlState& cs, int U) {
+__device__ __forceinline__ void plan_next(const Params& P, Shared& sh, CtrlState& cs, const int* off,
+                                          int U) {
     const int q = cs.planned++;
     const int slot = q % kPlanSlots;
     int kind;
@@ -990,6 +1026,7 @@ __device__ __forceinline__ void plan_next(const Params& P, Shared& sh, CtrlState
         const int j = cs.jq_head++ % kJobSlots;
         if ((threadIdx.x & 63) == 0) {
             sh.pl_u[slot] = sh.jq_u[j];
+            sh.pl_b[slot] = sh.jq_b[j];
             sh.pl_mt[slot] = sh.jq_mt[j];
             sh.pl_md[slot] = sh.jq_md[j];
             sh.pl_ist[slot] = sh.jq_ist[j];
@@ -997,7 +1034,17 @@ __device__ __forceinline__ void plan_next(const Params& P, Shared& sh, CtrlState
         }
     } else if (cs.next_unit < U) {
         kind = PL_UNIT;
-        if ((threadIdx.x & 63) == 0) sh.pl_u[slot] = cs.next_unit;
+        if ((cs.seq_n & 63) == 0) {
+            // Requests of the next 64 regular units, one binary search per lane.
+            const int lane = threadIdx.x & 63;
+            const int u = cs.next_unit + lane * (int)gridDim.x;
+            sh.seq_b[lane] = u < U ? request_of(P, off, u) : 0;
+        }
+        if ((threadIdx.x & 63) == 0) {
+            sh.pl_u[slot] = cs.next_unit;
+            sh.pl_b[slot] = sh.seq_b[cs.seq_n & 63];
+        }
+        ++cs.seq_n;
         cs.next_unit += gridDim.x;
     } else {
         kind = PL_END;
@@ -1012,8 +1059,11 @@ __device__ __forceinline__ void plan_next(const Params& P, Shared& sh, CtrlState
 
 // Push/pop helpers of the LDS rings (the control wave owns them; indices
 // live in registers, uniform).
-__device__ __forceinline__ void ring_put(int* ring, int slots, int& tail, int v) {
-    if ((threadIdx.x & 63) == 0) ring[tail % slots] = v;
+__device__ __forceinline__ void ring_put(int* ru, int* rb, int slots, int& tail, const Unit& u) {
+    if ((threadIdx.x & 63) == 0) {
+        ru[tail % slots] = u.u;
+        rb[tail % slots] = u.b;
+    }
     ++tail;
 }
 
@@ -1044,14 +1094,15 @@ __device__ __forceinline__ int control_loop(const Params& P, Shared& sh, const i
     cs.fr_head = cs.fr_tail = 0;
     cs.jq_head = cs.jq_tail = 0;
     cs.ow_head = cs.ow_tail = 0;
-    for (int q = 0; q < kPlanLead && cs.end_round == INT_MAX; ++q) plan_next(P, sh, cs, U);
+    cs.seq_n = 0;
+    for (int q = 0; q < kPlanLead && cs.end_round == INT_MAX; ++q) plan_next(P, sh, cs, off, U);
     Owed fresh;                      // chunk-0 unit consumed last round, to decide now
     fresh.u.u = -1;
     int ntasks = 0;
     TeamPoll pa, pb, pc;
     for (int r = 0; r < cs.end_round; ++r) {
         // P.
-        if (cs.end_round == INT_MAX && r + kPlanLead == cs.planned) plan_next(P, sh, cs, U);
+        if (cs.end_round == INT_MAX && r + kPlanLead == cs.planned) plan_next(P, sh, cs, off, U);
         // 1.
         const bool have_a = fresh.u.u >= 0;
         if (have_a) owed_issue<E, kGreedy>(P, fresh, pa);
@@ -1059,7 +1110,7 @@ __device__ __forceinline__ int control_loop(const Params& P, Shared& sh, const i
         old.u.u = -1;
         if (cs.ow_head != cs.ow_tail) {
             const int j = cs.ow_head % kOwedSlots;
-            old.u = decode_unit(P, off, sh.ow_u[j], U, kGreedy);
+            old.u = unit_from(P, off, sh.ow_u[j], sh.ow_b[j], kGreedy);
             old.x = sh.ow_x[j];
             owed_issue<E, kGreedy>(P, old, pb);
         }
@@ -1067,15 +1118,19 @@ __device__ __forceinline__ int control_loop(const Params& P, Shared& sh, const i
         c0.u = c1.u = -1;
         unsigned long long dw = 0;
         if (!kGreedy) {
-            if (cs.pd_head != cs.pd_tail) c0 = decode_unit(P, off, sh.pd_u[cs.pd_head % kPendSlots], U, false);
+            if (cs.pd_head != cs.pd_tail) {
+                const int j = cs.pd_head % kPendSlots;
+                c0 = unit_from(P, off, sh.pd_u[j], sh.pd_b[j], false);
+            }
             if (cs.pd_tail - cs.pd_head >= 2)
-                c1 = decode_unit(P, off, sh.pd_u[(cs.pd_head + 1) % kPendSlots], U, false);
+                c1 = unit_from(P, off, sh.pd_u[(cs.pd_head + 1) % kPendSlots],
+                               sh.pd_b[(cs.pd_head + 1) % kPendSlots], false);
             dw = prefix_issue(P, c0.b, c0.i, c0.u >= 0, 0) | prefix_issue(P, c1.b, c1.i, c1.u >= 0, 1);
         }
         Unit fj;
         fj.u = -1;
         if (!kGreedy && cs.fr_head != cs.fr_tail && cs.jq_tail - cs.jq_head < kJobSlots) {
-            fj = decode_unit(P, off, sh.fr_u[cs.fr_head % kFirstSlots], U, false);
+            fj = unit_from(P, off, sh.fr_u[cs.fr_head % kFirstSlots], sh.fr_b[cs.fr_head % kFirstSlots], false);
             poll_issue<false>(P, fj.tr, pc);
         }
         // 2.
@@ -1084,7 +1139,7 @@ __device__ __forceinline__ int control_loop(const Params& P, Shared& sh, const i
         {
             const int slot = r % kPlanSlots;
             const int kind = sh.pl_kind[slot];
-            const Unit cur = decode_unit(P, off, sh.pl_u[slot], U, kGreedy);
+            const Unit cur = unit_from(P, off, sh.pl_u[slot], sh.pl_b[slot], kGreedy);
             if (kind == PL_UNIT) {
                 control_unit<E, kGreedy>(P, sh, cur, r, ntasks);
                 if (cur.c == 0 && (kGreedy || cur.has_d)) {
@@ -1093,7 +1148,7 @@ __device__ __forceinline__ int control_loop(const Params& P, Shared& sh, const i
                 }
                 if (!kGreedy && cur.has_d) {
                     if (cs.pd_tail - cs.pd_head >= kPendSlots) ++cs.pd_head;   // oldest left to after the loop
-                    ring_put(sh.pd_u, kPendSlots, cs.pd_tail, cur.u);
+                    ring_put(sh.pd_u, sh.pd_b, kPendSlots, cs.pd_tail, cur);
                 }
             } else {
                 // A job's residual mass: one partial per data wave.
@@ -1119,7 +1174,7 @@ __device__ __forceinline__ int control_loop(const Params& P, Shared& sh, const i
                 owed_decide<kGreedy>(P, fresh, pa, ntasks);
             } else if (cs.ow_tail - cs.ow_head < kOwedSlots) {
                 if ((threadIdx.x & 63) == 0) sh.ow_x[cs.ow_tail % kOwedSlots] = fresh.x;
-                ring_put(sh.ow_u, kOwedSlots, cs.ow_tail, fresh.u.u);
+                ring_put(sh.ow_u, sh.ow_b, kOwedSlots, cs.ow_tail, fresh.u);
             } else {
                 poll_wait<kGreedy>(P, sh, fresh.u.tr, pa);   // ring full: wait (rare)
                 owed_decide<kGreedy>(P, fresh, pa, ntasks);
@@ -1135,12 +1190,12 @@ __device__ __forceinline__ int control_loop(const Params& P, Shared& sh, const i
                 const int s0 = prefix_status(P, dw, c0.i, 0);
                 if (s0 >= 0) {
                     ++cs.pd_head;
-                    if (s0 == 1 && cs.fr_tail - cs.fr_head < kFirstSlots) ring_put(sh.fr_u, kFirstSlots, cs.fr_tail, c0.u);
+                    if (s0 == 1 && cs.fr_tail - cs.fr_head < kFirstSlots) ring_put(sh.fr_u, sh.fr_b, kFirstSlots, cs.fr_tail, c0);
                     if (c1.u >= 0) {
                         const int s1 = prefix_status(P, dw, c1.i, 1);
                         if (s1 >= 0) {
                             ++cs.pd_head;
-                            if (s1 == 1 && cs.fr_tail - cs.fr_head < kFirstSlots) ring_put(sh.fr_u, kFirstSlots, cs.fr_tail, c1.u);
+                            if (s1 == 1 && cs.fr_tail - cs.fr_head < kFirstSlots) ring_put(sh.fr_u, sh.fr_b, kFirstSlots, cs.fr_tail, c1);
                         }
                     }
                 }
@@ -1150,6 +1205,7 @@ __device__ __forceinline__ int control_loop(const Params& P, Shared& sh, const i
                 const int j = cs.jq_tail++ % kJobSlots;
                 if ((threadIdx.x & 63) == 0) {
                     sh.jq_u[j] = fj.u;
+                    sh.jq_b[j] = fj.b;
                     sh.jq_mt[j] = ts.mt;
                     sh.jq_md[j] = ts.md;
                     sh.jq_ist[j] = (float)(1.0 / ts.st);
@@ -1169,7 +1225,7 @@ __device__ __forceinline__ int control_loop(const Params& P, Shared& sh, const i
     while (cs.ow_head != cs.ow_tail) {
         const int j = cs.ow_head % kOwedSlots;
         Owed o;
-        o.u = decode_unit(P, off, sh.ow_u[j], U, kGreedy);
+        o.u = unit_from(P, off, sh.ow_u[j], sh.ow_b[j], kGreedy);
         o.x = sh.ow_x[j];
         poll_wait<kGreedy>(P, sh, o.u.tr, pl);
         owed_issue<E, kGreedy>(P, o, pl);
@@ -1196,7 +1252,7 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
         const int slot = q % kPlanSlots;
         lds_wait(P, sh, &sh.pl_tag[slot], q);
         kind = sh.pl_kind[slot];
-        u = decode_unit(P, off, kind == PL_END ? U : sh.pl_u[slot], U, kGreedy);
+        u = unit_from(P, off, kind == PL_END ? -1 : sh.pl_u[slot], sh.pl_b[slot], kGreedy);
         if (kind == PL_JOB) u.has_d = true;
     };
 
