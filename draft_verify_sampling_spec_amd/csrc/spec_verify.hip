@@ -571,25 +571,13 @@ __device__ __forceinline__ unsigned long long* dec_word(const Params& P, int tr)
     return reinterpret_cast<unsigned long long*>(P.team + (size_t)tr * kTeamWords + TW_DEC);
 }
 
-// Control lane: team tr = (b, i) of a request with budget k is complete (its
-// decision and, if it drew one, its token are stored). The team completing
-// last for request b writes the request's outputs: j = the first rejected
-// position (k if none), the token drawn by team j.
+// One lane: request b (budget k) ends at position j (the first rejection,
+// k if none) with token y there: the accepted drafted tokens, y, then -1
+// padding; probabilities past the positions the request decides are NaN
+// (greedy decides none).
 template <bool kGreedy>
-__device__ void team_complete(const Params& P, int b, int k) {
-    drain();
-    const unsigned old = add32(&P.req_count[b * kReqStride], 1u);
-    if (old != (unsigned)k) return;
+__device__ void request_outputs(const Params& P, int b, int k, int j, int y) {
     const int K = P.K;
-    const int tr0 = b * (K + 1);
-    int j = k;
-    for (int t = 0; t < k; ++t) {
-        if ((ld64(dec_word(P, tr0 + t)) & 1ull) == 0) {
-            j = t;
-            break;
-        }
-    }
-    const int y = (int)ld32(&P.result[tr0 + j]);
     P.out_nacc[b] = j;
     for (int t = 0; t <= K; ++t) {
         int32_t v = -1;
@@ -601,6 +589,24 @@ __device__ void team_complete(const Params& P, int b, int k) {
         if (P.out_p) P.out_p[(size_t)b * K + t] = NAN;
         if (P.out_q) P.out_q[(size_t)b * K + t] = NAN;
     }
+}
+
+// Control lane, greedy: team tr = (b, i) of a request with budget k is
+// decided (its decision word and argmax are stored). The team completing
+// last for request b writes the request's outputs.
+__device__ void team_complete(const Params& P, int b, int k) {
+    drain();
+    const unsigned old = add32(&P.req_count[b * kReqStride], 1u);
+    if (old != (unsigned)k) return;
+    const int tr0 = b * (P.K + 1);
+    int j = k;
+    for (int t = 0; t < k; ++t) {
+        if ((ld64(dec_word(P, tr0 + t)) & 1ull) == 0) {
+            j = t;
+            break;
+        }
+    }
+    request_outputs<true>(P, b, k, j, (int)ld32(&P.result[tr0 + j]));
     // Every team of the request has been counted: reset the counter for the
     // next call (tagged words carry the call epoch and need no reset).
     st32(&P.req_count[b * kReqStride], 0u);
@@ -755,7 +761,7 @@ __device__ void decide_greedy(const Params& P, const TeamPoll& pl, int b, int i,
         }
         st32(&P.result[tr], (unsigned)best);
         st64(dec_word(P, tr), ((unsigned long long)P.epoch << 32) | (accept ? 1u : 0u));
-        team_complete<true>(P, b, k);
+        team_complete(P, b, k);
     }
 }
 
@@ -938,9 +944,8 @@ __device__ __forceinline__ void owed_issue(const Params& P, Owed& o, TeamPoll& p
 
 // Control wave: decide an owed team from its complete records. Greedy:
 // argmax, decision, completion. Sampled (a drafted position): p(x), q(x), the
-// accept decision, the decision word; an accepted team is complete, a
-// rejected one gets a deferred draw (made only if it is the request's first
-// rejection).
+// accept decision, the decision word; a rejected team gets a deferred draw
+// (made only if it is the request's first rejection).
 template <bool kGreedy>
 __device__ __forceinline__ void owed_decide(const Params& P, const Owed& o, const TeamPoll& pl,
                                             int& ntasks) {
@@ -965,7 +970,6 @@ __device__ __forceinline__ void owed_decide(const Params& P, const Owed& o, cons
         if (P.out_p) P.out_p[(size_t)u.b * K + u.i] = (float)px;
         if (P.out_q) P.out_q[(size_t)u.b * K + u.i] = (float)qx;
         st64(dec_word(P, u.tr), ((unsigned long long)P.epoch << 32) | (accept ? 1u : 0u));
-        if (accept) team_complete<false>(P, u.b, u.k);
     }
     if (!accept) add_task(P, u.tr, false, ntasks);
 }
@@ -1397,8 +1401,8 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
 
 // Control wave: are positions 0 .. i-1 of request b all accepted? Waits
 // (bounded) until the decisions that settle it are known: lane t polls
-// position t; done once every position before the first known rejection is
-// decided, or all are decided.
+// position t; no once any of them is known rejected, yes once all are known
+// accepted.
 __device__ bool earlier_accepted(const Params& P, Shared& sh, int b, int i) {
     const int lane = threadIdx.x & 63;
     const int K = P.K;
@@ -1407,14 +1411,8 @@ __device__ bool earlier_accepted(const Params& P, Shared& sh, int b, int i) {
         unsigned long long d = 0;
         if (lane < i) d = ld64(dec_word(P, b * (K + 1) + lane));
         const bool known = lane >= i || (unsigned)(d >> 32) == ep;
-        const unsigned long long rej = __ballot(lane < i && known && (d & 1ull) == 0);
-        const unsigned long long unknown = __ballot(!known);
-        if (rej != 0) {
-            const unsigned long long below = (rej & (~rej + 1)) - 1;   // lanes below the first rejection
-            if ((unknown & below) == 0) return false;
-        } else if (unknown == 0) {
-            return true;
-        }
+        if (__ballot(lane < i && known && (d & 1ull) == 0) != 0) return false;
+        if (__ballot(!known) == 0) return true;
         if (it >= kSpinLimit || lds_get(&sh.abort_wait)) {
             if (lane == 0) give_up(P, sh);
             return false;
@@ -1640,10 +1638,14 @@ __device__ void after_loop(const Params& P, Shared& sh, const int* off) {
         const int task = (int)ld32(list + t);
         if (wave == 0) task_prepare(P, sh, task);
         __syncthreads();
+        if (!sh.tk_draw) {                         // uniform: not the request's deciding position
+            __syncthreads();
+            continue;
+        }
         const int tr = task >> 1;
         const int b = tr / (K + 1), i = tr - b * (K + 1);
         int y = 0;
-        if (sh.tk_draw && sh.tk_chunk >= 0) {
+        if (sh.tk_chunk >= 0) {
             const int e0 = sh.tk_chunk * P.CE;
             const int n = min(P.CE, P.V - e0);
             const E* rt = target + ((size_t)b * (K + 1) + i) * (size_t)P.V + e0;
@@ -1656,8 +1658,7 @@ __device__ void after_loop(const Params& P, Shared& sh, const int* off) {
             // The request's budget, clamped as in the prologue.
             int k = P.budgets[b];
             k = k < 0 ? 0 : (k > K ? K : k);
-            if (sh.tk_draw) st32(&P.result[tr], (unsigned)y);
-            team_complete<false>(P, b, k);
+            request_outputs<false>(P, b, k, i, y);
         }
         __syncthreads();
     }
