@@ -78,15 +78,17 @@ constexpr int kDataWaves = kWaves - 1;
 constexpr int kDataThreads = kDataWaves * 64;
 constexpr int kG = 4;                          // 16-byte groups per data lane per row of a unit
 constexpr int kLaunchBatch = 8192;             // requests per launch (unit offsets live in LDS)
-constexpr int kPlanLead = 4;                   // rounds the control wave plans ahead
+constexpr int kMbox = 2;                       // result mailbox slots (rounds the data waves may lead)
+constexpr int kPlanLead = 4;                   // rounds the control wave plans ahead (>= kMbox)
 constexpr int kPlanSlots = 8;                  // plan ring (> kPlanLead + 1)
+static_assert(kPlanLead >= kMbox && kPlanSlots > kPlanLead + 1, "plan ring too short");
 constexpr int kPendSlots = 16;                 // drafted units awaiting first-rejection status
 constexpr int kJobSlots = 8;                   // re-read jobs ready to plan
 constexpr int kFirstSlots = 8;                 // first rejections whose normalisers are to load
 constexpr int kOwedSlots = 8;                  // chunk-0 units whose decision is owed
 constexpr int PL_END = 0, PL_UNIT = 1, PL_JOB = 2;
-constexpr int kScanElems = kDataThreads * 8;   // elements per scan sub-tile
-constexpr int kMaxSub = 4;                     // sub-tiles per chunk
+constexpr int kBlocks = kG * kDataWaves;       // element blocks of a chunk scan (group, data wave)
+static_assert(kBlocks <= 64, "a chunk scan locates its block in one wave");
 constexpr int kTeamWords = 32;                 // words per team record (128 bytes)
 constexpr int kReqStride = 16;                 // words between request counters (64 bytes)
 constexpr unsigned kSpinLimit = 1u << 20;      // bounded device-scope wait (~1 s)
@@ -287,17 +289,18 @@ struct Shared {
     int pl_kind[kPlanSlots];
     int pl_u[kPlanSlots], pl_b[kPlanSlots];      // unit and its request
     float pl_mt[kPlanSlots], pl_md[kPlanSlots], pl_ist[kPlanSlots], pl_isd[kPlanSlots];
-    // Data wave -> control wave: a round's per-wave results, by round parity.
+    // Data wave -> control wave: a round's per-wave results, in slot
+    // round % kMbox.
     //   regular, sampled: (max, sum of 2^((z - max) c)) of the target and
     //                     drafter parts; greedy: (max, lowest index of the max)
     //   job: the part's residual mass in st_st
-    float st_mt[2][kDataWaves];
-    float st_md[2][kDataWaves];
-    double st_st[2][kDataWaves];
-    double st_sd[2][kDataWaves];
-    int st_idx[2][kDataWaves];
-    int st_tag[2][kDataWaves];                   // round + 1
-    int st_done[2];                              // control wave: round + 1 of the slot it read last
+    float st_mt[kMbox][kDataWaves];
+    float st_md[kMbox][kDataWaves];
+    double st_st[kMbox][kDataWaves];
+    double st_sd[kMbox][kDataWaves];
+    int st_idx[kMbox][kDataWaves];
+    int st_tag[kMbox][kDataWaves];                   // round + 1
+    int st_done[kMbox];                          // control wave: round + 1 of the slot it read last
     // Control wave only (rings): drafted units whose first-rejection status
     // is not known yet, first rejections whose normalisers are to be loaded,
     // chunk-0 units whose decision is owed, and re-read jobs ready to plan.
@@ -324,7 +327,7 @@ struct Shared {
     int rr_b, rr_i, rr_c, rr_tr;
     float rr_mt, rr_md, rr_ist, rr_isd;
     // Block-wide scratch (after the loop only, under barriers).
-    double scan_ws[kMaxSub * kDataWaves];
+    double scan_ws[kBlocks];
     double red_d[kWaves];
     float red_f[kWaves];
     int red_i[kWaves];
@@ -391,136 +394,6 @@ __device__ __forceinline__ bool better_arg(float v, int i, float bv, int bi) {
 }
 
 // ------------------------------------------------------- mass and scans --
-
-// Sampling mass of the 8 elements [e, e + 8) of a chunk of n elements:
-// residual max(0, p - q) when rd is given, else p. p = 2^((z_t - mt) c) / S_t.
-template <typename E, bool kVec>
-__device__ __forceinline__ void mass8(const E* rt, const E* rd, int e, int n, bool vt, bool vd,
-                                      float mt, float ist, float md, float isd, float c,
-                                      float r[8]) {
-    constexpr int W = Elem<E>::W;
-    #pragma unroll
-    for (int h = 0; h < 8 / W; ++h) {
-        const uint4 gt = load_group<E, kVec>(rt, e + h * W, n, vt);
-        if (rd != nullptr) {
-            const uint4 gd = load_group<E, kVec>(rd, e + h * W, n, vd);
-            #pragma unroll
-            for (int k = 0; k < W; ++k) {
-                const float p = fast_exp2((Elem<E>::at(gt, k) - mt) * c) * ist;
-                const float q = fast_exp2((Elem<E>::at(gd, k) - md) * c) * isd;
-                r[h * W + k] = fmaxf(0.0f, p - q);
-            }
-        } else {
-            #pragma unroll
-            for (int k = 0; k < W; ++k) r[h * W + k] = fast_exp2((Elem<E>::at(gt, k) - mt) * c) * ist;
-        }
-    }
-}
-
-// Element-level inverse CDF inside one chunk (whole workgroup; the data
-// waves hold the elements): returns the offset in the chunk of the smallest
-// element whose running mass (from the chunk start) exceeds thr, zero-mass
-// elements excluded; if rounding leaves no crossing, the last positive-mass
-// element; -1 if the chunk has no mass.
-template <typename E, bool kVec>
-__device__ int chunk_scan(Shared& sh, const E* rt, const E* rd, int n, float mt, float ist,
-                          float md, float isd, float c, double thr) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const bool data = wave > 0;
-    const int dt = tid - 64;                       // data thread index
-    const bool vt = aligned16(rt);
-    const bool vd = rd != nullptr && aligned16(rd);
-    const int nsub = (n + kScanElems - 1) / kScanElems;
-    for (int s = 0; s < nsub; ++s) {
-        float ls = 0.0f;
-        if (data) {
-            float r[8];
-            mass8<E, kVec>(rt, rd, s * kScanElems + dt * 8, n, vt, vd, mt, ist, md, isd, c, r);
-            #pragma unroll
-            for (int k = 0; k < 8; ++k) ls += r[k];
-        }
-        const double ws = wave_sum((double)ls);
-        if (data && lane == 0) sh.scan_ws[s * kDataWaves + wave - 1] = ws;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        double acc = 0.0, acc_last = 0.0;
-        int star = -1, last = -1;
-        for (int s = 0; s < nsub; ++s) {
-            const double* ws = sh.scan_ws + s * kDataWaves;
-            double tot = ws[0];
-            for (int w = 1; w < kDataWaves; ++w) tot += ws[w];
-            if (tot > 0.0) {
-                last = s;
-                acc_last = acc;
-                if (acc + tot > thr) {
-                    star = s;
-                    break;
-                }
-            }
-            acc += tot;
-        }
-        if (star < 0) {
-            star = last;
-            acc = acc_last;
-        }
-        sh.sub_star = star;
-        sh.sub_base = acc;
-    }
-    __syncthreads();
-    const int s = sh.sub_star;
-    if (s < 0) {
-        __syncthreads();
-        return -1;
-    }
-    const int e = s * kScanElems + dt * 8;
-    float r[8];
-    #pragma unroll
-    for (int k = 0; k < 8; ++k) r[k] = 0.0f;
-    if (data) mass8<E, kVec>(rt, rd, e, n, vt, vd, mt, ist, md, isd, c, r);
-    double pre[8];
-    double run = 0.0;
-    #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        run += (double)r[k];
-        pre[k] = run;
-    }
-    const double incl = wave_incl_scan(run, lane);
-    if (lane == 63) sh.red_d[wave] = incl;
-    __syncthreads();
-    const double up = __shfl_up(incl, 1, 64);
-    double excl = lane ? up : 0.0;
-    for (int w = 1; w < wave; ++w) excl += sh.red_d[w];
-    const double t = thr - sh.sub_base;
-    int cand = INT_MAX, last_pos = -1;
-    if (data) {
-        #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            if (r[k] > 0.0f) {
-                last_pos = e + k;
-                if (cand == INT_MAX && excl + pre[k] > t) cand = e + k;
-            }
-        }
-    }
-    #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        cand = min(cand, __shfl_xor(cand, off, 64));
-        last_pos = max(last_pos, __shfl_xor(last_pos, off, 64));
-    }
-    if (lane == 0) {
-        sh.red_i[wave] = cand;
-        sh.red_f[wave] = __int_as_float(last_pos);
-    }
-    __syncthreads();
-    int y = INT_MAX, lp = -1;
-    #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        y = min(y, sh.red_i[w]);
-        lp = max(lp, __float_as_int(sh.red_f[w]));
-    }
-    __syncthreads();
-    return y != INT_MAX ? y : lp;
-}
 
 // Wave 0: find the chunk where the running mass over chunks 0..C-1 first
 // exceeds thr. mass(cc) gives chunk cc's mass. Returns (chunk, mass before it)
@@ -867,7 +740,7 @@ __device__ __forceinline__ void control_unit(const Params& P, Shared& sh, const 
                                              int& ntasks) {
     const int lane = threadIdx.x & 63;
     const int C = P.C;
-    const int slot = r & 1;
+    const int slot = r % kMbox;
     const unsigned ep = P.epoch;
     if (lane < kDataWaves) lds_wait(P, sh, &sh.st_tag[slot][lane], r + 1);
     unsigned long long* rec = P.rec + ((size_t)cur.tr * C + cur.c) * kRecWords;
@@ -1157,7 +1030,7 @@ __device__ __forceinline__ int control_loop(const Params& P, Shared& sh, const i
             } else {
                 // A job's residual mass: one partial per data wave.
                 const int lane = threadIdx.x & 63;
-                const int rs = r & 1;
+                const int rs = r % kMbox;
                 double v = 0.0;
                 if (lane < kDataWaves) {
                     lds_wait(P, sh, &sh.st_tag[rs][lane], r + 1);
@@ -1267,7 +1140,7 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
     if (kind == PL_END) return;
     issue_loads<E, kVec>(P, cur, dt, gt, gd);
     for (int r = 0;; ++r) {
-        const int slot = r & 1;
+        const int slot = r % kMbox;
         const int ps = r % kPlanSlots;
         Unit nxt;
         int nkind;
@@ -1382,7 +1255,7 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
             post_md = md;
         }
         if (lane == 0) {
-            if (r >= 2) lds_wait(P, sh, &sh.st_done[slot], r - 1);
+            if (r >= kMbox) lds_wait(P, sh, &sh.st_done[slot], r - kMbox + 1);
             sh.st_mt[slot][dw] = post_mt;
             sh.st_md[slot][dw] = post_md;
             sh.st_st[slot][dw] = post_a;
@@ -1398,28 +1271,6 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
 }
 
 // ------------------------------------------------------- after the loop --
-
-// Control wave: are positions 0 .. i-1 of request b all accepted? Waits
-// (bounded) until the decisions that settle it are known: lane t polls
-// position t; no once any of them is known rejected, yes once all are known
-// accepted.
-__device__ bool earlier_accepted(const Params& P, Shared& sh, int b, int i) {
-    const int lane = threadIdx.x & 63;
-    const int K = P.K;
-    const unsigned ep = P.epoch;
-    for (unsigned it = 0;; ++it) {
-        unsigned long long d = 0;
-        if (lane < i) d = ld64(dec_word(P, b * (K + 1) + lane));
-        const bool known = lane >= i || (unsigned)(d >> 32) == ep;
-        if (__ballot(lane < i && known && (d & 1ull) == 0) != 0) return false;
-        if (__ballot(!known) == 0) return true;
-        if (it >= kSpinLimit || lds_get(&sh.abort_wait)) {
-            if (lane == 0) give_up(P, sh);
-            return false;
-        }
-        __builtin_amdgcn_s_sleep(2);
-    }
-}
 
 // Control wave: which of this workgroup's drafted units (rounds base ..
 // base+63 of its regular sequence, lane = round - base) are chunks of a
@@ -1534,10 +1385,13 @@ __device__ void reread_residual(const Params& P, Shared& sh, const int* off, int
     __syncthreads();
 }
 
-// Control wave, step 4 (one deferred draw): if the draw is to be made, locate
-// the chunk holding the threshold -- over the residual masses of the team's
-// chunks for a first rejection, over p for the bonus position (or a residual
-// without mass) -- and leave its element scan to the whole workgroup.
+// Control wave, one deferred draw: does it draw (is it its request's
+// deciding position)? If so, locate the chunk holding the threshold -- over
+// the residual masses of the team's chunks for a first rejection, over p for
+// the bonus position (or a residual without mass) -- and leave the element
+// scan to the whole workgroup. Each attempt is one round of loads: the
+// decision words of the earlier positions (lane t: position t) and the
+// team's records and residual masses (lane c: chunk c).
 __device__ void task_prepare(const Params& P, Shared& sh, int task) {
     const int lane = threadIdx.x & 63;
     const int K = P.K, C = P.C;
@@ -1545,34 +1399,49 @@ __device__ void task_prepare(const Params& P, Shared& sh, int task) {
     const int tr = task >> 1;
     const bool bonus = task & 1;
     const int b = tr / (K + 1), i = tr - b * (K + 1);
-    // A rejection draws only as its request's first; the bonus position
-    // only if every drafted position was accepted.
-    const bool draw = earlier_accepted(P, sh, b, i);
+    unsigned long long* rec = P.rec + (size_t)tr * C * kRecWords;
+    TeamPoll pl;
+    unsigned long long rr = 0;
+    bool draw = false;
+    for (unsigned it = 0;; ++it) {
+        const unsigned long long d = lane < i ? ld64(dec_word(P, b * (K + 1) + lane)) : 0ull;
+        poll_issue<false>(P, tr, pl);
+        if (!bonus && lane < C) rr = ld64(rec + lane * kRecWords + R_RES);
+        // A rejection draws only as its request's first; the bonus position
+        // only if every drafted position was accepted.
+        const bool known = lane >= i || (unsigned)(d >> 32) == ep;
+        if (__ballot(lane < i && known && (d & 1ull) == 0) != 0) break;
+        if (__ballot(!known) == 0) {
+            bool ok = bonus || lane >= C || tag_ok(rr, ep);
+            for (int cc = lane + 64; !bonus && cc < C; cc += 64) ok = ok && tag_ok(ld64(rec + cc * kRecWords + R_RES), ep);
+            if (poll_complete<false>(P, pl) && __ballot(!ok) == 0) {
+                draw = true;
+                break;
+            }
+        }
+        if (it >= kSpinLimit || lds_get(&sh.abort_wait)) {
+            if (lane == 0) give_up(P, sh);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
     int chunk = -1, mode = 0;
     double thr = 0.0;
     TeamStats ts;
     ts.mt = ts.md = 0.0f;
     ts.st = ts.sd = 1.0;
     if (draw) {
-        ts = merge_team(P, sh, tr);
-        unsigned long long* rec = P.rec + (size_t)tr * C * kRecWords;
+        ts = team_stats(P, pl);
         const uint4 rw = philox4x32_10((uint32_t)(P.bbase + b), (uint32_t)i, 0u, 0u, P.key0, P.key1);
         const double u = word_to_uniform(rw.y);
         double total = 0.0, base = 0.0;
+        // Chunk cc's words: lane cc holds them for cc < 64.
+        auto word = [&](int cc, int f, unsigned long long held) -> float {
+            return tag_val(cc == lane ? held : ld64(rec + cc * kRecWords + f));
+        };
         if (!bonus) {
-            // Residual masses: every chunk member publishes its own.
-            for (unsigned it = 0;; ++it) {
-                bool ok = true;
-                for (int cc = lane; cc < C; cc += 64) ok = ok && tag_ok(ld64(rec + cc * kRecWords + R_RES), ep);
-                if (__ballot(!ok) == 0) break;
-                if (it >= kSpinLimit || lds_get(&sh.abort_wait)) {
-                    if (lane == 0) give_up(P, sh);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
             auto rmass = [&](int cc) -> double {
-                const float v = tag_val(ld64(rec + cc * kRecWords + R_RES));
+                const float v = word(cc, R_RES, rr);
                 return v > 0.0f ? (double)v : 0.0;
             };
             for (int cc = lane; cc < C; cc += 64) total += rmass(cc);
@@ -1587,8 +1456,8 @@ __device__ void task_prepare(const Params& P, Shared& sh, int task) {
             mode = 0;
             const double inv = 1.0 / ts.st;
             auto pmass = [&](int cc) -> double {
-                const float s1 = tag_val(ld64(rec + cc * kRecWords + R_ST));
-                const float m1 = tag_val(ld64(rec + cc * kRecWords + R_MT));
+                const float s1 = word(cc, R_ST, pl.w[R_ST]);
+                const float m1 = word(cc, R_MT, pl.w[R_MT]);
                 return s1 > 0.0f ? (double)s1 * exp2(((double)m1 - (double)ts.mt) * P.c64) * inv : 0.0;
             };
             total = 0.0;
@@ -1608,6 +1477,102 @@ __device__ void task_prepare(const Params& P, Shared& sh, int task) {
         sh.tk_ist = (float)(1.0 / ts.st);
         sh.tk_isd = (float)(1.0 / ts.sd);
     }
+}
+
+// Element-level inverse CDF inside one chunk (whole workgroup). The data
+// waves load the chunk once, in the streaming layout: group j of data thread
+// dt holds the W elements from (j * kDataThreads + dt) * W, so element order
+// runs over groups, then data waves, then lanes, then a lane's elements.
+// Wave 0 finds the (group, data wave) block whose running mass crosses thr;
+// that block's wave scans its elements. Mass: residual max(0, p - q) when
+// d.has_d, else p; p = 2^((z_t - mt) c) / S_t. Returns the offset in the
+// chunk of the smallest element whose running mass from the chunk start
+// exceeds thr, zero-mass elements excluded; if rounding leaves no crossing,
+// the last positive-mass element of the last block with mass; -1 if the
+// chunk has no mass.
+template <typename E, bool kVec>
+__device__ int chunk_scan(const Params& P, Shared& sh, const Unit& d, float mt, float ist,
+                          float md, float isd, double thr) {
+    constexpr int W = Elem<E>::W;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float c = P.c32;
+    const bool res = d.has_d;
+    auto mass = [&](const uint4& t, const uint4& q, int k) -> float {
+        const float pv = fast_exp2((Elem<E>::at(t, k) - mt) * c) * ist;
+        if (!res) return pv;
+        return fmaxf(0.0f, pv - fast_exp2((Elem<E>::at(q, k) - md) * c) * isd);
+    };
+    uint4 gt[kG], gd[kG];
+    if (wave > 0) {
+        issue_loads<E, kVec>(P, d, tid - 64, gt, gd);
+        #pragma unroll
+        for (int j = 0; j < kG; ++j) {
+            float sj = 0.0f;
+            #pragma unroll
+            for (int k = 0; k < W; ++k) sj += mass(gt[j], gd[j], k);
+            const double ws = wave_sum((double)sj);
+            if (lane == 0) sh.scan_ws[j * kDataWaves + wave - 1] = ws;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const double m = lane < kBlocks ? sh.scan_ws[lane] : 0.0;
+        const double incl = wave_incl_scan(m, lane);
+        const double up = __shfl_up(incl, 1, 64);
+        const double excl = lane ? up : 0.0;
+        const unsigned long long hit = __ballot(m > 0.0 && incl > thr);
+        const unsigned long long pos = __ballot(m > 0.0);
+        const int star = hit ? __ffsll((long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : -1);
+        const double base = __shfl(excl, star < 0 ? 0 : star, 64);
+        if (lane == 0) {
+            sh.sub_star = star;
+            sh.sub_base = base;
+        }
+    }
+    __syncthreads();
+    const int star = sh.sub_star;
+    if (star < 0) return -1;
+    if (wave == 1 + star % kDataWaves) {
+        const int js = star / kDataWaves;
+        uint4 t = gt[0], q = gd[0];
+        #pragma unroll
+        for (int j = 1; j < kG; ++j) {
+            if (js == j) {
+                t = gt[j];
+                q = gd[j];
+            }
+        }
+        float r[W];
+        double pre[W];
+        double run = 0.0;
+        #pragma unroll
+        for (int k = 0; k < W; ++k) {
+            r[k] = mass(t, q, k);
+            run += (double)r[k];
+            pre[k] = run;
+        }
+        const double incl = wave_incl_scan(run, lane);
+        const double up = __shfl_up(incl, 1, 64);
+        const double excl = lane ? up : 0.0;
+        const double tt = thr - sh.sub_base;
+        const int e = (js * kDataThreads + tid - 64) * W;
+        int cand = INT_MAX, last = -1;
+        #pragma unroll
+        for (int k = 0; k < W; ++k) {
+            if (r[k] > 0.0f) {
+                last = e + k;
+                if (cand == INT_MAX && excl + pre[k] > tt) cand = e + k;
+            }
+        }
+        #pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            cand = min(cand, __shfl_xor(cand, o, 64));
+            last = max(last, __shfl_xor(last, o, 64));
+        }
+        if (lane == 0) sh.red_i[0] = cand != INT_MAX ? cand : last;
+    }
+    __syncthreads();
+    return sh.red_i[0];
 }
 
 // After both loops (whole workgroup, under barriers): re-read the chunks of
@@ -1631,8 +1596,6 @@ __device__ void after_loop(const Params& P, Shared& sh, const int* off) {
         __syncthreads();
     }
     // Draws.
-    const E* target = static_cast<const E*>(P.target);
-    const E* draft = static_cast<const E*>(P.draft);
     unsigned* list = reinterpret_cast<unsigned*>(P.tasks) + (size_t)blockIdx.x * P.task_cap;
     for (int t = 0; t < nt; ++t) {
         const int task = (int)ld32(list + t);
@@ -1646,13 +1609,16 @@ __device__ void after_loop(const Params& P, Shared& sh, const int* off) {
         const int b = tr / (K + 1), i = tr - b * (K + 1);
         int y = 0;
         if (sh.tk_chunk >= 0) {
-            const int e0 = sh.tk_chunk * P.CE;
-            const int n = min(P.CE, P.V - e0);
-            const E* rt = target + ((size_t)b * (K + 1) + i) * (size_t)P.V + e0;
-            const E* rd = sh.tk_mode == 1 ? draft + ((size_t)b * K + i) * (size_t)P.V + e0 : nullptr;
-            const int o = chunk_scan<E, kVec>(sh, rt, rd, n, sh.tk_mt, sh.tk_ist, sh.tk_md,
-                                              sh.tk_isd, P.c32, sh.tk_thr);
-            y = o < 0 ? 0 : e0 + o;
+            Unit d;
+            d.b = b;
+            d.i = i;
+            d.c = sh.tk_chunk;
+            d.e0 = d.c * P.CE;
+            d.n = min(P.CE, P.V - d.e0);
+            d.has_d = sh.tk_mode == 1;
+            const int o = chunk_scan<E, kVec>(P, sh, d, sh.tk_mt, sh.tk_ist, sh.tk_md, sh.tk_isd,
+                                              sh.tk_thr);
+            y = o < 0 ? 0 : d.e0 + o;
         }
         if (tid == 0) {
             // The request's budget, clamped as in the prologue.
@@ -1697,8 +1663,8 @@ void verify_kernel(Params P) {
             if (lane >= o) incl += v;
         }
         if (lane == 63) sh.red_i[wave] = incl;
-        if (tid < 2 * kDataWaves) (&sh.st_tag[0][0])[tid] = 0;
-        if (tid < 2) sh.st_done[tid] = 0;
+        if (tid < kMbox * kDataWaves) (&sh.st_tag[0][0])[tid] = 0;
+        if (tid < kMbox) sh.st_done[tid] = 0;
         if (tid < kPlanSlots) sh.pl_tag[tid] = -1;
         if (tid == 0) sh.abort_wait = 0;
         __syncthreads();
