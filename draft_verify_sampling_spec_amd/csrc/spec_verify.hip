@@ -82,11 +82,8 @@ constexpr int kMbox = 2;                       // result mailbox slots (rounds t
 constexpr int kPlanLead = 4;                   // rounds the control wave plans ahead (>= kMbox)
 constexpr int kPlanSlots = 8;                  // plan ring (> kPlanLead + 1)
 static_assert(kPlanLead >= kMbox && kPlanSlots > kPlanLead + 1, "plan ring too short");
-constexpr int kPendSlots = 16;                 // drafted units awaiting first-rejection status
-constexpr int kJobSlots = 8;                   // re-read jobs ready to plan
-constexpr int kFirstSlots = 8;                 // first rejections whose normalisers are to load
 constexpr int kOwedSlots = 8;                  // chunk-0 units whose decision is owed
-constexpr int PL_END = 0, PL_UNIT = 1, PL_JOB = 2;
+constexpr int PL_END = 0, PL_UNIT = 1;
 constexpr int kBlocks = kG * kDataWaves;       // element blocks of a chunk scan (group, data wave)
 static_assert(kBlocks <= 64, "a chunk scan locates its block in one wave");
 constexpr int kTeamWords = 32;                 // words per team record (128 bytes)
@@ -97,14 +94,14 @@ constexpr unsigned kLdsSpinLimit = 1u << 26;   // bounded LDS mailbox wait (~3 s
 // Team record words.
 constexpr int TW_DEC = 2;       // 64-bit decision: (epoch << 32) | accepted (words 2-3)
 
-// Unit record: 8 64-bit words.
+// Unit record: 4 64-bit words.
 //   sampled: word f = (value bits << 32) | epoch for the fp32 values
 //            R_MT max of z_t, R_MD max of z_d, R_ST sum of 2^((z_t - M_t) c),
-//            R_SD likewise, R_RES residual mass once the team has rejected
+//            R_SD likewise
 //   greedy:  word R_MT = (max bits << 32) | epoch, word R_MD = (lowest index
 //            of the max << 32) | epoch
-constexpr int kRecWords = 8;
-constexpr int R_MT = 0, R_MD = 1, R_ST = 2, R_SD = 3, R_RES = 4;
+constexpr int kRecWords = 4;
+constexpr int R_MT = 0, R_MD = 1, R_ST = 2, R_SD = 3;
 constexpr int kStatWords = 4;   // words R_MT..R_SD make a record complete
 
 // Philox4x32 constants (Salmon et al., SC'11): round multipliers and the key
@@ -127,15 +124,13 @@ struct Params {
     float* out_q;                  // [B, K] or null
     unsigned long long* rec;       // [B*(K+1)*C][kRecWords]
     unsigned* team;                // [B*(K+1)][kTeamWords]
-    unsigned* result;              // [B*(K+1)]: drawn token of the team
-    unsigned* req_count;           // [B][kReqStride]: teams completed
-    int* tasks;                    // [G][task_cap]: deferred draws, 2 * team + is_bonus
+    unsigned* result;              // [B*(K+1)]: greedy: argmax of the team's row
+    unsigned* req_count;           // [B][kReqStride]: greedy: teams completed
     unsigned* status;              // 1 word
     int B, K, V;
     int bbase;                     // index of request 0 of this launch in the caller's batch
     int C;                         // chunks per row
     int CE;                        // elements per chunk
-    int task_cap;                  // task list entries per workgroup
     float c32;                     // log2(e) / T
     double c64;
     uint32_t key0, key1;
@@ -282,18 +277,14 @@ __device__ __forceinline__ bool aligned16(const void* p) {
 // complete in order, so a reader that sees the tag sees the payload).
 struct Shared {
     // Control wave -> data waves: the plan of data round q, written kPlanLead
-    // rounds ahead into slot q % kPlanSlots: a regular unit (the next one of
-    // the workgroup's sequence), a re-read job (a chunk of a first rejection,
-    // with its team's normalisers), or the end of the loop.
+    // rounds ahead into slot q % kPlanSlots: the next unit of the workgroup's
+    // sequence, or the end of the loop.
     int pl_tag[kPlanSlots];
     int pl_kind[kPlanSlots];
     int pl_u[kPlanSlots], pl_b[kPlanSlots];      // unit and its request
-    float pl_mt[kPlanSlots], pl_md[kPlanSlots], pl_ist[kPlanSlots], pl_isd[kPlanSlots];
     // Data wave -> control wave: a round's per-wave results, in slot
-    // round % kMbox.
-    //   regular, sampled: (max, sum of 2^((z - max) c)) of the target and
-    //                     drafter parts; greedy: (max, lowest index of the max)
-    //   job: the part's residual mass in st_st
+    // round % kMbox. Sampled: (max, sum of 2^((z - max) c)) of the target and
+    // drafter parts; greedy: (max, lowest index of the max).
     float st_mt[kMbox][kDataWaves];
     float st_md[kMbox][kDataWaves];
     double st_st[kMbox][kDataWaves];
@@ -301,32 +292,18 @@ struct Shared {
     int st_idx[kMbox][kDataWaves];
     int st_tag[kMbox][kDataWaves];                   // round + 1
     int st_done[kMbox];                          // control wave: round + 1 of the slot it read last
-    // Control wave only (rings): drafted units whose first-rejection status
-    // is not known yet, first rejections whose normalisers are to be loaded,
-    // chunk-0 units whose decision is owed, and re-read jobs ready to plan.
-    int pd_u[kPendSlots], pd_b[kPendSlots];
-    int fr_u[kFirstSlots], fr_b[kFirstSlots];
+    // Control wave only: chunk-0 units whose decision is owed (a ring).
     int ow_u[kOwedSlots], ow_b[kOwedSlots], ow_x[kOwedSlots];
-    int jq_u[kJobSlots], jq_b[kJobSlots];
-    // Control wave only: requests of the next 64 units of the regular
-    // sequence (decoded 64 at a time, one per lane).
+    // Control wave only: requests of the next 64 units of the sequence
+    // (decoded 64 at a time, one per lane).
     int seq_b[64];
-    float jq_mt[kJobSlots], jq_md[kJobSlots], jq_ist[kJobSlots], jq_isd[kJobSlots];
     // Set once a bounded wait expired: every later wait returns at once.
     int abort_wait;
-    // After the loop: deferred draws of this workgroup and the one at hand.
-    int ntasks;
-    int tk_draw;                                 // 1: scan tk_chunk
-    int tk_chunk, tk_mode;                       // mode: 0 target row, 1 residual
-    double tk_thr;
-    float tk_mt, tk_md, tk_ist, tk_isd;
-    // After the loop: chunks of first rejections still to re-read (round
-    // indices of this workgroup), and the one at hand.
-    int rr_n;
-    int rr_round[64];
-    int rr_b, rr_i, rr_c, rr_tr;
-    float rr_mt, rr_md, rr_ist, rr_isd;
-    // Block-wide scratch (after the loop only, under barriers).
+    // Draw pass: the request's draw, set by wave 0 for the whole workgroup.
+    int dr_j, dr_k, dr_mode, dr_chunk;           // mode: 0 p (chunk dr_chunk), 1 residual
+    double dr_u, dr_thr;
+    float dr_mt, dr_md, dr_ist, dr_isd;
+    // Block-wide scratch of the draw pass (under barriers).
     double scan_ws[kBlocks];
     double red_d[kWaves];
     float red_f[kWaves];
@@ -638,15 +615,6 @@ __device__ void decide_greedy(const Params& P, const TeamPoll& pl, int b, int i,
     }
 }
 
-// Control wave: queue a deferred draw (team tr; bonus or rejection).
-__device__ __forceinline__ void add_task(const Params& P, int tr, bool bonus, int& ntasks) {
-    if ((threadIdx.x & 63) == 0 && ntasks < P.task_cap) {
-        st32(reinterpret_cast<unsigned*>(P.tasks) + (size_t)blockIdx.x * P.task_cap + ntasks,
-             (unsigned)(2 * tr + (bonus ? 1 : 0)));
-    }
-    ++ntasks;
-}
-
 // ---------------------------------------------------------- main kernel --
 
 // Coordinates of a work unit (uniform across the workgroup).
@@ -713,31 +681,51 @@ __device__ __forceinline__ Unit unit_from(const Params& P, const int* off, int u
     return d;
 }
 
+// A unit's two row segments as a data thread loads them: group j of data
+// thread dt holds the W elements from (dt + j * kDataThreads) * W.
+template <typename E>
+struct UnitRows {
+    const E* bt;       // target row segment
+    const E* bd;       // drafter row segment (null: not read)
+    int n;             // segment length
+    bool vt, vd;       // 16-byte loads are legal
+};
+
+template <typename E>
+__device__ __forceinline__ UnitRows<E> unit_rows(const Params& P, const Unit& d) {
+    const E* target = static_cast<const E*>(P.target);
+    const E* draft = static_cast<const E*>(P.draft);
+    UnitRows<E> w;
+    w.bt = target + ((size_t)d.b * (P.K + 1) + d.i) * (size_t)P.V + d.e0;
+    w.bd = d.has_d ? draft + ((size_t)d.b * P.K + d.i) * (size_t)P.V + d.e0 : nullptr;
+    w.n = d.n;
+    w.vt = aligned16(w.bt);
+    w.vd = d.has_d && aligned16(w.bd);
+    return w;
+}
+
+// Data thread dt: issue group j's loads of a unit (no wait).
+template <typename E, bool kVec>
+__device__ __forceinline__ void load_pair(const UnitRows<E>& w, int dt, int j, uint4& t, uint4& q) {
+    constexpr int W = Elem<E>::W;
+    const int e = (dt + j * kDataThreads) * W;
+    t = e < w.n ? load_group<E, kVec>(w.bt, e, w.n, w.vt) : neg_group<E>();
+    q = (w.bd != nullptr && e < w.n) ? load_group<E, kVec>(w.bd, e, w.n, w.vd) : neg_group<E>();
+}
+
 // Data waves: issue the 16-byte loads of a unit into registers (no wait).
 template <typename E, bool kVec>
 __device__ __forceinline__ void issue_loads(const Params& P, const Unit& d, int dt,
                                             uint4 (&gt)[kG], uint4 (&gd)[kG]) {
-    constexpr int W = Elem<E>::W;
-    const E* target = static_cast<const E*>(P.target);
-    const E* draft = static_cast<const E*>(P.draft);
-    const E* bt = target + ((size_t)d.b * (P.K + 1) + d.i) * (size_t)P.V + d.e0;
-    const E* bd = d.has_d ? draft + ((size_t)d.b * P.K + d.i) * (size_t)P.V + d.e0 : nullptr;
-    const bool vt = aligned16(bt);
-    const bool vd = d.has_d && aligned16(bd);
+    const UnitRows<E> w = unit_rows<E>(P, d);
     #pragma unroll
-    for (int j = 0; j < kG; ++j) {
-        const int e = (dt + j * kDataThreads) * W;
-        gt[j] = e < d.n ? load_group<E, kVec>(bt, e, d.n, vt) : neg_group<E>();
-        gd[j] = (d.has_d && e < d.n) ? load_group<E, kVec>(bd, e, d.n, vd) : neg_group<E>();
-    }
+    for (int j = 0; j < kG; ++j) load_pair<E, kVec>(w, dt, j, gt[j], gd[j]);
 }
 
 // Control wave: collect the data waves' statistics of the unit of round r,
 // merge them and publish the unit's record (epoch-tagged words, no wait).
-// Sampled: the chunk-0 member of a bonus position queues the bonus draw.
 template <typename E, bool kGreedy>
-__device__ __forceinline__ void control_unit(const Params& P, Shared& sh, const Unit& cur, int r,
-                                             int& ntasks) {
+__device__ __forceinline__ void control_unit(const Params& P, Shared& sh, const Unit& cur, int r) {
     const int lane = threadIdx.x & 63;
     const int C = P.C;
     const int slot = r % kMbox;
@@ -788,7 +776,6 @@ __device__ __forceinline__ void control_unit(const Params& P, Shared& sh, const 
             st64(rec + R_ST, tagged((float)St, ep));
             st64(rec + R_SD, tagged((float)Sd, ep));
         }
-        if (cur.i == cur.k && cur.c == 0) add_task(P, cur.tr, true, ntasks);
     }
 }
 
@@ -817,11 +804,9 @@ __device__ __forceinline__ void owed_issue(const Params& P, Owed& o, TeamPoll& p
 
 // Control wave: decide an owed team from its complete records. Greedy:
 // argmax, decision, completion. Sampled (a drafted position): p(x), q(x), the
-// accept decision, the decision word; a rejected team gets a deferred draw
-// (made only if it is the request's first rejection).
+// accept decision and the decision word (the draw pass reads them).
 template <bool kGreedy>
-__device__ __forceinline__ void owed_decide(const Params& P, const Owed& o, const TeamPoll& pl,
-                                            int& ntasks) {
+__device__ __forceinline__ void owed_decide(const Params& P, const Owed& o, const TeamPoll& pl) {
     const Unit& u = o.u;
     if (kGreedy) {
         decide_greedy(P, pl, u.b, u.i, u.k, u.tr);
@@ -844,75 +829,30 @@ __device__ __forceinline__ void owed_decide(const Params& P, const Owed& o, cons
         if (P.out_q) P.out_q[(size_t)u.b * K + u.i] = (float)qx;
         st64(dec_word(P, u.tr), ((unsigned long long)P.epoch << 32) | (accept ? 1u : 0u));
     }
-    if (!accept) add_task(P, u.tr, false, ntasks);
 }
 
 // -------------------------------------------------------------- planning --
 
-// Decision words of up to two positions' prefixes, one per half-wave: lanes
-// 0..31 read positions 0..i of request b (first candidate), lanes 32..63 the
-// second candidate's. Issued in one round, read in the same round after the
-// mailbox work.
-__device__ __forceinline__ unsigned long long prefix_issue(const Params& P, int b, int i, bool valid,
-                                                           int half) {
-    const int lane = threadIdx.x & 63;
-    const int t = lane - 32 * half;
-    if (valid && t >= 0 && t < 32 && t <= i) return ld64(dec_word(P, b * (P.K + 1) + t));
-    return 0;
-}
-
-// First-rejection status from a half-wave's loaded decision words (see
-// prefix_issue): 1 = position i rejected and every earlier one accepted,
-// 0 = not, -1 = not known yet.
-__device__ __forceinline__ int prefix_status(const Params& P, unsigned long long d, int i, int half) {
-    const int lane = threadIdx.x & 63;
-    const int t = lane - 32 * half;
-    const bool mine = t >= 0 && t < 32 && t <= i;
-    const bool known = !mine || (unsigned)(d >> 32) == P.epoch;
-    const unsigned long long rej = __ballot(mine && known && (d & 1ull) == 0) >> (32 * half);
-    const unsigned long long unknown = (__ballot(!known) >> (32 * half)) & 0xFFFFFFFFull;
-    if (rej != 0) {
-        const unsigned long long low = rej & (~rej + 1);
-        if ((unknown & (low - 1)) != 0) return -1;
-        return low == (1ull << i) ? 1 : 0;
-    }
-    return unknown == 0 ? 0 : -1;
-}
-
 // Control wave state of the streaming loop (uniform).
 struct CtrlState {
-    int next_unit;          // next regular unit of this workgroup's sequence
+    int next_unit;          // next unit of this workgroup's sequence
     int planned;            // rounds planned so far (plans 0 .. planned-1 exist)
     int end_round;          // round planned as the end (INT_MAX: not yet)
-    int pd_head, pd_tail;   // pending ring: drafted units awaiting first-rejection status
-    int fr_head, fr_tail;   // first-rejection ring: units whose team stats are to be loaded
-    int jq_head, jq_tail;   // job ring: re-read jobs ready to plan
     int ow_head, ow_tail;   // owed ring: chunk-0 units whose team was incomplete when polled
-    int seq_n;              // regular units planned so far
+    int seq_n;              // units planned so far
 };
 
-// Control wave: write the plan of the next round: a ready re-read job, else
-// the next regular unit, else the end.
+// Control wave: write the plan of the next round: the next unit of the
+// workgroup's sequence, else the end.
 __device__ __forceinline__ void plan_next(const Params& P, Shared& sh, CtrlState& cs, const int* off,
                                           int U) {
     const int q = cs.planned++;
     const int slot = q % kPlanSlots;
     int kind;
-    if (cs.jq_head != cs.jq_tail) {
-        kind = PL_JOB;
-        const int j = cs.jq_head++ % kJobSlots;
-        if ((threadIdx.x & 63) == 0) {
-            sh.pl_u[slot] = sh.jq_u[j];
-            sh.pl_b[slot] = sh.jq_b[j];
-            sh.pl_mt[slot] = sh.jq_mt[j];
-            sh.pl_md[slot] = sh.jq_md[j];
-            sh.pl_ist[slot] = sh.jq_ist[j];
-            sh.pl_isd[slot] = sh.jq_isd[j];
-        }
-    } else if (cs.next_unit < U) {
+    if (cs.next_unit < U) {
         kind = PL_UNIT;
         if ((cs.seq_n & 63) == 0) {
-            // Requests of the next 64 regular units, one binary search per lane.
+            // Requests of the next 64 units, one binary search per lane.
             const int lane = threadIdx.x & 63;
             const int u = cs.next_unit + lane * (int)gridDim.x;
             sh.seq_b[lane] = u < U ? request_of(P, off, u) : 0;
@@ -934,49 +874,31 @@ __device__ __forceinline__ void plan_next(const Params& P, Shared& sh, CtrlState
     }
 }
 
-// Push/pop helpers of the LDS rings (the control wave owns them; indices
-// live in registers, uniform).
-__device__ __forceinline__ void ring_put(int* ru, int* rb, int slots, int& tail, const Unit& u) {
-    if ((threadIdx.x & 63) == 0) {
-        ru[tail % slots] = u.u;
-        rb[tail % slots] = u.b;
-    }
-    ++tail;
-}
-
-// The control wave's loop. Every round issues all of its device-scope loads
-// first, does the mailbox work while they are in flight, then reads them:
+// The control wave's loop. Every round issues its device-scope loads first,
+// does the mailbox work while they are in flight, then reads them:
 //  P. plan round r + kPlanLead (the data waves read it at the end of round
 //     r + kPlanLead - 1, by which time this write is always done);
 //  1. issue: the team records of the chunk-0 unit consumed last round and of
-//     the oldest owed one (decisions), the decision words of the two oldest
-//     pending drafted units' request prefixes (first-rejection status), and
-//     the team records of the oldest first rejection (its normalisers);
-//  2. the data waves' results of round r: a regular unit's statistics are
-//     merged and published (a chunk-0 unit is decided next round, a drafted
-//     unit joins the pending ring); a job's residual mass is published;
+//     the oldest owed one;
+//  2. the data waves' results of round r: the unit's statistics are merged
+//     and published (a chunk-0 unit is decided from next round on);
 //  3. read what step 1 loaded: decide complete teams (an incomplete one is
-//     owed), settle pending units in order (a first rejection goes to the
-//     first-rejection ring), turn a loaded first rejection into a job.
+//     owed).
 // After the last round, owed decisions are waited for. Nothing the data
 // waves do waits on a decision.
 template <typename E, bool kGreedy, bool kVec>
-__device__ __forceinline__ int control_loop(const Params& P, Shared& sh, const int* off) {
+__device__ __forceinline__ void control_loop(const Params& P, Shared& sh, const int* off) {
     const int U = off[P.B];
     CtrlState cs;
     cs.next_unit = blockIdx.x;
     cs.planned = 0;
     cs.end_round = INT_MAX;
-    cs.pd_head = cs.pd_tail = 0;
-    cs.fr_head = cs.fr_tail = 0;
-    cs.jq_head = cs.jq_tail = 0;
     cs.ow_head = cs.ow_tail = 0;
     cs.seq_n = 0;
     for (int q = 0; q < kPlanLead && cs.end_round == INT_MAX; ++q) plan_next(P, sh, cs, off, U);
     Owed fresh;                      // chunk-0 unit consumed last round, to decide now
     fresh.u.u = -1;
-    int ntasks = 0;
-    TeamPoll pa, pb, pc;
+    TeamPoll pa, pb;
     for (int r = 0; r < cs.end_round; ++r) {
         // P.
         if (cs.end_round == INT_MAX && r + kPlanLead == cs.planned) plan_next(P, sh, cs, off, U);
@@ -991,113 +913,46 @@ __device__ __forceinline__ int control_loop(const Params& P, Shared& sh, const i
             old.x = sh.ow_x[j];
             owed_issue<E, kGreedy>(P, old, pb);
         }
-        Unit c0, c1;
-        c0.u = c1.u = -1;
-        unsigned long long dw = 0;
-        if (!kGreedy) {
-            if (cs.pd_head != cs.pd_tail) {
-                const int j = cs.pd_head % kPendSlots;
-                c0 = unit_from(P, off, sh.pd_u[j], sh.pd_b[j], false);
-            }
-            if (cs.pd_tail - cs.pd_head >= 2)
-                c1 = unit_from(P, off, sh.pd_u[(cs.pd_head + 1) % kPendSlots],
-                               sh.pd_b[(cs.pd_head + 1) % kPendSlots], false);
-            dw = prefix_issue(P, c0.b, c0.i, c0.u >= 0, 0) | prefix_issue(P, c1.b, c1.i, c1.u >= 0, 1);
-        }
-        Unit fj;
-        fj.u = -1;
-        if (!kGreedy && cs.fr_head != cs.fr_tail && cs.jq_tail - cs.jq_head < kJobSlots) {
-            fj = unit_from(P, off, sh.fr_u[cs.fr_head % kFirstSlots], sh.fr_b[cs.fr_head % kFirstSlots], false);
-            poll_issue<false>(P, fj.tr, pc);
-        }
         // 2.
         Owed next;
         next.u.u = -1;
         {
             const int slot = r % kPlanSlots;
-            const int kind = sh.pl_kind[slot];
             const Unit cur = unit_from(P, off, sh.pl_u[slot], sh.pl_b[slot], kGreedy);
-            if (kind == PL_UNIT) {
-                control_unit<E, kGreedy>(P, sh, cur, r, ntasks);
-                if (cur.c == 0 && (kGreedy || cur.has_d)) {
-                    next.u = cur;
-                    next.x = kGreedy ? 0 : P.tokens[(size_t)cur.b * P.K + cur.i];
-                }
-                if (!kGreedy && cur.has_d) {
-                    if (cs.pd_tail - cs.pd_head >= kPendSlots) ++cs.pd_head;   // oldest left to after the loop
-                    ring_put(sh.pd_u, sh.pd_b, kPendSlots, cs.pd_tail, cur);
-                }
-            } else {
-                // A job's residual mass: one partial per data wave.
-                const int lane = threadIdx.x & 63;
-                const int rs = r % kMbox;
-                double v = 0.0;
-                if (lane < kDataWaves) {
-                    lds_wait(P, sh, &sh.st_tag[rs][lane], r + 1);
-                    v = sh.st_st[rs][lane];
-                }
-                order();
-                if (lane == 0) lds_put(&sh.st_done[rs], r + 1);
-                v = wave_sum(v);
-                if (lane == 0) {
-                    st64(P.rec + ((size_t)cur.tr * P.C + cur.c) * kRecWords + R_RES,
-                         tagged((float)v, P.epoch));
-                }
+            control_unit<E, kGreedy>(P, sh, cur, r);
+            if (cur.c == 0 && (kGreedy || cur.has_d)) {
+                next.u = cur;
+                next.x = kGreedy ? 0 : P.tokens[(size_t)cur.b * P.K + cur.i];
             }
         }
         // 3.
         if (have_a) {
             if (poll_complete<kGreedy>(P, pa)) {
-                owed_decide<kGreedy>(P, fresh, pa, ntasks);
+                owed_decide<kGreedy>(P, fresh, pa);
             } else if (cs.ow_tail - cs.ow_head < kOwedSlots) {
-                if ((threadIdx.x & 63) == 0) sh.ow_x[cs.ow_tail % kOwedSlots] = fresh.x;
-                ring_put(sh.ow_u, sh.ow_b, kOwedSlots, cs.ow_tail, fresh.u);
+                const int j = cs.ow_tail++ % kOwedSlots;
+                if ((threadIdx.x & 63) == 0) {
+                    sh.ow_u[j] = fresh.u.u;
+                    sh.ow_b[j] = fresh.u.b;
+                    sh.ow_x[j] = fresh.x;
+                }
             } else {
                 poll_wait<kGreedy>(P, sh, fresh.u.tr, pa);   // ring full: wait (rare)
-                owed_decide<kGreedy>(P, fresh, pa, ntasks);
+                owed_decide<kGreedy>(P, fresh, pa);
             }
         }
         if (old.u.u >= 0 && poll_complete<kGreedy>(P, pb)) {
-            owed_decide<kGreedy>(P, old, pb, ntasks);
+            owed_decide<kGreedy>(P, old, pb);
             ++cs.ow_head;
         }
         fresh = next;
-        if (!kGreedy) {
-            if (c0.u >= 0) {
-                const int s0 = prefix_status(P, dw, c0.i, 0);
-                if (s0 >= 0) {
-                    ++cs.pd_head;
-                    if (s0 == 1 && cs.fr_tail - cs.fr_head < kFirstSlots) ring_put(sh.fr_u, sh.fr_b, kFirstSlots, cs.fr_tail, c0);
-                    if (c1.u >= 0) {
-                        const int s1 = prefix_status(P, dw, c1.i, 1);
-                        if (s1 >= 0) {
-                            ++cs.pd_head;
-                            if (s1 == 1 && cs.fr_tail - cs.fr_head < kFirstSlots) ring_put(sh.fr_u, sh.fr_b, kFirstSlots, cs.fr_tail, c1);
-                        }
-                    }
-                }
-            }
-            if (fj.u >= 0 && poll_complete<false>(P, pc)) {
-                const TeamStats ts = team_stats(P, pc);
-                const int j = cs.jq_tail++ % kJobSlots;
-                if ((threadIdx.x & 63) == 0) {
-                    sh.jq_u[j] = fj.u;
-                    sh.jq_b[j] = fj.b;
-                    sh.jq_mt[j] = ts.mt;
-                    sh.jq_md[j] = ts.md;
-                    sh.jq_ist[j] = (float)(1.0 / ts.st);
-                    sh.jq_isd[j] = (float)(1.0 / ts.sd);
-                }
-                ++cs.fr_head;
-            }
-        }
     }
     // Decisions still owed: wait for their records.
     TeamPoll pl;
     if (fresh.u.u >= 0) {
         poll_wait<kGreedy>(P, sh, fresh.u.tr, pl);
         owed_issue<E, kGreedy>(P, fresh, pl);
-        owed_decide<kGreedy>(P, fresh, pl, ntasks);
+        owed_decide<kGreedy>(P, fresh, pl);
     }
     while (cs.ow_head != cs.ow_tail) {
         const int j = cs.ow_head % kOwedSlots;
@@ -1106,15 +961,14 @@ __device__ __forceinline__ int control_loop(const Params& P, Shared& sh, const i
         o.x = sh.ow_x[j];
         poll_wait<kGreedy>(P, sh, o.u.tr, pl);
         owed_issue<E, kGreedy>(P, o, pl);
-        owed_decide<kGreedy>(P, o, pl, ntasks);
+        owed_decide<kGreedy>(P, o, pl);
         ++cs.ow_head;
     }
-    return ntasks;
 }
 
 // The data waves' loop: each round reads its plan, reduces the unit in
-// registers (or, for a job, its residual mass), issues the loads of the next
-// planned round, and posts its results to the control wave.
+// registers, issues the loads of the next planned round, and posts its
+// results to the control wave.
 template <typename E, bool kGreedy, bool kVec>
 __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int* off) {
     constexpr int W = Elem<E>::W;
@@ -1130,7 +984,6 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
         lds_wait(P, sh, &sh.pl_tag[slot], q);
         kind = sh.pl_kind[slot];
         u = unit_from(P, off, kind == PL_END ? -1 : sh.pl_u[slot], sh.pl_b[slot], kGreedy);
-        if (kind == PL_JOB) u.has_d = true;
     };
 
     uint4 gt[kG], gd[kG];
@@ -1141,37 +994,12 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
     issue_loads<E, kVec>(P, cur, dt, gt, gd);
     for (int r = 0;; ++r) {
         const int slot = r % kMbox;
-        const int ps = r % kPlanSlots;
         Unit nxt;
         int nkind;
         double post_a = 0.0, post_b = 0.0;
         float post_mt = -INFINITY, post_md = -INFINITY;
         int post_idx = INT_MAX;
-        if (!kGreedy && kind == PL_JOB) {
-            // Residual mass of the chunk with the team's normalisers.
-            const float mt = sh.pl_mt[ps], md = sh.pl_md[ps];
-            const float ist = sh.pl_ist[ps], isd = sh.pl_isd[ps];
-            float lr = 0.0f;
-            #pragma unroll
-            for (int j = 0; j < kG; ++j) {
-                float m8[W];
-                #pragma unroll
-                for (int kk = 0; kk < W; ++kk) {
-                    const float pv = fast_exp2((Elem<E>::at(gt[j], kk) - mt) * cs) * ist;
-                    const float qv = fast_exp2((Elem<E>::at(gd[j], kk) - md) * cs) * isd;
-                    m8[kk] = fmaxf(0.0f, pv - qv);
-                }
-                #pragma unroll
-                for (int h = W / 2; h > 0; h >>= 1) {
-                    #pragma unroll
-                    for (int kk = 0; kk < h; ++kk) m8[kk] += m8[kk + h];
-                }
-                lr += m8[0];
-            }
-            read_plan(r + 1, nxt, nkind);
-            if (nkind != PL_END) issue_loads<E, kVec>(P, nxt, dt, gt, gd);
-            post_a = wave_sum((double)lr);
-        } else if (kGreedy) {
+        if (kGreedy) {
             float bv = -INFINITY;
             int bi = INT_MAX;
             #pragma unroll
@@ -1217,38 +1045,35 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
             }
             mt = wave_max(mt);
             md = wave_max(md);
-            float lt = 0.0f, ld = 0.0f;
-            if (mt != -INFINITY) {
-                #pragma unroll
-                for (int j = 0; j < kG; ++j) {
-                    float e[W];
-                    #pragma unroll
-                    for (int kk = 0; kk < W; ++kk) e[kk] = fast_exp2((Elem<E>::at(gt[j], kk) - mt) * cs);
-                    #pragma unroll
-                    for (int h = W / 2; h > 0; h >>= 1) {
-                        #pragma unroll
-                        for (int kk = 0; kk < h; ++kk) e[kk] += e[kk + h];
-                    }
-                    lt += e[0];
-                }
-            }
-            if (cur.has_d && md != -INFINITY) {
-                #pragma unroll
-                for (int j = 0; j < kG; ++j) {
-                    float e[W];
-                    #pragma unroll
-                    for (int kk = 0; kk < W; ++kk) e[kk] = fast_exp2((Elem<E>::at(gd[j], kk) - md) * cs);
-                    #pragma unroll
-                    for (int h = W / 2; h > 0; h >>= 1) {
-                        #pragma unroll
-                        for (int kk = 0; kk < h; ++kk) e[kk] += e[kk + h];
-                    }
-                    ld += e[0];
-                }
-            }
-            // The unit's data is consumed: stream the next one.
+            // Exp pass, group by group; as soon as a group is consumed its
+            // registers take the next unit's group (loads overlap the rest
+            // of the pass).
             read_plan(r + 1, nxt, nkind);
-            if (nkind != PL_END) issue_loads<E, kVec>(P, nxt, dt, gt, gd);
+            const bool more = nkind != PL_END;
+            UnitRows<E> nw;
+            if (more) nw = unit_rows<E>(P, nxt);
+            const bool do_t = mt != -INFINITY, do_d = cur.has_d && md != -INFINITY;
+            float lt = 0.0f, ld = 0.0f;
+            #pragma unroll
+            for (int j = 0; j < kG; ++j) {
+                float e[W], f[W];
+                #pragma unroll
+                for (int kk = 0; kk < W; ++kk) {
+                    e[kk] = do_t ? fast_exp2((Elem<E>::at(gt[j], kk) - mt) * cs) : 0.0f;
+                    f[kk] = do_d ? fast_exp2((Elem<E>::at(gd[j], kk) - md) * cs) : 0.0f;
+                }
+                if (more) load_pair<E, kVec>(nw, dt, j, gt[j], gd[j]);
+                #pragma unroll
+                for (int h = W / 2; h > 0; h >>= 1) {
+                    #pragma unroll
+                    for (int kk = 0; kk < h; ++kk) {
+                        e[kk] += e[kk + h];
+                        f[kk] += f[kk + h];
+                    }
+                }
+                lt += e[0];
+                ld += f[0];
+            }
             post_a = wave_sum((double)lt);
             post_b = wave_sum((double)ld);
             post_mt = mt;
@@ -1270,214 +1095,7 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
     }
 }
 
-// ------------------------------------------------------- after the loop --
-
-// Control wave: which of this workgroup's drafted units (rounds base ..
-// base+63 of its regular sequence, lane = round - base) are chunks of a
-// request's first rejection whose residual mass is not published yet?
-template <bool kGreedy>
-__device__ void scan_members(const Params& P, Shared& sh, const int* off, int base) {
-    const int lane = threadIdx.x & 63;
-    const int U = off[P.B];
-    const unsigned ep = P.epoch;
-    const Unit u = decode_unit(P, off, blockIdx.x + (base + lane) * gridDim.x, U, kGreedy);
-    bool need = false;
-    if (u.u >= 0 && u.has_d) {
-        const unsigned long long rw =
-            ld64(P.rec + ((size_t)u.tr * P.C + u.c) * kRecWords + R_RES);
-        if (!tag_ok(rw, ep)) {
-            // Position u.i is the first rejection iff it is rejected and every
-            // earlier position accepted (bounded wait for their decisions).
-            const int K = P.K;
-            for (unsigned it = 0;; ++it) {
-                int status = -1;                           // -1 unknown, 0 not first, 1 first
-                for (int t = 0; t <= u.i; ++t) {
-                    const unsigned long long d = ld64(dec_word(P, u.b * (K + 1) + t));
-                    if ((unsigned)(d >> 32) != ep) {
-                        status = -1;
-                        break;
-                    }
-                    const bool rej = (d & 1ull) == 0;
-                    if (t < u.i && rej) {
-                        status = 0;
-                        break;
-                    }
-                    if (t == u.i) status = rej ? 1 : 0;
-                }
-                if (status >= 0) {
-                    need = status == 1;
-                    break;
-                }
-                if (it >= kSpinLimit || lds_get(&sh.abort_wait)) {
-                    give_up(P, sh);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
-            }
-        }
-    }
-    const unsigned long long m = __ballot(need);
-    if (need) sh.rr_round[__popcll(m & ((1ull << lane) - 1))] = base + lane;
-    if (lane == 0) sh.rr_n = __popcll(m);
-}
-
-// Whole workgroup, step 3: re-read the chunk of one first-rejection unit and
-// publish its residual mass sum max(0, p - q) with the team's normalisers.
-template <typename E, bool kVec>
-__device__ void reread_residual(const Params& P, Shared& sh, const int* off, int round) {
-    constexpr int W = Elem<E>::W;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int U = off[P.B];
-    if (wave == 0) {
-        const Unit u = decode_unit(P, off, blockIdx.x + round * gridDim.x, U, false);
-        const TeamStats ts = merge_team(P, sh, u.tr);
-        if (lane == 0) {
-            sh.rr_b = u.b;
-            sh.rr_i = u.i;
-            sh.rr_c = u.c;
-            sh.rr_tr = u.tr;
-            sh.rr_mt = ts.mt;
-            sh.rr_md = ts.md;
-            sh.rr_ist = (float)(1.0 / ts.st);
-            sh.rr_isd = (float)(1.0 / ts.sd);
-        }
-    }
-    __syncthreads();
-    float lr = 0.0f;
-    if (wave > 0) {
-        Unit u;
-        u.b = sh.rr_b;
-        u.i = sh.rr_i;
-        u.c = sh.rr_c;
-        u.e0 = u.c * P.CE;
-        u.n = min(P.CE, P.V - u.e0);
-        u.has_d = true;
-        uint4 gt[kG], gd[kG];
-        issue_loads<E, kVec>(P, u, tid - 64, gt, gd);
-        const float mt = sh.rr_mt, md = sh.rr_md, ist = sh.rr_ist, isd = sh.rr_isd;
-        const float cs = P.c32;
-        #pragma unroll
-        for (int j = 0; j < kG; ++j) {
-            float m8[W];
-            #pragma unroll
-            for (int kk = 0; kk < W; ++kk) {
-                const float pv = fast_exp2((Elem<E>::at(gt[j], kk) - mt) * cs) * ist;
-                const float qv = fast_exp2((Elem<E>::at(gd[j], kk) - md) * cs) * isd;
-                m8[kk] = fmaxf(0.0f, pv - qv);
-            }
-            #pragma unroll
-            for (int h = W / 2; h > 0; h >>= 1) {
-                #pragma unroll
-                for (int kk = 0; kk < h; ++kk) m8[kk] += m8[kk + h];
-            }
-            lr += m8[0];
-        }
-    }
-    const double v = wave_sum((double)lr);
-    if (lane == 0) sh.red_d[wave] = v;
-    __syncthreads();
-    if (tid == 0) {
-        double tot = 0.0;
-        for (int w = 1; w < kWaves; ++w) tot += sh.red_d[w];
-        st64(P.rec + ((size_t)sh.rr_tr * P.C + sh.rr_c) * kRecWords + R_RES,
-             tagged((float)tot, P.epoch));
-    }
-    __syncthreads();
-}
-
-// Control wave, one deferred draw: does it draw (is it its request's
-// deciding position)? If so, locate the chunk holding the threshold -- over
-// the residual masses of the team's chunks for a first rejection, over p for
-// the bonus position (or a residual without mass) -- and leave the element
-// scan to the whole workgroup. Each attempt is one round of loads: the
-// decision words of the earlier positions (lane t: position t) and the
-// team's records and residual masses (lane c: chunk c).
-__device__ void task_prepare(const Params& P, Shared& sh, int task) {
-    const int lane = threadIdx.x & 63;
-    const int K = P.K, C = P.C;
-    const unsigned ep = P.epoch;
-    const int tr = task >> 1;
-    const bool bonus = task & 1;
-    const int b = tr / (K + 1), i = tr - b * (K + 1);
-    unsigned long long* rec = P.rec + (size_t)tr * C * kRecWords;
-    TeamPoll pl;
-    unsigned long long rr = 0;
-    bool draw = false;
-    for (unsigned it = 0;; ++it) {
-        const unsigned long long d = lane < i ? ld64(dec_word(P, b * (K + 1) + lane)) : 0ull;
-        poll_issue<false>(P, tr, pl);
-        if (!bonus && lane < C) rr = ld64(rec + lane * kRecWords + R_RES);
-        // A rejection draws only as its request's first; the bonus position
-        // only if every drafted position was accepted.
-        const bool known = lane >= i || (unsigned)(d >> 32) == ep;
-        if (__ballot(lane < i && known && (d & 1ull) == 0) != 0) break;
-        if (__ballot(!known) == 0) {
-            bool ok = bonus || lane >= C || tag_ok(rr, ep);
-            for (int cc = lane + 64; !bonus && cc < C; cc += 64) ok = ok && tag_ok(ld64(rec + cc * kRecWords + R_RES), ep);
-            if (poll_complete<false>(P, pl) && __ballot(!ok) == 0) {
-                draw = true;
-                break;
-            }
-        }
-        if (it >= kSpinLimit || lds_get(&sh.abort_wait)) {
-            if (lane == 0) give_up(P, sh);
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-    }
-    int chunk = -1, mode = 0;
-    double thr = 0.0;
-    TeamStats ts;
-    ts.mt = ts.md = 0.0f;
-    ts.st = ts.sd = 1.0;
-    if (draw) {
-        ts = team_stats(P, pl);
-        const uint4 rw = philox4x32_10((uint32_t)(P.bbase + b), (uint32_t)i, 0u, 0u, P.key0, P.key1);
-        const double u = word_to_uniform(rw.y);
-        double total = 0.0, base = 0.0;
-        // Chunk cc's words: lane cc holds them for cc < 64.
-        auto word = [&](int cc, int f, unsigned long long held) -> float {
-            return tag_val(cc == lane ? held : ld64(rec + cc * kRecWords + f));
-        };
-        if (!bonus) {
-            auto rmass = [&](int cc) -> double {
-                const float v = word(cc, R_RES, rr);
-                return v > 0.0f ? (double)v : 0.0;
-            };
-            for (int cc = lane; cc < C; cc += 64) total += rmass(cc);
-            total = wave_sum(total);
-            if (total > 0.0) {
-                chunk_crossing(C, u * total, rmass, chunk, base);
-                mode = 1;
-            }
-        }
-        if (chunk < 0 && ts.st > 0.0) {
-            // Bonus draw, or a residual without mass (rounding only): from p_i.
-            mode = 0;
-            const double inv = 1.0 / ts.st;
-            auto pmass = [&](int cc) -> double {
-                const float s1 = word(cc, R_ST, pl.w[R_ST]);
-                const float m1 = word(cc, R_MT, pl.w[R_MT]);
-                return s1 > 0.0f ? (double)s1 * exp2(((double)m1 - (double)ts.mt) * P.c64) * inv : 0.0;
-            };
-            total = 0.0;
-            for (int cc = lane; cc < C; cc += 64) total += pmass(cc);
-            total = wave_sum(total);
-            chunk_crossing(C, u * total, pmass, chunk, base);
-        }
-        thr = u * total - base;
-    }
-    if (lane == 0) {
-        sh.tk_draw = draw;
-        sh.tk_chunk = chunk;
-        sh.tk_mode = mode;
-        sh.tk_thr = thr;
-        sh.tk_mt = ts.mt;
-        sh.tk_md = ts.md;
-        sh.tk_ist = (float)(1.0 / ts.st);
-        sh.tk_isd = (float)(1.0 / ts.sd);
-    }
-}
+// ------------------------------------------------------------- draw pass --
 
 // Element-level inverse CDF inside one chunk (whole workgroup). The data
 // waves load the chunk once, in the streaming layout: group j of data thread
@@ -1575,61 +1193,6 @@ __device__ int chunk_scan(const Params& P, Shared& sh, const Unit& d, float mt, 
     return sh.red_i[0];
 }
 
-// After both loops (whole workgroup, under barriers): re-read the chunks of
-// first rejections whose residual mass the loop did not publish, then make
-// this workgroup's draws. The re-reads wait only on decisions (taken in the
-// loops); the draws wait on residual masses (published in the loops or by
-// the re-reads), so no wait is circular.
-template <typename E, bool kVec>
-__device__ void after_loop(const Params& P, Shared& sh, const int* off) {
-    const int K = P.K;
-    const int tid = threadIdx.x, wave = tid >> 6;
-    const int nt = min(sh.ntasks, P.task_cap);
-    const int U = off[P.B];
-    const int rounds = (int)blockIdx.x < U ? (U - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
-    // Re-reads, 64 rounds of the regular sequence at a time.
-    for (int base = 0; base < rounds; base += 64) {
-        if (wave == 0) scan_members<false>(P, sh, off, base);
-        __syncthreads();
-        const int n = sh.rr_n;
-        for (int j = 0; j < n; ++j) reread_residual<E, kVec>(P, sh, off, sh.rr_round[j]);
-        __syncthreads();
-    }
-    // Draws.
-    unsigned* list = reinterpret_cast<unsigned*>(P.tasks) + (size_t)blockIdx.x * P.task_cap;
-    for (int t = 0; t < nt; ++t) {
-        const int task = (int)ld32(list + t);
-        if (wave == 0) task_prepare(P, sh, task);
-        __syncthreads();
-        if (!sh.tk_draw) {                         // uniform: not the request's deciding position
-            __syncthreads();
-            continue;
-        }
-        const int tr = task >> 1;
-        const int b = tr / (K + 1), i = tr - b * (K + 1);
-        int y = 0;
-        if (sh.tk_chunk >= 0) {
-            Unit d;
-            d.b = b;
-            d.i = i;
-            d.c = sh.tk_chunk;
-            d.e0 = d.c * P.CE;
-            d.n = min(P.CE, P.V - d.e0);
-            d.has_d = sh.tk_mode == 1;
-            const int o = chunk_scan<E, kVec>(P, sh, d, sh.tk_mt, sh.tk_ist, sh.tk_md, sh.tk_isd,
-                                              sh.tk_thr);
-            y = o < 0 ? 0 : d.e0 + o;
-        }
-        if (tid == 0) {
-            // The request's budget, clamped as in the prologue.
-            int k = P.budgets[b];
-            k = k < 0 ? 0 : (k > K ? K : k);
-            request_outputs<false>(P, b, k, i, y);
-        }
-        __syncthreads();
-    }
-}
-
 template <typename E, bool kGreedy, bool kVec>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void verify_kernel(Params P) {
@@ -1680,17 +1243,222 @@ void verify_kernel(Params P) {
         __syncthreads();
     }
 
-    // Wave specialisation (the branch is uniform per wave). No barrier
-    // until both loops are done.
+    // Wave specialisation (the branch is uniform per wave); no barrier
+    // after it.
     if (__builtin_amdgcn_readfirstlane(wave) == 0) {
-        const int nt = control_loop<E, kGreedy, kVec>(P, sh, off);
-        if (lane == 0) sh.ntasks = nt;
-        drain();                                   // task list entries are written
+        control_loop<E, kGreedy, kVec>(P, sh, off);
     } else {
         data_loop<E, kGreedy, kVec>(P, sh, off);
     }
+}
+
+// Wave 0: the chunk of team tr's target row (records in pl, normalisers ts)
+// where the running p mass, chunk by chunk, first exceeds u times the row's
+// total; thr = the part of that threshold inside the chunk. chunk -1: no
+// mass.
+__device__ void p_chunk(const Params& P, const TeamPoll& pl, const TeamStats& ts, double u,
+                        int& chunk, double& thr) {
+    const int lane = threadIdx.x & 63;
+    const int C = P.C;
+    unsigned long long* rec = team_rec(P, pl.tr);
+    chunk = -1;
+    thr = 0.0;
+    if (!(ts.st > 0.0)) return;
+    const double inv = 1.0 / ts.st;
+    // Chunk cc's words: lane cc holds them for cc < 64.
+    auto pmass = [&](int cc) -> double {
+        const float s1 = tag_val(cc == lane ? pl.w[R_ST] : ld64(rec + cc * kRecWords + R_ST));
+        const float m1 = tag_val(cc == lane ? pl.w[R_MT] : ld64(rec + cc * kRecWords + R_MT));
+        return s1 > 0.0f ? (double)s1 * exp2(((double)m1 - (double)ts.mt) * P.c64) * inv : 0.0;
+    };
+    double total = 0.0;
+    for (int cc = lane; cc < C; cc += 64) total += pmass(cc);
+    total = wave_sum(total);
+    double base = 0.0;
+    chunk_crossing(C, u * total, pmass, chunk, base);
+    thr = u * total - base;
+}
+
+// Sampled mode, second pass: one workgroup per request, launched after the
+// streaming pass on the same stream, so every decision word and record is
+// final. Wave 0 finds the request's deciding position j (the first rejected
+// drafted position, k if all k were accepted), merges team j's records into
+// its normalisers and takes the sampling uniform u. A first rejection draws
+// from the residual max(0, p_j - q_j): the data waves stream target row j and
+// drafter row j once, leaving the residual mass of every (chunk, group, data
+// wave) block in LDS; wave 0 finds the block where the running mass first
+// exceeds u R, and that block's wave scans its elements again. The bonus
+// position, or a residual without mass (rounding only), draws from p_j: its
+// chunk masses follow from the records and one chunk is scanned.
+template <typename E, bool kVec>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void draw_kernel(Params P) {
+    extern __shared__ __align__(16) unsigned char dyn_smem[];
+    __shared__ Shared sh;
+    double* blk = reinterpret_cast<double*>(dyn_smem);   // [C * kBlocks] residual block masses
+    constexpr int W = Elem<E>::W;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = blockIdx.x;
+    const int K = P.K, C = P.C;
+    const unsigned ep = P.epoch;
+    TeamPoll pl;                                   // wave 0: team j's records
+    TeamStats ts;
+    if (wave == 0) {
+        int k = P.budgets[b];
+        k = k < 0 ? 0 : (k > K ? K : k);
+        // Lane t: the decision of position t < k.
+        const unsigned long long d = lane < k ? ld64(dec_word(P, b * (K + 1) + lane)) : 0ull;
+        const bool known = lane >= k || (unsigned)(d >> 32) == ep;
+        if (__ballot(!known) != 0 && lane == 0) atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);
+        const unsigned long long rej = __ballot(lane < k && (!known || (d & 1ull) == 0));
+        const int j = rej ? __ffsll((long long)rej) - 1 : k;
+        poll_issue<false>(P, b * (K + 1) + j, pl);
+        if (!poll_complete<false>(P, pl) && lane == 0) atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);
+        ts = team_stats(P, pl);
+        const uint4 rw = philox4x32_10((uint32_t)(P.bbase + b), (uint32_t)j, 0u, 0u, P.key0, P.key1);
+        const double u = word_to_uniform(rw.y);
+        int chunk = -1;
+        double thr = 0.0;
+        if (j == k) p_chunk(P, pl, ts, u, chunk, thr);
+        if (lane == 0) {
+            sh.dr_j = j;
+            sh.dr_k = k;
+            sh.dr_mode = j < k ? 1 : 0;
+            sh.dr_chunk = chunk;
+            sh.dr_u = u;
+            sh.dr_thr = thr;
+            sh.dr_mt = ts.mt;
+            sh.dr_md = ts.md;
+            sh.dr_ist = (float)(1.0 / ts.st);
+            sh.dr_isd = (float)(1.0 / ts.sd);
+        }
+    }
     __syncthreads();
-    if (!kGreedy) after_loop<E, kVec>(P, sh, off);
+    const int j = sh.dr_j, k = sh.dr_k;
+    const float mt = sh.dr_mt, md = sh.dr_md, ist = sh.dr_ist, isd = sh.dr_isd;
+    const float c = P.c32;
+    auto rmass = [&](const uint4& t, const uint4& q, int kk) -> float {
+        const float pv = fast_exp2((Elem<E>::at(t, kk) - mt) * c) * ist;
+        const float qv = fast_exp2((Elem<E>::at(q, kk) - md) * c) * isd;
+        return fmaxf(0.0f, pv - qv);
+    };
+    auto chunk_unit = [&](int cc) -> Unit {
+        Unit d;
+        d.u = 0;
+        d.b = b;
+        d.i = j;
+        d.k = k;
+        d.c = cc;
+        d.tr = b * (K + 1) + j;
+        d.e0 = cc * P.CE;
+        d.n = min(P.CE, P.V - d.e0);
+        d.has_d = true;
+        return d;
+    };
+    int y = 0;
+    int mode = sh.dr_mode;
+    if (mode == 1) {
+        // Residual: stream both rows once (the next chunk's loads in flight
+        // while a chunk is reduced); block masses to LDS.
+        if (wave > 0) {
+            const int dt = tid - 64;
+            auto reduce = [&](int cc, const uint4 (&t)[kG], const uint4 (&q)[kG]) {
+                #pragma unroll
+                for (int g = 0; g < kG; ++g) {
+                    float sg = 0.0f;
+                    #pragma unroll
+                    for (int kk = 0; kk < W; ++kk) sg += rmass(t[g], q[g], kk);
+                    const double ws = wave_sum((double)sg);
+                    if (lane == 0) blk[cc * kBlocks + g * kDataWaves + wave - 1] = ws;
+                }
+            };
+            uint4 ta[kG], qa[kG], tb[kG], qb[kG];
+            issue_loads<E, kVec>(P, chunk_unit(0), dt, ta, qa);
+            for (int cc = 0; cc < C; cc += 2) {
+                if (cc + 1 < C) issue_loads<E, kVec>(P, chunk_unit(cc + 1), dt, tb, qb);
+                reduce(cc, ta, qa);
+                if (cc + 1 < C) {
+                    if (cc + 2 < C) issue_loads<E, kVec>(P, chunk_unit(cc + 2), dt, ta, qa);
+                    reduce(cc + 1, tb, qb);
+                }
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const int nb = C * kBlocks;
+            double total = 0.0;
+            for (int x = lane; x < nb; x += 64) total += blk[x];
+            total = wave_sum(total);
+            int star = -1;
+            double base = 0.0;
+            const double t = sh.dr_u * total;
+            if (total > 0.0) chunk_crossing(nb, t, [&](int x) -> double { return blk[x]; }, star, base);
+            int chunk = -1;
+            double thr = t - base;
+            if (star < 0) p_chunk(P, pl, ts, sh.dr_u, chunk, thr);   // no residual mass
+            if (lane == 0) {
+                sh.dr_mode = star >= 0 ? 1 : 0;
+                sh.sub_star = star;
+                sh.dr_chunk = chunk;
+                sh.dr_thr = thr;
+            }
+        }
+        __syncthreads();
+        mode = sh.dr_mode;
+        if (mode == 1) {
+            const int star = sh.sub_star;
+            const int cc = star / kBlocks, l = star - cc * kBlocks;
+            const int g = l / kDataWaves, w = l - g * kDataWaves;
+            if (wave == 1 + w) {
+                // The block's elements again (just read: cache-resident).
+                const Unit d = chunk_unit(cc);
+                const E* target = static_cast<const E*>(P.target);
+                const E* draft = static_cast<const E*>(P.draft);
+                const E* rt = target + ((size_t)b * (K + 1) + j) * (size_t)P.V + d.e0;
+                const E* rd = draft + ((size_t)b * K + j) * (size_t)P.V + d.e0;
+                const int e = (g * kDataThreads + w * 64 + lane) * W;
+                const uint4 t4 = load_group<E, kVec>(rt, e, d.n, aligned16(rt));
+                const uint4 q4 = load_group<E, kVec>(rd, e, d.n, aligned16(rd));
+                float r[W];
+                double pre[W];
+                double run = 0.0;
+                #pragma unroll
+                for (int kk = 0; kk < W; ++kk) {
+                    r[kk] = rmass(t4, q4, kk);
+                    run += (double)r[kk];
+                    pre[kk] = run;
+                }
+                const double incl = wave_incl_scan(run, lane);
+                const double up = __shfl_up(incl, 1, 64);
+                const double excl = lane ? up : 0.0;
+                const double tt = sh.dr_thr;
+                int cand = INT_MAX, last = -1;
+                #pragma unroll
+                for (int kk = 0; kk < W; ++kk) {
+                    if (r[kk] > 0.0f) {
+                        last = e + kk;
+                        if (cand == INT_MAX && excl + pre[kk] > tt) cand = e + kk;
+                    }
+                }
+                #pragma unroll
+                for (int o = 32; o > 0; o >>= 1) {
+                    cand = min(cand, __shfl_xor(cand, o, 64));
+                    last = max(last, __shfl_xor(last, o, 64));
+                }
+                if (lane == 0) sh.red_i[0] = d.e0 + (cand != INT_MAX ? cand : last);
+            }
+            __syncthreads();
+            y = sh.red_i[0];
+        }
+    }
+    if (mode == 0 && sh.dr_chunk >= 0) {
+        // From p_j: one chunk.
+        Unit d = chunk_unit(sh.dr_chunk);
+        d.has_d = false;
+        const int o = chunk_scan<E, kVec>(P, sh, d, mt, ist, md, isd, sh.dr_thr);
+        y = o < 0 ? 0 : d.e0 + o;
+    }
+    if (tid == 0) request_outputs<false>(P, b, k, j, y);
 }
 
 // Philox blocks as the verifier draws them, for checking the generator.
@@ -1720,10 +1488,10 @@ int chunks_for(int vocab, int dtype) {
     return (vocab + ce - 1) / ce;
 }
 
-size_t dyn_smem_bytes(int B, bool greedy) {
-    (void)greedy;
-    return (size_t)(B + 1) * sizeof(int);
-}
+size_t dyn_smem_bytes(int B) { return (size_t)(B + 1) * sizeof(int); }
+
+// The draw pass keeps one residual mass per (chunk, group, data wave) block.
+size_t draw_smem_bytes(int C) { return (size_t)C * kBlocks * sizeof(double); }
 
 }  // namespace
 
@@ -1738,8 +1506,6 @@ struct spec_verify_ctx {
     unsigned* result;
     unsigned* req_count;
     unsigned* status;
-    int* tasks;
-    size_t task_words;             // entries of the task lists' region
     unsigned calls;                // calls made so far (phase-word epochs)
     // occupancy cache: dynamic LDS bytes -> resident workgroups per CU, per kernel
     size_t occ_smem[8];
@@ -1762,24 +1528,25 @@ int occupancy_of(spec_verify_ctx* ctx, int slot, size_t smem) {
     return n;
 }
 
-// Launch shape: every workgroup resident (grid = CUs x occupancy); the
-// schedule needs at least as many workgroups as a team has members.
+// Launch shape of the streaming pass: every workgroup resident (grid = CUs x
+// occupancy); the schedule needs at least as many workgroups as a team has
+// members. Sampled mode then runs the draw pass, one workgroup per request.
 template <typename E, bool G, bool Vv>
 int launch(spec_verify_ctx* ctx, Params& p, hipStream_t stream) {
     const int slot = (std::is_same<E, uint16_t>::value ? 4 : 0) + (G ? 2 : 0) + (Vv ? 1 : 0);
-    const size_t smem = dyn_smem_bytes(p.B, G);
+    const size_t smem = dyn_smem_bytes(p.B);
     const int occ = occupancy_of<E, G, Vv>(ctx, slot, smem);
     const long long grid = (long long)ctx->cus * occ;
     if (grid < (long long)p.C) return SV_ERR_ARG;   // a team would not fit
-    // Task lists: at most two deferred draws per round of a workgroup.
-    const long long units = (long long)p.B * (p.K + 1) * p.C;
-    const long long cap = 2 * ((units + grid - 1) / grid) + 2;
-    if (cap > INT_MAX || (size_t)(grid * cap) > ctx->task_words) return SV_ERR_ARG;
-    p.tasks = ctx->tasks;
-    p.task_cap = (int)cap;
     hipLaunchKernelGGL((verify_kernel<E, G, Vv>), dim3((unsigned)grid), dim3(kThreads), smem, stream,
                        p);
-    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+    if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+    if (!G) {
+        hipLaunchKernelGGL((draw_kernel<E, Vv>), dim3((unsigned)p.B), dim3(kThreads),
+                           draw_smem_bytes(p.C), stream, p);
+        if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+    }
+    return SV_OK;
 }
 
 bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -1872,11 +1639,7 @@ int spec_verify_init(spec_verify_ctx** out, int device, int max_batch, int max_k
     const size_t team_bytes = round256(teams * kTeamWords * 4);
     const size_t result_bytes = round256(teams * 4);
     const size_t req_bytes = round256((size_t)max_batch * kReqStride * 4);
-    // Task lists: 2 entries per unit plus 4 per workgroup bound every launch
-    // (at most 4 resident workgroups per CU of 8 waves; 16 allowed for).
-    c->task_words = 2 * teams * (size_t)c->C + 4 * (size_t)c->cus * 16;
-    const size_t task_bytes = round256(c->task_words * 4);
-    const size_t total = rec_bytes + team_bytes + result_bytes + req_bytes + task_bytes + 256;
+    const size_t total = rec_bytes + team_bytes + result_bytes + req_bytes + 256;
     if (rc == SV_OK && hipMalloc(&c->ws, total) != hipSuccess) {
         c->ws = nullptr;
         rc = SV_ERR_NOMEM;
@@ -1892,8 +1655,6 @@ int spec_verify_init(spec_verify_ctx** out, int device, int max_batch, int max_k
         o += result_bytes;
         c->req_count = reinterpret_cast<unsigned*>(w + o);
         o += req_bytes;
-        c->tasks = reinterpret_cast<int*>(w + o);
-        o += task_bytes;
         c->status = reinterpret_cast<unsigned*>(w + o);
         if (hipMemset(c->ws, 0, total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
             rc = SV_ERR_HIP;
