@@ -1298,50 +1298,34 @@ void draw_kernel(Params P) {
     double* blk = reinterpret_cast<double*>(dyn_smem);   // [C * kBlocks] residual block masses
     constexpr int W = Elem<E>::W;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int b = blockIdx.x;
+    // Requests in reverse order: the streaming pass read the last requests'
+    // rows last, so they are the likeliest to still be cached.
+    const int b = P.B - 1 - (int)blockIdx.x;
     const int K = P.K, C = P.C;
     const unsigned ep = P.epoch;
-    TeamPoll pl;                                   // wave 0: team j's records
-    TeamStats ts;
+    TeamPoll pl;                                   // wave 0: team j's records (prologue)
     if (wave == 0) {
-        int k = P.budgets[b];
+        // One round of loads: lane t < K the decision of position t, lane 63
+        // the budget.
+        unsigned long long d = 0ull;
+        int kb = 0;
+        if (lane < K) d = ld64(dec_word(P, b * (K + 1) + lane));
+        if (lane == 63) kb = P.budgets[b];
+        int k = __shfl(kb, 63, 64);
         k = k < 0 ? 0 : (k > K ? K : k);
-        // Lane t: the decision of position t < k.
-        const unsigned long long d = lane < k ? ld64(dec_word(P, b * (K + 1) + lane)) : 0ull;
         const bool known = lane >= k || (unsigned)(d >> 32) == ep;
         if (__ballot(!known) != 0 && lane == 0) atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);
         const unsigned long long rej = __ballot(lane < k && (!known || (d & 1ull) == 0));
         const int j = rej ? __ffsll((long long)rej) - 1 : k;
         poll_issue<false>(P, b * (K + 1) + j, pl);
-        if (!poll_complete<false>(P, pl) && lane == 0) atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);
-        ts = team_stats(P, pl);
-        const uint4 rw = philox4x32_10((uint32_t)(P.bbase + b), (uint32_t)j, 0u, 0u, P.key0, P.key1);
-        const double u = word_to_uniform(rw.y);
-        int chunk = -1;
-        double thr = 0.0;
-        if (j == k) p_chunk(P, pl, ts, u, chunk, thr);
         if (lane == 0) {
             sh.dr_j = j;
             sh.dr_k = k;
             sh.dr_mode = j < k ? 1 : 0;
-            sh.dr_chunk = chunk;
-            sh.dr_u = u;
-            sh.dr_thr = thr;
-            sh.dr_mt = ts.mt;
-            sh.dr_md = ts.md;
-            sh.dr_ist = (float)(1.0 / ts.st);
-            sh.dr_isd = (float)(1.0 / ts.sd);
         }
     }
     __syncthreads();
     const int j = sh.dr_j, k = sh.dr_k;
-    const float mt = sh.dr_mt, md = sh.dr_md, ist = sh.dr_ist, isd = sh.dr_isd;
-    const float c = P.c32;
-    auto rmass = [&](const uint4& t, const uint4& q, int kk) -> float {
-        const float pv = fast_exp2((Elem<E>::at(t, kk) - mt) * c) * ist;
-        const float qv = fast_exp2((Elem<E>::at(q, kk) - md) * c) * isd;
-        return fmaxf(0.0f, pv - qv);
-    };
     auto chunk_unit = [&](int cc) -> Unit {
         Unit d;
         d.u = 0;
@@ -1355,13 +1339,46 @@ void draw_kernel(Params P) {
         d.has_d = true;
         return d;
     };
+    // Residual: the data waves start streaming the row pair (two chunks in
+    // flight) while wave 0 merges the team's records.
+    uint4 ta[kG], qa[kG], tb[kG], qb[kG];
+    const int dt = tid - 64;
+    if (sh.dr_mode == 1 && wave > 0) {
+        issue_loads<E, kVec>(P, chunk_unit(0), dt, ta, qa);
+        if (C > 1) issue_loads<E, kVec>(P, chunk_unit(1), dt, tb, qb);
+    }
+    if (wave == 0) {
+        if (!poll_complete<false>(P, pl) && lane == 0) atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);
+        const TeamStats ts = team_stats(P, pl);
+        const uint4 rw = philox4x32_10((uint32_t)(P.bbase + b), (uint32_t)j, 0u, 0u, P.key0, P.key1);
+        const double u = word_to_uniform(rw.y);
+        int chunk = -1;
+        double thr = 0.0;
+        if (j == k) p_chunk(P, pl, ts, u, chunk, thr);
+        if (lane == 0) {
+            sh.dr_chunk = chunk;
+            sh.dr_u = u;
+            sh.dr_thr = thr;
+            sh.dr_mt = ts.mt;
+            sh.dr_md = ts.md;
+            sh.dr_ist = (float)(1.0 / ts.st);
+            sh.dr_isd = (float)(1.0 / ts.sd);
+        }
+    }
+    __syncthreads();
+    const float mt = sh.dr_mt, md = sh.dr_md, ist = sh.dr_ist, isd = sh.dr_isd;
+    const float c = P.c32;
+    auto rmass = [&](const uint4& t, const uint4& q, int kk) -> float {
+        const float pv = fast_exp2((Elem<E>::at(t, kk) - mt) * c) * ist;
+        const float qv = fast_exp2((Elem<E>::at(q, kk) - md) * c) * isd;
+        return fmaxf(0.0f, pv - qv);
+    };
     int y = 0;
     int mode = sh.dr_mode;
     if (mode == 1) {
         // Residual: stream both rows once (the next chunk's loads in flight
         // while a chunk is reduced); block masses to LDS.
         if (wave > 0) {
-            const int dt = tid - 64;
             auto reduce = [&](int cc, const uint4 (&t)[kG], const uint4 (&q)[kG]) {
                 #pragma unroll
                 for (int g = 0; g < kG; ++g) {
@@ -1372,14 +1389,14 @@ void draw_kernel(Params P) {
                     if (lane == 0) blk[cc * kBlocks + g * kDataWaves + wave - 1] = ws;
                 }
             };
-            uint4 ta[kG], qa[kG], tb[kG], qb[kG];
-            issue_loads<E, kVec>(P, chunk_unit(0), dt, ta, qa);
+            // Chunks 0 and 1 are in flight; each reduce frees its buffer
+            // for the chunk after the other buffer's.
             for (int cc = 0; cc < C; cc += 2) {
-                if (cc + 1 < C) issue_loads<E, kVec>(P, chunk_unit(cc + 1), dt, tb, qb);
                 reduce(cc, ta, qa);
+                if (cc + 2 < C) issue_loads<E, kVec>(P, chunk_unit(cc + 2), dt, ta, qa);
                 if (cc + 1 < C) {
-                    if (cc + 2 < C) issue_loads<E, kVec>(P, chunk_unit(cc + 2), dt, ta, qa);
                     reduce(cc + 1, tb, qb);
+                    if (cc + 3 < C) issue_loads<E, kVec>(P, chunk_unit(cc + 3), dt, tb, qb);
                 }
             }
         }
@@ -1395,7 +1412,14 @@ void draw_kernel(Params P) {
             if (total > 0.0) chunk_crossing(nb, t, [&](int x) -> double { return blk[x]; }, star, base);
             int chunk = -1;
             double thr = t - base;
-            if (star < 0) p_chunk(P, pl, ts, sh.dr_u, chunk, thr);   // no residual mass
+            if (star < 0) {
+                // No residual mass (rounding only): from p_j, whose records
+                // are read again.
+                TeamPoll pr;
+                poll_issue<false>(P, b * (K + 1) + j, pr);
+                const TeamStats tr = team_stats(P, pr);
+                p_chunk(P, pr, tr, sh.dr_u, chunk, thr);
+            }
             if (lane == 0) {
                 sh.dr_mode = star >= 0 ? 1 : 0;
                 sh.sub_star = star;
