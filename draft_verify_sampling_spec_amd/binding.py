@@ -44,6 +44,8 @@ EXPORTED = (
     "spec_verify_check_args",
     "spec_verify_status",
     "spec_verify_philox_words",
+    "spec_verify_timing",
+    "spec_verify_timing_read",
     "spec_verify_free",
     "spec_verify_strerror",
     "spec_verify_chunks",
@@ -74,6 +76,10 @@ def _declare(lib):
     lib.spec_verify_strerror.restype = ctypes.c_char_p
     lib.spec_verify_chunks.argtypes = [_i, _i]
     lib.spec_verify_chunks.restype = _i
+    lib.spec_verify_timing.argtypes = [_vp, _i]
+    lib.spec_verify_timing.restype = _i
+    lib.spec_verify_timing_read.argtypes = [_vp, ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_double)]
+    lib.spec_verify_timing_read.restype = _i
 
 
 def load(path: str | None = None):
@@ -134,6 +140,18 @@ def spec_verify_status(ctx):
 
 def spec_verify_philox_words(seed: int, B: int, P: int, out_words, stream) -> int:
     return load().spec_verify_philox_words(ctypes.c_uint64(seed), B, P, out_words, stream)
+
+
+def spec_verify_timing(ctx, enable: bool) -> int:
+    return load().spec_verify_timing(ctx, 1 if enable else 0)
+
+
+def spec_verify_timing_read(ctx):
+    """Returns (status, [launches of pass 0, pass 1], [total ms of pass 0, pass 1])."""
+    counts = (_i * 2)()
+    total = (ctypes.c_double * 2)()
+    rc = load().spec_verify_timing_read(ctx, counts, total)
+    return rc, [counts[0], counts[1]], [total[0], total[1]]
 
 
 def spec_verify_free(ctx) -> None:
@@ -242,6 +260,17 @@ class SpecVerify:
         rc, flags = spec_verify_status(self._ctx)
         _check(rc, "spec_verify_status")
         return flags
+
+    def timing(self, enable: bool) -> None:
+        """Start (True) or stop and discard (False) per-pass event timing."""
+        _check(spec_verify_timing(self._ctx, enable), "spec_verify_timing")
+
+    def pass_times(self):
+        """Launch counts and summed milliseconds of the streaming pass and the
+        draw pass recorded since the last read (waits for them)."""
+        rc, counts, total = spec_verify_timing_read(self._ctx)
+        _check(rc, "spec_verify_timing_read")
+        return counts, total
 
 
 def philox_words(seed: int, B: int, P: int, device="cuda") -> torch.Tensor:

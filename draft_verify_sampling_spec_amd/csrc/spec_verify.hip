@@ -63,6 +63,7 @@
 #include <cstdint>
 #include <cstring>
 #include <type_traits>
+#include <vector>
 
 #include "spec_verify.h"
 
@@ -1530,7 +1531,16 @@ struct spec_verify_ctx {
     unsigned* result;
     unsigned* req_count;
     unsigned* status;
-    unsigned calls;                // calls made so far (phase-word epochs)
+    unsigned calls;
+    // Per-pass timing (off unless enabled): recorded event pairs of later
+    // runs, and a pool of events to reuse.
+    bool timing;
+    struct Timed {
+        int pass;                  // 0 streaming pass, 1 draw pass
+        hipEvent_t start, end;
+    };
+    std::vector<Timed> timed;
+    std::vector<hipEvent_t> event_pool;                // calls made so far (phase-word epochs)
     // occupancy cache: dynamic LDS bytes -> resident workgroups per CU, per kernel
     size_t occ_smem[8];
     int occ_val[8];
@@ -1552,6 +1562,39 @@ int occupancy_of(spec_verify_ctx* ctx, int slot, size_t smem) {
     return n;
 }
 
+constexpr size_t kMaxTimed = 1 << 16;   // recorded passes kept before recording stops
+
+hipEvent_t pooled_event(spec_verify_ctx* ctx) {
+    if (!ctx->event_pool.empty()) {
+        hipEvent_t e = ctx->event_pool.back();
+        ctx->event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    return hipEventCreate(&e) == hipSuccess ? e : nullptr;
+}
+
+// Start of a pass: when timing, an event pair is taken and its start
+// recorded; returns the record's index, or -1.
+int timed_begin(spec_verify_ctx* ctx, int pass, hipStream_t stream) {
+    if (!ctx->timing || ctx->timed.size() >= kMaxTimed) return -1;
+    spec_verify_ctx::Timed t;
+    t.pass = pass;
+    t.start = pooled_event(ctx);
+    t.end = pooled_event(ctx);
+    if (!t.start || !t.end || hipEventRecord(t.start, stream) != hipSuccess) {
+        if (t.start) ctx->event_pool.push_back(t.start);
+        if (t.end) ctx->event_pool.push_back(t.end);
+        return -1;
+    }
+    ctx->timed.push_back(t);
+    return (int)ctx->timed.size() - 1;
+}
+
+void timed_end(spec_verify_ctx* ctx, int idx, hipStream_t stream) {
+    if (idx >= 0) (void)hipEventRecord(ctx->timed[(size_t)idx].end, stream);
+}
+
 // Launch shape of the streaming pass: every workgroup resident (grid = CUs x
 // occupancy); the schedule needs at least as many workgroups as a team has
 // members. Sampled mode then runs the draw pass, one workgroup per request.
@@ -1562,13 +1605,17 @@ int launch(spec_verify_ctx* ctx, Params& p, hipStream_t stream) {
     const int occ = occupancy_of<E, G, Vv>(ctx, slot, smem);
     const long long grid = (long long)ctx->cus * occ;
     if (grid < (long long)p.C) return SV_ERR_ARG;   // a team would not fit
+    int t = timed_begin(ctx, 0, stream);
     hipLaunchKernelGGL((verify_kernel<E, G, Vv>), dim3((unsigned)grid), dim3(kThreads), smem, stream,
                        p);
     if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+    timed_end(ctx, t, stream);
     if (!G) {
+        t = timed_begin(ctx, 1, stream);
         hipLaunchKernelGGL((draw_kernel<E, Vv>), dim3((unsigned)p.B), dim3(kThreads),
                            draw_smem_bytes(p.C), stream, p);
         if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+        timed_end(ctx, t, stream);
     }
     return SV_OK;
 }
@@ -1814,12 +1861,62 @@ int spec_verify_philox_words(uint64_t seed, int B, int P, uint32_t* out_words, v
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+int spec_verify_timing(spec_verify_ctx* ctx, int enable) {
+    if (!ctx || ctx->magic != kMagic) return SV_ERR_STATE;
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) return SV_ERR_HIP;
+    if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return SV_ERR_HIP;
+    int rc = SV_OK;
+    if (!enable && !ctx->timed.empty()) {
+        for (const auto& t : ctx->timed) {
+            if (hipEventSynchronize(t.end) != hipSuccess) rc = SV_ERR_HIP;
+            ctx->event_pool.push_back(t.start);
+            ctx->event_pool.push_back(t.end);
+        }
+        ctx->timed.clear();
+    }
+    ctx->timing = enable != 0;
+    if (prev != ctx->device) (void)hipSetDevice(prev);
+    return rc;
+}
+
+int spec_verify_timing_read(spec_verify_ctx* ctx, int* counts, double* total_ms) {
+    if (!ctx || ctx->magic != kMagic) return SV_ERR_STATE;
+    if (!counts || !total_ms) return SV_ERR_NULL;
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) return SV_ERR_HIP;
+    if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return SV_ERR_HIP;
+    int rc = SV_OK;
+    counts[0] = counts[1] = 0;
+    total_ms[0] = total_ms[1] = 0.0;
+    for (const auto& t : ctx->timed) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(t.end) != hipSuccess ||
+            hipEventElapsedTime(&ms, t.start, t.end) != hipSuccess) {
+            rc = SV_ERR_HIP;
+        } else {
+            counts[t.pass] += 1;
+            total_ms[t.pass] += (double)ms;
+        }
+        ctx->event_pool.push_back(t.start);
+        ctx->event_pool.push_back(t.end);
+    }
+    ctx->timed.clear();
+    if (prev != ctx->device) (void)hipSetDevice(prev);
+    return rc;
+}
+
 void spec_verify_free(spec_verify_ctx* ctx) {
     if (!ctx || ctx->magic != kMagic) return;
     int prev = -1;
     (void)hipGetDevice(&prev);
     if (prev != ctx->device) (void)hipSetDevice(ctx->device);
     (void)hipDeviceSynchronize();
+    for (hipEvent_t e : ctx->event_pool) (void)hipEventDestroy(e);
+    for (const auto& t : ctx->timed) {
+        (void)hipEventDestroy(t.start);
+        (void)hipEventDestroy(t.end);
+    }
     if (ctx->ws) (void)hipFree(ctx->ws);
     if (prev != ctx->device && prev >= 0) (void)hipSetDevice(prev);
     ctx->magic = 0;

@@ -100,7 +100,8 @@ enum sv_status {
  *   vocab      V, the vocabulary size of every run, 1..SV_MAX_VOCAB.
  *   dtype      sv_dtype of the logits of every run.
  * Allocates and zeroes the device workspace (per-chunk partial statistics,
- * per-row team records, per-request counters, status word). Synchronous.
+ * per-row decision words, per-request counters of greedy mode, status
+ * word). Synchronous.
  * Errors: SV_ERR_NULL, SV_ERR_ARG, SV_ERR_DTYPE, SV_ERR_HIP, SV_ERR_NOMEM.
  */
 int spec_verify_init(spec_verify_ctx** out, int device, int max_batch, int max_k,
@@ -166,6 +167,28 @@ int spec_verify_status(spec_verify_ctx* ctx, uint32_t* flags);
  */
 int spec_verify_philox_words(uint64_t seed, int B, int P, uint32_t* out_words,
                              void* stream);
+
+/*
+ * spec_verify_timing -- per-pass device timing of later runs (off by
+ * default). enable != 0: every later spec_verify_run on this context records
+ * a HIP event pair on its stream around each pass it launches -- pass 0 the
+ * streaming pass (row statistics and decisions), pass 1 the draw pass of
+ * sampled mode (first rejection, residual or bonus draw, outputs) -- up to
+ * 65536 passes, then recording stops. enable == 0 waits for and discards
+ * what is recorded. The events are the context's; recording adds event
+ * markers between the launches and nothing else.
+ * Errors: SV_ERR_STATE, SV_ERR_HIP.
+ */
+int spec_verify_timing(spec_verify_ctx* ctx, int enable);
+
+/*
+ * spec_verify_timing_read -- wait for the recorded passes, write per pass p
+ * (0 streaming, 1 draw) the number of launches counts[p] and the sum of their
+ * durations total_ms[p] in milliseconds (host arrays of 2), and clear the
+ * record (timing stays as set).
+ * Errors: SV_ERR_STATE, SV_ERR_NULL, SV_ERR_HIP.
+ */
+int spec_verify_timing_read(spec_verify_ctx* ctx, int* counts, double* total_ms);
 
 /* spec_verify_free -- release the context (NULL-safe, idempotent on NULL).
  * Waits for the device before freeing the workspace. */

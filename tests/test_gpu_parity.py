@@ -348,3 +348,30 @@ def test_runs_on_a_non_default_stream():
     excused, unexcused = compare_sampled(toks.cpu().numpy(), nacc.cpu().numpy(), ref, 4)
     assert not unexcused
     sv.close()
+
+
+def test_pass_timing_counts_each_pass():
+    """Per-pass event timing: sampled runs launch the streaming and the draw
+    pass, greedy runs only the streaming pass; batches above the per-launch
+    limit of 8192 requests run as several launches of each."""
+    inp = make_inputs("tiny", B=8200, variant="sampled")
+    t, d, x, k = (inp[n].to(DEV) for n in ("target", "draft", "tokens", "budgets"))
+    sv = SpecVerify(DEV, max_batch=8200, max_k=4, vocab=32, dtype=torch.float32)
+    sv.run(t, d, x, k, 1.0, 5)                 # not recorded
+    sv.timing(True)
+    for s in range(3):
+        sv.run(t[:100].contiguous(), d[:100].contiguous(), x[:100].contiguous(),
+               k[:100].contiguous(), 1.0, s)
+    counts, total = sv.pass_times()
+    assert counts == [3, 3] and total[0] > 0.0 and total[1] > 0.0
+    sv.run(t, None, x, k, 0.0, 0)              # greedy, two launches
+    counts, total = sv.pass_times()
+    assert counts == [2, 0] and total[0] > 0.0 and total[1] == 0.0
+    sv.run(t, d, x, k, 1.0, 9)
+    sv.timing(False)                           # discards the record
+    sv.timing(True)
+    counts, _ = sv.pass_times()
+    assert counts == [0, 0]
+    sv.timing(False)
+    assert sv.status() == 0
+    sv.close()
