@@ -10,7 +10,8 @@ the step time), the roofline of the verify kernel (algorithmic HBM bytes per
 launch over its measured duration, against the 8 TB/s HBM peak), and the
 fp64 CPU oracle's rate on a bounded sample of the same workload.
 
-  python bench.py [--steps K] [--warmup W] [--workload heavy] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--warmup-settle S] [--workload heavy]
+                  [--no-cpu-baseline]
   python bench.py --copy-probe GIB   # plain copies of a known size (counter scale)
 """
 from __future__ import annotations
@@ -26,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E peak, GB/s
+WARMUP_SETTLE_S = 0.2           # minimum busy time before the timed steps
 KERNEL_SRC = os.path.join(ROOT, "draft_verify_sampling_spec_amd", "csrc", "spec_verify.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_kernel_heavy_traffic.json")
 WORKLOAD_INDEX = {"tiny": 1, "qwen3": 2, "ragged": 3, "gemma": 4, "heavy": 5}
@@ -116,6 +118,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-settle", type=float, default=WARMUP_SETTLE_S,
+                    help="minimum seconds of warmup (0: exactly --warmup steps)")
     ap.add_argument("--workload", default="heavy", choices=sorted(WORKLOAD_INDEX))
     ap.add_argument("--temperature", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -156,9 +160,17 @@ def main():
     alg_bytes, rows = algorithmic_bytes(budgets, K, V, elem, greedy)
     verified_per_step = int(sum(budgets))
 
-    log(f"[bench] warmup {args.warmup} steps")
-    for s in range(args.warmup):
-        sv.run(t, d, x, k, T, philox_seed(widx, s), out_t, out_n, want_probs=False)
+    # Warmup: W steps, continued (untimed) until the GPU has been busy for
+    # WARMUP_SETTLE_S -- its clocks ramp over the first tens of milliseconds
+    # of sustained load, and a short warmup would time the ramp.
+    log(f"[bench] warmup {args.warmup} steps (at least {args.warmup_settle} s)")
+    warm_steps = 0
+    w0 = time.perf_counter()
+    while warm_steps < args.warmup or time.perf_counter() - w0 < args.warmup_settle:
+        sv.run(t, d, x, k, T, philox_seed(widx, warm_steps), out_t, out_n, want_probs=False)
+        warm_steps += 1
+        if warm_steps % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -209,6 +221,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_steps,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",

@@ -1003,6 +1003,12 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
         if (kGreedy) {
             float bv = -INFINITY;
             int bi = INT_MAX;
+            // Group by group; a consumed group's registers take the next
+            // unit's group at once.
+            read_plan(r + 1, nxt, nkind);
+            const bool more = nkind != PL_END;
+            UnitRows<E> nw;
+            if (more) nw = unit_rows<E>(P, nxt);
             #pragma unroll
             for (int j = 0; j < kG; ++j) {
                 #pragma unroll
@@ -1013,9 +1019,8 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
                         bi = cur.e0 + (dt + j * kDataThreads) * W + kk;
                     }
                 }
+                if (more) load_pair<E, kVec>(nw, dt, j, gt[j], gd[j]);
             }
-            read_plan(r + 1, nxt, nkind);
-            if (nkind != PL_END) issue_loads<E, kVec>(P, nxt, dt, gt, gd);
             #pragma unroll
             for (int o = 32; o > 0; o >>= 1) {
                 const float ov = __shfl_xor(bv, o, 64);
