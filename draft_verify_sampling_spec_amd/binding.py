@@ -46,6 +46,7 @@ EXPORTED = (
     "spec_verify_philox_words",
     "spec_verify_timing",
     "spec_verify_timing_read",
+    "spec_budget_schedule",
     "spec_verify_free",
     "spec_verify_strerror",
     "spec_verify_chunks",
@@ -76,6 +77,8 @@ def _declare(lib):
     lib.spec_verify_strerror.restype = ctypes.c_char_p
     lib.spec_verify_chunks.argtypes = [_i, _i]
     lib.spec_verify_chunks.restype = _i
+    lib.spec_budget_schedule.argtypes = [_vp, _i, _i, _i, ctypes.c_float, _vp, _vp]
+    lib.spec_budget_schedule.restype = _i
     lib.spec_verify_timing.argtypes = [_vp, _i]
     lib.spec_verify_timing.restype = _i
     lib.spec_verify_timing_read.argtypes = [_vp, ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_double)]
@@ -140,6 +143,12 @@ def spec_verify_status(ctx):
 
 def spec_verify_philox_words(seed: int, B: int, P: int, out_words, stream) -> int:
     return load().spec_verify_philox_words(ctypes.c_uint64(seed), B, P, out_words, stream)
+
+
+def spec_budget_schedule(confidences, B: int, K: int, n_total: int, tau: float, out_budgets,
+                         stream) -> int:
+    return load().spec_budget_schedule(confidences, B, K, n_total, ctypes.c_float(tau),
+                                       out_budgets, stream)
 
 
 def spec_verify_timing(ctx, enable: bool) -> int:
@@ -280,3 +289,25 @@ def philox_words(seed: int, B: int, P: int, device="cuda") -> torch.Tensor:
                                   _stream_handle(out.device))
     _check(rc, "spec_verify_philox_words")
     return out.view(B, P, 4).to(torch.int64) & 0xFFFFFFFF
+
+
+def schedule_budgets(confidences: torch.Tensor, n_total: int, tau: float = 0.0,
+                     out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Per-request verify budgets (int32 [B]) from per-position confidences
+    (float32 [B, K], contiguous, on the GPU): the N largest gains above tau.
+    Enqueued on ``stream`` (default: the current torch stream)."""
+    if confidences.dim() != 2 or confidences.dtype != torch.float32:
+        raise ValueError("confidences must be a float32 [B, K] tensor")
+    if not confidences.is_cuda or not confidences.is_contiguous():
+        raise ValueError("confidences must be a contiguous GPU tensor")
+    B, K = confidences.shape
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=confidences.device)
+    elif out.dtype != torch.int32 or out.shape != (B,) or not out.is_contiguous() \
+            or out.device != confidences.device:
+        raise ValueError("out must be a contiguous int32 [B] tensor on the same device")
+    s = stream.cuda_stream if stream is not None else _stream_handle(confidences.device)
+    rc = spec_budget_schedule(confidences.data_ptr(), B, K, int(n_total), float(tau),
+                              out.data_ptr(), s)
+    _check(rc, "spec_budget_schedule")
+    return out

@@ -1,7 +1,8 @@
 """Build the HIP library in-tree with hipcc for gfx950.
 
 ``python -m draft_verify_sampling_spec_amd.build`` (or ``build_library()``)
-compiles ``csrc/spec_verify.hip`` into ``libspec_verify.so`` next to this file.
+compiles ``csrc/spec_verify.hip`` (verification) and ``csrc/budget_schedule.hip``
+(the verify-budget scheduler) into ``libspec_verify.so`` next to this file.
 """
 from __future__ import annotations
 
@@ -13,6 +14,7 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 SRC = os.path.join(PKG_DIR, "csrc", "spec_verify.hip")
+SOURCES = [SRC, os.path.join(PKG_DIR, "csrc", "budget_schedule.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libspec_verify.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
@@ -41,7 +43,7 @@ def compile_command(out: str = LIB_PATH) -> list:
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall",
         "-I", INCLUDE,
-        SRC,
+        *SOURCES,
         "-o", out,
     ]
 

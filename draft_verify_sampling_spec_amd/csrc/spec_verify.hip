@@ -7,51 +7,42 @@
 // per-request verify budgets of section "What DSpark adds", paragraph 2.
 // The ABI and its conventions are documented in include/spec_verify.h.
 //
-// Design: one persistent kernel per call; every logit byte is read from HBM
-// once, and only the rows of each request's first rejected position are read
-// a second time (interleaved into the same stream).
+// Design: a streaming pass reads every logit row the method needs exactly
+// once and takes every decision; in sampled mode a draw pass follows on the
+// stream and makes each request's one draw.
 //  * Work unit = vocabulary chunk c of position i of request b: the chunk of
 //    target row i and, for a drafted position, the same chunk of drafter row
 //    i. Every chunk has the same size (960 data lanes x 4 sixteen-byte loads
 //    per row). Units are numbered request-major, position-major, chunk-minor,
 //    so the C chunks of one position (a "team") are consecutive.
-//  * The grid is exactly the resident workgroups; workgroup w takes units
-//    w, w + G, w + 2G, ... (G = grid size >= C, so two units of one
-//    workgroup never share a team).
-//  * One workgroup of 16 waves per CU. Waves 1-15 stream data: 16-byte loads of a unit
-//    into registers, reduced per wave to the max and sum of
-//    2^((z - max) log2(e)/T) (sampled) or (max, lowest index) (greedy),
-//    posted to LDS; then the next unit's loads go out. They never wait on
-//    another workgroup. Wave 0 is the control wave: it merges the waves'
+//  * Streaming pass (verify_kernel): the grid is exactly the resident
+//    workgroups; workgroup w takes units w, w + G, w + 2G, ... (G = grid size
+//    >= C, so two units of one workgroup never share a team). One workgroup
+//    of 16 waves per CU. Waves 1-15 stream data: 16-byte loads of a unit into
+//    registers, reduced per wave to the max and sum of 2^((z - max) log2(e)/T)
+//    (sampled) or (max, lowest index) (greedy), posted to LDS; the next
+//    unit's loads go out group by group as the reduction consumes the
+//    registers. They never wait on another workgroup. Wave 0 is the control
+//    wave: it plans the units a few rounds ahead, merges the waves'
 //    statistics and publishes the chunk's record; the two kinds of waves
 //    exchange tagged LDS messages, with no workgroup barrier in the loop.
 //  * Every record word carries the call's epoch, so a record is complete when
 //    all its words carry it. The workgroup holding chunk 0 of a team reads
 //    the team's C records once complete (a poll issued one round later, so
 //    its latency overlaps the next unit) and decides: greedy, the row's
-//    first argmax; sampled, p(x), q(x) and the accept test. It writes the
-//    decision word and completes the team, or queues a draw for after the
-//    loop (a rejection, or the bonus position).
-//  * First rejections: the control wave keeps its drafted units in a ring
-//    until the decisions of their request's positions tell whether the unit
-//    belongs to the request's first rejection. Such a chunk becomes a re-read
-//    job, planned into the data waves' stream like a regular unit: the data
-//    waves re-load it and reduce it to its residual mass max(0, p - q) with
-//    the team's normalisers, which the control wave publishes. The control
-//    wave plans every round a few rounds ahead (regular unit, job, or end).
-//  * After the loop (barriers allowed): chunks of first rejections the loop
-//    did not get to are re-read; then each queued draw is made only for its
-//    request's first rejection (or the bonus position when none): the owner
-//    scans the residual CDF over chunks, and the whole workgroup re-reads the
-//    one chunk that holds the threshold for the element-level scan.
-//  * Per request, the team that completes last writes the outputs.
-//  * Waiting: in the loop only the control wave waits on other workgroups,
-//    and only for an owed decision: the records of a team whose units all
-//    precede the unit it publishes next (G >= C), so by induction on the unit
-//    index every record gets written. Pending first-rejection checks never
-//    wait. After the loop, re-reads wait only on decisions (taken in loops)
-//    and draws only on residual masses (published in loops or re-reads).
-//    Every wait is bounded (status flag on expiry) so the kernel drains.
+//    first argmax (the team completing last for a request writes its
+//    outputs); sampled, p(x), q(x), the accept test and the decision word.
+//  * Draw pass (draw_kernel, sampled): one workgroup per request finds the
+//    first rejection from the decision words, streams that position's
+//    target and drafter rows once for the residual masses of 512-element
+//    blocks, and scans the block holding the threshold; the bonus position
+//    picks its chunk from the records' p masses and scans that chunk. It
+//    writes the request's outputs. Nothing in it waits on another workgroup.
+//  * Waiting (streaming pass): only the control wave waits on other
+//    workgroups, and only for an owed decision: the records of a team whose
+//    units all precede the unit it publishes next (G >= C), so by induction
+//    on the unit index every record gets written. Every wait is bounded
+//    (status flag on expiry) so the kernel drains.
 //  * Synchronisation uses device-scope relaxed atomics (plus s_waitcnt where
 //    a counter orders earlier stores), never release/acquire fences: those
 //    write back and invalidate the whole L2.

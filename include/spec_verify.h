@@ -190,6 +190,37 @@ int spec_verify_timing(spec_verify_ctx* ctx, int enable);
  */
 int spec_verify_timing_read(spec_verify_ctx* ctx, int* counts, double* total_ms);
 
+/*
+ * spec_budget_schedule -- per-request verify budgets from per-position
+ * confidences ("Speculative decoding becomes standard: DSpark and
+ * multi-token drafters", section "What DSpark adds", paragraph 2: a
+ * confidence head gives each drafted position's chance of surviving
+ * verification given that the earlier ones did, and a scheduler chooses each
+ * request's verify length across all requests, shorter under heavy load; the
+ * Analytics Vidhya DSpark page, section "Gotchas and Issues": the cutoff is
+ * recomputed every batch and only what has positive expected value is
+ * verified). Stream-ordered, no host sync, no context and no workspace.
+ *   confidences  float [B, K] row-major (device): c[b, i] for drafted
+ *                position i of request b. NaN and negatives read as 0,
+ *                values above 1 as 1.
+ *   B, K         requests (0..SV_MAX_BATCH; 0 is a no-op) and drafted
+ *                positions per request (0..SV_MAX_K).
+ *   n_total      the batch's verify budget N >= 0: drafted positions to
+ *                verify over all requests (the load sets it).
+ *   tau          >= 0, finite: a position is verified only if its gain
+ *                exceeds tau.
+ *   out_budgets  int32 [B] (device): k_b, ready for spec_verify_run.
+ * The gain of position k of request b is g = c[b,0] * c[b,1] * ... * c[b,k]
+ * (the expected accepted tokens it adds), multiplied left to right in fp32.
+ * The N largest gains above tau are verified, equal gains by position, then
+ * request; k_b counts those of request b, always a prefix of its block.
+ * sum_b k_b = min(N, number of gains above tau).
+ * Errors (nothing enqueued): SV_ERR_ARG, SV_ERR_NULL, SV_ERR_ALIGN (pointers
+ * not 4-byte aligned); SV_ERR_HIP if the launch fails.
+ */
+int spec_budget_schedule(const float* confidences, int B, int K, int n_total, float tau,
+                         int32_t* out_budgets, void* stream);
+
 /* spec_verify_free -- release the context (NULL-safe, idempotent on NULL).
  * Waits for the device before freeing the workspace. */
 void spec_verify_free(spec_verify_ctx* ctx);

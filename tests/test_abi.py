@@ -18,7 +18,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(spec_verify_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(spec_(?:verify|budget)_[a-z_]+)\s*\(", text)))
 
 
 def _declared_constants():
@@ -141,3 +141,28 @@ def test_init_without_a_device_fails_cleanly():
         pytest.skip("a GPU is present")
     rc, ctx = sb.spec_verify_init(0, 8, 4, 1000, sb.SV_DTYPE_BF16)
     assert rc == sb.SV_ERR_HIP and ctx is None
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), sb.SV_ERR_ARG),
+    (dict(B=sb.SV_MAX_BATCH + 1), sb.SV_ERR_ARG),
+    (dict(K=-1), sb.SV_ERR_ARG),
+    (dict(K=sb.SV_MAX_K + 1), sb.SV_ERR_ARG),
+    (dict(n_total=-1), sb.SV_ERR_ARG),
+    (dict(tau=-0.5), sb.SV_ERR_ARG),
+    (dict(tau=math.nan), sb.SV_ERR_ARG),
+    (dict(tau=math.inf), sb.SV_ERR_ARG),
+    (dict(out=None), sb.SV_ERR_NULL),
+    (dict(conf=None), sb.SV_ERR_NULL),
+    (dict(out=0x1002), sb.SV_ERR_ALIGN),
+    (dict(conf=0x2001), sb.SV_ERR_ALIGN),
+    (dict(B=0, out=None, conf=None), sb.SV_OK),
+])
+def test_budget_schedule_argument_checks(kw, code):
+    """Host-side checks of spec_budget_schedule: they return before any
+    launch, so fake (never dereferenced) pointers are fine."""
+    args = dict(conf=0x1000, B=8, K=4, n_total=16, tau=0.0, out=0x2000)
+    args.update(kw)
+    rc = sb.spec_budget_schedule(args["conf"], args["B"], args["K"], args["n_total"],
+                                 args["tau"], args["out"], None)
+    assert rc == code
