@@ -100,6 +100,53 @@ def cpu_baseline(inp, seeds, n_requests, min_seconds=10.0, max_seconds=30.0):
     return verified / dt, dt, passes
 
 
+def bench_scheduler(B, K, steps, seed=5):
+    """The verify-budget scheduler on the workload's batch shape: per-position
+    confidences for B requests and K drafted positions, a batch verify budget
+    of 4 positions per request (the heavy batch's mean), tau = 0. Per-call
+    durations from HIP events around each launch; the oracle timed beside it
+    on the same confidences."""
+    import torch
+    from draft_verify_sampling_spec_amd import schedule_budgets
+    from workloads import make_confidences
+    conf_cpu = make_confidences(B, K, seed)
+    conf = conf_cpu.to("cuda")
+    out = torch.empty(B, dtype=torch.int32, device="cuda")
+    n_total = 4 * B
+    for _ in range(20):
+        schedule_budgets(conf, n_total, 0.0, out=out)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        schedule_budgets(conf, n_total, 0.0, out=out)
+        b.record()
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    from oracle import schedule as osch
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        want = osch.schedule(conf_cpu.numpy(), n_total, 0.0)
+        reps += 1
+        if time.perf_counter() - t0 > 1.0:
+            break
+    cpu_us = (time.perf_counter() - t0) / reps * 1e6
+    same = out.cpu().numpy().tolist() == want.tolist()
+    return {
+        "config": f"B={B} K={K} N={n_total} tau=0, synthetic sigmoid confidences (chat and math/code halves)",
+        "us_per_call": {"mean": sum(us) / len(us), "median": us[len(us) // 2],
+                        "p5": us[int(0.05 * (len(us) - 1))], "p95": us[int(0.95 * (len(us) - 1))]},
+        "calls": steps,
+        "bound": "latency",
+        "bytes_per_call": 4 * B * K + 4 * B,
+        "budgets_match_oracle": same,
+        "cpu_oracle_us_per_call": cpu_us,
+        "cpu_oracle_cores": 1,
+    }
+
+
 def copy_probe(gib):
     import torch
     n = int(gib * (1 << 30))
@@ -254,6 +301,9 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not greedy:
+        log("[bench] budget scheduler")
+        result["scheduler"] = bench_scheduler(B, K, args.steps)
     if not args.no_cpu_baseline and not greedy and args.workload == "heavy":
         n_req = min(args.cpu_requests, B)
         log(f"[bench] cpu baseline: oracle on {n_req} requests")

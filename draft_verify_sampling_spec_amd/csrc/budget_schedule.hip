@@ -14,13 +14,14 @@
 // prefix, since gains never increase along a block).
 //
 // Design: one workgroup of 1024 threads; thread t owns a contiguous range of
-// at most 16 requests and recomputes their gains from the confidences on
-// every pass (left-to-right fp32 products: the same bits each time, and the
-// same as any other implementation that multiplies in that order). The N-th
-// largest gain is found by a 4-pass, 8-bit radix select over the gains' bit
-// patterns (monotone for non-negative floats) with an LDS histogram; equal
-// gains at the cut are resolved with per-position counts and one block scan
-// over requests. No workspace and no global atomics.
+// at most 16 requests. Their gains (left-to-right fp32 products: the same
+// bits as any other implementation that multiplies in that order) are kept
+// in LDS when the batch's B*K gains fit, else recomputed from the
+// confidences on every pass. The N-th largest gain is found by a 4-pass,
+// 8-bit radix select over the gains' bit patterns (monotone for non-negative
+// floats) with an LDS histogram; equal gains at the cut are resolved with
+// per-position counts and one block scan over requests. No workspace and no
+// global atomics.
 
 #include <hip/hip_runtime.h>
 
@@ -33,6 +34,7 @@ namespace {
 
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedWaves = kSchedThreads / 64;
+constexpr int kLdsGains = 12288;        // B*K up to this: gains kept in LDS (48 KB)
 
 // Confidence as the scheduler reads it: NaN and negatives are 0, values
 // above 1 are 1, and -0 becomes +0 (so every gain is a non-negative float
@@ -42,30 +44,13 @@ __device__ __forceinline__ float clamp_conf(float c) {
 }
 
 struct SchedShared {
-    unsigned hist[256];
+    unsigned hist[2][256];          // radix histograms, alternating by pass
     unsigned level[SV_MAX_K + 1];
     unsigned wsum[kSchedWaves];
     unsigned total;
     unsigned digit, above;          // radix step: chosen digit, keys in higher bins
     int cut_level, cut_rank;        // ties: the partial level and how many it takes
 };
-
-__device__ unsigned block_sum(SchedShared& sh, unsigned v) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    if (lane == 0) sh.wsum[wave] = v;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned t = 0;
-        for (int w = 0; w < kSchedWaves; ++w) t += sh.wsum[w];
-        sh.total = t;
-    }
-    __syncthreads();
-    const unsigned t = sh.total;
-    __syncthreads();
-    return t;
-}
 
 // Exclusive prefix over threads in thread order (each thread one count).
 __device__ unsigned block_exclusive(SchedShared& sh, unsigned v) {
@@ -84,85 +69,122 @@ __device__ unsigned block_exclusive(SchedShared& sh, unsigned v) {
     return base + incl - v;
 }
 
+template <bool kLds>
 __global__ __launch_bounds__(kSchedThreads) void budget_schedule_kernel(
     const float* __restrict__ conf, int B, int K, int n_total, float tau,
     int32_t* __restrict__ out) {
     __shared__ SchedShared sh;
+    extern __shared__ float gl[];          // kLds: gains [B * K]
     const int tid = threadIdx.x;
     const int per = (B + kSchedThreads - 1) / kSchedThreads;
     const int b0 = min(tid * per, B), b1 = min(b0 + per, B);
 
-    // Calls f(b, k, gain) for every position of this thread's requests, in
-    // request then position order.
-    auto each_gain = [&](auto&& f) {
+    if (kLds) {
         for (int b = b0; b < b1; ++b) {
             const float* row = conf + (size_t)b * K;
             float run = 1.0f;
             for (int k = 0; k < K; ++k) {
                 run = run * clamp_conf(row[k]);
-                f(b, k, run);
+                gl[b * K + k] = run;
+            }
+        }
+        // Each thread reads only its own requests' gains: no barrier needed.
+    }
+
+    // Calls f(k, gain) for every position of request b, in position order.
+    auto row_gains = [&](int b, auto&& f) {
+        if (kLds) {
+            for (int k = 0; k < K; ++k) f(k, gl[b * K + k]);
+        } else {
+            const float* row = conf + (size_t)b * K;
+            float run = 1.0f;
+            for (int k = 0; k < K; ++k) {
+                run = run * clamp_conf(row[k]);
+                f(k, run);
             }
         }
     };
+    // The same over all of this thread's requests, in request order.
+    auto each_gain = [&](auto&& f) {
+        for (int b = b0; b < b1; ++b) row_gains(b, [&](int k, float g) { f(b, k, g); });
+    };
 
-    // Gains above tau (the only candidates).
-    unsigned mine = 0;
-    each_gain([&](int, int, float g) { mine += g > tau ? 1u : 0u; });
-    const unsigned cand = block_sum(sh, mine);
-
-    // The cut: positions whose gain key is above `cut` are taken; `need` of
-    // the positions whose key equals it are taken too, in (k, b) order.
-    // With no more candidates than N every candidate is taken.
-    bool all = (unsigned)n_total >= cand;
+    // Radix select of the N-th largest candidate key (candidates: gains
+    // above tau; key: the gain's bit pattern), 8 bits per pass from the top.
+    // A request's gains never increase along its block, so the keys that
+    // match the current prefix are one run of positions whose digits never
+    // increase: each thread adds run lengths, a few atomics per request. The
+    // first pass's histogram also counts the candidates; with no more of
+    // them than N (or N == 0) no cut is needed.
+    if (tid < 512) (&sh.hist[0][0])[tid] = 0;
+    if (tid <= SV_MAX_K) sh.level[tid] = 0;
+    __syncthreads();
+    bool all = true;
     unsigned cut = 0, need = 0;
-    if (!all && n_total > 0) {
-        unsigned prefix = 0, mask = 0, remaining = (unsigned)n_total;
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            if (tid < 256) sh.hist[tid] = 0;
-            __syncthreads();
-            each_gain([&](int, int, float g) {
-                if (!(g > tau)) return;
+    unsigned prefix = 0, mask = 0, remaining = (unsigned)n_total;
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        unsigned* h = sh.hist[pass & 1];
+        for (int b = b0; b < b1; ++b) {
+            int run_bin = -1;
+            unsigned run_len = 0;
+            row_gains(b, [&](int, float g) {
                 const unsigned key = __float_as_uint(g);
-                if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+                const int bin = (g > tau && (key & mask) == prefix) ? (int)((key >> shift) & 255u) : -1;
+                if (bin != run_bin) {
+                    if (run_bin >= 0) atomicAdd(&h[run_bin], run_len);
+                    run_bin = bin;
+                    run_len = 0;
+                }
+                if (bin >= 0) ++run_len;
             });
-            __syncthreads();
-            if (tid < 64) {
-                // Lane l holds bins 4l .. 4l+3; suffix sums from the top bin.
-                unsigned c[4], s = 0;
-                #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    c[q] = sh.hist[4 * tid + q];
-                    s += c[q];
-                }
-                unsigned suf = s;              // bins 4l .. 255
-                #pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const unsigned u = __shfl_down(suf, o, 64);
-                    if (tid + o < 64) suf += u;
-                }
-                const unsigned higher = suf - s;   // bins above this lane's four
-                // The lane whose bins hold the remaining-th largest key.
-                const bool hit = higher < remaining && suf >= remaining;
-                if (hit) {
-                    unsigned acc = higher;
-                    int d = 4 * tid + 3;
-                    for (int q = 3; q >= 0; --q) {
-                        if (acc + c[q] >= remaining) {
-                            d = 4 * tid + q;
-                            break;
-                        }
-                        acc += c[q];
-                    }
-                    sh.digit = (unsigned)d;
-                    sh.above = acc;
-                }
-            }
-            __syncthreads();
-            remaining -= sh.above;
-            prefix |= sh.digit << shift;
-            mask |= 255u << shift;
-            __syncthreads();
+            if (run_bin >= 0) atomicAdd(&h[run_bin], run_len);
         }
+        // The other histogram was last read before the previous pass's
+        // second barrier: clear it for the next pass.
+        if (tid < 256) sh.hist[(pass + 1) & 1][tid] = 0;
+        __syncthreads();
+        if (tid < 64) {
+            // Lane l holds bins 4l .. 4l+3; suffix sums from the top bin.
+            unsigned c[4], sl = 0;
+            #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                c[q] = h[4 * tid + q];
+                sl += c[q];
+            }
+            unsigned suf = sl;                 // bins 4l .. 255
+            #pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const unsigned u = __shfl_down(suf, o, 64);
+                if (tid + o < 64) suf += u;
+            }
+            if (tid == 0) sh.total = suf;      // keys counted in this pass
+            const unsigned higher = suf - sl;  // bins above this lane's four
+            // The lane whose bins hold the remaining-th largest key.
+            if (higher < remaining && suf >= remaining) {
+                unsigned acc = higher;
+                int d = 4 * tid + 3;
+                for (int q = 3; q >= 0; --q) {
+                    if (acc + c[q] >= remaining) {
+                        d = 4 * tid + q;
+                        break;
+                    }
+                    acc += c[q];
+                }
+                sh.digit = (unsigned)d;
+                sh.above = acc;
+            }
+        }
+        __syncthreads();
+        if (pass == 0) {
+            all = n_total == 0 || (unsigned)n_total >= sh.total;
+            if (all) break;
+        }
+        remaining -= sh.above;
+        prefix |= sh.digit << shift;
+        mask |= 255u << shift;
+    }
+    if (!all) {
         cut = prefix;
         need = remaining;
     }
@@ -171,13 +193,11 @@ __global__ __launch_bounds__(kSchedThreads) void budget_schedule_kernel(
     // it (gains never increase along a block, so both are prefixes and the
     // positions equal to the cut are [s_b, e_b)).
     auto above_cut = [&](float g) -> bool {
-        return all ? g > tau : (n_total > 0 && g > tau && __float_as_uint(g) > cut);
+        return all ? (n_total > 0 && g > tau) : (g > tau && __float_as_uint(g) > cut);
     };
     auto at_cut = [&](float g) -> bool {
-        return !all && n_total > 0 && g > tau && __float_as_uint(g) == cut;
+        return !all && g > tau && __float_as_uint(g) == cut;
     };
-    if (tid <= SV_MAX_K) sh.level[tid] = 0;
-    __syncthreads();
     if (need > 0) {
         each_gain([&](int, int k, float g) {
             if (at_cut(g)) atomicAdd(&sh.level[k], 1u);
@@ -212,16 +232,14 @@ __global__ __launch_bounds__(kSchedThreads) void budget_schedule_kernel(
     }
     unsigned rank = block_exclusive(sh, on_level);
     for (int b = b0; b < b1; ++b) {
-        const float* row = conf + (size_t)b * K;
-        float run = 1.0f;
         int s = 0, e = 0;
         bool lv_here = false;
-        for (int k = 0; k < K; ++k) {
-            run = run * clamp_conf(row[k]);
-            if (above_cut(run)) ++s;
-            if (above_cut(run) || at_cut(run)) ++e;
-            if (k == lv && at_cut(run)) lv_here = true;
-        }
+        auto visit = [&](int k, float g) {
+            if (above_cut(g)) ++s;
+            if (above_cut(g) || at_cut(g)) ++e;
+            if (k == lv && at_cut(g)) lv_here = true;
+        };
+        row_gains(b, visit);
         int kb = s + max(0, min(e, lv) - s);
         if (lv_here) {
             if (rank < rank_need) ++kb;
@@ -244,8 +262,14 @@ extern "C" int spec_budget_schedule(const float* confidences, int B, int K, int 
     if (B == 0) return SV_OK;
     if (!out_budgets || (K > 0 && !confidences)) return SV_ERR_NULL;
     if (!aligned4(out_budgets) || (K > 0 && !aligned4(confidences))) return SV_ERR_ALIGN;
-    hipLaunchKernelGGL(budget_schedule_kernel, dim3(1), dim3(kSchedThreads), 0,
-                       static_cast<hipStream_t>(stream), confidences, B, K, n_total, tau,
-                       out_budgets);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((long long)B * K <= kLdsGains) {
+        hipLaunchKernelGGL(budget_schedule_kernel<true>, dim3(1), dim3(kSchedThreads),
+                           (size_t)B * K * sizeof(float), s, confidences, B, K, n_total, tau,
+                           out_budgets);
+    } else {
+        hipLaunchKernelGGL(budget_schedule_kernel<false>, dim3(1), dim3(kSchedThreads), 0, s,
+                           confidences, B, K, n_total, tau, out_budgets);
+    }
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
