@@ -47,6 +47,8 @@ EXPORTED = (
     "spec_verify_timing",
     "spec_verify_timing_read",
     "spec_budget_schedule",
+    "spec_head_stats",
+    "spec_head_workspace_bytes",
     "spec_verify_free",
     "spec_verify_strerror",
     "spec_verify_chunks",
@@ -77,6 +79,11 @@ def _declare(lib):
     lib.spec_verify_strerror.restype = ctypes.c_char_p
     lib.spec_verify_chunks.argtypes = [_i, _i]
     lib.spec_verify_chunks.restype = _i
+    lib.spec_head_stats.argtypes = [_vp, _vp, _i, _i, _i, _vp, ctypes.c_float, _vp, _vp, _vp,
+                                    _vp, _vp, ctypes.c_size_t, _vp]
+    lib.spec_head_stats.restype = _i
+    lib.spec_head_workspace_bytes.argtypes = [_i, _i]
+    lib.spec_head_workspace_bytes.restype = ctypes.c_size_t
     lib.spec_budget_schedule.argtypes = [_vp, _i, _i, _i, ctypes.c_float, _vp, _vp]
     lib.spec_budget_schedule.restype = _i
     lib.spec_verify_timing.argtypes = [_vp, _i]
@@ -311,3 +318,47 @@ def schedule_budgets(confidences: torch.Tensor, n_total: int, tau: float = 0.0,
                               out.data_ptr(), s)
     _check(rc, "spec_budget_schedule")
     return out
+
+
+def spec_head_workspace_bytes(R: int, V: int) -> int:
+    return int(load().spec_head_workspace_bytes(int(R), int(V)))
+
+
+def spec_head_stats(hidden, weight, R, H, V, tokens, temperature, out_max, out_sumexp, out_ztok,
+                    out_argmax, workspace, workspace_bytes, stream) -> int:
+    return load().spec_head_stats(hidden, weight, R, H, V, tokens, ctypes.c_float(temperature),
+                                  out_max, out_sumexp, out_ztok, out_argmax, workspace,
+                                  ctypes.c_size_t(workspace_bytes), stream)
+
+
+def head_stats(hidden: torch.Tensor, weight: torch.Tensor, tokens: torch.Tensor | None,
+               temperature: float, stream=None):
+    """Row statistics of hidden @ weight^T (bf16 [R, H] and [V, H], contiguous,
+    on the GPU): (max, exp-sum, token logit, first argmax) as tensors [R].
+    Allocates its outputs and scratch with torch; enqueued on ``stream``."""
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise ValueError("hidden and weight must be bfloat16")
+    if hidden.dim() != 2 or weight.dim() != 2 or hidden.shape[1] != weight.shape[1]:
+        raise ValueError("hidden [R, H] and weight [V, H] must share H")
+    if not (hidden.is_cuda and weight.is_cuda and hidden.is_contiguous() and weight.is_contiguous()):
+        raise ValueError("hidden and weight must be contiguous GPU tensors")
+    R, H = hidden.shape
+    V = weight.shape[0]
+    dev = hidden.device
+    out_m = torch.empty(R, dtype=torch.float32, device=dev)
+    out_s = torch.empty(R, dtype=torch.float32, device=dev)
+    out_z = torch.empty(R, dtype=torch.float32, device=dev)
+    out_a = torch.empty(R, dtype=torch.int32, device=dev)
+    nbytes = spec_head_workspace_bytes(max(R, 1), V)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    tp = 0
+    if tokens is not None:
+        if tokens.dtype != torch.int32 or tokens.shape != (R,) or not tokens.is_contiguous():
+            raise ValueError("tokens must be a contiguous int32 [R] tensor")
+        tp = tokens.data_ptr()
+    s = stream.cuda_stream if stream is not None else _stream_handle(dev)
+    rc = spec_head_stats(hidden.data_ptr(), weight.data_ptr(), R, H, V, tp or None,
+                         float(temperature), out_m.data_ptr(), out_s.data_ptr(), out_z.data_ptr(),
+                         out_a.data_ptr(), ws.data_ptr(), ws.numel(), s)
+    _check(rc, "spec_head_stats")
+    return out_m, out_s, out_z, out_a

@@ -1,8 +1,9 @@
 """Build the HIP library in-tree with hipcc for gfx950.
 
 ``python -m draft_verify_sampling_spec_amd.build`` (or ``build_library()``)
-compiles ``csrc/spec_verify.hip`` (verification) and ``csrc/budget_schedule.hip``
-(the verify-budget scheduler) into ``libspec_verify.so`` next to this file.
+compiles ``csrc/spec_verify.hip`` (verification), ``csrc/budget_schedule.hip``
+(the verify-budget scheduler) and ``csrc/head_stats.hip`` (output-head row
+statistics) into ``libspec_verify.so`` next to this file.
 """
 from __future__ import annotations
 
@@ -14,7 +15,8 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 SRC = os.path.join(PKG_DIR, "csrc", "spec_verify.hip")
-SOURCES = [SRC, os.path.join(PKG_DIR, "csrc", "budget_schedule.hip")]
+SOURCES = [SRC, os.path.join(PKG_DIR, "csrc", "budget_schedule.hip"),
+           os.path.join(PKG_DIR, "csrc", "head_stats.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libspec_verify.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)

@@ -1,0 +1,354 @@
+// head_stats.hip -- the shared output head with a softmax-statistics
+// epilogue, for MI355X (gfx950, MFMA).
+//
+// What is computed: "Speculative decoding becomes standard: DSpark and
+// multi-token drafters", section "What DSpark adds", paragraph 1 (the drafter
+// shares the frozen output head with the target, so both models' logits for
+// a position are that head applied to a hidden state), and section "Why
+// draft-and-verify does not change the output", paragraphs 1 and 2 (what a
+// verify step needs from each scored row: the target's most likely token, or
+// p(x) and q(x) of the drafted token). For hidden states h [R, H] and the head
+// W [V, H] (bf16), per row r of z = h W^T: the maximum m, the sum
+// S = sum_v 2^((z_v - m) c) with c = log2(e) / T, z at a given token, and the
+// first argmax -- without writing z anywhere.
+//
+// Design: a bf16 matrix product on the matrix cores
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation). A workgroup of 4 waves owns
+// a 128-row tile of h and a contiguous range of 128-column tiles of the
+// vocabulary (one "split"); per k-step of 32 it stages both operand tiles in
+// LDS (double-buffered: the next step's global loads are in flight during
+// the current step's products), and each wave multiplies a 64 x 64 quarter
+// as 2 x 2 blocks of 32 x 32. After each vocabulary tile every lane folds its
+// accumulators into running per-row statistics of the 32 rows it holds
+// (lane l holds column l % 32 of rows 8(i/4) + 4(l/32) + i%4 of a block), so
+// no cross-lane work happens per tile; lanes and waves merge once at the end
+// and write one partial per (row, split). A second small kernel merges the
+// splits.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "spec_verify.h"
+
+namespace {
+
+constexpr int kHThreads = 256;             // 4 waves
+constexpr int kTM = 128;                   // rows of h per tile
+constexpr int kTN = 128;                   // vocabulary columns per tile
+constexpr int kTK = 32;                    // k per staged step
+constexpr int kPad = 8;                    // LDS row padding (bf16 elements)
+constexpr int kLdsRow = kTK + kPad;        // 40 bf16 = 80 bytes per staged row
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct HeadPart {                          // one row's statistics over one split
+    float m, s, zx;
+    int arg;                               // first argmax, INT_MAX if none
+};
+
+__device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Merge (m2, s2) into (m1, s1): both sums are relative to their own maximum.
+__device__ __forceinline__ void merge_ms(float& m1, float& s1, float m2, float s2, float c,
+                                         bool sampled) {
+    const float m = fmaxf(m1, m2);
+    if (sampled && m != -INFINITY) {
+        const float a = m1 == -INFINITY ? 0.0f : s1 * __builtin_amdgcn_exp2f((m1 - m) * c);
+        const float b = m2 == -INFINITY ? 0.0f : s2 * __builtin_amdgcn_exp2f((m2 - m) * c);
+        s1 = a + b;
+    }
+    m1 = m;
+}
+
+__device__ __forceinline__ void merge_arg(float& v1, int& i1, float v2, int i2) {
+    if (v2 > v1 || (v2 == v1 && i2 < i1)) {
+        v1 = v2;
+        i1 = i2;
+    }
+}
+
+// kSampled: running (max, exp-sum) per row; else (max, first argmax).
+template <bool kSampled>
+__global__ __launch_bounds__(kHThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void head_stats_kernel(const uint16_t* __restrict__ hid, const uint16_t* __restrict__ w, int R,
+                       int H, int V, const int32_t* __restrict__ tok, float c,
+                       int tiles_per_split, HeadPart* __restrict__ part) {
+    constexpr bool sampled = kSampled;
+    __shared__ __align__(16) uint16_t As[2][kTM][kLdsRow];
+    __shared__ __align__(16) uint16_t Bs[2][kTN][kLdsRow];
+    __shared__ int tok_s[kTM];
+    __shared__ float zx_s[kTM];            // the token's logit (one lane of the split finds it)
+    __shared__ HeadPart xw[kTM];           // wave-pair merge
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r0 = blockIdx.x * kTM;
+    const int split = blockIdx.y;
+    const int ntiles = (V + kTN - 1) / kTN;
+    const int t0 = split * tiles_per_split, t1 = min(ntiles, t0 + tiles_per_split);
+    const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;   // this wave's quarter
+    const int nk = (H + kTK - 1) / kTK;
+
+    if (tid < kTM) {
+        tok_s[tid] = (r0 + tid < R && tok) ? tok[r0 + tid] : -1;
+        zx_s[tid] = NAN;
+    }
+
+    // Running statistics of this lane's 32 rows (slot = 16 * br + i): the
+    // maximum, and the exp-sum under it (sampled) or the first argmax.
+    float rm[32];
+    float rx[32];                          // sampled: exp-sum; greedy: argmax bits
+    #pragma unroll
+    for (int q = 0; q < 32; ++q) {
+        rm[q] = -INFINITY;
+        rx[q] = sampled ? 0.0f : __int_as_float(INT_MAX);
+    }
+
+    // Staging: thread t moves 16 bf16 of row t / 2, k half (t % 2) * 16, of
+    // each operand tile per step.
+    const int srow = tid >> 1, skh = (tid & 1) * 16;
+    auto load_tile = [&](const uint16_t* base, int nrows, int row, int k0, uint4& x0, uint4& x1) {
+        x0 = make_uint4(0u, 0u, 0u, 0u);
+        x1 = x0;
+        const int k = k0 + skh;
+        if (row < nrows) {
+            const uint16_t* p = base + (size_t)row * H + k;
+            if (k + 16 <= H) {
+                x0 = *reinterpret_cast<const uint4*>(p);
+                x1 = *reinterpret_cast<const uint4*>(p + 8);
+            } else {
+                // The row's last step: elements at or beyond H read as 0.
+                uint32_t wd[8];
+                #pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t lo = k + 2 * j < H ? p[2 * j] : 0u;
+                    const uint32_t hi = k + 2 * j + 1 < H ? p[2 * j + 1] : 0u;
+                    wd[j] = lo | (hi << 16);
+                }
+                x0 = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                x1 = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+            }
+        }
+    };
+
+    for (int t = t0; t < t1; ++t) {
+        const int v0 = t * kTN;
+        f32x16 acc[2][2];
+        #pragma unroll
+        for (int a = 0; a < 2; ++a)
+            #pragma unroll
+            for (int b = 0; b < 2; ++b)
+                #pragma unroll
+                for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+
+        uint4 ha0, ha1, wb0, wb1;
+        load_tile(hid, R, r0 + srow, 0, ha0, ha1);
+        load_tile(w, V, v0 + srow, 0, wb0, wb1);
+        __syncthreads();                   // previous tile's readers are done
+        *reinterpret_cast<uint4*>(&As[0][srow][skh]) = ha0;
+        *reinterpret_cast<uint4*>(&As[0][srow][skh + 8]) = ha1;
+        *reinterpret_cast<uint4*>(&Bs[0][srow][skh]) = wb0;
+        *reinterpret_cast<uint4*>(&Bs[0][srow][skh + 8]) = wb1;
+        __syncthreads();
+        for (int ks = 0; ks < nk; ++ks) {
+            const int cur = ks & 1;
+            const bool more = ks + 1 < nk;
+            if (more) {
+                load_tile(hid, R, r0 + srow, (ks + 1) * kTK, ha0, ha1);
+                load_tile(w, V, v0 + srow, (ks + 1) * kTK, wb0, wb1);
+            }
+            #pragma unroll
+            for (int kk = 0; kk < kTK; kk += 16) {
+                bf16x8 af[2], bfr[2];
+                #pragma unroll
+                for (int a = 0; a < 2; ++a) {
+                    af[a] = *reinterpret_cast<const bf16x8*>(
+                        &As[cur][wr + 32 * a + (lane & 31)][kk + (lane >> 5) * 8]);
+                    bfr[a] = *reinterpret_cast<const bf16x8*>(
+                        &Bs[cur][wc + 32 * a + (lane & 31)][kk + (lane >> 5) * 8]);
+                }
+                #pragma unroll
+                for (int a = 0; a < 2; ++a)
+                    #pragma unroll
+                    for (int b = 0; b < 2; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+            }
+            if (more) {
+                const int nxt = cur ^ 1;
+                *reinterpret_cast<uint4*>(&As[nxt][srow][skh]) = ha0;
+                *reinterpret_cast<uint4*>(&As[nxt][srow][skh + 8]) = ha1;
+                *reinterpret_cast<uint4*>(&Bs[nxt][srow][skh]) = wb0;
+                *reinterpret_cast<uint4*>(&Bs[nxt][srow][skh + 8]) = wb1;
+            }
+            __syncthreads();
+        }
+
+        // Fold the tile into the lane's running row statistics.
+        #pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            #pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int q = 16 * a + i;
+                const int rl = wr + 32 * a + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                const int x = tok_s[rl];
+                #pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const int col = v0 + wc + 32 * b + (lane & 31);
+                    if (col < V) {
+                        const float z = acc[a][b][i];
+                        if (col == x) zx_s[rl] = z;
+                        if (sampled) {
+                            if (z > rm[q]) {
+                                rx[q] = rx[q] * __builtin_amdgcn_exp2f((rm[q] - z) * c) + 1.0f;
+                                rm[q] = z;
+                            } else {
+                                rx[q] += __builtin_amdgcn_exp2f((z - rm[q]) * c);
+                            }
+                        } else {
+                            // A lane's columns go up, so the first maximum wins.
+                            const bool better = z > rm[q];
+                            rm[q] = better ? z : rm[q];
+                            rx[q] = better ? __int_as_float(col) : rx[q];
+                        }
+                    }
+                }
+            }
+        }
+    }
+
+    // Lanes holding the same rows (same l / 32 half): merge across columns.
+    #pragma unroll
+    for (int q = 0; q < 32; ++q) {
+        float m = rm[q], x = rx[q];
+        #pragma unroll
+        for (int o = 1; o < 32; o <<= 1) {
+            const float m2 = __shfl_xor(m, o, 64), x2 = __shfl_xor(x, o, 64);
+            if (sampled) {
+                merge_ms(m, x, m2, x2, c, true);
+            } else {
+                int ai = __float_as_int(x);
+                merge_arg(m, ai, m2, __float_as_int(x2));
+                x = __int_as_float(ai);
+            }
+        }
+        rm[q] = m;
+        rx[q] = x;
+    }
+    // Waves with the same rows (wave and wave ^ 1) merge through LDS.
+    __syncthreads();
+    if ((wave & 1) == 1 && (lane & 31) == 0) {
+        #pragma unroll
+        for (int q = 0; q < 32; ++q) {
+            const int a = q >> 4, i = q & 15;
+            const int rl = wr + 32 * a + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            xw[rl] = HeadPart{rm[q], sampled ? rx[q] : 0.0f, 0.0f,
+                              sampled ? INT_MAX : __float_as_int(rx[q])};
+        }
+    }
+    __syncthreads();
+    if ((wave & 1) == 0 && (lane & 31) == 0) {
+        #pragma unroll
+        for (int q = 0; q < 32; ++q) {
+            const int a = q >> 4, i = q & 15;
+            const int rl = wr + 32 * a + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            const HeadPart o = xw[rl];
+            HeadPart out;
+            out.m = rm[q];
+            out.zx = zx_s[rl];
+            if (sampled) {
+                out.s = rx[q];
+                merge_ms(out.m, out.s, o.m, o.s, c, true);
+                out.arg = INT_MAX;
+            } else {
+                out.s = 0.0f;
+                out.arg = __float_as_int(rx[q]);
+                merge_arg(out.m, out.arg, o.m, o.arg);
+            }
+            if (r0 + rl < R) part[(size_t)split * R + r0 + rl] = out;
+        }
+    }
+}
+
+// Per row: merge the splits' partials (in split order) into the outputs.
+// Greedy partials carry the first argmax; sampled ones do not (INT_MAX), and
+// the sampled call reports none.
+__global__ void head_merge_kernel(const HeadPart* __restrict__ part, int R, int splits, float c,
+                                  int sampled, float* out_max, float* out_sum, float* out_z,
+                                  int32_t* out_arg) {
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= R) return;
+    float m = -INFINITY, s = 0.0f, z = NAN, bv = -INFINITY;
+    int ai = INT_MAX;
+    for (int sp = 0; sp < splits; ++sp) {
+        const HeadPart o = part[(size_t)sp * R + r];
+        if (sampled) merge_ms(m, s, o.m, o.s, c, true);
+        else merge_arg(bv, ai, o.m, o.arg);
+        if (z != z) z = o.zx;
+    }
+    out_max[r] = sampled ? m : bv;
+    if (out_sum) out_sum[r] = sampled ? s : NAN;
+    if (out_z) out_z[r] = z;
+    if (out_arg) out_arg[r] = sampled ? -1 : (ai == INT_MAX ? 0 : ai);
+}
+
+bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int splits_for(int R, int V) {
+    // About two workgroups per CU over the row tiles, each split at least
+    // eight vocabulary tiles long.
+    const int rt = (R + kTM - 1) / kTM, nt = (V + kTN - 1) / kTN;
+    int s = (512 + rt - 1) / rt;
+    s = s < 1 ? 1 : s;
+    const int cap = (nt + 7) / 8;
+    return s > cap ? cap : s;
+}
+
+}  // namespace
+
+extern "C" size_t spec_head_workspace_bytes(int R, int V) {
+    if (R < 1 || V < 1) return 0;
+    return (size_t)splits_for(R, V) * (size_t)R * sizeof(HeadPart);
+}
+
+extern "C" int spec_head_stats(const void* hidden, const void* weight, int R, int H, int V,
+                               const int32_t* tokens, float temperature, float* out_max,
+                               float* out_sumexp, float* out_ztok, int32_t* out_argmax,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    if (R < 0 || H < 1 || V < 1 || V > SV_MAX_VOCAB || (H % 8) != 0 ||
+        !std::isfinite(temperature) || temperature < 0.0f) {
+        return SV_ERR_ARG;
+    }
+    if (R == 0) return SV_OK;
+    if (!hidden || !weight || !out_max || !workspace) return SV_ERR_NULL;
+    if (!aligned_to(hidden, 16) || !aligned_to(weight, 16) || !aligned_to(out_max, 4) ||
+        (out_sumexp && !aligned_to(out_sumexp, 4)) || (out_ztok && !aligned_to(out_ztok, 4)) ||
+        (out_argmax && !aligned_to(out_argmax, 4)) || (tokens && !aligned_to(tokens, 4)) ||
+        !aligned_to(workspace, 16)) {
+        return SV_ERR_ALIGN;
+    }
+    if (workspace_bytes < spec_head_workspace_bytes(R, V)) return SV_ERR_ARG;
+    const int splits = splits_for(R, V);
+    const int ntiles = (V + kTN - 1) / kTN;
+    const int tps = (ntiles + splits - 1) / splits;
+    const bool sampled = temperature > 0.0f;
+    const float c = sampled ? (float)(1.4426950408889634 / (double)temperature) : 0.0f;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    HeadPart* part = static_cast<HeadPart*>(workspace);
+    const dim3 grid((unsigned)((R + kTM - 1) / kTM), (unsigned)splits);
+    const uint16_t* hp = static_cast<const uint16_t*>(hidden);
+    const uint16_t* wp = static_cast<const uint16_t*>(weight);
+    if (sampled) {
+        hipLaunchKernelGGL(head_stats_kernel<true>, grid, dim3(kHThreads), 0, s, hp, wp, R, H, V,
+                           tokens, c, tps, part);
+    } else {
+        hipLaunchKernelGGL(head_stats_kernel<false>, grid, dim3(kHThreads), 0, s, hp, wp, R, H, V,
+                           tokens, c, tps, part);
+    }
+    if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+    hipLaunchKernelGGL(head_merge_kernel, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s,
+                       part, R, splits, c, sampled ? 1 : 0, out_max, out_sumexp, out_ztok,
+                       out_argmax);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+}

@@ -221,6 +221,43 @@ int spec_verify_timing_read(spec_verify_ctx* ctx, int* counts, double* total_ms)
 int spec_budget_schedule(const float* confidences, int B, int K, int n_total, float tau,
                          int32_t* out_budgets, void* stream);
 
+/*
+ * spec_head_stats -- row statistics of the shared output head, computed on
+ * the matrix cores without writing the logits ("Speculative decoding becomes
+ * standard: DSpark and multi-token drafters", section "What DSpark adds",
+ * paragraph 1: the drafter shares the frozen output head with the target;
+ * section "Why draft-and-verify does not change the output", paragraphs 1
+ * and 2: a verify step needs each scored row's most likely token, or p(x)
+ * and q(x) of the drafted token). Stream-ordered, no host sync.
+ *   hidden      bf16 [R, H] row-major (device, 16-byte aligned): hidden
+ *               states, one row per scored position (target or drafter).
+ *   weight      bf16 [V, H] row-major (device, 16-byte aligned): the head.
+ *   R, H, V     rows (>= 0; 0 is a no-op), hidden size (>= 8, a multiple of
+ *               8) and vocabulary (1..SV_MAX_VOCAB).
+ *   tokens      int32 [R] or NULL: the token whose logit out_ztok reports.
+ *   temperature > 0: sampled statistics; 0: greedy (max and argmax only).
+ *   out_max     float [R]: m = max_v z[r, v], z = hidden weight^T (fp32
+ *               accumulation of exact bf16 products).
+ *   out_sumexp  float [R] or NULL: sum_v 2^((z[r, v] - m) log2(e) / T)
+ *               (sampled; NaN in greedy mode). p(x) = 2^((z_x - m) log2(e)/T)
+ *               / sum.
+ *   out_ztok    float [R] or NULL: z[r, tokens[r]], NaN if out of range.
+ *   out_argmax  int32 [R] or NULL: the first argmax (greedy; -1 when sampled).
+ *   workspace   device scratch of at least spec_head_workspace_bytes(R, V)
+ *               bytes (16-byte aligned), caller-owned; calls that share it
+ *               must not overlap.
+ * Errors (nothing enqueued): SV_ERR_ARG, SV_ERR_NULL, SV_ERR_ALIGN;
+ * SV_ERR_HIP if a launch fails.
+ */
+int spec_head_stats(const void* hidden, const void* weight, int R, int H, int V,
+                    const int32_t* tokens, float temperature, float* out_max,
+                    float* out_sumexp, float* out_ztok, int32_t* out_argmax,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* spec_head_workspace_bytes -- scratch spec_head_stats needs for (R, V):
+ * one partial per row and vocabulary split. 0 on bad arguments. Host only. */
+size_t spec_head_workspace_bytes(int R, int V);
+
 /* spec_verify_free -- release the context (NULL-safe, idempotent on NULL).
  * Waits for the device before freeing the workspace. */
 void spec_verify_free(spec_verify_ctx* ctx);

@@ -18,7 +18,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(spec_(?:verify|budget)_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(spec_(?:verify|budget|head)_[a-z_]+)\s*\(", text)))
 
 
 def _declared_constants():
@@ -166,3 +166,34 @@ def test_budget_schedule_argument_checks(kw, code):
     rc = sb.spec_budget_schedule(args["conf"], args["B"], args["K"], args["n_total"],
                                  args["tau"], args["out"], None)
     assert rc == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(R=-1), sb.SV_ERR_ARG),
+    (dict(H=0), sb.SV_ERR_ARG),
+    (dict(H=12), sb.SV_ERR_ARG),
+    (dict(V=0), sb.SV_ERR_ARG),
+    (dict(V=sb.SV_MAX_VOCAB + 1), sb.SV_ERR_ARG),
+    (dict(T=-1.0), sb.SV_ERR_ARG),
+    (dict(T=math.nan), sb.SV_ERR_ARG),
+    (dict(hid=None), sb.SV_ERR_NULL),
+    (dict(ws=None), sb.SV_ERR_NULL),
+    (dict(hid=0x1008), sb.SV_ERR_ALIGN),
+    (dict(ws_bytes=16), sb.SV_ERR_ARG),
+    (dict(R=0, hid=None, w=None, ws=None), sb.SV_OK),
+])
+def test_head_stats_argument_checks(kw, code):
+    """Host-side checks of spec_head_stats (they return before any launch)."""
+    args = dict(hid=0x1000, w=0x2000, R=300, H=64, V=1000, tok=None, T=1.0, m=0x3000, s=None,
+                z=None, a=None, ws=0x4000, ws_bytes=1 << 30)
+    args.update(kw)
+    rc = sb.spec_head_stats(args["hid"], args["w"], args["R"], args["H"], args["V"], args["tok"],
+                            args["T"], args["m"], args["s"], args["z"], args["a"], args["ws"],
+                            args["ws_bytes"], None)
+    assert rc == code
+
+
+def test_head_workspace_size():
+    assert sb.spec_head_workspace_bytes(0, 10) == 0
+    n = sb.spec_head_workspace_bytes(300, 1000)
+    assert n > 0 and n % (300 * 16) == 0
