@@ -147,6 +147,55 @@ def bench_scheduler(B, K, steps, seed=5):
     }
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+
+
+def bench_head(R, H, V, steps, T=1.0, seed=5):
+    """The shared output head with its statistics epilogue on the verify
+    batch's rows (target and drafter positions), synthetic bf16 hidden states
+    and head. Per-call durations from HIP events; the dense-MFMA roofline in
+    TFLOP/s; the oracle timed beside it on a few rows, scaled to the call."""
+    import numpy as np
+    import torch
+    from draft_verify_sampling_spec_amd import head_stats
+    from workloads import make_head_inputs
+    h, w, tok = make_head_inputs(R, H, V, seed)
+    for _ in range(3):
+        head_stats(h, w, tok, T)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        head_stats(h, w, tok, T)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    mean_ms = sum(ms) / len(ms)
+    flops = 2.0 * R * H * V
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+    from oracle import head as oh
+    rows = 2
+    hb = h[:rows].cpu().view(torch.int16).numpy().view(np.uint16)
+    wb = w.cpu().view(torch.int16).numpy().view(np.uint16)
+    t0 = time.perf_counter()
+    h64 = oh.bf16_bits_to_f64(hb)
+    for v0 in range(0, V, 16384):
+        oh.logits(h64, oh.bf16_bits_to_f64(wb[v0:v0 + 16384]))
+    cpu_s = (time.perf_counter() - t0) / rows * R
+    return {
+        "config": f"R={R} rows (target + drafter positions) H={H} V={V} bf16, T={T}",
+        "ms_per_call": {"mean": mean_ms, "median": ms[len(ms) // 2],
+                        "p5": ms[int(0.05 * (len(ms) - 1))], "p95": ms[int(0.95 * (len(ms) - 1))]},
+        "calls": steps,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "flops_per_call": flops},
+        "cpu_oracle_s_per_call": cpu_s,
+        "cpu_oracle_sample": f"fp64 NumPy logits of {rows} rows, scaled to {R} rows",
+    }
+
+
 def copy_probe(gib):
     import torch
     n = int(gib * (1 << 30))
@@ -304,6 +353,11 @@ def main():
     if not greedy:
         log("[bench] budget scheduler")
         result["scheduler"] = bench_scheduler(B, K, args.steps)
+        if args.workload == "heavy":
+            # One hidden state per scored row (the step's budgeted target and
+            # drafter rows), Qwen3-4B's hidden size.
+            log("[bench] output head")
+            result["head"] = bench_head(rows, 2560, V, min(args.steps, 10))
     if not args.no_cpu_baseline and not greedy and args.workload == "heavy":
         n_req = min(args.cpu_requests, B)
         log(f"[bench] cpu baseline: oracle on {n_req} requests")

@@ -295,11 +295,14 @@ __global__ void head_merge_kernel(const HeadPart* __restrict__ part, int R, int 
 
 bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Vocabulary splits: as many as fit one resident wave of workgroups (two per
+// CU on 256 CUs) over the row tiles -- a second, partial wave would cost a
+// whole workgroup's time -- each split at least eight vocabulary tiles long.
+constexpr int kResidentSlots = 512;
+
 int splits_for(int R, int V) {
-    // About two workgroups per CU over the row tiles, each split at least
-    // eight vocabulary tiles long.
     const int rt = (R + kTM - 1) / kTM, nt = (V + kTN - 1) / kTN;
-    int s = (512 + rt - 1) / rt;
+    int s = kResidentSlots / rt;
     s = s < 1 ? 1 : s;
     const int cap = (nt + 7) / 8;
     return s > cap ? cap : s;
