@@ -15,10 +15,10 @@
 // Design: a bf16 matrix product on the matrix cores
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulation). A workgroup of 4 waves owns
 // a 128-row tile of h and a contiguous range of 128-column tiles of the
-// vocabulary (one "split"); per k-step of 32 it stages both operand tiles in
-// LDS (double-buffered: the next step's global loads are in flight during
-// the current step's products), and each wave multiplies a 64 x 64 quarter
-// as 2 x 2 blocks of 32 x 32. After each vocabulary tile every lane folds its
+// vocabulary (one "split"); per k-step of 64 it stages both operand tiles in
+// LDS (the next step's global loads go to registers before the current
+// step's products and to LDS after them), and each wave multiplies a
+// 64 x 64 quarter as 2 x 2 blocks of 32 x 32. After each vocabulary tile every lane folds its
 // accumulators into running per-row statistics of the 32 rows it holds
 // (lane l holds column l % 32 of rows 8(i/4) + 4(l/32) + i%4 of a block), so
 // no cross-lane work happens per tile; lanes and waves merge once at the end
@@ -37,9 +37,9 @@ namespace {
 constexpr int kHThreads = 256;             // 4 waves
 constexpr int kTM = 128;                   // rows of h per tile
 constexpr int kTN = 128;                   // vocabulary columns per tile
-constexpr int kTK = 32;                    // k per staged step
+constexpr int kTK = 64;                    // k per staged step
 constexpr int kPad = 8;                    // LDS row padding (bf16 elements)
-constexpr int kLdsRow = kTK + kPad;        // 40 bf16 = 80 bytes per staged row
+constexpr int kLdsRow = kTK + kPad;        // 72 bf16 = 144 bytes per staged row
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -77,8 +77,8 @@ void head_stats_kernel(const uint16_t* __restrict__ hid, const uint16_t* __restr
                        int H, int V, const int32_t* __restrict__ tok, float c,
                        int tiles_per_split, HeadPart* __restrict__ part) {
     constexpr bool sampled = kSampled;
-    __shared__ __align__(16) uint16_t As[2][kTM][kLdsRow];
-    __shared__ __align__(16) uint16_t Bs[2][kTN][kLdsRow];
+    __shared__ __align__(16) uint16_t As[kTM][kLdsRow];
+    __shared__ __align__(16) uint16_t Bs[kTN][kLdsRow];
     __shared__ int tok_s[kTM];
     __shared__ float zx_s[kTM];            // the token's logit (one lane of the split finds it)
     __shared__ HeadPart xw[kTM];           // wave-pair merge
@@ -106,13 +106,12 @@ void head_stats_kernel(const uint16_t* __restrict__ hid, const uint16_t* __restr
         rx[q] = sampled ? 0.0f : __int_as_float(INT_MAX);
     }
 
-    // Staging: thread t moves 16 bf16 of row t / 2, k half (t % 2) * 16, of
-    // each operand tile per step.
-    const int srow = tid >> 1, skh = (tid & 1) * 16;
-    auto load_tile = [&](const uint16_t* base, int nrows, int row, int k0, uint4& x0, uint4& x1) {
+    // Staging: thread t moves 32 bf16 of row t / 2, k half (t % 2) * 32, of
+    // each operand tile per step, as two 16-element pieces.
+    const int srow = tid >> 1, skh = (tid & 1) * 32;
+    auto load16 = [&](const uint16_t* base, int nrows, int row, int k, uint4& x0, uint4& x1) {
         x0 = make_uint4(0u, 0u, 0u, 0u);
         x1 = x0;
-        const int k = k0 + skh;
         if (row < nrows) {
             const uint16_t* p = base + (size_t)row * H + k;
             if (k + 16 <= H) {
@@ -132,6 +131,21 @@ void head_stats_kernel(const uint16_t* __restrict__ hid, const uint16_t* __restr
             }
         }
     };
+    struct Piece {
+        uint4 a0, a1, a2, a3, b0, b1, b2, b3;
+    };
+    auto load_step = [&](int v0, int k0, Piece& pc) {
+        load16(hid, R, r0 + srow, k0 + skh, pc.a0, pc.a1);
+        load16(hid, R, r0 + srow, k0 + skh + 16, pc.a2, pc.a3);
+        load16(w, V, v0 + srow, k0 + skh, pc.b0, pc.b1);
+        load16(w, V, v0 + srow, k0 + skh + 16, pc.b2, pc.b3);
+    };
+    auto store_step = [&](const Piece& pc) {
+        uint4* ra = reinterpret_cast<uint4*>(&As[srow][skh]);
+        uint4* rb = reinterpret_cast<uint4*>(&Bs[srow][skh]);
+        ra[0] = pc.a0; ra[1] = pc.a1; ra[2] = pc.a2; ra[3] = pc.a3;
+        rb[0] = pc.b0; rb[1] = pc.b1; rb[2] = pc.b2; rb[3] = pc.b3;
+    };
 
     for (int t = t0; t < t1; ++t) {
         const int v0 = t * kTN;
@@ -143,31 +157,23 @@ void head_stats_kernel(const uint16_t* __restrict__ hid, const uint16_t* __restr
                 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-        uint4 ha0, ha1, wb0, wb1;
-        load_tile(hid, R, r0 + srow, 0, ha0, ha1);
-        load_tile(w, V, v0 + srow, 0, wb0, wb1);
+        Piece pc;
+        load_step(v0, 0, pc);
         __syncthreads();                   // previous tile's readers are done
-        *reinterpret_cast<uint4*>(&As[0][srow][skh]) = ha0;
-        *reinterpret_cast<uint4*>(&As[0][srow][skh + 8]) = ha1;
-        *reinterpret_cast<uint4*>(&Bs[0][srow][skh]) = wb0;
-        *reinterpret_cast<uint4*>(&Bs[0][srow][skh + 8]) = wb1;
+        store_step(pc);
         __syncthreads();
         for (int ks = 0; ks < nk; ++ks) {
-            const int cur = ks & 1;
             const bool more = ks + 1 < nk;
-            if (more) {
-                load_tile(hid, R, r0 + srow, (ks + 1) * kTK, ha0, ha1);
-                load_tile(w, V, v0 + srow, (ks + 1) * kTK, wb0, wb1);
-            }
+            if (more) load_step(v0, (ks + 1) * kTK, pc);
             #pragma unroll
             for (int kk = 0; kk < kTK; kk += 16) {
                 bf16x8 af[2], bfr[2];
                 #pragma unroll
                 for (int a = 0; a < 2; ++a) {
                     af[a] = *reinterpret_cast<const bf16x8*>(
-                        &As[cur][wr + 32 * a + (lane & 31)][kk + (lane >> 5) * 8]);
+                        &As[wr + 32 * a + (lane & 31)][kk + (lane >> 5) * 8]);
                     bfr[a] = *reinterpret_cast<const bf16x8*>(
-                        &Bs[cur][wc + 32 * a + (lane & 31)][kk + (lane >> 5) * 8]);
+                        &Bs[wc + 32 * a + (lane & 31)][kk + (lane >> 5) * 8]);
                 }
                 #pragma unroll
                 for (int a = 0; a < 2; ++a)
@@ -175,14 +181,11 @@ void head_stats_kernel(const uint16_t* __restrict__ hid, const uint16_t* __restr
                     for (int b = 0; b < 2; ++b)
                         acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
             }
-            if (more) {
-                const int nxt = cur ^ 1;
-                *reinterpret_cast<uint4*>(&As[nxt][srow][skh]) = ha0;
-                *reinterpret_cast<uint4*>(&As[nxt][srow][skh + 8]) = ha1;
-                *reinterpret_cast<uint4*>(&Bs[nxt][srow][skh]) = wb0;
-                *reinterpret_cast<uint4*>(&Bs[nxt][srow][skh + 8]) = wb1;
-            }
             __syncthreads();
+            if (more) {
+                store_step(pc);
+                __syncthreads();
+            }
         }
 
         // Fold the tile into the lane's running row statistics.
