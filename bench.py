@@ -6,9 +6,12 @@ Default workload: the heavy-load batch -- B=512 requests, K=8, budgets
 back to back with a fresh Philox seed per step, inputs resident in HBM.
 
 Prints one JSON line: verified draft tokens/s (sum of budgets per step over
-the step time), the roofline of the verify kernel (algorithmic HBM bytes per
-launch over its measured duration, against the 8 TB/s HBM peak), and the
-fp64 CPU oracle's rate on a bounded sample of the same workload.
+the step time); the roofline of the dominant kernel, the streaming pass
+(algorithmic HBM bytes per launch over its duration from the library's own
+per-pass HIP events, against the 8 TB/s HBM peak); the fp64 CPU oracle's rate
+on a bounded sample of the same workload; and, on the same batch shape, the
+verify-budget scheduler (per call, beside its oracle) and the fused output
+head (TFLOP/s against the 2.5 PFLOP/s dense bf16 peak, beside its oracle).
 
   python bench.py [--steps K] [--warmup W] [--warmup-settle S] [--workload heavy]
                   [--no-cpu-baseline]

@@ -49,8 +49,6 @@ struct HeadPart {                          // one row's statistics over one spli
     int arg;                               // first argmax, INT_MAX if none
 };
 
-__device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
 // Merge (m2, s2) into (m1, s1): both sums are relative to their own maximum.
 __device__ __forceinline__ void merge_ms(float& m1, float& s1, float m2, float s2, float c,
                                          bool sampled) {

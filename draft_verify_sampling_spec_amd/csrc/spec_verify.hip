@@ -295,10 +295,9 @@ struct Shared {
     int dr_j, dr_k, dr_mode, dr_chunk;           // mode: 0 p (chunk dr_chunk), 1 residual
     double dr_u, dr_thr;
     float dr_mt, dr_md, dr_ist, dr_isd;
-    // Block-wide scratch of the draw pass (under barriers).
+    // Block-wide scratch under barriers: the streaming pass's prologue (per
+    // wave sums) and the draw pass's scans.
     double scan_ws[kBlocks];
-    double red_d[kWaves];
-    float red_f[kWaves];
     int red_i[kWaves];
     int sub_star;
     double sub_base;
@@ -556,13 +555,6 @@ __device__ TeamStats team_stats(const Params& P, const TeamPoll& pl) {
     return t;
 }
 
-// Blocking wait and merge.
-__device__ TeamStats merge_team(const Params& P, Shared& sh, int tr) {
-    TeamPoll pl;
-    poll_wait<false>(P, sh, tr, pl);
-    return team_stats(P, pl);
-}
-
 // Control wave, greedy: complete records of team tr (position i of request
 // b with budget k): the row's first argmax; the decision; complete the team.
 __device__ void decide_greedy(const Params& P, const TeamPoll& pl, int b, int i, int k, int tr) {
@@ -617,30 +609,6 @@ struct Unit {
     int e0, n;     // chunk start and length (elements)
     bool has_d;    // drafted position in sampled mode: the drafter row is read too
 };
-
-__device__ __forceinline__ Unit decode_unit(const Params& P, const int* off, int u, int U,
-                                            bool greedy) {
-    Unit d;
-    d.u = u < U ? u : -1;
-    d.b = d.i = d.k = d.c = d.tr = d.e0 = d.n = 0;
-    d.has_d = false;
-    if (d.u < 0) return d;
-    int lo_b = 0, hi_b = P.B;                      // largest b with off[b] <= u
-    while (hi_b - lo_b > 1) {
-        const int mid = (lo_b + hi_b) >> 1;
-        if (off[mid] <= u) lo_b = mid; else hi_b = mid;
-    }
-    d.b = lo_b;
-    const int local = u - off[d.b];
-    d.k = (off[d.b + 1] - off[d.b]) / P.C - 1;
-    d.i = local / P.C;
-    d.c = local - d.i * P.C;
-    d.tr = d.b * (P.K + 1) + d.i;
-    d.e0 = d.c * P.CE;
-    d.n = min(P.CE, P.V - d.e0);
-    d.has_d = !greedy && d.i < d.k;
-    return d;
-}
 
 // The request of unit u: largest b with off[b] <= u (binary search).
 __device__ __forceinline__ int request_of(const Params& P, const int* off, int u) {
@@ -967,7 +935,6 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
     const int lane = threadIdx.x & 63;
     const int dw = (threadIdx.x >> 6) - 1;         // data wave index
     const int dt = threadIdx.x - 64;               // data thread index
-    const int U = off[P.B];
     const float cs = P.c32;
 
     // The plan of round q (the control wave wrote it long before).
