@@ -49,6 +49,8 @@ EXPORTED = (
     "spec_budget_schedule",
     "spec_head_stats",
     "spec_head_workspace_bytes",
+    "spec_verify_hidden",
+    "spec_verify_hidden_workspace_bytes",
     "spec_verify_free",
     "spec_verify_strerror",
     "spec_verify_chunks",
@@ -84,6 +86,12 @@ def _declare(lib):
     lib.spec_head_stats.restype = _i
     lib.spec_head_workspace_bytes.argtypes = [_i, _i]
     lib.spec_head_workspace_bytes.restype = ctypes.c_size_t
+    lib.spec_verify_hidden.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, ctypes.c_float,
+                                       ctypes.c_uint64, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       ctypes.c_size_t, _vp]
+    lib.spec_verify_hidden.restype = _i
+    lib.spec_verify_hidden_workspace_bytes.argtypes = [_i, _i, _i]
+    lib.spec_verify_hidden_workspace_bytes.restype = ctypes.c_size_t
     lib.spec_budget_schedule.argtypes = [_vp, _i, _i, _i, ctypes.c_float, _vp, _vp]
     lib.spec_budget_schedule.restype = _i
     lib.spec_verify_timing.argtypes = [_vp, _i]
@@ -362,3 +370,71 @@ def head_stats(hidden: torch.Tensor, weight: torch.Tensor, tokens: torch.Tensor 
                          out_a.data_ptr(), ws.data_ptr(), ws.numel(), s)
     _check(rc, "spec_head_stats")
     return out_m, out_s, out_z, out_a
+
+
+def spec_verify_hidden_workspace_bytes(B: int, K: int, V: int) -> int:
+    return int(load().spec_verify_hidden_workspace_bytes(int(B), int(K), int(V)))
+
+
+def spec_verify_hidden(target_hidden, draft_hidden, head, draft_tokens, budgets, B, K, H, V,
+                       temperature, seed, out_tokens, out_num_accepted, out_p, out_q,
+                       out_status, workspace, workspace_bytes, stream) -> int:
+    return load().spec_verify_hidden(target_hidden, draft_hidden, head, draft_tokens, budgets,
+                                     B, K, H, V, ctypes.c_float(temperature),
+                                     ctypes.c_uint64(seed), out_tokens, out_num_accepted, out_p,
+                                     out_q, out_status, workspace,
+                                     ctypes.c_size_t(workspace_bytes), stream)
+
+
+class HiddenVerify:
+    """Verify steps from hidden states through the shared head, for one
+    batch shape (B, K, V) on one device. Holds the library's workspace
+    (torch-allocated) across calls; outputs are fresh tensors per call."""
+
+    def __init__(self, device, B: int, K: int, V: int):
+        self.device = torch.device(device)
+        self.B, self.K, self.V = int(B), int(K), int(V)
+        nbytes = spec_verify_hidden_workspace_bytes(max(self.B, 1), self.K, self.V)
+        if nbytes == 0:
+            raise ValueError(f"bad shape B={B} K={K} V={V}")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+
+    def run(self, target_hidden: torch.Tensor, draft_hidden: torch.Tensor | None,
+            head: torch.Tensor, tokens: torch.Tensor, budgets: torch.Tensor,
+            temperature: float, seed: int, stream=None):
+        """(tokens [B, K+1], n_accepted [B], p_x [B, K], q_x [B, K], status [1])."""
+        B, K, V = self.B, self.K, self.V
+        if target_hidden.dim() != 3 or target_hidden.shape[:2] != (B, K + 1):
+            raise ValueError("target_hidden must be [B, K+1, H]")
+        H = int(target_hidden.shape[2])
+        if head.shape != (V, H):
+            raise ValueError("head must be [V, H]")
+        greedy = float(temperature) == 0.0
+        mats = [target_hidden, head] + ([] if draft_hidden is None else [draft_hidden])
+        for m in mats:
+            if m.dtype != torch.bfloat16 or not m.is_contiguous() or m.device != self.device:
+                raise ValueError("hidden states and head must be contiguous bf16 on the device")
+        if draft_hidden is not None and draft_hidden.shape != (B, K, H):
+            raise ValueError("draft_hidden must be [B, K, H]")
+        if not greedy and K > 0 and draft_hidden is None:
+            raise ValueError("sampled verification needs draft_hidden")
+        for t, shape in ((tokens, (B, K)), (budgets, (B,))):
+            if t.dtype != torch.int32 or t.shape != shape or not t.is_contiguous():
+                raise ValueError(f"expected a contiguous int32 tensor of shape {shape}")
+        dev = self.device
+        out_tok = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        out_n = torch.empty(B, dtype=torch.int32, device=dev)
+        out_p = torch.empty((B, K), dtype=torch.float32, device=dev)
+        out_q = torch.empty((B, K), dtype=torch.float32, device=dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        s = stream.cuda_stream if stream is not None else _stream_handle(dev)
+        rc = spec_verify_hidden(target_hidden.data_ptr(),
+                                None if draft_hidden is None else draft_hidden.data_ptr(),
+                                head.data_ptr(), tokens.data_ptr() if K > 0 else None,
+                                budgets.data_ptr(), B, K, H, V, float(temperature),
+                                int(seed) & 0xFFFFFFFFFFFFFFFF, out_tok.data_ptr(),
+                                out_n.data_ptr(), out_p.data_ptr(), out_q.data_ptr(),
+                                status.data_ptr(), self.workspace.data_ptr(),
+                                self.workspace.numel(), s)
+        _check(rc, "spec_verify_hidden")
+        return out_tok, out_n, out_p, out_q, status

@@ -16,7 +16,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 SRC = os.path.join(PKG_DIR, "csrc", "spec_verify.hip")
 SOURCES = [SRC, os.path.join(PKG_DIR, "csrc", "budget_schedule.hip"),
-           os.path.join(PKG_DIR, "csrc", "head_stats.hip")]
+           os.path.join(PKG_DIR, "csrc", "head_stats.hip"),
+           os.path.join(PKG_DIR, "csrc", "verify_hidden.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libspec_verify.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)

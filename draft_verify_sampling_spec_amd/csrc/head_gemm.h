@@ -1,0 +1,50 @@
+// head_gemm.h -- internal interface of the output-head matrix product
+// (head_stats.hip) for the other translation units of the library. Not part
+// of the C ABI.
+//
+// The product z = h W^T of bf16 hidden states and the shared head runs on the
+// matrix cores with one of three epilogues: per-row statistics for sampled or
+// greedy verification, or the fp32 logits themselves for a few rows. Every
+// epilogue accumulates each logit in the same order, so the logits written
+// for a row equal, bit for bit, the values its statistics were taken over.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace svhead {
+
+// Where the hidden state of packed row r lives. Virtual rows [0, a_rows)
+// are rows of `a`, virtual rows from a_rows on are rows of `b`. `map` turns
+// packed rows into virtual rows (NULL: identity); a negative entry is a row
+// of zeros whose outputs nobody reads.
+struct HeadRows {
+    const uint16_t* a;
+    const uint16_t* b;
+    const int32_t* map;
+    int a_rows;
+};
+
+// Scratch (bytes) for head_stats_launch with at most r_max rows.
+size_t stats_workspace_bytes(int r_max, int V);
+
+// `weight` is the head, bf16 [V, H] row-major. H is a multiple of 8 and
+// every pointer 16-byte aligned (the callers check).
+//
+// Row statistics of packed rows [0, R), R = min(*d_rows, r_max) read on the
+// device when d_rows is non-NULL, else R = r_max. Outputs as spec_head_stats
+// (out_max [R]; out_sum, out_z, out_arg [R] or NULL); temperature == 0 gives
+// the greedy statistics. Returns an sv_status code.
+int head_stats_launch(const HeadRows& rows, const uint16_t* weight, int r_max,
+                      const int* d_rows, int H, int V, const int32_t* tokens,
+                      float temperature, float* out_max, float* out_sum, float* out_z,
+                      int32_t* out_arg, void* workspace, hipStream_t stream);
+
+// fp32 logits of packed rows [0, R) into out [R, V] (rows whose map entry is
+// negative are not written). Returns an sv_status code.
+int head_logits_launch(const HeadRows& rows, const uint16_t* weight, int R, int H, int V,
+                       float* out, hipStream_t stream);
+
+}  // namespace svhead

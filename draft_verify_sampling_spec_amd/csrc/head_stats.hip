@@ -10,7 +10,8 @@
 // p(x) and q(x) of the drafted token). For hidden states h [R, H] and the head
 // W [V, H] (bf16), per row r of z = h W^T: the maximum m, the sum
 // S = sum_v 2^((z_v - m) c) with c = log2(e) / T, z at a given token, and the
-// first argmax -- without writing z anywhere.
+// first argmax -- without writing z anywhere. The same product can instead
+// write the fp32 logits of a few rows (the rows a verify step samples from).
 //
 // Design: a bf16 matrix product on the matrix cores
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulation). A workgroup of 4 waves owns
@@ -23,16 +24,21 @@
 // (lane l holds column l % 32 of rows 8(i/4) + 4(l/32) + i%4 of a block), so
 // no cross-lane work happens per tile; lanes and waves merge once at the end
 // and write one partial per (row, split). A second small kernel merges the
-// splits.
+// splits. The rows may be gathered through a row map from two buffers, and
+// their count may be read on the device (the grid then covers the items of
+// any count up to a bound, and workgroups without an item exit).
 
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
 
+#include "head_gemm.h"
 #include "spec_verify.h"
 
 namespace {
+
+using svhead::HeadRows;
 
 constexpr int kHThreads = 256;             // 4 waves
 constexpr int kTM = 128;                   // rows of h per tile
@@ -40,6 +46,10 @@ constexpr int kTN = 128;                   // vocabulary columns per tile
 constexpr int kTK = 64;                    // k per staged step
 constexpr int kPad = 8;                    // LDS row padding (bf16 elements)
 constexpr int kLdsRow = kTK + kPad;        // 72 bf16 = 144 bytes per staged row
+
+constexpr int kResidentSlots = 512;        // one resident wave of workgroups: 2 per CU
+
+enum Epi { kEpiGreedy = 0, kEpiSampled = 1, kEpiLogits = 2 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -68,29 +78,67 @@ __device__ __forceinline__ void merge_arg(float& v1, int& i1, float v2, int i2) 
     }
 }
 
-// kSampled: running (max, exp-sum) per row; else (max, first argmax).
-template <bool kSampled>
+// Vocabulary splits: as many as fit one resident wave of workgroups (two per
+// CU on 256 CUs) over the row tiles -- a second, partial wave would cost a
+// whole workgroup's time -- each split at least eight vocabulary tiles long.
+__host__ __device__ inline int splits_for(int R, int V) {
+    const int rt = (R + kTM - 1) / kTM, nt = (V + kTN - 1) / kTN;
+    int s = kResidentSlots / (rt < 1 ? 1 : rt);
+    s = s < 1 ? 1 : s;
+    const int cap = (nt + 7) / 8;
+    return s > cap ? cap : s;
+}
+
+__device__ __forceinline__ int rows_now(int r_max, const int* d_rows) {
+    if (!d_rows) return r_max;
+    const int r = *d_rows;
+    return r < 0 ? 0 : (r > r_max ? r_max : r);
+}
+
+// Hidden state of packed row r (NULL: a row of zeros).
+__device__ __forceinline__ const uint16_t* row_ptr(const HeadRows& hr, int r, int H) {
+    const int v = hr.map ? hr.map[r] : r;
+    if (v < 0) return nullptr;
+    return v < hr.a_rows ? hr.a + (size_t)v * H : hr.b + (size_t)(v - hr.a_rows) * H;
+}
+
+// kEpi: running (max, exp-sum) per row (sampled), (max, first argmax)
+// (greedy), or the fp32 logits written to `out` (logits).
+template <int kEpi>
 __global__ __launch_bounds__(kHThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void head_stats_kernel(const uint16_t* __restrict__ hid, const uint16_t* __restrict__ w, int R,
-                       int H, int V, const int32_t* __restrict__ tok, float c,
-                       int tiles_per_split, HeadPart* __restrict__ part) {
-    constexpr bool sampled = kSampled;
+void head_stats_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
+                       const int* __restrict__ d_rows, int H, int V,
+                       const int32_t* __restrict__ tok, float c, HeadPart* __restrict__ part,
+                       float* __restrict__ out) {
+    constexpr bool sampled = kEpi == kEpiSampled;
+    constexpr bool logits = kEpi == kEpiLogits;
     __shared__ __align__(16) uint16_t As[kTM][kLdsRow];
     __shared__ __align__(16) uint16_t Bs[kTN][kLdsRow];
-    __shared__ int tok_s[kTM];
+    __shared__ int tok_s[kTM];             // statistics: the token; logits: row present
     __shared__ float zx_s[kTM];            // the token's logit (one lane of the split finds it)
     __shared__ HeadPart xw[kTM];           // wave-pair merge
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r0 = blockIdx.x * kTM;
-    const int split = blockIdx.y;
+    const int R = rows_now(r_max, d_rows);
+    const int rtiles = (R + kTM - 1) / kTM;
+    const int nsplit = splits_for(R, V);
     const int ntiles = (V + kTN - 1) / kTN;
-    const int t0 = split * tiles_per_split, t1 = min(ntiles, t0 + tiles_per_split);
+    const int tiles_per_split = (ntiles + nsplit - 1) / nsplit;
     const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;   // this wave's quarter
     const int nk = (H + kTK - 1) / kTK;
 
+    // One (row tile, split) item per workgroup; workgroups beyond this
+    // call's items (a count read on the device) have nothing to do.
+    const int item = blockIdx.x;
+    if (item >= rtiles * nsplit) return;
+    const int r0 = (item % rtiles) * kTM;
+    const int split = item / rtiles;
+    const int t0 = split * tiles_per_split, t1 = min(ntiles, t0 + tiles_per_split);
+
     if (tid < kTM) {
-        tok_s[tid] = (r0 + tid < R && tok) ? tok[r0 + tid] : -1;
+        const bool have = r0 + tid < R;
+        if (logits) tok_s[tid] = have && row_ptr(hr, r0 + tid, H) != nullptr;
+        else tok_s[tid] = (have && tok) ? tok[r0 + tid] : -1;
         zx_s[tid] = NAN;
     }
 
@@ -107,11 +155,12 @@ void head_stats_kernel(const uint16_t* __restrict__ hid, const uint16_t* __restr
     // Staging: thread t moves 32 bf16 of row t / 2, k half (t % 2) * 32, of
     // each operand tile per step, as two 16-element pieces.
     const int srow = tid >> 1, skh = (tid & 1) * 32;
-    auto load16 = [&](const uint16_t* base, int nrows, int row, int k, uint4& x0, uint4& x1) {
+    const uint16_t* arow = r0 + srow < R ? row_ptr(hr, r0 + srow, H) : nullptr;
+    auto load16 = [&](const uint16_t* rowp, int k, uint4& x0, uint4& x1) {
         x0 = make_uint4(0u, 0u, 0u, 0u);
         x1 = x0;
-        if (row < nrows) {
-            const uint16_t* p = base + (size_t)row * H + k;
+        if (rowp) {
+            const uint16_t* p = rowp + k;
             if (k + 16 <= H) {
                 x0 = *reinterpret_cast<const uint4*>(p);
                 x1 = *reinterpret_cast<const uint4*>(p + 8);
@@ -133,10 +182,11 @@ void head_stats_kernel(const uint16_t* __restrict__ hid, const uint16_t* __restr
         uint4 a0, a1, a2, a3, b0, b1, b2, b3;
     };
     auto load_step = [&](int v0, int k0, Piece& pc) {
-        load16(hid, R, r0 + srow, k0 + skh, pc.a0, pc.a1);
-        load16(hid, R, r0 + srow, k0 + skh + 16, pc.a2, pc.a3);
-        load16(w, V, v0 + srow, k0 + skh, pc.b0, pc.b1);
-        load16(w, V, v0 + srow, k0 + skh + 16, pc.b2, pc.b3);
+        const uint16_t* brow = v0 + srow < V ? w + (size_t)(v0 + srow) * H : nullptr;
+        load16(arow, k0 + skh, pc.a0, pc.a1);
+        load16(arow, k0 + skh + 16, pc.a2, pc.a3);
+        load16(brow, k0 + skh, pc.b0, pc.b1);
+        load16(brow, k0 + skh + 16, pc.b2, pc.b3);
     };
     auto store_step = [&](const Piece& pc) {
         uint4* ra = reinterpret_cast<uint4*>(&As[srow][skh]);
@@ -186,6 +236,23 @@ void head_stats_kernel(const uint16_t* __restrict__ hid, const uint16_t* __restr
             }
         }
 
+        if (logits) {
+            // The tile's logits, one row segment of 32 columns per block.
+            #pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                #pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int rl = wr + 32 * a + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                    if (!tok_s[rl]) continue;
+                    #pragma unroll
+                    for (int b = 0; b < 2; ++b) {
+                        const int col = v0 + wc + 32 * b + (lane & 31);
+                        if (col < V) out[(size_t)(r0 + rl) * V + col] = acc[a][b][i];
+                    }
+                }
+            }
+            continue;
+        }
         // Fold the tile into the lane's running row statistics.
         #pragma unroll
         for (int a = 0; a < 2; ++a) {
@@ -219,6 +286,7 @@ void head_stats_kernel(const uint16_t* __restrict__ hid, const uint16_t* __restr
         }
     }
 
+    if (logits) return;
     // Lanes holding the same rows (same l / 32 half): merge across columns.
     #pragma unroll
     for (int q = 0; q < 32; ++q) {
@@ -275,9 +343,12 @@ void head_stats_kernel(const uint16_t* __restrict__ hid, const uint16_t* __restr
 // Per row: merge the splits' partials (in split order) into the outputs.
 // Greedy partials carry the first argmax; sampled ones do not (INT_MAX), and
 // the sampled call reports none.
-__global__ void head_merge_kernel(const HeadPart* __restrict__ part, int R, int splits, float c,
-                                  int sampled, float* out_max, float* out_sum, float* out_z,
+__global__ void head_merge_kernel(const HeadPart* __restrict__ part, int r_max,
+                                  const int* __restrict__ d_rows, int V, float c, int sampled,
+                                  float* out_max, float* out_sum, float* out_z,
                                   int32_t* out_arg) {
+    const int R = rows_now(r_max, d_rows);
+    const int splits = splits_for(R, V);
     const int r = blockIdx.x * blockDim.x + threadIdx.x;
     if (r >= R) return;
     float m = -INFINITY, s = 0.0f, z = NAN, bv = -INFINITY;
@@ -296,20 +367,62 @@ __global__ void head_merge_kernel(const HeadPart* __restrict__ part, int R, int 
 
 bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Vocabulary splits: as many as fit one resident wave of workgroups (two per
-// CU on 256 CUs) over the row tiles -- a second, partial wave would cost a
-// whole workgroup's time -- each split at least eight vocabulary tiles long.
-constexpr int kResidentSlots = 512;
-
-int splits_for(int R, int V) {
-    const int rt = (R + kTM - 1) / kTM, nt = (V + kTN - 1) / kTN;
-    int s = kResidentSlots / rt;
-    s = s < 1 ? 1 : s;
-    const int cap = (nt + 7) / 8;
-    return s > cap ? cap : s;
-}
+int items_for(int R, int V) { return ((R + kTM - 1) / kTM) * splits_for(R, V); }
 
 }  // namespace
+
+namespace svhead {
+
+// splits(R) * R stays within max(65536, R) (one resident wave of 128-row
+// tiles, or a single split) and within cap * R.
+size_t stats_workspace_bytes(int r_max, int V) {
+    if (r_max < 1 || V < 1) return 0;
+    const long long cap = ((V + kTN - 1) / kTN + 7) / 8;
+    long long n = (long long)kResidentSlots * kTM;
+    if (r_max > n) n = r_max;
+    if (cap * r_max < n) n = cap * r_max;
+    return (size_t)n * sizeof(HeadPart);
+}
+
+int head_stats_launch(const HeadRows& rows, const uint16_t* weight, int r_max,
+                      const int* d_rows, int H, int V, const int32_t* tokens,
+                      float temperature, float* out_max, float* out_sum, float* out_z,
+                      int32_t* out_arg, void* workspace, hipStream_t s) {
+    if (r_max < 1) return SV_OK;
+    const bool sampled = temperature > 0.0f;
+    const float c = sampled ? (float)(1.4426950408889634 / (double)temperature) : 0.0f;
+    HeadPart* part = static_cast<HeadPart*>(workspace);
+    // One workgroup per item. With the count read on the device, the grid
+    // covers every count up to r_max: up to 512 row tiles a count has at most
+    // 512 items, beyond that one split, so no more items than r_max has.
+    int grid = items_for(r_max, V);
+    if (d_rows && grid < kResidentSlots) grid = kResidentSlots;
+    if (sampled) {
+        hipLaunchKernelGGL(head_stats_kernel<kEpiSampled>, dim3((unsigned)grid),
+                           dim3(kHThreads), 0, s, rows, weight, r_max, d_rows, H, V, tokens, c,
+                           part, nullptr);
+    } else {
+        hipLaunchKernelGGL(head_stats_kernel<kEpiGreedy>, dim3((unsigned)grid),
+                           dim3(kHThreads), 0, s, rows, weight, r_max, d_rows, H, V, tokens, c,
+                           part, nullptr);
+    }
+    if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+    hipLaunchKernelGGL(head_merge_kernel, dim3((unsigned)((r_max + 255) / 256)), dim3(256), 0, s,
+                       part, r_max, d_rows, V, c, sampled ? 1 : 0, out_max, out_sum, out_z,
+                       out_arg);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+int head_logits_launch(const HeadRows& rows, const uint16_t* weight, int R, int H, int V,
+                       float* out, hipStream_t s) {
+    if (R < 1) return SV_OK;
+    hipLaunchKernelGGL(head_stats_kernel<kEpiLogits>, dim3((unsigned)items_for(R, V)),
+                       dim3(kHThreads), 0, s, rows, weight, R, nullptr, H, V, nullptr, 0.0f,
+                       nullptr, out);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+}  // namespace svhead
 
 extern "C" size_t spec_head_workspace_bytes(int R, int V) {
     if (R < 1 || V < 1) return 0;
@@ -333,26 +446,8 @@ extern "C" int spec_head_stats(const void* hidden, const void* weight, int R, in
         return SV_ERR_ALIGN;
     }
     if (workspace_bytes < spec_head_workspace_bytes(R, V)) return SV_ERR_ARG;
-    const int splits = splits_for(R, V);
-    const int ntiles = (V + kTN - 1) / kTN;
-    const int tps = (ntiles + splits - 1) / splits;
-    const bool sampled = temperature > 0.0f;
-    const float c = sampled ? (float)(1.4426950408889634 / (double)temperature) : 0.0f;
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    HeadPart* part = static_cast<HeadPart*>(workspace);
-    const dim3 grid((unsigned)((R + kTM - 1) / kTM), (unsigned)splits);
-    const uint16_t* hp = static_cast<const uint16_t*>(hidden);
-    const uint16_t* wp = static_cast<const uint16_t*>(weight);
-    if (sampled) {
-        hipLaunchKernelGGL(head_stats_kernel<true>, grid, dim3(kHThreads), 0, s, hp, wp, R, H, V,
-                           tokens, c, tps, part);
-    } else {
-        hipLaunchKernelGGL(head_stats_kernel<false>, grid, dim3(kHThreads), 0, s, hp, wp, R, H, V,
-                           tokens, c, tps, part);
-    }
-    if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
-    hipLaunchKernelGGL(head_merge_kernel, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s,
-                       part, R, splits, c, sampled ? 1 : 0, out_max, out_sumexp, out_ztok,
-                       out_argmax);
-    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+    const HeadRows rows{static_cast<const uint16_t*>(hidden), nullptr, nullptr, R};
+    return svhead::head_stats_launch(rows, static_cast<const uint16_t*>(weight), R, nullptr, H,
+                                     V, tokens, temperature, out_max, out_sumexp, out_ztok,
+                                     out_argmax, workspace, static_cast<hipStream_t>(stream));
 }

@@ -56,6 +56,7 @@
 #include <type_traits>
 #include <vector>
 
+#include "philox_device.h"
 #include "spec_verify.h"
 
 namespace {
@@ -95,13 +96,6 @@ constexpr int TW_DEC = 2;       // 64-bit decision: (epoch << 32) | accepted (wo
 constexpr int kRecWords = 4;
 constexpr int R_MT = 0, R_MD = 1, R_ST = 2, R_SD = 3;
 constexpr int kStatWords = 4;   // words R_MT..R_SD make a record complete
-
-// Philox4x32 constants (Salmon et al., SC'11): round multipliers and the key
-// increments applied between rounds.
-constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
-constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
-constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;
-constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
 
 constexpr double kLog2e = 1.4426950408889634073599246810019;
 
@@ -170,29 +164,8 @@ __device__ __forceinline__ bool tag_ok(unsigned long long w, unsigned ep) {
 
 // ----------------------------------------------------------------- Philox --
 
-__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
-                                               uint32_t c3, uint32_t k0, uint32_t k1) {
-    #pragma unroll
-    for (int r = 0; r < 10; ++r) {
-        if (r > 0) {
-            k0 += kPhiloxW0;
-            k1 += kPhiloxW1;
-        }
-        const uint32_t lo0 = kPhiloxM0 * c0, hi0 = __umulhi(kPhiloxM0, c0);
-        const uint32_t lo1 = kPhiloxM1 * c2, hi1 = __umulhi(kPhiloxM1, c2);
-        const uint32_t n0 = hi1 ^ c1 ^ k0;
-        const uint32_t n2 = hi0 ^ c3 ^ k1;
-        c0 = n0;
-        c1 = lo1;
-        c2 = n2;
-        c3 = lo0;
-    }
-    return make_uint4(c0, c1, c2, c3);
-}
-
-__device__ __forceinline__ double word_to_uniform(uint32_t w) {
-    return (double)(w >> 8) * (1.0 / 16777216.0);
-}
+using svrng::philox4x32_10;
+using svrng::word_to_uniform;
 
 // ---------------------------------------------------------- element types --
 

@@ -1,0 +1,445 @@
+// verify_hidden.hip -- batched draft verification from hidden states through
+// the shared output head, for MI355X (gfx950).
+//
+// What is computed: "Speculative decoding becomes standard: DSpark and
+// multi-token drafters", section "What DSpark adds", paragraph 1 (the drafter
+// shares the frozen output head with the target, so both models' logits for
+// a position are that head applied to a hidden state), section "Why
+// draft-and-verify does not change the output", paragraphs 1 and 2 (keep
+// drafted tokens while the target agrees -- greedy: equal to its most likely
+// token; sampled: u < min(1, p/q) -- then emit the target's own token drawn
+// from the residual max(0, p - q), or one more token from the target when the
+// whole budget survives), and section "What DSpark adds", paragraph 2 (ragged
+// per-request budgets). The outputs are those of spec_verify_run on the
+// logits z = h W^T, but the logits of the scored rows never reach memory.
+//
+// Design, five stream-ordered launches:
+//   1. plan (one workgroup): clamps budgets, checks drafted tokens, and packs
+//      the rows a request needs -- target rows 0..k_b, and in sampled mode
+//      drafter rows 0..k_b-1 -- into a row map, with the row count left on
+//      the device;
+//   2. the head product with the statistics epilogue over the packed rows
+//      (max, exp-sum and drafted token's logit; greedy: first argmax), its
+//      grid covering any count up to the batch's bound;
+//   3. decide (a thread per request): p(x), q(x), the accept test with the
+//      Philox uniforms, the first rejection; greedy outputs are final here;
+//   4. sampled only: the head product once more for each request's draw rows
+//      (target and drafter row j_b for a residual, target row k_b for a
+//      bonus), writing their fp32 logits -- bit-identical to the values the
+//      statistics were taken over, since each logit accumulates in the same
+//      order;
+//   5. sampled only: the inverse-CDF draw (a workgroup per request) over
+//      those rows in vocabulary order: segment masses first, then one wave
+//      rescans the segment where the running mass crosses u R.
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "head_gemm.h"
+#include "philox_device.h"
+#include "spec_verify.h"
+
+namespace {
+
+using svhead::HeadRows;
+using svrng::philox4x32_10;
+using svrng::word_to_uniform;
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kDrawThreads = 256;                  // 4 waves
+constexpr int kSegRows = 16;                       // a segment: 16 rows of 64 elements
+constexpr int kSeg = kSegRows * 64;
+constexpr int kMaxSegs = (SV_MAX_VOCAB + kSeg - 1) / kSeg;
+
+enum DrawKind { kNoDraw = 0, kResidual = 1, kBonus = 2 };
+
+struct DrawDesc {                                  // one request's draw
+    float mt, st;                                  // target row: max, exp-sum
+    float md, sd;                                  // drafter row (residual)
+    float u;                                       // u_smp of the drawn position
+    int kind;                                      // DrawKind
+    int pos;                                       // output position j_b
+    int pad;
+};
+
+// Workspace layout (byte offsets, each 256-aligned).
+struct Layout {
+    size_t rowmap, rowtok, off, nrows, sm, ss, sz, sa, part, drawmap, desc, logits, total;
+};
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Layout layout_for(int B, int K, int V) {
+    const size_t rmax = (size_t)B * (2 * K + 1);
+    Layout L{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o += up256(bytes);
+        return at;
+    };
+    L.rowmap = take(rmax * 4);
+    L.rowtok = take(rmax * 4);
+    L.off = take((size_t)B * 4);
+    L.nrows = take(4);
+    L.sm = take(rmax * 4);
+    L.ss = take(rmax * 4);
+    L.sz = take(rmax * 4);
+    L.sa = take(rmax * 4);
+    L.part = take(svhead::stats_workspace_bytes((int)rmax, V));
+    L.drawmap = take((size_t)B * 2 * 4);
+    L.desc = take((size_t)B * sizeof(DrawDesc));
+    L.logits = take((size_t)B * 2 * (size_t)V * 4);
+    L.total = o;
+    return L;
+}
+
+__device__ __forceinline__ int clamp_budget(int k, int K, unsigned& flags) {
+    if (k < 0 || k > K) {
+        flags |= SV_FLAG_BAD_BUDGET;
+        return k < 0 ? 0 : K;
+    }
+    return k;
+}
+
+// Exclusive prefix over threads in thread order (each thread one count).
+__device__ unsigned plan_exclusive(unsigned* wsum, unsigned v) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    unsigned incl = v;
+    #pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const unsigned u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    unsigned base = 0;
+    for (int w = 0; w < wave; ++w) base += wsum[w];
+    return base + incl - v;
+}
+
+// Packed rows of request b start at off[b]: target rows 0..k (virtual row
+// b (K+1) + i), then in sampled mode drafter rows 0..k-1 (virtual row
+// B (K+1) + b K + i). Each carries the drafted token of its position (-1 for
+// the target row k, and for a token outside [0, V), which is flagged).
+__global__ __launch_bounds__(kPlanThreads) void hv_plan_kernel(
+    const int32_t* __restrict__ budgets, const int32_t* __restrict__ tokens, int B, int K, int V,
+    int greedy, int32_t* __restrict__ rowmap, int32_t* __restrict__ rowtok,
+    int32_t* __restrict__ off, int32_t* __restrict__ nrows, int32_t* __restrict__ status) {
+    __shared__ unsigned wsum[kPlanWaves];
+    __shared__ unsigned flags_s;
+    const int tid = threadIdx.x;
+    if (tid == 0) flags_s = 0u;
+    const int per = (B + kPlanThreads - 1) / kPlanThreads;
+    const int b0 = min(tid * per, B), b1 = min(b0 + per, B);
+    unsigned flags = 0u, cnt = 0u;
+    for (int b = b0; b < b1; ++b) {
+        const int k = clamp_budget(budgets[b], K, flags);
+        cnt += greedy ? (unsigned)(k + 1) : (unsigned)(2 * k + 1);
+    }
+    const unsigned base = plan_exclusive(wsum, cnt);
+    unsigned o = base;
+    unsigned ignore = 0u;
+    for (int b = b0; b < b1; ++b) {
+        const int k = clamp_budget(budgets[b], K, ignore);
+        off[b] = (int32_t)o;
+        for (int i = 0; i <= k; ++i) {
+            int x = -1;
+            if (i < k) {
+                x = tokens[(size_t)b * K + i];
+                if (x < 0 || x >= V) {
+                    flags |= SV_FLAG_BAD_TOKEN;
+                    x = -1;
+                }
+            }
+            rowmap[o + i] = b * (K + 1) + i;
+            rowtok[o + i] = x;
+            if (!greedy && i < k) {
+                rowmap[o + k + 1 + i] = B * (K + 1) + b * K + i;
+                rowtok[o + k + 1 + i] = x;
+            }
+        }
+        o += greedy ? (unsigned)(k + 1) : (unsigned)(2 * k + 1);
+    }
+    if (flags) atomicOr(&flags_s, flags);
+    if (tid == kPlanThreads - 1) *nrows = (int32_t)o;   // the last thread ends the packing
+    __syncthreads();
+    if (tid == 0 && status) *status = (int32_t)flags_s;
+}
+
+// One thread per request: the accept tests, the first rejection, the emitted
+// drafted prefix; greedy also the target's token. Sampled requests leave a
+// draw descriptor and their draw rows for the next two launches.
+__global__ void hv_decide_kernel(const int32_t* __restrict__ budgets,
+                                 const int32_t* __restrict__ tokens, int B, int K, int V,
+                                 int greedy, double c64, uint32_t key0, uint32_t key1,
+                                 const int32_t* __restrict__ off, const float* __restrict__ sm,
+                                 const float* __restrict__ ss, const float* __restrict__ sz,
+                                 const int32_t* __restrict__ sa, int32_t* __restrict__ out_tokens,
+                                 int32_t* __restrict__ out_n, float* __restrict__ out_p,
+                                 float* __restrict__ out_q, int32_t* __restrict__ drawmap,
+                                 DrawDesc* __restrict__ desc) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    unsigned ignore = 0u;
+    const int k = clamp_budget(budgets[b], K, ignore);
+    const int o = off[b];
+    int32_t* row = out_tokens + (size_t)b * (K + 1);
+    int j = k;
+    if (greedy) {
+        for (int i = 0; i < k; ++i) {
+            if (tokens[(size_t)b * K + i] != sa[o + i]) {
+                j = i;
+                break;
+            }
+        }
+        for (int i = 0; i < j; ++i) row[i] = tokens[(size_t)b * K + i];
+        row[j] = sa[o + j];
+        for (int i = j + 1; i <= K; ++i) row[i] = -1;
+        if (out_p) for (int i = 0; i < K; ++i) out_p[(size_t)b * K + i] = NAN;
+        if (out_q) for (int i = 0; i < K; ++i) out_q[(size_t)b * K + i] = NAN;
+        out_n[b] = j;
+        DrawDesc d{};
+        d.kind = kNoDraw;
+        desc[b] = d;
+        drawmap[2 * b] = -1;
+        drawmap[2 * b + 1] = -1;
+        return;
+    }
+    for (int i = 0; i < k; ++i) {
+        const int x = tokens[(size_t)b * K + i];
+        const bool valid = x >= 0 && x < V;
+        const int rt = o + i, rd = o + k + 1 + i;
+        double px = 0.0, qx = 0.0;
+        if (valid) {
+            px = exp2(((double)sz[rt] - (double)sm[rt]) * c64) / (double)ss[rt];
+            qx = exp2(((double)sz[rd] - (double)sm[rd]) * c64) / (double)ss[rd];
+        }
+        const uint4 rw = philox4x32_10((uint32_t)b, (uint32_t)i, 0u, 0u, key0, key1);
+        const bool accept = word_to_uniform(rw.x) * qx < px;
+        if (out_p) out_p[(size_t)b * K + i] = (float)px;
+        if (out_q) out_q[(size_t)b * K + i] = (float)qx;
+        if (!accept && j == k) j = i;
+    }
+    for (int i = k; i < K; ++i) {
+        if (out_p) out_p[(size_t)b * K + i] = NAN;
+        if (out_q) out_q[(size_t)b * K + i] = NAN;
+    }
+    for (int i = 0; i < j; ++i) row[i] = tokens[(size_t)b * K + i];
+    for (int i = j; i <= K; ++i) row[i] = -1;           // row[j] is the draw's
+    out_n[b] = j;
+    const uint4 rw = philox4x32_10((uint32_t)b, (uint32_t)j, 0u, 0u, key0, key1);
+    DrawDesc d{};
+    d.u = (float)word_to_uniform(rw.y);
+    d.pos = j;
+    d.mt = sm[o + j];
+    d.st = ss[o + j];
+    drawmap[2 * b] = b * (K + 1) + j;
+    if (j < k) {
+        d.kind = kResidual;
+        d.md = sm[o + k + 1 + j];
+        d.sd = ss[o + k + 1 + j];
+        drawmap[2 * b + 1] = B * (K + 1) + b * K + j;
+    } else {
+        d.kind = kBonus;
+        drawmap[2 * b + 1] = -1;
+    }
+    desc[b] = d;
+}
+
+__device__ __forceinline__ float wave_incl_scan(float x) {
+    const int lane = threadIdx.x & 63;
+    #pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float u = __shfl_up(x, o, 64);
+        if (lane >= o) x += u;
+    }
+    return x;
+}
+
+// The draw of one request. mass(v) = max(0, p(v) - q(v)) for a residual
+// (p from the target row, q from the drafter row, each 2^((z - m) c) / S),
+// p(v) for a bonus or when the residual has no mass. y is the smallest v
+// whose running mass, in vocabulary order, exceeds u times the total; if
+// rounding leaves no such v, the last v with positive mass. The running mass
+// within a segment is a wave prefix over 16 rows of 64, the same arithmetic
+// in the segment pass and the rescan, so the rescanned segment's running
+// mass ends at exactly the segment mass the crossing was found with.
+__global__ __launch_bounds__(kDrawThreads) void hv_draw_kernel(
+    const float* __restrict__ logits, int K, int V, float c, const DrawDesc* __restrict__ desc,
+    int32_t* __restrict__ out_tokens) {
+    __shared__ float seg_s[kMaxSegs];
+    __shared__ int pick_s;
+    __shared__ float base_s, t_s;
+    const int b = blockIdx.x;
+    const DrawDesc d = desc[b];
+    if (d.kind == kNoDraw) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float* zt = logits + (size_t)(2 * b) * V;
+    const float* zd = zt + V;
+    const int nseg = (V + kSeg - 1) / kSeg;
+    const float ist = 1.0f / d.st;
+    const float isd = d.kind == kResidual ? 1.0f / d.sd : 0.0f;
+
+    auto mass = [&](int v, bool resid) -> float {
+        if (v >= V) return 0.0f;
+        const float p = __builtin_amdgcn_exp2f((zt[v] - d.mt) * c) * ist;
+        if (!resid) return p;
+        const float q = __builtin_amdgcn_exp2f((zd[v] - d.md) * c) * isd;
+        return fmaxf(p - q, 0.0f);
+    };
+    // Running mass of segment s up to the end of each 64-element row.
+    auto seg_mass = [&](int s, bool resid) -> float {
+        float carry = 0.0f;
+        for (int e = 0; e < kSegRows; ++e) {
+            const float incl = wave_incl_scan(mass(s * kSeg + e * 64 + lane, resid));
+            carry += __shfl(incl, 63, 64);
+        }
+        return carry;
+    };
+
+    bool resid = d.kind == kResidual;
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int s = wave; s < nseg; s += kDrawThreads / 64) {
+            const float m = seg_mass(s, resid);
+            if (lane == 0) seg_s[s] = m;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float total = 0.0f;
+            for (int s = 0; s < nseg; ++s) total += seg_s[s];
+            pick_s = total > 0.0f ? 1 : 0;
+            if (total > 0.0f) {
+                const float t = d.u * total;
+                float cum = 0.0f, base = 0.0f;
+                int pick = -1, lastpos = -1;
+                for (int s = 0; s < nseg; ++s) {
+                    const float next = cum + seg_s[s];
+                    if (seg_s[s] > 0.0f) lastpos = s;
+                    if (pick < 0 && next > t) {
+                        pick = s;
+                        base = cum;
+                    }
+                    cum = next;
+                }
+                // No crossing (u R rounded up to R): the last segment with
+                // mass, whose rescan then finds no crossing either and takes
+                // its last positive-mass element.
+                if (pick < 0) {
+                    pick = lastpos;
+                    base = -INFINITY;
+                }
+                pick_s = pick + 1;
+                base_s = base;
+                t_s = t;
+            }
+        }
+        __syncthreads();
+        if (pick_s > 0 || !resid) break;
+        resid = false;                                  // no residual mass: draw from p
+        __syncthreads();
+    }
+    if (wave != 0) return;
+    const int s = pick_s - 1;
+    int y = -1, lastpos = -1;
+    if (s >= 0) {
+        const float base = base_s, t = t_s;
+        float carry = 0.0f;
+        for (int e = 0; e < kSegRows && y < 0; ++e) {
+            const int v = s * kSeg + e * 64 + lane;
+            const float x = mass(v, resid);
+            const float incl = wave_incl_scan(x);
+            const unsigned long long cross = __ballot(base + (carry + incl) > t);
+            const unsigned long long pos = __ballot(x > 0.0f);
+            if (cross) y = s * kSeg + e * 64 + __builtin_ctzll(cross);
+            if (pos) lastpos = s * kSeg + e * 64 + 63 - __builtin_clzll(pos);
+            carry += __shfl(incl, 63, 64);
+        }
+    }
+    if (y < 0) y = lastpos;
+    if (lane == 0) out_tokens[(size_t)b * (K + 1) + d.pos] = y < 0 ? 0 : y;
+}
+
+bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" size_t spec_verify_hidden_workspace_bytes(int B, int K, int V) {
+    if (B < 1 || B > SV_MAX_BATCH || K < 0 || K > SV_MAX_K || V < 1 || V > SV_MAX_VOCAB) {
+        return 0;
+    }
+    return layout_for(B, K, V).total;
+}
+
+extern "C" int spec_verify_hidden(const void* target_hidden, const void* draft_hidden,
+                                  const void* head, const int32_t* draft_tokens,
+                                  const int32_t* budgets, int B, int K, int H, int V,
+                                  float temperature, uint64_t seed, int32_t* out_tokens,
+                                  int32_t* out_num_accepted, float* out_p_draft,
+                                  float* out_q_draft, int32_t* out_status, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    if (B < 0 || B > SV_MAX_BATCH || K < 0 || K > SV_MAX_K || H < 8 || (H % 8) != 0 ||
+        V < 1 || V > SV_MAX_VOCAB || !std::isfinite(temperature) || temperature < 0.0f) {
+        return SV_ERR_ARG;
+    }
+    if (B == 0) return SV_OK;
+    const bool greedy = temperature == 0.0f;
+    if (!target_hidden || !head || !budgets || !out_tokens || !out_num_accepted || !workspace ||
+        (K > 0 && !draft_tokens) || (!greedy && K > 0 && !draft_hidden)) {
+        return SV_ERR_NULL;
+    }
+    if (!aligned_to(target_hidden, 16) || (draft_hidden && !aligned_to(draft_hidden, 16)) ||
+        !aligned_to(head, 16) || (draft_tokens && !aligned_to(draft_tokens, 4)) ||
+        !aligned_to(budgets, 4) || !aligned_to(out_tokens, 4) ||
+        !aligned_to(out_num_accepted, 4) || (out_p_draft && !aligned_to(out_p_draft, 4)) ||
+        (out_q_draft && !aligned_to(out_q_draft, 4)) ||
+        (out_status && !aligned_to(out_status, 4)) || !aligned_to(workspace, 256)) {
+        return SV_ERR_ALIGN;
+    }
+    const Layout L = layout_for(B, K, V);
+    if (workspace_bytes < L.total) return SV_ERR_ARG;
+
+    char* ws = static_cast<char*>(workspace);
+    auto i32 = [&](size_t o) { return reinterpret_cast<int32_t*>(ws + o); };
+    auto f32 = [&](size_t o) { return reinterpret_cast<float*>(ws + o); };
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint16_t* th = static_cast<const uint16_t*>(target_hidden);
+    const uint16_t* dh = static_cast<const uint16_t*>(draft_hidden);
+    const uint16_t* w = static_cast<const uint16_t*>(head);
+    const int rmax = greedy ? B * (K + 1) : B * (2 * K + 1);
+    const double c64 = greedy ? 0.0 : 1.4426950408889634073599246810019 / (double)temperature;
+
+    hipLaunchKernelGGL(hv_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, budgets, draft_tokens,
+                       B, K, V, greedy ? 1 : 0, i32(L.rowmap), i32(L.rowtok), i32(L.off),
+                       i32(L.nrows), out_status);
+    if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+
+    const HeadRows rows{th, dh, i32(L.rowmap), B * (K + 1)};
+    int rc = svhead::head_stats_launch(rows, w, rmax, i32(L.nrows), H, V, i32(L.rowtok),
+                                       temperature, f32(L.sm), greedy ? nullptr : f32(L.ss),
+                                       greedy ? nullptr : f32(L.sz), greedy ? i32(L.sa) : nullptr,
+                                       ws + L.part, s);
+    if (rc != SV_OK) return rc;
+
+    const int dthreads = 256;
+    hipLaunchKernelGGL(hv_decide_kernel, dim3((unsigned)((B + dthreads - 1) / dthreads)),
+                       dim3(dthreads), 0, s, budgets, draft_tokens, B, K, V, greedy ? 1 : 0, c64,
+                       (uint32_t)(seed & 0xFFFFFFFFull), (uint32_t)(seed >> 32), i32(L.off),
+                       f32(L.sm), f32(L.ss), f32(L.sz), i32(L.sa), out_tokens, out_num_accepted,
+                       out_p_draft, out_q_draft, i32(L.drawmap),
+                       reinterpret_cast<DrawDesc*>(ws + L.desc));
+    if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+    if (greedy) return SV_OK;
+
+    const HeadRows draw_rows{th, dh, i32(L.drawmap), B * (K + 1)};
+    rc = svhead::head_logits_launch(draw_rows, w, 2 * B, H, V, f32(L.logits), s);
+    if (rc != SV_OK) return rc;
+    hipLaunchKernelGGL(hv_draw_kernel, dim3((unsigned)B), dim3(kDrawThreads), 0, s,
+                       f32(L.logits), K, V, (float)c64,
+                       reinterpret_cast<const DrawDesc*>(ws + L.desc), out_tokens);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+}

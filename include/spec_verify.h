@@ -258,6 +258,56 @@ int spec_head_stats(const void* hidden, const void* weight, int R, int H, int V,
  * one partial per row and vocabulary split. 0 on bad arguments. Host only. */
 size_t spec_head_workspace_bytes(int R, int V);
 
+/*
+ * spec_verify_hidden -- one verify step from hidden states through the shared
+ * output head: the outputs of spec_verify_run on the logits z = h W^T,
+ * without writing the logits of the scored rows anywhere ("Speculative
+ * decoding becomes standard: DSpark and multi-token drafters", section "What
+ * DSpark adds", paragraph 1: the drafter shares the frozen output head with
+ * the target; section "Why draft-and-verify does not change the output",
+ * paragraphs 1 and 2: the greedy and sampled rules; section "What DSpark
+ * adds", paragraph 2: per-request budgets). Logits are fp32 accumulations of
+ * exact bf16 products; p and q, the accept test, the Philox counters and the
+ * inverse-CDF draw are those of spec_verify_run. Stream-ordered, no host
+ * sync; five launches (plan, head statistics, decide, and in sampled mode
+ * the head's logits for each request's draw rows and the draw).
+ *   target_hidden  bf16 [B, K+1, H] row-major (device, 16-byte aligned).
+ *   draft_hidden   bf16 [B, K, H] (device, 16-byte aligned); may be NULL
+ *                  when temperature == 0 or K == 0.
+ *   head           bf16 [V, H] row-major (device, 16-byte aligned).
+ *   draft_tokens   int32 [B, K] (device); may be NULL when K == 0.
+ *   budgets        int32 [B] (device), 0 <= k_b <= K.
+ *   B, K, H, V     requests (0..SV_MAX_BATCH; 0 is a no-op), drafted
+ *                  positions (0..SV_MAX_K), hidden size (>= 8, a multiple
+ *                  of 8), vocabulary (1..SV_MAX_VOCAB).
+ *   temperature    > 0 sampled, 0 greedy (drafter states and seed unused).
+ *   seed           Philox key; counter (b, i, 0, 0) as in spec_verify_run.
+ *   out_tokens     int32 [B, K+1]: x_0..x_{j-1}, y, then -1.
+ *   out_num_accepted int32 [B]: j_b.
+ *   out_p_draft, out_q_draft  float [B, K] or NULL: p_i(x_i), q_i(x_i) for
+ *                  i < k_b, NaN elsewhere and in greedy mode.
+ *   out_status     int32 [1] (device) or NULL: this call's SV_FLAG_BAD_BUDGET
+ *                  and SV_FLAG_BAD_TOKEN bits (written, not accumulated). A
+ *                  flagged request's outputs are undefined.
+ *   workspace      device scratch of at least
+ *                  spec_verify_hidden_workspace_bytes(B, K, V) bytes,
+ *                  256-byte aligned, caller-owned; calls sharing it must not
+ *                  overlap. Most of it is the fp32 logits of two rows per
+ *                  request (8 B V bytes).
+ * Errors (nothing enqueued): SV_ERR_ARG, SV_ERR_NULL, SV_ERR_ALIGN;
+ * SV_ERR_HIP if a launch fails.
+ */
+int spec_verify_hidden(const void* target_hidden, const void* draft_hidden, const void* head,
+                       const int32_t* draft_tokens, const int32_t* budgets, int B, int K, int H,
+                       int V, float temperature, uint64_t seed, int32_t* out_tokens,
+                       int32_t* out_num_accepted, float* out_p_draft, float* out_q_draft,
+                       int32_t* out_status, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* spec_verify_hidden_workspace_bytes -- scratch spec_verify_hidden needs for
+ * (B, K, V); 0 on bad arguments. Host only. */
+size_t spec_verify_hidden_workspace_bytes(int B, int K, int V);
+
 /* spec_verify_free -- release the context (NULL-safe, idempotent on NULL).
  * Waits for the device before freeing the workspace. */
 void spec_verify_free(spec_verify_ctx* ctx);

@@ -30,15 +30,17 @@ def to_oracle(x: torch.Tensor):
     return x.numpy(), "f32"
 
 
-def check_probabilities(gpu_p, ora_p, budgets):
-    """p_x / q_x parity on every budgeted position."""
+def check_probabilities(gpu_p, ora_p, budgets, rtol=None):
+    """p_x / q_x parity on every budgeted position (rtol: an array of
+    per-position relative tolerances, default PROB_RTOL everywhere)."""
     gpu_p = np.asarray(gpu_p, dtype=np.float64)
     bad = []
     for n, k in enumerate(budgets):
         for i in range(int(k)):
             o, g = ora_p[n, i], gpu_p[n, i]
+            tol = PROB_RTOL if rtol is None else float(rtol[n, i])
             if o >= PROB_FLOOR:
-                ok = abs(g - o) <= PROB_RTOL * o
+                ok = abs(g - o) <= tol * o
             else:
                 ok = 0.0 <= g <= PROB_FLOOR
             if not ok:
@@ -51,9 +53,11 @@ def padded(tokens, K):
     return out
 
 
-def compare_sampled(gpu_tokens, gpu_n, decisions, K):
+def compare_sampled(gpu_tokens, gpu_n, decisions, K, acc_window=None, cdf_window=None):
     """Compare sampled outputs with the oracle's decisions, excusing near-ties.
 
+    acc_window[n][i] and cdf_window[n] widen the near-tie band of request n's
+    acceptance at position i and of its draw (default NEAR_TIE).
     Returns (n_excused, unexcused) where unexcused lists the requests whose
     first diverging decision was not within the near-tie band.
     """
@@ -67,13 +71,15 @@ def compare_sampled(gpu_tokens, gpu_n, decisions, K):
         if g_n != d.n_accepted:
             i = min(g_n, d.n_accepted)        # first position decided differently
             margin = d.acc_margin[i] if i < len(d.acc_margin) else np.inf
-            if margin < NEAR_TIE:
+            band = NEAR_TIE if acc_window is None else float(acc_window[n][i])
+            if margin < band:
                 excused += 1
             else:
                 unexcused.append((n, "accept", i, g_n, d.n_accepted, margin))
             continue
         # Same acceptance path: only the drawn token can differ.
-        if d.cdf_margin < NEAR_TIE:
+        band = NEAR_TIE if cdf_window is None else float(cdf_window[n])
+        if d.cdf_margin < band:
             excused += 1
         else:
             unexcused.append((n, "sample", d.n_accepted, g_tok, o_tok, d.cdf_margin,

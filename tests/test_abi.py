@@ -143,6 +143,9 @@ def test_init_without_a_device_fails_cleanly():
     assert rc == sb.SV_ERR_HIP and ctx is None
 
 
+_VALID = 1     # marks valid arguments in the table below
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(B=-1), sb.SV_ERR_ARG),
     (dict(B=sb.SV_MAX_BATCH + 1), sb.SV_ERR_ARG),
@@ -197,3 +200,52 @@ def test_head_workspace_size():
     assert sb.spec_head_workspace_bytes(0, 10) == 0
     n = sb.spec_head_workspace_bytes(300, 1000)
     assert n > 0 and n % (300 * 16) == 0
+
+
+_VALID = 1     # marks valid arguments in the table below
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), sb.SV_ERR_ARG),
+    (dict(B=sb.SV_MAX_BATCH + 1), sb.SV_ERR_ARG),
+    (dict(K=-1), sb.SV_ERR_ARG),
+    (dict(K=sb.SV_MAX_K + 1), sb.SV_ERR_ARG),
+    (dict(H=4), sb.SV_ERR_ARG),
+    (dict(H=12), sb.SV_ERR_ARG),
+    (dict(V=0), sb.SV_ERR_ARG),
+    (dict(T=-0.5), sb.SV_ERR_ARG),
+    (dict(T=math.inf), sb.SV_ERR_ARG),
+    (dict(th=None), sb.SV_ERR_NULL),
+    (dict(head=None), sb.SV_ERR_NULL),
+    (dict(dh=None), sb.SV_ERR_NULL),
+    (dict(dh=None, T=0.0), _VALID),
+    (dict(tok=None), sb.SV_ERR_NULL),
+    (dict(ws=None), sb.SV_ERR_NULL),
+    (dict(th=0x1008), sb.SV_ERR_ALIGN),
+    (dict(ws=0x4010), sb.SV_ERR_ALIGN),
+    (dict(n=0x3002), sb.SV_ERR_ALIGN),
+    (dict(ws_bytes=4096), sb.SV_ERR_ARG),
+    (dict(B=0, th=None, dh=None, head=None, tok=None, bud=None, ws=None), sb.SV_OK),
+])
+def test_verify_hidden_argument_checks(kw, code):
+    """Host-side checks of spec_verify_hidden (they return before any launch)."""
+    args = dict(th=0x1000, dh=0x2000, head=0x3000, tok=0x5000, bud=0x6000, B=8, K=4, H=64,
+                V=1000, T=1.0, out=0x7000, n=0x8000, ws=0x4000, ws_bytes=0)
+    args.update(kw)
+    if code == _VALID:
+        # Valid arguments: only the workspace size check (too small here)
+        # stands between them and a launch.
+        code = sb.SV_ERR_ARG
+    rc = sb.spec_verify_hidden(args["th"], args["dh"], args["head"], args["tok"], args["bud"],
+                               args["B"], args["K"], args["H"], args["V"], args["T"], 1,
+                               args["out"], args["n"], None, None, None, args["ws"],
+                               args["ws_bytes"] if "ws_bytes" in kw else 0, None)
+    assert rc == code
+
+
+def test_verify_hidden_workspace_size():
+    assert sb.spec_verify_hidden_workspace_bytes(0, 4, 100) == 0
+    assert sb.spec_verify_hidden_workspace_bytes(4, sb.SV_MAX_K + 1, 100) == 0
+    n = sb.spec_verify_hidden_workspace_bytes(512, 8, 151936)
+    # Dominated by the fp32 logits of two draw rows per request.
+    assert 8 * 512 * 151936 <= n < 8 * 512 * 151936 + (8 << 20)

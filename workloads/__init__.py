@@ -8,5 +8,5 @@ the HIP library's tests and the CPU oracle can take their inputs from it.
 """
 from .configs import CONFIGS, Workload, get  # noqa: F401
 from .confidence import make_confidences  # noqa: F401
-from .head import make_head_inputs  # noqa: F401
+from .head import make_head_inputs, make_hidden_inputs  # noqa: F401
 from .gen import make_inputs, philox_seed  # noqa: F401
