@@ -10,8 +10,10 @@ the step time); the roofline of the dominant kernel, the streaming pass
 (algorithmic HBM bytes per launch over its duration from the library's own
 per-pass HIP events, against the 8 TB/s HBM peak); the fp64 CPU oracle's rate
 on a bounded sample of the same workload; and, on the same batch shape, the
-verify-budget scheduler (per call, beside its oracle) and the fused output
-head (TFLOP/s against the 2.5 PFLOP/s dense bf16 peak, beside its oracle).
+verify-budget scheduler (per call, beside its oracle), the fused output
+head (TFLOP/s against the 2.5 PFLOP/s dense bf16 peak, beside its oracle) and
+a whole verify step from hidden states through that head (per call, beside
+its oracle).
 
   python bench.py [--steps K] [--warmup W] [--warmup-settle S] [--workload heavy]
                   [--no-cpu-baseline]
@@ -199,6 +201,68 @@ def bench_head(R, H, V, steps, T=1.0, seed=5):
     }
 
 
+def bench_hidden(B, K, H, V, steps, T=1.0, seed=5):
+    """A whole verify step from hidden states through the shared head at the
+    verify batch's shape (budgets 2 + Binomial(6, 1/3)): plan, the head
+    product with the statistics epilogue over every budgeted row, decide,
+    the head product again over each request's draw rows (fp32 logits), and
+    the inverse-CDF draw. Per-call durations from HIP events. The matrix
+    work is 2 H V flops per scored row plus per draw row; its rate over the
+    whole call is a lower bound on the product kernels' own rate. The oracle
+    is timed on one request and scaled to the batch."""
+    import numpy as np
+    import torch
+    from draft_verify_sampling_spec_amd import HiddenVerify
+    from workloads import make_hidden_inputs, philox_seed
+    inp = make_hidden_inputs(B, K, H, V, seed, device="cuda", variant="heavy", temperature=T)
+    hv = HiddenVerify("cuda", B, K, V)
+    args = (inp["target_hidden"], inp["draft_hidden"], inp["head"], inp["tokens"], inp["budgets"], T)
+    for s in range(3):
+        hv.run(*args, philox_seed(WORKLOAD_INDEX["heavy"], 3_000_000 + s))
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    outs = []
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        outs.append(hv.run(*args, philox_seed(WORKLOAD_INDEX["heavy"], 3_100_000 + i)))
+        b.record()
+    torch.cuda.synchronize()
+    if any(int(o[4].item()) != 0 for o in outs):
+        raise RuntimeError("spec_verify_hidden set device status flags")
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    mean_ms = sum(ms) / len(ms)
+    budgets = inp["budgets"].cpu().numpy()
+    scored = int(np.sum(2 * budgets + 1))
+    n_acc = outs[-1][1].cpu().numpy()
+    draw_rows = int(np.sum(np.where(n_acc < budgets, 2, 1)))
+    flops = 2.0 * (scored + draw_rows) * H * V
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+    from oracle import hidden as ohid
+
+    def bits(x):
+        return x.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    th, dh, w = bits(inp["target_hidden"][:1]), bits(inp["draft_hidden"][:1]), bits(inp["head"])
+    t0 = time.perf_counter()
+    ohid.verify_from_hidden(th, dh, w, inp["tokens"][:1].cpu().numpy(), budgets[:1], T,
+                            philox_seed(WORKLOAD_INDEX["heavy"], 3_100_000))
+    cpu_s = (time.perf_counter() - t0) * B
+    verified = int(budgets.sum())
+    return {
+        "config": f"B={B} K={K} H={H} V={V} bf16 hidden states and head, budgets 2..8 "
+                  f"(mean 4), T={T}; {scored} scored rows, {draw_rows} draw rows (last call)",
+        "ms_per_call": {"mean": mean_ms, "median": ms[len(ms) // 2],
+                        "p5": ms[int(0.05 * (len(ms) - 1))], "p95": ms[int(0.95 * (len(ms) - 1))]},
+        "calls": steps,
+        "verified_draft_tokens_per_s": verified / (mean_ms * 1e-3),
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "flops_per_call": flops, "note": "whole call, all five launches"},
+        "cpu_oracle_s_per_call": cpu_s,
+        "cpu_oracle_sample": f"fp64 oracle on request 0 ({int(budgets[0])} drafted), scaled to {B} requests",
+    }
+
+
 def copy_probe(gib):
     import torch
     n = int(gib * (1 << 30))
@@ -361,6 +425,8 @@ def main():
             # drafter rows), Qwen3-4B's hidden size.
             log("[bench] output head")
             result["head"] = bench_head(rows, 2560, V, min(args.steps, 10))
+            log("[bench] verify from hidden states")
+            result["hidden"] = bench_hidden(B, K, 2560, V, min(args.steps, 10), T)
     if not args.no_cpu_baseline and not greedy and args.workload == "heavy":
         n_req = min(args.cpu_requests, B)
         log(f"[bench] cpu baseline: oracle on {n_req} requests")
