@@ -16,7 +16,7 @@ a whole verify step from hidden states through that head (per call, beside
 its oracle).
 
   python bench.py [--steps K] [--warmup W] [--warmup-settle S] [--workload heavy]
-                  [--no-cpu-baseline]
+                  [--no-cpu-baseline] [--verify-only]
   python bench.py --copy-probe GIB   # plain copies of a known size (counter scale)
 """
 from __future__ import annotations
@@ -214,8 +214,8 @@ def bench_hidden(B, K, H, V, steps, T=1.0, seed=5):
     import torch
     from draft_verify_sampling_spec_amd import HiddenVerify
     from workloads import make_hidden_inputs, philox_seed
-    inp = make_hidden_inputs(B, K, H, V, seed, device="cuda", variant="heavy", temperature=T)
-    hv = HiddenVerify("cuda", B, K, V)
+    inp = make_hidden_inputs(B, K, H, V, seed, device="cuda:0", variant="heavy", temperature=T)
+    hv = HiddenVerify("cuda:0", B, K, V)
     args = (inp["target_hidden"], inp["draft_hidden"], inp["head"], inp["tokens"], inp["budgets"], T)
     for s in range(3):
         hv.run(*args, philox_seed(WORKLOAD_INDEX["heavy"], 3_000_000 + s))
@@ -286,6 +286,8 @@ def main():
     ap.add_argument("--workload", default="heavy", choices=sorted(WORKLOAD_INDEX))
     ap.add_argument("--temperature", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--verify-only", action="store_true",
+                    help="time the verify step only (no scheduler, head or hidden-state legs)")
     ap.add_argument("--cpu-requests", type=int, default=512)
     ap.add_argument("--copy-probe", type=float, default=None)
     args = ap.parse_args()
@@ -417,7 +419,7 @@ def main():
         },
         "cpu_baseline": None,
     }
-    if not greedy:
+    if not greedy and not args.verify_only:
         log("[bench] budget scheduler")
         result["scheduler"] = bench_scheduler(B, K, args.steps)
         if args.workload == "heavy":

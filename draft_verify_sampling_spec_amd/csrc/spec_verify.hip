@@ -32,12 +32,13 @@
 //    its latency overlaps the next unit) and decides: greedy, the row's
 //    first argmax (the team completing last for a request writes its
 //    outputs); sampled, p(x), q(x), the accept test and the decision word.
-//  * Draw pass (draw_kernel, sampled): one workgroup per request finds the
-//    first rejection from the decision words, streams that position's
-//    target and drafter rows once for the residual masses of 512-element
-//    blocks, and scans the block holding the threshold; the bonus position
-//    picks its chunk from the records' p masses and scans that chunk. It
-//    writes the request's outputs. Nothing in it waits on another workgroup.
+//  * Draw pass (draw_kernel, sampled): one 8-wave workgroup per request, two
+//    per CU, finds the first rejection from the decision words, streams that
+//    position's target and drafter rows once for the residual masses of
+//    512-element blocks, and scans the block holding the threshold; the bonus
+//    position picks its chunk from the records' p masses and streams that
+//    chunk's blocks the same way. It writes the request's outputs. Nothing in
+//    it waits on another workgroup.
 //  * Waiting (streaming pass): only the control wave waits on other
 //    workgroups, and only for an owed decision: the records of a team whose
 //    units all precede the unit it publishes next (G >= C), so by induction
@@ -77,8 +78,7 @@ constexpr int kPlanSlots = 8;                  // plan ring (> kPlanLead + 1)
 static_assert(kPlanLead >= kMbox && kPlanSlots > kPlanLead + 1, "plan ring too short");
 constexpr int kOwedSlots = 8;                  // chunk-0 units whose decision is owed
 constexpr int PL_END = 0, PL_UNIT = 1;
-constexpr int kBlocks = kG * kDataWaves;       // element blocks of a chunk scan (group, data wave)
-static_assert(kBlocks <= 64, "a chunk scan locates its block in one wave");
+constexpr int kBlocks = kG * kDataWaves;       // 64-group blocks (one 16-byte load per lane) in a chunk
 constexpr int kTeamWords = 32;                 // words per team record (128 bytes)
 constexpr int kReqStride = 16;                 // words between request counters (64 bytes)
 constexpr unsigned kSpinLimit = 1u << 20;      // bounded device-scope wait (~1 s)
@@ -264,16 +264,8 @@ struct Shared {
     int seq_b[64];
     // Set once a bounded wait expired: every later wait returns at once.
     int abort_wait;
-    // Draw pass: the request's draw, set by wave 0 for the whole workgroup.
-    int dr_j, dr_k, dr_mode, dr_chunk;           // mode: 0 p (chunk dr_chunk), 1 residual
-    double dr_u, dr_thr;
-    float dr_mt, dr_md, dr_ist, dr_isd;
-    // Block-wide scratch under barriers: the streaming pass's prologue (per
-    // wave sums) and the draw pass's scans.
-    double scan_ws[kBlocks];
+    // Prologue scratch under barriers: per-wave partial sums.
     int red_i[kWaves];
-    int sub_star;
-    double sub_base;
 };
 
 // Relaxed workgroup-scope accesses for the mailboxes.
@@ -1032,104 +1024,6 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
     }
 }
 
-// ------------------------------------------------------------- draw pass --
-
-// Element-level inverse CDF inside one chunk (whole workgroup). The data
-// waves load the chunk once, in the streaming layout: group j of data thread
-// dt holds the W elements from (j * kDataThreads + dt) * W, so element order
-// runs over groups, then data waves, then lanes, then a lane's elements.
-// Wave 0 finds the (group, data wave) block whose running mass crosses thr;
-// that block's wave scans its elements. Mass: residual max(0, p - q) when
-// d.has_d, else p; p = 2^((z_t - mt) c) / S_t. Returns the offset in the
-// chunk of the smallest element whose running mass from the chunk start
-// exceeds thr, zero-mass elements excluded; if rounding leaves no crossing,
-// the last positive-mass element of the last block with mass; -1 if the
-// chunk has no mass.
-template <typename E, bool kVec>
-__device__ int chunk_scan(const Params& P, Shared& sh, const Unit& d, float mt, float ist,
-                          float md, float isd, double thr) {
-    constexpr int W = Elem<E>::W;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const float c = P.c32;
-    const bool res = d.has_d;
-    auto mass = [&](const uint4& t, const uint4& q, int k) -> float {
-        const float pv = fast_exp2((Elem<E>::at(t, k) - mt) * c) * ist;
-        if (!res) return pv;
-        return fmaxf(0.0f, pv - fast_exp2((Elem<E>::at(q, k) - md) * c) * isd);
-    };
-    uint4 gt[kG], gd[kG];
-    if (wave > 0) {
-        issue_loads<E, kVec>(P, d, tid - 64, gt, gd);
-        #pragma unroll
-        for (int j = 0; j < kG; ++j) {
-            float sj = 0.0f;
-            #pragma unroll
-            for (int k = 0; k < W; ++k) sj += mass(gt[j], gd[j], k);
-            const double ws = wave_sum((double)sj);
-            if (lane == 0) sh.scan_ws[j * kDataWaves + wave - 1] = ws;
-        }
-    }
-    __syncthreads();
-    if (wave == 0) {
-        const double m = lane < kBlocks ? sh.scan_ws[lane] : 0.0;
-        const double incl = wave_incl_scan(m, lane);
-        const double up = __shfl_up(incl, 1, 64);
-        const double excl = lane ? up : 0.0;
-        const unsigned long long hit = __ballot(m > 0.0 && incl > thr);
-        const unsigned long long pos = __ballot(m > 0.0);
-        const int star = hit ? __ffsll((long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : -1);
-        const double base = __shfl(excl, star < 0 ? 0 : star, 64);
-        if (lane == 0) {
-            sh.sub_star = star;
-            sh.sub_base = base;
-        }
-    }
-    __syncthreads();
-    const int star = sh.sub_star;
-    if (star < 0) return -1;
-    if (wave == 1 + star % kDataWaves) {
-        const int js = star / kDataWaves;
-        uint4 t = gt[0], q = gd[0];
-        #pragma unroll
-        for (int j = 1; j < kG; ++j) {
-            if (js == j) {
-                t = gt[j];
-                q = gd[j];
-            }
-        }
-        float r[W];
-        double pre[W];
-        double run = 0.0;
-        #pragma unroll
-        for (int k = 0; k < W; ++k) {
-            r[k] = mass(t, q, k);
-            run += (double)r[k];
-            pre[k] = run;
-        }
-        const double incl = wave_incl_scan(run, lane);
-        const double up = __shfl_up(incl, 1, 64);
-        const double excl = lane ? up : 0.0;
-        const double tt = thr - sh.sub_base;
-        const int e = (js * kDataThreads + tid - 64) * W;
-        int cand = INT_MAX, last = -1;
-        #pragma unroll
-        for (int k = 0; k < W; ++k) {
-            if (r[k] > 0.0f) {
-                last = e + k;
-                if (cand == INT_MAX && excl + pre[k] > tt) cand = e + k;
-            }
-        }
-        #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            cand = min(cand, __shfl_xor(cand, o, 64));
-            last = max(last, __shfl_xor(last, o, 64));
-        }
-        if (lane == 0) sh.red_i[0] = cand != INT_MAX ? cand : last;
-    }
-    __syncthreads();
-    return sh.red_i[0];
-}
-
 template <typename E, bool kGreedy, bool kVec>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void verify_kernel(Params P) {
@@ -1189,6 +1083,8 @@ void verify_kernel(Params P) {
     }
 }
 
+// ------------------------------------------------------------- draw pass --
+
 // Wave 0: the chunk of team tr's target row (records in pl, normalisers ts)
 // where the running p mass, chunk by chunk, first exceeds u times the row's
 // total; thr = the part of that threshold inside the chunk. chunk -1: no
@@ -1220,27 +1116,56 @@ __device__ void p_chunk(const Params& P, const TeamPoll& pl, const TeamStats& ts
 // streaming pass on the same stream, so every decision word and record is
 // final. Wave 0 finds the request's deciding position j (the first rejected
 // drafted position, k if all k were accepted), merges team j's records into
-// its normalisers and takes the sampling uniform u. A first rejection draws
-// from the residual max(0, p_j - q_j): the data waves stream target row j and
-// drafter row j once, leaving the residual mass of every (chunk, group, data
-// wave) block in LDS; wave 0 finds the block where the running mass first
-// exceeds u R, and that block's wave scans its elements again. The bonus
-// position, or a residual without mass (rounding only), draws from p_j: its
-// chunk masses follow from the records and one chunk is scanned.
+// its normalisers and takes the sampling uniform u. The draw is an inverse
+// CDF in vocabulary order over blocks of 64 groups (512 bf16 or 256 fp32
+// elements, one 16-byte load per lane): the data waves stream the blocks of
+// a range, wave d taking every (kDrawDataWaves)-th block with kDrawSlots
+// blocks in flight, and leave each block's mass in LDS; wave 0 finds the
+// block where the running mass first exceeds the threshold, and one data
+// wave scans that block's elements again (cache-resident).
+//  * First rejection (j < k): the residual max(0, p_j - q_j) over the whole
+//    row pair, threshold u R. The first blocks' loads go out while wave 0
+//    merges the records.
+//  * Bonus position (j == k), or a residual without mass (rounding only):
+//    p_j. Its chunk masses follow from the records; the blocks of the chunk
+//    holding u times the total are streamed.
+// Eight waves per workgroup and two workgroups per CU, so one request's
+// start-up and final scan overlap another's streaming.
+constexpr int kDrawWaves = 8;                  // wave 0: control; waves 1-7: data
+constexpr int kDrawThreads = kDrawWaves * 64;
+constexpr int kDrawDataWaves = kDrawWaves - 1;
+constexpr int kDrawSlots = 6;                  // blocks in flight per data wave
+constexpr int kDrawNone = 0, kDrawResidual = 1, kDrawP = 2;
+
+// Draw pass state, written by wave 0 between barriers.
+struct DrawShared {
+    int j, k;
+    int mode;          // kDrawNone, kDrawResidual or kDrawP
+    int x0, x1;        // block range streamed
+    int star;          // block holding the threshold, from x0 (-1: none)
+    int done;          // star found
+    int y;             // drawn token
+    double u;          // sampling uniform of position j
+    double thr;        // threshold, as mass from block x0's start (then from block star's)
+    float mt, md, ist, isd;
+};
+
 template <typename E, bool kVec>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(kDrawThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void draw_kernel(Params P) {
     extern __shared__ __align__(16) unsigned char dyn_smem[];
-    __shared__ Shared sh;
-    double* blk = reinterpret_cast<double*>(dyn_smem);   // [C * kBlocks] residual block masses
+    __shared__ DrawShared dsh;
+    double* blk = reinterpret_cast<double*>(dyn_smem);   // block masses of the range [x0, x1)
     constexpr int W = Elem<E>::W;
+    constexpr int BE = 64 * W;                           // elements per block
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // Requests in reverse order: the streaming pass read the last requests'
     // rows last, so they are the likeliest to still be cached.
     const int b = P.B - 1 - (int)blockIdx.x;
-    const int K = P.K, C = P.C;
+    const int K = P.K, V = P.V;
+    const int NB = (V + BE - 1) / BE;                    // blocks per row
     const unsigned ep = P.epoch;
-    TeamPoll pl;                                   // wave 0: team j's records (prologue)
+    TeamPoll pl;                                         // wave 0: team j's records
     if (wave == 0) {
         // One round of loads: lane t < K the decision of position t, lane 63
         // the budget.
@@ -1256,170 +1181,187 @@ void draw_kernel(Params P) {
         const int j = rej ? __ffsll((long long)rej) - 1 : k;
         poll_issue<false>(P, b * (K + 1) + j, pl);
         if (lane == 0) {
-            sh.dr_j = j;
-            sh.dr_k = k;
-            sh.dr_mode = j < k ? 1 : 0;
+            dsh.j = j;
+            dsh.k = k;
+            dsh.mode = j < k ? kDrawResidual : kDrawP;
+            dsh.done = 0;
+            dsh.y = 0;
         }
     }
     __syncthreads();
-    const int j = sh.dr_j, k = sh.dr_k;
-    auto chunk_unit = [&](int cc) -> Unit {
-        Unit d;
-        d.u = 0;
-        d.b = b;
-        d.i = j;
-        d.k = k;
-        d.c = cc;
-        d.tr = b * (K + 1) + j;
-        d.e0 = cc * P.CE;
-        d.n = min(P.CE, P.V - d.e0);
-        d.has_d = true;
-        return d;
+    const int j = dsh.j, k = dsh.k;
+    const E* rt = static_cast<const E*>(P.target) + ((size_t)b * (K + 1) + j) * (size_t)V;
+    const E* rd = j < k ? static_cast<const E*>(P.draft) + ((size_t)b * K + j) * (size_t)V : nullptr;
+    const bool vt = aligned16(rt), vd = rd != nullptr && aligned16(rd);
+    const int dw = wave - 1;
+    const int stride = kDrawSlots * kDrawDataWaves;      // blocks between a slot's loads
+
+    // Block x's group of this lane: elements (x * 64 + lane) * W onwards;
+    // past V they read as -inf (zero mass).
+    uint4 gt[kDrawSlots], gd[kDrawSlots];
+    auto issue = [&](int x, bool res, uint4& t, uint4& q) __attribute__((always_inline)) {
+        const int e = (x * 64 + lane) * W;
+        t = load_group<E, kVec>(rt, e, V, vt);
+        if (res) q = load_group<E, kVec>(rd, e, V, vd);
     };
-    // Residual: the data waves start streaming the row pair (two chunks in
-    // flight) while wave 0 merges the team's records.
-    uint4 ta[kG], qa[kG], tb[kG], qb[kG];
-    const int dt = tid - 64;
-    if (sh.dr_mode == 1 && wave > 0) {
-        issue_loads<E, kVec>(P, chunk_unit(0), dt, ta, qa);
-        if (C > 1) issue_loads<E, kVec>(P, chunk_unit(1), dt, tb, qb);
+    auto preload = [&](int x0, int x1, bool res) __attribute__((always_inline)) {
+        #pragma unroll
+        for (int s = 0; s < kDrawSlots; ++s) {
+            const int x = x0 + dw + s * kDrawDataWaves;
+            if (x < x1) issue(x, res, gt[s], gd[s]);
+        }
+    };
+    bool pre = false;
+    if (dsh.mode == kDrawResidual && wave > 0) {
+        preload(0, NB, true);
+        pre = true;
     }
     if (wave == 0) {
         if (!poll_complete<false>(P, pl) && lane == 0) atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);
         const TeamStats ts = team_stats(P, pl);
         const uint4 rw = philox4x32_10((uint32_t)(P.bbase + b), (uint32_t)j, 0u, 0u, P.key0, P.key1);
         const double u = word_to_uniform(rw.y);
-        int chunk = -1;
+        int x0 = 0, x1 = NB, mode = dsh.mode;
         double thr = 0.0;
-        if (j == k) p_chunk(P, pl, ts, u, chunk, thr);
+        if (mode == kDrawP) {
+            int chunk = -1;
+            p_chunk(P, pl, ts, u, chunk, thr);
+            if (chunk < 0) {
+                mode = kDrawNone;
+            } else {
+                x0 = chunk * kBlocks;
+                x1 = min(x0 + kBlocks, NB);
+            }
+        }
         if (lane == 0) {
-            sh.dr_chunk = chunk;
-            sh.dr_u = u;
-            sh.dr_thr = thr;
-            sh.dr_mt = ts.mt;
-            sh.dr_md = ts.md;
-            sh.dr_ist = (float)(1.0 / ts.st);
-            sh.dr_isd = (float)(1.0 / ts.sd);
+            dsh.mode = mode;
+            dsh.x0 = x0;
+            dsh.x1 = x1;
+            dsh.u = u;
+            dsh.thr = thr;
+            dsh.mt = ts.mt;
+            dsh.md = ts.md;
+            dsh.ist = (float)(1.0 / ts.st);
+            dsh.isd = (float)(1.0 / ts.sd);
         }
     }
     __syncthreads();
-    const float mt = sh.dr_mt, md = sh.dr_md, ist = sh.dr_ist, isd = sh.dr_isd;
+    const float mt = dsh.mt, md = dsh.md, ist = dsh.ist, isd = dsh.isd;
     const float c = P.c32;
-    auto rmass = [&](const uint4& t, const uint4& q, int kk) -> float {
+    auto mass = [&](const uint4& t, const uint4& q, int kk, bool res) -> float {
         const float pv = fast_exp2((Elem<E>::at(t, kk) - mt) * c) * ist;
-        const float qv = fast_exp2((Elem<E>::at(q, kk) - md) * c) * isd;
-        return fmaxf(0.0f, pv - qv);
+        if (!res) return pv;
+        return fmaxf(0.0f, pv - fast_exp2((Elem<E>::at(q, kk) - md) * c) * isd);
     };
-    int y = 0;
-    int mode = sh.dr_mode;
-    if (mode == 1) {
-        // Residual: stream both rows once (the next chunk's loads in flight
-        // while a chunk is reduced); block masses to LDS.
+    // At most two rounds: the residual, then p_j if the residual had no mass.
+    for (int round = 0; round < 2; ++round) {
+        const int mode = dsh.mode;
+        if (mode == kDrawNone) break;
+        const bool res = mode == kDrawResidual;
+        const int x0 = dsh.x0, x1 = dsh.x1;
         if (wave > 0) {
-            auto reduce = [&](int cc, const uint4 (&t)[kG], const uint4 (&q)[kG]) {
+            if (!(pre && round == 0)) preload(x0, x1, res);
+            for (int xr = x0 + dw; xr < x1; xr += stride) {
                 #pragma unroll
-                for (int g = 0; g < kG; ++g) {
-                    float sg = 0.0f;
-                    #pragma unroll
-                    for (int kk = 0; kk < W; ++kk) sg += rmass(t[g], q[g], kk);
-                    const double ws = wave_sum((double)sg);
-                    if (lane == 0) blk[cc * kBlocks + g * kDataWaves + wave - 1] = ws;
-                }
-            };
-            // Chunks 0 and 1 are in flight; each reduce frees its buffer
-            // for the chunk after the other buffer's.
-            for (int cc = 0; cc < C; cc += 2) {
-                reduce(cc, ta, qa);
-                if (cc + 2 < C) issue_loads<E, kVec>(P, chunk_unit(cc + 2), dt, ta, qa);
-                if (cc + 1 < C) {
-                    reduce(cc + 1, tb, qb);
-                    if (cc + 3 < C) issue_loads<E, kVec>(P, chunk_unit(cc + 3), dt, tb, qb);
+                for (int s = 0; s < kDrawSlots; ++s) {
+                    const int x = xr + s * kDrawDataWaves;
+                    if (x < x1) {
+                        float sg = 0.0f;
+                        #pragma unroll
+                        for (int kk = 0; kk < W; ++kk) sg += mass(gt[s], gd[s], kk, res);
+                        const double ws = wave_sum((double)sg);
+                        if (lane == 0) blk[x - x0] = ws;
+                        if (x + stride < x1) issue(x + stride, res, gt[s], gd[s]);
+                    }
                 }
             }
         }
         __syncthreads();
         if (wave == 0) {
-            const int nb = C * kBlocks;
-            double total = 0.0;
-            for (int x = lane; x < nb; x += 64) total += blk[x];
-            total = wave_sum(total);
+            const int nb = x1 - x0;
+            double thr = dsh.thr;
+            bool any = true;
+            if (res) {
+                double total = 0.0;
+                for (int x = lane; x < nb; x += 64) total += blk[x];
+                total = wave_sum(total);
+                thr = dsh.u * total;
+                any = total > 0.0;
+            }
             int star = -1;
             double base = 0.0;
-            const double t = sh.dr_u * total;
-            if (total > 0.0) chunk_crossing(nb, t, [&](int x) -> double { return blk[x]; }, star, base);
-            int chunk = -1;
-            double thr = t - base;
+            if (any) chunk_crossing(nb, thr, [&](int x) -> double { return blk[x]; }, star, base);
+            int nmode = mode, nx0 = x0, nx1 = x1;
+            double nthr = thr - base;
             if (star < 0) {
-                // No residual mass (rounding only): from p_j, whose records
-                // are read again.
-                TeamPoll pr;
-                poll_issue<false>(P, b * (K + 1) + j, pr);
-                const TeamStats tr = team_stats(P, pr);
-                p_chunk(P, pr, tr, sh.dr_u, chunk, thr);
+                nmode = kDrawNone;
+                if (res) {
+                    // No residual mass (rounding only): from p_j, whose
+                    // records are read again.
+                    TeamPoll pr;
+                    poll_issue<false>(P, b * (K + 1) + j, pr);
+                    const TeamStats tr = team_stats(P, pr);
+                    int chunk = -1;
+                    p_chunk(P, pr, tr, dsh.u, chunk, nthr);
+                    if (chunk >= 0) {
+                        nmode = kDrawP;
+                        nx0 = chunk * kBlocks;
+                        nx1 = min(nx0 + kBlocks, NB);
+                    }
+                }
             }
             if (lane == 0) {
-                sh.dr_mode = star >= 0 ? 1 : 0;
-                sh.sub_star = star;
-                sh.dr_chunk = chunk;
-                sh.dr_thr = thr;
+                dsh.star = star;
+                dsh.done = star >= 0;
+                dsh.mode = nmode;
+                dsh.x0 = nx0;
+                dsh.x1 = nx1;
+                dsh.thr = nthr;
             }
         }
         __syncthreads();
-        mode = sh.dr_mode;
-        if (mode == 1) {
-            const int star = sh.sub_star;
-            const int cc = star / kBlocks, l = star - cc * kBlocks;
-            const int g = l / kDataWaves, w = l - g * kDataWaves;
-            if (wave == 1 + w) {
-                // The block's elements again (just read: cache-resident).
-                const Unit d = chunk_unit(cc);
-                const E* target = static_cast<const E*>(P.target);
-                const E* draft = static_cast<const E*>(P.draft);
-                const E* rt = target + ((size_t)b * (K + 1) + j) * (size_t)P.V + d.e0;
-                const E* rd = draft + ((size_t)b * K + j) * (size_t)P.V + d.e0;
-                const int e = (g * kDataThreads + w * 64 + lane) * W;
-                const uint4 t4 = load_group<E, kVec>(rt, e, d.n, aligned16(rt));
-                const uint4 q4 = load_group<E, kVec>(rd, e, d.n, aligned16(rd));
-                float r[W];
-                double pre[W];
-                double run = 0.0;
-                #pragma unroll
-                for (int kk = 0; kk < W; ++kk) {
-                    r[kk] = rmass(t4, q4, kk);
-                    run += (double)r[kk];
-                    pre[kk] = run;
-                }
-                const double incl = wave_incl_scan(run, lane);
-                const double up = __shfl_up(incl, 1, 64);
-                const double excl = lane ? up : 0.0;
-                const double tt = sh.dr_thr;
-                int cand = INT_MAX, last = -1;
-                #pragma unroll
-                for (int kk = 0; kk < W; ++kk) {
-                    if (r[kk] > 0.0f) {
-                        last = e + kk;
-                        if (cand == INT_MAX && excl + pre[kk] > tt) cand = e + kk;
-                    }
-                }
-                #pragma unroll
-                for (int o = 32; o > 0; o >>= 1) {
-                    cand = min(cand, __shfl_xor(cand, o, 64));
-                    last = max(last, __shfl_xor(last, o, 64));
-                }
-                if (lane == 0) sh.red_i[0] = d.e0 + (cand != INT_MAX ? cand : last);
+        if (dsh.done) break;
+    }
+    if (dsh.done) {
+        if (wave == 1) {
+            // The block's elements again, in order: the first whose running
+            // mass exceeds the threshold; zero-mass elements are never drawn.
+            const bool res = dsh.mode == kDrawResidual;
+            const int x = dsh.x0 + dsh.star;
+            uint4 t4, q4;
+            issue(x, res, t4, q4);
+            const int e = (x * 64 + lane) * W;
+            float r[W];
+            double pref[W];
+            double run = 0.0;
+            #pragma unroll
+            for (int kk = 0; kk < W; ++kk) {
+                r[kk] = mass(t4, q4, kk, res);
+                run += (double)r[kk];
+                pref[kk] = run;
             }
-            __syncthreads();
-            y = sh.red_i[0];
+            const double incl = wave_incl_scan(run, lane);
+            const double up = __shfl_up(incl, 1, 64);
+            const double excl = lane ? up : 0.0;
+            const double tt = dsh.thr;
+            int cand = INT_MAX, last = -1;
+            #pragma unroll
+            for (int kk = 0; kk < W; ++kk) {
+                if (r[kk] > 0.0f) {
+                    last = e + kk;
+                    if (cand == INT_MAX && excl + pref[kk] > tt) cand = e + kk;
+                }
+            }
+            #pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                cand = min(cand, __shfl_xor(cand, o, 64));
+                last = max(last, __shfl_xor(last, o, 64));
+            }
+            if (lane == 0) dsh.y = cand != INT_MAX ? cand : (last >= 0 ? last : 0);
         }
+        __syncthreads();
     }
-    if (mode == 0 && sh.dr_chunk >= 0) {
-        // From p_j: one chunk.
-        Unit d = chunk_unit(sh.dr_chunk);
-        d.has_d = false;
-        const int o = chunk_scan<E, kVec>(P, sh, d, mt, ist, md, isd, sh.dr_thr);
-        y = o < 0 ? 0 : d.e0 + o;
-    }
-    if (tid == 0) request_outputs<false>(P, b, k, j, y);
+    if (tid == 0) request_outputs<false>(P, b, k, j, dsh.y);
 }
 
 // Philox blocks as the verifier draws them, for checking the generator.
@@ -1451,7 +1393,8 @@ int chunks_for(int vocab, int dtype) {
 
 size_t dyn_smem_bytes(int B) { return (size_t)(B + 1) * sizeof(int); }
 
-// The draw pass keeps one residual mass per (chunk, group, data wave) block.
+// The draw pass keeps one mass per block of a row (at most C chunks of
+// kBlocks blocks).
 size_t draw_smem_bytes(int C) { return (size_t)C * kBlocks * sizeof(double); }
 
 }  // namespace
@@ -1548,7 +1491,7 @@ int launch(spec_verify_ctx* ctx, Params& p, hipStream_t stream) {
     timed_end(ctx, t, stream);
     if (!G) {
         t = timed_begin(ctx, 1, stream);
-        hipLaunchKernelGGL((draw_kernel<E, Vv>), dim3((unsigned)p.B), dim3(kThreads),
+        hipLaunchKernelGGL((draw_kernel<E, Vv>), dim3((unsigned)p.B), dim3(kDrawThreads),
                            draw_smem_bytes(p.C), stream, p);
         if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
         timed_end(ctx, t, stream);
