@@ -330,7 +330,8 @@ __device__ __forceinline__ bool better_arg(float v, int i, float bv, int bi) {
 
 // Wave 0: find the chunk where the running mass over chunks 0..C-1 first
 // exceeds thr. mass(cc) gives chunk cc's mass. Returns (chunk, mass before it)
-// in every lane; chunk -1 if there is no mass.
+// in every lane; if rounding leaves no crossing, the last chunk with mass;
+// chunk -1 if there is no mass.
 template <typename F>
 __device__ void chunk_crossing(int C, double thr, F mass, int& chunk, double& base) {
     const int lane = threadIdx.x & 63;
@@ -341,7 +342,10 @@ __device__ void chunk_crossing(int C, double thr, F mass, int& chunk, double& ba
     const double incl = wave_incl_scan(acc, lane);
     const double prev = __shfl_up(incl, 1, 64);
     const unsigned long long hit = __ballot(incl > thr);
-    const int lane_star = hit ? (__ffsll((long long)hit) - 1) : 63;
+    // No crossing (rounding): the last lane holding mass, whose last block
+    // with mass is taken below.
+    const unsigned long long pos = __ballot(acc > 0.0);
+    const int lane_star = hit ? (__ffsll((long long)hit) - 1) : (pos ? 63 - __clzll((long long)pos) : 63);
     chunk = -1;
     base = 0.0;
     if (lane == lane_star) {

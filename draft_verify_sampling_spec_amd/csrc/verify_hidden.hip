@@ -28,9 +28,9 @@
 //      bonus), writing their fp32 logits -- bit-identical to the values the
 //      statistics were taken over, since each logit accumulates in the same
 //      order;
-//   5. sampled only: the inverse-CDF draw (a workgroup per request) over
-//      those rows in vocabulary order: segment masses first, then one wave
-//      rescans the segment where the running mass crosses u R.
+//   5. sampled only: the inverse-CDF draw (an 8-wave workgroup per request)
+//      over those rows in vocabulary order: 256-element block masses first,
+//      then one wave rescans the block where the running mass crosses u R.
 
 #include <hip/hip_runtime.h>
 
@@ -50,10 +50,6 @@ using svrng::word_to_uniform;
 
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
-constexpr int kDrawThreads = 256;                  // 4 waves
-constexpr int kSegRows = 16;                       // a segment: 16 rows of 64 elements
-constexpr int kSeg = kSegRows * 64;
-constexpr int kMaxSegs = (SV_MAX_VOCAB + kSeg - 1) / kSeg;
 
 enum DrawKind { kNoDraw = 0, kResidual = 1, kBonus = 2 };
 
@@ -251,117 +247,205 @@ __global__ void hv_decide_kernel(const int32_t* __restrict__ budgets,
     desc[b] = d;
 }
 
-__device__ __forceinline__ float wave_incl_scan(float x) {
-    const int lane = threadIdx.x & 63;
+// Running mass in vocabulary order over blocks of 256 elements: each lane
+// holds 4 consecutive elements of a block (one 16-byte load per row), the
+// block's mass is the fp64 wave sum of the lanes' fp32 sums, and the row's
+// masses run block by block in fp64.
+constexpr int kHvBlock = 256;
+constexpr int kHvDrawWaves = 8;
+constexpr int kHvDrawThreads = kHvDrawWaves * 64;
+constexpr int kHvDrawSlots = 6;                    // blocks in flight per wave
+
+__device__ __forceinline__ double hv_wave_sum(double v) {
     #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const float u = __shfl_up(x, o, 64);
-        if (lane >= o) x += u;
-    }
-    return x;
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
 }
 
-// The draw of one request. mass(v) = max(0, p(v) - q(v)) for a residual
-// (p from the target row, q from the drafter row, each 2^((z - m) c) / S),
-// p(v) for a bonus or when the residual has no mass. y is the smallest v
-// whose running mass, in vocabulary order, exceeds u times the total; if
-// rounding leaves no such v, the last v with positive mass. The running mass
-// within a segment is a wave prefix over 16 rows of 64, the same arithmetic
-// in the segment pass and the rescan, so the rescanned segment's running
-// mass ends at exactly the segment mass the crossing was found with.
-__global__ __launch_bounds__(kDrawThreads) void hv_draw_kernel(
-    const float* __restrict__ logits, int K, int V, float c, const DrawDesc* __restrict__ desc,
-    int32_t* __restrict__ out_tokens) {
-    __shared__ float seg_s[kMaxSegs];
-    __shared__ int pick_s;
-    __shared__ float base_s, t_s;
+__device__ __forceinline__ double hv_wave_incl_scan(double v, int lane) {
+    #pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double o = __shfl_up(v, off, 64);
+        if (lane >= off) v += o;
+    }
+    return v;
+}
+
+// Wave: the block where the running mass over blocks 0..n-1 first exceeds
+// thr, and the mass before it (every lane); if rounding leaves no crossing,
+// the last block with mass; -1 if no block has mass.
+__device__ void hv_block_crossing(const double* m, int n, double thr, int& star, double& base) {
+    const int lane = threadIdx.x & 63;
+    const int per = (n + 63) / 64;
+    const int a0 = min(lane * per, n), a1 = min(a0 + per, n);
+    double acc = 0.0;
+    for (int x = a0; x < a1; ++x) acc += m[x];
+    const double incl = hv_wave_incl_scan(acc, lane);
+    const double prev = __shfl_up(incl, 1, 64);
+    const unsigned long long hit = __ballot(incl > thr);
+    const unsigned long long pos = __ballot(acc > 0.0);
+    const int ls = hit ? __ffsll((long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : 63);
+    int found = -1;
+    double fb = 0.0;
+    if (lane == ls) {
+        double run = lane ? prev : 0.0;
+        int last = -1;
+        double run_last = 0.0;
+        for (int x = a0; x < a1; ++x) {
+            if (m[x] > 0.0) {
+                last = x;
+                run_last = run;
+                if (run + m[x] > thr) {
+                    found = x;
+                    break;
+                }
+            }
+            run += m[x];
+        }
+        if (found < 0) {
+            found = last;
+            run = run_last;
+        }
+        fb = run;
+    }
+    star = __shfl(found, ls, 64);
+    base = __shfl(fb, ls, 64);
+}
+
+// The draw of one request (a workgroup of 8 waves). mass(v) = max(0, p(v) -
+// q(v)) for a residual (p from the target row, q from the drafter row, each
+// 2^((z - m) c) / S), p(v) for a bonus or when the residual has no mass. y is
+// the smallest v whose running mass, in vocabulary order, exceeds u times the
+// total; if rounding leaves no such v, the last v with positive mass. Every
+// wave streams every eighth block of the row (or row pair) with
+// kHvDrawSlots blocks in flight and leaves each block's mass in LDS; wave 0
+// finds the block holding the threshold and scans its elements again.
+template <bool kVec>
+__global__ __launch_bounds__(kHvDrawThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void hv_draw_kernel(const float* __restrict__ logits, int K, int V, float c,
+                    const DrawDesc* __restrict__ desc, int32_t* __restrict__ out_tokens) {
+    extern __shared__ double blk[];                  // block masses [nb]
+    __shared__ int star_s, resid_s;
+    __shared__ double thr_s;
     const int b = blockIdx.x;
     const DrawDesc d = desc[b];
-    if (d.kind == kNoDraw) return;
+    if (d.kind == kNoDraw) return;                   // the whole workgroup
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* zt = logits + (size_t)(2 * b) * V;
     const float* zd = zt + V;
-    const int nseg = (V + kSeg - 1) / kSeg;
+    const int nb = (V + kHvBlock - 1) / kHvBlock;
+    const int stride = kHvDrawSlots * kHvDrawWaves;
     const float ist = 1.0f / d.st;
     const float isd = d.kind == kResidual ? 1.0f / d.sd : 0.0f;
 
-    auto mass = [&](int v, bool resid) -> float {
-        if (v >= V) return 0.0f;
-        const float p = __builtin_amdgcn_exp2f((zt[v] - d.mt) * c) * ist;
-        if (!resid) return p;
-        const float q = __builtin_amdgcn_exp2f((zd[v] - d.md) * c) * isd;
-        return fmaxf(p - q, 0.0f);
-    };
-    // Running mass of segment s up to the end of each 64-element row.
-    auto seg_mass = [&](int s, bool resid) -> float {
-        float carry = 0.0f;
-        for (int e = 0; e < kSegRows; ++e) {
-            const float incl = wave_incl_scan(mass(s * kSeg + e * 64 + lane, resid));
-            carry += __shfl(incl, 63, 64);
+    // This lane's 4 elements of block x (past V: -inf, zero mass).
+    auto load4 = [&](const float* row, int x) -> float4 {
+        const int e = x * kHvBlock + lane * 4;
+        if (kVec) {
+            return e < V ? *reinterpret_cast<const float4*>(row + e)
+                         : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         }
-        return carry;
+        float4 r;
+        r.x = e < V ? row[e] : -INFINITY;
+        r.y = e + 1 < V ? row[e + 1] : -INFINITY;
+        r.z = e + 2 < V ? row[e + 2] : -INFINITY;
+        r.w = e + 3 < V ? row[e + 3] : -INFINITY;
+        return r;
+    };
+    auto mass = [&](float t, float q, bool resid) -> float {
+        const float p = __builtin_amdgcn_exp2f((t - d.mt) * c) * ist;
+        if (!resid) return p;
+        return fmaxf(p - __builtin_amdgcn_exp2f((q - d.md) * c) * isd, 0.0f);
+    };
+    auto mass4 = [&](const float4& t, const float4& q, bool resid, float (&r)[4]) {
+        r[0] = mass(t.x, q.x, resid);
+        r[1] = mass(t.y, q.y, resid);
+        r[2] = mass(t.z, q.z, resid);
+        r[3] = mass(t.w, q.w, resid);
     };
 
-    bool resid = d.kind == kResidual;
     for (int pass = 0; pass < 2; ++pass) {
-        for (int s = wave; s < nseg; s += kDrawThreads / 64) {
-            const float m = seg_mass(s, resid);
-            if (lane == 0) seg_s[s] = m;
+        const bool resid = pass == 0 && d.kind == kResidual;
+        float4 gt[kHvDrawSlots], gd[kHvDrawSlots];
+        #pragma unroll
+        for (int s = 0; s < kHvDrawSlots; ++s) {
+            const int x = wave + s * kHvDrawWaves;
+            if (x < nb) {
+                gt[s] = load4(zt, x);
+                if (resid) gd[s] = load4(zd, x);
+            }
         }
-        __syncthreads();
-        if (tid == 0) {
-            float total = 0.0f;
-            for (int s = 0; s < nseg; ++s) total += seg_s[s];
-            pick_s = total > 0.0f ? 1 : 0;
-            if (total > 0.0f) {
-                const float t = d.u * total;
-                float cum = 0.0f, base = 0.0f;
-                int pick = -1, lastpos = -1;
-                for (int s = 0; s < nseg; ++s) {
-                    const float next = cum + seg_s[s];
-                    if (seg_s[s] > 0.0f) lastpos = s;
-                    if (pick < 0 && next > t) {
-                        pick = s;
-                        base = cum;
+        for (int xr = wave; xr < nb; xr += stride) {
+            #pragma unroll
+            for (int s = 0; s < kHvDrawSlots; ++s) {
+                const int x = xr + s * kHvDrawWaves;
+                if (x < nb) {
+                    float r[4];
+                    mass4(gt[s], gd[s], resid, r);
+                    const double ws = hv_wave_sum((double)(((r[0] + r[1]) + r[2]) + r[3]));
+                    if (lane == 0) blk[x] = ws;
+                    if (x + stride < nb) {
+                        gt[s] = load4(zt, x + stride);
+                        if (resid) gd[s] = load4(zd, x + stride);
                     }
-                    cum = next;
                 }
-                // No crossing (u R rounded up to R): the last segment with
-                // mass, whose rescan then finds no crossing either and takes
-                // its last positive-mass element.
-                if (pick < 0) {
-                    pick = lastpos;
-                    base = -INFINITY;
-                }
-                pick_s = pick + 1;
-                base_s = base;
-                t_s = t;
             }
         }
         __syncthreads();
-        if (pick_s > 0 || !resid) break;
-        resid = false;                                  // no residual mass: draw from p
+        if (wave == 0) {
+            double total = 0.0;
+            for (int x = lane; x < nb; x += 64) total += blk[x];
+            total = hv_wave_sum(total);
+            int star = -1;
+            double base = 0.0;
+            const double t = (double)d.u * total;
+            if (total > 0.0) hv_block_crossing(blk, nb, t, star, base);
+            if (lane == 0) {
+                star_s = star;
+                thr_s = t - base;
+                resid_s = resid ? 1 : 0;
+            }
+        }
         __syncthreads();
+        if (star_s >= 0 || !resid) break;               // no residual mass: from p
     }
     if (wave != 0) return;
-    const int s = pick_s - 1;
-    int y = -1, lastpos = -1;
-    if (s >= 0) {
-        const float base = base_s, t = t_s;
-        float carry = 0.0f;
-        for (int e = 0; e < kSegRows && y < 0; ++e) {
-            const int v = s * kSeg + e * 64 + lane;
-            const float x = mass(v, resid);
-            const float incl = wave_incl_scan(x);
-            const unsigned long long cross = __ballot(base + (carry + incl) > t);
-            const unsigned long long pos = __ballot(x > 0.0f);
-            if (cross) y = s * kSeg + e * 64 + __builtin_ctzll(cross);
-            if (pos) lastpos = s * kSeg + e * 64 + 63 - __builtin_clzll(pos);
-            carry += __shfl(incl, 63, 64);
+    const int x = star_s;
+    int y = 0;
+    if (x >= 0) {
+        const bool resid = resid_s != 0;
+        const float4 t4 = load4(zt, x);
+        const float4 q4 = resid ? load4(zd, x) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        float r[4];
+        mass4(t4, q4, resid, r);
+        double pre[4];
+        double run = 0.0;
+        #pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            run += (double)r[k];
+            pre[k] = run;
         }
+        const double incl = hv_wave_incl_scan(run, lane);
+        const double up = __shfl_up(incl, 1, 64);
+        const double excl = lane ? up : 0.0;
+        const double tt = thr_s;
+        const int e = x * kHvBlock + lane * 4;
+        int cand = INT_MAX, last = -1;
+        #pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (r[k] > 0.0f) {
+                last = e + k;
+                if (cand == INT_MAX && excl + pre[k] > tt) cand = e + k;
+            }
+        }
+        #pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            cand = min(cand, __shfl_xor(cand, o, 64));
+            last = max(last, __shfl_xor(last, o, 64));
+        }
+        y = cand != INT_MAX ? cand : (last >= 0 ? last : 0);
     }
-    if (y < 0) y = lastpos;
-    if (lane == 0) out_tokens[(size_t)b * (K + 1) + d.pos] = y < 0 ? 0 : y;
+    if (lane == 0) out_tokens[(size_t)b * (K + 1) + d.pos] = y;
 }
 
 bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -438,8 +522,16 @@ extern "C" int spec_verify_hidden(const void* target_hidden, const void* draft_h
     const HeadRows draw_rows{th, dh, i32(L.drawmap), B * (K + 1)};
     rc = svhead::head_logits_launch(draw_rows, w, 2 * B, H, V, f32(L.logits), s);
     if (rc != SV_OK) return rc;
-    hipLaunchKernelGGL(hv_draw_kernel, dim3((unsigned)B), dim3(kDrawThreads), 0, s,
-                       f32(L.logits), K, V, (float)c64,
-                       reinterpret_cast<const DrawDesc*>(ws + L.desc), out_tokens);
+    // 16-byte loads of the fp32 rows when every row starts 16-byte aligned.
+    const size_t draw_smem = (size_t)((V + kHvBlock - 1) / kHvBlock) * sizeof(double);
+    if (V % 4 == 0) {
+        hipLaunchKernelGGL(hv_draw_kernel<true>, dim3((unsigned)B), dim3(kHvDrawThreads), draw_smem,
+                           s, f32(L.logits), K, V, (float)c64,
+                           reinterpret_cast<const DrawDesc*>(ws + L.desc), out_tokens);
+    } else {
+        hipLaunchKernelGGL(hv_draw_kernel<false>, dim3((unsigned)B), dim3(kHvDrawThreads), draw_smem,
+                           s, f32(L.logits), K, V, (float)c64,
+                           reinterpret_cast<const DrawDesc*>(ws + L.desc), out_tokens);
+    }
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
