@@ -10,6 +10,10 @@ Modules:
   philox  -- Philox4x32-10 from the SC'11 definition, and the stream layout
              (key = seed, counter = (request, position, 0, 0)).
   verify  -- the verification rule itself (greedy and sampled), per request.
+  schedule -- the confidence-driven verify-budget scheduler.
+  head    -- the shared output head's row statistics.
+  hidden  -- a verify step whose logits come from hidden states and the head.
+  markov  -- the drafter's low-rank Markov head (previous-token logit bias).
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against facts that
 do not come from the oracle itself: library routines (rocRAND's Philox,
