@@ -11,9 +11,9 @@ the step time); the roofline of the dominant kernel, the streaming pass
 per-pass HIP events, against the 8 TB/s HBM peak); the fp64 CPU oracle's rate
 on a bounded sample of the same workload; and, on the same batch shape, the
 verify-budget scheduler (per call, beside its oracle), the fused output
-head (TFLOP/s against the 2.5 PFLOP/s dense bf16 peak, beside its oracle) and
-a whole verify step from hidden states through that head (per call, beside
-its oracle).
+head (TFLOP/s against the 2.5 PFLOP/s dense bf16 peak, beside its oracle), a
+whole verify step from hidden states through that head, and the drafter's
+low-rank Markov head over a drafted block (each per call, beside its oracle).
 
   python bench.py [--steps K] [--warmup W] [--warmup-settle S] [--workload heavy]
                   [--no-cpu-baseline] [--verify-only]
@@ -263,6 +263,66 @@ def bench_hidden(B, K, H, V, steps, T=1.0, seed=5):
     }
 
 
+def bench_markov(B, K, V, r, steps, seed=5):
+    """The drafter's low-rank Markov head over a drafted block at the verify
+    batch's shape: K positions in order, each the rank-r transition product
+    of the previous tokens plus the backbone row, stored as bf16, with the
+    first argmax drafted. Per-call durations from HIP events. Algorithmic HBM
+    bytes per call: backbone logits read and drafter logits written once
+    (B K V bf16 each), the vocabulary factor read once per position (V r
+    bf16), the previous tokens' rows of the other factor; the fp32 bias rows
+    the two launches of a position exchange are implementation traffic. The
+    oracle is timed on one request's block and scaled to the batch."""
+    import numpy as np
+    import torch
+    from draft_verify_sampling_spec_amd import MarkovDraft
+    from workloads import make_markov_inputs
+    inp = make_markov_inputs(B, K, V, r, seed, device="cuda:0")
+    md = MarkovDraft("cuda:0", B, K, V)
+    out_z = torch.empty((B, K, V), dtype=torch.bfloat16, device="cuda:0")
+    out_x = torch.empty((B, K), dtype=torch.int32, device="cuda:0")
+    args = (inp["base"], inp["markov_a"], inp["markov_b"], inp["prev"])
+    for _ in range(3):
+        md.run(*args, out_logits=out_z, out_tokens=out_x)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        _, _, st = md.run(*args, out_logits=out_z, out_tokens=out_x)
+        b.record()
+    torch.cuda.synchronize()
+    if int(st.item()) != 0:
+        raise RuntimeError("spec_markov_draft set device status flags")
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    mean_ms = sum(ms) / len(ms)
+    alg = 2 * (2 * B * K * V) + K * (2 * V * r + 2 * B * r) + 4 * B + 4 * B * K
+    impl_extra = K * 2 * (4 * B * V)
+    achieved = alg / (mean_ms * 1e-3) / 1e9
+    from oracle import markov as om
+
+    def vals(t):
+        return om.bf16_bits_to_f64(t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+    A, Bm = vals(inp["markov_a"]), vals(inp["markov_b"])
+    base0 = vals(inp["base"][:1])
+    t0 = time.perf_counter()
+    om.draft_block(base0, A, Bm, inp["prev"][:1].cpu().numpy())
+    cpu_s = (time.perf_counter() - t0) * B
+    return {
+        "config": f"B={B} K={K} V={V} r={r} bf16 backbone logits and factors",
+        "ms_per_call": {"mean": mean_ms, "median": ms[len(ms) // 2],
+                        "p5": ms[int(0.05 * (len(ms) - 1))], "p95": ms[int(0.95 * (len(ms) - 1))]},
+        "calls": steps,
+        "drafted_tokens_per_s": B * K / (mean_ms * 1e-3),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes_per_call": alg,
+                     "implementation_bias_bytes_per_call": impl_extra,
+                     "note": "whole call, 1 + 2K launches"},
+        "cpu_oracle_s_per_call": cpu_s,
+        "cpu_oracle_sample": f"fp64 oracle on request 0's block of {K} positions, scaled to {B} requests",
+    }
+
+
 def copy_probe(gib):
     import torch
     n = int(gib * (1 << 30))
@@ -429,6 +489,8 @@ def main():
             result["head"] = bench_head(rows, 2560, V, min(args.steps, 10))
             log("[bench] verify from hidden states")
             result["hidden"] = bench_hidden(B, K, 2560, V, min(args.steps, 10), T)
+            log("[bench] Markov head draft")
+            result["markov"] = bench_markov(B, K, V, 256, min(args.steps, 10))
     if not args.no_cpu_baseline and not greedy and args.workload == "heavy":
         n_req = min(args.cpu_requests, B)
         log(f"[bench] cpu baseline: oracle on {n_req} requests")

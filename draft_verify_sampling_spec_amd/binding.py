@@ -51,6 +51,8 @@ EXPORTED = (
     "spec_head_workspace_bytes",
     "spec_verify_hidden",
     "spec_verify_hidden_workspace_bytes",
+    "spec_markov_draft",
+    "spec_markov_draft_workspace_bytes",
     "spec_verify_free",
     "spec_verify_strerror",
     "spec_verify_chunks",
@@ -92,6 +94,11 @@ def _declare(lib):
     lib.spec_verify_hidden.restype = _i
     lib.spec_verify_hidden_workspace_bytes.argtypes = [_i, _i, _i]
     lib.spec_verify_hidden_workspace_bytes.restype = ctypes.c_size_t
+    lib.spec_markov_draft.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
+                                      ctypes.c_size_t, _vp]
+    lib.spec_markov_draft.restype = _i
+    lib.spec_markov_draft_workspace_bytes.argtypes = [_i, _i]
+    lib.spec_markov_draft_workspace_bytes.restype = ctypes.c_size_t
     lib.spec_budget_schedule.argtypes = [_vp, _i, _i, _i, ctypes.c_float, _vp, _vp]
     lib.spec_budget_schedule.restype = _i
     lib.spec_verify_timing.argtypes = [_vp, _i]
@@ -438,3 +445,57 @@ class HiddenVerify:
                                 self.workspace.numel(), s)
         _check(rc, "spec_verify_hidden")
         return out_tok, out_n, out_p, out_q, status
+
+
+def spec_markov_draft_workspace_bytes(B: int, V: int) -> int:
+    return int(load().spec_markov_draft_workspace_bytes(int(B), int(V)))
+
+
+def spec_markov_draft(base_logits, markov_a, markov_b, prev_tokens, B, K, r, V, out_logits,
+                      out_tokens, out_status, workspace, workspace_bytes, stream) -> int:
+    return load().spec_markov_draft(base_logits, markov_a, markov_b, prev_tokens, B, K, r, V,
+                                    out_logits, out_tokens, out_status, workspace,
+                                    ctypes.c_size_t(workspace_bytes), stream)
+
+
+class MarkovDraft:
+    """Drafted blocks through the low-rank Markov head, for one batch shape
+    (B, K, V) on one device. Holds the library's workspace (torch-allocated)
+    across calls; outputs are fresh tensors per call unless given."""
+
+    def __init__(self, device, B: int, K: int, V: int):
+        self.device = torch.device(device)
+        self.B, self.K, self.V = int(B), int(K), int(V)
+        nbytes = spec_markov_draft_workspace_bytes(max(self.B, 1), self.V)
+        if nbytes == 0:
+            raise ValueError(f"bad shape B={B} V={V}")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+
+    def run(self, base_logits: torch.Tensor, markov_a: torch.Tensor, markov_b: torch.Tensor,
+            prev_tokens: torch.Tensor, out_logits=None, out_tokens=None, stream=None):
+        """(drafter logits bf16 [B, K, V], drafted tokens int32 [B, K], status int32 [1])."""
+        B, K, V = self.B, self.K, self.V
+        if base_logits.shape != (B, K, V):
+            raise ValueError("base_logits must be [B, K, V]")
+        if markov_a.dim() != 2 or markov_a.shape[0] != V or markov_b.shape != markov_a.shape:
+            raise ValueError("markov_a and markov_b must both be [V, r]")
+        r = int(markov_a.shape[1])
+        for m in (base_logits, markov_a, markov_b):
+            if m.dtype != torch.bfloat16 or not m.is_contiguous() or m.device != self.device:
+                raise ValueError("logits and Markov factors must be contiguous bf16 on the device")
+        if (prev_tokens.dtype != torch.int32 or prev_tokens.shape != (B,)
+                or not prev_tokens.is_contiguous() or prev_tokens.device != self.device):
+            raise ValueError(f"prev_tokens must be a contiguous int32 tensor of shape ({B},)")
+        dev = self.device
+        if out_logits is None:
+            out_logits = torch.empty((B, K, V), dtype=torch.bfloat16, device=dev)
+        if out_tokens is None:
+            out_tokens = torch.empty((B, K), dtype=torch.int32, device=dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        s = stream.cuda_stream if stream is not None else _stream_handle(dev)
+        rc = spec_markov_draft(base_logits.data_ptr(), markov_a.data_ptr(), markov_b.data_ptr(),
+                               prev_tokens.data_ptr(), B, K, r, V, out_logits.data_ptr(),
+                               out_tokens.data_ptr(), status.data_ptr(),
+                               self.workspace.data_ptr(), self.workspace.numel(), s)
+        _check(rc, "spec_markov_draft")
+        return out_logits, out_tokens, status

@@ -2,8 +2,10 @@
 
 ``python -m draft_verify_sampling_spec_amd.build`` (or ``build_library()``)
 compiles ``csrc/spec_verify.hip`` (verification), ``csrc/budget_schedule.hip``
-(the verify-budget scheduler) and ``csrc/head_stats.hip`` (output-head row
-statistics) into ``libspec_verify.so`` next to this file.
+(the verify-budget scheduler), ``csrc/head_stats.hip`` (output-head row
+statistics), ``csrc/verify_hidden.hip`` (verification from hidden states) and
+``csrc/markov_draft.hip`` (the drafter's low-rank Markov head) into
+``libspec_verify.so`` next to this file.
 """
 from __future__ import annotations
 
@@ -17,7 +19,8 @@ ROOT = os.path.dirname(PKG_DIR)
 SRC = os.path.join(PKG_DIR, "csrc", "spec_verify.hip")
 SOURCES = [SRC, os.path.join(PKG_DIR, "csrc", "budget_schedule.hip"),
            os.path.join(PKG_DIR, "csrc", "head_stats.hip"),
-           os.path.join(PKG_DIR, "csrc", "verify_hidden.hip")]
+           os.path.join(PKG_DIR, "csrc", "verify_hidden.hip"),
+           os.path.join(PKG_DIR, "csrc", "markov_draft.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libspec_verify.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)

@@ -308,6 +308,48 @@ int spec_verify_hidden(const void* target_hidden, const void* draft_hidden, cons
  * (B, K, V); 0 on bad arguments. Host only. */
 size_t spec_verify_hidden_workspace_bytes(int B, int K, int V);
 
+/*
+ * spec_markov_draft -- the drafter's low-rank Markov head over a block of K
+ * drafted positions ("Speculative decoding becomes standard: DSpark and
+ * multi-token drafters", section "What DSpark adds", paragraph 1: a parallel
+ * backbone proposes the block and a rank-256 Markov module models the
+ * dependencies between its positions; "DSpark" (finds page): the Markov head
+ * uses only the previous token and a low-rank matrix). For i = 0..K-1 in
+ * order: z_i = base_i + A[x_{i-1}] Bm^T, the bias an fp32 sum of exact bf16
+ * products, the sum formed in fp32 and rounded once to bf16 (to nearest,
+ * ties to even) and stored; x_i = the first (lowest index) argmax of the
+ * stored row; x_{-1} = prev_tokens. The stored rows are drafter logits a
+ * verify step can read. Stream-ordered, no host sync; 1 + 2K launches.
+ *   base_logits  bf16 [B, K, V] row-major (device, 16-byte aligned): the
+ *                backbone's logits.
+ *   markov_a     bf16 [V, r] (device, 16-byte aligned): the previous token's
+ *                factor.
+ *   markov_b     bf16 [V, r] (device, 16-byte aligned): the vocabulary factor.
+ *   prev_tokens  int32 [B] (device): the last token of each sequence.
+ *   B, K, r, V   requests (0..SV_MAX_BATCH; 0 is a no-op), positions
+ *                (0..SV_MAX_K; 0 is a no-op), rank (>= 8, a multiple of 8),
+ *                vocabulary (1..SV_MAX_VOCAB).
+ *   out_logits   bf16 [B, K, V] (device, 16-byte aligned, not base_logits).
+ *   out_tokens   int32 [B, K] (device): the drafted tokens.
+ *   out_status   int32 [1] (device) or NULL: SV_FLAG_BAD_TOKEN if a previous
+ *                token is outside [0, V) (written, not accumulated); that
+ *                request's outputs are undefined.
+ *   workspace    device scratch of at least
+ *                spec_markov_draft_workspace_bytes(B, V) bytes, 256-byte
+ *                aligned, caller-owned; calls sharing it must not overlap.
+ *                Most of it is one fp32 bias row per request (4 B V bytes).
+ * Errors (nothing enqueued): SV_ERR_ARG, SV_ERR_NULL, SV_ERR_ALIGN;
+ * SV_ERR_HIP if a launch fails.
+ */
+int spec_markov_draft(const void* base_logits, const void* markov_a, const void* markov_b,
+                      const int32_t* prev_tokens, int B, int K, int r, int V, void* out_logits,
+                      int32_t* out_tokens, int32_t* out_status, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* spec_markov_draft_workspace_bytes -- scratch spec_markov_draft needs for
+ * (B, V); 0 on bad arguments. Host only. */
+size_t spec_markov_draft_workspace_bytes(int B, int V);
+
 /* spec_verify_free -- release the context (NULL-safe, idempotent on NULL).
  * Waits for the device before freeing the workspace. */
 void spec_verify_free(spec_verify_ctx* ctx);

@@ -18,7 +18,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(spec_(?:verify|budget|head)_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(spec_(?:verify|budget|head|markov)_[a-z_]+)\s*\(", text)))
 
 
 def _declared_constants():
@@ -249,3 +249,48 @@ def test_verify_hidden_workspace_size():
     n = sb.spec_verify_hidden_workspace_bytes(512, 8, 151936)
     # Dominated by the fp32 logits of two draw rows per request.
     assert 8 * 512 * 151936 <= n < 8 * 512 * 151936 + (8 << 20)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), _VALID),
+    (dict(B=-1), sb.SV_ERR_ARG),
+    (dict(B=sb.SV_MAX_BATCH + 1), sb.SV_ERR_ARG),
+    (dict(K=sb.SV_MAX_K + 1), sb.SV_ERR_ARG),
+    (dict(r=4), sb.SV_ERR_ARG),
+    (dict(r=260), sb.SV_ERR_ARG),
+    (dict(V=0), sb.SV_ERR_ARG),
+    (dict(V=sb.SV_MAX_VOCAB + 1), sb.SV_ERR_ARG),
+    (dict(base=None), sb.SV_ERR_NULL),
+    (dict(a=None), sb.SV_ERR_NULL),
+    (dict(prev=None), sb.SV_ERR_NULL),
+    (dict(ws=None), sb.SV_ERR_NULL),
+    (dict(base=0x1008), sb.SV_ERR_ALIGN),
+    (dict(out=0x7004), sb.SV_ERR_ALIGN),
+    (dict(ws=0x4010), sb.SV_ERR_ALIGN),
+    (dict(out=0x1000), sb.SV_ERR_ARG),                 # the output may not be the input
+    (dict(ws_bytes=4096), sb.SV_ERR_ARG),
+    (dict(B=0, base=None, a=None, b=None, prev=None, out=None, tok=None, ws=None), sb.SV_OK),
+    (dict(K=0, base=None, a=None, b=None, prev=None, out=None, tok=None, ws=None), sb.SV_OK),
+])
+def test_markov_draft_argument_checks(kw, code):
+    """Host-side checks of spec_markov_draft (they return before any launch)."""
+    args = dict(base=0x1000, a=0x2000, b=0x3000, prev=0x5000, B=8, K=4, r=256, V=1000,
+                out=0x7000, tok=0x8000, ws=0x4000, ws_bytes=0)
+    args.update(kw)
+    if code == _VALID:
+        # Valid arguments: only the workspace size check (too small here)
+        # stands between them and a launch.
+        code = sb.SV_ERR_ARG
+    rc = sb.spec_markov_draft(args["base"], args["a"], args["b"], args["prev"], args["B"],
+                              args["K"], args["r"], args["V"], args["out"], args["tok"], None,
+                              args["ws"], args["ws_bytes"] if "ws_bytes" in kw else 0, None)
+    assert rc == code
+
+
+def test_markov_draft_workspace_size():
+    assert sb.spec_markov_draft_workspace_bytes(0, 100) == 0
+    assert sb.spec_markov_draft_workspace_bytes(4, 0) == 0
+    assert sb.spec_markov_draft_workspace_bytes(4, sb.SV_MAX_VOCAB + 1) == 0
+    n = sb.spec_markov_draft_workspace_bytes(512, 151936)
+    # Dominated by one fp32 bias row per request.
+    assert 4 * 512 * 151936 <= n < 4 * 512 * 151936 + (1 << 16)
