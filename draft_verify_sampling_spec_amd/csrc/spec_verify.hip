@@ -19,8 +19,9 @@
 //    workgroups; workgroup w takes units w, w + G, w + 2G, ... (G = grid size
 //    >= C, so two units of one workgroup never share a team). One workgroup
 //    of 16 waves per CU. Waves 1-15 stream data: 16-byte loads of a unit into
-//    registers, reduced per wave to the max and sum of 2^((z - max) log2(e)/T)
-//    (sampled) or (max, lowest index) (greedy), posted to LDS; the next
+//    registers, reduced per wave to the scaled max s = max(z) c and the sum
+//    of 2^(z c - s), c = log2(e)/T (sampled; one fused multiply-add and an
+//    exp2 per element), or (max, lowest index) (greedy), posted to LDS; the next
 //    unit's loads go out group by group as the reduction consumes the
 //    registers. They never wait on another workgroup. Wave 0 is the control
 //    wave: it plans the units a few rounds ahead, merges the waves'
@@ -89,8 +90,9 @@ constexpr int TW_DEC = 2;       // 64-bit decision: (epoch << 32) | accepted (wo
 
 // Unit record: 4 64-bit words.
 //   sampled: word f = (value bits << 32) | epoch for the fp32 values
-//            R_MT max of z_t, R_MD max of z_d, R_ST sum of 2^((z_t - M_t) c),
-//            R_SD likewise
+//            R_MT the scaled maximum s_t = max(z_t) c (c = log2(e) / T,
+//            rounded once), R_MD likewise for z_d, R_ST the sum of
+//            2^(z_t c - s_t), R_SD likewise
 //   greedy:  word R_MT = (max bits << 32) | epoch, word R_MD = (lowest index
 //            of the max << 32) | epoch
 constexpr int kRecWords = 4;
@@ -248,8 +250,8 @@ struct Shared {
     int pl_kind[kPlanSlots];
     int pl_u[kPlanSlots], pl_b[kPlanSlots];      // unit and its request
     // Data wave -> control wave: a round's per-wave results, in slot
-    // round % kMbox. Sampled: (max, sum of 2^((z - max) c)) of the target and
-    // drafter parts; greedy: (max, lowest index of the max).
+    // round % kMbox. Sampled: (scaled max s, sum of 2^(z c - s)) of the
+    // target and drafter parts; greedy: (max, lowest index of the max).
     float st_mt[kMbox][kDataWaves];
     float st_md[kMbox][kDataWaves];
     double st_st[kMbox][kDataWaves];
@@ -485,12 +487,12 @@ __device__ void poll_wait(const Params& P, Shared& sh, int tr, TeamPoll& pl) {
 // Team-wide normalisers (identical in every workgroup that computes them:
 // same inputs, same lanes, same reduction order).
 struct TeamStats {
-    float mt, md;      // max of the target / drafter row
-    double st, sd;     // sum of 2^((z - max) c) over the row
+    float mt, md;      // scaled maximum of the target / drafter row, max(z) c
+    double st, sd;     // sum of 2^(z c - scaled maximum) over the row
 };
 
-// Merge complete sampled records: M = max of chunk maxima,
-// S = sum of S_c 2^((M_c - M) c).
+// Merge complete sampled records: M = max of the chunks' scaled maxima,
+// S = sum of S_c 2^(M_c - M).
 __device__ TeamStats team_stats(const Params& P, const TeamPoll& pl) {
     const int lane = threadIdx.x & 63;
     const int C = P.C;
@@ -508,8 +510,8 @@ __device__ TeamStats team_stats(const Params& P, const TeamPoll& pl) {
     md = wave_max(md);
     double st = 0.0, sd = 0.0;
     auto add = [&](float m1, float m2, float s1, float s2) {
-        if (s1 > 0.0f) st += (double)s1 * exp2(((double)m1 - (double)mt) * P.c64);
-        if (s2 > 0.0f) sd += (double)s2 * exp2(((double)m2 - (double)md) * P.c64);
+        if (s1 > 0.0f) st += (double)s1 * exp2((double)m1 - (double)mt);
+        if (s2 > 0.0f) sd += (double)s2 * exp2((double)m2 - (double)md);
     };
     if (lane < C) add(tag_val(pl.w[R_MT]), tag_val(pl.w[R_MD]), tag_val(pl.w[R_ST]), tag_val(pl.w[R_SD]));
     for (int cc = lane + 64; cc < C; cc += 64) {
@@ -695,9 +697,10 @@ __device__ __forceinline__ void control_unit(const Params& P, Shared& sh, const 
         order();
         if (lane == 0) lds_put(&sh.st_done[slot], r + 1);
         const float Mt = wave_max(mt), Md = wave_max(md);
-        // Rescale each wave's sum from its own maximum to the chunk maximum.
-        if (a > 0.0) a *= (double)fast_exp2((mt - Mt) * P.c32);
-        if (d > 0.0) d *= (double)fast_exp2((md - Md) * P.c32);
+        // Rescale each wave's sum from its own maximum to the chunk maximum
+        // (both scaled by c).
+        if (a > 0.0) a *= (double)fast_exp2(mt - Mt);
+        if (d > 0.0) d *= (double)fast_exp2(md - Md);
         const double St = wave_sum(a), Sd = wave_sum(d);
         if (lane == 0) {
             st64(rec + R_MT, tagged(Mt, ep));
@@ -747,8 +750,10 @@ __device__ __forceinline__ void owed_decide(const Params& P, const Owed& o, cons
     const bool valid = o.x >= 0 && o.x < P.V;
     double px = 0.0, qx = 0.0;
     if (valid) {
-        px = exp2(((double)o.zt - (double)ts.mt) * P.c64) / ts.st;
-        qx = exp2(((double)o.zd - (double)ts.md) * P.c64) / ts.sd;
+        // z c exactly (a product of two fp32 values fits fp64), minus the
+        // scaled maximum the row's sum was taken under.
+        px = exp2((double)o.zt * (double)P.c32 - (double)ts.mt) / ts.st;
+        qx = exp2((double)o.zd * (double)P.c32 - (double)ts.md) / ts.sd;
     }
     const uint4 rw = philox4x32_10((uint32_t)(P.bbase + u.b), (uint32_t)u.i, 0u, 0u, P.key0, P.key1);
     const bool accept = word_to_uniform(rw.x) * qx < px;
@@ -986,14 +991,17 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
             UnitRows<E> nw;
             if (more) nw = unit_rows<E>(P, nxt);
             const bool do_t = mt != -INFINITY, do_d = cur.has_d && md != -INFINITY;
+            // Maxima in scaled units (s = m c, rounded once); each term is
+            // 2^(z c - s), one fused multiply-add and an exp2.
+            const float smt = mt * cs, smd = md * cs;
             float lt = 0.0f, ld = 0.0f;
             #pragma unroll
             for (int j = 0; j < kG; ++j) {
                 float e[W], f[W];
                 #pragma unroll
                 for (int kk = 0; kk < W; ++kk) {
-                    e[kk] = do_t ? fast_exp2((Elem<E>::at(gt[j], kk) - mt) * cs) : 0.0f;
-                    f[kk] = do_d ? fast_exp2((Elem<E>::at(gd[j], kk) - md) * cs) : 0.0f;
+                    e[kk] = do_t ? fast_exp2(__builtin_fmaf(Elem<E>::at(gt[j], kk), cs, -smt)) : 0.0f;
+                    f[kk] = do_d ? fast_exp2(__builtin_fmaf(Elem<E>::at(gd[j], kk), cs, -smd)) : 0.0f;
                 }
                 if (more) load_pair<E, kVec>(nw, dt, j, gt[j], gd[j]);
                 #pragma unroll
@@ -1009,8 +1017,8 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
             }
             post_a = wave_sum((double)lt);
             post_b = wave_sum((double)ld);
-            post_mt = mt;
-            post_md = md;
+            post_mt = smt;
+            post_md = smd;
         }
         if (lane == 0) {
             if (r >= kMbox) lds_wait(P, sh, &sh.st_done[slot], r - kMbox + 1);
@@ -1106,7 +1114,7 @@ __device__ void p_chunk(const Params& P, const TeamPoll& pl, const TeamStats& ts
     auto pmass = [&](int cc) -> double {
         const float s1 = tag_val(cc == lane ? pl.w[R_ST] : ld64(rec + cc * kRecWords + R_ST));
         const float m1 = tag_val(cc == lane ? pl.w[R_MT] : ld64(rec + cc * kRecWords + R_MT));
-        return s1 > 0.0f ? (double)s1 * exp2(((double)m1 - (double)ts.mt) * P.c64) * inv : 0.0;
+        return s1 > 0.0f ? (double)s1 * exp2((double)m1 - (double)ts.mt) * inv : 0.0;
     };
     double total = 0.0;
     for (int cc = lane; cc < C; cc += 64) total += pmass(cc);
@@ -1252,10 +1260,12 @@ void draw_kernel(Params P) {
     __syncthreads();
     const float mt = dsh.mt, md = dsh.md, ist = dsh.ist, isd = dsh.isd;
     const float c = P.c32;
+    // p = 2^(z c - s_t) / S_t and q likewise, with the scaled maxima the
+    // sums were taken under.
     auto mass = [&](const uint4& t, const uint4& q, int kk, bool res) -> float {
-        const float pv = fast_exp2((Elem<E>::at(t, kk) - mt) * c) * ist;
+        const float pv = fast_exp2(__builtin_fmaf(Elem<E>::at(t, kk), c, -mt)) * ist;
         if (!res) return pv;
-        return fmaxf(0.0f, pv - fast_exp2((Elem<E>::at(q, kk) - md) * c) * isd);
+        return fmaxf(0.0f, pv - fast_exp2(__builtin_fmaf(Elem<E>::at(q, kk), c, -md)) * isd);
     };
     // At most two rounds: the residual, then p_j if the residual had no mass.
     for (int round = 0; round < 2; ++round) {

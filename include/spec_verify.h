@@ -117,7 +117,10 @@ int spec_verify_init(spec_verify_ctx** out, int device, int max_batch, int max_k
  *   budgets           int32 [B] verify budgets k_b, 0 <= k_b <= K (device).
  *   B, K              batch size (0..max_batch; 0 is a no-op) and block
  *                     width (0..max_k).
- *   temperature       0 = greedy; > 0 = sampled; must be finite.
+ *   temperature       0 = greedy; > 0 = sampled; must be finite. Sampled
+ *                     rows are reduced with c = log2(e) / T in fp32 and the
+ *                     scaled maximum max(z) c, so |z| c must stay inside the
+ *                     fp32 range (for logits below 1e4 in magnitude: T >= 1e-30).
  *   seed              Philox key of this call.
  *   out_tokens        int32 [B, K+1]: x_0..x_{j-1}, then the drawn token,
  *                     then -1 padding (device).
