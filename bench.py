@@ -13,7 +13,10 @@ on a bounded sample of the same workload; and, on the same batch shape, the
 verify-budget scheduler (per call, beside its oracle), the fused output
 head (TFLOP/s against the 2.5 PFLOP/s dense bf16 peak, beside its oracle), a
 whole verify step from hidden states through that head, and the drafter's
-low-rank Markov head over a drafted block (each per call, beside its oracle).
+low-rank Markov head over a drafted block (each per call, beside its oracle);
+the other synthetic workloads (Qwen3- and Gemma-shaped vocabularies, the
+ragged batch) and, as context, a plain read-only reduction over the same
+logits.
 
   python bench.py [--steps K] [--warmup W] [--warmup-settle S] [--workload heavy]
                   [--no-cpu-baseline] [--verify-only]
@@ -323,6 +326,105 @@ def bench_markov(B, K, V, r, steps, seed=5):
     }
 
 
+def bench_workloads(steps=50, settle_s=0.1):
+    """The other synthetic workloads at one GPU, each verified back to back
+    with a fresh Philox seed per step: the Qwen3-4B-shaped batch (fp32) at
+    T = 0 and T = 1, the ragged moderate-load batch and the Gemma-shaped
+    vocabulary (bf16). Distinct input sets (other data seeds) rotate from
+    step to step, more than 512 MB in all, so no step finds its logits in the
+    last-level cache. Per workload: step time (HIP events around each step),
+    verified draft tokens/s, the path's algorithmic GB/s, and the streaming
+    pass's roofline from the library's per-pass events."""
+    import torch
+    from draft_verify_sampling_spec_amd import SpecVerify
+    from workloads import make_inputs, philox_seed
+    dev = torch.device("cuda:0")
+    out = {}
+    for name, T_over, nsets in (("qwen3", 0.0, 12), ("qwen3", 1.0, 12), ("ragged", None, 3),
+                                ("gemma", None, 2)):
+        widx = WORKLOAD_INDEX[name]
+        sets = [make_inputs(name, device=dev, seed=100 * widx + j) for j in range(nsets)]
+        T = sets[0]["temperature"] if T_over is None else T_over
+        greedy = T == 0.0
+        B, K1, V = sets[0]["target"].shape
+        K = K1 - 1
+        elem = sets[0]["target"].element_size()
+        sv = SpecVerify(dev, max_batch=B, max_k=K, vocab=V, dtype=sets[0]["target"].dtype)
+        out_t = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+        out_n = torch.empty(B, dtype=torch.int32, device=dev)
+        args = [(x["target"], None if greedy else x["draft"], x["tokens"], x["budgets"]) for x in sets]
+        alg = [algorithmic_bytes(x["budgets"].cpu().tolist(), K, V, elem, greedy)[0] for x in sets]
+        ver = [int(x["budgets"].sum().item()) for x in sets]
+        n = 0
+        t0 = time.perf_counter()
+        while n < 20 or time.perf_counter() - t0 < settle_s:
+            a = args[n % nsets]
+            sv.run(a[0], a[1], a[2], a[3], T, philox_seed(widx, n), out_t, out_n, want_probs=False)
+            n += 1
+            if n % 16 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        stream = torch.cuda.current_stream(dev)
+        for s_, (e0, e1) in enumerate(ev):
+            a = args[s_ % nsets]
+            e0.record(stream)
+            sv.run(a[0], a[1], a[2], a[3], T, philox_seed(widx, 1_000_000 + s_), out_t, out_n,
+                   want_probs=False)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        sv.timing(True)
+        for s_ in range(steps):
+            a = args[s_ % nsets]
+            sv.run(a[0], a[1], a[2], a[3], T, philox_seed(widx, 2_000_000 + s_), out_t, out_n,
+                   want_probs=False)
+        counts, pass_ms = sv.pass_times()
+        sv.timing(False)
+        if sv.status() != 0:
+            raise RuntimeError(f"device status flags set on workload {name}")
+        ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        mean_ms = sum(ms) / len(ms)
+        mean_alg = sum(alg[s_ % nsets] for s_ in range(steps)) / steps
+        mean_ver = sum(ver[s_ % nsets] for s_ in range(steps)) / steps
+        stream_ms = pass_ms[0] / max(counts[0], 1)
+        sv.close()
+        out[f"{name} T={T:g}"] = {
+            "config": sets[0]["workload"].summary,
+            "input_sets": nsets,
+            "ms_per_step": {"mean": mean_ms, "median": ms[len(ms) // 2],
+                            "p5": ms[int(0.05 * (len(ms) - 1))], "p95": ms[int(0.95 * (len(ms) - 1))]},
+            "verified_draft_tokens_per_s": mean_ver / (mean_ms * 1e-3),
+            "algorithmic_bytes_per_step": mean_alg,
+            "path_gbs": mean_alg / (mean_ms * 1e-3) / 1e9,
+            "stream_pass_ms": stream_ms,
+            "stream_pass_frac_of_peak": mean_alg / (stream_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        }
+        del sets, args
+        torch.cuda.empty_cache()
+    return out
+
+
+def read_ceiling(t, d, reps=10):
+    """Context: a plain read-only streaming reduction (torch's sum in fp32)
+    over the same logit buffers, whole tensors, as the achievable read rate."""
+    import torch
+    for _ in range(2):
+        t.sum(dtype=torch.float32)
+        d.sum(dtype=torch.float32)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        t.sum(dtype=torch.float32)
+        d.sum(dtype=torch.float32)
+    b.record()
+    torch.cuda.synchronize()
+    nbytes = (t.numel() * t.element_size() + d.numel() * d.element_size()) * reps
+    return {"gbs": nbytes / (a.elapsed_time(b) * 1e-3) / 1e9, "bytes_per_pass": nbytes // reps,
+            "kernel": "torch sum (fp32 accumulation) over the target and drafter logits"}
+
+
 def copy_probe(gib):
     import torch
     n = int(gib * (1 << 30))
@@ -419,10 +521,13 @@ def main():
     # above because the event markers add a little time between the passes.
     log(f"[bench] timing {args.steps} steps per pass")
     sv.timing(True)
+    acc_sum = torch.zeros((), dtype=torch.int64, device=dev)
     for s in range(args.steps):
         sv.run(t, d, x, k, T, philox_seed(widx, 1_000_000 + s), out_t, out_n,
                want_probs=False)
+        acc_sum += out_n.sum()
     pass_counts, pass_ms = sv.pass_times()
+    accepted_per_step = float(acc_sum.item()) / args.steps
     sv.timing(False)
     kernel_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     kernel_ms.sort()
@@ -459,7 +564,10 @@ def main():
             "verified_draft_tokens_per_step": verified_per_step,
             "logit_rows_per_step": rows,
             "accepted_last_step": int(accepted.item()),
+            "accepted_per_step_mean": accepted_per_step,
         },
+        "accepted_draft_tokens_per_s": accepted_per_step / (ms_per_step * 1e-3),
+        "emitted_tokens_per_s": (accepted_per_step + B) / (ms_per_step * 1e-3),
         "hbm_gbs": path_gbs,
         "hbm_frac_of_peak": path_gbs / HBM_PEAK_GBS,
         "kernel_ms": {"mean": mean_kernel_ms, "median": kernel_ms[len(kernel_ms) // 2],
@@ -491,6 +599,11 @@ def main():
             result["hidden"] = bench_hidden(B, K, 2560, V, min(args.steps, 10), T)
             log("[bench] Markov head draft")
             result["markov"] = bench_markov(B, K, V, 256, min(args.steps, 10))
+    if not greedy and not args.verify_only and args.workload == "heavy":
+        log("[bench] read ceiling")
+        result["read_ceiling"] = read_ceiling(t, d)
+        log("[bench] other workloads")
+        result["workloads"] = bench_workloads()
     if not args.no_cpu_baseline and not greedy and args.workload == "heavy":
         n_req = min(args.cpu_requests, B)
         log(f"[bench] cpu baseline: oracle on {n_req} requests")
