@@ -115,6 +115,9 @@ struct Params {
     unsigned* result;              // [B*(K+1)]: greedy: argmax of the team's row
     unsigned* req_count;           // [B][kReqStride]: greedy: teams completed
     unsigned* status;              // 1 word
+    double* dmass;                 // draw pass split over workgroups: block masses [requests][C * kBlocks]
+    unsigned* dcnt;                // draw pass split: slices finished per request, kReqStride apart
+    int dsplit;                    // workgroups per request in the draw pass
     int B, K, V;
     int bbase;                     // index of request 0 of this launch in the caller's batch
     int C;                         // chunks per row
@@ -1146,7 +1149,7 @@ __device__ void p_chunk(const Params& P, const TeamPoll& pl, const TeamStats& ts
 constexpr int kDrawWaves = 8;                  // wave 0: control; waves 1-7: data
 constexpr int kDrawThreads = kDrawWaves * 64;
 constexpr int kDrawDataWaves = kDrawWaves - 1;
-constexpr int kDrawSlots = 6;                  // blocks in flight per data wave
+constexpr int kDrawSlots = 5;                  // blocks in flight per data wave
 constexpr int kDrawNone = 0, kDrawResidual = 1, kDrawP = 2;
 
 // Draw pass state, written by wave 0 between barriers.
@@ -1156,6 +1159,7 @@ struct DrawShared {
     int x0, x1;        // block range streamed
     int star;          // block holding the threshold, from x0 (-1: none)
     int done;          // star found
+    int last;          // this workgroup finished a request's masses last
     int y;             // drawn token
     double u;          // sampling uniform of position j
     double thr;        // threshold, as mass from block x0's start (then from block star's)
@@ -1172,8 +1176,12 @@ void draw_kernel(Params P) {
     constexpr int BE = 64 * W;                           // elements per block
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // Requests in reverse order: the streaming pass read the last requests'
-    // rows last, so they are the likeliest to still be cached.
-    const int b = P.B - 1 - (int)blockIdx.x;
+    // rows last, so they are the likeliest to still be cached. With a split
+    // (small batches), workgroup sl of a request takes the sl-th of dsplit
+    // slices of its blocks; the slices of one request are B workgroups apart.
+    const int S = P.dsplit;
+    const int b = P.B - 1 - (int)(blockIdx.x % (unsigned)P.B);
+    const int sl = (int)(blockIdx.x / (unsigned)P.B);
     const int K = P.K, V = P.V;
     const int NB = (V + BE - 1) / BE;                    // blocks per row
     const unsigned ep = P.epoch;
@@ -1197,6 +1205,7 @@ void draw_kernel(Params P) {
             dsh.k = k;
             dsh.mode = j < k ? kDrawResidual : kDrawP;
             dsh.done = 0;
+            dsh.last = 0;
             dsh.y = 0;
         }
     }
@@ -1223,9 +1232,17 @@ void draw_kernel(Params P) {
             if (x < x1) issue(x, res, gt[s], gd[s]);
         }
     };
+    // This workgroup's slice of a block range in the first round.
+    auto slice = [&](int x0, int x1, int& a0, int& a1) __attribute__((always_inline)) {
+        const int n = x1 - x0;
+        a0 = x0 + (int)(((long long)sl * n) / S);
+        a1 = x0 + (int)(((long long)(sl + 1) * n) / S);
+    };
     bool pre = false;
     if (dsh.mode == kDrawResidual && wave > 0) {
-        preload(0, NB, true);
+        int a0, a1;
+        slice(0, NB, a0, a1);
+        preload(a0, a1, true);
         pre = true;
     }
     if (wave == 0) {
@@ -1268,26 +1285,57 @@ void draw_kernel(Params P) {
         return fmaxf(0.0f, pv - fast_exp2(__builtin_fmaf(Elem<E>::at(q, kk), c, -md)) * isd);
     };
     // At most two rounds: the residual, then p_j if the residual had no mass.
+    // Only the first is split over workgroups; the fallback runs in the
+    // workgroup that finished the first round last.
     for (int round = 0; round < 2; ++round) {
         const int mode = dsh.mode;
         if (mode == kDrawNone) break;
         const bool res = mode == kDrawResidual;
         const int x0 = dsh.x0, x1 = dsh.x1;
+        const bool split = round == 0 && S > 1;
+        int a0 = x0, a1 = x1;
+        if (split) slice(x0, x1, a0, a1);
+        double* gm = P.dmass + (size_t)b * (size_t)(P.C * kBlocks);
         if (wave > 0) {
-            if (!(pre && round == 0)) preload(x0, x1, res);
-            for (int xr = x0 + dw; xr < x1; xr += stride) {
+            if (!(pre && round == 0)) preload(a0, a1, res);
+            for (int xr = a0 + dw; xr < a1; xr += stride) {
                 #pragma unroll
                 for (int s = 0; s < kDrawSlots; ++s) {
                     const int x = xr + s * kDrawDataWaves;
-                    if (x < x1) {
+                    if (x < a1) {
                         float sg = 0.0f;
                         #pragma unroll
                         for (int kk = 0; kk < W; ++kk) sg += mass(gt[s], gd[s], kk, res);
                         const double ws = wave_sum((double)sg);
-                        if (lane == 0) blk[x - x0] = ws;
-                        if (x + stride < x1) issue(x + stride, res, gt[s], gd[s]);
+                        if (lane == 0) {
+                            blk[x - x0] = ws;
+                            if (split) {
+                                st64(reinterpret_cast<unsigned long long*>(gm + (x - x0)),
+                                     (unsigned long long)__double_as_longlong(ws));
+                            }
+                        }
+                        if (x + stride < a1) issue(x + stride, res, gt[s], gd[s]);
                     }
                 }
+            }
+            // The published masses are complete before the count below.
+            if (split) drain();
+        }
+        if (split) {
+            __syncthreads();
+            if (tid == 0) {
+                const unsigned old = add32(&P.dcnt[(size_t)b * kReqStride], 1u);
+                const int last = old == (unsigned)(S - 1);
+                // Every slice of the request has been counted: reset for the
+                // next call.
+                if (last) st32(&P.dcnt[(size_t)b * kReqStride], 0u);
+                dsh.last = last;
+            }
+            __syncthreads();
+            if (!dsh.last) return;                          // another workgroup finishes
+            for (int x = tid; x < x1 - x0; x += kDrawThreads) {
+                blk[x] = __longlong_as_double(
+                    (long long)ld64(reinterpret_cast<unsigned long long*>(gm + x)));
             }
         }
         __syncthreads();
@@ -1375,7 +1423,8 @@ void draw_kernel(Params P) {
         }
         __syncthreads();
     }
-    if (tid == 0) request_outputs<false>(P, b, k, j, dsh.y);
+    // With no draw (no mass anywhere), the first slice writes the outputs.
+    if (tid == 0 && (dsh.done || dsh.last || sl == 0)) request_outputs<false>(P, b, k, j, dsh.y);
 }
 
 // Philox blocks as the verifier draws them, for checking the generator.
@@ -1424,6 +1473,9 @@ struct spec_verify_ctx {
     unsigned* result;
     unsigned* req_count;
     unsigned* status;
+    double* dmass;                 // split draw pass: block masses of up to split_reqs requests
+    unsigned* dcnt;                // split draw pass: slice counters, kReqStride apart
+    int split_reqs;                // requests a split draw pass can hold
     unsigned calls;
     // Per-pass timing (off unless enabled): recorded event pairs of later
     // runs, and a pool of events to reuse.
@@ -1504,8 +1556,20 @@ int launch(spec_verify_ctx* ctx, Params& p, hipStream_t stream) {
     if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
     timed_end(ctx, t, stream);
     if (!G) {
+        // Two draw workgroups fit a CU. A batch of fewer requests than that
+        // splits each request's blocks over several workgroups (at least 16
+        // blocks each, at most 64 workgroups per request).
+        const int nb = (p.V + 64 * Elem<E>::W - 1) / (64 * Elem<E>::W);
+        int S = 1;
+        if (p.B <= ctx->split_reqs) {
+            S = (2 * ctx->cus) / p.B;
+            S = S < 1 ? 1 : (S > 64 ? 64 : S);
+            const int smax = nb / 16 < 1 ? 1 : nb / 16;
+            S = S > smax ? smax : S;
+        }
+        p.dsplit = S;
         t = timed_begin(ctx, 1, stream);
-        hipLaunchKernelGGL((draw_kernel<E, Vv>), dim3((unsigned)p.B), dim3(kDrawThreads),
+        hipLaunchKernelGGL((draw_kernel<E, Vv>), dim3((unsigned)(p.B * S)), dim3(kDrawThreads),
                            draw_smem_bytes(p.C), stream, p);
         if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
         timed_end(ctx, t, stream);
@@ -1603,7 +1667,13 @@ int spec_verify_init(spec_verify_ctx** out, int device, int max_batch, int max_k
     const size_t team_bytes = round256(teams * kTeamWords * 4);
     const size_t result_bytes = round256(teams * 4);
     const size_t req_bytes = round256((size_t)max_batch * kReqStride * 4);
-    const size_t total = rec_bytes + team_bytes + result_bytes + req_bytes + 256;
+    // The draw pass splits a request over workgroups only when the batch has
+    // fewer requests than the GPU has CUs.
+    c->split_reqs = max_batch < c->cus ? max_batch : c->cus;
+    const size_t dmass_bytes = round256((size_t)c->split_reqs * c->C * kBlocks * 8);
+    const size_t dcnt_bytes = round256((size_t)c->split_reqs * kReqStride * 4);
+    const size_t total = rec_bytes + team_bytes + result_bytes + req_bytes + dmass_bytes +
+                         dcnt_bytes + 256;
     if (rc == SV_OK && hipMalloc(&c->ws, total) != hipSuccess) {
         c->ws = nullptr;
         rc = SV_ERR_NOMEM;
@@ -1619,6 +1689,10 @@ int spec_verify_init(spec_verify_ctx** out, int device, int max_batch, int max_k
         o += result_bytes;
         c->req_count = reinterpret_cast<unsigned*>(w + o);
         o += req_bytes;
+        c->dmass = reinterpret_cast<double*>(w + o);
+        o += dmass_bytes;
+        c->dcnt = reinterpret_cast<unsigned*>(w + o);
+        o += dcnt_bytes;
         c->status = reinterpret_cast<unsigned*>(w + o);
         if (hipMemset(c->ws, 0, total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
             rc = SV_ERR_HIP;
@@ -1664,6 +1738,8 @@ int spec_verify_run(spec_verify_ctx* ctx, const void* target_logits, const void*
     p.result = ctx->result;
     p.req_count = ctx->req_count;
     p.status = ctx->status;
+    p.dmass = ctx->dmass;
+    p.dcnt = ctx->dcnt;
     p.B = B;
     p.K = K;
     p.V = ctx->vocab;
