@@ -3,10 +3,12 @@
 // of the C ABI.
 //
 // The product z = h W^T of bf16 hidden states and the shared head runs on the
-// matrix cores with one of three epilogues: per-row statistics for sampled or
-// greedy verification, or the fp32 logits themselves for a few rows. Every
-// epilogue accumulates each logit in the same order, so the logits written
-// for a row equal, bit for bit, the values its statistics were taken over.
+// matrix cores with one of four epilogues: per-row statistics for sampled or
+// greedy verification, the fp32 logits themselves for a few rows, or the
+// logits added to bf16 rows and stored rounded (the Markov head's transition
+// term on the backbone's logits). Every epilogue accumulates each logit in
+// the same order, so the logits written for a row equal, bit for bit, the
+// values its statistics were taken over.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -46,5 +48,15 @@ int head_stats_launch(const HeadRows& rows, const uint16_t* weight, int r_max,
 // negative are not written). Returns an sv_status code.
 int head_logits_launch(const HeadRows& rows, const uint16_t* weight, int R, int H, int V,
                        float* out, hipStream_t stream);
+
+// Logits of packed rows [0, R) added to bf16 rows: for row r and column v,
+// out[r * row_stride + v] = bf16(base[r * row_stride + v] + z[r, v]), the sum
+// in fp32 and one rounding to nearest even (a row whose map entry is
+// negative has z = 0). The tile is staged in LDS so that global loads and
+// stores are 16 bytes wide when V is a multiple of 8. Returns an sv_status
+// code.
+int head_add_bf16_launch(const HeadRows& rows, const uint16_t* weight, int R, int H, int V,
+                         const uint16_t* base, uint16_t* out, long long row_stride,
+                         hipStream_t stream);
 
 }  // namespace svhead

@@ -49,7 +49,24 @@ constexpr int kLdsRow = kTK + kPad;        // 72 bf16 = 144 bytes per staged row
 
 constexpr int kResidentSlots = 512;        // one resident wave of workgroups: 2 per CU
 
-enum Epi { kEpiGreedy = 0, kEpiSampled = 1, kEpiLogits = 2 };
+enum Epi { kEpiGreedy = 0, kEpiSampled = 1, kEpiLogits = 2, kEpiAddBf16 = 3 };
+
+// Add-and-store epilogue: row r's output row is out + r * stride (bf16), and
+// the value stored there is bf16(base[same place] + logit), one rounding to
+// nearest even.
+struct RowAdd {
+    const uint16_t* base;
+    uint16_t* out;
+    long long stride;
+};
+
+constexpr int kTS = kTN + 8;               // staged output tile row (bf16 elements, 272 bytes)
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0u) return (u >> 16) | 0x0040u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -109,9 +126,10 @@ __global__ __launch_bounds__(kHThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void head_stats_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
                        const int* __restrict__ d_rows, int H, int V,
                        const int32_t* __restrict__ tok, float c, HeadPart* __restrict__ part,
-                       float* __restrict__ out) {
+                       float* __restrict__ out, RowAdd ra) {
     constexpr bool sampled = kEpi == kEpiSampled;
     constexpr bool logits = kEpi == kEpiLogits;
+    constexpr bool addbf = kEpi == kEpiAddBf16;
     __shared__ __align__(16) uint16_t As[kTM][kLdsRow];
     __shared__ __align__(16) uint16_t Bs[kTN][kLdsRow];
     __shared__ int tok_s[kTM];             // statistics: the token; logits: row present
@@ -138,6 +156,7 @@ void head_stats_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
     if (tid < kTM) {
         const bool have = r0 + tid < R;
         if (logits) tok_s[tid] = have && row_ptr(hr, r0 + tid, H) != nullptr;
+        else if (addbf) tok_s[tid] = have;
         else tok_s[tid] = (have && tok) ? tok[r0 + tid] : -1;
         zx_s[tid] = NAN;
     }
@@ -253,6 +272,67 @@ void head_stats_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
             }
             continue;
         }
+        if constexpr (addbf) {
+            // The staged output tile (this instantiation only). The previous
+            // tile's stores from it ended before the barrier that opened
+            // this tile's product.
+            __shared__ __align__(16) uint16_t T[kTM * kTS];
+            // 1. The tile's backbone values into LDS, 16-byte loads: thread
+            //    t takes row t / 2, columns (t % 2) * 64 .. + 64.
+            const int trow = tid >> 1, tc0 = (tid & 1) * 64;
+            const bool rok = tok_s[trow] != 0;
+            const size_t goff = (size_t)(r0 + trow) * (size_t)ra.stride + (size_t)(v0 + tc0);
+            const bool vec = (V & 7) == 0;         // 16-byte aligned rows and columns
+            if (rok) {
+                #pragma unroll
+                for (int q8 = 0; q8 < 8; ++q8) {
+                    const int col = v0 + tc0 + q8 * 8;
+                    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+                    if (vec && col + 8 <= V) {
+                        x = *reinterpret_cast<const uint4*>(ra.base + goff + q8 * 8);
+                    } else if (col < V) {
+                        uint32_t wd[4] = {0u, 0u, 0u, 0u};
+                        for (int e = 0; e < 8 && col + e < V; ++e)
+                            wd[e >> 1] |= (uint32_t)ra.base[goff + q8 * 8 + e] << ((e & 1) * 16);
+                        x = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                    }
+                    *reinterpret_cast<uint4*>(&T[trow * kTS + tc0 + q8 * 8]) = x;
+                }
+            }
+            __syncthreads();
+            // 2. Each lane adds its accumulators in place, one rounding.
+            #pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                #pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int rl = wr + 32 * a + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                    #pragma unroll
+                    for (int b = 0; b < 2; ++b) {
+                        const int cl = wc + 32 * b + (lane & 31);
+                        uint16_t& cell = T[rl * kTS + cl];
+                        const float sum = __uint_as_float((uint32_t)cell << 16) + acc[a][b][i];
+                        cell = (uint16_t)bf16_rne_bits(sum);
+                    }
+                }
+            }
+            __syncthreads();
+            // 3. The tile back out, 16-byte stores.
+            if (rok) {
+                #pragma unroll
+                for (int q8 = 0; q8 < 8; ++q8) {
+                    const int col = v0 + tc0 + q8 * 8;
+                    const uint4 x = *reinterpret_cast<const uint4*>(&T[trow * kTS + tc0 + q8 * 8]);
+                    if (vec && col + 8 <= V) {
+                        *reinterpret_cast<uint4*>(ra.out + goff + q8 * 8) = x;
+                    } else if (col < V) {
+                        const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
+                        for (int e = 0; e < 8 && col + e < V; ++e)
+                            ra.out[goff + q8 * 8 + e] = (uint16_t)(wd[e >> 1] >> ((e & 1) * 16));
+                    }
+                }
+            }
+            continue;
+        }
         // Fold the tile into the lane's running row statistics.
         #pragma unroll
         for (int a = 0; a < 2; ++a) {
@@ -286,7 +366,7 @@ void head_stats_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
         }
     }
 
-    if (logits) return;
+    if (logits || addbf) return;
     // Lanes holding the same rows (same l / 32 half): merge across columns.
     #pragma unroll
     for (int q = 0; q < 32; ++q) {
@@ -400,11 +480,11 @@ int head_stats_launch(const HeadRows& rows, const uint16_t* weight, int r_max,
     if (sampled) {
         hipLaunchKernelGGL(head_stats_kernel<kEpiSampled>, dim3((unsigned)grid),
                            dim3(kHThreads), 0, s, rows, weight, r_max, d_rows, H, V, tokens, c,
-                           part, nullptr);
+                           part, nullptr, RowAdd{});
     } else {
         hipLaunchKernelGGL(head_stats_kernel<kEpiGreedy>, dim3((unsigned)grid),
                            dim3(kHThreads), 0, s, rows, weight, r_max, d_rows, H, V, tokens, c,
-                           part, nullptr);
+                           part, nullptr, RowAdd{});
     }
     if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
     hipLaunchKernelGGL(head_merge_kernel, dim3((unsigned)((r_max + 255) / 256)), dim3(256), 0, s,
@@ -418,7 +498,17 @@ int head_logits_launch(const HeadRows& rows, const uint16_t* weight, int R, int 
     if (R < 1) return SV_OK;
     hipLaunchKernelGGL(head_stats_kernel<kEpiLogits>, dim3((unsigned)items_for(R, V)),
                        dim3(kHThreads), 0, s, rows, weight, R, nullptr, H, V, nullptr, 0.0f,
-                       nullptr, out);
+                       nullptr, out, RowAdd{});
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+int head_add_bf16_launch(const HeadRows& rows, const uint16_t* weight, int R, int H, int V,
+                         const uint16_t* base, uint16_t* out, long long row_stride,
+                         hipStream_t s) {
+    if (R < 1) return SV_OK;
+    hipLaunchKernelGGL(head_stats_kernel<kEpiAddBf16>, dim3((unsigned)items_for(R, V)),
+                       dim3(kHThreads), 0, s, rows, weight, R, nullptr, H, V, nullptr, 0.0f,
+                       nullptr, nullptr, RowAdd{base, out, row_stride});
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

@@ -14,13 +14,16 @@
 //
 // Design, per drafted position i (two stream-ordered launches; positions run
 // in order because x_i feeds position i+1):
-//   1. the matrix cores form bias[b, :] = A[x_{i-1}[b]] Bm^T in fp32: the
-//      output head's product with the previous tokens as its row map, the
-//      rank r as the product's depth;
-//   2. one workgroup per request adds the bias to the backbone row in fp32,
-//      rounds once to bf16 (to nearest, ties to even), stores the row and
-//      takes the first argmax of the stored values, which is x_i and the next
-//      position's row map (two map buffers alternate).
+//   1. the matrix cores form the bias A[x_{i-1}[b]] Bm^T in fp32 -- the
+//      output head's product with the previous tokens as its row map and the
+//      rank r as its depth -- and its epilogue stages each output tile in
+//      LDS: the backbone values come in with 16-byte loads, each bias is
+//      added in fp32 and rounded once to bf16 (to nearest, ties to even), and
+//      the drafter rows go out with 16-byte stores, so the bias never reaches
+//      memory;
+//   2. one workgroup per request reads its stored row back and takes the
+//      first argmax, which is x_i and the next position's row map (two map
+//      buffers alternate).
 // A seed launch checks the given last tokens and writes the first row map.
 
 #include <hip/hip_runtime.h>
@@ -41,7 +44,7 @@ constexpr int kMkGroup = 8;                        // elements per lane per step
 constexpr int kMkUnroll = 2;                       // groups in flight per lane
 
 struct MkLayout {
-    size_t map0, map1, bias, total;
+    size_t map0, map1, total;
 };
 
 size_t mk_up256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -54,9 +57,9 @@ MkLayout mk_layout(int B, int V) {
         o += mk_up256(bytes);
         return at;
     };
+    (void)V;
     L.map0 = take((size_t)B * 4);
     L.map1 = take((size_t)B * 4);
-    L.bias = take((size_t)B * (size_t)V * 4);
     L.total = o;
     return L;
 }
@@ -84,61 +87,42 @@ __device__ __forceinline__ float bf16_value(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest, ties to even (NaN kept quiet).
-__device__ __forceinline__ uint32_t to_bf16_rne(float x) {
-    const uint32_t u = __float_as_uint(x);
-    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0u) return (u >> 16) | 0x0040u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 __device__ __forceinline__ bool mk_better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
 }
 
-// One request row of position i: out = bf16(base + bias), x_i = first argmax
-// of the stored values. kVec: 16-byte loads and stores are legal (V % 8 == 0).
+// The first argmax of one stored request row of position i: x_i, written to
+// the drafted tokens and the next position's row map. kVec: 16-byte loads
+// are legal (V % 8 == 0).
 template <bool kVec>
-__global__ __launch_bounds__(kMkThreads) void mk_add_kernel(
-    const uint16_t* __restrict__ base, const float* __restrict__ bias, int K, int V, int i,
-    uint16_t* __restrict__ out, int32_t* __restrict__ out_tokens, int32_t* __restrict__ next_map) {
+__global__ __launch_bounds__(kMkThreads) void mk_argmax_kernel(
+    const uint16_t* __restrict__ z, int K, int V, int i, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ next_map) {
     __shared__ float wv[kMkThreads / 64];
     __shared__ int wi[kMkThreads / 64];
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t row = (size_t)b * K + i;
-    const uint16_t* src = base + row * (size_t)V;
-    uint16_t* dst = out + row * (size_t)V;
-    const float* bs = bias + (size_t)b * V;
+    const uint16_t* src = z + row * (size_t)V;
     float bv = -INFINITY;
     int bi = INT_MAX;
     constexpr int step = kMkThreads * kMkGroup;
     if (kVec) {
         for (int e0 = tid * kMkGroup; e0 < V; e0 += step * kMkUnroll) {
-            uint4 zb[kMkUnroll];
-            float4 b0[kMkUnroll], b1[kMkUnroll];
+            uint4 g[kMkUnroll];
             #pragma unroll
             for (int u = 0; u < kMkUnroll; ++u) {
                 const int e = e0 + u * step;
-                if (e < V) {
-                    zb[u] = *reinterpret_cast<const uint4*>(src + e);
-                    b0[u] = *reinterpret_cast<const float4*>(bs + e);
-                    b1[u] = *reinterpret_cast<const float4*>(bs + e + 4);
-                }
+                if (e < V) g[u] = *reinterpret_cast<const uint4*>(src + e);
             }
             #pragma unroll
             for (int u = 0; u < kMkUnroll; ++u) {
                 const int e = e0 + u * step;
                 if (e < V) {
-                    const uint32_t w[4] = {zb[u].x, zb[u].y, zb[u].z, zb[u].w};
-                    const float bb[8] = {b0[u].x, b0[u].y, b0[u].z, b0[u].w,
-                                         b1[u].x, b1[u].y, b1[u].z, b1[u].w};
-                    uint32_t o[4];
+                    const uint32_t w[4] = {g[u].x, g[u].y, g[u].z, g[u].w};
                     #pragma unroll
                     for (int k = 0; k < 4; ++k) {
-                        const uint32_t lo = to_bf16_rne(bf16_value(w[k] & 0xFFFFu) + bb[2 * k]);
-                        const uint32_t hi = to_bf16_rne(bf16_value(w[k] >> 16) + bb[2 * k + 1]);
-                        o[k] = lo | (hi << 16);
-                        const float vl = bf16_value(lo), vh = bf16_value(hi);
+                        const float vl = bf16_value(w[k] & 0xFFFFu), vh = bf16_value(w[k] >> 16);
                         if (vl > bv) {              // a lane's elements go up in index order
                             bv = vl;
                             bi = e + 2 * k;
@@ -148,7 +132,6 @@ __global__ __launch_bounds__(kMkThreads) void mk_add_kernel(
                             bi = e + 2 * k + 1;
                         }
                     }
-                    *reinterpret_cast<uint4*>(dst + e) = make_uint4(o[0], o[1], o[2], o[3]);
                 }
             }
         }
@@ -158,9 +141,7 @@ __global__ __launch_bounds__(kMkThreads) void mk_add_kernel(
             for (int k = 0; k < kMkGroup; ++k) {
                 const int e = e0 + k;
                 if (e < V) {
-                    const uint32_t s = to_bf16_rne(bf16_value(src[e]) + bs[e]);
-                    dst[e] = (uint16_t)s;
-                    const float v = bf16_value(s);
+                    const float v = bf16_value(src[e]);
                     if (v > bv) {
                         bv = v;
                         bi = e;
@@ -230,7 +211,6 @@ extern "C" int spec_markov_draft(const void* base_logits, const void* markov_a,
     char* ws = static_cast<char*>(workspace);
     int32_t* map[2] = {reinterpret_cast<int32_t*>(ws + L.map0),
                        reinterpret_cast<int32_t*>(ws + L.map1)};
-    float* bias = reinterpret_cast<float*>(ws + L.bias);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const uint16_t* A = static_cast<const uint16_t*>(markov_a);
     const uint16_t* Bm = static_cast<const uint16_t*>(markov_b);
@@ -244,14 +224,15 @@ extern "C" int spec_markov_draft(const void* base_logits, const void* markov_a,
         // Rows of A indexed by the previous tokens; virtual rows >= V never
         // occur (tokens are checked, argmaxes lie in [0, V)).
         const HeadRows rows{A, nullptr, map[i & 1], V};
-        const int rc = svhead::head_logits_launch(rows, Bm, B, r, V, bias, s);
+        const int rc = svhead::head_add_bf16_launch(rows, Bm, B, r, V, base + (size_t)i * V,
+                                                    out + (size_t)i * V, (long long)K * V, s);
         if (rc != SV_OK) return rc;
         if (V % kMkGroup == 0) {
-            hipLaunchKernelGGL(mk_add_kernel<true>, dim3((unsigned)B), dim3(kMkThreads), 0, s, base,
-                               bias, K, V, i, out, out_tokens, map[(i + 1) & 1]);
+            hipLaunchKernelGGL(mk_argmax_kernel<true>, dim3((unsigned)B), dim3(kMkThreads), 0, s, out,
+                               K, V, i, out_tokens, map[(i + 1) & 1]);
         } else {
-            hipLaunchKernelGGL(mk_add_kernel<false>, dim3((unsigned)B), dim3(kMkThreads), 0, s,
-                               base, bias, K, V, i, out, out_tokens, map[(i + 1) & 1]);
+            hipLaunchKernelGGL(mk_argmax_kernel<false>, dim3((unsigned)B), dim3(kMkThreads), 0, s,
+                               out, K, V, i, out_tokens, map[(i + 1) & 1]);
         }
         if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
     }

@@ -340,7 +340,8 @@ size_t spec_verify_hidden_workspace_bytes(int B, int K, int V);
  *   workspace    device scratch of at least
  *                spec_markov_draft_workspace_bytes(B, V) bytes, 256-byte
  *                aligned, caller-owned; calls sharing it must not overlap.
- *                Most of it is one fp32 bias row per request (4 B V bytes).
+ *                It holds two token maps of B entries (the bias rows never
+ *                reach memory).
  * Errors (nothing enqueued): SV_ERR_ARG, SV_ERR_NULL, SV_ERR_ALIGN;
  * SV_ERR_HIP if a launch fails.
  */

@@ -268,7 +268,7 @@ def test_verify_hidden_workspace_size():
     (dict(out=0x7004), sb.SV_ERR_ALIGN),
     (dict(ws=0x4010), sb.SV_ERR_ALIGN),
     (dict(out=0x1000), sb.SV_ERR_ARG),                 # the output may not be the input
-    (dict(ws_bytes=4096), sb.SV_ERR_ARG),
+    (dict(ws_bytes=100), sb.SV_ERR_ARG),
     (dict(B=0, base=None, a=None, b=None, prev=None, out=None, tok=None, ws=None), sb.SV_OK),
     (dict(K=0, base=None, a=None, b=None, prev=None, out=None, tok=None, ws=None), sb.SV_OK),
 ])
@@ -292,5 +292,5 @@ def test_markov_draft_workspace_size():
     assert sb.spec_markov_draft_workspace_bytes(4, 0) == 0
     assert sb.spec_markov_draft_workspace_bytes(4, sb.SV_MAX_VOCAB + 1) == 0
     n = sb.spec_markov_draft_workspace_bytes(512, 151936)
-    # Dominated by one fp32 bias row per request.
-    assert 4 * 512 * 151936 <= n < 4 * 512 * 151936 + (1 << 16)
+    # Two token maps of B entries each (the bias rows never reach memory).
+    assert 2 * 4 * 512 <= n <= 2 * (4 * 512 + 255)
