@@ -333,35 +333,41 @@ void head_stats_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
             }
             continue;
         }
-        // Fold the tile into the lane's running row statistics.
+        // Fold the tile into the lane's running row statistics, without
+        // branches: columns past V (the last tile only) read as -inf; the
+        // sampled sum is rescaled once per row slot and tile.
+        const bool full = v0 + kTN <= V;
+        const int col0 = v0 + wc + (lane & 31), col1 = col0 + 32;
         #pragma unroll
         for (int a = 0; a < 2; ++a) {
             #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int q = 16 * a + i;
+                float z0 = acc[a][0][i], z1 = acc[a][1][i];
+                if (!full) {
+                    z0 = col0 < V ? z0 : -INFINITY;
+                    z1 = col1 < V ? z1 : -INFINITY;
+                }
+                if (sampled) {
+                    const float mn = fmaxf(rm[q], fmaxf(z0, z1));
+                    const float mr = mn == -INFINITY ? 0.0f : mn;   // all -inf so far: terms stay 0
+                    rx[q] = rx[q] * __builtin_amdgcn_exp2f((rm[q] - mr) * c) +
+                            __builtin_amdgcn_exp2f((z0 - mr) * c) +
+                            __builtin_amdgcn_exp2f((z1 - mr) * c);
+                    rm[q] = mn;
+                } else {
+                    // A lane's columns go up, so the first maximum wins.
+                    const bool b0 = z0 > rm[q];
+                    rm[q] = b0 ? z0 : rm[q];
+                    rx[q] = b0 ? __int_as_float(col0) : rx[q];
+                    const bool b1 = z1 > rm[q];
+                    rm[q] = b1 ? z1 : rm[q];
+                    rx[q] = b1 ? __int_as_float(col1) : rx[q];
+                }
+                // The drafted token's logit: one lane of the row's split.
                 const int rl = wr + 32 * a + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
                 const int x = tok_s[rl];
-                #pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    const int col = v0 + wc + 32 * b + (lane & 31);
-                    if (col < V) {
-                        const float z = acc[a][b][i];
-                        if (col == x) zx_s[rl] = z;
-                        if (sampled) {
-                            if (z > rm[q]) {
-                                rx[q] = rx[q] * __builtin_amdgcn_exp2f((rm[q] - z) * c) + 1.0f;
-                                rm[q] = z;
-                            } else {
-                                rx[q] += __builtin_amdgcn_exp2f((z - rm[q]) * c);
-                            }
-                        } else {
-                            // A lane's columns go up, so the first maximum wins.
-                            const bool better = z > rm[q];
-                            rm[q] = better ? z : rm[q];
-                            rx[q] = better ? __int_as_float(col) : rx[q];
-                        }
-                    }
-                }
+                if (x == col0 || x == col1) zx_s[rl] = x == col0 ? z0 : z1;
             }
         }
     }
