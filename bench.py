@@ -487,6 +487,17 @@ def main():
     alg_bytes, rows = algorithmic_bytes(budgets, K, V, elem, greedy)
     verified_per_step = int(sum(budgets))
 
+    # Everything the timed regions use is set up before the warmup, so that
+    # the first timed step follows the last warmup step with no idle gap.
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for e in starts + ends:
+        e.record(stream)
+    accepted = torch.zeros((), dtype=torch.int64, device=dev)
+    acc_sum = torch.zeros((), dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+
     # Warmup: W steps, continued (untimed) until the GPU has been busy for
     # WARMUP_SETTLE_S -- its clocks ramp over the first tens of milliseconds
     # of sustained load, and a short warmup would time the ramp.
@@ -500,28 +511,30 @@ def main():
             torch.cuda.synchronize()
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream(dev)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    accepted = torch.zeros((), dtype=torch.int64, device=dev)
-    log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
+    # The timed steps: nothing but the verify calls between the two
+    # synchronisations (wall clock).
     t0 = time.perf_counter()
+    for s in range(args.steps):
+        sv.run(t, d, x, k, T, philox_seed(widx, 1_000_000 + s), out_t, out_n,
+               want_probs=False)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    accepted += out_n.sum()
+    # The same steps again with a HIP event pair around each, for the
+    # per-step distribution (the event packets add a little time per step).
+    log(f"[bench] timing {args.steps} steps with per-step events")
     for s in range(args.steps):
         starts[s].record(stream)
         sv.run(t, d, x, k, T, philox_seed(widx, 1_000_000 + s), out_t, out_n,
                want_probs=False)
         ends[s].record(stream)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    accepted += out_n.sum()
-    # Second timed region, same steps: per-pass HIP events that the library
+    # Third timed region, same steps: per-pass HIP events that the library
     # records on this stream around each launch (pass 0: the streaming pass,
-    # the dominant kernel; pass 1: the draw pass). Kept apart from the region
+    # the dominant kernel; pass 1: the draw pass). Kept apart from the regions
     # above because the event markers add a little time between the passes.
     log(f"[bench] timing {args.steps} steps per pass")
     sv.timing(True)
-    acc_sum = torch.zeros((), dtype=torch.int64, device=dev)
     for s in range(args.steps):
         sv.run(t, d, x, k, T, philox_seed(widx, 1_000_000 + s), out_t, out_n,
                want_probs=False)
