@@ -269,6 +269,33 @@ def test_edge_shapes(B, K, V, dtype, budgets, T, masks):
                    tag=f"edge-{B}-{K}-{V}")
 
 
+MAXIMA = [
+    # B, K, V, dtype, budgets: the header's largest K, vocabulary and batch
+    (3, 32, 4099, torch.bfloat16, [32, 17, 0]),
+    (2, 2, 1 << 20, torch.bfloat16, [2, 1]),
+    (2, 2, 1 << 20, torch.float32, [2, 0]),        # 69 chunks per row: more than one wave's lanes
+    (16384, 1, 40, torch.float32, None),           # two launches of 8192 requests
+]
+
+
+@pytest.mark.parametrize("B,K,V,dtype,budgets", MAXIMA)
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_maximum_sizes(B, K, V, dtype, budgets, T):
+    if budgets is None:
+        budgets = [b % (K + 1) for b in range(B)]
+    inp = _edge_inputs(B, K, V, dtype, budgets, seed=B + K + V, ties=(T == 0))
+    inp["temperature"] = T
+    seed = 0x5EED0000 + B + K
+    _log(f"maximum B={B} K={K} V={V} {dtype} T={T}")
+    gpu = _run(inp, seed, temperature=T)
+    # The oracle on every request of the small batches; on the largest batch,
+    # every 41st request and the last ones of both launches.
+    reqs = list(range(B)) if B <= 64 else sorted(set(range(0, B, 41)) | set(range(8187, 8197)) |
+                                                 set(range(B - 5, B)))
+    _assert_parity(inp, seed, gpu, _oracle(inp, seed, requests=reqs, temperature=T),
+                   requests=reqs, temperature=T, tag=f"max-{B}-{K}-{V}")
+
+
 def test_empty_batch_is_a_no_op():
     sv = SpecVerify(DEV, max_batch=4, max_k=2, vocab=64, dtype=torch.float32)
     t = torch.zeros(0, 3, 64, device=DEV)
