@@ -49,14 +49,27 @@ int head_stats_launch(const HeadRows& rows, const uint16_t* weight, int r_max,
 int head_logits_launch(const HeadRows& rows, const uint16_t* weight, int R, int H, int V,
                        float* out, hipStream_t stream);
 
+// One row's first argmax over one vocabulary split of the add-and-store
+// product: the largest stored value and the lowest column holding it
+// (v = -inf, i = INT_MAX: no column of the split holds a value above -inf).
+struct ArgPart {
+    float v;
+    int i;
+};
+
+// Vocabulary splits of head_add_bf16_launch for R rows; split s covers
+// columns below those of split s + 1.
+int add_splits(int R, int V);
+
 // Logits of packed rows [0, R) added to bf16 rows: for row r and column v,
 // out[r * row_stride + v] = bf16(base[r * row_stride + v] + z[r, v]), the sum
 // in fp32 and one rounding to nearest even (a row whose map entry is
 // negative has z = 0). The tile is staged in LDS so that global loads and
-// stores are 16 bytes wide when V is a multiple of 8. Returns an sv_status
-// code.
+// stores are 16 bytes wide when V is a multiple of 8. With arg non-NULL
+// ([add_splits(R, V)][R]), each (split, row) also gets the first argmax of
+// the values stored there. Returns an sv_status code.
 int head_add_bf16_launch(const HeadRows& rows, const uint16_t* weight, int R, int H, int V,
                          const uint16_t* base, uint16_t* out, long long row_stride,
-                         hipStream_t stream);
+                         ArgPart* arg, hipStream_t stream);
 
 }  // namespace svhead

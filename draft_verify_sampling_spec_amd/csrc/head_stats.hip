@@ -58,6 +58,7 @@ struct RowAdd {
     const uint16_t* base;
     uint16_t* out;
     long long stride;
+    svhead::ArgPart* arg;                  // [splits][R] first argmaxes, or NULL
 };
 
 constexpr int kTS = kTN + 8;               // staged output tile row (bf16 elements, 272 bytes)
@@ -214,6 +215,11 @@ void head_stats_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
         rb[0] = pc.b0; rb[1] = pc.b1; rb[2] = pc.b2; rb[3] = pc.b3;
     };
 
+    // Add-and-store: this thread's running first argmax over the values it
+    // stores (its row, its half of every tile's columns, in column order).
+    float am_v = -INFINITY;
+    int am_i = INT_MAX;
+
     for (int t = t0; t < t1; ++t) {
         const int v0 = t * kTN;
         f32x16 acc[2][2];
@@ -316,18 +322,48 @@ void head_stats_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
                 }
             }
             __syncthreads();
-            // 3. The tile back out, 16-byte stores.
+            // 3. The tile back out, 16-byte stores; the first argmax follows
+            //    the stored values in column order (a strictly larger value
+            //    replaces it, so the lowest column wins ties).
             if (rok) {
                 #pragma unroll
                 for (int q8 = 0; q8 < 8; ++q8) {
                     const int col = v0 + tc0 + q8 * 8;
                     const uint4 x = *reinterpret_cast<const uint4*>(&T[trow * kTS + tc0 + q8 * 8]);
+                    const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
                     if (vec && col + 8 <= V) {
                         *reinterpret_cast<uint4*>(ra.out + goff + q8 * 8) = x;
                     } else if (col < V) {
-                        const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
                         for (int e = 0; e < 8 && col + e < V; ++e)
                             ra.out[goff + q8 * 8 + e] = (uint16_t)(wd[e >> 1] >> ((e & 1) * 16));
+                    }
+                    if (ra.arg) {
+                        float f[8];
+                        #pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            f[e] = __uint_as_float((wd[e >> 1] >> ((e & 1) * 16)) << 16);
+                        if (col + 8 <= V) {
+                            // The group's maximum first (NaN never wins); only
+                            // a group that beats the running value is searched
+                            // for its first column holding that maximum.
+                            const float g = fmaxf(fmaxf(fmaxf(f[0], f[1]), fmaxf(f[2], f[3])),
+                                                  fmaxf(fmaxf(f[4], f[5]), fmaxf(f[6], f[7])));
+                            if (g > am_v) {
+                                int e0 = 7;
+                                #pragma unroll
+                                for (int e = 6; e >= 0; --e) e0 = f[e] == g ? e : e0;
+                                am_v = g;
+                                am_i = col + e0;
+                            }
+                        } else {
+                            #pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                if (col + e < V && f[e] > am_v) {
+                                    am_v = f[e];
+                                    am_i = col + e;
+                                }
+                            }
+                        }
                     }
                 }
             }
@@ -372,6 +408,16 @@ void head_stats_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
         }
     }
 
+    if constexpr (addbf) {
+        if (ra.arg) {
+            // A row's two threads (lanes 2m and 2m + 1, the tiles' two column
+            // halves) merge; the first writes the split's entry.
+            merge_arg(am_v, am_i, __shfl_xor(am_v, 1, 64), __shfl_xor(am_i, 1, 64));
+            const int trow = tid >> 1;
+            if ((tid & 1) == 0 && r0 + trow < R)
+                ra.arg[(size_t)split * R + r0 + trow] = svhead::ArgPart{am_v, am_i};
+        }
+    }
     if (logits || addbf) return;
     // Lanes holding the same rows (same l / 32 half): merge across columns.
     #pragma unroll
@@ -508,13 +554,15 @@ int head_logits_launch(const HeadRows& rows, const uint16_t* weight, int R, int 
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+int add_splits(int R, int V) { return splits_for(R, V); }
+
 int head_add_bf16_launch(const HeadRows& rows, const uint16_t* weight, int R, int H, int V,
                          const uint16_t* base, uint16_t* out, long long row_stride,
-                         hipStream_t s) {
+                         ArgPart* arg, hipStream_t s) {
     if (R < 1) return SV_OK;
     hipLaunchKernelGGL(head_stats_kernel<kEpiAddBf16>, dim3((unsigned)items_for(R, V)),
                        dim3(kHThreads), 0, s, rows, weight, R, nullptr, H, V, nullptr, 0.0f,
-                       nullptr, nullptr, RowAdd{base, out, row_stride});
+                       nullptr, nullptr, RowAdd{base, out, row_stride, arg});
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

@@ -20,10 +20,12 @@
 //      LDS: the backbone values come in with 16-byte loads, each bias is
 //      added in fp32 and rounded once to bf16 (to nearest, ties to even), and
 //      the drafter rows go out with 16-byte stores, so the bias never reaches
-//      memory;
-//   2. one workgroup per request reads its stored row back and takes the
-//      first argmax, which is x_i and the next position's row map (two map
-//      buffers alternate).
+//      memory. The same epilogue follows the values it stores with a first
+//      argmax per row and vocabulary split;
+//   2. one wave per request merges its splits' argmaxes (ties to the lower
+//      column): the first argmax of the stored row, which is x_i and the
+//      next position's row map (two map buffers alternate). The stored rows
+//      are not read back.
 // A seed launch checks the given last tokens and writes the first row map.
 
 #include <hip/hip_runtime.h>
@@ -37,14 +39,14 @@
 
 namespace {
 
+using svhead::ArgPart;
 using svhead::HeadRows;
 
-constexpr int kMkThreads = 512;                    // 8 waves per request row
-constexpr int kMkGroup = 8;                        // elements per lane per step (16 B of bf16)
-constexpr int kMkUnroll = 2;                       // groups in flight per lane
+constexpr int kMkPickThreads = 256;
+constexpr int kMkPickWaves = kMkPickThreads / 64;     // one request per wave
 
 struct MkLayout {
-    size_t map0, map1, total;
+    size_t map0, map1, parts, total;
 };
 
 size_t mk_up256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -57,9 +59,9 @@ MkLayout mk_layout(int B, int V) {
         o += mk_up256(bytes);
         return at;
     };
-    (void)V;
     L.map0 = take((size_t)B * 4);
     L.map1 = take((size_t)B * 4);
+    L.parts = take((size_t)svhead::add_splits(B, V) * (size_t)B * sizeof(ArgPart));
     L.total = o;
     return L;
 }
@@ -83,71 +85,27 @@ __global__ void mk_seed_kernel(const int32_t* __restrict__ prev, int B, int V,
     if (threadIdx.x == 0 && status) status[0] = bad ? (int32_t)SV_FLAG_BAD_TOKEN : 0;
 }
 
-__device__ __forceinline__ float bf16_value(uint32_t bits16) {
-    return __uint_as_float(bits16 << 16);
-}
-
 __device__ __forceinline__ bool mk_better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
 }
 
-// The first argmax of one stored request row of position i: x_i, written to
-// the drafted tokens and the next position's row map. kVec: 16-byte loads
-// are legal (V % 8 == 0).
-template <bool kVec>
-__global__ __launch_bounds__(kMkThreads) void mk_argmax_kernel(
-    const uint16_t* __restrict__ z, int K, int V, int i, int32_t* __restrict__ out_tokens,
-    int32_t* __restrict__ next_map) {
-    __shared__ float wv[kMkThreads / 64];
-    __shared__ int wi[kMkThreads / 64];
-    const int b = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const size_t row = (size_t)b * K + i;
-    const uint16_t* src = z + row * (size_t)V;
+// Position i's token of each request, one wave per request: the first
+// argmax over its splits' entries. A larger value wins, an equal one only
+// from a lower column; columns are unique, so the result does not depend on
+// the order of the merges, and the lanes take the splits in parallel.
+__global__ __launch_bounds__(kMkPickThreads) void mk_pick_kernel(
+    const ArgPart* __restrict__ part, int splits, int B, int K, int V, int i,
+    int32_t* __restrict__ out_tokens, int32_t* __restrict__ next_map) {
+    const int lane = threadIdx.x & 63;
+    const int b = blockIdx.x * kMkPickWaves + (int)(threadIdx.x >> 6);
+    if (b >= B) return;                                // whole waves leave together
     float bv = -INFINITY;
     int bi = INT_MAX;
-    constexpr int step = kMkThreads * kMkGroup;
-    if (kVec) {
-        for (int e0 = tid * kMkGroup; e0 < V; e0 += step * kMkUnroll) {
-            uint4 g[kMkUnroll];
-            #pragma unroll
-            for (int u = 0; u < kMkUnroll; ++u) {
-                const int e = e0 + u * step;
-                if (e < V) g[u] = *reinterpret_cast<const uint4*>(src + e);
-            }
-            #pragma unroll
-            for (int u = 0; u < kMkUnroll; ++u) {
-                const int e = e0 + u * step;
-                if (e < V) {
-                    const uint32_t w[4] = {g[u].x, g[u].y, g[u].z, g[u].w};
-                    #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const float vl = bf16_value(w[k] & 0xFFFFu), vh = bf16_value(w[k] >> 16);
-                        if (vl > bv) {              // a lane's elements go up in index order
-                            bv = vl;
-                            bi = e + 2 * k;
-                        }
-                        if (vh > bv) {
-                            bv = vh;
-                            bi = e + 2 * k + 1;
-                        }
-                    }
-                }
-            }
-        }
-    } else {
-        for (int e0 = tid * kMkGroup; e0 < V; e0 += step) {
-            #pragma unroll
-            for (int k = 0; k < kMkGroup; ++k) {
-                const int e = e0 + k;
-                if (e < V) {
-                    const float v = bf16_value(src[e]);
-                    if (v > bv) {
-                        bv = v;
-                        bi = e;
-                    }
-                }
-            }
+    for (int sp = lane; sp < splits; sp += 64) {
+        const ArgPart a = part[(size_t)sp * B + b];
+        if (mk_better(a.v, a.i, bv, bi)) {
+            bv = a.v;
+            bi = a.i;
         }
     }
     #pragma unroll
@@ -160,19 +118,8 @@ __global__ __launch_bounds__(kMkThreads) void mk_argmax_kernel(
         }
     }
     if (lane == 0) {
-        wv[wave] = bv;
-        wi[wave] = bi;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        for (int w = 1; w < kMkThreads / 64; ++w) {
-            if (mk_better(wv[w], wi[w], bv, bi)) {
-                bv = wv[w];
-                bi = wi[w];
-            }
-        }
-        const int x = (bi >= 0 && bi < V) ? bi : 0;   // an all-NaN row (undefined input)
-        out_tokens[row] = x;
+        const int x = (bi >= 0 && bi < V) ? bi : 0;   // no value above -inf: token 0
+        out_tokens[(size_t)b * K + i] = x;
         next_map[b] = x;
     }
 }
@@ -211,6 +158,8 @@ extern "C" int spec_markov_draft(const void* base_logits, const void* markov_a,
     char* ws = static_cast<char*>(workspace);
     int32_t* map[2] = {reinterpret_cast<int32_t*>(ws + L.map0),
                        reinterpret_cast<int32_t*>(ws + L.map1)};
+    ArgPart* parts = reinterpret_cast<ArgPart*>(ws + L.parts);
+    const int splits = svhead::add_splits(B, V);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const uint16_t* A = static_cast<const uint16_t*>(markov_a);
     const uint16_t* Bm = static_cast<const uint16_t*>(markov_b);
@@ -225,15 +174,12 @@ extern "C" int spec_markov_draft(const void* base_logits, const void* markov_a,
         // occur (tokens are checked, argmaxes lie in [0, V)).
         const HeadRows rows{A, nullptr, map[i & 1], V};
         const int rc = svhead::head_add_bf16_launch(rows, Bm, B, r, V, base + (size_t)i * V,
-                                                    out + (size_t)i * V, (long long)K * V, s);
+                                                    out + (size_t)i * V, (long long)K * V, parts,
+                                                    s);
         if (rc != SV_OK) return rc;
-        if (V % kMkGroup == 0) {
-            hipLaunchKernelGGL(mk_argmax_kernel<true>, dim3((unsigned)B), dim3(kMkThreads), 0, s, out,
-                               K, V, i, out_tokens, map[(i + 1) & 1]);
-        } else {
-            hipLaunchKernelGGL(mk_argmax_kernel<false>, dim3((unsigned)B), dim3(kMkThreads), 0, s,
-                               out, K, V, i, out_tokens, map[(i + 1) & 1]);
-        }
+        hipLaunchKernelGGL(mk_pick_kernel, dim3((unsigned)((B + kMkPickWaves - 1) / kMkPickWaves)),
+                           dim3(kMkPickThreads), 0, s, parts, splits, B, K, V, i, out_tokens,
+                           map[(i + 1) & 1]);
         if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
     }
     return SV_OK;

@@ -340,8 +340,10 @@ size_t spec_verify_hidden_workspace_bytes(int B, int K, int V);
  *   workspace    device scratch of at least
  *                spec_markov_draft_workspace_bytes(B, V) bytes, 256-byte
  *                aligned, caller-owned; calls sharing it must not overlap.
- *                It holds two token maps of B entries (the bias rows never
- *                reach memory).
+ *                It holds two token maps of B entries and one first-argmax
+ *                entry (8 bytes) per request and vocabulary split of the
+ *                product; the bias rows never reach memory, and the stored
+ *                rows are not read back.
  * Errors (nothing enqueued): SV_ERR_ARG, SV_ERR_NULL, SV_ERR_ALIGN;
  * SV_ERR_HIP if a launch fails.
  */

@@ -144,6 +144,32 @@ def test_successor_chain():
             last = want[b][i]
 
 
+def test_ties_across_vocabulary_splits():
+    # No transition term, so the stored rows are the backbone's; values on a
+    # coarse grid tie for the maximum in many vocabulary splits (40 splits of
+    # 8 tiles at V = 40,960), and the token must be the lowest such column.
+    B, K, V, r = 6, 3, 40960, 16
+    g = torch.Generator().manual_seed(21)
+    base = torch.randint(-2, 3, (B, K, V), generator=g).float()
+    base[0, :, :] = 0.0                        # every column ties: token 0
+    base[0, 1, :] = -float("inf")              # no value above -inf: token 0
+    base[1, :, :] = -1.0
+    base[1, :, V - 3] = 2.0                    # the only maximum, in the last split
+    base[2, :, :] = 1.0
+    base[2, :, 1000] = 1.5
+    base[2, :, 30000] = 1.5                    # the first of two maxima in different splits
+    inp = make_markov_inputs(B, K, V, r, seed=22, device=DEV)
+    inp["base"] = base.to(torch.bfloat16).to(DEV)
+    inp["markov_b"] = torch.zeros_like(inp["markov_b"])
+    z, x, st = _run(inp)
+    assert st == 0
+    assert torch.equal(z.view(torch.int16), inp["base"].view(torch.int16))
+    want = torch.argmax(base, dim=2).numpy()   # first maximum (-inf rows: 0)
+    assert np.array_equal(x, want)
+    assert x[0].tolist() == [0, 0, 0] and x[1].tolist() == [V - 3] * K
+    assert x[2].tolist() == [1000] * K
+
+
 def test_heavy_shape_full_launch():
     # The bench's shape: 512 requests, 8 drafted positions, Qwen3-4B's
     # vocabulary, rank 256; the oracle on every 64th request.
