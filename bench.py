@@ -21,6 +21,7 @@ logits.
   python bench.py [--steps K] [--warmup W] [--warmup-settle S] [--workload heavy]
                   [--no-cpu-baseline] [--verify-only]
   python bench.py --copy-probe GIB   # plain copies of a known size (counter scale)
+  python bench.py --markov-only      # the Markov head alone at the heavy shape (profiling)
 """
 from __future__ import annotations
 
@@ -454,6 +455,8 @@ def main():
                     help="time the verify step only (no scheduler, head or hidden-state legs)")
     ap.add_argument("--cpu-requests", type=int, default=512)
     ap.add_argument("--copy-probe", type=float, default=None)
+    ap.add_argument("--markov-only", action="store_true",
+                    help="time only the Markov head over a heavy-shape block (3 calls)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -467,6 +470,9 @@ def main():
 
     if args.copy_probe is not None:
         copy_probe(args.copy_probe)
+        return
+    if args.markov_only:
+        print(json.dumps({"markov": bench_markov(512, 8, 151936, 256, 3)}), flush=True)
         return
 
     dev = torch.device("cuda:0")
