@@ -48,6 +48,7 @@ constexpr int kPad = 8;                    // LDS row padding (bf16 elements)
 constexpr int kLdsRow = kTK + kPad;        // 72 bf16 = 144 bytes per staged row
 
 constexpr int kResidentSlots = 512;        // one resident wave of workgroups: 2 per CU
+constexpr int kAddDeep = 4;                // add-and-store: the two-deep path's k-steps (depth <= 256)
 
 enum Epi { kEpiGreedy = 0, kEpiSampled = 1, kEpiLogits = 2, kEpiAddBf16 = 3 };
 
@@ -222,6 +223,8 @@ void head_stats_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
 
     for (int t = t0; t < t1; ++t) {
         const int v0 = t * kTN;
+        Piece bp;                          // add-and-store: this thread's 8 backbone groups,
+        bool pre = false;                  // loaded during the product
         f32x16 acc[2][2];
         #pragma unroll
         for (int a = 0; a < 2; ++a)
@@ -230,6 +233,113 @@ void head_stats_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
                 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
+        if constexpr (addbf) {
+            if (nk <= kAddDeep && H % kTK == 0) {
+                // A shallow product (the Markov head's rank): two k-steps'
+                // operand loads in flight instead of one. Every step is full
+                // depth, so the loads take no ragged-tail path: a missing row
+                // reads the weight's first row and is zeroed afterwards, and
+                // every lane issues the same loads, which lets each step wait
+                // for its own loads only.
+                const uint16_t* brow = v0 + srow < V ? w + (size_t)(v0 + srow) * H : nullptr;
+                const uint16_t* pa = (arow ? arow : w) + skh;
+                const uint16_t* pb = (brow ? brow : w) + skh;
+                // Missing rows are zeroed by masking the words as they are
+                // staged (a select at the load would split it into 4-byte
+                // loads, and masking there would wait for it at once).
+                const uint32_t ma = arow ? 0xFFFFFFFFu : 0u, mb = brow ? 0xFFFFFFFFu : 0u;
+                auto ld = [&](const uint16_t* p, int k) -> uint4 {
+                    return *reinterpret_cast<const uint4*>(p + k);
+                };
+                auto fetch = [&](int k0) -> Piece {
+                    Piece pc;
+                    pc.a0 = ld(pa, k0);
+                    pc.a1 = ld(pa, k0 + 8);
+                    pc.a2 = ld(pa, k0 + 16);
+                    pc.a3 = ld(pa, k0 + 24);
+                    pc.b0 = ld(pb, k0);
+                    pc.b1 = ld(pb, k0 + 8);
+                    pc.b2 = ld(pb, k0 + 16);
+                    pc.b3 = ld(pb, k0 + 24);
+                    return pc;
+                };
+                auto mk = [](const uint4& x, uint32_t m) {
+                    return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
+                };
+                auto stage = [&](const Piece& pc) {
+                    uint4* sa = reinterpret_cast<uint4*>(&As[srow][skh]);
+                    uint4* sb = reinterpret_cast<uint4*>(&Bs[srow][skh]);
+                    sa[0] = mk(pc.a0, ma); sa[1] = mk(pc.a1, ma); sa[2] = mk(pc.a2, ma); sa[3] = mk(pc.a3, ma);
+                    sb[0] = mk(pc.b0, mb); sb[1] = mk(pc.b1, mb); sb[2] = mk(pc.b2, mb); sb[3] = mk(pc.b3, mb);
+                };
+                auto mma = [&]() {
+                    #pragma unroll
+                    for (int kk = 0; kk < kTK; kk += 16) {
+                        bf16x8 af[2], bfr[2];
+                        #pragma unroll
+                        for (int a = 0; a < 2; ++a) {
+                            af[a] = *reinterpret_cast<const bf16x8*>(
+                                &As[wr + 32 * a + (lane & 31)][kk + (lane >> 5) * 8]);
+                            bfr[a] = *reinterpret_cast<const bf16x8*>(
+                                &Bs[wc + 32 * a + (lane & 31)][kk + (lane >> 5) * 8]);
+                        }
+                        #pragma unroll
+                        for (int a = 0; a < 2; ++a)
+                            #pragma unroll
+                            for (int b = 0; b < 2; ++b)
+                                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+                    }
+                };
+                // Steps 0 and 1 go out together; step ks + 2 as soon as step
+                // ks is staged. Every fetch is unconditional, so no wait
+                // hides behind a branch; a step past the last is the last
+                // step again (in bounds, not used).
+                auto kstep = [&](int st) { return (st < nk ? st : nk - 1) * kTK; };
+                Piece p0 = fetch(0);
+                Piece p1 = fetch(kstep(1));
+                __syncthreads();           // earlier readers of the operand tiles are done
+                stage(p0);
+                p0 = fetch(kstep(2));
+                if ((V & 7) == 0) {
+                    // The tile's backbone groups (epilogue step 1) go out now,
+                    // behind the operand loads. Absent rows read the tile's
+                    // first row and columns past V the row's last group
+                    // (in bounds; neither is stored).
+                    const int rr = min(r0 + (tid >> 1), R - 1);
+                    const uint16_t* src = ra.base + (size_t)rr * (size_t)ra.stride;
+                    const int c0 = v0 + (tid & 1) * 64;
+                    auto grp = [&](int q8) {
+                        return *reinterpret_cast<const uint4*>(src + min(c0 + q8 * 8, V - 8));
+                    };
+                    bp.a0 = grp(0); bp.a1 = grp(1); bp.a2 = grp(2); bp.a3 = grp(3);
+                    bp.b0 = grp(4); bp.b1 = grp(5); bp.b2 = grp(6); bp.b3 = grp(7);
+                    pre = true;
+                }
+                __syncthreads();
+                mma();
+                if (nk > 1) {
+                    __syncthreads();
+                    stage(p1);
+                    p1 = fetch(kstep(3));
+                    __syncthreads();
+                    mma();
+                }
+                if (nk > 2) {
+                    __syncthreads();
+                    stage(p0);
+                    __syncthreads();
+                    mma();
+                }
+                if (nk > 3) {
+                    __syncthreads();
+                    stage(p1);
+                    __syncthreads();
+                    mma();
+                }
+                goto epilogue;
+            }
+        }
+        {
         Piece pc;
         load_step(v0, 0, pc);
         __syncthreads();                   // previous tile's readers are done
@@ -260,6 +370,8 @@ void head_stats_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
                 __syncthreads();
             }
         }
+        }
+    epilogue:
 
         if (logits) {
             // The tile's logits, one row segment of 32 columns per block.
@@ -289,7 +401,11 @@ void head_stats_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
             const bool rok = tok_s[trow] != 0;
             const size_t goff = (size_t)(r0 + trow) * (size_t)ra.stride + (size_t)(v0 + tc0);
             const bool vec = (V & 7) == 0;         // 16-byte aligned rows and columns
-            if (rok) {
+            if (pre) {
+                uint4* dst = reinterpret_cast<uint4*>(&T[trow * kTS + tc0]);
+                dst[0] = bp.a0; dst[1] = bp.a1; dst[2] = bp.a2; dst[3] = bp.a3;
+                dst[4] = bp.b0; dst[5] = bp.b1; dst[6] = bp.b2; dst[7] = bp.b3;
+            } else if (rok) {
                 #pragma unroll
                 for (int q8 = 0; q8 < 8; ++q8) {
                     const int col = v0 + tc0 + q8 * 8;
