@@ -149,8 +149,18 @@ void head_stats_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
 
     // One (row tile, split) item per workgroup; workgroups beyond this
     // call's items (a count read on the device) have nothing to do.
-    const int item = blockIdx.x;
+    int item = blockIdx.x;
     if (item >= rtiles * nsplit) return;
+    if constexpr (addbf) {
+        // Workgroups go to the eight XCDs round-robin. Renumber so that a
+        // split's row tiles are consecutive workgroups of one XCD: they read
+        // the same weight rows at about the same time through one L2. A
+        // bijection on [0, rtiles * nsplit) when nsplit is a multiple of 8.
+        if (nsplit % 8 == 0) {
+            const int xcd = item % 8, slot = item / 8;
+            item = ((slot / rtiles) * 8 + xcd) * rtiles + slot % rtiles;
+        }
+    }
     const int r0 = (item % rtiles) * kTM;
     const int split = item / rtiles;
     const int t0 = split * tiles_per_split, t1 = min(ntiles, t0 + tiles_per_split);
