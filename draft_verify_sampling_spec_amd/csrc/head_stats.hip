@@ -151,7 +151,7 @@ void head_stats_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
     // call's items (a count read on the device) have nothing to do.
     int item = blockIdx.x;
     if (item >= rtiles * nsplit) return;
-    if constexpr (addbf) {
+    if constexpr (addbf || logits) {
         // Workgroups go to the eight XCDs round-robin. Renumber so that a
         // split's row tiles are consecutive workgroups of one XCD: they read
         // the same weight rows at about the same time through one L2. A
