@@ -93,6 +93,9 @@ SHAPES = [
     (5, 3, 40003, 256),
     (2, 2, 5, 8),
     (33, 6, 2048, 256),
+    (16, 4, 65536, 128),      # two k-steps, 64 splits (XCD order)
+    (9, 3, 30000, 192),       # three k-steps: the last fetch repeats step 2
+    (200, 2, 40960, 128),     # two row tiles, 40 splits (XCD order)
 ]
 
 
