@@ -212,8 +212,29 @@ void head_stats_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
     struct Piece {
         uint4 a0, a1, a2, a3, b0, b1, b2, b3;
     };
+    // Depth a multiple of kTK: every load is a full 16-byte load from a valid
+    // row (a missing row reads the weight's first row), and missing rows
+    // are zeroed by masks as the words are staged. Not in the greedy
+    // statistics, whose registers it would push into spills.
+    const bool hfull = kEpi != kEpiGreedy && H % kTK == 0;
+    const uint32_t mask_a = arow ? 0xFFFFFFFFu : 0u;
+    uint32_t mask_b = 0xFFFFFFFFu;
     auto load_step = [&](int v0, int k0, Piece& pc) {
         const uint16_t* brow = v0 + srow < V ? w + (size_t)(v0 + srow) * H : nullptr;
+        if (hfull) {
+            const uint16_t* pa = (arow ? arow : w) + k0 + skh;
+            const uint16_t* pb = (brow ? brow : w) + k0 + skh;
+            pc.a0 = *reinterpret_cast<const uint4*>(pa);
+            pc.a1 = *reinterpret_cast<const uint4*>(pa + 8);
+            pc.a2 = *reinterpret_cast<const uint4*>(pa + 16);
+            pc.a3 = *reinterpret_cast<const uint4*>(pa + 24);
+            pc.b0 = *reinterpret_cast<const uint4*>(pb);
+            pc.b1 = *reinterpret_cast<const uint4*>(pb + 8);
+            pc.b2 = *reinterpret_cast<const uint4*>(pb + 16);
+            pc.b3 = *reinterpret_cast<const uint4*>(pb + 24);
+            mask_b = brow ? 0xFFFFFFFFu : 0u;
+            return;
+        }
         load16(arow, k0 + skh, pc.a0, pc.a1);
         load16(arow, k0 + skh + 16, pc.a2, pc.a3);
         load16(brow, k0 + skh, pc.b0, pc.b1);
@@ -222,8 +243,10 @@ void head_stats_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
     auto store_step = [&](const Piece& pc) {
         uint4* ra = reinterpret_cast<uint4*>(&As[srow][skh]);
         uint4* rb = reinterpret_cast<uint4*>(&Bs[srow][skh]);
-        ra[0] = pc.a0; ra[1] = pc.a1; ra[2] = pc.a2; ra[3] = pc.a3;
-        rb[0] = pc.b0; rb[1] = pc.b1; rb[2] = pc.b2; rb[3] = pc.b3;
+        const uint32_t ma = hfull ? mask_a : 0xFFFFFFFFu, mb = hfull ? mask_b : 0xFFFFFFFFu;
+        auto m = [](const uint4& x, uint32_t k) { return make_uint4(x.x & k, x.y & k, x.z & k, x.w & k); };
+        ra[0] = m(pc.a0, ma); ra[1] = m(pc.a1, ma); ra[2] = m(pc.a2, ma); ra[3] = m(pc.a3, ma);
+        rb[0] = m(pc.b0, mb); rb[1] = m(pc.b1, mb); rb[2] = m(pc.b2, mb); rb[3] = m(pc.b3, mb);
     };
 
     // Add-and-store: this thread's running first argmax over the values it
