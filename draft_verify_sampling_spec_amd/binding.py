@@ -33,6 +33,7 @@ SV_DTYPE_BF16 = 1
 
 SV_FLAG_BAD_BUDGET = 0x1
 SV_FLAG_BAD_TOKEN = 0x2
+SV_FLAG_SYNC_TIMEOUT = 0x4
 
 SV_MAX_BATCH = 16384
 SV_MAX_K = 32
@@ -41,6 +42,7 @@ SV_MAX_VOCAB = 1 << 20
 EXPORTED = (
     "spec_verify_init",
     "spec_verify_run",
+    "spec_verify_run_ex",
     "spec_verify_check_args",
     "spec_verify_status",
     "spec_verify_philox_words",
@@ -70,6 +72,9 @@ def _declare(lib):
     lib.spec_verify_run.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, ctypes.c_float,
                                     ctypes.c_uint64, _vp, _vp, _vp, _vp, _vp]
     lib.spec_verify_run.restype = _i
+    lib.spec_verify_run_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, ctypes.c_float,
+                                       ctypes.c_uint64, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp]
+    lib.spec_verify_run_ex.restype = _i
     lib.spec_verify_check_args.argtypes = [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i,
                                            ctypes.c_float, _vp, _vp, _vp, _vp]
     lib.spec_verify_check_args.restype = _i
@@ -154,6 +159,15 @@ def spec_verify_run(ctx, target, draft, tokens, budgets, B, K, temperature, seed
                                   ctypes.c_float(temperature), ctypes.c_uint64(seed),
                                   out_tokens, out_num_accepted, out_p_draft, out_q_draft,
                                   stream)
+
+
+def spec_verify_run_ex(ctx, target, draft, tokens, budgets, B, K, temperature, seed,
+                       request_base, out_tokens, out_num_accepted, out_p_draft, out_q_draft,
+                       stream) -> int:
+    return load().spec_verify_run_ex(ctx, target, draft, tokens, budgets, B, K,
+                                     ctypes.c_float(temperature), ctypes.c_uint64(seed),
+                                     ctypes.c_int64(request_base), out_tokens, out_num_accepted,
+                                     out_p_draft, out_q_draft, stream)
 
 
 def spec_verify_status(ctx):
@@ -245,11 +259,14 @@ class SpecVerify:
 
     def run(self, target, draft, tokens, budgets, temperature: float, seed: int,
             out_tokens=None, out_num_accepted=None, out_p=None, out_q=None,
-            want_probs: bool = True, stream=None):
+            want_probs: bool = True, stream=None, request_base: int = 0):
         """Verify a batch. Returns (tokens [B,K+1], n_accepted [B], p_x, q_x).
 
         p_x/q_x are None unless ``want_probs`` (or output buffers are given).
-        Enqueued on ``stream`` (default: the current torch stream), not waited for.
+        ``request_base``: index of row 0 in the whole batch (its Philox
+        counter). Enqueued on ``stream`` (default: the current torch stream),
+        not waited for; device-side problems (a bad budget or token) only
+        show in ``status()``, which waits.
         """
         if target.dim() != 3:
             raise ValueError("target logits must be [B, K+1, V]")
@@ -282,9 +299,10 @@ class SpecVerify:
         op = self._tensor(out_p, "out_p", torch.float32, (B, K)) if out_p is not None else None
         oq = self._tensor(out_q, "out_q", torch.float32, (B, K)) if out_q is not None else None
         s = stream.cuda_stream if stream is not None else _stream_handle(dev)
-        rc = spec_verify_run(self._ctx, t_ptr, d_ptr, x_ptr, k_ptr, B, K, temperature,
-                             int(seed) & 0xFFFFFFFFFFFFFFFF, ot, on, op, oq, s)
-        _check(rc, "spec_verify_run")
+        rc = spec_verify_run_ex(self._ctx, t_ptr, d_ptr, x_ptr, k_ptr, B, K, temperature,
+                                int(seed) & 0xFFFFFFFFFFFFFFFF, int(request_base), ot, on, op, oq,
+                                s)
+        _check(rc, "spec_verify_run_ex")
         return out_tokens, out_num_accepted, out_p, out_q
 
     def status(self) -> int:

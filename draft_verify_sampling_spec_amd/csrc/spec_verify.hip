@@ -119,7 +119,7 @@ struct Params {
     unsigned* dcnt;                // draw pass split: slices finished per request, kReqStride apart
     int dsplit;                    // workgroups per request in the draw pass
     int B, K, V;
-    int bbase;                     // index of request 0 of this launch in the caller's batch
+    uint32_t bbase;                // Philox request index of request 0 of this launch
     int C;                         // chunks per row
     int CE;                        // elements per chunk
     float c32;                     // log2(e) / T
@@ -758,7 +758,7 @@ __device__ __forceinline__ void owed_decide(const Params& P, const Owed& o, cons
         px = exp2((double)o.zt * (double)P.c32 - (double)ts.mt) / ts.st;
         qx = exp2((double)o.zd * (double)P.c32 - (double)ts.md) / ts.sd;
     }
-    const uint4 rw = philox4x32_10((uint32_t)(P.bbase + u.b), (uint32_t)u.i, 0u, 0u, P.key0, P.key1);
+    const uint4 rw = philox4x32_10(P.bbase + (uint32_t)u.b, (uint32_t)u.i, 0u, 0u, P.key0, P.key1);
     const bool accept = word_to_uniform(rw.x) * qx < px;
     if (lane == 0) {
         if (!valid) atomicOr(P.status, SV_FLAG_BAD_TOKEN);
@@ -1248,7 +1248,7 @@ void draw_kernel(Params P) {
     if (wave == 0) {
         if (!poll_complete<false>(P, pl) && lane == 0) atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);
         const TeamStats ts = team_stats(P, pl);
-        const uint4 rw = philox4x32_10((uint32_t)(P.bbase + b), (uint32_t)j, 0u, 0u, P.key0, P.key1);
+        const uint4 rw = philox4x32_10(P.bbase + (uint32_t)b, (uint32_t)j, 0u, 0u, P.key0, P.key1);
         const double u = word_to_uniform(rw.y);
         int x0 = 0, x1 = NB, mode = dsh.mode;
         double thr = 0.0;
@@ -1460,23 +1460,70 @@ size_t dyn_smem_bytes(int B) { return (size_t)(B + 1) * sizeof(int); }
 // kBlocks blocks).
 size_t draw_smem_bytes(int C) { return (size_t)C * kBlocks * sizeof(double); }
 
+// Byte offsets of the kernels' device workspace, for launches of up to
+// max_batch requests with up to max_k drafted positions and C chunks per row.
+// The draw pass splits a request over several workgroups only for batches of
+// at most split_reqs requests. Counters in [req, req_end) and [dcnt, dcnt_end)
+// must read zero when a call starts; every kernel that raises them leaves
+// them at zero when it completes.
+struct WsLayout {
+    size_t rec, team, result, req, req_end, dmass, dcnt, dcnt_end, status, total;
+    int split_reqs;
+};
+
+WsLayout ws_layout(int max_batch, int max_k, int C, int split_reqs) {
+    auto round256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t teams = (size_t)max_batch * (max_k + 1);
+    WsLayout L;
+    size_t o = 0;
+    L.rec = o;
+    o += round256(teams * C * kRecWords * 8);
+    L.team = o;
+    o += round256(teams * kTeamWords * 4);
+    L.result = o;
+    o += round256(teams * 4);
+    L.req = o;
+    o += round256((size_t)max_batch * kReqStride * 4);
+    L.req_end = o;
+    L.dmass = o;
+    o += round256((size_t)split_reqs * C * kBlocks * 8);
+    L.dcnt = o;
+    o += round256((size_t)split_reqs * kReqStride * 4);
+    L.dcnt_end = o;
+    L.status = o;
+    o += 256;
+    L.total = o;
+    L.split_reqs = split_reqs;
+    return L;
+}
+
+// Launch facts of one device: CUs and, per instantiation of the streaming
+// pass, the resident workgroups per CU (cached by dynamic LDS size).
+struct DeviceInfo {
+    int cus;
+    size_t occ_smem[8];
+    int occ_val[8];
+};
+
+int device_info(int device, DeviceInfo& di) {
+    std::memset(&di, 0, sizeof(di));
+    if (hipDeviceGetAttribute(&di.cus, hipDeviceAttributeMultiprocessorCount, device) !=
+            hipSuccess || di.cus < 1) {
+        return SV_ERR_HIP;
+    }
+    return SV_OK;
+}
+
 }  // namespace
 
 struct spec_verify_ctx {
     uint32_t magic;
     int device, max_batch, max_k, vocab, dtype;
     int C, CE;
-    int cus;
-    void* ws;
-    unsigned long long* rec;
-    unsigned* team;
-    unsigned* result;
-    unsigned* req_count;
-    unsigned* status;
-    double* dmass;                 // split draw pass: block masses of up to split_reqs requests
-    unsigned* dcnt;                // split draw pass: slice counters, kReqStride apart
-    int split_reqs;                // requests a split draw pass can hold
-    unsigned calls;
+    DeviceInfo info;
+    WsLayout lay;
+    unsigned char* ws;
+    unsigned calls;                // calls made so far (record and decision word epochs)
     // Per-pass timing (off unless enabled): recorded event pairs of later
     // runs, and a pool of events to reuse.
     bool timing;
@@ -1485,25 +1532,22 @@ struct spec_verify_ctx {
         hipEvent_t start, end;
     };
     std::vector<Timed> timed;
-    std::vector<hipEvent_t> event_pool;                // calls made so far (phase-word epochs)
-    // occupancy cache: dynamic LDS bytes -> resident workgroups per CU, per kernel
-    size_t occ_smem[8];
-    int occ_val[8];
+    std::vector<hipEvent_t> event_pool;
 };
 
 namespace {
 
 template <typename E, bool G, bool Vv>
-int occupancy_of(spec_verify_ctx* ctx, int slot, size_t smem) {
-    if (ctx->occ_smem[slot] == smem && ctx->occ_val[slot] > 0) return ctx->occ_val[slot];
+int occupancy_of(DeviceInfo& di, int slot, size_t smem) {
+    if (di.occ_smem[slot] == smem && di.occ_val[slot] > 0) return di.occ_val[slot];
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, verify_kernel<E, G, Vv>, kThreads, smem) !=
             hipSuccess ||
         n < 1) {
         n = 1;
     }
-    ctx->occ_smem[slot] = smem;
-    ctx->occ_val[slot] = n;
+    di.occ_smem[slot] = smem;
+    di.occ_val[slot] = n;
     return n;
 }
 
@@ -1520,9 +1564,9 @@ hipEvent_t pooled_event(spec_verify_ctx* ctx) {
 }
 
 // Start of a pass: when timing, an event pair is taken and its start
-// recorded; returns the record's index, or -1.
+// recorded; returns the record's index, or -1. ctx may be null (no timing).
 int timed_begin(spec_verify_ctx* ctx, int pass, hipStream_t stream) {
-    if (!ctx->timing || ctx->timed.size() >= kMaxTimed) return -1;
+    if (!ctx || !ctx->timing || ctx->timed.size() >= kMaxTimed) return -1;
     spec_verify_ctx::Timed t;
     t.pass = pass;
     t.start = pooled_event(ctx);
@@ -1537,47 +1581,132 @@ int timed_begin(spec_verify_ctx* ctx, int pass, hipStream_t stream) {
 }
 
 void timed_end(spec_verify_ctx* ctx, int idx, hipStream_t stream) {
-    if (idx >= 0) (void)hipEventRecord(ctx->timed[(size_t)idx].end, stream);
+    if (ctx && idx >= 0) (void)hipEventRecord(ctx->timed[(size_t)idx].end, stream);
 }
 
 // Launch shape of the streaming pass: every workgroup resident (grid = CUs x
 // occupancy); the schedule needs at least as many workgroups as a team has
 // members. Sampled mode then runs the draw pass, one workgroup per request.
 template <typename E, bool G, bool Vv>
-int launch(spec_verify_ctx* ctx, Params& p, hipStream_t stream) {
+int launch(DeviceInfo& di, spec_verify_ctx* tctx, int split_reqs, Params& p, hipStream_t stream) {
     const int slot = (std::is_same<E, uint16_t>::value ? 4 : 0) + (G ? 2 : 0) + (Vv ? 1 : 0);
     const size_t smem = dyn_smem_bytes(p.B);
-    const int occ = occupancy_of<E, G, Vv>(ctx, slot, smem);
-    const long long grid = (long long)ctx->cus * occ;
+    const int occ = occupancy_of<E, G, Vv>(di, slot, smem);
+    const long long grid = (long long)di.cus * occ;
     if (grid < (long long)p.C) return SV_ERR_ARG;   // a team would not fit
-    int t = timed_begin(ctx, 0, stream);
+    int t = timed_begin(tctx, 0, stream);
     hipLaunchKernelGGL((verify_kernel<E, G, Vv>), dim3((unsigned)grid), dim3(kThreads), smem, stream,
                        p);
     if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
-    timed_end(ctx, t, stream);
+    timed_end(tctx, t, stream);
     if (!G) {
         // Two draw workgroups fit a CU. A batch of fewer requests than that
         // splits each request's blocks over several workgroups (at least 16
         // blocks each, at most 64 workgroups per request).
         const int nb = (p.V + 64 * Elem<E>::W - 1) / (64 * Elem<E>::W);
         int S = 1;
-        if (p.B <= ctx->split_reqs) {
-            S = (2 * ctx->cus) / p.B;
+        if (p.B <= split_reqs) {
+            S = (2 * di.cus) / p.B;
             S = S < 1 ? 1 : (S > 64 ? 64 : S);
             const int smax = nb / 16 < 1 ? 1 : nb / 16;
             S = S > smax ? smax : S;
         }
         p.dsplit = S;
-        t = timed_begin(ctx, 1, stream);
+        t = timed_begin(tctx, 1, stream);
         hipLaunchKernelGGL((draw_kernel<E, Vv>), dim3((unsigned)(p.B * S)), dim3(kDrawThreads),
                            draw_smem_bytes(p.C), stream, p);
         if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
-        timed_end(ctx, t, stream);
+        timed_end(tctx, t, stream);
     }
     return SV_OK;
 }
 
 bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// The caller's arguments of one verify call (already checked).
+struct RunArgs {
+    const void* target;
+    const void* draft;
+    const int32_t* tokens;
+    const int32_t* budgets;
+    int B, K;
+    float temperature;
+    uint64_t seed;
+    uint32_t request_base;
+    int32_t* out_tokens;
+    int32_t* out_nacc;
+    float* out_p;
+    float* out_q;
+};
+
+// Enqueue one verify call on the stream: batches beyond kLaunchBatch requests
+// run as consecutive launches (each launch keeps its request table in LDS);
+// the workspace ws (laid out by L) is reused, and the Philox counter keeps
+// the caller's request index. calls: the epoch counter of this workspace.
+int run_batches(DeviceInfo& di, spec_verify_ctx* tctx, int vocab, int dtype, unsigned char* ws,
+                const WsLayout& L, unsigned& calls, unsigned* status, const RunArgs& a,
+                hipStream_t s) {
+    const bool greedy = a.temperature == 0.0f;
+    const int K = a.K;
+    Params p;
+    std::memset(&p, 0, sizeof(p));
+    p.rec = reinterpret_cast<unsigned long long*>(ws + L.rec);
+    p.team = reinterpret_cast<unsigned*>(ws + L.team);
+    p.result = reinterpret_cast<unsigned*>(ws + L.result);
+    p.req_count = reinterpret_cast<unsigned*>(ws + L.req);
+    p.status = status;
+    p.dmass = reinterpret_cast<double*>(ws + L.dmass);
+    p.dcnt = reinterpret_cast<unsigned*>(ws + L.dcnt);
+    p.K = K;
+    p.V = vocab;
+    p.C = chunks_for(vocab, dtype);
+    p.CE = chunk_elems(dtype);
+    p.c64 = greedy ? 0.0 : kLog2e / (double)a.temperature;
+    p.c32 = (float)p.c64;
+    p.key0 = (uint32_t)(a.seed & 0xFFFFFFFFu);
+    p.key1 = (uint32_t)(a.seed >> 32);
+    // Vector-only loads when every row starts on a 16-byte boundary.
+    const size_t es = dtype == SV_DTYPE_BF16 ? 2 : 4;
+    const bool vec = aligned_to(a.target, 16) && (greedy || K == 0 || aligned_to(a.draft, 16)) &&
+                     ((size_t)vocab * es) % 16 == 0;
+    const size_t V = (size_t)vocab;
+    int r = SV_OK;
+    for (int b0 = 0; b0 < a.B && r == SV_OK; b0 += kLaunchBatch) {
+        Params q = p;
+        q.B = a.B - b0 < kLaunchBatch ? a.B - b0 : kLaunchBatch;
+        q.bbase = a.request_base + (uint32_t)b0;
+        q.target = static_cast<const unsigned char*>(a.target) + (size_t)b0 * (K + 1) * V * es;
+        q.draft = greedy ? nullptr
+                         : static_cast<const unsigned char*>(a.draft) + (size_t)b0 * K * V * es;
+        q.tokens = a.tokens ? a.tokens + (size_t)b0 * K : nullptr;
+        q.budgets = a.budgets + b0;
+        q.out_tokens = a.out_tokens + (size_t)b0 * (K + 1);
+        q.out_nacc = a.out_nacc + b0;
+        q.out_p = a.out_p ? a.out_p + (size_t)b0 * K : nullptr;
+        q.out_q = a.out_q ? a.out_q + (size_t)b0 * K : nullptr;
+        calls = calls % 0xFFFFFFFFu + 1u;      // 1 .. 2^32 - 1, never 0
+        q.epoch = calls;
+        const int sr = L.split_reqs;
+        if (dtype == SV_DTYPE_BF16) {
+            if (vec) {
+                r = greedy ? launch<uint16_t, true, true>(di, tctx, sr, q, s)
+                           : launch<uint16_t, false, true>(di, tctx, sr, q, s);
+            } else {
+                r = greedy ? launch<uint16_t, true, false>(di, tctx, sr, q, s)
+                           : launch<uint16_t, false, false>(di, tctx, sr, q, s);
+            }
+        } else {
+            if (vec) {
+                r = greedy ? launch<float, true, true>(di, tctx, sr, q, s)
+                           : launch<float, false, true>(di, tctx, sr, q, s);
+            } else {
+                r = greedy ? launch<float, true, false>(di, tctx, sr, q, s)
+                           : launch<float, false, false>(di, tctx, sr, q, s);
+            }
+        }
+    }
+    return r;
+}
 
 }  // namespace
 
@@ -1656,46 +1785,22 @@ int spec_verify_init(spec_verify_ctx** out, int device, int max_batch, int max_k
     c->dtype = dtype;
     c->C = chunks_for(vocab, dtype);
     c->CE = chunk_elems(dtype);
-    int rc = SV_OK;
-    if (hipDeviceGetAttribute(&c->cus, hipDeviceAttributeMultiprocessorCount, device) !=
-        hipSuccess) {
-        rc = SV_ERR_HIP;
-    }
-    auto round256 = [](size_t x) { return (x + 255) / 256 * 256; };
-    const size_t teams = (size_t)max_batch * (max_k + 1);
-    const size_t rec_bytes = round256(teams * c->C * kRecWords * 8);
-    const size_t team_bytes = round256(teams * kTeamWords * 4);
-    const size_t result_bytes = round256(teams * 4);
-    const size_t req_bytes = round256((size_t)max_batch * kReqStride * 4);
-    // The draw pass splits a request over workgroups only when the batch has
-    // fewer requests than the GPU has CUs.
-    c->split_reqs = max_batch < c->cus ? max_batch : c->cus;
-    const size_t dmass_bytes = round256((size_t)c->split_reqs * c->C * kBlocks * 8);
-    const size_t dcnt_bytes = round256((size_t)c->split_reqs * kReqStride * 4);
-    const size_t total = rec_bytes + team_bytes + result_bytes + req_bytes + dmass_bytes +
-                         dcnt_bytes + 256;
-    if (rc == SV_OK && hipMalloc(&c->ws, total) != hipSuccess) {
-        c->ws = nullptr;
-        rc = SV_ERR_NOMEM;
-    }
+    c->ws = nullptr;
+    int rc = device_info(device, c->info);
     if (rc == SV_OK) {
-        unsigned char* w = static_cast<unsigned char*>(c->ws);
-        size_t o = 0;
-        c->rec = reinterpret_cast<unsigned long long*>(w + o);
-        o += rec_bytes;
-        c->team = reinterpret_cast<unsigned*>(w + o);
-        o += team_bytes;
-        c->result = reinterpret_cast<unsigned*>(w + o);
-        o += result_bytes;
-        c->req_count = reinterpret_cast<unsigned*>(w + o);
-        o += req_bytes;
-        c->dmass = reinterpret_cast<double*>(w + o);
-        o += dmass_bytes;
-        c->dcnt = reinterpret_cast<unsigned*>(w + o);
-        o += dcnt_bytes;
-        c->status = reinterpret_cast<unsigned*>(w + o);
-        if (hipMemset(c->ws, 0, total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-            rc = SV_ERR_HIP;
+        // The draw pass splits a request over workgroups only when the batch
+        // has fewer requests than the GPU has CUs.
+        const int mb = max_batch < kLaunchBatch ? max_batch : kLaunchBatch;
+        c->lay = ws_layout(mb, max_k, c->C, mb < c->info.cus ? mb : c->info.cus);
+        void* w = nullptr;
+        if (hipMalloc(&w, c->lay.total) != hipSuccess) {
+            rc = SV_ERR_NOMEM;
+        } else {
+            c->ws = static_cast<unsigned char*>(w);
+            if (hipMemset(c->ws, 0, c->lay.total) != hipSuccess ||
+                hipDeviceSynchronize() != hipSuccess) {
+                rc = SV_ERR_HIP;
+            }
         }
     }
     (void)hipSetDevice(prev);
@@ -1709,92 +1814,39 @@ int spec_verify_init(spec_verify_ctx** out, int device, int max_batch, int max_k
     return SV_OK;
 }
 
-int spec_verify_run(spec_verify_ctx* ctx, const void* target_logits, const void* draft_logits,
-                    const int32_t* draft_tokens, const int32_t* budgets, int B, int K,
-                    float temperature, uint64_t seed, int32_t* out_tokens,
-                    int32_t* out_num_accepted, float* out_p_draft, float* out_q_draft,
-                    void* stream) {
+int spec_verify_run_ex(spec_verify_ctx* ctx, const void* target_logits, const void* draft_logits,
+                       const int32_t* draft_tokens, const int32_t* budgets, int B, int K,
+                       float temperature, uint64_t seed, int64_t request_base,
+                       int32_t* out_tokens, int32_t* out_num_accepted, float* out_p_draft,
+                       float* out_q_draft, void* stream) {
     if (!ctx || ctx->magic != kMagic) return SV_ERR_STATE;
     const int rc = spec_verify_check_args(ctx->max_batch, ctx->max_k, ctx->vocab, ctx->dtype,
                                           target_logits, draft_logits, draft_tokens, budgets, B,
                                           K, temperature, out_tokens, out_num_accepted,
                                           out_p_draft, out_q_draft);
     if (rc != SV_OK) return rc;
+    if (request_base < 0 || request_base > (int64_t)0xFFFFFFFFll - B) return SV_ERR_ARG;
     if (B == 0) return SV_OK;
-    const bool greedy = temperature == 0.0f;
-
-    Params p;
-    std::memset(&p, 0, sizeof(p));
-    p.target = target_logits;
-    p.draft = greedy ? nullptr : draft_logits;
-    p.tokens = draft_tokens;
-    p.budgets = budgets;
-    p.out_tokens = out_tokens;
-    p.out_nacc = out_num_accepted;
-    p.out_p = out_p_draft;
-    p.out_q = out_q_draft;
-    p.rec = ctx->rec;
-    p.team = ctx->team;
-    p.result = ctx->result;
-    p.req_count = ctx->req_count;
-    p.status = ctx->status;
-    p.dmass = ctx->dmass;
-    p.dcnt = ctx->dcnt;
-    p.B = B;
-    p.K = K;
-    p.V = ctx->vocab;
-    p.C = ctx->C;
-    p.CE = ctx->CE;
-    p.c64 = greedy ? 0.0 : kLog2e / (double)temperature;
-    p.c32 = (float)p.c64;
-    p.key0 = (uint32_t)(seed & 0xFFFFFFFFu);
-    p.key1 = (uint32_t)(seed >> 32);
-
     int prev = -1;
     if (hipGetDevice(&prev) != hipSuccess) return SV_ERR_HIP;
     if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return SV_ERR_HIP;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    int r = SV_OK;
-    // Vector-only loads when every row starts on a 16-byte boundary.
-    const size_t es = ctx->dtype == SV_DTYPE_BF16 ? 2 : 4;
-    const bool vec = aligned_to(target_logits, 16) &&
-                     (greedy || K == 0 || aligned_to(draft_logits, 16)) &&
-                     ((size_t)ctx->vocab * es) % 16 == 0;
-    // Batches beyond kLaunchBatch requests run as consecutive launches on the
-    // stream (each launch keeps its request table in LDS); the workspace is
-    // reused, and the Philox counter keeps the caller's request index.
-    const size_t V = (size_t)ctx->vocab;
-    for (int b0 = 0; b0 < B && r == SV_OK; b0 += kLaunchBatch) {
-        Params q = p;
-        q.B = B - b0 < kLaunchBatch ? B - b0 : kLaunchBatch;
-        q.bbase = b0;
-        q.target = static_cast<const unsigned char*>(target_logits) + (size_t)b0 * (K + 1) * V * es;
-        q.draft = greedy ? nullptr
-                         : static_cast<const unsigned char*>(draft_logits) + (size_t)b0 * K * V * es;
-        q.tokens = draft_tokens ? draft_tokens + (size_t)b0 * K : nullptr;
-        q.budgets = budgets + b0;
-        q.out_tokens = out_tokens + (size_t)b0 * (K + 1);
-        q.out_nacc = out_num_accepted + b0;
-        q.out_p = out_p_draft ? out_p_draft + (size_t)b0 * K : nullptr;
-        q.out_q = out_q_draft ? out_q_draft + (size_t)b0 * K : nullptr;
-        ctx->calls = ctx->calls % 0xFFFFFFFFu + 1u;     // 1 .. 2^32 - 1, never 0
-        q.epoch = ctx->calls;
-        if (ctx->dtype == SV_DTYPE_BF16) {
-            if (vec) {
-                r = greedy ? launch<uint16_t, true, true>(ctx, q, s) : launch<uint16_t, false, true>(ctx, q, s);
-            } else {
-                r = greedy ? launch<uint16_t, true, false>(ctx, q, s) : launch<uint16_t, false, false>(ctx, q, s);
-            }
-        } else {
-            if (vec) {
-                r = greedy ? launch<float, true, true>(ctx, q, s) : launch<float, false, true>(ctx, q, s);
-            } else {
-                r = greedy ? launch<float, true, false>(ctx, q, s) : launch<float, false, false>(ctx, q, s);
-            }
-        }
-    }
+    RunArgs a{target_logits, draft_logits, draft_tokens, budgets, B, K, temperature, seed,
+              (uint32_t)request_base, out_tokens, out_num_accepted, out_p_draft, out_q_draft};
+    const int r = run_batches(ctx->info, ctx, ctx->vocab, ctx->dtype, ctx->ws, ctx->lay,
+                              ctx->calls, reinterpret_cast<unsigned*>(ctx->ws + ctx->lay.status),
+                              a, static_cast<hipStream_t>(stream));
     if (prev != ctx->device) (void)hipSetDevice(prev);
     return r;
+}
+
+int spec_verify_run(spec_verify_ctx* ctx, const void* target_logits, const void* draft_logits,
+                    const int32_t* draft_tokens, const int32_t* budgets, int B, int K,
+                    float temperature, uint64_t seed, int32_t* out_tokens,
+                    int32_t* out_num_accepted, float* out_p_draft, float* out_q_draft,
+                    void* stream) {
+    return spec_verify_run_ex(ctx, target_logits, draft_logits, draft_tokens, budgets, B, K,
+                              temperature, seed, 0, out_tokens, out_num_accepted, out_p_draft,
+                              out_q_draft, stream);
 }
 
 int spec_verify_status(spec_verify_ctx* ctx, uint32_t* flags) {
@@ -1805,9 +1857,10 @@ int spec_verify_status(spec_verify_ctx* ctx, uint32_t* flags) {
     if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return SV_ERR_HIP;
     int rc = SV_OK;
     unsigned v = 0;
+    unsigned* status = reinterpret_cast<unsigned*>(ctx->ws + ctx->lay.status);
     if (hipDeviceSynchronize() != hipSuccess ||
-        hipMemcpy(&v, ctx->status, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess ||
-        hipMemset(ctx->status, 0, sizeof(unsigned)) != hipSuccess ||
+        hipMemcpy(&v, status, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemset(status, 0, sizeof(unsigned)) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {
         rc = SV_ERR_HIP;
     }

@@ -92,7 +92,11 @@ enum sv_status {
 #define SV_MAX_VOCAB (1 << 20)
 
 /*
- * spec_verify_init -- create a context for one device and one problem shape.
+ * spec_verify_init -- create a context for one device and one problem shape
+ * (the batched verify step of "Speculative decoding becomes standard: DSpark
+ * and multi-token drafters", section "Why draft-and-verify does not change
+ * the output", with the per-request budgets of section "What DSpark adds",
+ * paragraph 2).
  *   out        receives the context (set to NULL on failure).
  *   device     HIP device ordinal.
  *   max_batch  largest B a run will pass, 1..SV_MAX_BATCH.
@@ -101,14 +105,19 @@ enum sv_status {
  *   dtype      sv_dtype of the logits of every run.
  * Allocates and zeroes the device workspace (per-chunk partial statistics,
  * per-row decision words, per-request counters of greedy mode, status
- * word). Synchronous.
+ * word). The context owns it until spec_verify_free. Synchronous.
  * Errors: SV_ERR_NULL, SV_ERR_ARG, SV_ERR_DTYPE, SV_ERR_HIP, SV_ERR_NOMEM.
  */
 int spec_verify_init(spec_verify_ctx** out, int device, int max_batch, int max_k,
                      int vocab, int dtype);
 
 /*
- * spec_verify_run -- verify one batch (stream-ordered, no host sync).
+ * spec_verify_run -- verify one batch (stream-ordered, no host sync): the
+ * greedy rule ("Speculative decoding becomes standard: DSpark and
+ * multi-token drafters", section "Why draft-and-verify does not change the
+ * output", paragraph 1) when temperature == 0, else the rejection rule with
+ * residual and bonus draws (same section, paragraph 2), over the budgeted
+ * positions of each request (section "What DSpark adds", paragraph 2).
  *   target_logits     [B, K+1, V] row-major, storage ctx dtype (device).
  *   draft_logits      [B, K, V] row-major, same storage (device); may be
  *                     NULL when temperature == 0 (never read then).
@@ -129,6 +138,8 @@ int spec_verify_init(spec_verify_ctx** out, int device, int max_batch, int max_k
  *                     i >= k_b and in greedy mode (device).
  *   out_q_draft       float [B, K] or NULL: q_i(x_i), same layout.
  *   stream            hipStream_t or NULL.
+ * The caller keeps ownership of every tensor. Request b uses Philox counter
+ * (b, i, 0, 0); spec_verify_run_ex offsets b.
  * Pointers must be aligned to their element size; a 16-byte aligned logit
  * base with V * sizeof(element) a multiple of 16 takes the vector-load path
  * for every row. Rows b*(K+1)+i beyond i = k_b are never read.
@@ -140,6 +151,22 @@ int spec_verify_run(spec_verify_ctx* ctx, const void* target_logits,
                     const int32_t* budgets, int B, int K, float temperature,
                     uint64_t seed, int32_t* out_tokens, int32_t* out_num_accepted,
                     float* out_p_draft, float* out_q_draft, void* stream);
+
+/*
+ * spec_verify_run_ex -- spec_verify_run on a slice of a larger batch: row b
+ * of the tensors is request request_base + b of the whole batch, and its
+ * Philox counters are (request_base + b, i, 0, 0). Requests are independent,
+ * so calls over disjoint slices with their own bases give the outputs of one
+ * call over the whole batch, bit for bit (how the batch would be split across
+ * GPUs, each taking a contiguous range of requests). Arguments as in
+ * spec_verify_run; 0 <= request_base <= 2^32 - 1 - B, else SV_ERR_ARG.
+ */
+int spec_verify_run_ex(spec_verify_ctx* ctx, const void* target_logits,
+                       const void* draft_logits, const int32_t* draft_tokens,
+                       const int32_t* budgets, int B, int K, float temperature,
+                       uint64_t seed, int64_t request_base, int32_t* out_tokens,
+                       int32_t* out_num_accepted, float* out_p_draft,
+                       float* out_q_draft, void* stream);
 
 /*
  * spec_verify_check_args -- the host-side argument check of spec_verify_run

@@ -134,6 +134,28 @@ def inverse_cdf(mass: np.ndarray, u: float):
     return y, margin, total
 
 
+def cdf_interval(mass: np.ndarray, y: int):
+    """Token y's interval [C(y-1)/R, C(y)/R) of the normalised running sum
+    that inverse_cdf draws from (empty when y has no mass)."""
+    total = float(np.sum(mass))
+    cdf = np.cumsum(mass)
+    lo = float(cdf[y - 1]) / total if y > 0 else 0.0
+    return lo, float(cdf[y]) / total
+
+
+def draw_mass(p_rows, q_rows, j: int, k: int) -> np.ndarray:
+    """The unnormalised mass of the draw at position j of a request with
+    budget k: the residual max(0, p_j - q_j) after a rejection (j < k), p_j
+    itself if rounding left that residual without mass, and p_k for the bonus
+    token (j == k)."""
+    if j < k:
+        mass = np.maximum(0.0, np.asarray(p_rows[j]) - np.asarray(q_rows[j]))
+        if np.any(mass > 0.0):
+            return mass
+        return np.asarray(p_rows[j], dtype=np.float64)
+    return np.asarray(p_rows[k], dtype=np.float64)
+
+
 @dataclass
 class Decision:
     """Outcome of verifying one request."""
@@ -168,14 +190,8 @@ def decide_sampled(p_rows, q_rows, drafted, u_acc, u_smp) -> Decision:
         margins.append(margin)
         accepted.append(bool(ok))
     j = next((i for i in range(k) if not accepted[i]), k)
-    if j < k:
-        mode = RESIDUAL
-        mass = np.maximum(0.0, np.asarray(p_rows[j]) - np.asarray(q_rows[j]))
-        if not np.any(mass > 0.0):          # rounding only: fall back to p_j
-            mass = np.asarray(p_rows[j], dtype=np.float64)
-    else:
-        mode = BONUS
-        mass = np.asarray(p_rows[k], dtype=np.float64)
+    mode = RESIDUAL if j < k else BONUS
+    mass = draw_mass(p_rows, q_rows, j, k)
     y, cdf_margin, total = inverse_cdf(mass, float(u_smp[j]))
     tokens = [int(t) for t in drafted[:j]] + [y]
     return Decision(n_accepted=j, tokens=tokens, mode=mode, p_x=p_x, q_x=q_x,
@@ -192,6 +208,14 @@ def decide_greedy(target_rows, drafted) -> Decision:
     j = next((i for i in range(k) if not accepted[i]), k)
     tokens = [int(t) for t in drafted[:j]] + [best[j]]
     return Decision(n_accepted=j, tokens=tokens, mode=GREEDY, accepted=accepted)
+
+
+def request_draw_mass(target_rows, draft_rows, j: int, k: int, temperature: float):
+    """The draw mass of position j of a request from its logits (sampled
+    mode): the rows' temperature softmax, then draw_mass."""
+    p_rows = [softmax_row(target_rows[i], temperature)[2] for i in range(k + 1)]
+    q_rows = [softmax_row(draft_rows[i], temperature)[2] for i in range(k)]
+    return draw_mass(p_rows, q_rows, j, k)
 
 
 def verify_request(b: int, target_rows, draft_rows, drafted, temperature: float,

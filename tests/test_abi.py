@@ -54,8 +54,7 @@ def test_strerror_covers_every_code():
 
 
 def test_chunk_count():
-    # A chunk is 256 lanes x 4 sixteen-byte loads: 8192 bf16 or 4096 fp32 values.
-    # a chunk is 960 lanes x 4 sixteen-byte groups: 30720 bf16 or 15360 fp32
+    # A chunk is 960 lanes x 4 sixteen-byte groups: 30720 bf16 or 15360 fp32 values.
     assert sb.spec_verify_chunks(151936, sb.SV_DTYPE_BF16) == 5
     assert sb.spec_verify_chunks(262144, sb.SV_DTYPE_BF16) == 9
     assert sb.spec_verify_chunks(151936, sb.SV_DTYPE_F32) == 10
@@ -298,3 +297,8 @@ def test_markov_draft_workspace_size():
     # reach memory.
     want = 2 * 4 * 512 + 128 * 512 * 8
     assert want <= n <= want + 3 * 255
+
+
+def test_run_ex_checks_context_and_request_base():
+    assert sb.spec_verify_run_ex(None, A, A, A, A, 8, 4, 1.0, 1, 0, A, A, None, None,
+                                 None) == sb.SV_ERR_STATE

@@ -32,7 +32,8 @@ from scipy import special, stats
 from draft_verify_sampling_spec_amd import HiddenVerify, binding
 from oracle import head as oh
 from oracle import hidden as ohid
-from tests.helpers import NEAR_TIE, PROB_RTOL, check_probabilities, compare_sampled, padded
+from tests.helpers import NEAR_TIE, PROB_RTOL, assert_sampled, check_probabilities, padded
+from oracle import verify as ov
 from workloads import make_hidden_inputs
 
 pytestmark = pytest.mark.gpu
@@ -134,11 +135,14 @@ def _assert_sampled(host, gpu, res, reqs, T, tag):
     assert not bad_q, (tag, "q_x", bad_q[:5])
     for n, kb in enumerate(budgets):
         assert np.all(np.isnan(p[reqs[n], kb:])) and np.all(np.isnan(q[reqs[n], kb:]))
-    excused, unexcused = compare_sampled(toks[reqs], nacc[reqs], res.decisions, K,
-                                         acc_window=acc_w, cdf_window=cdf_w)
-    _log(f"[{tag}] sampled requests={len(reqs)} excused near-ties={excused} "
-         f"unexcused={len(unexcused)}")
-    assert not unexcused, (tag, unexcused[:5])
+    def mass_fn(n):
+        b, k = int(reqs[n]), int(budgets[n])
+        zt = oh.logits(ohid.decode_states(host.th[b, : k + 1]), host.w64)
+        zd = oh.logits(ohid.decode_states(host.dh[b, :k]), host.w64)
+        return ov.request_draw_mass(zt, zd, res.decisions[n].n_accepted, k, T)
+
+    assert_sampled(tag, toks[reqs], nacc[reqs], res.decisions, K, host.tokens[reqs], mass_fn,
+                   log=_log, acc_window=acc_w, cdf_window=cdf_w)
 
 
 def _check(inp, T, seed, tag, reqs=None, gpu=None):

@@ -12,7 +12,7 @@ import torch
 from draft_verify_sampling_spec_amd import SpecVerify, schedule_budgets
 from oracle import schedule as osch
 from oracle import verify as ov
-from tests.helpers import compare_sampled, to_oracle
+from tests.helpers import assert_sampled, logits_mass_fn, to_oracle
 from workloads import make_confidences, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -106,7 +106,8 @@ def test_scheduled_budgets_drive_verification_on_one_stream():
         tok = inp["tokens"][b].numpy().copy()
         ref.append(ov.verify_request(b, ov.as_f64_rows(zt, fmt)[: k_ref[b] + 1],
                                      ov.as_f64_rows(zd, fmt)[: k_ref[b]], tok[: k_ref[b]], 1.0, 123))
-    excused, unexcused = compare_sampled(toks.cpu().numpy(), nacc.cpu().numpy(), ref, K)
-    assert not unexcused
+    assert_sampled("scheduled-budgets", toks.cpu().numpy(), nacc.cpu().numpy(), ref, K,
+                   inp["tokens"].numpy(),
+                   logits_mass_fn(inp["target"], inp["draft"], k_ref, np.arange(B), ref, 1.0))
     assert sv.status() == 0
     sv.close()
