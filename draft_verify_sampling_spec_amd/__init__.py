@@ -5,4 +5,4 @@ The hot path is the HIP library ``libspec_verify.so`` (C ABI in
 torch tensors. Build with ``python -m draft_verify_sampling_spec_amd.build``.
 """
 from .binding import (HiddenVerify, MarkovDraft, SpecVerify, head_stats, load,  # noqa: F401
-                      philox_words, schedule_budgets)
+                      philox_words, schedule_budgets, verify_noalloc)

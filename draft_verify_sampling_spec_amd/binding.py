@@ -27,6 +27,7 @@ SV_ERR_ALIGN = -4
 SV_ERR_HIP = -5
 SV_ERR_NOMEM = -6
 SV_ERR_STATE = -7
+SV_ERR_TOO_BIG = -8
 
 SV_DTYPE_F32 = 0
 SV_DTYPE_BF16 = 1
@@ -38,11 +39,13 @@ SV_FLAG_SYNC_TIMEOUT = 0x4
 SV_MAX_BATCH = 16384
 SV_MAX_K = 32
 SV_MAX_VOCAB = 1 << 20
+SV_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTED = (
     "spec_verify_init",
     "spec_verify_run",
     "spec_verify_run_ex",
+    "spec_verify_run_noalloc",
     "spec_verify_check_args",
     "spec_verify_status",
     "spec_verify_philox_words",
@@ -75,6 +78,10 @@ def _declare(lib):
     lib.spec_verify_run_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, ctypes.c_float,
                                        ctypes.c_uint64, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp]
     lib.spec_verify_run_ex.restype = _i
+    lib.spec_verify_run_noalloc.argtypes = [_i, _i, _vp, _vp, _vp, _vp, _i, _i, ctypes.c_float,
+                                            ctypes.c_uint64, ctypes.c_int64, _vp, _vp, _vp, _vp,
+                                            _vp, _vp]
+    lib.spec_verify_run_noalloc.restype = _i
     lib.spec_verify_check_args.argtypes = [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i,
                                            ctypes.c_float, _vp, _vp, _vp, _vp]
     lib.spec_verify_check_args.restype = _i
@@ -168,6 +175,16 @@ def spec_verify_run_ex(ctx, target, draft, tokens, budgets, B, K, temperature, s
                                      ctypes.c_float(temperature), ctypes.c_uint64(seed),
                                      ctypes.c_int64(request_base), out_tokens, out_num_accepted,
                                      out_p_draft, out_q_draft, stream)
+
+
+def spec_verify_run_noalloc(vocab, dtype, target, draft, tokens, budgets, B, K, temperature,
+                            seed, request_base, out_tokens, out_num_accepted, out_p_draft,
+                            out_q_draft, out_status, stream) -> int:
+    return load().spec_verify_run_noalloc(vocab, dtype, target, draft, tokens, budgets, B, K,
+                                          ctypes.c_float(temperature), ctypes.c_uint64(seed),
+                                          ctypes.c_int64(request_base), out_tokens,
+                                          out_num_accepted, out_p_draft, out_q_draft, out_status,
+                                          stream)
 
 
 def spec_verify_status(ctx):
@@ -320,6 +337,48 @@ class SpecVerify:
         rc, counts, total = spec_verify_timing_read(self._ctx)
         _check(rc, "spec_verify_timing_read")
         return counts, total
+
+
+def verify_noalloc(target, draft, tokens, budgets, temperature: float, seed: int,
+                   request_base: int = 0, out_tokens=None, out_num_accepted=None, out_p=None,
+                   out_q=None, out_status=None, stream=None):
+    """One verify call through the allocation-free entry point (the library's
+    static scratch; no context). Tensors as for ``SpecVerify.run``; outputs
+    not given are allocated here with torch (a caller that cannot allocate
+    passes them all). Returns (tokens, n_accepted, p_x, q_x, status [1])."""
+    if target.dim() != 3 or target.dtype not in _DTYPES:
+        raise ValueError("target logits must be a float32 or bfloat16 [B, K+1, V] tensor")
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    mats = [(target, target.dtype, (B, K + 1, V)), (tokens, torch.int32, (B, K)),
+            (budgets, torch.int32, (B,))]
+    if draft is not None:
+        mats.append((draft, target.dtype, (B, K, V)))
+    for t, dt, shape in mats:
+        if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"expected a contiguous {dt} tensor of shape {shape} on {dev}")
+    if out_tokens is None:
+        out_tokens = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    if out_num_accepted is None:
+        out_num_accepted = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_p is None:
+        out_p = torch.empty(B, K, dtype=torch.float32, device=dev)
+    if out_q is None:
+        out_q = torch.empty(B, K, dtype=torch.float32, device=dev)
+    if out_status is None:
+        out_status = torch.empty(1, dtype=torch.int32, device=dev)
+    s = stream.cuda_stream if stream is not None else _stream_handle(dev)
+    with torch.cuda.device(dev):
+        rc = spec_verify_run_noalloc(V, _DTYPES[target.dtype], target.data_ptr(),
+                                     None if draft is None else draft.data_ptr(),
+                                     tokens.data_ptr(), budgets.data_ptr(), B, K,
+                                     float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                                     int(request_base), out_tokens.data_ptr(),
+                                     out_num_accepted.data_ptr(), out_p.data_ptr(),
+                                     out_q.data_ptr(), out_status.data_ptr(), s)
+    _check(rc, "spec_verify_run_noalloc")
+    return out_tokens, out_num_accepted, out_p, out_q, out_status
 
 
 def philox_words(seed: int, B: int, P: int, device="cuda") -> torch.Tensor:

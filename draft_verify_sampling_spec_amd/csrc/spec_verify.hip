@@ -55,6 +55,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 #include <vector>
 
@@ -1708,6 +1709,38 @@ int run_batches(DeviceInfo& di, spec_verify_ctx* tctx, int vocab, int dtype, uns
     return r;
 }
 
+// ------------------------------------------------ allocation-free variant --
+
+// The allocation-free entry point's workspace: one static array per device
+// (every GPU the library runs on holds its own copy until the process ends).
+// In host code `scratch` names a host-side stand-in, never the device memory:
+// its device address is taken once per device with hipGetSymbolAddress and
+// only that address is used.
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+struct NoallocDevice {
+    bool ready;
+    unsigned char* ptr;            // device address of this device's `scratch`
+    DeviceInfo info;
+    unsigned calls;                // epochs of calls on this device's scratch
+};
+
+std::mutex g_noalloc_mu;
+NoallocDevice g_noalloc[kMaxDevices];
+
+// Zero the call-start counters of the scratch (a fill kernel rather than a
+// memset, so the call can be captured in a HIP graph) and the caller's
+// status word.
+__global__ void clear_words_kernel(unsigned* a, int na, unsigned* b, int nb, uint32_t* status) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    const int stride = gridDim.x * blockDim.x;
+    for (int i = t; i < na; i += stride) a[i] = 0u;
+    for (int i = t; i < nb; i += stride) b[i] = 0u;
+    if (t == 0 && status) *status = 0u;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1722,6 +1755,9 @@ const char* spec_verify_strerror(int code) {
         case SV_ERR_HIP: return "HIP runtime error";
         case SV_ERR_NOMEM: return "device workspace allocation failed";
         case SV_ERR_STATE: return "NULL or freed context";
+        case SV_ERR_TOO_BIG:
+            return "the call needs more workspace than the allocation-free entry point's "
+                   "static scratch holds";
         default: return "unknown status code";
     }
 }
@@ -1847,6 +1883,55 @@ int spec_verify_run(spec_verify_ctx* ctx, const void* target_logits, const void*
     return spec_verify_run_ex(ctx, target_logits, draft_logits, draft_tokens, budgets, B, K,
                               temperature, seed, 0, out_tokens, out_num_accepted, out_p_draft,
                               out_q_draft, stream);
+}
+
+int spec_verify_run_noalloc(int vocab, int dtype, const void* target_logits,
+                            const void* draft_logits, const int32_t* draft_tokens,
+                            const int32_t* budgets, int B, int K, float temperature,
+                            uint64_t seed, int64_t request_base, int32_t* out_tokens,
+                            int32_t* out_num_accepted, float* out_p_draft, float* out_q_draft,
+                            uint32_t* out_status, void* stream) {
+    const int mb = B < 1 ? 1 : (B > SV_MAX_BATCH ? SV_MAX_BATCH : B);
+    const int rc = spec_verify_check_args(mb, K < 0 ? 0 : K, vocab, dtype, target_logits,
+                                          draft_logits, draft_tokens, budgets, B, K,
+                                          temperature, out_tokens, out_num_accepted,
+                                          out_p_draft, out_q_draft);
+    if (rc != SV_OK) return rc;
+    if (request_base < 0 || request_base > (int64_t)0xFFFFFFFFll - B) return SV_ERR_ARG;
+    if (out_status && !aligned_to(out_status, 4)) return SV_ERR_ALIGN;
+    if (B == 0) return SV_OK;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SV_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return SV_ERR_ARG;
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    NoallocDevice& nd = g_noalloc[dev];
+    if (!nd.ready) {
+        // Once per device, with the device current: the device address of
+        // this device's copy of `scratch`.
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            return SV_ERR_HIP;
+        }
+        if (device_info(dev, nd.info) != SV_OK) return SV_ERR_HIP;
+        nd.ptr = static_cast<unsigned char*>(ptr);
+        nd.calls = 0;
+        nd.ready = true;
+    }
+    const int lb = B < kLaunchBatch ? B : kLaunchBatch;
+    const int C = chunks_for(vocab, dtype);
+    const WsLayout L = ws_layout(lb, K, C, lb < nd.info.cus ? lb : nd.info.cus);
+    if (L.total > (size_t)SV_NOALLOC_SCRATCH_BYTES) return SV_ERR_TOO_BIG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    unsigned* req = reinterpret_cast<unsigned*>(nd.ptr + L.req);
+    unsigned* dcnt = reinterpret_cast<unsigned*>(nd.ptr + L.dcnt);
+    hipLaunchKernelGGL(clear_words_kernel, dim3(8), dim3(256), 0, s, req,
+                       (int)((L.req_end - L.req) / 4), dcnt, (int)((L.dcnt_end - L.dcnt) / 4),
+                       out_status);
+    if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+    unsigned* status = out_status ? out_status : reinterpret_cast<unsigned*>(nd.ptr + L.status);
+    RunArgs a{target_logits, draft_logits, draft_tokens, budgets, B, K, temperature, seed,
+              (uint32_t)request_base, out_tokens, out_num_accepted, out_p_draft, out_q_draft};
+    return run_batches(nd.info, nullptr, vocab, dtype, nd.ptr, L, nd.calls, status, a, s);
 }
 
 int spec_verify_status(spec_verify_ctx* ctx, uint32_t* flags) {

@@ -73,7 +73,9 @@ enum sv_status {
     SV_ERR_ALIGN = -4,   /* a pointer is not aligned to its element size */
     SV_ERR_HIP = -5,     /* the HIP runtime reported an error */
     SV_ERR_NOMEM = -6,   /* device workspace allocation failed */
-    SV_ERR_STATE = -7    /* NULL or already freed context */
+    SV_ERR_STATE = -7,   /* NULL or already freed context */
+    SV_ERR_TOO_BIG = -8  /* spec_verify_run_noalloc: the call needs more
+                            workspace than its static scratch holds */
 };
 
 /* Bits of the device status word (spec_verify_status). */
@@ -90,6 +92,9 @@ enum sv_status {
 #define SV_MAX_BATCH 16384
 #define SV_MAX_K 32
 #define SV_MAX_VOCAB (1 << 20)
+
+/* Size of the static device scratch of spec_verify_run_noalloc (per GPU). */
+#define SV_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 /*
  * spec_verify_init -- create a context for one device and one problem shape
@@ -167,6 +172,36 @@ int spec_verify_run_ex(spec_verify_ctx* ctx, const void* target_logits,
                        uint64_t seed, int64_t request_base, int32_t* out_tokens,
                        int32_t* out_num_accepted, float* out_p_draft,
                        float* out_q_draft, void* stream);
+
+/*
+ * spec_verify_run_noalloc -- spec_verify_run_ex without a context, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation). It calls no
+ * hipMalloc or hipFree: its workspace is a static device array of
+ * SV_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds until the
+ * process ends. It runs on the current HIP device; vocab and dtype are given
+ * per call. Every call on one GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (on different streams, or from different threads) race
+ * and their outputs are undefined; calls in stream order are safe (each call
+ * clears the counters it needs with a fill kernel, no memset).
+ *   vocab, dtype  as in spec_verify_init.
+ *   out_status    uint32 [1] (device) or NULL: this call's SV_FLAG_BAD_BUDGET
+ *                 and SV_FLAG_BAD_TOKEN bits (written, not accumulated).
+ *   other arguments as in spec_verify_run_ex.
+ * Three launches: the fill kernel, the streaming pass and, in sampled mode,
+ * the draw pass.
+ * Errors (nothing enqueued): SV_ERR_NULL, SV_ERR_ARG, SV_ERR_DTYPE,
+ * SV_ERR_ALIGN; SV_ERR_TOO_BIG when the call's workspace (it grows with
+ * min(B, 8192) * (K + 1) and the vocabulary's chunk count) exceeds the
+ * static array, e.g. B = 512, K = 8, V = 151936 in bf16 or fp32 fits;
+ * SV_ERR_HIP if a launch fails.
+ */
+int spec_verify_run_noalloc(int vocab, int dtype, const void* target_logits,
+                            const void* draft_logits, const int32_t* draft_tokens,
+                            const int32_t* budgets, int B, int K, float temperature,
+                            uint64_t seed, int64_t request_base, int32_t* out_tokens,
+                            int32_t* out_num_accepted, float* out_p_draft,
+                            float* out_q_draft, uint32_t* out_status, void* stream);
 
 /*
  * spec_verify_check_args -- the host-side argument check of spec_verify_run

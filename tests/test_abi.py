@@ -48,7 +48,7 @@ def test_binding_constants_match_header():
 
 
 def test_strerror_covers_every_code():
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         assert sb.spec_verify_strerror(code) != "unknown status code"
     assert sb.spec_verify_strerror(42) == "unknown status code"
 
@@ -297,6 +297,37 @@ def test_markov_draft_workspace_size():
     # reach memory.
     want = 2 * 4 * 512 + 128 * 512 * 8
     assert want <= n <= want + 3 * 255
+
+
+def _noalloc(**kw):
+    args = dict(vocab=1000, dtype=sb.SV_DTYPE_BF16, target=A, draft=A, tokens=A, budgets=A, B=8,
+                K=4, temperature=1.0, seed=1, request_base=0, out_tokens=A, out_num_accepted=A,
+                out_p_draft=None, out_q_draft=None, out_status=None, stream=None)
+    args.update(kw)
+    return sb.spec_verify_run_noalloc(**args)
+
+
+@pytest.mark.parametrize("kw, code", [
+    (dict(B=-1), sb.SV_ERR_ARG),
+    (dict(B=sb.SV_MAX_BATCH + 1), sb.SV_ERR_ARG),
+    (dict(K=sb.SV_MAX_K + 1), sb.SV_ERR_ARG),
+    (dict(vocab=0), sb.SV_ERR_ARG),
+    (dict(dtype=5), sb.SV_ERR_DTYPE),
+    (dict(temperature=-1.0), sb.SV_ERR_ARG),
+    (dict(target=None), sb.SV_ERR_NULL),
+    (dict(draft=None), sb.SV_ERR_NULL),
+    (dict(target=A + 1), sb.SV_ERR_ALIGN),
+    (dict(out_status=A + 2), sb.SV_ERR_ALIGN),
+    (dict(request_base=-1), sb.SV_ERR_ARG),
+    (dict(request_base=2**32 - 8), sb.SV_ERR_ARG),   # the last request's counter would wrap
+])
+def test_noalloc_rejects_bad_arguments_before_any_device_call(kw, code):
+    assert _noalloc(**kw) == code
+
+
+def test_noalloc_empty_batch_is_a_no_op():
+    assert _noalloc(B=0, target=None, budgets=None, out_tokens=None,
+                    out_num_accepted=None) == sb.SV_OK
 
 
 def test_run_ex_checks_context_and_request_base():
