@@ -24,6 +24,9 @@ SOURCES = [SRC, os.path.join(PKG_DIR, "csrc", "budget_schedule.hip"),
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libspec_verify.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+# A test helper (not part of the library): a bounded kernel that holds CUs.
+TEST_SRC = os.path.join(ROOT, "tests", "occupy_kernel.hip")
+TEST_LIB_PATH = os.path.join(ROOT, "tests", "libsv_occupy.so")
 ARCH = "gfx950"
 
 
@@ -34,7 +37,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
 
 
-def compile_command(out: str = LIB_PATH) -> list:
+def compile_command(out: str = LIB_PATH, sources=None) -> list:
     return [
         hipcc(),
         f"--offload-arch={ARCH}",
@@ -49,15 +52,21 @@ def compile_command(out: str = LIB_PATH) -> list:
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall",
         "-I", INCLUDE,
-        *SOURCES,
+        *(SOURCES if sources is None else sources),
         "-o", out,
     ]
 
 
 def build_library(verbose: bool = True) -> str:
-    """Compile the library (always; the output is replaced atomically)."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = compile_command(tmp)
+    """Compile the library and the tests' helper (always; outputs are
+    replaced atomically)."""
+    if os.path.exists(TEST_SRC):
+        _compile(compile_command(TEST_LIB_PATH + ".tmp", [TEST_SRC]), TEST_LIB_PATH, verbose)
+    return _compile(compile_command(LIB_PATH + ".tmp"), LIB_PATH, verbose)
+
+
+def _compile(cmd, out, verbose):
+    tmp = out + ".tmp"
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -69,8 +78,8 @@ def build_library(verbose: bool = True) -> str:
         lines = [l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l]
         if any(l.strip() for l in lines):
             sys.stderr.write("\n".join(lines) + "\n")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

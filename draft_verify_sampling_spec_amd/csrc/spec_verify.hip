@@ -15,24 +15,27 @@
 //    i. Every chunk has the same size (960 data lanes x 4 sixteen-byte loads
 //    per row). Units are numbered request-major, position-major, chunk-minor,
 //    so the C chunks of one position (a "team") are consecutive.
-//  * Streaming pass (verify_kernel): the grid is exactly the resident
-//    workgroups; workgroup w takes units w, w + G, w + 2G, ... (G = grid size
-//    >= C, so two units of one workgroup never share a team). One workgroup
-//    of 16 waves per CU. Waves 1-15 stream data: 16-byte loads of a unit into
-//    registers, reduced per wave to the scaled max s = max(z) c and the sum
-//    of 2^(z c - s), c = log2(e)/T (sampled; one fused multiply-add and an
-//    exp2 per element), or (max, lowest index) (greedy), posted to LDS; the next
-//    unit's loads go out group by group as the reduction consumes the
-//    registers. They never wait on another workgroup. Wave 0 is the control
-//    wave: it plans the units a few rounds ahead, merges the waves'
-//    statistics and publishes the chunk's record; the two kinds of waves
-//    exchange tagged LDS messages, with no workgroup barrier in the loop.
-//  * Every record word carries the call's epoch, so a record is complete when
-//    all its words carry it. The workgroup holding chunk 0 of a team reads
-//    the team's C records once complete (a poll issued one round later, so
-//    its latency overlaps the next unit) and decides: greedy, the row's
-//    first argmax (the team completing last for a request writes its
-//    outputs); sampled, p(x), q(x), the accept test and the decision word.
+//  * Streaming pass (verify_kernel): one workgroup of 16 waves per CU, grid =
+//    the resident workgroups. Units are handed out dynamically: the first
+//    rounds of workgroup w take units w, w + G, ..., later ones the values of
+//    a device-scope counter, so faster workgroups take more units and the C
+//    units of a team are taken, and finish, close together. Waves 1-15
+//    stream data: 16-byte loads of a unit into registers, reduced per wave to
+//    the scaled max s = max(z) c and the sum of 2^(z c - s), c = log2(e)/T
+//    (sampled; one fused multiply-add and an exp2 per element), or (max,
+//    lowest index) (greedy), posted to LDS; the next unit's loads go out
+//    group by group as the reduction consumes the registers. They never wait
+//    on another workgroup. Wave 0 is the control wave: it plans the units a
+//    few rounds ahead, merges the waves' statistics and publishes the chunk's
+//    record; the two kinds of waves exchange tagged LDS messages, with no
+//    workgroup barrier in the loop.
+//  * Every record word carries the call's epoch. After publishing a record
+//    that a decision needs (greedy: every unit; sampled: the units of
+//    drafted positions), the control wave adds one to its team's arrival
+//    counter; the workgroup whose addition completes the team reads the C
+//    records and decides: greedy, the row's first argmax (the team
+//    completing last for a request writes its outputs); sampled, p(x), q(x),
+//    the accept test and the decision word.
 //  * Draw pass (draw_kernel, sampled): one 8-wave workgroup per request, two
 //    per CU, finds the first rejection from the decision words, streams that
 //    position's target and drafter rows once for the residual masses of
@@ -40,11 +43,10 @@
 //    position picks its chunk from the records' p masses and streams that
 //    chunk's blocks the same way. It writes the request's outputs. Nothing in
 //    it waits on another workgroup.
-//  * Waiting (streaming pass): only the control wave waits on other
-//    workgroups, and only for an owed decision: the records of a team whose
-//    units all precede the unit it publishes next (G >= C), so by induction
-//    on the unit index every record gets written. Every wait is bounded
-//    (status flag on expiry) so the kernel drains.
+//  * No wave of either pass waits on another workgroup, so neither pass
+//    depends on which of its workgroups are resident at a time: a team is
+//    decided by whichever workgroup completes it, and the last workgroup to
+//    finish resets the schedule counter for the next call.
 //  * Synchronisation uses device-scope relaxed atomics (plus s_waitcnt where
 //    a counter orders earlier stores), never release/acquire fences: those
 //    write back and invalidate the whole L2.
@@ -78,16 +80,19 @@ constexpr int kMbox = 2;                       // result mailbox slots (rounds t
 constexpr int kPlanLead = 4;                   // rounds the control wave plans ahead (>= kMbox)
 constexpr int kPlanSlots = 8;                  // plan ring (> kPlanLead + 1)
 static_assert(kPlanLead >= kMbox && kPlanSlots > kPlanLead + 1, "plan ring too short");
-constexpr int kOwedSlots = 8;                  // chunk-0 units whose decision is owed
 constexpr int PL_END = 0, PL_UNIT = 1;
 constexpr int kBlocks = kG * kDataWaves;       // 64-group blocks (one 16-byte load per lane) in a chunk
 constexpr int kTeamWords = 32;                 // words per team record (128 bytes)
 constexpr int kReqStride = 16;                 // words between request counters (64 bytes)
-constexpr unsigned kSpinLimit = 1u << 20;      // bounded device-scope wait (~1 s)
 constexpr unsigned kLdsSpinLimit = 1u << 26;   // bounded LDS mailbox wait (~3 s)
 
 // Team record words.
+constexpr int TW_CNT = 0;       // arrivals of the team's units (reset by the unit that completes it)
 constexpr int TW_DEC = 2;       // 64-bit decision: (epoch << 32) | accepted (words 2-3)
+
+// Scheduling words (Params::sched, 64 bytes apart): the next unit to hand
+// out, and the workgroups that finished the streaming loop.
+constexpr int SC_NEXT = 0, SC_DONE = 16;
 
 // Unit record: 4 64-bit words.
 //   sampled: word f = (value bits << 32) | epoch for the fp32 values
@@ -115,6 +120,7 @@ struct Params {
     unsigned* team;                // [B*(K+1)][kTeamWords]
     unsigned* result;              // [B*(K+1)]: greedy: argmax of the team's row
     unsigned* req_count;           // [B][kReqStride]: greedy: teams completed
+    unsigned* sched;               // scheduling words SC_NEXT, SC_DONE
     unsigned* status;              // 1 word
     double* dmass;                 // draw pass split over workgroups: block masses [requests][C * kBlocks]
     unsigned* dcnt;                // draw pass split: slices finished per request, kReqStride apart
@@ -263,11 +269,6 @@ struct Shared {
     int st_idx[kMbox][kDataWaves];
     int st_tag[kMbox][kDataWaves];                   // round + 1
     int st_done[kMbox];                          // control wave: round + 1 of the slot it read last
-    // Control wave only: chunk-0 units whose decision is owed (a ring).
-    int ow_u[kOwedSlots], ow_b[kOwedSlots], ow_x[kOwedSlots];
-    // Control wave only: requests of the next 64 units of the sequence
-    // (decoded 64 at a time, one per lane).
-    int seq_b[64];
     // Set once a bounded wait expired: every later wait returns at once.
     int abort_wait;
     // Prologue scratch under barriers: per-wave partial sums.
@@ -306,16 +307,116 @@ __device__ __forceinline__ void lds_wait(const Params& P, Shared& sh, int* tag, 
 
 // ------------------------------------------------------ wave reductions --
 
+// Whole-wave reductions on the VALU's data-parallel primitives (DPP): a
+// butterfly inside each quad (lane xor 1, xor 2), the row's half mirror and
+// mirror (the 8- and 16-lane groups), then two row broadcasts that carry
+// rows 0-2's results up so that lane 63 holds the whole wave's; one read of
+// lane 63 makes the result uniform. No LDS traffic and no cross-lane wait on
+// memory, unlike permutes through the LDS crossbar. The reduction order is
+// fixed, so every wave that reduces the same values gets the same result.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E;          // quad_perm [1,0,3,2], [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141, kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+// Lane's DPP source value under control CTRL; lanes of rows outside ROWS
+// keep `identity`.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp32(int v, int identity) {
+    return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dppf(float v, float identity) {
+    return __int_as_float(dpp32<CTRL, ROWS>(__float_as_int(v), __float_as_int(identity)));
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ double dppd(double v) {                // identity 0.0
+    const long long b = __double_as_longlong(v);
+    const int lo = dpp32<CTRL, ROWS>((int)(unsigned)(unsigned long long)b, 0);
+    const int hi = dpp32<CTRL, ROWS>((int)(b >> 32), 0);
+    return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
+}
+
+__device__ __forceinline__ float lane63f(float v) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ double lane63d(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)(unsigned)(unsigned long long)b, 63);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), 63);
+    return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
+    const float ni = -INFINITY;
+    v = fmaxf(v, dppf<kDppXor1>(v, ni));
+    v = fmaxf(v, dppf<kDppXor2>(v, ni));
+    v = fmaxf(v, dppf<kDppHalfMirror>(v, ni));
+    v = fmaxf(v, dppf<kDppMirror>(v, ni));
+    v = fmaxf(v, dppf<kDppBcast15, 0xA>(v, ni));
+    v = fmaxf(v, dppf<kDppBcast31, 0xC>(v, ni));
+    return lane63f(v);
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+    v += dppd<kDppXor1>(v);
+    v += dppd<kDppXor2>(v);
+    v += dppd<kDppHalfMirror>(v);
+    v += dppd<kDppMirror>(v);
+    v += dppd<kDppBcast15, 0xA>(v);
+    v += dppd<kDppBcast31, 0xC>(v);
+    return lane63d(v);
+}
+
+// The same reductions through the LDS crossbar (permutes). Waves whose
+// bottleneck is the VALU (the streaming pass's data waves, the draw pass)
+// use these: the permutes run on the otherwise idle LDS unit.
+__device__ __forceinline__ double wave_sum_xbar(double v) {
+    #pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_max_xbar(float v) {
     #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
     return v;
 }
 
-__device__ __forceinline__ double wave_sum(double v) {
+__device__ __forceinline__ bool better_arg(float v, int i, float bv, int bi);
+
+__device__ __forceinline__ void wave_argmax_xbar(float& bv, int& bi) {
     #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, 64);
+        const int oi = __shfl_xor(bi, off, 64);
+        if (better_arg(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+        }
+    }
+}
+
+// (value, index) of the largest value, lowest index among equal values, over
+// the wave (uniform result). Ties and the order of merging do not change it.
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
+    const float ni = -INFINITY;
+#define SV_ARG_STEP(CTRL, ROWS)                                                 \
+    {                                                                           \
+        const float ov = dppf<CTRL, ROWS>(bv, ni);                              \
+        const int oi = dpp32<CTRL, ROWS>(bi, INT_MAX);                          \
+        if (better_arg(ov, oi, bv, bi)) {                                       \
+            bv = ov;                                                            \
+            bi = oi;                                                            \
+        }                                                                       \
+    }
+    SV_ARG_STEP(kDppXor1, 0xF)
+    SV_ARG_STEP(kDppXor2, 0xF)
+    SV_ARG_STEP(kDppHalfMirror, 0xF)
+    SV_ARG_STEP(kDppMirror, 0xF)
+    SV_ARG_STEP(kDppBcast15, 0xA)
+    SV_ARG_STEP(kDppBcast31, 0xC)
+#undef SV_ARG_STEP
+    bv = lane63f(bv);
+    bi = __builtin_amdgcn_readlane(bi, 63);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave, in lane order.
@@ -474,20 +575,6 @@ __device__ __forceinline__ bool poll_complete(const Params& P, const TeamPoll& p
     return __ballot(!ok) == 0;
 }
 
-// Poll until complete (bounded).
-template <bool kGreedy>
-__device__ void poll_wait(const Params& P, Shared& sh, int tr, TeamPoll& pl) {
-    for (unsigned it = 0;; ++it) {
-        poll_issue<kGreedy>(P, tr, pl);
-        if (poll_complete<kGreedy>(P, pl)) break;
-        if (it >= kSpinLimit || lds_get(&sh.abort_wait)) {
-            if ((threadIdx.x & 63) == 0) give_up(P, sh);
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-    }
-}
-
 // Team-wide normalisers (identical in every workgroup that computes them:
 // same inputs, same lanes, same reduction order).
 struct TeamStats {
@@ -550,15 +637,7 @@ __device__ void decide_greedy(const Params& P, const TeamPoll& pl, int b, int i,
     for (int cc = lane + 64; cc < C; cc += 64) {
         take(ld64(rec + cc * kRecWords + R_MT), ld64(rec + cc * kRecWords + R_MD));
     }
-    #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oi = __shfl_xor(bi, off, 64);
-        if (better_arg(ov, oi, bv, bi)) {
-            bv = ov;
-            bi = oi;
-        }
-    }
+    wave_argmax(bv, bi);
     if (lane == 0) {
         const int best = bi == INT_MAX ? 0 : bi;      // an all -inf row: index 0
         bool accept = true;
@@ -584,16 +663,6 @@ struct Unit {
     int e0, n;     // chunk start and length (elements)
     bool has_d;    // drafted position in sampled mode: the drafter row is read too
 };
-
-// The request of unit u: largest b with off[b] <= u (binary search).
-__device__ __forceinline__ int request_of(const Params& P, const int* off, int u) {
-    int lo_b = 0, hi_b = P.B;
-    while (hi_b - lo_b > 1) {
-        const int mid = (lo_b + hi_b) >> 1;
-        if (off[mid] <= u) lo_b = mid; else hi_b = mid;
-    }
-    return lo_b;
-}
 
 // The coordinates of unit u of request b (two independent LDS reads; no
 // search). u < 0 gives the empty unit.
@@ -676,15 +745,7 @@ __device__ __forceinline__ void control_unit(const Params& P, Shared& sh, const 
         }
         order();
         if (lane == 0) lds_put(&sh.st_done[slot], r + 1);
-        #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float ov = __shfl_xor(bv, o, 64);
-            const int oi = __shfl_xor(bi, o, 64);
-            if (better_arg(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
+        wave_argmax(bv, bi);
         if (lane == 0) {
             st64(rec + R_MT, tagged(bv, ep));
             st64(rec + R_MD, ((unsigned long long)(unsigned)bi << 32) | ep);
@@ -771,136 +832,149 @@ __device__ __forceinline__ void owed_decide(const Params& P, const Owed& o, cons
 
 // -------------------------------------------------------------- planning --
 
-// Control wave state of the streaming loop (uniform).
-struct CtrlState {
-    int next_unit;          // next unit of this workgroup's sequence
-    int planned;            // rounds planned so far (plans 0 .. planned-1 exist)
-    int end_round;          // round planned as the end (INT_MAX: not yet)
-    int ow_head, ow_tail;   // owed ring: chunk-0 units whose team was incomplete when polled
-    int seq_n;              // units planned so far
-};
-
-// Control wave: write the plan of the next round: the next unit of the
-// workgroup's sequence, else the end.
-__device__ __forceinline__ void plan_next(const Params& P, Shared& sh, CtrlState& cs, const int* off,
-                                          int U) {
-    const int q = cs.planned++;
-    const int slot = q % kPlanSlots;
-    int kind;
-    if (cs.next_unit < U) {
-        kind = PL_UNIT;
-        if ((cs.seq_n & 63) == 0) {
-            // Requests of the next 64 units, one binary search per lane.
-            const int lane = threadIdx.x & 63;
-            const int u = cs.next_unit + lane * (int)gridDim.x;
-            sh.seq_b[lane] = u < U ? request_of(P, off, u) : 0;
-        }
-        if ((threadIdx.x & 63) == 0) {
-            sh.pl_u[slot] = cs.next_unit;
-            sh.pl_b[slot] = sh.seq_b[cs.seq_n & 63];
-        }
-        ++cs.seq_n;
-        cs.next_unit += gridDim.x;
-    } else {
-        kind = PL_END;
-        cs.end_round = q;
+// The request of unit u (off[b] <= u < off[b + 1]; every request has at
+// least C units, so the offsets increase strictly) by a 64-ary search over
+// the offsets in LDS. Control wave; uniform result.
+__device__ int request_of(const Params& P, const int* off, int u) {
+    const int lane = threadIdx.x & 63;
+    int lo = 0, n = P.B;                 // off[lo] <= u < off[lo + n]
+    while (n > 1) {
+        const int step = (n + 63) >> 6;
+        const bool le = lane * step < n && off[lo + lane * step] <= u;
+        const unsigned long long m = __ballot(le);            // lane 0 always holds
+        const int last = 63 - __clzll((long long)m);
+        lo += last * step;
+        n = min(step, n - last * step);
     }
+    return lo;
+}
+
+// Control wave: write the plan of data round q: unit u of the sequence, or
+// the end of the loop (u >= U).
+__device__ __forceinline__ void plan_round(const Params& P, Shared& sh, const int* off, int q,
+                                           int u, int U) {
+    const int slot = q % kPlanSlots;
+    const bool unit = u < U;
+    const int b = unit ? request_of(P, off, u) : 0;
     if ((threadIdx.x & 63) == 0) {
-        sh.pl_kind[slot] = kind;
+        sh.pl_u[slot] = u;
+        sh.pl_b[slot] = b;
+        sh.pl_kind[slot] = unit ? PL_UNIT : PL_END;
         order();
         lds_put(&sh.pl_tag[slot], q);
     }
 }
 
-// The control wave's loop. Every round issues its device-scope loads first,
-// does the mailbox work while they are in flight, then reads them:
-//  P. plan round r + kPlanLead (the data waves read it at the end of round
-//     r + kPlanLead - 1, by which time this write is always done);
-//  1. issue: the team records of the chunk-0 unit consumed last round and of
-//     the oldest owed one;
-//  2. the data waves' results of round r: the unit's statistics are merged
-//     and published (a chunk-0 unit is decided from next round on);
-//  3. read what step 1 loaded: decide complete teams (an incomplete one is
-//     owed).
-// After the last round, owed decisions are waited for. Nothing the data
-// waves do waits on a decision.
+// A team's arrival counter: every unit of a team that needs a decision adds
+// one after its record is visible; the unit whose addition completes the
+// team decides it and resets the counter.
+__device__ __forceinline__ unsigned* team_count(const Params& P, int tr) {
+    return P.team + (size_t)tr * kTeamWords + TW_CNT;
+}
+
+// A unit whose team decision may fall to this workgroup: its arrival was
+// counted (old = the counter's value before) and is decided once the
+// returned value shows it completed the team.
+struct Pending {
+    Owed o;
+    unsigned old;
+    bool valid;
+};
+
+// Control wave: decide team o (its C records are complete: this workgroup's
+// arrival completed the team). Greedy: argmax, decision, request completion.
+// Sampled: p(x), q(x), the accept decision and the decision word.
+template <typename E, bool kGreedy>
+__device__ void decide_team(const Params& P, Owed& o) {
+    TeamPoll pl;
+    owed_issue<E, kGreedy>(P, o, pl);
+    if (!poll_complete<kGreedy>(P, pl) && (threadIdx.x & 63) == 0) {
+        atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);       // cannot happen: records precede arrivals
+    }
+    owed_decide<kGreedy>(P, o, pl);
+    if ((threadIdx.x & 63) == 0) st32(team_count(P, o.u.tr), 0u);
+}
+
+// The control wave's loop. Units are handed out dynamically: the first
+// kPlanLead rounds of workgroup w take units w, w + G, w + 2G, ...; later
+// rounds take the values of a device-scope counter (from kPlanLead * G on),
+// one fetch in flight at a time, so a workgroup that runs faster takes more
+// units and the units of one team are taken, and finish, close together in
+// time. Every round:
+//  P. plan round r + kPlanLead from the fetched value, and fetch the next;
+//  1. the data waves' results of round r: the unit's statistics are merged
+//     and published;
+//  2. the arrival counted last round: if it completed its team, decide it;
+//  3. count this unit's arrival in its team (after its record is visible);
+//     the returned count is read next round.
+// No step waits on another workgroup: a team is decided by whichever
+// workgroup completes it, so the loop never depends on which workgroups are
+// resident. Nothing the data waves do waits on a decision.
 template <typename E, bool kGreedy, bool kVec>
 __device__ __forceinline__ void control_loop(const Params& P, Shared& sh, const int* off) {
     const int U = off[P.B];
-    CtrlState cs;
-    cs.next_unit = blockIdx.x;
-    cs.planned = 0;
-    cs.end_round = INT_MAX;
-    cs.ow_head = cs.ow_tail = 0;
-    cs.seq_n = 0;
-    for (int q = 0; q < kPlanLead && cs.end_round == INT_MAX; ++q) plan_next(P, sh, cs, off, U);
-    Owed fresh;                      // chunk-0 unit consumed last round, to decide now
-    fresh.u.u = -1;
-    TeamPoll pa, pb;
-    for (int r = 0; r < cs.end_round; ++r) {
+    const int G = (int)gridDim.x;
+    const int base = kPlanLead * G;
+    int planned = 0, end_round = INT_MAX;
+    for (int q = 0; q < kPlanLead && end_round == INT_MAX; ++q) {
+        const int u = (int)blockIdx.x + q * G;
+        plan_round(P, sh, off, planned++, u, U);
+        if (u >= U) end_round = q;
+    }
+    // Device-scope counters are fetched by lane 0 only; its value is made
+    // uniform where it is used (the wait for the atomic falls there).
+    const int lane = threadIdx.x & 63;
+    unsigned fetched = 0;
+    if (end_round == INT_MAX && lane == 0) fetched = add32(P.sched + SC_NEXT, 1u);
+    Pending pend;
+    pend.valid = false;
+    auto settle = [&]() __attribute__((always_inline)) {
+        if (pend.valid &&
+            (unsigned)__builtin_amdgcn_readfirstlane((int)pend.old) == (unsigned)(P.C - 1)) {
+            decide_team<E, kGreedy>(P, pend.o);
+        }
+        pend.valid = false;
+    };
+    for (int r = 0; r < end_round; ++r) {
         // P.
-        if (cs.end_round == INT_MAX && r + kPlanLead == cs.planned) plan_next(P, sh, cs, off, U);
+        if (end_round == INT_MAX && r + kPlanLead == planned) {
+            const long long u64 =
+                (long long)base + (unsigned)__builtin_amdgcn_readfirstlane((int)fetched);
+            const int u = u64 < U ? (int)u64 : U;
+            plan_round(P, sh, off, planned, u, U);
+            if (u >= U) {
+                end_round = planned;
+            } else if (lane == 0) {
+                fetched = add32(P.sched + SC_NEXT, 1u);
+            }
+            ++planned;
+        }
         // 1.
-        const bool have_a = fresh.u.u >= 0;
-        if (have_a) owed_issue<E, kGreedy>(P, fresh, pa);
-        Owed old;
-        old.u.u = -1;
-        if (cs.ow_head != cs.ow_tail) {
-            const int j = cs.ow_head % kOwedSlots;
-            old.u = unit_from(P, off, sh.ow_u[j], sh.ow_b[j], kGreedy);
-            old.x = sh.ow_x[j];
-            owed_issue<E, kGreedy>(P, old, pb);
-        }
+        const int slot = r % kPlanSlots;
+        const Unit cur = unit_from(P, off, sh.pl_u[slot], sh.pl_b[slot], kGreedy);
+        control_unit<E, kGreedy>(P, sh, cur, r);
         // 2.
-        Owed next;
-        next.u.u = -1;
-        {
-            const int slot = r % kPlanSlots;
-            const Unit cur = unit_from(P, off, sh.pl_u[slot], sh.pl_b[slot], kGreedy);
-            control_unit<E, kGreedy>(P, sh, cur, r);
-            if (cur.c == 0 && (kGreedy || cur.has_d)) {
-                next.u = cur;
-                next.x = kGreedy ? 0 : P.tokens[(size_t)cur.b * P.K + cur.i];
-            }
-        }
+        settle();
         // 3.
-        if (have_a) {
-            if (poll_complete<kGreedy>(P, pa)) {
-                owed_decide<kGreedy>(P, fresh, pa);
-            } else if (cs.ow_tail - cs.ow_head < kOwedSlots) {
-                const int j = cs.ow_tail++ % kOwedSlots;
-                if ((threadIdx.x & 63) == 0) {
-                    sh.ow_u[j] = fresh.u.u;
-                    sh.ow_b[j] = fresh.u.b;
-                    sh.ow_x[j] = fresh.x;
-                }
-            } else {
-                poll_wait<kGreedy>(P, sh, fresh.u.tr, pa);   // ring full: wait (rare)
-                owed_decide<kGreedy>(P, fresh, pa);
-            }
+        if (kGreedy || cur.has_d) {
+            pend.o.u = cur;
+            pend.o.x = kGreedy ? 0 : P.tokens[(size_t)cur.b * P.K + cur.i];
+            drain();                                   // the record is visible first
+            pend.old = 0;
+            if (lane == 0) pend.old = add32(team_count(P, cur.tr), 1u);
+            pend.valid = true;
         }
-        if (old.u.u >= 0 && poll_complete<kGreedy>(P, pb)) {
-            owed_decide<kGreedy>(P, old, pb);
-            ++cs.ow_head;
+    }
+    settle();
+    // The last workgroup to finish resets the schedule for the next call
+    // (every fetch of every workgroup precedes its count here).
+    drain();
+    if (lane == 0) {
+        const unsigned done = add32(P.sched + SC_DONE, 1u);
+        if (done == (unsigned)(G - 1)) {
+            st32(P.sched + SC_NEXT, 0u);
+            st32(P.sched + SC_DONE, 0u);
         }
-        fresh = next;
-    }
-    // Decisions still owed: wait for their records.
-    TeamPoll pl;
-    if (fresh.u.u >= 0) {
-        poll_wait<kGreedy>(P, sh, fresh.u.tr, pl);
-        owed_issue<E, kGreedy>(P, fresh, pl);
-        owed_decide<kGreedy>(P, fresh, pl);
-    }
-    while (cs.ow_head != cs.ow_tail) {
-        const int j = cs.ow_head % kOwedSlots;
-        Owed o;
-        o.u = unit_from(P, off, sh.ow_u[j], sh.ow_b[j], kGreedy);
-        o.x = sh.ow_x[j];
-        poll_wait<kGreedy>(P, sh, o.u.tr, pl);
-        owed_issue<E, kGreedy>(P, o, pl);
-        owed_decide<kGreedy>(P, o, pl);
-        ++cs.ow_head;
     }
 }
 
@@ -957,15 +1031,7 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
                 }
                 if (more) load_pair<E, kVec>(nw, dt, j, gt[j], gd[j]);
             }
-            #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                const float ov = __shfl_xor(bv, o, 64);
-                const int oi = __shfl_xor(bi, o, 64);
-                if (better_arg(ov, oi, bv, bi)) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
+            wave_argmax_xbar(bv, bi);
             post_mt = bv;
             post_idx = bi;
         } else {
@@ -985,8 +1051,8 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
                 asm volatile("" : "+v"(gt[j].x), "+v"(gt[j].y), "+v"(gt[j].z), "+v"(gt[j].w));
                 asm volatile("" : "+v"(gd[j].x), "+v"(gd[j].y), "+v"(gd[j].z), "+v"(gd[j].w));
             }
-            mt = wave_max(mt);
-            md = wave_max(md);
+            mt = wave_max_xbar(mt);
+            md = wave_max_xbar(md);
             // Exp pass, group by group; as soon as a group is consumed its
             // registers take the next unit's group (loads overlap the rest
             // of the pass).
@@ -1019,8 +1085,8 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
                 lt += e[0];
                 ld += f[0];
             }
-            post_a = wave_sum((double)lt);
-            post_b = wave_sum((double)ld);
+            post_a = wave_sum_xbar((double)lt);
+            post_b = wave_sum_xbar((double)ld);
             post_mt = smt;
             post_md = smd;
         }
@@ -1307,7 +1373,7 @@ void draw_kernel(Params P) {
                         float sg = 0.0f;
                         #pragma unroll
                         for (int kk = 0; kk < W; ++kk) sg += mass(gt[s], gd[s], kk, res);
-                        const double ws = wave_sum((double)sg);
+                        const double ws = wave_sum_xbar((double)sg);
                         if (lane == 0) {
                             blk[x - x0] = ws;
                             if (split) {
@@ -1464,11 +1530,14 @@ size_t draw_smem_bytes(int C) { return (size_t)C * kBlocks * sizeof(double); }
 // Byte offsets of the kernels' device workspace, for launches of up to
 // max_batch requests with up to max_k drafted positions and C chunks per row.
 // The draw pass splits a request over several workgroups only for batches of
-// at most split_reqs requests. Counters in [req, req_end) and [dcnt, dcnt_end)
-// must read zero when a call starts; every kernel that raises them leaves
-// them at zero when it completes.
+// at most split_reqs requests. The counters must read zero when a call
+// starts: the team arrival counters (word TW_CNT of each team record), the
+// words in [req, req_end) and [dcnt, dcnt_end), and the scheduling words at
+// status + 64; every kernel that raises one leaves it at zero when it
+// completes. The status word at `status` accumulates device-side flags.
 struct WsLayout {
     size_t rec, team, result, req, req_end, dmass, dcnt, dcnt_end, status, total;
+    size_t teams;
     int split_reqs;
 };
 
@@ -1494,6 +1563,7 @@ WsLayout ws_layout(int max_batch, int max_k, int C, int split_reqs) {
     L.status = o;
     o += 256;
     L.total = o;
+    L.teams = teams;
     L.split_reqs = split_reqs;
     return L;
 }
@@ -1655,6 +1725,7 @@ int run_batches(DeviceInfo& di, spec_verify_ctx* tctx, int vocab, int dtype, uns
     p.team = reinterpret_cast<unsigned*>(ws + L.team);
     p.result = reinterpret_cast<unsigned*>(ws + L.result);
     p.req_count = reinterpret_cast<unsigned*>(ws + L.req);
+    p.sched = reinterpret_cast<unsigned*>(ws + L.status + 64);
     p.status = status;
     p.dmass = reinterpret_cast<double*>(ws + L.dmass);
     p.dcnt = reinterpret_cast<unsigned*>(ws + L.dcnt);
@@ -1731,14 +1802,21 @@ std::mutex g_noalloc_mu;
 NoallocDevice g_noalloc[kMaxDevices];
 
 // Zero the call-start counters of the scratch (a fill kernel rather than a
-// memset, so the call can be captured in a HIP graph) and the caller's
-// status word.
-__global__ void clear_words_kernel(unsigned* a, int na, unsigned* b, int nb, uint32_t* status) {
+// memset, so the call can be captured in a HIP graph): the team arrival
+// counters (one word every kTeamWords), the request and draw-split counters,
+// the scheduling words, and the caller's status word.
+__global__ void clear_words_kernel(unsigned* team, int nteam, unsigned* a, int na, unsigned* b,
+                                   int nb, unsigned* sched, uint32_t* status) {
     const int t = blockIdx.x * blockDim.x + threadIdx.x;
     const int stride = gridDim.x * blockDim.x;
+    for (int i = t; i < nteam; i += stride) team[(size_t)i * kTeamWords + TW_CNT] = 0u;
     for (int i = t; i < na; i += stride) a[i] = 0u;
     for (int i = t; i < nb; i += stride) b[i] = 0u;
-    if (t == 0 && status) *status = 0u;
+    if (t == 0) {
+        sched[SC_NEXT] = 0u;
+        sched[SC_DONE] = 0u;
+        if (status) *status = 0u;
+    }
 }
 
 }  // namespace
@@ -1924,9 +2002,10 @@ int spec_verify_run_noalloc(int vocab, int dtype, const void* target_logits,
     hipStream_t s = static_cast<hipStream_t>(stream);
     unsigned* req = reinterpret_cast<unsigned*>(nd.ptr + L.req);
     unsigned* dcnt = reinterpret_cast<unsigned*>(nd.ptr + L.dcnt);
-    hipLaunchKernelGGL(clear_words_kernel, dim3(8), dim3(256), 0, s, req,
+    hipLaunchKernelGGL(clear_words_kernel, dim3(8), dim3(256), 0, s,
+                       reinterpret_cast<unsigned*>(nd.ptr + L.team), (int)L.teams, req,
                        (int)((L.req_end - L.req) / 4), dcnt, (int)((L.dcnt_end - L.dcnt) / 4),
-                       out_status);
+                       reinterpret_cast<unsigned*>(nd.ptr + L.status + 64), out_status);
     if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
     unsigned* status = out_status ? out_status : reinterpret_cast<unsigned*>(nd.ptr + L.status);
     RunArgs a{target_logits, draft_logits, draft_tokens, budgets, B, K, temperature, seed,

@@ -82,11 +82,12 @@ enum sv_status {
 #define SV_FLAG_BAD_BUDGET 0x1u /* a budget was outside [0, K]; it was clamped */
 #define SV_FLAG_BAD_TOKEN  0x2u /* a checked drafted token was outside [0, V);
                                    it was treated as rejected, its p and q as 0 */
-#define SV_FLAG_SYNC_TIMEOUT 0x4u /* a workgroup gave up waiting for the other
-                                   chunks of a row pair (bounded wait); the
-                                   outputs of that call are not valid. Only
-                                   possible if the device could not keep the
-                                   launch's workgroups resident. */
+#define SV_FLAG_SYNC_TIMEOUT 0x4u /* an internal consistency check failed (a
+                                   wave's bounded wait for another wave of its
+                                   own workgroup expired, or a decision was
+                                   read before it was final); the outputs of
+                                   that call are not valid. No wait depends on
+                                   other workgroups being resident. */
 
 /* Library limits. */
 #define SV_MAX_BATCH 16384

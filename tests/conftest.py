@@ -28,7 +28,7 @@ def gpu_lib():
 def pytest_sessionstart(session):
     """Build the HIP library once if this checkout has none yet."""
     from draft_verify_sampling_spec_amd import build
-    if not os.path.exists(build.LIB_PATH):
+    if not (os.path.exists(build.LIB_PATH) and os.path.exists(build.TEST_LIB_PATH)):
         build.build_library(verbose=False)
 
 

@@ -483,3 +483,74 @@ def test_tiny_temperature_reproduces_greedy():
     _assert_parity(inp, seed, greedy, _oracle(inp, seed, temperature=0.0), temperature=0.0,
                    tag="T0+-greedy")
     assert np.any(greedy[1] < K) and np.any(greedy[1] > 0)
+
+
+# ------------------------------------------------- partial residency ---
+
+def test_verify_while_another_stream_holds_half_the_cus():
+    """A verify call while a bounded kernel on another stream holds half of
+    the CUs (each of its workgroups takes a CU's whole LDS): the streaming
+    pass's workgroups cannot all be resident at once. No wave of the verify
+    kernels waits on another workgroup, so the calls complete, concurrently
+    with the other kernel, with the outputs of an unobstructed call and no
+    status flag."""
+    import ctypes
+    from draft_verify_sampling_spec_amd import build
+    helper = ctypes.CDLL(build.TEST_LIB_PATH)
+    helper.sv_test_occupy.argtypes = [ctypes.c_int, ctypes.c_uint, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    helper.sv_test_occupy.restype = ctypes.c_int
+    inp = make_inputs("ragged", device=DEV)
+    t, d, x, k = inp["target"], inp["draft"], inp["tokens"], inp["budgets"]
+    B, K1, V = t.shape
+    sv = SpecVerify(DEV, max_batch=B, max_k=K1 - 1, vocab=V, dtype=t.dtype)
+    seeds = [philox_seed(3, 900 + i) for i in range(4)]
+    modes = [0.8, 0.0, 0.8, 0.0]
+    free = []
+    for T, seed in zip(modes, seeds):
+        free.append([o.clone() for o in sv.run(t, d if T > 0 else None, x, k, T, seed)])
+    torch.cuda.synchronize()
+    cus = torch.cuda.get_device_properties(DEV).multi_processor_count
+    busy_out = torch.zeros(cus // 2, dtype=torch.int32, device=DEV)
+    # Streams go to the hardware queues in turn, so of four work streams at
+    # least one runs beside the other kernel rather than behind it.
+    busy = torch.cuda.Stream(DEV)
+    works = [torch.cuda.Stream(DEV) for _ in range(4)]
+    b0, b1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+    ends = [torch.cuda.Event(enable_timing=True) for _ in works]
+    # Everything that allocates or synchronises (contexts, outputs) comes
+    # first; one context per stream, since calls that overlap in time must
+    # not share one.
+    ctxs = [SpecVerify(DEV, max_batch=B, max_k=K1 - 1, vocab=V, dtype=t.dtype) for _ in works]
+    held = [[[torch.empty_like(o) for o in f] for f in free] for _ in works]
+    for c, outs in zip(ctxs, held):                 # first calls (launch queries) now
+        for (T, seed), o in zip(zip(modes, seeds), outs):
+            c.run(t, d if T > 0 else None, x, k, T, seed, out_tokens=o[0], out_num_accepted=o[1],
+                  out_p=o[2], out_q=o[3])
+    torch.cuda.synchronize()
+    for outs in held:
+        for o in outs:
+            for v in o:
+                v.fill_(-5)
+    b0.record(busy)
+    assert helper.sv_test_occupy(cus // 2, 30000, busy_out.data_ptr(), busy.cuda_stream) == 0
+    b1.record(busy)
+    for work, end, c, outs in zip(works, ends, ctxs, held):
+        for (T, seed), o in zip(zip(modes, seeds), outs):
+            c.run(t, d if T > 0 else None, x, k, T, seed, out_tokens=o[0], out_num_accepted=o[1],
+                  out_p=o[2], out_q=o[3], stream=work)
+        end.record(work)
+    torch.cuda.synchronize()
+    assert int(busy_out.sum()) == cus // 2
+    busy_ms = b0.elapsed_time(b1)
+    done_ms = [b0.elapsed_time(e) for e in ends]
+    _log(f"occupier: {busy_ms:.2f} ms; verify calls on four streams done after "
+         + ", ".join(f"{v:.2f}" for v in done_ms) + " ms")
+    assert min(done_ms) < busy_ms, "no call overlapped the other kernel"
+    for outs in held:
+        for a, b in zip(free, outs):
+            for n in range(4):
+                assert torch.equal(a[n].nan_to_num(-7.0), b[n].nan_to_num(-7.0)), n
+    for c in ctxs + [sv]:
+        assert c.status() == 0
+        c.close()
