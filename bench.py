@@ -6,17 +6,19 @@ Default workload: the heavy-load batch -- B=512 requests, K=8, budgets
 back to back with a fresh Philox seed per step, inputs resident in HBM.
 
 Prints one JSON line: verified draft tokens/s (sum of budgets per step over
-the step time); the roofline of the dominant kernel, the streaming pass
-(algorithmic HBM bytes per launch over its duration from the library's own
-per-pass HIP events, against the 8 TB/s HBM peak); the fp64 CPU oracle's rate
-on a bounded sample of the same workload; and, on the same batch shape, the
-verify-budget scheduler (per call, beside its oracle), the fused output
-head (TFLOP/s against the 2.5 PFLOP/s dense bf16 peak, beside its oracle), a
-whole verify step from hidden states through that head, and the drafter's
-low-rank Markov head over a drafted block (each per call, beside its oracle);
-the other synthetic workloads (Qwen3- and Gemma-shaped vocabularies, the
-ragged batch) and, as context, a plain read-only reduction over the same
-logits.
+the step time); the roofline of the whole verify call (algorithmic HBM bytes
+per call over the streaming pass's plus the draw pass's duration, from the
+library's own per-pass HIP events, against the 8 TB/s HBM peak), with the
+streaming pass's own figure beside it; the timed step's outputs against the
+fp64 CPU oracle on every request (near-ties excused and counted); the oracle
+as a CPU baseline on a pool of host processes (every workload's step); and,
+on the same batch shape, the verify-budget scheduler (per call, beside its
+oracle), the fused output head (TFLOP/s against the 2.5 PFLOP/s dense bf16
+peak, beside its oracle), a whole verify step from hidden states through that
+head, and the drafter's low-rank Markov head over a drafted block (each per
+call, beside its oracle); the other synthetic workloads (Qwen3- and
+Gemma-shaped vocabularies, the ragged batch) and, as context, a plain
+read-only reduction over the same logits.
 
   python bench.py [--steps K] [--warmup W] [--warmup-settle S] [--workload heavy]
                   [--no-cpu-baseline] [--verify-only]
@@ -61,9 +63,9 @@ def kernel_source_hash():
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def load_traffic(bytes_per_launch_expected):
-    """HBM traffic per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source."""
+def load_traffic():
+    """HBM traffic per launch of each pass and per call, from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -71,14 +73,19 @@ def load_traffic(bytes_per_launch_expected):
         return None
     if rec.get("kernel_source_sha256") != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    ks = rec.get("kernels", {})
+    stream = ks.get("streaming pass", {}).get("hbm_bytes_per_launch")
+    draw = ks.get("draw pass", {}).get("hbm_bytes_per_launch")
+    if stream is None or draw is None:
+        return None
+    return {"stream": stream, "draw": draw, "call": stream + draw}
 
 
-def cpu_baseline(inp, seeds, n_requests, min_seconds=10.0, max_seconds=30.0):
-    """The fp64 oracle, as it stands, on the first n_requests of the batch,
-    repeated with fresh Philox seeds until about min_seconds of CPU work
-    (never starting a pass after max_seconds). Returns (tokens/s, seconds,
-    passes)."""
+def cpu_baseline(inp, seeds, n_requests, min_seconds=5.0, max_seconds=15.0):
+    """The fp64 oracle, as it stands, in this one process on the first
+    n_requests of the batch, repeated with fresh Philox seeds until about
+    min_seconds of CPU work (never starting a pass after max_seconds).
+    Returns (tokens/s, seconds, passes)."""
     import numpy as np
     import torch
     from oracle import verify as ov
@@ -107,6 +114,141 @@ def cpu_baseline(inp, seeds, n_requests, min_seconds=10.0, max_seconds=30.0):
             break
     dt = time.perf_counter() - t0
     return verified / dt, dt, passes
+
+
+# ------------------------------------------------------- oracle on a pool ---
+
+def cpu_workers():
+    """Worker processes for the oracle pool: the host cores this process may
+    run on, at most 16 (the CPU share of one GPU on the benchmark hosts)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+_WORKER_MAPS = {}
+
+
+def _worker_array(path, shape, dtype):
+    import numpy as np
+    key = (path, tuple(shape), dtype)
+    if key not in _WORKER_MAPS:
+        _WORKER_MAPS[key] = np.memmap(path, dtype=dtype, mode="r", shape=tuple(shape))
+    return _WORKER_MAPS[key]
+
+
+def _oracle_task(args):
+    """Pool worker: the oracle on requests [b0, b1) of a stored batch."""
+    desc, T, seed, b0, b1 = args
+    from oracle import verify as ov
+    target = _worker_array(*desc["target"])
+    draft = _worker_array(*desc["draft"]) if desc["draft"] else None
+    tokens = _worker_array(*desc["tokens"])
+    budgets = _worker_array(*desc["budgets"])
+    fmt = desc["fmt"]
+    out = []
+    for b in range(b0, b1):
+        k = int(budgets[b])
+        zt = ov.as_f64_rows(target[b, : k + 1], fmt)
+        zd = ov.as_f64_rows(draft[b, :k], fmt) if T > 0 else None
+        out.append(ov.verify_request(b, zt, zd, tokens[b, :k], T, seed))
+    return out
+
+
+class OraclePool:
+    """The fp64 oracle, unchanged, run over the requests of a batch on a pool
+    of worker processes. The pool is forked before this process touches the
+    GPU; batches reach the workers as files they map read-only (the exact
+    bytes the GPU was given), so nothing large is pickled."""
+
+    def __init__(self, workers):
+        import multiprocessing as mp
+        import tempfile
+        self.workers = workers
+        self.pool = mp.get_context("fork").Pool(workers)
+        self.dir = tempfile.mkdtemp(prefix="sv_oracle_")
+        self.files = []
+
+    def _store(self, name, arr):
+        import numpy as np
+        path = os.path.join(self.dir, name)
+        mm = np.memmap(path, dtype=arr.dtype, mode="w+", shape=arr.shape)
+        mm[...] = arr
+        mm.flush()
+        del mm
+        self.files.append(path)
+        return (path, arr.shape, arr.dtype.str)
+
+    def store(self, name, inp):
+        """Copy a batch's tensors to the host files the workers read."""
+        import numpy as np
+        import torch
+
+        def host(x):
+            x = x.detach().cpu().contiguous()
+            if x.dtype == torch.bfloat16:
+                return x.view(torch.int16).numpy().view(np.uint16), "bf16"
+            return x.numpy(), "f32"
+        t, fmt = host(inp["target"])
+        d, _ = host(inp["draft"])
+        return {"target": self._store(name + ".t", t), "draft": self._store(name + ".d", d),
+                "tokens": self._store(name + ".x", inp["tokens"].cpu().numpy()),
+                "budgets": self._store(name + ".k", inp["budgets"].cpu().numpy()),
+                "fmt": fmt, "B": int(t.shape[0])}
+
+    def step(self, desc, T, seed):
+        """One verify step of the oracle over every request: (decisions in
+        request order, wall seconds)."""
+        B = desc["B"]
+        parts = max(1, min(B, 4 * self.workers))
+        cuts = [B * i // parts for i in range(parts + 1)]
+        tasks = [(desc, T, seed, cuts[i], cuts[i + 1]) for i in range(parts) if cuts[i] < cuts[i + 1]]
+        t0 = time.perf_counter()
+        res = self.pool.map(_oracle_task, tasks)
+        dt = time.perf_counter() - t0
+        return [d for part in res for d in part], dt
+
+    def close(self):
+        self.pool.terminate()
+        self.pool.join()
+        for f in self.files:
+            try:
+                os.remove(f)
+            except OSError:
+                pass
+        try:
+            os.rmdir(self.dir)
+        except OSError:
+            pass
+
+
+def near_ties_on_step(inp, decisions, gpu_out, T):
+    """The bench step's outputs against the oracle's decisions under the
+    parity bar (tests/helpers.py): excused near-ties, unexcused mismatches,
+    the smallest residual mass, and the largest relative error of p(x), q(x)."""
+    import numpy as np
+    from tests.helpers import PROB_FLOOR, compare_sampled, logits_mass_fn
+    toks, nacc, p, q = (x.cpu().numpy() for x in gpu_out)
+    budgets = inp["budgets"].cpu().numpy()
+    reqs = np.arange(len(budgets))
+    mass_fn = logits_mass_fn(inp["target"], inp["draft"], budgets, reqs, decisions, T)
+    cmp = compare_sampled(toks, nacc, decisions, inp["tokens"].shape[1],
+                          inp["tokens"].cpu().numpy(), mass_fn)
+    worst = 0.0
+    for n, d in enumerate(decisions):
+        for i, (po, qo) in enumerate(zip(d.p_x, d.q_x)):
+            for g, o in ((p[n, i], po), (q[n, i], qo)):
+                if o >= PROB_FLOOR:
+                    worst = max(worst, abs(float(g) - o) / o)
+    return {"requests": cmp.requests,
+            "excused_accept": sum(1 for e in cmp.excused if e[1] == "accept"),
+            "excused_sample": sum(1 for e in cmp.excused if e[1] == "sample"),
+            "unexcused": len(cmp.unexcused),
+            "min_residual_R": cmp.min_residual_R,
+            "max_rel_err_p_q": worst,
+            "band": 1e-6}
 
 
 def bench_scheduler(B, K, steps, seed=5):
@@ -464,6 +606,21 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
+    # The oracle's worker pool is forked here, before this process touches
+    # the GPU (torch is not imported yet).
+    pool = None
+    want_cpu = (not args.no_cpu_baseline and args.workload == "heavy" and args.copy_probe is None
+                and not args.markov_only)
+    if want_cpu:
+        pool = OraclePool(cpu_workers())
+    try:
+        run(args, pool)
+    finally:
+        if pool is not None:
+            pool.close()
+
+
+def run(args, pool):
     import torch
     from draft_verify_sampling_spec_amd import SpecVerify
     from workloads import make_inputs, philox_seed
@@ -560,11 +717,14 @@ def main():
 
     path_gbs = alg_bytes / (mean_kernel_ms * 1e-3) / 1e9
     stream_ms = pass_ms[0] / max(pass_counts[0], 1)
-    draw_ms = pass_ms[1] / pass_counts[1] if pass_counts[1] else None
-    # The streaming pass reads every logit row the method needs once: the
-    # algorithmic bytes are its bytes.
-    achieved = alg_bytes / (stream_ms * 1e-3) / 1e9
-    traffic = load_traffic(alg_bytes)
+    draw_ms = pass_ms[1] / pass_counts[1] if pass_counts[1] else 0.0
+    call_ms = stream_ms + draw_ms
+    # Roofline of the whole call (streaming pass + draw pass): the
+    # algorithmic bytes are read once by the streaming pass; the draw pass
+    # re-reads each first-rejected row pair, which is implementation cost.
+    achieved = alg_bytes / (call_ms * 1e-3) / 1e9
+    stream_achieved = alg_bytes / (stream_ms * 1e-3) / 1e9
+    traffic = load_traffic()
     result = {
         "metric": "verified draft tokens/s + achieved HBM GB/s (% peak), B=512 V=151936 bf16",
         "value": verified_per_step / (ms_per_step * 1e-3),
@@ -594,20 +754,62 @@ def main():
         "kernel_ms": {"mean": mean_kernel_ms, "median": kernel_ms[len(kernel_ms) // 2],
                       "p5": kernel_ms[int(0.05 * (len(kernel_ms) - 1))],
                       "p95": kernel_ms[int(0.95 * (len(kernel_ms) - 1))]},
-        "pass_ms": {"stream": stream_ms, "draw": draw_ms, "launches": pass_counts},
+        "pass_ms": {"stream": stream_ms, "draw": draw_ms if pass_counts[1] else None,
+                    "launches": pass_counts},
         "roofline": {
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic,
+            "traffic": traffic["call"] if traffic else None,
             "algorithmic_bytes_per_launch": alg_bytes,
-            "kernel": ("verify_kernel<bf16, sampled>" if not greedy else "verify_kernel<bf16, greedy>")
-                      + " (streaming pass)",
+            "kernel": ("verify call: verify_kernel (streaming pass) + draw_kernel (draw pass)"
+                       if not greedy else "verify call: verify_kernel (greedy, one pass)"),
+            "streaming_pass": {"kernel": "verify_kernel", "ms": stream_ms,
+                               "achieved": stream_achieved,
+                               "frac": stream_achieved / HBM_PEAK_GBS,
+                               "traffic": traffic["stream"] if traffic else None},
+            "draw_pass": None if greedy else {
+                "kernel": "draw_kernel", "ms": draw_ms,
+                "traffic": traffic["draw"] if traffic else None,
+                "note": "re-reads each first-rejected row pair (implementation bytes)"},
         },
         "cpu_baseline": None,
     }
+    if pool is not None and not greedy:
+        s0 = philox_seed(widx, 1_000_000)
+        gpu_out = sv.run(t, d, x, k, T, s0)
+        torch.cuda.synchronize()
+        log(f"[bench] oracle pool ({pool.workers} processes): heavy step")
+        desc = pool.store("heavy", inp)
+        decisions, dt0 = pool.step(desc, T, s0)
+        result["near_ties"] = near_ties_on_step(inp, decisions, gpu_out, T)
+        result["near_ties"]["seed"] = s0
+        if result["near_ties"]["unexcused"]:
+            log(f"[bench] PARITY: {result['near_ties']['unexcused']} unexcused mismatches")
+        heavy_s = [dt0] + [pool.step(desc, T, philox_seed(widx, 1_000_001 + i))[1]
+                           for i in range(2)]
+        cpu = {"heavy": sum(heavy_s) / len(heavy_s)}
+        for name in ("qwen3", "ragged", "gemma"):
+            other = make_inputs(name, device=dev)
+            cpu[name] = pool.step(pool.store(name, other), other["temperature"],
+                                  philox_seed(WORKLOAD_INDEX[name], 5))[1]
+            del other
+            torch.cuda.empty_cache()
+        single_rate, single_s, single_passes = cpu_baseline(
+            inp, [philox_seed(widx, 2_000_000 + i) for i in range(64)], min(args.cpu_requests, B))
+        result["cpu_baseline"] = {
+            "value": verified_per_step / cpu["heavy"], "unit": "verified draft tokens/s",
+            "cores": pool.workers, "kind": "oracle",
+            "sample": f"the whole heavy step ({B} requests) on {pool.workers} worker processes, "
+                      f"mean of 3 steps with fresh seeds; one step of each other workload",
+            "s_per_step": cpu,
+            "single_process": {"value": single_rate, "cores": 1,
+                               "sample": f"{single_passes} passes over the first "
+                                         f"{min(args.cpu_requests, B)} requests "
+                                         f"({single_s:.1f} s)"},
+        }
     if not greedy and not args.verify_only:
         log("[bench] budget scheduler")
         result["scheduler"] = bench_scheduler(B, K, args.steps)
@@ -625,17 +827,6 @@ def main():
         result["read_ceiling"] = read_ceiling(t, d)
         log("[bench] other workloads")
         result["workloads"] = bench_workloads()
-    if not args.no_cpu_baseline and not greedy and args.workload == "heavy":
-        n_req = min(args.cpu_requests, B)
-        log(f"[bench] cpu baseline: oracle on {n_req} requests")
-        rate, dt, passes = cpu_baseline(inp, [philox_seed(widx, 2_000_000 + i) for i in range(64)],
-                                        n_req)
-        result["cpu_baseline"] = {
-            "value": rate, "unit": "verified draft tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} passes over the first {n_req} of the {B} requests of the heavy "
-                      f"step, fresh seed per pass ({dt:.1f} s of fp64 NumPy, one process, "
-                      f"one thread)",
-        }
     print(json.dumps(result), flush=True)
     sv.close()
 
