@@ -1,11 +1,12 @@
 // budget_schedule.hip -- confidence-driven verify budgets for MI355X (gfx950).
 //
 // What is computed: "Speculative decoding becomes standard: DSpark and
-// multi-token drafters", section "What DSpark adds", paragraph 2 (a
-// confidence per drafted position: the chance the token survives
-// verification given that the earlier ones did; a scheduler that chooses
-// each request's verify length as a throughput problem over all requests,
-// shorter under heavy load), and the Analytics Vidhya DSpark page, section
+// multi-token drafters", section "What DSpark adds", paragraph 2 (each
+// drafted position has a confidence, read as its chance of acceptance once
+// every earlier position of the block was accepted; the verify window of
+// every request is sized jointly across the batch for accepted tokens per
+// unit of verification, and shrinks as load grows), and the Analytics
+// Vidhya DSpark page, section
 // "Gotchas and Issues" (a cutoff recomputed for every batch; verify only
 // what has positive expected value). Reading: verifying position k of
 // request b adds g[b, k] = prod_{l <= k} c[b, l] expected accepted tokens;

@@ -2,12 +2,12 @@
 // block, for MI355X (gfx950).
 //
 // What is computed: "Speculative decoding becomes standard: DSpark and
-// multi-token drafters", section "What DSpark adds", paragraph 1 (a parallel
-// backbone proposes a block of tokens and a small sequential head, a
-// low-rank Markov module of rank 256, models the dependencies between the
-// block's positions), and the "DSpark" finds page's list of the two
-// sequential structures (the Markov head uses only the previous token and a
-// low-rank matrix). Reading: drafted position i's logits are the backbone's
+// multi-token drafters", section "What DSpark adds", paragraph 1 (the block
+// comes from a parallel backbone, and a light sequential correction, a
+// factorised rank-256 Markov model over consecutive positions, keeps the
+// block consistent), and the "DSpark" finds page's comparison of its two
+// sequential structures (the deployed one conditions only on the preceding
+// token, through a low-rank matrix). Reading: drafted position i's logits are the backbone's
 // row plus row x_{i-1} of the factored transition matrix A Bm^T (A, Bm are
 // [V, r]); the row is stored as bf16 and the drafted token x_i is its first
 // argmax; x_{-1} is the last token already in each sequence.

@@ -3,7 +3,7 @@
 //
 // What is computed: "Speculative decoding becomes standard: DSpark and
 // multi-token drafters", section "What DSpark adds", paragraph 1 (the drafter
-// shares the frozen output head with the target, so both models' logits for
+// reuses the target's output projection unchanged, so both models' logits for
 // a position are that head applied to a hidden state), section "Why
 // draft-and-verify does not change the output", paragraphs 1 and 2 (keep
 // drafted tokens while the target agrees -- greedy: equal to its most likely

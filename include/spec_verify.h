@@ -259,13 +259,13 @@ int spec_verify_timing_read(spec_verify_ctx* ctx, int* counts, double* total_ms)
 /*
  * spec_budget_schedule -- per-request verify budgets from per-position
  * confidences ("Speculative decoding becomes standard: DSpark and
- * multi-token drafters", section "What DSpark adds", paragraph 2: a
- * confidence head gives each drafted position's chance of surviving
- * verification given that the earlier ones did, and a scheduler chooses each
- * request's verify length across all requests, shorter under heavy load; the
- * Analytics Vidhya DSpark page, section "Gotchas and Issues": the cutoff is
- * recomputed every batch and only what has positive expected value is
- * verified). Stream-ordered, no host sync, no context and no workspace.
+ * multi-token drafters", section "What DSpark adds", paragraph 2: each
+ * drafted position has a confidence, read as its chance of acceptance once
+ * every earlier position of the block was accepted, and verify windows are
+ * sized jointly over the batch, shrinking as load grows; the Analytics
+ * Vidhya DSpark page, section "Gotchas and Issues": the cut is set afresh
+ * for every batch, and a position is verified only if it is expected to
+ * pay off). Stream-ordered, no host sync, no context and no workspace.
  *   confidences  float [B, K] row-major (device): c[b, i] for drafted
  *                position i of request b. NaN and negatives read as 0,
  *                values above 1 as 1.
@@ -291,7 +291,7 @@ int spec_budget_schedule(const float* confidences, int B, int K, int n_total, fl
  * spec_head_stats -- row statistics of the shared output head, computed on
  * the matrix cores without writing the logits ("Speculative decoding becomes
  * standard: DSpark and multi-token drafters", section "What DSpark adds",
- * paragraph 1: the drafter shares the frozen output head with the target;
+ * paragraph 1: the drafter reuses the target's output projection unchanged;
  * section "Why draft-and-verify does not change the output", paragraphs 1
  * and 2: a verify step needs each scored row's most likely token, or p(x)
  * and q(x) of the drafted token). Stream-ordered, no host sync.
@@ -329,8 +329,8 @@ size_t spec_head_workspace_bytes(int R, int V);
  * output head: the outputs of spec_verify_run on the logits z = h W^T,
  * without writing the logits of the scored rows anywhere ("Speculative
  * decoding becomes standard: DSpark and multi-token drafters", section "What
- * DSpark adds", paragraph 1: the drafter shares the frozen output head with
- * the target; section "Why draft-and-verify does not change the output",
+ * DSpark adds", paragraph 1: the drafter reuses the target's output
+ * projection unchanged; section "Why draft-and-verify does not change the output",
  * paragraphs 1 and 2: the greedy and sampled rules; section "What DSpark
  * adds", paragraph 2: per-request budgets). Logits are fp32 accumulations of
  * exact bf16 products; p and q, the accept test, the Philox counters and the
@@ -377,10 +377,11 @@ size_t spec_verify_hidden_workspace_bytes(int B, int K, int V);
 /*
  * spec_markov_draft -- the drafter's low-rank Markov head over a block of K
  * drafted positions ("Speculative decoding becomes standard: DSpark and
- * multi-token drafters", section "What DSpark adds", paragraph 1: a parallel
- * backbone proposes the block and a rank-256 Markov module models the
- * dependencies between its positions; "DSpark" (finds page): the Markov head
- * uses only the previous token and a low-rank matrix). For i = 0..K-1 in
+ * multi-token drafters", section "What DSpark adds", paragraph 1: the block
+ * comes from a parallel backbone and a factorised rank-256 Markov model over
+ * consecutive positions corrects it; "DSpark" (finds page): the deployed
+ * sequential structure conditions only on the preceding token, through a
+ * low-rank matrix). For i = 0..K-1 in
  * order: z_i = base_i + A[x_{i-1}] Bm^T, the bias an fp32 sum of exact bf16
  * products, the sum formed in fp32 and rounded once to bf16 (to nearest,
  * ties to even) and stored; x_i = the first (lowest index) argmax of the

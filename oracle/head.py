@@ -7,10 +7,10 @@ code with the HIP library and the library never calls it.
 Sources (the pages' own titles and sections):
 
 * "Speculative decoding becomes standard: DSpark and multi-token drafters",
-  section "What DSpark adds", paragraph 1: the drafter shares the frozen
-  embedding and output head with the target, so the target's and the
-  drafter's logits for a position are both the shared head applied to a
-  hidden state.
+  section "What DSpark adds", paragraph 1: the drafter reuses the target's
+  embedding and output projection unchanged, so at a given position both
+  models' logits are that one projection applied to each model's hidden
+  state.
 * Same page, section "Why draft-and-verify does not change the output",
   paragraphs 1 and 2: verification needs, per scored position, the target's
   most likely token (greedy) or the probabilities p(x) and q(x) of the drafted

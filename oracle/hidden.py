@@ -8,10 +8,10 @@ code with the HIP library and the library never calls it.
 Sources (the pages' own titles and sections):
 
 * "Speculative decoding becomes standard: DSpark and multi-token drafters",
-  section "What DSpark adds", paragraph 1: the drafter shares the frozen
-  embedding and output head with the target, so the target's and the
-  drafter's logits for a drafted position are the one head applied to each
-  model's hidden state for that position.
+  section "What DSpark adds", paragraph 1: the drafter reuses the target's
+  embedding and output projection unchanged, so at a drafted position both
+  models' logits are that one projection applied to each model's own hidden
+  state.
 * Same page, section "Why draft-and-verify does not change the output",
   paragraphs 1 and 2: the greedy and the sampled verification rules, which
   ``oracle.verify`` implements on logits.

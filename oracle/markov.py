@@ -7,13 +7,13 @@ code with the HIP library and the library never calls it.
 Sources (the pages' own titles and sections):
 
 * "Speculative decoding becomes standard: DSpark and multi-token drafters",
-  section "What DSpark adds", paragraph 1: the drafter's parallel backbone
-  proposes a block of tokens, and a small sequential head, a low-rank Markov
-  module of rank 256, models the dependencies between the block's positions
-  so that later tokens stay coherent.
-* "DSpark" (finds page), its list of the two sequential structures: the
-  Markov head uses only the previous token and a low-rank matrix, and it is
-  the one put into production.
+  section "What DSpark adds", paragraph 1: a block of tokens comes out of a
+  parallel backbone in one pass, and a light sequential correction -- a
+  factorised (rank 256) Markov model over consecutive positions -- keeps the
+  block's later tokens consistent with its earlier ones.
+* "DSpark" (finds page), where it compares two sequential structures: the
+  one deployed conditions on nothing but the immediately preceding token,
+  through a low-rank matrix.
 
 Reading (the pages give no formula): the Markov head is a first-order
 transition term over tokens in factored form. With tables A and Bm, both

@@ -7,12 +7,12 @@ code with the HIP library and the library never calls it.
 Sources (the pages' own titles and sections):
 
 * "Speculative decoding becomes standard: DSpark and multi-token drafters",
-  section "What DSpark adds", paragraph 2: a confidence head gives, for each
-  drafted position, the probability that the token survives verification
-  given that the earlier ones did; a scheduler chooses how many drafted
-  tokens of each request to verify by treating it as a throughput problem
-  over all requests on the engine, verifying long blocks (four to six
-  tokens) under moderate load and shortening them under heavy load.
+  section "What DSpark adds", paragraph 2: every drafted position carries a
+  confidence, read here as the chance it is accepted when all earlier
+  positions of its block were; the scheduler sizes each request's verify
+  window jointly across the whole batch, to get the most accepted tokens for
+  the verification it pays for -- windows of four to six under moderate
+  load, shorter ones as the engine fills up.
 * "DSpark" (the finds page): the confidence report lets the server spend more
   verification on the requests likely to pay off, scaled to how busy the
   GPUs are.

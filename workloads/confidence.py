@@ -1,5 +1,6 @@
-"""Seeded synthetic per-position confidences, standing in for a confidence
-head (a linear projection with a sigmoid, so values lie in (0, 1)).
+"""Seeded synthetic per-position confidences, standing in for the output of
+a confidence head (values in (0, 1), as a logistic function of a learned
+score would give).
 
 Request b is chat-like (lower confidence, falling faster along the block) or
 math/code-like; c[b, i] = sigmoid(a_b - s_b * i + 0.5 * eps[b, i]) with
