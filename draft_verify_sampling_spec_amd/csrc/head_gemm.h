@@ -19,14 +19,18 @@
 namespace svhead {
 
 // Where the hidden state of packed row r lives. Virtual rows [0, a_rows)
-// are rows of `a`, virtual rows from a_rows on are rows of `b`. `map` turns
-// packed rows into virtual rows (NULL: identity); a negative entry is a row
-// of zeros whose outputs nobody reads.
+// are rows of `a`, virtual rows [a_rows, a_rows + b_rows) rows of `b`.
+// `map` turns packed rows into virtual rows (NULL: identity); a negative
+// entry is a row of zeros whose outputs nobody reads. grouped8: the packed
+// rows 8i .. 8i + 7 never mix rows of a and rows of b (the many-row product
+// needs this when b has rows).
 struct HeadRows {
     const uint16_t* a;
     const uint16_t* b;
     const int32_t* map;
     int a_rows;
+    int b_rows;
+    bool grouped8;
 };
 
 // Scratch (bytes) for head_stats_launch with at most r_max rows.

@@ -621,15 +621,469 @@ void head_stats_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
     }
 }
 
+// ------------------------------------------- the product for many rows --
+
+// For many rows (a verify batch's scored rows) the product above is bound by
+// LDS traffic (64 FLOP per staged byte at 128 x 128 tiles) and re-streams
+// each workgroup's hidden-state tile from beyond the L2 for every vocabulary
+// tile. This kernel instead gives each workgroup a 256 x 256 tile, four
+// waves of 128 x 128 (16 blocks of 32 x 32, 256 accumulators per lane), and
+// stages k-steps of 64 through two LDS buffers filled by buffer-to-LDS
+// 16-byte loads (no registers in between). A k-step of 64 gives each row
+// one whole 128-byte line per load: the L2 serves whole lines at about
+// twice the rate of half lines, and a CU needs about 32 bytes a clock to
+// keep its matrix cores busy on this tile. Each step's 64 of k is
+// multiplied as four groups of 16; the workgroup synchronises before a
+// step's last group, so the load of the step after next goes out a whole
+// step before it is needed. (Buffer loads rather than global ones: with a
+// global load to LDS in flight the compiler must assume it may also count
+// as an LDS access and drains every LDS read before the first product; with
+// buffer loads it waits only for the fragments it uses. Their range check
+// also reads rows past the vocabulary and rows of zeros as zeros.) The
+// workgroups of one XCD work together on a 6 x 5 super-tile -- six row
+// tiles (a "band") by five vocabulary tiles -- and move it along the
+// vocabulary, so the operands one step needs are shared through that XCD's
+// L2, and each workgroup keeps one row tile while its running row
+// statistics stay in registers. One workgroup per CU; the schedule assumes
+// the dispatcher deals workgroups to the XCDs round-robin (correct under
+// any dealing, only slower).
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kMmThreads = 256;
+constexpr int kBandTiles = 6;                        // row tiles per band
+constexpr int kColTiles = 5;                         // vocabulary tiles per super-step
+constexpr int kXcds = 8;
+constexpr int kMmParts = kXcds * kColTiles;          // partials per row
+constexpr int kMmGrid = kXcds * 32;                  // one workgroup per CU
+constexpr int kMmOpBytes = kBM * kBK * 2;            // one operand of one stage (32 KB)
+constexpr int kMmLds = 2 * 2 * kMmOpBytes;           // two stages, both operands
+constexpr unsigned kMmOob = 0x80000000u;             // a buffer offset past every range below
+
+// Row and column counts for which a call takes this path (the workspace is
+// sized from these alone): at least one full band, and every XCD with a
+// super-step in every band.
+__host__ __device__ inline bool mm_shape(int r_max, int V) {
+    return r_max >= kBM * kBandTiles && (V + kBN - 1) / kBN >= kColTiles * kXcds;
+}
+
+// The whole condition: the shape, whole k-steps, rows of the two buffers in
+// separate groups of 8 (one load instruction reads one group through one
+// buffer descriptor), and byte offsets within each hidden-state buffer and
+// within a vocabulary tile that stay below kMmOob (32-bit buffer offsets).
+inline bool mm_path(const HeadRows& hr, int r_max, int H, int V) {
+    const unsigned long long row = 2ull * (unsigned long long)H;
+    return mm_shape(r_max, V) && H % kBK == 0 && row * kBN <= kMmOob / 2 &&
+           (hr.b_rows == 0 || hr.grouped8) &&
+           row * (unsigned long long)hr.a_rows <= kMmOob &&
+           row * (unsigned long long)hr.b_rows <= kMmOob;
+}
+
+// A raw buffer descriptor over n bytes from p (n <= 2^31): loads at byte
+// offsets past n read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mm_rsrc(const void* p, unsigned n) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
+// One 16-byte buffer-to-LDS load per lane: lane l's 16 bytes at byte
+// offset off of r land at lds + 16 l (lds is the same for the whole wave).
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, unsigned off,
+                                           unsigned char* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                             (int)off, 0, 0, 0);
+}
+
+// Wait until at most N of this wave's vector memory operations are
+// outstanding (loads complete in issue order), leaving the other counters.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// A workgroup barrier that waits for this wave's LDS reads but not for its
+// vector memory operations: the ring's direct-to-LDS loads are ordered by
+// wait_vm() before it, and the loads of later stages stay in flight across
+// it (a __syncthreads() fence would drain them). The clobber keeps the
+// compiler from moving memory operations across it.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <bool kSampled>
+__global__ __launch_bounds__(kMmThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
+                    const int* __restrict__ d_rows, int H, int V,
+                    const int32_t* __restrict__ tok, float c, HeadPart* __restrict__ part) {
+    extern __shared__ __align__(16) unsigned char mm_smem[];
+    __shared__ HeadPart xw[kBM];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // Wave (wm, wn): hidden rows wm * 128 .. + 128 of the row tile and
+    // vocabulary columns wn * 128 .. + 128 of the vocabulary tile. The
+    // product is formed transposed (head rows as the first operand), so in
+    // each 32 x 32 block a lane holds one hidden row (lane % 32) and 16 of
+    // the block's vocabulary columns: a lane's statistics cover 4 rows.
+    const int wm = wave >> 1, wn = wave & 1;
+    const int R = rows_now(r_max, d_rows);
+    const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
+    if (slot >= kBandTiles * kColTiles || R == 0) return;
+    const int rt_in = slot % kBandTiles, vt = slot / kBandTiles;
+    const int rtiles = (R + kBM - 1) / kBM;
+    const int nbands = (rtiles + kBandTiles - 1) / kBandTiles;
+    const int ntiles = (V + kBN - 1) / kBN;
+    const int spb = (ntiles + kColTiles - 1) / kColTiles;   // super-steps per band
+    const int total = nbands * spb;
+    const int nk = H / kBK;
+
+    // The workgroup's tiles, in order: super-steps stp = xcd, xcd + 8, ...
+    // Super-step stp covers row tile (stp / spb) * kBandTiles + rt_in and
+    // vocabulary tile (stp % spb) * kColTiles + vt; it is skipped when
+    // either lies past the end (every band that has this row tile has at
+    // least one vocabulary tile here, as the path needs kColTiles * kXcds
+    // vocabulary tiles).
+    auto row0_of = [&](int stp) { return (stp / spb * kBandTiles + rt_in) * kBM; };
+    auto v0_of = [&](int stp) { return ((stp % spb) * kColTiles + vt) * kBN; };
+    auto next_tile = [&](int stp) {
+        while (stp < total && (row0_of(stp) >= R || v0_of(stp) >= V)) stp += kXcds;
+        return stp < total ? stp : total;
+    };
+
+    // ---- loads: the hidden and head rows of one k-step into one of two
+    // LDS stages. Instruction j of wave w moves rows 8q .. 8q + 7 of an
+    // operand tile (q = 8w + j), one 16-byte piece per lane, 8 lanes a row.
+    // Row r's k-piece kc (of 8) sits at piece position kc ^ ((r / 2) % 8) of
+    // its 128-byte LDS row, so a fragment read (16 rows at one k-piece per
+    // 256-byte bank sweep) touches every bank once; the piece a lane moves
+    // depends on the parity of q (rows 8q .. 8q + 7 have (r / 2) % 8 =
+    // 4 (q % 2) + lane / 16).
+    const int lrow = lane >> 3;
+    const int lkc0 = (lane & 7) ^ ((lane >> 4) & 7);         // even q
+    const int lkc1 = (lane & 7) ^ ((4 + (lane >> 4)) & 7);   // odd q
+    const unsigned hrow_bytes = 2u * (unsigned)H;
+    const __amdgpu_buffer_rsrc_t rsrc_a = mm_rsrc(hr.a, hrow_bytes * (unsigned)hr.a_rows);
+    const __amdgpu_buffer_rsrc_t rsrc_b = mm_rsrc(hr.b, hrow_bytes * (unsigned)hr.b_rows);
+    __amdgpu_buffer_rsrc_t rsrc_w = rsrc_a;          // head rows of the loader's vocabulary tile
+    // Hidden rows of the loader's band: this lane's byte offsets (a row of
+    // zeros: out of range) and, in bit j (the same in every lane), whether
+    // instruction j's rows are rows of b. The rows of one instruction come
+    // from one buffer (the path's condition); a row of zeros reads zeros
+    // from either.
+    unsigned hoff[8];
+    unsigned hbu = 0;
+    int l_band = -1;
+    auto set_rows = [&](int r0) {
+        hbu = 0;
+        #pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            int r = r0 + 8 * (wave * 8 + j) + lrow;
+            r = r < R ? r : R - 1;
+            const int v = hr.map ? hr.map[r] : r;
+            const bool in_b = v >= hr.a_rows;
+            hoff[j] = v < 0 ? kMmOob
+                            : (unsigned)(in_b ? v - hr.a_rows : v) * hrow_bytes +
+                                  16u * (unsigned)((j & 1) ? lkc1 : lkc0);
+            hbu |= __builtin_amdgcn_ballot_w64(in_b) != 0 ? 1u << j : 0u;
+        }
+    };
+    // The loader walks the same steps as the product, ahead of it: l_stp,
+    // l_ks is the step whose loads go out next (l_stp == total: none).
+    int l_stp = total, l_ks = 0;
+    auto loader_at = [&](int stp) {
+        l_stp = stp;
+        l_ks = 0;
+        if (stp >= total) return;
+        const int v0 = v0_of(stp);
+        // Head rows v0 .. v0 + 255; rows past V read as zeros.
+        rsrc_w = mm_rsrc(w + (size_t)v0 * H, (unsigned)min(kBN, V - v0) * hrow_bytes);
+        const int band = stp / spb;
+        if (band != l_band) {
+            l_band = band;
+            set_rows(row0_of(stp));
+        }
+    };
+    // Load i (0 .. 15) of the loader's step into stage st: row group i / 2,
+    // head rows when i is odd.
+    auto load_one = [&](int st, int i) {
+        const int j = i >> 1, q = wave * 8 + j;
+        const unsigned k0b = 2u * (unsigned)(l_ks * kBK);
+        unsigned char* dst = mm_smem + st * 2 * kMmOpBytes + q * 1024;
+        if (i & 1) {
+            lds_load16(rsrc_w, (unsigned)(8 * q + lrow) * hrow_bytes +
+                                   16u * (unsigned)((j & 1) ? lkc1 : lkc0) + k0b,
+                       dst + kMmOpBytes);
+        } else {
+            lds_load16(((hbu >> j) & 1u) ? rsrc_b : rsrc_a, hoff[j] + k0b, dst);
+        }
+    };
+    auto loader_next = [&]() {
+        if (l_stp < total && ++l_ks == nk) loader_at(next_tile(l_stp + kXcds));
+    };
+
+    // ---- the product: 16 blocks of 32 x 32 per wave, fragments of one
+    // group (16 of k) at a time.
+    f32x16 acc[4][4];                                // [vocabulary block][hidden block]
+    struct Frags { bf16x8 h[4], w[4]; };
+    auto read_frags = [&](Frags& f, int st, int kk) {
+        const unsigned char* sh_h = mm_smem + st * 2 * kMmOpBytes;
+        const unsigned char* sh_w = sh_h + kMmOpBytes;
+        // Row r's piece 2kk + lane / 32 sits at position piece ^ ((r / 2) % 8);
+        // the blocks start at multiples of 32.
+        const int piece = ((2 * kk + (lane >> 5)) ^ ((lane >> 1) & 7)) << 4;
+        #pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            f.h[a] = *reinterpret_cast<const bf16x8*>(sh_h + (wm * 128 + 32 * a + (lane & 31)) * 128 + piece);
+            f.w[a] = *reinterpret_cast<const bf16x8*>(sh_w + (wn * 128 + 32 * a + (lane & 31)) * 128 + piece);
+        }
+    };
+    auto multiply = [&](const Frags& f) {
+        #pragma unroll
+        for (int b2 = 0; b2 < 4; ++b2)
+            #pragma unroll
+            for (int a = 0; a < 4; ++a)
+                acc[b2][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[b2], f.h[a], acc[b2][a], 0, 0, 0);
+    };
+    // The same 16 products with loads i0 .. i0 + 7 of the loader's step
+    // placed one after every second product, so the address unit takes them
+    // while the matrix cores work instead of stalling the wave. The loads go
+    // out even past the end of the stream (they then refill a stage nobody
+    // reads again): no branch among the products.
+    auto multiply_ld = [&](const Frags& f, int st, int i0) {
+        #pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int b2 = u >> 2, a = u & 3;
+            acc[b2][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.w[b2], f.h[a], acc[b2][a], 0, 0, 0);
+            if (u & 1) load_one(st, i0 + (u >> 1));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto zero_acc = [&]() {
+        #pragma unroll
+        for (int b2 = 0; b2 < 4; ++b2)
+            #pragma unroll
+            for (int a = 0; a < 4; ++a)
+                #pragma unroll
+                for (int i = 0; i < 16; ++i) acc[b2][a][i] = 0.0f;
+    };
+
+    // ---- running statistics of this lane's 4 hidden rows (a: row
+    // wm * 128 + 32 a + lane % 32 of the tile) over its columns so far: the
+    // maximum and the exp-sum under it (sampled) or the first argmax, and
+    // the drafted token's logit where this lane saw it.
+    float rm[4], rx[4], rz[4];
+    int xt[4];                                       // the rows' drafted tokens (-1: none)
+    auto start_band = [&](int r0) {
+        #pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            rm[a] = -INFINITY;
+            rx[a] = kSampled ? 0.0f : __int_as_float(INT_MAX);
+            rz[a] = NAN;
+            const int r = r0 + wm * 128 + 32 * a + (lane & 31);
+            xt[a] = (tok && r < R) ? tok[r] : -1;
+        }
+    };
+    // Fold the tile into the running statistics, one 32 x 32 block at a
+    // time. A lane's columns of a row go up with (vocabulary block, i):
+    // column cbase + 32 b2 + 8 (i / 4) + i % 4, so the first maximum wins.
+    // In the last vocabulary tile the columns past V (whose head rows read as
+    // zeros) read as -inf.
+    auto fold = [&](int v0) {
+        const int cbase = v0 + wn * 128 + 4 * (lane >> 5);
+        const bool full = v0 + kBN <= V;
+        #pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            // Where the drafted token lies among this lane's columns, if it
+            // does: block tb, element ti.
+            const unsigned o = (unsigned)(xt[a] - (v0 + wn * 128));
+            const bool hit = o < 128u && ((o >> 2) & 1u) == (unsigned)(lane >> 5);
+            const int tb = (int)(o >> 5), ti = (int)(((o >> 3) & 3u) * 4u + (o & 3u));
+            const bool any_hit = __builtin_amdgcn_ballot_w64(hit) != 0;
+            #pragma unroll
+            for (int b2 = 0; b2 < 4; ++b2) {
+                float z[16];
+                if (full) {
+                    #pragma unroll
+                    for (int i = 0; i < 16; ++i) z[i] = acc[b2][a][i];
+                } else {
+                    #pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        z[i] = cbase + 32 * b2 + 8 * (i >> 2) + (i & 3) < V ? acc[b2][a][i] : -INFINITY;
+                }
+                if (any_hit) {
+                    #pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (hit && tb == b2 && ti == i) rz[a] = z[i];
+                }
+                float mb = z[0];
+                #pragma unroll
+                for (int i = 1; i < 16; ++i) mb = fmaxf(mb, z[i]);
+                if (kSampled) {
+                    const float mn = fmaxf(rm[a], mb);
+                    const float mr = mn == -INFINITY ? 0.0f : mn;   // all -inf so far: terms stay 0
+                    float sum = 0.0f;
+                    #pragma unroll
+                    for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f((z[i] - mr) * c);
+                    rx[a] = rx[a] * __builtin_amdgcn_exp2f((rm[a] - mr) * c) + sum;
+                    rm[a] = mn;
+                } else if (mb > rm[a]) {
+                    // A new maximum in this block: its first column.
+                    int ib = 15;
+                    #pragma unroll
+                    for (int i = 14; i >= 0; --i) ib = z[i] == mb ? i : ib;
+                    rm[a] = mb;
+                    rx[a] = __int_as_float(cbase + 32 * b2 + 8 * (ib >> 2) + (ib & 3));
+                }
+            }
+        }
+    };
+
+    // The band's partial of this (XCD, column slot) for each of its rows:
+    // the lane pair holding a row (lane, lane ^ 32) merges, then the two
+    // waves with the same rows through LDS.
+    auto flush = [&](int r0) {
+        #pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            float m2 = __shfl_xor(rm[a], 32, 64), x2 = __shfl_xor(rx[a], 32, 64);
+            const float z2 = __shfl_xor(rz[a], 32, 64);
+            if (kSampled) {
+                merge_ms(rm[a], rx[a], m2, x2, c, true);
+            } else {
+                int ai = __float_as_int(rx[a]);
+                merge_arg(rm[a], ai, m2, __float_as_int(x2));
+                rx[a] = __int_as_float(ai);
+            }
+            if (rz[a] != rz[a]) rz[a] = z2;
+        }
+        const int rl0 = wm * 128 + (lane & 31);
+        if (wn == 1 && lane < 32) {
+            #pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                xw[rl0 + 32 * a] = HeadPart{rm[a], kSampled ? rx[a] : 0.0f, rz[a],
+                                            kSampled ? INT_MAX : __float_as_int(rx[a])};
+            }
+        }
+        __syncthreads();
+        if (wn == 0 && lane < 32) {
+            #pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const int rl = rl0 + 32 * a;
+                const HeadPart o = xw[rl];
+                HeadPart out;
+                out.m = rm[a];
+                out.zx = rz[a] == rz[a] ? rz[a] : o.zx;
+                if (kSampled) {
+                    out.s = rx[a];
+                    merge_ms(out.m, out.s, o.m, o.s, c, true);
+                    out.arg = INT_MAX;
+                } else {
+                    out.s = 0.0f;
+                    out.arg = __float_as_int(rx[a]);
+                    merge_arg(out.m, out.arg, o.m, o.arg);
+                }
+                if (r0 + rl < R) part[(size_t)(xcd * kColTiles + vt) * R + r0 + rl] = out;
+            }
+        }
+        __syncthreads();
+    };
+
+    // ---- the stream. Step g (tile c_stp, k-step ks) lives in stage g % 2.
+    // Its 64 of k are multiplied as four groups of 16, each group's
+    // fragments read while the previous group is multiplied. Before the
+    // last group the workgroup synchronises (step g + 1 has landed, and every
+    // wave has read step g into registers), reads step g + 1's first group
+    // and starts refilling stage g % 2 with step g + 2: half of its loads go
+    // out among the last group's products, half among the first group's
+    // products of step g + 1. Tiles follow one another without a pause; a
+    // tile's statistics are folded after its last product.
+    int c_stp = next_tile(xcd);
+    if (c_stp >= total) return;                      // (cannot happen: see above)
+    loader_at(c_stp);
+    #pragma unroll
+    for (int i = 0; i < 16; ++i) load_one(0, i);     // step 0, whole
+    loader_next();
+    int band = c_stp / spb;
+    start_band(row0_of(c_stp));
+    zero_acc();
+    __builtin_amdgcn_s_waitcnt(0);                   // step 0 and the tokens
+    ring_barrier();
+    Frags f0, f1;
+    read_frags(f0, 0, 0);
+    if (l_stp < total) {
+        #pragma unroll
+        for (int i = 0; i < 8; ++i) load_one(1, i);  // step 1, first half
+    }
+    int st = 0;
+    for (;;) {
+        // Steps 0 .. nk - 2 of the tile: the next step is in this tile.
+        for (int ks = 0; ks + 1 < nk; ++ks) {
+            read_frags(f1, st, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            multiply_ld(f0, st ^ 1, 8);              // step g + 1, second half
+            loader_next();                           // the loader moves on to step g + 2
+            read_frags(f0, st, 2);
+            __builtin_amdgcn_sched_barrier(0);
+            multiply(f1);
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(f1, st, 3);
+            __builtin_amdgcn_sched_barrier(0);
+            multiply(f0);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vm<0>();                            // this wave's loads of step g + 1
+            ring_barrier();                          // everyone's; step g read by all
+            read_frags(f0, st ^ 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            multiply_ld(f1, st, 0);                  // step g + 2, first half
+            __builtin_amdgcn_sched_barrier(0);
+            st ^= 1;
+        }
+        // The tile's last step; the next step, if any, starts the next tile
+        // (its first group is read after the fold). The synchronisation
+        // happens even when nothing follows: the loads among the last
+        // group's products then refill the stage this step used.
+        const int n_stp = next_tile(c_stp + kXcds);
+        const bool has_next = n_stp < total;
+        read_frags(f1, st, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        multiply_ld(f0, st ^ 1, 8);
+        loader_next();
+        read_frags(f0, st, 2);
+        __builtin_amdgcn_sched_barrier(0);
+        multiply(f1);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(f1, st, 3);
+        __builtin_amdgcn_sched_barrier(0);
+        multiply(f0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<0>();
+        ring_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        multiply_ld(f1, st, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        st ^= 1;
+        fold(v0_of(c_stp));
+        if (!has_next) break;
+        const int nb = n_stp / spb;
+        if (nb != band) {
+            flush(row0_of(c_stp));
+            band = nb;
+            start_band(row0_of(n_stp));
+        }
+        zero_acc();
+        read_frags(f0, st, 0);                       // the next tile's first group
+        c_stp = n_stp;
+    }
+    flush(row0_of(c_stp));                           // (drains the last loads too)
+}
+
 // Per row: merge the splits' partials (in split order) into the outputs.
 // Greedy partials carry the first argmax; sampled ones do not (INT_MAX), and
 // the sampled call reports none.
+// parts > 0: that many partials per row (the many-row product), else one
+// per vocabulary split of the product above.
 __global__ void head_merge_kernel(const HeadPart* __restrict__ part, int r_max,
                                   const int* __restrict__ d_rows, int V, float c, int sampled,
-                                  float* out_max, float* out_sum, float* out_z,
+                                  int parts, float* out_max, float* out_sum, float* out_z,
                                   int32_t* out_arg) {
     const int R = rows_now(r_max, d_rows);
-    const int splits = splits_for(R, V);
+    const int splits = parts > 0 ? parts : splits_for(R, V);
     const int r = blockIdx.x * blockDim.x + threadIdx.x;
     if (r >= R) return;
     float m = -INFINITY, s = 0.0f, z = NAN, bv = -INFINITY;
@@ -662,6 +1116,8 @@ size_t stats_workspace_bytes(int r_max, int V) {
     long long n = (long long)kResidentSlots * kTM;
     if (r_max > n) n = r_max;
     if (cap * r_max < n) n = cap * r_max;
+    // The many-row product (whatever H is): kMmParts partials per row.
+    if (mm_shape(r_max, V) && n < (long long)kMmParts * r_max) n = (long long)kMmParts * r_max;
     return (size_t)n * sizeof(HeadPart);
 }
 
@@ -673,6 +1129,31 @@ int head_stats_launch(const HeadRows& rows, const uint16_t* weight, int r_max,
     const bool sampled = temperature > 0.0f;
     const float c = sampled ? (float)(1.4426950408889634 / (double)temperature) : 0.0f;
     HeadPart* part = static_cast<HeadPart*>(workspace);
+    if (mm_path(rows, r_max, H, V)) {
+        // Many rows: the large-tile product, one workgroup per CU.
+        static bool attr_set = false;
+        if (!attr_set) {
+            if (hipFuncSetAttribute(reinterpret_cast<const void*>(&head_mm_kernel<true>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, kMmLds) != hipSuccess ||
+                hipFuncSetAttribute(reinterpret_cast<const void*>(&head_mm_kernel<false>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, kMmLds) != hipSuccess) {
+                return SV_ERR_HIP;
+            }
+            attr_set = true;
+        }
+        if (sampled) {
+            hipLaunchKernelGGL(head_mm_kernel<true>, dim3(kMmGrid), dim3(kMmThreads), kMmLds, s,
+                               rows, weight, r_max, d_rows, H, V, tokens, c, part);
+        } else {
+            hipLaunchKernelGGL(head_mm_kernel<false>, dim3(kMmGrid), dim3(kMmThreads), kMmLds, s,
+                               rows, weight, r_max, d_rows, H, V, tokens, c, part);
+        }
+        if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+        hipLaunchKernelGGL(head_merge_kernel, dim3((unsigned)((r_max + 255) / 256)), dim3(256), 0,
+                           s, part, r_max, d_rows, V, c, sampled ? 1 : 0, kMmParts, out_max,
+                           out_sum, out_z, out_arg);
+        return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+    }
     // One workgroup per item. With the count read on the device, the grid
     // covers every count up to r_max: up to 512 row tiles a count has at most
     // 512 items, beyond that one split, so no more items than r_max has.
@@ -689,7 +1170,7 @@ int head_stats_launch(const HeadRows& rows, const uint16_t* weight, int r_max,
     }
     if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
     hipLaunchKernelGGL(head_merge_kernel, dim3((unsigned)((r_max + 255) / 256)), dim3(256), 0, s,
-                       part, r_max, d_rows, V, c, sampled ? 1 : 0, out_max, out_sum, out_z,
+                       part, r_max, d_rows, V, c, sampled ? 1 : 0, 0, out_max, out_sum, out_z,
                        out_arg);
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
@@ -719,7 +1200,9 @@ int head_add_bf16_launch(const HeadRows& rows, const uint16_t* weight, int R, in
 
 extern "C" size_t spec_head_workspace_bytes(int R, int V) {
     if (R < 1 || V < 1) return 0;
-    return (size_t)splits_for(R, V) * (size_t)R * sizeof(HeadPart);
+    size_t n = (size_t)splits_for(R, V) * (size_t)R;
+    if (mm_shape(R, V) && n < (size_t)kMmParts * (size_t)R) n = (size_t)kMmParts * (size_t)R;
+    return n * sizeof(HeadPart);
 }
 
 extern "C" int spec_head_stats(const void* hidden, const void* weight, int R, int H, int V,
@@ -739,7 +1222,7 @@ extern "C" int spec_head_stats(const void* hidden, const void* weight, int R, in
         return SV_ERR_ALIGN;
     }
     if (workspace_bytes < spec_head_workspace_bytes(R, V)) return SV_ERR_ARG;
-    const HeadRows rows{static_cast<const uint16_t*>(hidden), nullptr, nullptr, R};
+    const HeadRows rows{static_cast<const uint16_t*>(hidden), nullptr, nullptr, R, 0};
     return svhead::head_stats_launch(rows, static_cast<const uint16_t*>(weight), R, nullptr, H,
                                      V, tokens, temperature, out_max, out_sumexp, out_ztok,
                                      out_argmax, workspace, static_cast<hipStream_t>(stream));

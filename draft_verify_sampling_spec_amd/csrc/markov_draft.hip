@@ -172,7 +172,7 @@ extern "C" int spec_markov_draft(const void* base_logits, const void* markov_a,
     for (int i = 0; i < K; ++i) {
         // Rows of A indexed by the previous tokens; virtual rows >= V never
         // occur (tokens are checked, argmaxes lie in [0, V)).
-        const HeadRows rows{A, nullptr, map[i & 1], V};
+        const HeadRows rows{A, nullptr, map[i & 1], V, 0};
         const int rc = svhead::head_add_bf16_launch(rows, Bm, B, r, V, base + (size_t)i * V,
                                                     out + (size_t)i * V, (long long)K * V, parts,
                                                     s);

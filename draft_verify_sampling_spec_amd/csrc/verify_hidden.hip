@@ -17,7 +17,9 @@
 //   1. plan (one workgroup): clamps budgets, checks drafted tokens, and packs
 //      the rows a request needs -- target rows 0..k_b, and in sampled mode
 //      drafter rows 0..k_b-1 -- into a row map, with the row count left on
-//      the device;
+//      the device: every request's target rows first, then (from a multiple
+//      of 8, so that no group of 8 packed rows mixes the two buffers) every
+//      request's drafter rows;
 //   2. the head product with the statistics epilogue over the packed rows
 //      (max, exp-sum and drafted token's logit; greedy: first argmax), its
 //      grid covering any count up to the batch's bound;
@@ -64,13 +66,17 @@ struct DrawDesc {                                  // one request's draw
 
 // Workspace layout (byte offsets, each 256-aligned).
 struct Layout {
-    size_t rowmap, rowtok, off, nrows, sm, ss, sz, sa, part, drawmap, desc, logits, total;
+    size_t rowmap, rowtok, off, offd, nrows, sm, ss, sz, sa, part, drawmap, desc, logits, total;
 };
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Packed rows at most: the target rows, up to 7 rows of padding, the
+// drafter rows.
+size_t packed_rows_max(int B, int K) { return (size_t)B * (2 * K + 1) + 7; }
+
 Layout layout_for(int B, int K, int V) {
-    const size_t rmax = (size_t)B * (2 * K + 1);
+    const size_t rmax = packed_rows_max(B, K);
     Layout L{};
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -81,6 +87,7 @@ Layout layout_for(int B, int K, int V) {
     L.rowmap = take(rmax * 4);
     L.rowtok = take(rmax * 4);
     L.off = take((size_t)B * 4);
+    L.offd = take((size_t)B * 4);
     L.nrows = take(4);
     L.sm = take(rmax * 4);
     L.ss = take(rmax * 4);
@@ -118,31 +125,39 @@ __device__ unsigned plan_exclusive(unsigned* wsum, unsigned v) {
     return base + incl - v;
 }
 
-// Packed rows of request b start at off[b]: target rows 0..k (virtual row
-// b (K+1) + i), then in sampled mode drafter rows 0..k-1 (virtual row
-// B (K+1) + b K + i). Each carries the drafted token of its position (-1 for
-// the target row k, and for a token outside [0, V), which is flagged).
+// Packed rows: request b's target rows 0..k (virtual row b (K+1) + i) at
+// off[b] + i, all requests' target rows together from row 0; in sampled mode
+// its drafter rows 0..k-1 (virtual row B (K+1) + b K + i) at offd[b] + i, all
+// together from the first multiple of 8 after the target rows (the rows in
+// between are rows of zeros, virtual row -1). Each carries the drafted token
+// of its position (-1 for the target row k, for padding, and for a token
+// outside [0, V), which is flagged).
 __global__ __launch_bounds__(kPlanThreads) void hv_plan_kernel(
     const int32_t* __restrict__ budgets, const int32_t* __restrict__ tokens, int B, int K, int V,
     int greedy, int32_t* __restrict__ rowmap, int32_t* __restrict__ rowtok,
-    int32_t* __restrict__ off, int32_t* __restrict__ nrows, int32_t* __restrict__ status) {
+    int32_t* __restrict__ off, int32_t* __restrict__ offd, int32_t* __restrict__ nrows,
+    int32_t* __restrict__ status) {
     __shared__ unsigned wsum[kPlanWaves];
-    __shared__ unsigned flags_s;
+    __shared__ unsigned flags_s, total_s;
     const int tid = threadIdx.x;
     if (tid == 0) flags_s = 0u;
     const int per = (B + kPlanThreads - 1) / kPlanThreads;
     const int b0 = min(tid * per, B), b1 = min(b0 + per, B);
     unsigned flags = 0u, cnt = 0u;
-    for (int b = b0; b < b1; ++b) {
-        const int k = clamp_budget(budgets[b], K, flags);
-        cnt += greedy ? (unsigned)(k + 1) : (unsigned)(2 * k + 1);
-    }
-    const unsigned base = plan_exclusive(wsum, cnt);
-    unsigned o = base;
-    unsigned ignore = 0u;
+    for (int b = b0; b < b1; ++b) cnt += (unsigned)(clamp_budget(budgets[b], K, flags) + 1);
+    const unsigned base_t = plan_exclusive(wsum, cnt);
+    if (tid == kPlanThreads - 1) total_s = base_t + cnt;   // the target rows
+    __syncthreads();
+    const unsigned nt = total_s;
+    const unsigned nt8 = (nt + 7u) & ~7u;
+    unsigned ignore = 0u, cnt_d = 0u;
+    for (int b = b0; b < b1; ++b) cnt_d += (unsigned)clamp_budget(budgets[b], K, ignore);
+    const unsigned base_d = greedy ? 0u : nt8 + plan_exclusive(wsum, cnt_d);
+    unsigned o = base_t, od = base_d;
     for (int b = b0; b < b1; ++b) {
         const int k = clamp_budget(budgets[b], K, ignore);
         off[b] = (int32_t)o;
+        offd[b] = (int32_t)od;
         for (int i = 0; i <= k; ++i) {
             int x = -1;
             if (i < k) {
@@ -155,14 +170,19 @@ __global__ __launch_bounds__(kPlanThreads) void hv_plan_kernel(
             rowmap[o + i] = b * (K + 1) + i;
             rowtok[o + i] = x;
             if (!greedy && i < k) {
-                rowmap[o + k + 1 + i] = B * (K + 1) + b * K + i;
-                rowtok[o + k + 1 + i] = x;
+                rowmap[od + i] = B * (K + 1) + b * K + i;
+                rowtok[od + i] = x;
             }
         }
-        o += greedy ? (unsigned)(k + 1) : (unsigned)(2 * k + 1);
+        o += (unsigned)(k + 1);
+        od += (unsigned)k;
+    }
+    if (!greedy && tid < (int)(nt8 - nt)) {          // padding between the two parts
+        rowmap[nt + tid] = -1;
+        rowtok[nt + tid] = -1;
     }
     if (flags) atomicOr(&flags_s, flags);
-    if (tid == kPlanThreads - 1) *nrows = (int32_t)o;   // the last thread ends the packing
+    if (tid == kPlanThreads - 1) *nrows = (int32_t)(greedy ? nt : od);   // the last thread ends the packing
     __syncthreads();
     if (tid == 0 && status) *status = (int32_t)flags_s;
 }
@@ -173,7 +193,8 @@ __global__ __launch_bounds__(kPlanThreads) void hv_plan_kernel(
 __global__ void hv_decide_kernel(const int32_t* __restrict__ budgets,
                                  const int32_t* __restrict__ tokens, int B, int K, int V,
                                  int greedy, double c64, uint32_t key0, uint32_t key1,
-                                 const int32_t* __restrict__ off, const float* __restrict__ sm,
+                                 const int32_t* __restrict__ off, const int32_t* __restrict__ offd,
+                                 const float* __restrict__ sm,
                                  const float* __restrict__ ss, const float* __restrict__ sz,
                                  const int32_t* __restrict__ sa, int32_t* __restrict__ out_tokens,
                                  int32_t* __restrict__ out_n, float* __restrict__ out_p,
@@ -183,7 +204,7 @@ __global__ void hv_decide_kernel(const int32_t* __restrict__ budgets,
     if (b >= B) return;
     unsigned ignore = 0u;
     const int k = clamp_budget(budgets[b], K, ignore);
-    const int o = off[b];
+    const int o = off[b], od = offd[b];
     int32_t* row = out_tokens + (size_t)b * (K + 1);
     int j = k;
     if (greedy) {
@@ -209,7 +230,7 @@ __global__ void hv_decide_kernel(const int32_t* __restrict__ budgets,
     for (int i = 0; i < k; ++i) {
         const int x = tokens[(size_t)b * K + i];
         const bool valid = x >= 0 && x < V;
-        const int rt = o + i, rd = o + k + 1 + i;
+        const int rt = o + i, rd = od + i;
         double px = 0.0, qx = 0.0;
         if (valid) {
             px = exp2(((double)sz[rt] - (double)sm[rt]) * c64) / (double)ss[rt];
@@ -237,8 +258,8 @@ __global__ void hv_decide_kernel(const int32_t* __restrict__ budgets,
     drawmap[2 * b] = b * (K + 1) + j;
     if (j < k) {
         d.kind = kResidual;
-        d.md = sm[o + k + 1 + j];
-        d.sd = ss[o + k + 1 + j];
+        d.md = sm[od + j];
+        d.sd = ss[od + j];
         drawmap[2 * b + 1] = B * (K + 1) + b * K + j;
     } else {
         d.kind = kBonus;
@@ -494,15 +515,15 @@ extern "C" int spec_verify_hidden(const void* target_hidden, const void* draft_h
     const uint16_t* th = static_cast<const uint16_t*>(target_hidden);
     const uint16_t* dh = static_cast<const uint16_t*>(draft_hidden);
     const uint16_t* w = static_cast<const uint16_t*>(head);
-    const int rmax = greedy ? B * (K + 1) : B * (2 * K + 1);
+    const int rmax = greedy ? B * (K + 1) : (int)packed_rows_max(B, K);
     const double c64 = greedy ? 0.0 : 1.4426950408889634073599246810019 / (double)temperature;
 
     hipLaunchKernelGGL(hv_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, budgets, draft_tokens,
-                       B, K, V, greedy ? 1 : 0, i32(L.rowmap), i32(L.rowtok), i32(L.off),
+                       B, K, V, greedy ? 1 : 0, i32(L.rowmap), i32(L.rowtok), i32(L.off), i32(L.offd),
                        i32(L.nrows), out_status);
     if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
 
-    const HeadRows rows{th, dh, i32(L.rowmap), B * (K + 1)};
+    const HeadRows rows{th, dh, i32(L.rowmap), B * (K + 1), dh ? B * K : 0, true};
     int rc = svhead::head_stats_launch(rows, w, rmax, i32(L.nrows), H, V, i32(L.rowtok),
                                        temperature, f32(L.sm), greedy ? nullptr : f32(L.ss),
                                        greedy ? nullptr : f32(L.sz), greedy ? i32(L.sa) : nullptr,
@@ -512,14 +533,14 @@ extern "C" int spec_verify_hidden(const void* target_hidden, const void* draft_h
     const int dthreads = 256;
     hipLaunchKernelGGL(hv_decide_kernel, dim3((unsigned)((B + dthreads - 1) / dthreads)),
                        dim3(dthreads), 0, s, budgets, draft_tokens, B, K, V, greedy ? 1 : 0, c64,
-                       (uint32_t)(seed & 0xFFFFFFFFull), (uint32_t)(seed >> 32), i32(L.off),
+                       (uint32_t)(seed & 0xFFFFFFFFull), (uint32_t)(seed >> 32), i32(L.off), i32(L.offd),
                        f32(L.sm), f32(L.ss), f32(L.sz), i32(L.sa), out_tokens, out_num_accepted,
                        out_p_draft, out_q_draft, i32(L.drawmap),
                        reinterpret_cast<DrawDesc*>(ws + L.desc));
     if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
     if (greedy) return SV_OK;
 
-    const HeadRows draw_rows{th, dh, i32(L.drawmap), B * (K + 1)};
+    const HeadRows draw_rows{th, dh, i32(L.drawmap), B * (K + 1), dh ? B * K : 0};
     rc = svhead::head_logits_launch(draw_rows, w, 2 * B, H, V, f32(L.logits), s);
     if (rc != SV_OK) return rc;
     // 16-byte loads of the fp32 rows when every row starts 16-byte aligned.
