@@ -649,29 +649,37 @@ void head_stats_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
 // any dealing, only slower).
 constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kMmThreads = 256;
-constexpr int kBandTiles = 6;                        // row tiles per band
-constexpr int kColTiles = 5;                         // vocabulary tiles per super-step
+constexpr int kBandTiles = 6;                        // row tiles per band (statistics)
+constexpr int kColTiles = 5;                         // vocabulary tiles per super-step (statistics)
+constexpr int kLogBand = 4, kLogCols = 8;            // the same for logits (few rows)
 constexpr int kXcds = 8;
 constexpr int kMmParts = kXcds * kColTiles;          // partials per row
 constexpr int kMmGrid = kXcds * 32;                  // one workgroup per CU
 constexpr int kMmOpBytes = kBM * kBK * 2;            // one operand of one stage (32 KB)
 constexpr int kMmLds = 2 * 2 * kMmOpBytes;           // two stages, both operands
 constexpr unsigned kMmOob = 0x80000000u;             // a buffer offset past every range below
+enum MmMode { kMmGreedy = 0, kMmSampled = 1, kMmLogits = 2 };
 
-// Row and column counts for which a call takes this path (the workspace is
-// sized from these alone): at least one full band, and every XCD with a
-// super-step in every band.
+// Row and column counts for which a call takes this path with super-tiles
+// of kB row tiles by kC vocabulary tiles (the workspace is sized from these
+// alone): at least one full band, and every XCD with a super-step in every
+// band.
+template <int kB, int kC>
+__host__ __device__ inline bool mm_shape_t(int r_max, int V) {
+    return r_max >= kBM * kB && (V + kBN - 1) / kBN >= kC * kXcds;
+}
 __host__ __device__ inline bool mm_shape(int r_max, int V) {
-    return r_max >= kBM * kBandTiles && (V + kBN - 1) / kBN >= kColTiles * kXcds;
+    return mm_shape_t<kBandTiles, kColTiles>(r_max, V);
 }
 
 // The whole condition: the shape, whole k-steps, rows of the two buffers in
 // separate groups of 8 (one load instruction reads one group through one
 // buffer descriptor), and byte offsets within each hidden-state buffer and
 // within a vocabulary tile that stay below kMmOob (32-bit buffer offsets).
+template <int kB, int kC>
 inline bool mm_path(const HeadRows& hr, int r_max, int H, int V) {
     const unsigned long long row = 2ull * (unsigned long long)H;
-    return mm_shape(r_max, V) && H % kBK == 0 && row * kBN <= kMmOob / 2 &&
+    return mm_shape_t<kB, kC>(r_max, V) && H % kBK == 0 && row * kBN <= kMmOob / 2 &&
            (hr.b_rows == 0 || hr.grouped8) &&
            row * (unsigned long long)hr.a_rows <= kMmOob &&
            row * (unsigned long long)hr.b_rows <= kMmOob;
@@ -708,11 +716,17 @@ __device__ __forceinline__ void ring_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <bool kSampled>
+// kMode: the row statistics (greedy or sampled, partials per (XCD, column
+// slot) into part) or the fp32 logits themselves (into out, row-major,
+// R x V). kBandT x kColT: the XCD's super-tile.
+template <int kMode, int kBandT, int kColT>
 __global__ __launch_bounds__(kMmThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
                     const int* __restrict__ d_rows, int H, int V,
-                    const int32_t* __restrict__ tok, float c, HeadPart* __restrict__ part) {
+                    const int32_t* __restrict__ tok, float c, HeadPart* __restrict__ part,
+                    float* __restrict__ out) {
+    constexpr bool kSampled = kMode == kMmSampled;
+    constexpr bool kLogits = kMode == kMmLogits;
     extern __shared__ __align__(16) unsigned char mm_smem[];
     __shared__ HeadPart xw[kBM];
 
@@ -725,23 +739,23 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
     const int wm = wave >> 1, wn = wave & 1;
     const int R = rows_now(r_max, d_rows);
     const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
-    if (slot >= kBandTiles * kColTiles || R == 0) return;
-    const int rt_in = slot % kBandTiles, vt = slot / kBandTiles;
+    if (slot >= kBandT * kColT || R == 0) return;
+    const int rt_in = slot % kBandT, vt = slot / kBandT;
     const int rtiles = (R + kBM - 1) / kBM;
-    const int nbands = (rtiles + kBandTiles - 1) / kBandTiles;
+    const int nbands = (rtiles + kBandT - 1) / kBandT;
     const int ntiles = (V + kBN - 1) / kBN;
-    const int spb = (ntiles + kColTiles - 1) / kColTiles;   // super-steps per band
+    const int spb = (ntiles + kColT - 1) / kColT;   // super-steps per band
     const int total = nbands * spb;
     const int nk = H / kBK;
 
     // The workgroup's tiles, in order: super-steps stp = xcd, xcd + 8, ...
-    // Super-step stp covers row tile (stp / spb) * kBandTiles + rt_in and
-    // vocabulary tile (stp % spb) * kColTiles + vt; it is skipped when
-    // either lies past the end (every band that has this row tile has at
-    // least one vocabulary tile here, as the path needs kColTiles * kXcds
-    // vocabulary tiles).
-    auto row0_of = [&](int stp) { return (stp / spb * kBandTiles + rt_in) * kBM; };
-    auto v0_of = [&](int stp) { return ((stp % spb) * kColTiles + vt) * kBN; };
+    // Super-step stp covers row tile (stp / spb) * kBandT + rt_in and
+    // vocabulary tile (stp % spb) * kColT + vt; it is skipped when either
+    // lies past the end (every band that has this row tile has at least one
+    // vocabulary tile here, as the path needs kColT * kXcds vocabulary
+    // tiles).
+    auto row0_of = [&](int stp) { return (stp / spb * kBandT + rt_in) * kBM; };
+    auto v0_of = [&](int stp) { return ((stp % spb) * kColT + vt) * kBN; };
     auto next_tile = [&](int stp) {
         while (stp < total && (row0_of(stp) >= R || v0_of(stp) >= V)) stp += kXcds;
         return stp < total ? stp : total;
@@ -935,6 +949,34 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
         }
     };
 
+    // Logits: the tile's values to out, 4 consecutive columns per store (16
+    // bytes when V is a multiple of 4); rows from R on and columns from V on
+    // are not written.
+    auto store = [&](int v0, int r0) {
+        const int cbase = v0 + wn * 128 + 4 * (lane >> 5);
+        const bool vec = (V & 3) == 0;
+        #pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int r = r0 + wm * 128 + 32 * a + (lane & 31);
+            float* orow = out + (size_t)(r < R ? r : 0) * V;
+            #pragma unroll
+            for (int b2 = 0; b2 < 4; ++b2)
+                #pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int col = cbase + 32 * b2 + 8 * q;
+                    const f32x16& t = acc[b2][a];
+                    if (r < R && vec && col + 3 < V) {
+                        *reinterpret_cast<float4*>(orow + col) =
+                            float4{t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]};
+                    } else if (r < R) {
+                        #pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (col + e < V) orow[col + e] = t[4 * q + e];
+                    }
+                }
+        }
+    };
+
     // The band's partial of this (XCD, column slot) for each of its rows:
     // the lane pair holding a row (lane, lane ^ 32) merges, then the two
     // waves with the same rows through LDS.
@@ -966,19 +1008,19 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
             for (int a = 0; a < 4; ++a) {
                 const int rl = rl0 + 32 * a;
                 const HeadPart o = xw[rl];
-                HeadPart out;
-                out.m = rm[a];
-                out.zx = rz[a] == rz[a] ? rz[a] : o.zx;
+                HeadPart o2;
+                o2.m = rm[a];
+                o2.zx = rz[a] == rz[a] ? rz[a] : o.zx;
                 if (kSampled) {
-                    out.s = rx[a];
-                    merge_ms(out.m, out.s, o.m, o.s, c, true);
-                    out.arg = INT_MAX;
+                    o2.s = rx[a];
+                    merge_ms(o2.m, o2.s, o.m, o.s, c, true);
+                    o2.arg = INT_MAX;
                 } else {
-                    out.s = 0.0f;
-                    out.arg = __float_as_int(rx[a]);
-                    merge_arg(out.m, out.arg, o.m, o.arg);
+                    o2.s = 0.0f;
+                    o2.arg = __float_as_int(rx[a]);
+                    merge_arg(o2.m, o2.arg, o.m, o.arg);
                 }
-                if (r0 + rl < R) part[(size_t)(xcd * kColTiles + vt) * R + r0 + rl] = out;
+                if (r0 + rl < R) part[(size_t)(xcd * kColT + vt) * R + r0 + rl] = o2;
             }
         }
         __syncthreads();
@@ -1000,7 +1042,7 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
     for (int i = 0; i < 16; ++i) load_one(0, i);     // step 0, whole
     loader_next();
     int band = c_stp / spb;
-    start_band(row0_of(c_stp));
+    if (!kLogits) start_band(row0_of(c_stp));
     zero_acc();
     __builtin_amdgcn_s_waitcnt(0);                   // step 0 and the tokens
     ring_barrier();
@@ -1058,19 +1100,21 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
         multiply_ld(f1, st, 0);
         __builtin_amdgcn_sched_barrier(0);
         st ^= 1;
-        fold(v0_of(c_stp));
+        if (kLogits) store(v0_of(c_stp), row0_of(c_stp));
+        else fold(v0_of(c_stp));
         if (!has_next) break;
         const int nb = n_stp / spb;
-        if (nb != band) {
+        if (!kLogits && nb != band) {
             flush(row0_of(c_stp));
-            band = nb;
             start_band(row0_of(n_stp));
         }
+        band = nb;
         zero_acc();
         read_frags(f0, st, 0);                       // the next tile's first group
         c_stp = n_stp;
     }
-    flush(row0_of(c_stp));                           // (drains the last loads too)
+    if (!kLogits) flush(row0_of(c_stp));
+    __builtin_amdgcn_s_waitcnt(0);                   // the last loads and stores
 }
 
 // Per row: merge the splits' partials (in split order) into the outputs.
@@ -1106,6 +1150,24 @@ int items_for(int R, int V) { return ((R + kTM - 1) / kTM) * splits_for(R, V); }
 
 }  // namespace
 
+// The many-row product's instantiations may use more than the default
+// dynamic LDS: raised once per process (a thread-safe static).
+static hipError_t mm_attrs() {
+    static const hipError_t rc = []() {
+        const void* fns[] = {
+            reinterpret_cast<const void*>(&head_mm_kernel<kMmSampled, kBandTiles, kColTiles>),
+            reinterpret_cast<const void*>(&head_mm_kernel<kMmGreedy, kBandTiles, kColTiles>),
+            reinterpret_cast<const void*>(&head_mm_kernel<kMmLogits, kLogBand, kLogCols>)};
+        for (const void* f : fns) {
+            const hipError_t e =
+                hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kMmLds);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }();
+    return rc;
+}
+
 namespace svhead {
 
 // splits(R) * R stays within max(65536, R) (one resident wave of 128-row
@@ -1129,24 +1191,17 @@ int head_stats_launch(const HeadRows& rows, const uint16_t* weight, int r_max,
     const bool sampled = temperature > 0.0f;
     const float c = sampled ? (float)(1.4426950408889634 / (double)temperature) : 0.0f;
     HeadPart* part = static_cast<HeadPart*>(workspace);
-    if (mm_path(rows, r_max, H, V)) {
+    if (mm_path<kBandTiles, kColTiles>(rows, r_max, H, V)) {
         // Many rows: the large-tile product, one workgroup per CU.
-        static bool attr_set = false;
-        if (!attr_set) {
-            if (hipFuncSetAttribute(reinterpret_cast<const void*>(&head_mm_kernel<true>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, kMmLds) != hipSuccess ||
-                hipFuncSetAttribute(reinterpret_cast<const void*>(&head_mm_kernel<false>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, kMmLds) != hipSuccess) {
-                return SV_ERR_HIP;
-            }
-            attr_set = true;
-        }
+        if (mm_attrs() != hipSuccess) return SV_ERR_HIP;
         if (sampled) {
-            hipLaunchKernelGGL(head_mm_kernel<true>, dim3(kMmGrid), dim3(kMmThreads), kMmLds, s,
-                               rows, weight, r_max, d_rows, H, V, tokens, c, part);
+            hipLaunchKernelGGL((head_mm_kernel<kMmSampled, kBandTiles, kColTiles>), dim3(kMmGrid),
+                               dim3(kMmThreads), kMmLds, s, rows, weight, r_max, d_rows, H, V,
+                               tokens, c, part, nullptr);
         } else {
-            hipLaunchKernelGGL(head_mm_kernel<false>, dim3(kMmGrid), dim3(kMmThreads), kMmLds, s,
-                               rows, weight, r_max, d_rows, H, V, tokens, c, part);
+            hipLaunchKernelGGL((head_mm_kernel<kMmGreedy, kBandTiles, kColTiles>), dim3(kMmGrid),
+                               dim3(kMmThreads), kMmLds, s, rows, weight, r_max, d_rows, H, V,
+                               tokens, c, part, nullptr);
         }
         if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
         hipLaunchKernelGGL(head_merge_kernel, dim3((unsigned)((r_max + 255) / 256)), dim3(256), 0,
@@ -1178,6 +1233,13 @@ int head_stats_launch(const HeadRows& rows, const uint16_t* weight, int r_max,
 int head_logits_launch(const HeadRows& rows, const uint16_t* weight, int R, int H, int V,
                        float* out, hipStream_t s) {
     if (R < 1) return SV_OK;
+    if (mm_path<kLogBand, kLogCols>(rows, R, H, V)) {
+        if (mm_attrs() != hipSuccess) return SV_ERR_HIP;
+        hipLaunchKernelGGL((head_mm_kernel<kMmLogits, kLogBand, kLogCols>), dim3(kMmGrid),
+                           dim3(kMmThreads), kMmLds, s, rows, weight, R, nullptr, H, V, nullptr,
+                           0.0f, nullptr, out);
+        return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+    }
     hipLaunchKernelGGL(head_stats_kernel<kEpiLogits>, dim3((unsigned)items_for(R, V)),
                        dim3(kHThreads), 0, s, rows, weight, R, nullptr, H, V, nullptr, 0.0f,
                        nullptr, out, RowAdd{});

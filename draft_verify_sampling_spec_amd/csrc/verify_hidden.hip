@@ -27,9 +27,10 @@
 //      Philox uniforms, the first rejection; greedy outputs are final here;
 //   4. sampled only: the head product once more for each request's draw rows
 //      (target and drafter row j_b for a residual, target row k_b for a
-//      bonus), writing their fp32 logits -- bit-identical to the values the
-//      statistics were taken over, since each logit accumulates in the same
-//      order;
+//      bonus; every request's target row first, then from a multiple of 8
+//      every drafter row), writing their fp32 logits -- bit-identical to the
+//      values the statistics were taken over when both go through the
+//      many-row product (each logit accumulates in the same order);
 //   5. sampled only: the inverse-CDF draw (an 8-wave workgroup per request)
 //      over those rows in vocabulary order: 256-element block masses first,
 //      then one wave rescans the block where the running mass crosses u R.
@@ -75,6 +76,10 @@ size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 // drafter rows.
 size_t packed_rows_max(int B, int K) { return (size_t)B * (2 * K + 1) + 7; }
 
+// Draw rows: request b's target row at b, its drafter row at up8(B) + b.
+__host__ __device__ inline int draw_split(int B) { return (B + 7) & ~7; }
+size_t draw_rows_for(int B) { return (size_t)draw_split(B) + (size_t)B; }
+
 Layout layout_for(int B, int K, int V) {
     const size_t rmax = packed_rows_max(B, K);
     Layout L{};
@@ -94,9 +99,9 @@ Layout layout_for(int B, int K, int V) {
     L.sz = take(rmax * 4);
     L.sa = take(rmax * 4);
     L.part = take(svhead::stats_workspace_bytes((int)rmax, V));
-    L.drawmap = take((size_t)B * 2 * 4);
+    L.drawmap = take(draw_rows_for(B) * 4);
     L.desc = take((size_t)B * sizeof(DrawDesc));
-    L.logits = take((size_t)B * 2 * (size_t)V * 4);
+    L.logits = take(draw_rows_for(B) * (size_t)V * 4);
     L.total = o;
     return L;
 }
@@ -201,6 +206,7 @@ __global__ void hv_decide_kernel(const int32_t* __restrict__ budgets,
                                  float* __restrict__ out_q, int32_t* __restrict__ drawmap,
                                  DrawDesc* __restrict__ desc) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < draw_split(B) - B) drawmap[B + b] = -1;  // padding between the two parts
     if (b >= B) return;
     unsigned ignore = 0u;
     const int k = clamp_budget(budgets[b], K, ignore);
@@ -223,8 +229,8 @@ __global__ void hv_decide_kernel(const int32_t* __restrict__ budgets,
         DrawDesc d{};
         d.kind = kNoDraw;
         desc[b] = d;
-        drawmap[2 * b] = -1;
-        drawmap[2 * b + 1] = -1;
+        drawmap[b] = -1;
+        drawmap[draw_split(B) + b] = -1;
         return;
     }
     for (int i = 0; i < k; ++i) {
@@ -255,15 +261,15 @@ __global__ void hv_decide_kernel(const int32_t* __restrict__ budgets,
     d.pos = j;
     d.mt = sm[o + j];
     d.st = ss[o + j];
-    drawmap[2 * b] = b * (K + 1) + j;
+    drawmap[b] = b * (K + 1) + j;
     if (j < k) {
         d.kind = kResidual;
         d.md = sm[od + j];
         d.sd = ss[od + j];
-        drawmap[2 * b + 1] = B * (K + 1) + b * K + j;
+        drawmap[draw_split(B) + b] = B * (K + 1) + b * K + j;
     } else {
         d.kind = kBonus;
-        drawmap[2 * b + 1] = -1;
+        drawmap[draw_split(B) + b] = -1;
     }
     desc[b] = d;
 }
@@ -352,8 +358,8 @@ void hv_draw_kernel(const float* __restrict__ logits, int K, int V, float c,
     const DrawDesc d = desc[b];
     if (d.kind == kNoDraw) return;                   // the whole workgroup
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const float* zt = logits + (size_t)(2 * b) * V;
-    const float* zd = zt + V;
+    const float* zt = logits + (size_t)b * V;
+    const float* zd = logits + (size_t)(draw_split((int)gridDim.x) + b) * V;
     const int nb = (V + kHvBlock - 1) / kHvBlock;
     const int stride = kHvDrawSlots * kHvDrawWaves;
     const float ist = 1.0f / d.st;
@@ -540,8 +546,8 @@ extern "C" int spec_verify_hidden(const void* target_hidden, const void* draft_h
     if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
     if (greedy) return SV_OK;
 
-    const HeadRows draw_rows{th, dh, i32(L.drawmap), B * (K + 1), dh ? B * K : 0};
-    rc = svhead::head_logits_launch(draw_rows, w, 2 * B, H, V, f32(L.logits), s);
+    const HeadRows draw_rows{th, dh, i32(L.drawmap), B * (K + 1), dh ? B * K : 0, true};
+    rc = svhead::head_logits_launch(draw_rows, w, (int)draw_rows_for(B), H, V, f32(L.logits), s);
     if (rc != SV_OK) return rc;
     // 16-byte loads of the fp32 rows when every row starts 16-byte aligned.
     const size_t draw_smem = (size_t)((V + kHvBlock - 1) / kHvBlock) * sizeof(double);

@@ -69,6 +69,23 @@ def test_small_shapes_match_oracle(R, H, V, T):
     _check_rows(z, scale, tok.cpu().numpy(), T, got, H)
 
 
+@pytest.mark.parametrize("R,H,V", [(1700, 128, 10243), (1541, 192, 10001)])
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_many_row_product_every_row(R, H, V, T):
+    """Shapes that take the many-row product (at least 1,536 rows, at least
+    40 vocabulary tiles of 256, H a multiple of 64) with ragged row and
+    vocabulary tails (a partial last row tile and a partial last vocabulary
+    tile, a partial last band): every row against the oracle."""
+    _log(f"[head] many-row product R={R} H={H} V={V} T={T}")
+    h, w, tok = make_head_inputs(R, H, V, seed=R + V)
+    tok[::7] = -1
+    got = head_stats(h, w, tok, T)
+    h64, w64 = oh.bf16_bits_to_f64(_bits(h)), oh.bf16_bits_to_f64(_bits(w))
+    z = oh.logits(h64, w64)
+    scale = (np.abs(h64) @ np.abs(w64).T).max(axis=1)
+    _check_rows(z, scale, tok.cpu().numpy(), T, got, H)
+
+
 def test_full_size_sampled_rows():
     """The heavy batch's shape: 8,704 rows (4,608 target + 4,096 drafter
     positions), H = 2,560, V = 151,936; the oracle recomputes 6 rows."""

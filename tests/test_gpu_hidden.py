@@ -176,6 +176,22 @@ def test_small_shapes_match_oracle(B, K, H, V, T):
     _check(inp, T, seed, f"B={B} K={K} H={H} V={V} T={T}")
 
 
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_many_row_products_every_request(T):
+    """A batch large enough for the many-row product in both launches: the
+    scored rows' statistics (at least 1,536 rows bound, 40 vocabulary tiles)
+    and, sampled, the draw rows' logits (B = 512 gives 1,024 draw rows; at
+    least 64 vocabulary tiles), with V not a multiple of 4 (the logits'
+    4-wide stores fall back to single ones): every request against the
+    oracle."""
+    B, K, H, V = 512, 3, 64, 16421
+    _log(f"[hidden] many-row products B={B} K={K} H={H} V={V} T={T}")
+    rng = np.random.default_rng(77)
+    budgets = rng.integers(0, K + 1, size=B)
+    inp = make_hidden_inputs(B, K, H, V, seed=77, device=DEV, budgets=budgets)
+    _check(inp, T, (77 << 32) | 5, f"many-row B={B} K={K} H={H} V={V} T={T}")
+
+
 def test_q_equal_p_accepts_everything():
     inp = make_hidden_inputs(64, 5, 128, 3000, seed=3, device=DEV, variant="q_eq_p")
     toks, nacc, p, q, status = _gpu(inp, 1.0, 77)
