@@ -24,6 +24,8 @@ read-only reduction over the same logits.
                   [--no-cpu-baseline] [--verify-only]
   python bench.py --copy-probe GIB   # plain copies of a known size (counter scale)
   python bench.py --markov-only      # the Markov head alone at the heavy shape (profiling)
+  python bench.py --head-only        # the output head alone at the heavy rows (profiling)
+  python bench.py --hidden-only      # the whole step from hidden states alone (profiling)
 """
 from __future__ import annotations
 
@@ -599,6 +601,10 @@ def main():
     ap.add_argument("--copy-probe", type=float, default=None)
     ap.add_argument("--markov-only", action="store_true",
                     help="time only the Markov head over a heavy-shape block (3 calls)")
+    ap.add_argument("--head-only", action="store_true",
+                    help="time only the output head at the heavy rows (3 calls per temperature)")
+    ap.add_argument("--hidden-only", action="store_true",
+                    help="time only the verify step from hidden states (3 calls)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -610,7 +616,7 @@ def main():
     # the GPU (torch is not imported yet).
     pool = None
     want_cpu = (not args.no_cpu_baseline and args.workload == "heavy" and args.copy_probe is None
-                and not args.markov_only)
+                and not (args.markov_only or args.head_only or args.hidden_only))
     if want_cpu:
         pool = OraclePool(cpu_workers())
     try:
@@ -630,6 +636,13 @@ def run(args, pool):
         return
     if args.markov_only:
         print(json.dumps({"markov": bench_markov(512, 8, 151936, 256, 3)}), flush=True)
+        return
+    if args.head_only:
+        out = {f"T={T}": bench_head(4592, 2560, 151936, 3, T=T) for T in (1.0, 0.0)}
+        print(json.dumps({"head": out}), flush=True)
+        return
+    if args.hidden_only:
+        print(json.dumps({"hidden": bench_hidden(512, 8, 2560, 151936, 3)}), flush=True)
         return
 
     dev = torch.device("cuda:0")

@@ -869,13 +869,19 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    auto zero_acc = [&]() {
+    // A tile's accumulators start at 0, except for columns past V (in the
+    // last vocabulary tile), which start at -inf: their head rows read as
+    // zeros, so they stay -inf and drop out of every statistic without a
+    // mask in the fold (the logits mode does not store them).
+    auto zero_acc = [&](int v0) {
+        const int lim = V - (v0 + wn * 128 + 4 * (lane >> 5));
         #pragma unroll
         for (int b2 = 0; b2 < 4; ++b2)
             #pragma unroll
             for (int a = 0; a < 4; ++a)
                 #pragma unroll
-                for (int i = 0; i < 16; ++i) acc[b2][a][i] = 0.0f;
+                for (int i = 0; i < 16; ++i)
+                    acc[b2][a][i] = 32 * b2 + 8 * (i >> 2) + (i & 3) < lim ? 0.0f : -INFINITY;
     };
 
     // ---- running statistics of this lane's 4 hidden rows (a: row
@@ -897,11 +903,9 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
     // Fold the tile into the running statistics, one 32 x 32 block at a
     // time. A lane's columns of a row go up with (vocabulary block, i):
     // column cbase + 32 b2 + 8 (i / 4) + i % 4, so the first maximum wins.
-    // In the last vocabulary tile the columns past V (whose head rows read as
-    // zeros) read as -inf.
+    // Columns past V hold -inf (see zero_acc).
     auto fold = [&](int v0) {
         const int cbase = v0 + wn * 128 + 4 * (lane >> 5);
-        const bool full = v0 + kBN <= V;
         #pragma unroll
         for (int a = 0; a < 4; ++a) {
             // Where the drafted token lies among this lane's columns, if it
@@ -913,14 +917,8 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
             #pragma unroll
             for (int b2 = 0; b2 < 4; ++b2) {
                 float z[16];
-                if (full) {
-                    #pragma unroll
-                    for (int i = 0; i < 16; ++i) z[i] = acc[b2][a][i];
-                } else {
-                    #pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        z[i] = cbase + 32 * b2 + 8 * (i >> 2) + (i & 3) < V ? acc[b2][a][i] : -INFINITY;
-                }
+                #pragma unroll
+                for (int i = 0; i < 16; ++i) z[i] = acc[b2][a][i];
                 if (any_hit) {
                     #pragma unroll
                     for (int i = 0; i < 16; ++i)
@@ -930,13 +928,17 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
                 #pragma unroll
                 for (int i = 1; i < 16; ++i) mb = fmaxf(mb, z[i]);
                 if (kSampled) {
-                    const float mn = fmaxf(rm[a], mb);
-                    const float mr = mn == -INFINITY ? 0.0f : mn;   // all -inf so far: terms stay 0
-                    float sum = 0.0f;
-                    #pragma unroll
-                    for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f((z[i] - mr) * c);
-                    rx[a] = rx[a] * __builtin_amdgcn_exp2f((rm[a] - mr) * c) + sum;
-                    rm[a] = mn;
+                    // A block of -inf (past V) adds nothing. (Taking the
+                    // block as a branch also keeps the compiler from
+                    // interleaving all 16 blocks' values at once.)
+                    if (mb > -INFINITY) {
+                        const float mr = fmaxf(rm[a], mb);
+                        float sum = 0.0f;
+                        #pragma unroll
+                        for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f((z[i] - mr) * c);
+                        rx[a] = rx[a] * __builtin_amdgcn_exp2f((rm[a] - mr) * c) + sum;
+                        rm[a] = mr;
+                    }
                 } else if (mb > rm[a]) {
                     // A new maximum in this block: its first column.
                     int ib = 15;
@@ -1043,7 +1045,7 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
     loader_next();
     int band = c_stp / spb;
     if (!kLogits) start_band(row0_of(c_stp));
-    zero_acc();
+    zero_acc(v0_of(c_stp));
     __builtin_amdgcn_s_waitcnt(0);                   // step 0 and the tokens
     ring_barrier();
     Frags f0, f1;
@@ -1109,7 +1111,7 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
             start_band(row0_of(n_stp));
         }
         band = nb;
-        zero_acc();
+        zero_acc(v0_of(n_stp));
         read_frags(f0, st, 0);                       // the next tile's first group
         c_stp = n_stp;
     }
