@@ -34,6 +34,7 @@
 #include <cstdint>
 
 #include "head_gemm.h"
+#include "lds_dma.h"
 #include "spec_verify.h"
 
 namespace {
@@ -685,35 +686,15 @@ inline bool mm_path(const HeadRows& hr, int r_max, int H, int V) {
            row * (unsigned long long)hr.b_rows <= kMmOob;
 }
 
-// A raw buffer descriptor over n bytes from p (n <= 2^31): loads at byte
-// offsets past n read zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t mm_rsrc(const void* p, unsigned n) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
-}
+using svdma::ring_barrier;
+using svdma::wait_vm;
 
-// One 16-byte buffer-to-LDS load per lane: lane l's 16 bytes at byte
-// offset off of r land at lds + 16 l (lds is the same for the whole wave).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mm_rsrc(const void* p, unsigned n) {
+    return svdma::rsrc(p, n);
+}
 __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, unsigned off,
                                            unsigned char* lds) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
-                                             (int)off, 0, 0, 0);
-}
-
-// Wait until at most N of this wave's vector memory operations are
-// outstanding (loads complete in issue order), leaving the other counters.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
-}
-
-// A workgroup barrier that waits for this wave's LDS reads but not for its
-// vector memory operations: the ring's direct-to-LDS loads are ordered by
-// wait_vm() before it, and the loads of later stages stay in flight across
-// it (a __syncthreads() fence would drain them). The clobber keeps the
-// compiler from moving memory operations across it.
-__device__ __forceinline__ void ring_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    svdma::load16(r, off, lds);
 }
 
 // kMode: the row statistics (greedy or sampled, partials per (XCD, column

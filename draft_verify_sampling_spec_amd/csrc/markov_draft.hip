@@ -30,11 +30,13 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
 
 #include "head_gemm.h"
+#include "lds_dma.h"
 #include "spec_verify.h"
 
 namespace {
@@ -44,6 +46,18 @@ using svhead::HeadRows;
 
 constexpr int kMkPickThreads = 256;
 constexpr int kMkPickWaves = kMkPickThreads / 64;     // one request per wave
+
+constexpr int kMsGrid = 256;                       // streaming product: one workgroup per CU
+constexpr int kMsRows = 256;                       // requests per workgroup
+
+// Groups of 256 requests for B requests (a power of two up to 32): the
+// streaming product's workgroups split into that many groups, each with
+// kMsGrid / groups column slots.
+inline int ms_halves(int B) {
+    int nh = 1;
+    while (nh * kMsRows < B) nh <<= 1;
+    return nh;
+}
 
 struct MkLayout {
     size_t map0, map1, parts, total;
@@ -61,7 +75,11 @@ MkLayout mk_layout(int B, int V) {
     };
     L.map0 = take((size_t)B * 4);
     L.map1 = take((size_t)B * 4);
-    L.parts = take((size_t)svhead::add_splits(B, V) * (size_t)B * sizeof(ArgPart));
+    // First-argmax entries per request: one per vocabulary split of either
+    // product path (the streaming one has a split per column slot).
+    const size_t splits =
+        std::max<size_t>((size_t)svhead::add_splits(B, V), (size_t)(kMsGrid / ms_halves(B)));
+    L.parts = take(splits * (size_t)B * sizeof(ArgPart));
     L.total = o;
     return L;
 }
@@ -87,6 +105,357 @@ __global__ void mk_seed_kernel(const int32_t* __restrict__ prev, int B, int V,
 
 __device__ __forceinline__ bool mk_better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
+}
+
+
+// ---------------------------------------------------------------------------
+// The streaming product for rank r a multiple of 16 up to 256 and V a
+// multiple of 8 (the bench's rank-256 shape). Per position the work is
+// bound by HBM -- the backbone rows in, the drafter rows out, the factor Bm
+// once -- so every CU streams vocabulary tiles of 32 columns for 256
+// requests while the matrix cores form the bias:
+//   * 8 waves, two per SIMD, so that one wave's LDS and memory waits pass
+//     under the other's work; each keeps its 32 requests' rows of A
+//     (x_{i-1}[b]'s row) as MFMA fragments in registers for the whole
+//     launch (the transposed product: Bm's columns as the first operand, so
+//     a lane holds one request's row and 16 columns of the 32 x 32 block);
+//   * Bm's tile (32 rows of r) and the backbone's tile (256 rows of 32
+//     columns) come in by buffer-to-LDS loads into rings of 4 and 5 slots,
+//     three tiles ahead of use; one wait and one barrier per tile;
+//   * tile t's bias is added to its backbone values, rounded once to bf16
+//     and stored while tile t + 1's product runs, and the running maximum
+//     of the stored values is kept per request, with the first tile that
+//     reached it; the column within that tile is read back at the end.
+// The workgroups that share a column slot (one per group of 256 requests)
+// sit on one XCD and walk the same tiles, so Bm's tiles come from HBM once.
+constexpr int kMsThreads = 512;                    // 8 waves, 32 requests each
+constexpr int kMsCols = 32;                        // vocabulary columns per tile
+constexpr int kMsMaxG = 16;                        // k-groups of 16: r <= 256
+constexpr int kMsBmBytes = kMsCols * 512;          // one Bm tile: 32 rows of 512 bytes
+constexpr int kMsBaseBytes = kMsRows * kMsCols * 2;   // one backbone tile: 256 rows of 64 bytes
+constexpr int kMsBmSlots = 4, kMsBaseSlots = 5;    // tiles three ahead
+constexpr int kMsLds = kMsBmSlots * kMsBmBytes + kMsBaseSlots * kMsBaseBytes;   // 144 KB
+constexpr unsigned kMsOob = 0x80000000u;           // past every buffer's range
+
+typedef __bf16 ms_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float ms_f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 ms_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float ms_f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned ms_u32x4 __attribute__((ext_vector_type(4)));
+
+// Two fp32 values to packed bf16 bits (lo in the low half), one
+// v_cvt_pk_bf16_f32: to nearest, ties to even, under the default float
+// mode; a NaN becomes the quiet NaN that keeps its sign and upper payload
+// bits, i.e. the bits (u >> 16) | 0x40 of its pattern u.
+__device__ __forceinline__ uint32_t ms_pack_bf16(float lo, float hi) {
+    const ms_f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, ms_bf16x2));
+}
+
+// The LDS reads and writes of the epilogue, each waited for inside its asm
+// block (read outputs are early-clobbered, so no result lands on an address
+// still to be used). Written out because the compiler, seeing an LDS read
+// while buffer-to-LDS loads into the same array are in flight, would
+// otherwise wait for every one of those loads first, though the slot read
+// has been ordered already.
+__device__ __forceinline__ void ms_read4(uint2 (&v)[4], const unsigned (&ad)[4]) {
+    asm volatile(
+        "ds_read_b64 %0, %4\n\t"
+        "ds_read_b64 %1, %5\n\t"
+        "ds_read_b64 %2, %6\n\t"
+        "ds_read_b64 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+        : "memory");
+}
+__device__ __forceinline__ void ms_write4(const uint2 (&v)[4], const unsigned (&ad)[4]) {
+    asm volatile(
+        "ds_write_b64 %0, %4\n\t"
+        "ds_write_b64 %1, %5\n\t"
+        "ds_write_b64 %2, %6\n\t"
+        "ds_write_b64 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        :
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(v[0]), "v"(v[1]), "v"(v[2]),
+          "v"(v[3])
+        : "memory");
+}
+__device__ __forceinline__ void ms_read2x16(uint4 (&v)[2], const unsigned (&ad)[2]) {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1])
+        : "v"(ad[0]), "v"(ad[1])
+        : "memory");
+}
+
+// The LDS byte address of p (a pointer into dynamic shared memory).
+__device__ __forceinline__ unsigned ms_lds_addr(const void* p) {
+    return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// The streaming path's condition.
+inline bool ms_path(int B, int K, int V, int r) {
+    return r % 16 == 0 && r <= 16 * kMsMaxG && V % 8 == 0 && B <= 32 * kMsRows &&
+           (unsigned long long)B * K * V * 2 <= kMsOob && (unsigned long long)V * r * 2 <= kMsOob;
+}
+
+__global__ __launch_bounds__(kMsThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mk_stream_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bm,
+                      const int32_t* __restrict__ map, const uint16_t* __restrict__ base,
+                      uint16_t* __restrict__ out, int B, int K, int V, int r, int pos, int nh,
+                      ArgPart* __restrict__ part) {
+    extern __shared__ __align__(16) unsigned char ms_lds[];
+    unsigned char* const bm_lds = ms_lds;
+    unsigned char* const base_lds = ms_lds + kMsBmSlots * kMsBmBytes;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int xcd = (int)blockIdx.x % 8, idx = (int)blockIdx.x / 8;
+    const int half = idx % nh;
+    const int S = kMsGrid / nh;                    // column slots
+    const int slot = xcd * (32 / nh) + idx / nh;
+    const int row0 = half * kMsRows;
+    if (row0 >= B) return;                         // no requests here (whole workgroup)
+    const int ntile = (V + kMsCols - 1) / kMsCols;
+    const int ng = r / 16;
+    // The slot's tiles are a contiguous range t0 .. t0 + nj - 1 of the row:
+    // at any time the CUs then touch many separate stretches of the rows,
+    // which HBM serves faster than every CU in one narrow band of columns.
+    const int t0 = (int)((long long)slot * ntile / S);
+    const int nj = (int)((long long)(slot + 1) * ntile / S) - t0;
+    const long long rowlen = (long long)K * V;     // elements between one request's rows
+
+    // This lane's request: tile row trow = 32 wave + l % 32, request
+    // row0 + trow (lanes l and l + 32 share it, k-pieces l / 32).
+    const int trow = wave * 32 + (lane & 31);
+    const int req = row0 + trow;
+    ms_bf16x8 af[kMsMaxG];
+    {
+        const int x = req < B ? map[req] : -1;
+        const uint16_t* arow = A + (size_t)(x < 0 ? 0 : x) * r + 8 * (lane >> 5);
+        #pragma unroll
+        for (int g = 0; g < kMsMaxG; ++g) {
+            ms_bf16x8 v = {};
+            if (g < ng && x >= 0) v = *reinterpret_cast<const ms_bf16x8*>(arow + 16 * g);
+            af[g] = v;
+        }
+    }
+
+    const __amdgpu_buffer_rsrc_t bm_rs = svdma::rsrc(Bm, (unsigned)((size_t)V * r * 2));
+    // The backbone's and the stored rows' range ends with request B - 1's
+    // row of this position.
+    const unsigned row_range = (unsigned)(((size_t)(B - 1) * rowlen + V) * 2);
+    const __amdgpu_buffer_rsrc_t base_rs = svdma::rsrc(base, row_range);
+    const __amdgpu_buffer_rsrc_t out_rs = svdma::rsrc(out, row_range);
+
+    // Tile loads, 2 of Bm and then 2 of the backbone per wave. Bm:
+    // instruction q = 2 wave + n moves rows 2q, 2q + 1 of the tile, lane l
+    // row 2q + l / 32, its 16-byte piece l % 32 holding k-piece
+    // (l % 32) ^ (row % 16) (pieces past r / 8 and rows past V read zeros).
+    // Backbone: instruction q moves rows 16q .. 16q + 15, lane l row
+    // 16q + l / 4, piece l % 4 holding columns 8 ((l % 4) ^ ((row / 4) % 4))
+    // .. + 8 (requests past B read zeros): a wave moves its own requests'
+    // rows. The lane parts of the offsets are fixed; a tile adds its first
+    // column's (an offset past the range stays past it).
+    unsigned bm_off[2], base_off[2];
+    #pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int q = 2 * wave + n;
+        const int row = 2 * q + (lane >> 5);
+        const int p = (lane & 31) ^ (row & 15);
+        bm_off[n] = p < r / 8 ? (unsigned)row * (unsigned)(2 * r) + 16u * (unsigned)p : kMsOob;
+        const int brow = 16 * q + (lane >> 2);
+        const int b = row0 + brow;
+        base_off[n] = b < B ? (unsigned)((long long)b * rowlen * 2) +
+                                  16u * (unsigned)((lane & 3) ^ ((brow >> 2) & 3))
+                            : kMsOob;
+    }
+    auto issue = [&](int j) {
+        const unsigned v0 = (unsigned)((t0 + j) * kMsCols);
+        unsigned char* bdst = bm_lds + (j % kMsBmSlots) * kMsBmBytes;
+        unsigned char* ddst = base_lds + (j % kMsBaseSlots) * kMsBaseBytes;
+        #pragma unroll
+        for (int n = 0; n < 2; ++n)
+            svdma::load16(bm_rs, bm_off[n] + v0 * (unsigned)(2 * r), bdst + (2 * wave + n) * 1024);
+        #pragma unroll
+        for (int n = 0; n < 2; ++n)
+            svdma::load16(base_rs, base_off[n] + 2u * v0, ddst + (2 * wave + n) * 1024);
+    };
+
+    // The running maximum of this lane's stored values over its columns,
+    // and the first tile that reached it (-1: none yet).
+    float bv = -INFINITY;
+    int bt = -1;
+    ms_f32x16 acc[2];                              // [tile parity]
+
+    // Tile j's bias into c: Bm's fragment of k-group g is lane l's row
+    // l % 32, k-piece 2 g + l / 32. Every k-group takes part: past r / 8
+    // pieces both operands hold zeros.
+    auto product = [&](int j, ms_f32x16& c) {
+        const unsigned char* src = bm_lds + (j % kMsBmSlots) * kMsBmBytes + (lane & 31) * 512;
+        ms_bf16x8 bf[kMsMaxG];
+        #pragma unroll
+        for (int g = 0; g < kMsMaxG; ++g)
+            bf[g] = *reinterpret_cast<const ms_bf16x8*>(src + 16 * ((2 * g + (lane >> 5)) ^ (lane & 15)));
+        const ms_f32x16 zero = {};
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[0], af[0], zero, 0, 0, 0);
+        #pragma unroll
+        for (int g = 1; g < kMsMaxG; ++g)
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[g], af[g], c, 0, 0, 0);
+    };
+
+    // The epilogue's lane parts: the backbone values of row trow, columns
+    // 4 (l / 32) + 8 q .. + 4, sit at ad0[q] of a slot; the store pieces
+    // (row 16 (2 wave + n) + l / 4, columns st_col[n] .. + 8 of the tile)
+    // at 1024 (2 wave + n) + 16 l, their rows at st_off[n] (past the range
+    // for requests past B).
+    unsigned ad0[4], sa0[2], st_off[2];
+    int st_col[2];
+    #pragma unroll
+    for (int q = 0; q < 4; ++q)
+        ad0[q] = (unsigned)(trow * 64 + 16 * (q ^ ((trow >> 2) & 3)) + 8 * (lane >> 5));
+    #pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int row = 16 * (2 * wave + n) + (lane >> 2);
+        sa0[n] = (unsigned)((2 * wave + n) * 1024 + 16 * lane);
+        st_col[n] = 8 * ((lane & 3) ^ ((row >> 2) & 3));
+        st_off[n] = row0 + row < B ? (unsigned)((long long)(row0 + row) * rowlen * 2) +
+                                         2u * (unsigned)st_col[n]
+                                   : kMsOob;
+    }
+
+    // Tile j's rows out: lane l's values are columns v0 + 4 (l / 32) + 8 q
+    // + e (q, e < 4), element 4 q + e of the block. The rounded values go
+    // back into the backbone's slot (each lane where it read its backbone
+    // values) and leave from there as 16-byte pieces, 4 lanes a 64-byte row
+    // segment, in the backbone loads' layout. A wave's backbone rows are its
+    // own in both layouts, so the slot needs no barrier.
+    auto finish = [&](int j, const ms_f32x16& c) {
+        const int v0 = (t0 + j) * kMsCols;
+        const unsigned sb = ms_lds_addr(base_lds + (j % kMsBaseSlots) * kMsBaseBytes);
+        unsigned ad[4];
+        #pragma unroll
+        for (int q = 0; q < 4; ++q) ad[q] = sb + ad0[q];
+        uint2 bw[4];
+        ms_read4(bw, ad);
+        float sm[16];
+        #pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            sm[4 * q] = __uint_as_float(bw[q].x << 16) + c[4 * q];
+            sm[4 * q + 1] = __uint_as_float(bw[q].x & 0xFFFF0000u) + c[4 * q + 1];
+            sm[4 * q + 2] = __uint_as_float(bw[q].y << 16) + c[4 * q + 2];
+            sm[4 * q + 3] = __uint_as_float(bw[q].y & 0xFFFF0000u) + c[4 * q + 3];
+            bw[q] = make_uint2(ms_pack_bf16(sm[4 * q], sm[4 * q + 1]),
+                               ms_pack_bf16(sm[4 * q + 2], sm[4 * q + 3]));
+        }
+        ms_write4(bw, ad);
+        unsigned sa[2];
+        #pragma unroll
+        for (int n = 0; n < 2; ++n) sa[n] = sb + sa0[n];
+        uint4 ov[2];
+        ms_read2x16(ov, sa);
+        #pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const unsigned off = v0 + st_col[n] < V ? st_off[n] + 2u * (unsigned)v0 : kMsOob;
+            const ms_u32x4 d = {ov[n].x, ov[n].y, ov[n].z, ov[n].w};
+            __builtin_amdgcn_raw_buffer_store_b128(d, out_rs, off, 0, 0);
+        }
+        // Columns from V on (only in the row's last tile) take no part.
+        if (v0 + kMsCols > V) {
+            const int c0 = v0 + 4 * (lane >> 5);
+            #pragma unroll
+            for (int k = 0; k < 16; ++k)
+                sm[k] = c0 + 8 * (k >> 2) + (k & 3) < V ? sm[k] : __uint_as_float(0x7FC00000u);
+        }
+        // The sums' maximum (fmaxf drops NaNs) rounds to the maximum of the
+        // stored values, rounding being monotone. A lane meets its columns in
+        // increasing order, over the elements and the tiles, so the first
+        // tile that reaches the maximum holds the first argmax, unless no
+        // tile has been taken yet (an equal value, -inf, wins only then).
+        float m[8];
+        #pragma unroll
+        for (int k = 0; k < 8; ++k) m[k] = fmaxf(sm[k], sm[k + 8]);
+        #pragma unroll
+        for (int k = 0; k < 4; ++k) m[k] = fmaxf(m[k], m[k + 4]);
+        const float ms = fmaxf(fmaxf(m[0], m[2]), fmaxf(m[1], m[3]));
+        const float mx = __uint_as_float(ms_pack_bf16(ms, ms) << 16);
+        const bool take = (mx > bv) | ((mx == bv) & (bt < 0));
+        bv = take ? mx : bv;
+        bt = take ? j : bt;
+    };
+
+    // Tiles 0, 1 and 2 go out first; every step issues one more tile's
+    // loads, past the last tile too (into slots that are not read again), so
+    // each wait counts the same loads: the 2 of the awaited tile's backbone
+    // and the 8 of the next two tiles. Step j (1 <= j < nj) waits for tile
+    // j's Bm (and every earlier load), passes the barrier that makes the Bm
+    // tile visible and frees tile j - 1's Bm slot, finishes tile j - 1,
+    // refills the slots tile j - 1 used with tile j + 3 and forms tile j's
+    // bias; the loop is unrolled by two so that each half takes one
+    // accumulator parity. The backbone tile of the last finish is the
+    // wave's own, so it needs only the wait.
+    if (nj > 0) {
+        issue(0);
+        issue(1);
+        issue(2);
+        svdma::wait_vm<10>();
+        svdma::ring_barrier();
+        issue(3);
+        product(0, acc[0]);
+        auto step = [&](int j, ms_f32x16& cur, const ms_f32x16& prev) {
+            svdma::wait_vm<10>();
+            svdma::ring_barrier();
+            finish(j - 1, prev);
+            issue(j + 3);
+            product(j, cur);
+        };
+        for (int j = 1; j < nj; j += 2) {
+            step(j, acc[1], acc[0]);
+            if (j + 1 < nj) step(j + 1, acc[0], acc[1]);
+        }
+        // Loads after tile nj - 1's backbone: tiles nj .. nj + 2.
+        svdma::wait_vm<12>();
+        if (nj & 1) finish(nj - 1, acc[0]);
+        else finish(nj - 1, acc[1]);
+    }
+
+    // The lane's first column holding its maximum, in the tile that first
+    // reached it: that tile's stored values of the request, read back once
+    // the wave's stores are complete (the wave stored them itself; the loads
+    // bypass the vector L1). Columns from V on are not read, and a valid
+    // column reaches the maximum before them.
+    svdma::wait_vm<0>();
+    int bi = INT_MAX;
+    if (bt >= 0) {
+        const int c0 = (t0 + bt) * kMsCols + 4 * (lane >> 5);
+        uint2 w[4];
+        #pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int col = c0 + 8 * q;
+            const unsigned off = col < V ? (unsigned)(((long long)req * rowlen + col) * 2) : kMsOob;
+            w[q] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(out_rs, off, 0, 1));
+        }
+        #pragma unroll
+        for (int k = 15; k >= 0; --k) {
+            const uint32_t h = (k & 2) ? w[k >> 2].y : w[k >> 2].x;
+            const float v = __uint_as_float((k & 1) ? (h & 0xFFFF0000u) : (h << 16));
+            bi = v == bv ? c0 + 8 * (k >> 2) + (k & 3) : bi;
+        }
+    }
+
+    // The lane pair holding a request merges, lane < 32 writes its partial.
+    {
+        const float ov = __shfl_xor(bv, 32, 64);
+        const int oi = __shfl_xor(bi, 32, 64);
+        if (mk_better(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+        }
+        if (lane < 32 && req < B) part[(size_t)slot * B + req] = ArgPart{bv, bi};
+    }
+    svdma::wait_vm<0>();                           // the last stores
 }
 
 // Position i's token of each request, one wave per request: the first
@@ -169,6 +538,25 @@ extern "C" int spec_markov_draft(const void* base_logits, const void* markov_a,
     hipLaunchKernelGGL(mk_seed_kernel, dim3(1), dim3(1024), 0, s, prev_tokens, B, V, map[0],
                        out_status);
     if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+    if (ms_path(B, K, V, r)) {
+        static const hipError_t attr = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&mk_stream_kernel),
+            hipFuncAttributeMaxDynamicSharedMemorySize, kMsLds);
+        if (attr != hipSuccess) return SV_ERR_HIP;
+        const int nh = ms_halves(B), slots = kMsGrid / nh;
+        for (int i = 0; i < K; ++i) {
+            hipLaunchKernelGGL(mk_stream_kernel, dim3(kMsGrid), dim3(kMsThreads), kMsLds, s, A, Bm,
+                               map[i & 1], base + (size_t)i * V, out + (size_t)i * V, B, K, V, r,
+                               i, nh, parts);
+            if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+            hipLaunchKernelGGL(mk_pick_kernel,
+                               dim3((unsigned)((B + kMkPickWaves - 1) / kMkPickWaves)),
+                               dim3(kMkPickThreads), 0, s, parts, slots, B, K, V, i, out_tokens,
+                               map[(i + 1) & 1]);
+            if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+        }
+        return SV_OK;
+    }
     for (int i = 0; i < K; ++i) {
         // Rows of A indexed by the previous tokens; virtual rows >= V never
         // occur (tokens are checked, argmaxes lie in [0, V)).

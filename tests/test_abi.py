@@ -292,9 +292,9 @@ def test_markov_draft_workspace_size():
     assert sb.spec_markov_draft_workspace_bytes(4, sb.SV_MAX_VOCAB + 1) == 0
     n = sb.spec_markov_draft_workspace_bytes(512, 151936)
     # Two token maps of B entries each and an 8-byte first argmax per request
-    # and vocabulary split: 128 splits of the 1,187 vocabulary tiles for four
-    # 128-row tiles (one resident wave of 512 workgroups). The bias rows never
-    # reach memory.
+    # and vocabulary split: 128 column slots for each of the two groups of 256
+    # requests (one workgroup per CU), as many as the many-row product's
+    # splits. The bias rows never reach memory.
     want = 2 * 4 * 512 + 128 * 512 * 8
     assert want <= n <= want + 3 * 255
 
