@@ -28,9 +28,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, unsigned n
 // loads rather than global ones: with a global load to LDS in flight the
 // compiler must assume it may also count as an LDS access and drains every
 // LDS read before the next use of one.
+// kAux is the instruction's cache policy (2: non-temporal, for data read
+// once, so that it leaves the L2 before data that is read again).
+template <int kAux = 0>
 __device__ __forceinline__ void load16(__amdgpu_buffer_rsrc_t r, unsigned off, unsigned char* lds) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
-                                             (int)off, 0, 0, 0);
+                                             (int)off, 0, 0, kAux);
 }
 
 // Wait until at most N of this wave's vector memory operations are

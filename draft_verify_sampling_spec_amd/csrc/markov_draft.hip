@@ -132,9 +132,10 @@ constexpr int kMsThreads = 512;                    // 8 waves, 32 requests each
 constexpr int kMsCols = 32;                        // vocabulary columns per tile
 constexpr int kMsMaxG = 16;                        // k-groups of 16: r <= 256
 constexpr int kMsBmBytes = kMsCols * 512;          // one Bm tile: 32 rows of 512 bytes
-constexpr int kMsBaseBytes = kMsRows * kMsCols * 2;   // one backbone tile: 256 rows of 64 bytes
-constexpr int kMsBmSlots = 4, kMsBaseSlots = 5;    // tiles three ahead
-constexpr int kMsLds = kMsBmSlots * kMsBmBytes + kMsBaseSlots * kMsBaseBytes;   // 144 KB
+constexpr int kMsPairBytes = kMsRows * kMsCols * 4;   // two backbone tiles: 256 rows of 128 bytes
+constexpr int kMsBmSlots = 4;                      // Bm tiles three ahead
+constexpr int kMsPairSlots = 3;                    // backbone pairs two ahead
+constexpr int kMsLds = kMsBmSlots * kMsBmBytes + kMsPairSlots * kMsPairBytes;   // 160 KB
 constexpr unsigned kMsOob = 0x80000000u;           // past every buffer's range
 
 typedef __bf16 ms_bf16x8 __attribute__((ext_vector_type(8)));
@@ -181,6 +182,17 @@ __device__ __forceinline__ void ms_write4(const uint2 (&v)[4], const unsigned (&
           "v"(v[3])
         : "memory");
 }
+__device__ __forceinline__ void ms_read4x16(uint4 (&v)[4], const unsigned (&ad)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+        : "memory");
+}
 __device__ __forceinline__ void ms_read2x16(uint4 (&v)[2], const unsigned (&ad)[2]) {
     asm volatile(
         "ds_read_b128 %0, %2\n\t"
@@ -220,11 +232,12 @@ void mk_stream_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
     if (row0 >= B) return;                         // no requests here (whole workgroup)
     const int ntile = (V + kMsCols - 1) / kMsCols;
     const int ng = r / 16;
-    // The slot's tiles are a contiguous range t0 .. t0 + nj - 1 of the row:
-    // at any time the CUs then touch many separate stretches of the rows,
-    // which HBM serves faster than every CU in one narrow band of columns.
-    const int t0 = (int)((long long)slot * ntile / S);
-    const int nj = (int)((long long)(slot + 1) * ntile / S) - t0;
+    // The slot's tiles are a contiguous range t0 .. t0 + nj - 1 of the row,
+    // whole pairs of tiles (t0 even) but for the row's last, so that two
+    // tiles' rows leave as 128-byte segments.
+    const int npair = (ntile + 1) / 2;
+    const int t0 = 2 * (int)((long long)slot * npair / S);
+    const int nj = std::min(2 * (int)((long long)(slot + 1) * npair / S), ntile) - t0;
     const long long rowlen = (long long)K * V;     // elements between one request's rows
 
     // This lane's request: tile row trow = 32 wave + l % 32, request
@@ -250,38 +263,48 @@ void mk_stream_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
     const __amdgpu_buffer_rsrc_t base_rs = svdma::rsrc(base, row_range);
     const __amdgpu_buffer_rsrc_t out_rs = svdma::rsrc(out, row_range);
 
-    // Tile loads, 2 of Bm and then 2 of the backbone per wave. Bm:
-    // instruction q = 2 wave + n moves rows 2q, 2q + 1 of the tile, lane l
-    // row 2q + l / 32, its 16-byte piece l % 32 holding k-piece
-    // (l % 32) ^ (row % 16) (pieces past r / 8 and rows past V read zeros).
-    // Backbone: instruction q moves rows 16q .. 16q + 15, lane l row
-    // 16q + l / 4, piece l % 4 holding columns 8 ((l % 4) ^ ((row / 4) % 4))
-    // .. + 8 (requests past B read zeros): a wave moves its own requests'
-    // rows. The lane parts of the offsets are fixed; a tile adds its first
-    // column's (an offset past the range stays past it).
-    unsigned bm_off[2], base_off[2];
+    // Loads. Bm, tile j, 2 per wave: instruction q = 2 wave + n moves rows
+    // 2q, 2q + 1 of the tile, lane l row 2q + l / 32, its 16-byte piece
+    // l % 32 holding k-piece (l % 32) ^ (row % 16) (pieces past r / 8 and
+    // rows past V read zeros). Backbone, tiles 2P and 2P + 1 as one pair of
+    // 128-byte row segments, 4 per wave: instruction q = 4 wave + n moves
+    // rows 8q .. 8q + 7, lane l row 8q + l / 8 at position l % 8, which holds
+    // the row's 16-byte piece (l % 8) ^ (row % 8), columns 8 of them from
+    // the pair's first (requests past B read zeros): a wave moves its own
+    // requests' rows. The lane parts of the offsets are fixed; a tile or a
+    // pair adds its first column's (an offset past the range stays past it).
+    unsigned bm_off[2], bp_off[4];
     #pragma unroll
     for (int n = 0; n < 2; ++n) {
         const int q = 2 * wave + n;
         const int row = 2 * q + (lane >> 5);
         const int p = (lane & 31) ^ (row & 15);
         bm_off[n] = p < r / 8 ? (unsigned)row * (unsigned)(2 * r) + 16u * (unsigned)p : kMsOob;
-        const int brow = 16 * q + (lane >> 2);
-        const int b = row0 + brow;
-        base_off[n] = b < B ? (unsigned)((long long)b * rowlen * 2) +
-                                  16u * (unsigned)((lane & 3) ^ ((brow >> 2) & 3))
-                            : kMsOob;
     }
-    auto issue = [&](int j) {
+    #pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        const int row = 8 * (4 * wave + n) + (lane >> 3);
+        const int b = row0 + row;
+        bp_off[n] = b < B ? (unsigned)((long long)b * rowlen * 2) +
+                                16u * (unsigned)((lane & 7) ^ (row & 7))
+                          : kMsOob;
+    }
+    auto issue_bm = [&](int j) {
         const unsigned v0 = (unsigned)((t0 + j) * kMsCols);
-        unsigned char* bdst = bm_lds + (j % kMsBmSlots) * kMsBmBytes;
-        unsigned char* ddst = base_lds + (j % kMsBaseSlots) * kMsBaseBytes;
+        unsigned char* dst = bm_lds + (j % kMsBmSlots) * kMsBmBytes;
         #pragma unroll
         for (int n = 0; n < 2; ++n)
-            svdma::load16(bm_rs, bm_off[n] + v0 * (unsigned)(2 * r), bdst + (2 * wave + n) * 1024);
+            svdma::load16(bm_rs, bm_off[n] + v0 * (unsigned)(2 * r), dst + (2 * wave + n) * 1024);
+    };
+    // The backbone is read once and the stored rows are not read again, so
+    // both go non-temporal: they leave the L2 first and Bm's tiles, which the
+    // slot's other workgroup reads too, stay.
+    auto issue_pair = [&](int P) {
+        const unsigned vp = (unsigned)((t0 + 2 * P) * kMsCols);
+        unsigned char* dst = base_lds + (P % kMsPairSlots) * kMsPairBytes;
         #pragma unroll
-        for (int n = 0; n < 2; ++n)
-            svdma::load16(base_rs, base_off[n] + 2u * v0, ddst + (2 * wave + n) * 1024);
+        for (int n = 0; n < 4; ++n)
+            svdma::load16<2>(base_rs, bp_off[n] + 2u * vp, dst + (4 * wave + n) * 1024);
     };
 
     // The running maximum of this lane's stored values over its columns,
@@ -306,38 +329,51 @@ void mk_stream_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
             c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[g], af[g], c, 0, 0, 0);
     };
 
-    // The epilogue's lane parts: the backbone values of row trow, columns
-    // 4 (l / 32) + 8 q .. + 4, sit at ad0[q] of a slot; the store pieces
-    // (row 16 (2 wave + n) + l / 4, columns st_col[n] .. + 8 of the tile)
-    // at 1024 (2 wave + n) + 16 l, their rows at st_off[n] (past the range
-    // for requests past B).
-    unsigned ad0[4], sa0[2], st_off[2];
-    int st_col[2];
+    // The epilogue's lane parts, within a pair's slot: the backbone values
+    // of row trow, columns 4 (l / 32) + 8 q .. + 4 of the pair's first tile,
+    // sit at ad0[q] (of its second tile at ad0[q] ^ 64: piece q + 4); the
+    // store pieces of a pair (row 8 (4 wave + n) + l / 8, columns
+    // 8 (l % 8) .. + 8 of the pair) at pa0[n], their rows at pr_off[n]; those
+    // of a lone first tile (row 16 (2 wave + n) + l / 4, columns
+    // 8 (l % 4) .. + 8) at sa0[n], their rows at st_off[n] (offsets past the
+    // range for requests past B).
+    unsigned ad0[4], pa0[4], pr_off[4], sa0[2], st_off[2];
     #pragma unroll
     for (int q = 0; q < 4; ++q)
-        ad0[q] = (unsigned)(trow * 64 + 16 * (q ^ ((trow >> 2) & 3)) + 8 * (lane >> 5));
+        ad0[q] = (unsigned)(trow * 128 + 16 * (q ^ (trow & 7)) + 8 * (lane >> 5));
+    #pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        const int row = 8 * (4 * wave + n) + (lane >> 3);
+        pa0[n] = (unsigned)(row * 128 + 16 * ((lane & 7) ^ (row & 7)));
+        pr_off[n] = row0 + row < B ? (unsigned)((long long)(row0 + row) * rowlen * 2) +
+                                         16u * (unsigned)(lane & 7)
+                                   : kMsOob;
+    }
     #pragma unroll
     for (int n = 0; n < 2; ++n) {
         const int row = 16 * (2 * wave + n) + (lane >> 2);
-        sa0[n] = (unsigned)((2 * wave + n) * 1024 + 16 * lane);
-        st_col[n] = 8 * ((lane & 3) ^ ((row >> 2) & 3));
+        sa0[n] = (unsigned)(row * 128 + 16 * ((lane & 3) ^ (row & 7)));
         st_off[n] = row0 + row < B ? (unsigned)((long long)(row0 + row) * rowlen * 2) +
-                                         2u * (unsigned)st_col[n]
+                                         16u * (unsigned)(lane & 3)
                                    : kMsOob;
     }
 
     // Tile j's rows out: lane l's values are columns v0 + 4 (l / 32) + 8 q
     // + e (q, e < 4), element 4 q + e of the block. The rounded values go
-    // back into the backbone's slot (each lane where it read its backbone
-    // values) and leave from there as 16-byte pieces, 4 lanes a 64-byte row
-    // segment, in the backbone loads' layout. A wave's backbone rows are its
+    // back into the pair's slot (each lane where it read its backbone
+    // values) and leave from there once the pair is complete, as 16-byte
+    // pieces, 8 lanes a 128-byte row segment. A wave's backbone rows are its
     // own in both layouts, so the slot needs no barrier.
-    auto finish = [&](int j, const ms_f32x16& c) {
+    // `out_mode`: 0 keeps tile j (even) in its pair's slot, 1 stores the
+    // pair with tile j (odd), 2 stores tile j alone (the row's last tile,
+    // even and unpaired).
+    auto finish = [&](int j, const ms_f32x16& c, int out_mode) {
         const int v0 = (t0 + j) * kMsCols;
-        const unsigned sb = ms_lds_addr(base_lds + (j % kMsBaseSlots) * kMsBaseBytes);
+        const unsigned sb = ms_lds_addr(base_lds + ((j >> 1) % kMsPairSlots) * kMsPairBytes);
+        const unsigned hx = out_mode == 1 ? 64u : 0u;   // the pair's second tile
         unsigned ad[4];
         #pragma unroll
-        for (int q = 0; q < 4; ++q) ad[q] = sb + ad0[q];
+        for (int q = 0; q < 4; ++q) ad[q] = sb + (ad0[q] ^ hx);
         uint2 bw[4];
         ms_read4(bw, ad);
         float sm[16];
@@ -351,16 +387,33 @@ void mk_stream_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
                                ms_pack_bf16(sm[4 * q + 2], sm[4 * q + 3]));
         }
         ms_write4(bw, ad);
-        unsigned sa[2];
-        #pragma unroll
-        for (int n = 0; n < 2; ++n) sa[n] = sb + sa0[n];
-        uint4 ov[2];
-        ms_read2x16(ov, sa);
-        #pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            const unsigned off = v0 + st_col[n] < V ? st_off[n] + 2u * (unsigned)v0 : kMsOob;
-            const ms_u32x4 d = {ov[n].x, ov[n].y, ov[n].z, ov[n].w};
-            __builtin_amdgcn_raw_buffer_store_b128(d, out_rs, off, 0, 0);
+        if (out_mode == 1) {
+            const int vp = v0 - kMsCols;           // the pair's first column
+            unsigned sa[4];
+            #pragma unroll
+            for (int n = 0; n < 4; ++n) sa[n] = sb + pa0[n];
+            uint4 ov[4];
+            ms_read4x16(ov, sa);
+            #pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const unsigned off =
+                    vp + 8 * (lane & 7) < V ? pr_off[n] + 2u * (unsigned)vp : kMsOob;
+                const ms_u32x4 d = {ov[n].x, ov[n].y, ov[n].z, ov[n].w};
+                __builtin_amdgcn_raw_buffer_store_b128(d, out_rs, off, 0, 2);
+            }
+        } else if (out_mode == 2) {
+            unsigned sa[2];
+            #pragma unroll
+            for (int n = 0; n < 2; ++n) sa[n] = sb + sa0[n];
+            uint4 ov[2];
+            ms_read2x16(ov, sa);
+            #pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const unsigned off =
+                    v0 + 8 * (lane & 3) < V ? st_off[n] + 2u * (unsigned)v0 : kMsOob;
+                const ms_u32x4 d = {ov[n].x, ov[n].y, ov[n].z, ov[n].w};
+                __builtin_amdgcn_raw_buffer_store_b128(d, out_rs, off, 0, 2);
+            }
         }
         // Columns from V on (only in the row's last tile) take no part.
         if (v0 + kMsCols > V) {
@@ -386,39 +439,45 @@ void mk_stream_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
         bt = take ? j : bt;
     };
 
-    // Tiles 0, 1 and 2 go out first; every step issues one more tile's
-    // loads, past the last tile too (into slots that are not read again), so
-    // each wait counts the same loads: the 2 of the awaited tile's backbone
-    // and the 8 of the next two tiles. Step j (1 <= j < nj) waits for tile
-    // j's Bm (and every earlier load), passes the barrier that makes the Bm
-    // tile visible and frees tile j - 1's Bm slot, finishes tile j - 1,
-    // refills the slots tile j - 1 used with tile j + 3 and forms tile j's
+    // Load order, as if steps -4 .. -1 had run: step s issues backbone pair
+    // s / 2 + 2 when s is even, then Bm tile s + 3, so pair 0 and Bm tiles
+    // 0 .. 2 and pair 1 go out first; every step issues its loads, past the
+    // last tile too (into slots that are not read again), so each wait
+    // counts the same loads. Step j waits for Bm tile j (and every earlier
+    // load: pair (j - 1) / 2 went out before it); after it come Bm tiles
+    // j + 1 and j + 2 (2 loads each) and one pair (4). It passes the barrier
+    // that makes the Bm tile visible and frees tile j - 1's Bm slot,
+    // finishes tile j - 1 (storing the pair when j - 1 is odd, which frees
+    // that pair's slot for the pair issued next), issues and forms tile j's
     // bias; the loop is unrolled by two so that each half takes one
-    // accumulator parity. The backbone tile of the last finish is the
-    // wave's own, so it needs only the wait.
+    // accumulator parity and one tile parity.
     if (nj > 0) {
-        issue(0);
-        issue(1);
-        issue(2);
-        svdma::wait_vm<10>();
+        issue_pair(0);
+        issue_bm(0);
+        issue_pair(1);
+        issue_bm(1);
+        issue_bm(2);
+        svdma::wait_vm<8>();
         svdma::ring_barrier();
-        issue(3);
+        issue_pair(2);
+        issue_bm(3);
         product(0, acc[0]);
-        auto step = [&](int j, ms_f32x16& cur, const ms_f32x16& prev) {
-            svdma::wait_vm<10>();
+        auto step = [&](int j, ms_f32x16& cur, const ms_f32x16& prev, int out_mode) {
+            svdma::wait_vm<8>();
             svdma::ring_barrier();
-            finish(j - 1, prev);
-            issue(j + 3);
+            finish(j - 1, prev, out_mode);
+            if (out_mode == 1) issue_pair(j / 2 + 2);
+            issue_bm(j + 3);
             product(j, cur);
         };
         for (int j = 1; j < nj; j += 2) {
-            step(j, acc[1], acc[0]);
-            if (j + 1 < nj) step(j + 1, acc[0], acc[1]);
+            step(j, acc[1], acc[0], 0);            // tile j - 1 even: kept
+            if (j + 1 < nj) step(j + 1, acc[0], acc[1], 1);   // tile j odd: the pair leaves
         }
-        // Loads after tile nj - 1's backbone: tiles nj .. nj + 2.
-        svdma::wait_vm<12>();
-        if (nj & 1) finish(nj - 1, acc[0]);
-        else finish(nj - 1, acc[1]);
+        // The last pair's backbone went out at least 16 loads before the end.
+        svdma::wait_vm<16>();
+        if (nj & 1) finish(nj - 1, acc[0], 2);
+        else finish(nj - 1, acc[1], 1);
     }
 
     // The lane's first column holding its maximum, in the tile that first
