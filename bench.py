@@ -303,6 +303,21 @@ def bench_scheduler(B, K, steps, seed=5):
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 
 
+def warm_up(fn, min_s=0.25, min_calls=3):
+    """Untimed calls until the clocks have settled under the load: at least
+    `min_calls`, and at least `min_s` seconds of work."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while n < min_calls or time.perf_counter() - t0 < min_s:
+        fn(n)
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def bench_head(R, H, V, steps, T=1.0, seed=5):
     """The shared output head with its statistics epilogue on the verify
     batch's rows (target and drafter positions), synthetic bf16 hidden states
@@ -313,9 +328,7 @@ def bench_head(R, H, V, steps, T=1.0, seed=5):
     from draft_verify_sampling_spec_amd import head_stats
     from workloads import make_head_inputs
     h, w, tok = make_head_inputs(R, H, V, seed)
-    for _ in range(3):
-        head_stats(h, w, tok, T)
-    torch.cuda.synchronize()
+    warm_up(lambda n: head_stats(h, w, tok, T))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     for a, b in ev:
@@ -365,9 +378,7 @@ def bench_hidden(B, K, H, V, steps, T=1.0, seed=5):
     inp = make_hidden_inputs(B, K, H, V, seed, device="cuda:0", variant="heavy", temperature=T)
     hv = HiddenVerify("cuda:0", B, K, V)
     args = (inp["target_hidden"], inp["draft_hidden"], inp["head"], inp["tokens"], inp["budgets"], T)
-    for s in range(3):
-        hv.run(*args, philox_seed(WORKLOAD_INDEX["heavy"], 3_000_000 + s))
-    torch.cuda.synchronize()
+    warm_up(lambda n: hv.run(*args, philox_seed(WORKLOAD_INDEX["heavy"], 3_000_000 + n)))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     outs = []
@@ -423,8 +434,8 @@ def bench_markov(B, K, V, r, steps, seed=5):
     (only the 32 columns of each request's best tile); each group of 256
     requests after the first may read the vocabulary factor again where the
     L2 has not kept it, which is implementation traffic (counted in full
-    below, as an upper bound). Ten untimed calls first bring the clocks to
-    their sustained state. The oracle is timed on one request's block and
+    below, as an upper bound). Untimed calls first bring the clocks to their
+    sustained state. The oracle is timed on one request's block and
     scaled to the batch."""
     import numpy as np
     import torch
@@ -435,9 +446,7 @@ def bench_markov(B, K, V, r, steps, seed=5):
     out_z = torch.empty((B, K, V), dtype=torch.bfloat16, device="cuda:0")
     out_x = torch.empty((B, K), dtype=torch.int32, device="cuda:0")
     args = (inp["base"], inp["markov_a"], inp["markov_b"], inp["prev"])
-    for _ in range(10):
-        md.run(*args, out_logits=out_z, out_tokens=out_x)
-    torch.cuda.synchronize()
+    warm_up(lambda n: md.run(*args, out_logits=out_z, out_tokens=out_x), min_calls=10)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     for a, b in ev:
