@@ -96,6 +96,17 @@ SHAPES = [
     (16, 4, 65536, 128),      # two k-steps, 64 splits (XCD order)
     (9, 3, 30000, 192),       # three k-steps: the last fetch repeats step 2
     (200, 2, 40960, 128),     # two row tiles, 40 splits (XCD order)
+    # The streaming product (r a multiple of 16, V of 8): 32-column tiles,
+    # stored in pairs; these give an odd tile count (the row's last tile
+    # stored alone), a partial last tile alone and as the second of a pair,
+    # four groups of 256 requests (the last empty), one request in the
+    # second group, a single k-group, and one position.
+    (40, 3, 3104, 64),        # 97 tiles: the last one unpaired and full
+    (24, 2, 3080, 32),        # 97 tiles: the last one unpaired, 8 columns
+    (24, 2, 3048, 48),        # 96 tiles: the last pair's second tile, 8 columns
+    (600, 2, 8192, 64),       # four request groups, the fourth empty
+    (257, 2, 4096, 16),       # one request in the second group; one k-group
+    (64, 1, 16384, 128),      # one position
 ]
 
 
@@ -149,8 +160,9 @@ def test_successor_chain():
 
 def test_ties_across_vocabulary_splits():
     # No transition term, so the stored rows are the backbone's; values on a
-    # coarse grid tie for the maximum in many vocabulary splits (40 splits of
-    # 8 tiles at V = 40,960), and the token must be the lowest such column.
+    # coarse grid tie for the maximum in many vocabulary splits (at
+    # V = 40,960: 1,280 tiles of 32 columns over 256 column slots), and the
+    # token must be the lowest such column.
     B, K, V, r = 6, 3, 40960, 16
     g = torch.Generator().manual_seed(21)
     base = torch.randint(-2, 3, (B, K, V), generator=g).float()
