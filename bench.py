@@ -482,7 +482,7 @@ def bench_markov(B, K, V, r, steps, seed=5):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes_per_call": alg,
                      "implementation_factor_rereads_bytes_per_call": impl_extra,
-                     "note": "whole call, 1 + 2K launches"},
+                     "note": "whole call, K + 2 launches"},
         "cpu_oracle_s_per_call": cpu_s,
         "cpu_oracle_sample": f"fp64 oracle on request 0's block of {K} positions, scaled to {B} requests",
     }

@@ -60,7 +60,7 @@ inline int ms_halves(int B) {
 }
 
 struct MkLayout {
-    size_t map0, map1, parts, total;
+    size_t map0, map1, parts, keys, total;
 };
 
 size_t mk_up256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -75,19 +75,22 @@ MkLayout mk_layout(int B, int V) {
     };
     L.map0 = take((size_t)B * 4);
     L.map1 = take((size_t)B * 4);
-    // First-argmax entries per request: one per vocabulary split of either
-    // product path (the streaming one has a split per column slot).
-    const size_t splits =
-        std::max<size_t>((size_t)svhead::add_splits(B, V), (size_t)(kMsGrid / ms_halves(B)));
-    L.parts = take(splits * (size_t)B * sizeof(ArgPart));
+    // First-argmax entries per request and vocabulary split of the
+    // product path for other shapes.
+    L.parts = take((size_t)svhead::add_splits(B, V) * (size_t)B * sizeof(ArgPart));
+    // The streaming path's first-argmax keys: three arrays of B (position i
+    // writes array i % 3, the next reads it, the one before clears i + 1's).
+    L.keys = take((size_t)3 * B * sizeof(unsigned long long));
     L.total = o;
     return L;
 }
 
 // The first row map: the given last tokens; one outside [0, V) becomes -1 (a
 // row of zeros in the product) and raises SV_FLAG_BAD_TOKEN.
+// With `keys` (the streaming path) it also clears position 0's argmax keys.
 __global__ void mk_seed_kernel(const int32_t* __restrict__ prev, int B, int V,
-                               int32_t* __restrict__ map, int32_t* __restrict__ status) {
+                               int32_t* __restrict__ map, int32_t* __restrict__ status,
+                               unsigned long long* __restrict__ keys) {
     __shared__ int bad;
     if (threadIdx.x == 0) bad = 0;
     __syncthreads();
@@ -97,6 +100,7 @@ __global__ void mk_seed_kernel(const int32_t* __restrict__ prev, int B, int V,
         const bool ok = t >= 0 && t < V;
         map[b] = ok ? t : -1;
         mine |= ok ? 0 : 1;
+        if (keys) keys[b] = 0ull;
     }
     if (mine) atomicOr(&bad, 1);
     __syncthreads();
@@ -105,6 +109,30 @@ __global__ void mk_seed_kernel(const int32_t* __restrict__ prev, int B, int V,
 
 __device__ __forceinline__ bool mk_better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
+}
+
+// A (value, column) entry as a 64-bit key whose unsigned order is
+// mk_better's: the value's order-preserving bits (-0 taken as +0, so that
+// equal values tie), then the column inverted, so an equal value at a lower
+// column is larger. A column of INT_MAX (nothing taken) loses to every real
+// column; the key 0 (no entry) decodes to no column. Values are never NaN.
+__device__ __forceinline__ unsigned long long mk_key(float v, int i) {
+    const unsigned u = __float_as_uint(v == 0.0f ? 0.0f : v);
+    const unsigned hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)hi << 32) | (unsigned long long)(0xFFFFFFFFu - (unsigned)i);
+}
+// The drafted token of a merged key: its column, or 0 when no value above
+// -inf was taken (the pick kernel's rule).
+__device__ __forceinline__ int mk_key_token(unsigned long long key, int V) {
+    const unsigned i = 0xFFFFFFFFu - (unsigned)key;
+    return i < (unsigned)V ? (int)i : 0;
+}
+
+// The last position's tokens from its merged keys (the streaming path).
+__global__ void mk_final_kernel(const unsigned long long* __restrict__ keys, int B, int K, int V,
+                                int32_t* __restrict__ out_tokens) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < B) out_tokens[(size_t)b * K + K - 1] = mk_key_token(keys[b], V);
 }
 
 
@@ -216,9 +244,10 @@ inline bool ms_path(int B, int K, int V, int r) {
 
 __global__ __launch_bounds__(kMsThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mk_stream_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bm,
-                      const int32_t* __restrict__ map, const uint16_t* __restrict__ base,
-                      uint16_t* __restrict__ out, int B, int K, int V, int r, int pos, int nh,
-                      ArgPart* __restrict__ part) {
+                      const int32_t* __restrict__ map, const unsigned long long* __restrict__ kin,
+                      unsigned long long* __restrict__ kout, unsigned long long* __restrict__ kclear,
+                      const uint16_t* __restrict__ base, uint16_t* __restrict__ out, int B, int K,
+                      int V, int r, int pos, int nh, int32_t* __restrict__ out_tokens) {
     extern __shared__ __align__(16) unsigned char ms_lds[];
     unsigned char* const bm_lds = ms_lds;
     unsigned char* const base_lds = ms_lds + kMsBmSlots * kMsBmBytes;
@@ -246,7 +275,20 @@ void mk_stream_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
     const int req = row0 + trow;
     ms_bf16x8 af[kMsMaxG];
     {
-        const int x = req < B ? map[req] : -1;
+        // The previous token: the given one (map, -1 when invalid) at
+        // position 0, else the merged key of position pos - 1, whose token
+        // the column slot 0 workgroups write out. Those also clear position
+        // pos + 1's keys (read by no launch until then).
+        int x = -1;
+        if (req < B) {
+            if (kin == nullptr) {
+                x = map[req];
+            } else {
+                x = mk_key_token(kin[req], V);
+                if (slot == 0 && lane < 32) out_tokens[(size_t)req * K + pos - 1] = x;
+            }
+            if (slot == 0 && lane < 32) kclear[req] = 0ull;
+        }
         const uint16_t* arow = A + (size_t)(x < 0 ? 0 : x) * r + 8 * (lane >> 5);
         #pragma unroll
         for (int g = 0; g < kMsMaxG; ++g) {
@@ -512,7 +554,8 @@ void mk_stream_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
             bv = ov;
             bi = oi;
         }
-        if (lane < 32 && req < B) part[(size_t)slot * B + req] = ArgPart{bv, bi};
+        // Merged over the column slots by an atomic maximum of the keys.
+        if (lane < 32 && req < B) atomicMax(kout + req, mk_key(bv, bi));
     }
     svdma::wait_vm<0>();                           // the last stores
 }
@@ -594,26 +637,31 @@ extern "C" int spec_markov_draft(const void* base_logits, const void* markov_a,
     const uint16_t* base = static_cast<const uint16_t*>(base_logits);
     uint16_t* out = static_cast<uint16_t*>(out_logits);
 
+    const bool streamed = ms_path(B, K, V, r);
+    unsigned long long* keys = reinterpret_cast<unsigned long long*>(ws + L.keys);
     hipLaunchKernelGGL(mk_seed_kernel, dim3(1), dim3(1024), 0, s, prev_tokens, B, V, map[0],
-                       out_status);
+                       out_status, streamed ? keys : nullptr);
     if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
-    if (ms_path(B, K, V, r)) {
+    if (streamed) {
         static const hipError_t attr = hipFuncSetAttribute(
             reinterpret_cast<const void*>(&mk_stream_kernel),
             hipFuncAttributeMaxDynamicSharedMemorySize, kMsLds);
         if (attr != hipSuccess) return SV_ERR_HIP;
-        const int nh = ms_halves(B), slots = kMsGrid / nh;
+        // One launch per position: position i merges its first argmaxes
+        // into keys array i % 3, reads position i - 1's and clears i + 1's;
+        // a last small launch writes position K - 1's tokens.
+        const int nh = ms_halves(B);
+        auto kbuf = [&](int i) { return keys + (size_t)(i % 3) * B; };
         for (int i = 0; i < K; ++i) {
             hipLaunchKernelGGL(mk_stream_kernel, dim3(kMsGrid), dim3(kMsThreads), kMsLds, s, A, Bm,
-                               map[i & 1], base + (size_t)i * V, out + (size_t)i * V, B, K, V, r,
-                               i, nh, parts);
-            if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
-            hipLaunchKernelGGL(mk_pick_kernel,
-                               dim3((unsigned)((B + kMkPickWaves - 1) / kMkPickWaves)),
-                               dim3(kMkPickThreads), 0, s, parts, slots, B, K, V, i, out_tokens,
-                               map[(i + 1) & 1]);
+                               map[0], i > 0 ? kbuf(i - 1) : nullptr, kbuf(i), kbuf(i + 1),
+                               base + (size_t)i * V, out + (size_t)i * V, B, K, V, r, i, nh,
+                               out_tokens);
             if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
         }
+        hipLaunchKernelGGL(mk_final_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, s,
+                           kbuf(K - 1), B, K, V, out_tokens);
+        if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
         return SV_OK;
     }
     for (int i = 0; i < K; ++i) {

@@ -386,7 +386,8 @@ size_t spec_verify_hidden_workspace_bytes(int B, int K, int V);
  * products, the sum formed in fp32 and rounded once to bf16 (to nearest,
  * ties to even) and stored; x_i = the first (lowest index) argmax of the
  * stored row; x_{-1} = prev_tokens. The stored rows are drafter logits a
- * verify step can read. Stream-ordered, no host sync; 1 + 2K launches.
+ * verify step can read. Stream-ordered, no host sync; K + 2 launches when r
+ * is a multiple of 16 up to 256 and V a multiple of 8, else 1 + 2K.
  *   base_logits  bf16 [B, K, V] row-major (device, 16-byte aligned): the
  *                backbone's logits.
  *   markov_a     bf16 [V, r] (device, 16-byte aligned): the previous token's
@@ -404,10 +405,12 @@ size_t spec_verify_hidden_workspace_bytes(int B, int K, int V);
  *   workspace    device scratch of at least
  *                spec_markov_draft_workspace_bytes(B, V) bytes, 256-byte
  *                aligned, caller-owned; calls sharing it must not overlap.
- *                It holds two token maps of B entries and one first-argmax
- *                entry (8 bytes) per request and vocabulary split of the
- *                product; the bias rows never reach memory, and the stored
- *                rows are not read back.
+ *                It holds two token maps of B entries, three arrays of one
+ *                8-byte first-argmax key per request (positions in turn),
+ *                and one 8-byte first-argmax entry per request and
+ *                vocabulary split for the product of other shapes; the bias
+ *                rows never reach memory, and of the stored rows only each
+ *                request's best 32 columns per position are read back.
  * Errors (nothing enqueued): SV_ERR_ARG, SV_ERR_NULL, SV_ERR_ALIGN;
  * SV_ERR_HIP if a launch fails.
  */

@@ -291,12 +291,12 @@ def test_markov_draft_workspace_size():
     assert sb.spec_markov_draft_workspace_bytes(4, 0) == 0
     assert sb.spec_markov_draft_workspace_bytes(4, sb.SV_MAX_VOCAB + 1) == 0
     n = sb.spec_markov_draft_workspace_bytes(512, 151936)
-    # Two token maps of B entries each and an 8-byte first argmax per request
-    # and vocabulary split: 128 column slots for each of the two groups of 256
-    # requests (one workgroup per CU), as many as the many-row product's
-    # splits. The bias rows never reach memory.
-    want = 2 * 4 * 512 + 128 * 512 * 8
-    assert want <= n <= want + 3 * 255
+    # Two token maps of B entries each, an 8-byte first argmax per request and
+    # vocabulary split of the product for other shapes (128 splits), and the
+    # streaming path's three arrays of one 8-byte argmax key per request. The
+    # bias rows never reach memory.
+    want = 2 * 4 * 512 + 128 * 512 * 8 + 3 * 8 * 512
+    assert want <= n <= want + 4 * 255
 
 
 def _noalloc(**kw):
