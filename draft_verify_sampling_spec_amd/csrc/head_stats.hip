@@ -711,7 +711,9 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
     extern __shared__ __align__(16) unsigned char mm_smem[];
     __shared__ HeadPart xw[kBM];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // The wave index in a scalar register, so that the loads' LDS
+    // destinations (M0) are formed by scalar instructions.
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // Wave (wm, wn): hidden rows wm * 128 .. + 128 of the row tile and
     // vocabulary columns wn * 128 .. + 128 of the vocabulary tile. The
     // product is formed transposed (head rows as the first operand), so in
