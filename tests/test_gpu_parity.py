@@ -48,8 +48,9 @@ def _run(inp, seed, sv=None, temperature=None):
     return out
 
 
-def _oracle(inp, seed, requests=None, temperature=None):
-    """Oracle decisions for the given requests (global indices keep their counters)."""
+def _oracle(inp, seed, requests=None, temperature=None, request_base=0):
+    """Oracle decisions for the given requests (global indices keep their
+    counters; request b's Philox counter is request_base + b)."""
     T = inp["temperature"] if temperature is None else temperature
     budgets = inp["budgets"].cpu().numpy()
     tokens = inp["tokens"].cpu().numpy()
@@ -63,7 +64,8 @@ def _oracle(inp, seed, requests=None, temperature=None):
         if T > 0:
             zd, _ = to_oracle(inp["draft"][b, :k])
             zd = ov.as_f64_rows(zd, fmt)
-        out.append(ov.verify_request(int(b), zt, zd, tokens[b, :k], float(T), seed))
+        out.append(ov.verify_request(int(request_base) + int(b), zt, zd, tokens[b, :k], float(T),
+                                     seed))
     return out
 
 
@@ -446,6 +448,26 @@ def test_request_base_slices_reproduce_the_whole_batch(name, T):
 
 
 WORKLOAD_SEEDS = {"tiny": 1, "qwen3": 2, "ragged": 3, "gemma": 4, "heavy": 5}
+
+
+@pytest.mark.parametrize("name,T", [("qwen3", 1.0), ("ragged", 0.8)])
+def test_request_base_at_the_counter_limit(name, T):
+    """The largest request base the ABI accepts, so the device generator runs
+    on counter words just below 2^32: every draw and acceptance follows the
+    oracle given the same global request indices."""
+    inp = make_inputs(name, device=DEV)
+    t, d, x, k = inp["target"], inp["draft"], inp["tokens"], inp["budgets"]
+    B, K1, V = t.shape
+    base = 2 ** 32 - 1 - B
+    seed = philox_seed(WORKLOAD_SEEDS[name], 91)
+    _log(f"request base {base} {name} T={T}")
+    sv = SpecVerify(DEV, max_batch=B, max_k=K1 - 1, vocab=V, dtype=t.dtype)
+    toks, nacc, p, q = sv.run(t, d, x, k, T, seed, request_base=base)
+    torch.cuda.synchronize()
+    gpu = (toks.cpu().numpy(), nacc.cpu().numpy(), p.cpu().numpy(), q.cpu().numpy(), sv.status())
+    sv.close()
+    decisions = _oracle(inp, seed, temperature=T, request_base=base)
+    _assert_parity(inp, seed, gpu, decisions, temperature=T, tag=f"base-{name}")
 
 
 # ------------------------------------------------------- low temperatures ---
