@@ -661,6 +661,41 @@ constexpr int kMmLds = 2 * 2 * kMmOpBytes;           // two stages, both operand
 constexpr unsigned kMmOob = 0x80000000u;             // a buffer offset past every range below
 enum MmMode { kMmGreedy = 0, kMmSampled = 1, kMmLogits = 2 };
 
+// Side workgroups. An XCD's CUs beyond its kB x kC super-tile (two at 6 x 5)
+// take the vocabulary's last side_cols tiles, for every row tile, column by
+// column; the super-tiles keep the first kC * spb tiles. spb balances the
+// two: a super-tile workgroup takes about nb * spb / 8 tiles (nb bands), a
+// side one side_cols * rtiles / (8 * side workgroups per XCD). spb stays at
+// least 8, so that every XCD has a super-step in every band, and side_cols
+// at most mm_side_max(V) (the workspace's bound). Both the product and the
+// merge of its partials compute it from the row count.
+struct MmSplit {
+    int spb, side_cols;
+};
+__host__ __device__ inline int mm_side_max(int V) { return (V + kBN - 1) / kBN / 8 + 2; }
+template <int kB, int kC>
+__host__ __device__ inline MmSplit mm_split(int R, int V) {
+    const int rtiles = (R + kBM - 1) / kBM, ntiles = (V + kBN - 1) / kBN;
+    const int nb = (rtiles + kB - 1) / kB;
+    const int s_all = (ntiles + kC - 1) / kC;
+    constexpr int kSide = 32 - kB * kC;
+    MmSplit best{s_all, 0};
+    if (kSide <= 0 || R < 1) return best;
+    long long best_cost = ((long long)nb * s_all + kXcds - 1) / kXcds;
+    for (int sp = s_all - 1; sp >= kXcds; --sp) {
+        const int side = ntiles - kC * sp;
+        if (side > mm_side_max(V)) break;
+        const long long tm = ((long long)nb * sp + kXcds - 1) / kXcds;
+        const long long ts = ((long long)side * rtiles + kXcds * kSide - 1) / (kXcds * kSide);
+        const long long cost = tm > ts ? tm : ts;
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = MmSplit{sp, side};
+        }
+    }
+    return best;
+}
+
 // Row and column counts for which a call takes this path with super-tiles
 // of kB row tiles by kC vocabulary tiles (the workspace is sized from these
 // alone): at least one full band, and every XCD with a super-step in every
@@ -722,25 +757,46 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
     const int wm = wave >> 1, wn = wave & 1;
     const int R = rows_now(r_max, d_rows);
     const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
-    if (slot >= kBandT * kColT || R == 0) return;
-    const int rt_in = slot % kBandT, vt = slot / kBandT;
+    constexpr int kSuper = kBandT * kColT, kSide = 32 - kSuper;
+    const MmSplit split = mm_split<kBandT, kColT>(R, V);
+    const bool side = slot >= kSuper;                // a side workgroup (see mm_split)
+    if (R == 0 || (side && split.side_cols == 0)) return;
+    const int rt_in = side ? 0 : slot % kBandT, vt = side ? 0 : slot / kBandT;
     const int rtiles = (R + kBM - 1) / kBM;
     const int nbands = (rtiles + kBandT - 1) / kBandT;
     const int ntiles = (V + kBN - 1) / kBN;
-    const int spb = (ntiles + kColT - 1) / kColT;   // super-steps per band
-    const int total = nbands * spb;
+    const int spb = split.spb;                       // super-steps per band
+    const int ncm = ntiles - split.side_cols;        // the super-tiles' vocabulary tiles
+    // A side workgroup's tiles: t_beg .. t_end - 1 of the side region's
+    // side_cols * rtiles tiles, numbered column-major (a column's row tiles
+    // in turn, so its head rows stay in the L2).
+    const int sw = xcd * kSide + (slot - kSuper);
+    const long long n_side = (long long)split.side_cols * rtiles;
+    const int t_beg = side ? (int)(sw * n_side / (kXcds * kSide)) : 0;
+    const int total = side ? (int)((sw + 1) * n_side / (kXcds * kSide)) : nbands * spb;
+    const int stride = side ? 1 : kXcds;
     const int nk = H / kBK;
 
-    // The workgroup's tiles, in order: super-steps stp = xcd, xcd + 8, ...
-    // Super-step stp covers row tile (stp / spb) * kBandT + rt_in and
-    // vocabulary tile (stp % spb) * kColT + vt; it is skipped when either
-    // lies past the end (every band that has this row tile has at least one
-    // vocabulary tile here, as the path needs kColT * kXcds vocabulary
-    // tiles).
-    auto row0_of = [&](int stp) { return (stp / spb * kBandT + rt_in) * kBM; };
-    auto v0_of = [&](int stp) { return ((stp % spb) * kColT + vt) * kBN; };
+    // The workgroup's tiles, in order. Super-tile workgroups: super-steps
+    // stp = xcd, xcd + 8, ...; super-step stp covers row tile
+    // (stp / spb) * kBandT + rt_in and vocabulary tile (stp % spb) * kColT +
+    // vt, skipped when either lies past the end (every band that has this
+    // row tile has at least one vocabulary tile here: spb >= 8, and with
+    // side columns every group of kColT is whole). Side workgroups: tile t
+    // covers row tile t % rtiles and vocabulary tile ncm + t / rtiles, and
+    // each is its own band, written to its column's partial slot.
+    auto row0_of = [&](int stp) {
+        return (side ? stp % rtiles : stp / spb * kBandT + rt_in) * kBM;
+    };
+    auto v0_of = [&](int stp) {
+        return (side ? ncm + stp / rtiles : (stp % spb) * kColT + vt) * kBN;
+    };
+    auto band_of = [&](int stp) { return side ? stp : stp / spb; };
+    auto pslot_of = [&](int stp) {
+        return side ? kXcds * kColT + stp / rtiles : xcd * kColT + vt;
+    };
     auto next_tile = [&](int stp) {
-        while (stp < total && (row0_of(stp) >= R || v0_of(stp) >= V)) stp += kXcds;
+        while (stp < total && (row0_of(stp) >= R || v0_of(stp) >= V)) stp += stride;
         return stp < total ? stp : total;
     };
 
@@ -768,12 +824,17 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
     unsigned hbu = 0;
     int l_band = -1;
     auto set_rows = [&](int r0) {
-        hbu = 0;
+        int vr[8];                                   // the row map's entries, loaded together
         #pragma unroll
         for (int j = 0; j < 8; ++j) {
             int r = r0 + 8 * (wave * 8 + j) + lrow;
             r = r < R ? r : R - 1;
-            const int v = hr.map ? hr.map[r] : r;
+            vr[j] = hr.map ? hr.map[r] : r;
+        }
+        hbu = 0;
+        #pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int v = vr[j];
             const bool in_b = v >= hr.a_rows;
             hoff[j] = v < 0 ? kMmOob
                             : (unsigned)(in_b ? v - hr.a_rows : v) * hrow_bytes +
@@ -791,7 +852,7 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
         const int v0 = v0_of(stp);
         // Head rows v0 .. v0 + 255; rows past V read as zeros.
         rsrc_w = mm_rsrc(w + (size_t)v0 * H, (unsigned)min(kBN, V - v0) * hrow_bytes);
-        const int band = stp / spb;
+        const int band = band_of(stp);
         if (band != l_band) {
             l_band = band;
             set_rows(row0_of(stp));
@@ -812,7 +873,7 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
         }
     };
     auto loader_next = [&]() {
-        if (l_stp < total && ++l_ks == nk) loader_at(next_tile(l_stp + kXcds));
+        if (l_stp < total && ++l_ks == nk) loader_at(next_tile(l_stp + stride));
     };
 
     // ---- the product: 16 blocks of 32 x 32 per wave, fragments of one
@@ -965,7 +1026,7 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
     // The band's partial of this (XCD, column slot) for each of its rows:
     // the lane pair holding a row (lane, lane ^ 32) merges, then the two
     // waves with the same rows through LDS.
-    auto flush = [&](int r0) {
+    auto flush = [&](int r0, int ps) {
         #pragma unroll
         for (int a = 0; a < 4; ++a) {
             float m2 = __shfl_xor(rm[a], 32, 64), x2 = __shfl_xor(rx[a], 32, 64);
@@ -1005,7 +1066,7 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
                     o2.arg = __float_as_int(rx[a]);
                     merge_arg(o2.m, o2.arg, o.m, o.arg);
                 }
-                if (r0 + rl < R) part[(size_t)(xcd * kColT + vt) * R + r0 + rl] = o2;
+                if (r0 + rl < R) part[(size_t)ps * R + r0 + rl] = o2;
             }
         }
         __syncthreads();
@@ -1020,13 +1081,13 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
     // out among the last group's products, half among the first group's
     // products of step g + 1. Tiles follow one another without a pause; a
     // tile's statistics are folded after its last product.
-    int c_stp = next_tile(xcd);
-    if (c_stp >= total) return;                      // (cannot happen: see above)
+    int c_stp = next_tile(side ? t_beg : xcd);
+    if (c_stp >= total) return;                      // (a side workgroup without tiles)
     loader_at(c_stp);
     #pragma unroll
     for (int i = 0; i < 16; ++i) load_one(0, i);     // step 0, whole
     loader_next();
-    int band = c_stp / spb;
+    int band = band_of(c_stp);
     if (!kLogits) start_band(row0_of(c_stp));
     zero_acc(v0_of(c_stp));
     __builtin_amdgcn_s_waitcnt(0);                   // step 0 and the tokens
@@ -1065,7 +1126,7 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
         // (its first group is read after the fold). The synchronisation
         // happens even when nothing follows: the loads among the last
         // group's products then refill the stage this step used.
-        const int n_stp = next_tile(c_stp + kXcds);
+        const int n_stp = next_tile(c_stp + stride);
         const bool has_next = n_stp < total;
         read_frags(f1, st, 1);
         __builtin_amdgcn_sched_barrier(0);
@@ -1088,9 +1149,9 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
         if (kLogits) store(v0_of(c_stp), row0_of(c_stp));
         else fold(v0_of(c_stp));
         if (!has_next) break;
-        const int nb = n_stp / spb;
+        const int nb = band_of(n_stp);
         if (!kLogits && nb != band) {
-            flush(row0_of(c_stp));
+            flush(row0_of(c_stp), pslot_of(c_stp));
             start_band(row0_of(n_stp));
         }
         band = nb;
@@ -1098,21 +1159,24 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
         read_frags(f0, st, 0);                       // the next tile's first group
         c_stp = n_stp;
     }
-    if (!kLogits) flush(row0_of(c_stp));
+    if (!kLogits) flush(row0_of(c_stp), pslot_of(c_stp));
     __builtin_amdgcn_s_waitcnt(0);                   // the last loads and stores
 }
 
 // Per row: merge the splits' partials (in split order) into the outputs.
 // Greedy partials carry the first argmax; sampled ones do not (INT_MAX), and
 // the sampled call reports none.
-// parts > 0: that many partials per row (the many-row product), else one
-// per vocabulary split of the product above.
+// parts > 0: that many partials per row; parts < 0: the many-row product's
+// (its super-tile slots and its side columns'); 0: one per vocabulary split
+// of the product above.
 __global__ void head_merge_kernel(const HeadPart* __restrict__ part, int r_max,
                                   const int* __restrict__ d_rows, int V, float c, int sampled,
                                   int parts, float* out_max, float* out_sum, float* out_z,
                                   int32_t* out_arg) {
     const int R = rows_now(r_max, d_rows);
-    const int splits = parts > 0 ? parts : splits_for(R, V);
+    const int splits = parts > 0   ? parts
+                       : parts < 0 ? kMmParts + mm_split<kBandTiles, kColTiles>(R, V).side_cols
+                                   : splits_for(R, V);
     const int r = blockIdx.x * blockDim.x + threadIdx.x;
     if (r >= R) return;
     float m = -INFINITY, s = 0.0f, z = NAN, bv = -INFINITY;
@@ -1163,8 +1227,10 @@ size_t stats_workspace_bytes(int r_max, int V) {
     long long n = (long long)kResidentSlots * kTM;
     if (r_max > n) n = r_max;
     if (cap * r_max < n) n = cap * r_max;
-    // The many-row product (whatever H is): kMmParts partials per row.
-    if (mm_shape(r_max, V) && n < (long long)kMmParts * r_max) n = (long long)kMmParts * r_max;
+    // The many-row product (whatever H is): kMmParts partials per row and
+    // one per side column.
+    const long long mm = (long long)(kMmParts + mm_side_max(V)) * r_max;
+    if (mm_shape(r_max, V) && n < mm) n = mm;
     return (size_t)n * sizeof(HeadPart);
 }
 
@@ -1190,7 +1256,7 @@ int head_stats_launch(const HeadRows& rows, const uint16_t* weight, int r_max,
         }
         if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
         hipLaunchKernelGGL(head_merge_kernel, dim3((unsigned)((r_max + 255) / 256)), dim3(256), 0,
-                           s, part, r_max, d_rows, V, c, sampled ? 1 : 0, kMmParts, out_max,
+                           s, part, r_max, d_rows, V, c, sampled ? 1 : 0, -1, out_max,
                            out_sum, out_z, out_arg);
         return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
     }
@@ -1248,7 +1314,8 @@ int head_add_bf16_launch(const HeadRows& rows, const uint16_t* weight, int R, in
 extern "C" size_t spec_head_workspace_bytes(int R, int V) {
     if (R < 1 || V < 1) return 0;
     size_t n = (size_t)splits_for(R, V) * (size_t)R;
-    if (mm_shape(R, V) && n < (size_t)kMmParts * (size_t)R) n = (size_t)kMmParts * (size_t)R;
+    const size_t mm = (size_t)(kMmParts + mm_side_max(V)) * (size_t)R;
+    if (mm_shape(R, V) && n < mm) n = mm;
     return n * sizeof(HeadPart);
 }
 
