@@ -665,14 +665,15 @@ enum MmMode { kMmGreedy = 0, kMmSampled = 1, kMmLogits = 2 };
 // take the vocabulary's last side_cols tiles, for every row tile, column by
 // column; the super-tiles keep the first kC * spb tiles. spb balances the
 // two: a super-tile workgroup takes about nb * spb / 8 tiles (nb bands), a
-// side one side_cols * rtiles / (8 * side workgroups per XCD). spb stays at
-// least 8, so that every XCD has a super-step in every band, and side_cols
-// at most mm_side_max(V) (the workspace's bound). Both the product and the
+// side one side_cols * rtiles / (8 * side workgroups per XCD) -- about a
+// sixteenth of the vocabulary when the bands are whole. spb stays at least
+// 8, so that every XCD has a super-step in every band, and side_cols at
+// most mm_side_max(V) (the workspace's bound). Both the product and the
 // merge of its partials compute it from the row count.
 struct MmSplit {
     int spb, side_cols;
 };
-__host__ __device__ inline int mm_side_max(int V) { return (V + kBN - 1) / kBN / 8 + 2; }
+__host__ __device__ inline int mm_side_max(int V) { return (V + kBN - 1) / kBN / 16 + 4; }
 template <int kB, int kC>
 __host__ __device__ inline MmSplit mm_split(int R, int V) {
     const int rtiles = (R + kBM - 1) / kBM, ntiles = (V + kBN - 1) / kBN;

@@ -246,8 +246,11 @@ def test_verify_hidden_workspace_size():
     assert sb.spec_verify_hidden_workspace_bytes(0, 4, 100) == 0
     assert sb.spec_verify_hidden_workspace_bytes(4, sb.SV_MAX_K + 1, 100) == 0
     n = sb.spec_verify_hidden_workspace_bytes(512, 8, 151936)
-    # Dominated by the fp32 logits of two draw rows per request.
-    assert 8 * 512 * 151936 <= n < 8 * 512 * 151936 + (8 << 20)
+    # Dominated by the fp32 logits of two draw rows per request; then the
+    # head statistics' 16-byte partials for up to 512 * 17 + 7 packed rows,
+    # 40 super-tile slots and up to 594 / 16 + 4 side columns per row.
+    partials = (512 * 17 + 7) * (40 + 594 // 16 + 4) * 16
+    assert 8 * 512 * 151936 <= n < 8 * 512 * 151936 + partials + (1 << 20)
 
 
 @pytest.mark.parametrize("kw,code", [
