@@ -1182,11 +1182,21 @@ __global__ void head_merge_kernel(const HeadPart* __restrict__ part, int r_max,
     if (r >= R) return;
     float m = -INFINITY, s = 0.0f, z = NAN, bv = -INFINITY;
     int ai = INT_MAX;
-    for (int sp = 0; sp < splits; ++sp) {
-        const HeadPart o = part[(size_t)sp * R + r];
-        if (sampled) merge_ms(m, s, o.m, o.s, c, true);
-        else merge_arg(bv, ai, o.m, o.arg);
-        if (z != z) z = o.zx;
+    // Eight partials' loads in flight at a time; merged in split order.
+    constexpr int kBatch = 8;
+    for (int sp0 = 0; sp0 < splits; sp0 += kBatch) {
+        HeadPart ob[kBatch];
+        #pragma unroll
+        for (int k = 0; k < kBatch; ++k)
+            if (sp0 + k < splits) ob[k] = part[(size_t)(sp0 + k) * R + r];
+        #pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            if (sp0 + k >= splits) break;
+            const HeadPart& o = ob[k];
+            if (sampled) merge_ms(m, s, o.m, o.s, c, true);
+            else merge_arg(bv, ai, o.m, o.arg);
+            if (z != z) z = o.zx;
+        }
     }
     out_max[r] = sampled ? m : bv;
     if (out_sum) out_sum[r] = sampled ? s : NAN;
