@@ -69,13 +69,15 @@ def test_small_shapes_match_oracle(R, H, V, T):
     _check_rows(z, scale, tok.cpu().numpy(), T, got, H)
 
 
-@pytest.mark.parametrize("R,H,V", [(1700, 128, 10243), (1541, 192, 10001)])
+@pytest.mark.parametrize("R,H,V", [(1700, 128, 10243), (1541, 192, 10001), (4000, 64, 24576),
+                                   (3329, 128, 49153)])
 @pytest.mark.parametrize("T", [0.0, 1.0])
 def test_many_row_product_every_row(R, H, V, T):
     """Shapes that take the many-row product (at least 1,536 rows, at least
     40 vocabulary tiles of 256, H a multiple of 64) with ragged row and
     vocabulary tails (a partial last row tile and a partial last vocabulary
-    tile, a partial last band): every row against the oracle."""
+    tile, a partial last band), and with the side workgroups' columns (1, 0,
+    6 and 8 of them, over 1 to 3 bands): every row against the oracle."""
     _log(f"[head] many-row product R={R} H={H} V={V} T={T}")
     h, w, tok = make_head_inputs(R, H, V, seed=R + V)
     tok[::7] = -1
