@@ -321,7 +321,9 @@ int spec_head_stats(const void* hidden, const void* weight, int R, int H, int V,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* spec_head_workspace_bytes -- scratch spec_head_stats needs for (R, V):
- * one partial per row and vocabulary split. 0 on bad arguments. Host only. */
+ * one 16-byte partial per row and vocabulary split (for 1,536 rows or more
+ * and V of at least 10,240: 40 per row plus at most ceil(V / 256) / 16 + 4).
+ * 0 on bad arguments. Host only. */
 size_t spec_head_workspace_bytes(int R, int V);
 
 /*
