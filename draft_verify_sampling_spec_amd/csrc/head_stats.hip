@@ -759,6 +759,7 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
     const int R = rows_now(r_max, d_rows);
     const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
     constexpr int kSuper = kBandT * kColT, kSide = 32 - kSuper;
+    constexpr int kSideN = kSide > 0 ? kSide : 1;     // (divisor; no side workgroups when kSide is 0)
     const MmSplit split = mm_split<kBandT, kColT>(R, V);
     const bool side = slot >= kSuper;                // a side workgroup (see mm_split)
     if (R == 0 || (side && split.side_cols == 0)) return;
@@ -773,8 +774,8 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
     // in turn, so its head rows stay in the L2).
     const int sw = xcd * kSide + (slot - kSuper);
     const long long n_side = (long long)split.side_cols * rtiles;
-    const int t_beg = side ? (int)(sw * n_side / (kXcds * kSide)) : 0;
-    const int total = side ? (int)((sw + 1) * n_side / (kXcds * kSide)) : nbands * spb;
+    const int t_beg = side ? (int)(sw * n_side / (kXcds * kSideN)) : 0;
+    const int total = side ? (int)((sw + 1) * n_side / (kXcds * kSideN)) : nbands * spb;
     const int stride = side ? 1 : kXcds;
     const int nk = H / kBK;
 
