@@ -920,6 +920,13 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
     // zeros, so they stay -inf and drop out of every statistic without a
     // mask in the fold (the logits mode does not store them).
     auto zero_acc = [&](int v0) {
+        if (v0 + kBN <= V) {                         // no column past V: plain zeros
+            #pragma unroll
+            for (int b2 = 0; b2 < 4; ++b2)
+                #pragma unroll
+                for (int a = 0; a < 4; ++a) acc[b2][a] = f32x16{};
+            return;
+        }
         const int lim = V - (v0 + wn * 128 + 4 * (lane >> 5));
         #pragma unroll
         for (int b2 = 0; b2 < 4; ++b2)
