@@ -366,8 +366,9 @@ def bench_hidden(B, K, H, V, steps, T=1.0, seed=5):
     """A whole verify step from hidden states through the shared head at the
     verify batch's shape (budgets 2 + Binomial(6, 1/3)): plan, the head
     product with the statistics epilogue over every budgeted row, decide,
-    the head product again over each request's draw rows (fp32 logits), and
-    the inverse-CDF draw. Per-call durations from HIP events. The matrix
+    the head product again over each request's paired draw rows (its
+    epilogue leaves per-block draw masses, no logits), and the inverse-CDF
+    draw. Per-call durations from HIP events. The matrix
     work is 2 H V flops per scored row plus per draw row; its rate over the
     whole call is a lower bound on the product kernels' own rate. The oracle
     is timed on one request and scaled to the batch."""

@@ -39,7 +39,11 @@
 
 namespace {
 
+using svhead::DrawDesc;
+using svhead::DrawMass;
 using svhead::HeadRows;
+using svhead::kNoDraw;
+using svhead::kResidual;
 
 constexpr int kHThreads = 256;             // 4 waves
 constexpr int kTM = 128;                   // rows of h per tile
@@ -659,7 +663,7 @@ constexpr int kMmGrid = kXcds * 32;                  // one workgroup per CU
 constexpr int kMmOpBytes = kBM * kBK * 2;            // one operand of one stage (32 KB)
 constexpr int kMmLds = 2 * 2 * kMmOpBytes;           // two stages, both operands
 constexpr unsigned kMmOob = 0x80000000u;             // a buffer offset past every range below
-enum MmMode { kMmGreedy = 0, kMmSampled = 1, kMmLogits = 2 };
+enum MmMode { kMmGreedy = 0, kMmSampled = 1, kMmLogits = 2, kMmMass = 3 };
 
 // Side workgroups. An XCD's CUs beyond its kB x kC super-tile (two at 6 x 5)
 // take the vocabulary's last side_cols tiles, for every row tile, column by
@@ -734,16 +738,19 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, unsigned of
 }
 
 // kMode: the row statistics (greedy or sampled, partials per (XCD, column
-// slot) into part) or the fp32 logits themselves (into out, row-major,
-// R x V). kBandT x kColT: the XCD's super-tile.
+// slot) into part), the fp32 logits themselves (into out, row-major,
+// R x V), or the draw masses of paired draw rows (into dm). kBandT x kColT:
+// the XCD's super-tile.
 template <int kMode, int kBandT, int kColT>
 __global__ __launch_bounds__(kMmThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
                     const int* __restrict__ d_rows, int H, int V,
                     const int32_t* __restrict__ tok, float c, HeadPart* __restrict__ part,
-                    float* __restrict__ out) {
+                    float* __restrict__ out, DrawMass dm) {
     constexpr bool kSampled = kMode == kMmSampled;
     constexpr bool kLogits = kMode == kMmLogits;
+    constexpr bool kMass = kMode == kMmMass;
+    constexpr bool kRowStats = !kLogits && !kMass;
     extern __shared__ __align__(16) unsigned char mm_smem[];
     __shared__ HeadPart xw[kBM];
 
@@ -1032,6 +1039,74 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
         }
     };
 
+    // Draw masses (kMass). Packed row r is the target row (bit 3 of r clear)
+    // or the drafter row of request 8 (r / 16) + r % 8, so in each 32 x 32
+    // block the lanes l and l ^ 8 hold a request's two rows over the same
+    // columns. Each lane's 4 rows' normalisers are set per row tile.
+    float dm_k[4];                                   // the row's exponent offset (mass_offset)
+    int dm_b[4];                                     // the row's request (-1: none)
+    auto start_mass_rows = [&](int r0) {
+        #pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int r = r0 + wm * 128 + 32 * a + (lane & 31);
+            const int b = 8 * (r >> 4) + (r & 7);
+            dm_b[a] = -1;
+            dm_k[a] = INFINITY;                      // a row without mass
+            if (b < dm.nreq) {
+                const DrawDesc d = dm.desc[b];
+                if (d.kind != kNoDraw) {
+                    dm_b[a] = b;
+                    if (((r >> 3) & 1) == 0) {
+                        dm_k[a] = svhead::mass_offset(d.mt, d.st, c);
+                    } else if (d.kind == kResidual) {
+                        dm_k[a] = svhead::mass_offset(d.md, d.sd, c);
+                    }
+                }
+            }
+        }
+    };
+    // The tile's draw masses: each lane's values 2^(z c - k) of its row
+    // (k = mass_offset(m, S, c)), the drafter row's taken from lane ^ 8 (a DPP rotation by 8 within
+    // a row of 16 lanes), summed per 4 consecutive columns in fp32 and per
+    // half block (16 columns: lanes l < 32 hold columns 0-3, 8-11, 16-19,
+    // 24-27 of a 32-column block, lanes l + 32 the others) in fp64. The
+    // target row's lanes store both halves; a block's mass is their sum.
+    auto mass_fold = [&](int v0) {
+        const int nb32 = (V + 31) >> 5;
+        const int cw = v0 + wn * 128;
+        const bool tgt = ((lane >> 3) & 1) == 0;
+        const int half = lane >> 5;
+        #pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            #pragma unroll
+            for (int b2 = 0; b2 < 4; ++b2) {
+                double sr = 0.0, sp = 0.0;
+                #pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float r4 = 0.0f, p4 = 0.0f;
+                    #pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const float pv =
+                            __builtin_amdgcn_exp2f(__builtin_fmaf(acc[b2][a][4 * g + t], c, -dm_k[a]));
+                        const float qv = __int_as_float(__builtin_amdgcn_mov_dpp(
+                            __float_as_int(pv), 0x128, 0xF, 0xF, false));   // row_ror:8
+                        const float rv = fmaxf(pv - qv, 0.0f);
+                        r4 = t ? r4 + rv : rv;
+                        p4 = t ? p4 + pv : pv;
+                    }
+                    sr += (double)r4;
+                    sp += (double)p4;
+                }
+                const int col = cw + 32 * b2;
+                if (tgt && dm_b[a] >= 0 && col < V) {
+                    const size_t at = ((size_t)dm_b[a] * (size_t)nb32 + (size_t)(col >> 5)) * 2 + half;
+                    dm.mres[at] = sr;
+                    dm.mp[at] = sp;
+                }
+            }
+        }
+    };
+
     // The band's partial of this (XCD, column slot) for each of its rows:
     // the lane pair holding a row (lane, lane ^ 32) merges, then the two
     // waves with the same rows through LDS.
@@ -1097,7 +1172,8 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
     for (int i = 0; i < 16; ++i) load_one(0, i);     // step 0, whole
     loader_next();
     int band = band_of(c_stp);
-    if (!kLogits) start_band(row0_of(c_stp));
+    if (kRowStats) start_band(row0_of(c_stp));
+    if (kMass) start_mass_rows(row0_of(c_stp));
     zero_acc(v0_of(c_stp));
     __builtin_amdgcn_s_waitcnt(0);                   // step 0 and the tokens
     ring_barrier();
@@ -1156,19 +1232,21 @@ void head_mm_kernel(HeadRows hr, const uint16_t* __restrict__ w, int r_max,
         __builtin_amdgcn_sched_barrier(0);
         st ^= 1;
         if (kLogits) store(v0_of(c_stp), row0_of(c_stp));
+        else if (kMass) mass_fold(v0_of(c_stp));
         else fold(v0_of(c_stp));
         if (!has_next) break;
         const int nb = band_of(n_stp);
-        if (!kLogits && nb != band) {
+        if (kRowStats && nb != band) {
             flush(row0_of(c_stp), pslot_of(c_stp));
             start_band(row0_of(n_stp));
         }
+        if (kMass && nb != band) start_mass_rows(row0_of(n_stp));
         band = nb;
         zero_acc(v0_of(n_stp));
         read_frags(f0, st, 0);                       // the next tile's first group
         c_stp = n_stp;
     }
-    if (!kLogits) flush(row0_of(c_stp), pslot_of(c_stp));
+    if (kRowStats) flush(row0_of(c_stp), pslot_of(c_stp));
     __builtin_amdgcn_s_waitcnt(0);                   // the last loads and stores
 }
 
@@ -1225,7 +1303,8 @@ static hipError_t mm_attrs() {
         const void* fns[] = {
             reinterpret_cast<const void*>(&head_mm_kernel<kMmSampled, kBandTiles, kColTiles>),
             reinterpret_cast<const void*>(&head_mm_kernel<kMmGreedy, kBandTiles, kColTiles>),
-            reinterpret_cast<const void*>(&head_mm_kernel<kMmLogits, kLogBand, kLogCols>)};
+            reinterpret_cast<const void*>(&head_mm_kernel<kMmLogits, kLogBand, kLogCols>),
+            reinterpret_cast<const void*>(&head_mm_kernel<kMmMass, kLogBand, kLogCols>)};
         for (const void* f : fns) {
             const hipError_t e =
                 hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kMmLds);
@@ -1267,11 +1346,11 @@ int head_stats_launch(const HeadRows& rows, const uint16_t* weight, int r_max,
         if (sampled) {
             hipLaunchKernelGGL((head_mm_kernel<kMmSampled, kBandTiles, kColTiles>), dim3(kMmGrid),
                                dim3(kMmThreads), kMmLds, s, rows, weight, r_max, d_rows, H, V,
-                               tokens, c, part, nullptr);
+                               tokens, c, part, nullptr, DrawMass{});
         } else {
             hipLaunchKernelGGL((head_mm_kernel<kMmGreedy, kBandTiles, kColTiles>), dim3(kMmGrid),
                                dim3(kMmThreads), kMmLds, s, rows, weight, r_max, d_rows, H, V,
-                               tokens, c, part, nullptr);
+                               tokens, c, part, nullptr, DrawMass{});
         }
         if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
         hipLaunchKernelGGL(head_merge_kernel, dim3((unsigned)((r_max + 255) / 256)), dim3(256), 0,
@@ -1307,12 +1386,26 @@ int head_logits_launch(const HeadRows& rows, const uint16_t* weight, int R, int 
         if (mm_attrs() != hipSuccess) return SV_ERR_HIP;
         hipLaunchKernelGGL((head_mm_kernel<kMmLogits, kLogBand, kLogCols>), dim3(kMmGrid),
                            dim3(kMmThreads), kMmLds, s, rows, weight, R, nullptr, H, V, nullptr,
-                           0.0f, nullptr, out);
+                           0.0f, nullptr, out, DrawMass{});
         return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
     }
     hipLaunchKernelGGL(head_stats_kernel<kEpiLogits>, dim3((unsigned)items_for(R, V)),
                        dim3(kHThreads), 0, s, rows, weight, R, nullptr, H, V, nullptr, 0.0f,
                        nullptr, out, RowAdd{});
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+bool mass_path(const HeadRows& rows, int R, int H, int V) {
+    return R >= 1 && mm_path<kLogBand, kLogCols>(rows, R, H, V);
+}
+
+int head_mass_launch(const HeadRows& rows, const uint16_t* weight, int R, int H, int V, float c,
+                     const DrawMass& dm, hipStream_t s) {
+    if (!mass_path(rows, R, H, V)) return SV_ERR_ARG;
+    if (mm_attrs() != hipSuccess) return SV_ERR_HIP;
+    hipLaunchKernelGGL((head_mm_kernel<kMmMass, kLogBand, kLogCols>), dim3(kMmGrid),
+                       dim3(kMmThreads), kMmLds, s, rows, weight, R, nullptr, H, V, nullptr, c,
+                       nullptr, nullptr, dm);
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

@@ -27,13 +27,21 @@
 //      Philox uniforms, the first rejection; greedy outputs are final here;
 //   4. sampled only: the head product once more for each request's draw rows
 //      (target and drafter row j_b for a residual, target row k_b for a
-//      bonus; every request's target row first, then from a multiple of 8
-//      every drafter row), writing their fp32 logits -- bit-identical to the
-//      values the statistics were taken over when both go through the
-//      many-row product (each logit accumulates in the same order);
-//   5. sampled only: the inverse-CDF draw (an 8-wave workgroup per request)
-//      over those rows in vocabulary order: 256-element block masses first,
-//      then one wave rescans the block where the running mass crosses u R.
+//      bonus). When the many-row product takes them (at least 512 requests),
+//      the rows are paired -- request b's target row at 16 (b / 8) + b % 8,
+//      its drafter row 8 rows further -- and the product's epilogue turns
+//      each pair's logits into draw masses per 32-column block (the residual
+//      max(0, p - q) and p alone), so no logit reaches memory; otherwise
+//      (every target row first, then from a multiple of 8 every drafter row)
+//      it writes the rows' fp32 logits. Either way the logits are
+//      bit-identical to the values the statistics were taken over when both
+//      go through the many-row product (each accumulates in the same order);
+//   5. sampled only: the inverse-CDF draw in vocabulary order, one workgroup
+//      per request: from the block masses, the block where the running mass
+//      crosses u R and that block's 32 logits recomputed by the same
+//      matrix-core products (hv_pick_kernel); or, from the stored logits,
+//      256-element block masses and a rescan of the crossing block
+//      (hv_draw_kernel).
 
 #include <hip/hip_runtime.h>
 
@@ -54,16 +62,11 @@ using svrng::word_to_uniform;
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
 
-enum DrawKind { kNoDraw = 0, kResidual = 1, kBonus = 2 };
-
-struct DrawDesc {                                  // one request's draw
-    float mt, st;                                  // target row: max, exp-sum
-    float md, sd;                                  // drafter row (residual)
-    float u;                                       // u_smp of the drawn position
-    int kind;                                      // DrawKind
-    int pos;                                       // output position j_b
-    int pad;
-};
+using svhead::DrawDesc;
+using svhead::DrawMass;
+using svhead::kBonus;
+using svhead::kNoDraw;
+using svhead::kResidual;
 
 // Workspace layout (byte offsets, each 256-aligned).
 struct Layout {
@@ -76,9 +79,16 @@ size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 // drafter rows.
 size_t packed_rows_max(int B, int K) { return (size_t)B * (2 * K + 1) + 7; }
 
-// Draw rows: request b's target row at b, its drafter row at up8(B) + b.
+// Draw rows: request b's target row at b, its drafter row at up8(B) + b
+// (the logits path); or, paired (the mass path), request b's target row at
+// 16 (b / 8) + b % 8 and its drafter row 8 rows further.
 __host__ __device__ inline int draw_split(int B) { return (B + 7) & ~7; }
 size_t draw_rows_for(int B) { return (size_t)draw_split(B) + (size_t)B; }
+size_t paired_rows_for(int B) { return 2 * (size_t)draw_split(B); }
+__host__ __device__ inline int paired_target_row(int b) { return 16 * (b >> 3) + (b & 7); }
+
+// Blocks of 32 vocabulary columns (the mass path's draw masses).
+__host__ __device__ inline int mass_blocks(int V) { return (V + 31) >> 5; }
 
 Layout layout_for(int B, int K, int V) {
     const size_t rmax = packed_rows_max(B, K);
@@ -99,8 +109,10 @@ Layout layout_for(int B, int K, int V) {
     L.sz = take(rmax * 4);
     L.sa = take(rmax * 4);
     L.part = take(svhead::stats_workspace_bytes((int)rmax, V));
-    L.drawmap = take(draw_rows_for(B) * 4);
+    L.drawmap = take(paired_rows_for(B) * 4);
     L.desc = take((size_t)B * sizeof(DrawDesc));
+    // The draw rows' fp32 logits, or (the mass path) two arrays of B x
+    // mass_blocks(V) x 2 fp64 half-block masses, which take less room.
     L.logits = take(draw_rows_for(B) * (size_t)V * 4);
     L.total = o;
     return L;
@@ -204,9 +216,20 @@ __global__ void hv_decide_kernel(const int32_t* __restrict__ budgets,
                                  const int32_t* __restrict__ sa, int32_t* __restrict__ out_tokens,
                                  int32_t* __restrict__ out_n, float* __restrict__ out_p,
                                  float* __restrict__ out_q, int32_t* __restrict__ drawmap,
-                                 DrawDesc* __restrict__ desc) {
+                                 DrawDesc* __restrict__ desc, int paired) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
-    if (b < draw_split(B) - B) drawmap[B + b] = -1;  // padding between the two parts
+    // The draw rows' map: request b's target row at tb, its drafter row at db.
+    const int tb = paired ? paired_target_row(b) : b;
+    const int db = paired ? tb + 8 : draw_split(B) + b;
+    if (b < draw_split(B) - B) {                       // padding rows
+        const int bp = B + b;
+        if (paired) {
+            drawmap[paired_target_row(bp)] = -1;
+            drawmap[paired_target_row(bp) + 8] = -1;
+        } else {
+            drawmap[bp] = -1;
+        }
+    }
     if (b >= B) return;
     unsigned ignore = 0u;
     const int k = clamp_budget(budgets[b], K, ignore);
@@ -229,8 +252,8 @@ __global__ void hv_decide_kernel(const int32_t* __restrict__ budgets,
         DrawDesc d{};
         d.kind = kNoDraw;
         desc[b] = d;
-        drawmap[b] = -1;
-        drawmap[draw_split(B) + b] = -1;
+        drawmap[tb] = -1;
+        drawmap[db] = -1;
         return;
     }
     for (int i = 0; i < k; ++i) {
@@ -261,15 +284,15 @@ __global__ void hv_decide_kernel(const int32_t* __restrict__ budgets,
     d.pos = j;
     d.mt = sm[o + j];
     d.st = ss[o + j];
-    drawmap[b] = b * (K + 1) + j;
+    drawmap[tb] = b * (K + 1) + j;
     if (j < k) {
         d.kind = kResidual;
         d.md = sm[od + j];
         d.sd = ss[od + j];
-        drawmap[draw_split(B) + b] = B * (K + 1) + b * K + j;
+        drawmap[db] = B * (K + 1) + b * K + j;
     } else {
         d.kind = kBonus;
-        drawmap[draw_split(B) + b] = -1;
+        drawmap[db] = -1;
     }
     desc[b] = d;
 }
@@ -475,6 +498,151 @@ void hv_draw_kernel(const float* __restrict__ logits, int K, int V, float c,
     if (lane == 0) out_tokens[(size_t)b * (K + 1) + d.pos] = y;
 }
 
+// The mass path's draw (one 4-wave workgroup per request), from the block
+// masses of the paired product: the 32-column block where the running mass
+// in vocabulary order first exceeds u times the total (the residual's, or
+// p's for a bonus draw or a residual without mass), then that block's
+// logits again -- the target row's and, for a residual, the drafter row's --
+// from the same matrix-core products in the same order as the product's, so
+// bit for bit the values its masses were taken over; then the first column
+// whose running mass exceeds the rest of the threshold (if rounding leaves
+// none, the last column with mass).
+constexpr int kPickThreads = 256;
+
+typedef float pk_f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 pk_bf16x8 __attribute__((ext_vector_type(8)));
+
+// Dynamic LDS of hv_pick_kernel: the block masses, then the two hidden rows.
+size_t pick_smem_bytes(int V, int H) { return (size_t)mass_blocks(V) * 8 + (size_t)4 * H; }
+constexpr size_t kPickSmemMax = 64 * 1024;
+
+__global__ __launch_bounds__(kPickThreads)
+void hv_pick_kernel(const uint16_t* __restrict__ th, const uint16_t* __restrict__ dh,
+                    const uint16_t* __restrict__ w, const int32_t* __restrict__ drawmap,
+                    int a_rows, int K, int H, int V, float c, const DrawDesc* __restrict__ desc,
+                    const double* __restrict__ mres, const double* __restrict__ mp,
+                    int32_t* __restrict__ out_tokens) {
+    extern __shared__ __align__(16) unsigned char pk_smem[];
+    __shared__ int star_s, resid_s;
+    __shared__ double thr_s;
+    __shared__ float col_m[32];
+    const int b = blockIdx.x;
+    const DrawDesc d = desc[b];
+    if (d.kind == kNoDraw) return;                   // the whole workgroup
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nb = mass_blocks(V);
+    double* blk = reinterpret_cast<double*>(pk_smem);
+    uint16_t* hs = reinterpret_cast<uint16_t*>(pk_smem + (size_t)nb * 8);   // [2][H]
+    const int tr = drawmap[paired_target_row(b)], dr = drawmap[paired_target_row(b) + 8];
+    // The two hidden rows into LDS (zeros for a row that is not drawn from).
+    for (int e = tid * 8; e < 2 * H; e += kPickThreads * 8) {
+        const int row = e >= H, k = e - row * H;
+        const uint16_t* src = nullptr;
+        if (row == 0 && tr >= 0) src = th + (size_t)tr * H;
+        if (row == 1 && d.kind == kResidual && dr >= 0) src = dh + (size_t)(dr - a_rows) * H;
+        *reinterpret_cast<uint4*>(hs + e) = src ? *reinterpret_cast<const uint4*>(src + k)
+                                                : make_uint4(0u, 0u, 0u, 0u);
+    }
+    for (int pass = 0; pass < 2; ++pass) {
+        const bool resid = pass == 0 && d.kind == kResidual;
+        // Each block's mass: the sum of its two halves.
+        const double2* m = reinterpret_cast<const double2*>(resid ? mres : mp) + (size_t)b * nb;
+        for (int x0 = tid; x0 < nb; x0 += 8 * kPickThreads) {
+            double2 v[8];
+            #pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                v[u] = x0 + u * kPickThreads < nb ? m[x0 + u * kPickThreads] : make_double2(0.0, 0.0);
+            }
+            #pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (x0 + u * kPickThreads < nb) blk[x0 + u * kPickThreads] = v[u].x + v[u].y;
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            double total = 0.0;
+            for (int x = lane; x < nb; x += 64) total += blk[x];
+            total = hv_wave_sum(total);
+            int star = -1;
+            double base = 0.0;
+            const double t = (double)d.u * total;
+            if (total > 0.0) hv_block_crossing(blk, nb, t, star, base);
+            if (lane == 0) {
+                star_s = star;
+                thr_s = t - base;
+                resid_s = resid ? 1 : 0;
+            }
+        }
+        __syncthreads();
+        if (star_s >= 0 || !resid) break;               // no residual mass: from p
+        __syncthreads();                                // blk is read again below
+    }
+    if (wave != 0) return;
+    const int x = star_s;
+    int y = 0;
+    if (x >= 0) {
+        const bool resid = resid_s != 0;
+        // Vocabulary row v0 + lane % 32 as the first operand, hidden rows as
+        // the second (slot 0 the target row, slot 8 the drafter row, zeros
+        // elsewhere), this lane's 8 of each 16 of k: the product's layout.
+        const int v0 = 32 * x;
+        const int vr = v0 + (lane & 31);
+        const int kh = 8 * (lane >> 5);
+        const int slot = lane & 31;
+        const uint16_t* wrow = w + (size_t)(vr < V ? vr : 0) * H;
+        const uint16_t* hrow = slot == 0 ? hs : (slot == 8 ? hs + H : nullptr);
+        const pk_bf16x8 zero8 = {};
+        pk_f32x16 acc = {};
+        constexpr int kDepth = 16;                      // groups of 16 of k in flight
+        const int ng = H / 16;
+        for (int g0 = 0; g0 < ng; g0 += kDepth) {
+            pk_bf16x8 wa[kDepth];
+            #pragma unroll
+            for (int u = 0; u < kDepth; ++u) {
+                const int g = g0 + u;
+                wa[u] = (g < ng && vr < V)
+                            ? *reinterpret_cast<const pk_bf16x8*>(wrow + 16 * g + kh) : zero8;
+            }
+            #pragma unroll
+            for (int u = 0; u < kDepth; ++u) {
+                const int g = g0 + u;
+                if (g < ng) {
+                    const pk_bf16x8 hb = hrow ? *reinterpret_cast<const pk_bf16x8*>(hrow + 16 * g + kh)
+                                              : zero8;
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[u], hb, acc, 0, 0, 0);
+                }
+            }
+        }
+        // Lane l holds hidden slot l % 32 and 16 columns of the block: column
+        // 8 (i / 4) + i % 4 + 4 (l / 32) for element i. Element masses as the
+        // product's epilogue takes them.
+        const float k = slot == 0 ? svhead::mass_offset(d.mt, d.st, c)
+                                  : (resid && slot == 8 ? svhead::mass_offset(d.md, d.sd, c) : INFINITY);
+        #pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], c, -k));
+            const float q = __shfl_xor(e, 8, 64);
+            const int col = 8 * (i >> 2) + (i & 3) + 4 * (lane >> 5);
+            if (slot == 0) col_m[col] = v0 + col < V ? (resid ? fmaxf(e - q, 0.0f) : e) : 0.0f;
+        }
+        if (lane == 0) {
+            const double tt = thr_s;
+            double run = 0.0;
+            int cand = -1, last = -1;
+            for (int k2 = 0; k2 < 32; ++k2) {
+                const float r = col_m[k2];
+                if (r > 0.0f) {
+                    last = v0 + k2;
+                    run += (double)r;
+                    if (cand < 0 && run > tt) cand = v0 + k2;
+                }
+            }
+            y = cand >= 0 ? cand : (last >= 0 ? last : 0);
+        }
+    }
+    if (lane == 0) out_tokens[(size_t)b * (K + 1) + d.pos] = y;
+}
+
 bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 }  // namespace
@@ -536,17 +704,39 @@ extern "C" int spec_verify_hidden(const void* target_hidden, const void* draft_h
                                        ws + L.part, s);
     if (rc != SV_OK) return rc;
 
+    // The draw's path: block masses from the paired product when its
+    // many-row form takes the paired rows and the pick kernel's LDS holds the
+    // masses and two hidden rows; otherwise the draw rows' logits.
+    const HeadRows pair_probe{th, dh, nullptr, B * (K + 1), dh ? B * K : 0, true};
+    const bool paired = !greedy && svhead::mass_path(pair_probe, (int)paired_rows_for(B), H, V) &&
+                        pick_smem_bytes(V, H) <= kPickSmemMax;
     const int dthreads = 256;
     hipLaunchKernelGGL(hv_decide_kernel, dim3((unsigned)((B + dthreads - 1) / dthreads)),
                        dim3(dthreads), 0, s, budgets, draft_tokens, B, K, V, greedy ? 1 : 0, c64,
                        (uint32_t)(seed & 0xFFFFFFFFull), (uint32_t)(seed >> 32), i32(L.off), i32(L.offd),
                        f32(L.sm), f32(L.ss), f32(L.sz), i32(L.sa), out_tokens, out_num_accepted,
                        out_p_draft, out_q_draft, i32(L.drawmap),
-                       reinterpret_cast<DrawDesc*>(ws + L.desc));
+                       reinterpret_cast<DrawDesc*>(ws + L.desc), paired ? 1 : 0);
     if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
     if (greedy) return SV_OK;
 
     const HeadRows draw_rows{th, dh, i32(L.drawmap), B * (K + 1), dh ? B * K : 0, true};
+    if (paired) {
+        // The draw rows' masses from the product's epilogue (no logits
+        // written), then one workgroup per request picks the token.
+        double* mres = reinterpret_cast<double*>(ws + L.logits);
+        double* mpv = mres + 2 * (size_t)B * mass_blocks(V);
+        rc = svhead::head_mass_launch(draw_rows, w, (int)paired_rows_for(B), H, V, (float)c64,
+                                      DrawMass{reinterpret_cast<const DrawDesc*>(ws + L.desc), mres,
+                                               mpv, B},
+                                      s);
+        if (rc != SV_OK) return rc;
+        hipLaunchKernelGGL(hv_pick_kernel, dim3((unsigned)B), dim3(kPickThreads),
+                           pick_smem_bytes(V, H), s, th, dh, w, i32(L.drawmap), B * (K + 1), K,
+                           H, V, (float)c64, reinterpret_cast<const DrawDesc*>(ws + L.desc), mres,
+                           mpv, out_tokens);
+        return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+    }
     rc = svhead::head_logits_launch(draw_rows, w, (int)draw_rows_for(B), H, V, f32(L.logits), s);
     if (rc != SV_OK) return rc;
     // 16-byte loads of the fp32 rows when every row starts 16-byte aligned.
