@@ -338,7 +338,11 @@ size_t spec_head_workspace_bytes(int R, int V);
  * exact bf16 products; p and q, the accept test, the Philox counters and the
  * inverse-CDF draw are those of spec_verify_run. Stream-ordered, no host
  * sync; five launches (plan, head statistics, decide, and in sampled mode
- * the head's logits for each request's draw rows and the draw).
+ * the head product over each request's draw rows and the draw). With at
+ * least 512 requests (when the head's many-row product takes the draw rows)
+ * that product leaves per-block draw masses instead of logits, so no logit
+ * reaches memory; with fewer it writes the draw rows' fp32 logits to the
+ * workspace.
  *   target_hidden  bf16 [B, K+1, H] row-major (device, 16-byte aligned).
  *   draft_hidden   bf16 [B, K, H] (device, 16-byte aligned); may be NULL
  *                  when temperature == 0 or K == 0.
