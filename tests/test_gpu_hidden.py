@@ -192,6 +192,19 @@ def test_many_row_products_every_request(T):
     _check(inp, T, (77 << 32) | 5, f"many-row B={B} K={K} H={H} V={V} T={T}")
 
 
+def test_paired_draw_rows_with_a_partial_group_of_eight():
+    """The draw masses' paired rows when B is not a multiple of 8 (B = 517:
+    requests 512..516 share a group of eight with three padding requests,
+    whose rows are rows of zeros), with budgets from 0 to K: every request
+    against the oracle."""
+    B, K, H, V = 517, 2, 64, 16421
+    _log(f"[hidden] paired rows B={B} K={K} H={H} V={V}")
+    rng = np.random.default_rng(78)
+    budgets = rng.integers(0, K + 1, size=B)
+    inp = make_hidden_inputs(B, K, H, V, seed=78, device=DEV, budgets=budgets)
+    _check(inp, 1.0, (78 << 32) | 5, f"paired B={B} K={K} H={H} V={V}")
+
+
 def test_q_equal_p_accepts_everything():
     inp = make_hidden_inputs(64, 5, 128, 3000, seed=3, device=DEV, variant="q_eq_p")
     toks, nacc, p, q, status = _gpu(inp, 1.0, 77)
