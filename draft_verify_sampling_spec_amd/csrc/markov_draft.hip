@@ -12,21 +12,26 @@
 // [V, r]); the row is stored as bf16 and the drafted token x_i is its first
 // argmax; x_{-1} is the last token already in each sequence.
 //
-// Design, per drafted position i (two stream-ordered launches; positions run
-// in order because x_i feeds position i+1):
-//   1. the matrix cores form the bias A[x_{i-1}[b]] Bm^T in fp32 -- the
-//      output head's product with the previous tokens as its row map and the
-//      rank r as its depth -- and its epilogue stages each output tile in
-//      LDS: the backbone values come in with 16-byte loads, each bias is
-//      added in fp32 and rounded once to bf16 (to nearest, ties to even), and
-//      the drafter rows go out with 16-byte stores, so the bias never reaches
-//      memory. The same epilogue follows the values it stores with a first
-//      argmax per row and vocabulary split;
-//   2. one wave per request merges its splits' argmaxes (ties to the lower
-//      column): the first argmax of the stored row, which is x_i and the
-//      next position's row map (two map buffers alternate). The stored rows
-//      are not read back.
-// A seed launch checks the given last tokens and writes the first row map.
+// Design, per drafted position i (positions run in order, because x_i feeds
+// position i + 1):
+//   * The streaming path (rank r a multiple of 16 up to 256, V a multiple of
+//     8: the heavy shape). One launch of mk_stream_kernel per position: every
+//     CU streams 32-column vocabulary tiles for 256 requests while the
+//     matrix cores form the bias A[x_{i-1}[b]] Bm^T in fp32 (rank r as the
+//     depth); each bias is added to its backbone value, rounded once to bf16
+//     and stored, so the bias never reaches memory. Each request's first
+//     argmax over its stored row merges across the column slots through a
+//     64-bit atomic maximum on an order-preserving key, and the next
+//     position's launch decodes those keys into its rows of A. A seed launch
+//     comes first and a last launch writes the final position's tokens:
+//     K + 2 launches per call.
+//   * Otherwise, two launches per position: the output head's product with
+//     the previous tokens as its row map and an add-and-store epilogue (the
+//     backbone values in and the drafter rows out with 16-byte accesses
+//     through LDS), which also keeps a first argmax per row and vocabulary
+//     split; then one wave per request merges its splits' entries (ties to
+//     the lower column). The stored rows are not read back. 1 + 2K launches.
+// The seed launch checks the given last tokens and writes the first row map.
 
 #include <hip/hip_runtime.h>
 
@@ -147,15 +152,18 @@ __global__ void mk_final_kernel(const unsigned long long* __restrict__ keys, int
 //     (x_{i-1}[b]'s row) as MFMA fragments in registers for the whole
 //     launch (the transposed product: Bm's columns as the first operand, so
 //     a lane holds one request's row and 16 columns of the 32 x 32 block);
-//   * Bm's tile (32 rows of r) and the backbone's tile (256 rows of 32
-//     columns) come in by buffer-to-LDS loads into rings of 4 and 5 slots,
-//     three tiles ahead of use; one wait and one barrier per tile;
+//   * Bm's tile (32 rows of r) and the backbone's tiles (256 rows of 32
+//     columns, taken in pairs so that each row moves as a 128-byte piece)
+//     come in by buffer-to-LDS loads into a ring of 4 Bm slots (three tiles
+//     ahead of use) and a ring of 3 pair slots (two pairs ahead); one wait
+//     and one barrier per tile;
 //   * tile t's bias is added to its backbone values, rounded once to bf16
 //     and stored while tile t + 1's product runs, and the running maximum
 //     of the stored values is kept per request, with the first tile that
 //     reached it; the column within that tile is read back at the end.
 // The workgroups that share a column slot (one per group of 256 requests)
-// sit on one XCD and walk the same tiles, so Bm's tiles come from HBM once.
+// sit on one XCD and walk the same tiles, so the second one can find Bm's
+// tiles in that XCD's L2 (about half of its loads do).
 constexpr int kMsThreads = 512;                    // 8 waves, 32 requests each
 constexpr int kMsCols = 32;                        // vocabulary columns per tile
 constexpr int kMsMaxG = 16;                        // k-groups of 16: r <= 256
