@@ -8,8 +8,9 @@
 // The ABI and its conventions are documented in include/spec_verify.h.
 //
 // Design: a streaming pass reads every logit row the method needs exactly
-// once and takes every decision; in sampled mode a draw pass follows on the
-// stream and makes each request's one draw.
+// once (and takes the greedy decisions); in sampled mode a draw pass follows
+// on the stream, decides the drafted positions and makes each request's one
+// draw.
 //  * Work unit = vocabulary chunk c of position i of request b: the chunk of
 //    target row i and, for a drafted position, the same chunk of drafter row
 //    i. Every chunk has the same size (960 data lanes x 4 sixteen-byte loads
@@ -29,24 +30,24 @@
 //    few rounds ahead, merges the waves' statistics and publishes the chunk's
 //    record; the two kinds of waves exchange tagged LDS messages, with no
 //    workgroup barrier in the loop.
-//  * Every record word carries the call's epoch. After publishing a record
-//    that a decision needs (greedy: every unit; sampled: the units of
-//    drafted positions), the control wave adds one to its team's arrival
-//    counter; the workgroup whose addition completes the team reads the C
-//    records and decides: greedy, the row's first argmax (the team
-//    completing last for a request writes its outputs); sampled, p(x), q(x),
-//    the accept test and the decision word.
+//  * Every record word carries the call's epoch. Greedy: after publishing a
+//    record the control wave adds one to its team's arrival counter; the
+//    workgroup whose addition completes the team reads the C records and
+//    decides the row's first argmax (the team completing last for a request
+//    writes its outputs). Sampled: the chunk of a drafted position that
+//    holds the drafted token adds that token's two logits to its record.
 //  * Draw pass (draw_kernel, sampled): one 8-wave workgroup per request, two
-//    per CU, finds the first rejection from the decision words, streams that
-//    position's target and drafter rows once for the residual masses of
-//    512-element blocks, and scans the block holding the threshold; the bonus
-//    position picks its chunk from the records' p masses and streams that
-//    chunk's blocks the same way. It writes the request's outputs. Nothing in
-//    it waits on another workgroup.
+//    per CU. Its waves decide the request's drafted positions side by side
+//    (p(x) and q(x) from each team's records, the accept test), then it
+//    streams the first rejected position's target and drafter rows once for
+//    the residual masses of 512-element blocks and scans the block holding
+//    the threshold; the bonus position picks its chunk from the records' p
+//    masses and streams that chunk's blocks the same way. It writes the
+//    request's outputs. Nothing in it waits on another workgroup.
 //  * No wave of either pass waits on another workgroup, so neither pass
-//    depends on which of its workgroups are resident at a time: a team is
-//    decided by whichever workgroup completes it, and the last workgroup to
-//    finish resets the schedule counter for the next call.
+//    depends on which of its workgroups are resident at a time: a greedy
+//    team is decided by whichever workgroup completes it, and the last
+//    workgroup to finish resets the schedule counter for the next call.
 //  * Synchronisation uses device-scope relaxed atomics (plus s_waitcnt where
 //    a counter orders earlier stores), never release/acquire fences: those
 //    write back and invalidate the whole L2.
@@ -88,21 +89,24 @@ constexpr unsigned kLdsSpinLimit = 1u << 26;   // bounded LDS mailbox wait (~3 s
 
 // Team record words.
 constexpr int TW_CNT = 0;       // arrivals of the team's units (reset by the unit that completes it)
-constexpr int TW_DEC = 2;       // 64-bit decision: (epoch << 32) | accepted (words 2-3)
+constexpr int TW_DEC = 2;       // greedy 64-bit decision: (epoch << 32) | accepted (words 2-3)
 
 // Scheduling words (Params::sched, 64 bytes apart): the next unit to hand
 // out, and the workgroups that finished the streaming loop.
 constexpr int SC_NEXT = 0, SC_DONE = 16;
 
-// Unit record: 4 64-bit words.
+// Unit record: 6 64-bit words.
 //   sampled: word f = (value bits << 32) | epoch for the fp32 values
 //            R_MT the scaled maximum s_t = max(z_t) c (c = log2(e) / T,
 //            rounded once), R_MD likewise for z_d, R_ST the sum of
 //            2^(z_t c - s_t), R_SD likewise
+//            and, in the one chunk of a drafted position that holds its
+//            drafted token x, R_ZT = (z_t(x) bits << 32) | epoch, R_ZD
+//            likewise for z_d(x)
 //   greedy:  word R_MT = (max bits << 32) | epoch, word R_MD = (lowest index
 //            of the max << 32) | epoch
-constexpr int kRecWords = 4;
-constexpr int R_MT = 0, R_MD = 1, R_ST = 2, R_SD = 3;
+constexpr int kRecWords = 6;
+constexpr int R_MT = 0, R_MD = 1, R_ST = 2, R_SD = 3, R_ZT = 4, R_ZD = 5;
 constexpr int kStatWords = 4;   // words R_MT..R_SD make a record complete
 
 constexpr double kLog2e = 1.4426950408889634073599246810019;
@@ -734,6 +738,20 @@ __device__ __forceinline__ void control_unit(const Params& P, Shared& sh, const 
     const int C = P.C;
     const int slot = r % kMbox;
     const unsigned ep = P.epoch;
+    // Sampled, a drafted position: the drafted token's logits when this
+    // chunk holds it (the loads go out before the wait below).
+    bool has_x = false;
+    float zt = 0.0f, zd = 0.0f;
+    if (!kGreedy && cur.has_d) {
+        const int x = P.tokens[(size_t)cur.b * P.K + cur.i];
+        has_x = x >= cur.e0 && x < cur.e0 + cur.n;
+        if (has_x) {
+            const E* target = static_cast<const E*>(P.target);
+            const E* draft = static_cast<const E*>(P.draft);
+            zt = Elem<E>::one(target + ((size_t)cur.b * (P.K + 1) + cur.i) * (size_t)P.V + x);
+            zd = Elem<E>::one(draft + ((size_t)cur.b * P.K + cur.i) * (size_t)P.V + x);
+        }
+    }
     if (lane < kDataWaves) lds_wait(P, sh, &sh.st_tag[slot][lane], r + 1);
     unsigned long long* rec = P.rec + ((size_t)cur.tr * C + cur.c) * kRecWords;
     if (kGreedy) {
@@ -772,61 +790,11 @@ __device__ __forceinline__ void control_unit(const Params& P, Shared& sh, const 
             st64(rec + R_MD, tagged(Md, ep));
             st64(rec + R_ST, tagged((float)St, ep));
             st64(rec + R_SD, tagged((float)Sd, ep));
+            if (has_x) {
+                st64(rec + R_ZT, tagged(zt, ep));
+                st64(rec + R_ZD, tagged(zd, ep));
+            }
         }
-    }
-}
-
-// A chunk-0 unit whose team decision this workgroup owes, with what the
-// decision needs besides the records (loaded when its poll is issued).
-struct Owed {
-    Unit u;
-    int x;              // drafted token (sampled)
-    float zt, zd;       // the drafted token's logits (sampled)
-};
-
-template <typename E, bool kGreedy>
-__device__ __forceinline__ void owed_issue(const Params& P, Owed& o, TeamPoll& pl) {
-    if (!kGreedy) {
-        const int K = P.K;
-        const E* target = static_cast<const E*>(P.target);
-        const E* draft = static_cast<const E*>(P.draft);
-        o.zt = o.zd = 0.0f;
-        if (o.x >= 0 && o.x < P.V) {
-            o.zt = Elem<E>::one(target + ((size_t)o.u.b * (K + 1) + o.u.i) * (size_t)P.V + o.x);
-            o.zd = Elem<E>::one(draft + ((size_t)o.u.b * K + o.u.i) * (size_t)P.V + o.x);
-        }
-    }
-    poll_issue<kGreedy>(P, o.u.tr, pl);
-}
-
-// Control wave: decide an owed team from its complete records. Greedy:
-// argmax, decision, completion. Sampled (a drafted position): p(x), q(x), the
-// accept decision and the decision word (the draw pass reads them).
-template <bool kGreedy>
-__device__ __forceinline__ void owed_decide(const Params& P, const Owed& o, const TeamPoll& pl) {
-    const Unit& u = o.u;
-    if (kGreedy) {
-        decide_greedy(P, pl, u.b, u.i, u.k, u.tr);
-        return;
-    }
-    const int lane = threadIdx.x & 63;
-    const int K = P.K;
-    const TeamStats ts = team_stats(P, pl);
-    const bool valid = o.x >= 0 && o.x < P.V;
-    double px = 0.0, qx = 0.0;
-    if (valid) {
-        // z c exactly (a product of two fp32 values fits fp64), minus the
-        // scaled maximum the row's sum was taken under.
-        px = exp2((double)o.zt * (double)P.c32 - (double)ts.mt) / ts.st;
-        qx = exp2((double)o.zd * (double)P.c32 - (double)ts.md) / ts.sd;
-    }
-    const uint4 rw = philox4x32_10(P.bbase + (uint32_t)u.b, (uint32_t)u.i, 0u, 0u, P.key0, P.key1);
-    const bool accept = word_to_uniform(rw.x) * qx < px;
-    if (lane == 0) {
-        if (!valid) atomicOr(P.status, SV_FLAG_BAD_TOKEN);
-        if (P.out_p) P.out_p[(size_t)u.b * K + u.i] = (float)px;
-        if (P.out_q) P.out_q[(size_t)u.b * K + u.i] = (float)qx;
-        st64(dec_word(P, u.tr), ((unsigned long long)P.epoch << 32) | (accept ? 1u : 0u));
     }
 }
 
@@ -872,27 +840,26 @@ __device__ __forceinline__ unsigned* team_count(const Params& P, int tr) {
     return P.team + (size_t)tr * kTeamWords + TW_CNT;
 }
 
-// A unit whose team decision may fall to this workgroup: its arrival was
-// counted (old = the counter's value before) and is decided once the
-// returned value shows it completed the team.
+// Greedy: a unit whose team decision may fall to this workgroup. Its
+// arrival was counted (old = the counter's value before); the team is
+// decided here once old shows that this arrival completed it.
 struct Pending {
-    Owed o;
+    Unit u;
     unsigned old;
     bool valid;
 };
 
-// Control wave: decide team o (its C records are complete: this workgroup's
-// arrival completed the team). Greedy: argmax, decision, request completion.
-// Sampled: p(x), q(x), the accept decision and the decision word.
-template <typename E, bool kGreedy>
-__device__ void decide_team(const Params& P, Owed& o) {
+// Control wave, greedy: decide team u (its C records are complete: this
+// workgroup's arrival completed the team): argmax, decision, request
+// completion; then reset the team's counter.
+__device__ void decide_team(const Params& P, const Unit& u) {
     TeamPoll pl;
-    owed_issue<E, kGreedy>(P, o, pl);
-    if (!poll_complete<kGreedy>(P, pl) && (threadIdx.x & 63) == 0) {
+    poll_issue<true>(P, u.tr, pl);
+    if (!poll_complete<true>(P, pl) && (threadIdx.x & 63) == 0) {
         atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);       // cannot happen: records precede arrivals
     }
-    owed_decide<kGreedy>(P, o, pl);
-    if ((threadIdx.x & 63) == 0) st32(team_count(P, o.u.tr), 0u);
+    decide_greedy(P, pl, u.b, u.i, u.k, u.tr);
+    if ((threadIdx.x & 63) == 0) st32(team_count(P, u.tr), 0u);
 }
 
 // The control wave's loop. Units are handed out dynamically: the first
@@ -904,12 +871,15 @@ __device__ void decide_team(const Params& P, Owed& o) {
 //  P. plan round r + kPlanLead from the fetched value, and fetch the next;
 //  1. the data waves' results of round r: the unit's statistics are merged
 //     and published;
-//  2. the arrival counted last round: if it completed its team, decide it;
-//  3. count this unit's arrival in its team (after its record is visible);
-//     the returned count is read next round.
-// No step waits on another workgroup: a team is decided by whichever
-// workgroup completes it, so the loop never depends on which workgroups are
-// resident. Nothing the data waves do waits on a decision.
+//  2. greedy: the arrival counted last round: if it completed its team,
+//     decide it;
+//  3. greedy: count this unit's arrival in its team (after its record is
+//     visible); the returned count is read next round.
+// Sampled, the records are all the pass leaves: the draw pass decides the
+// drafted positions. No step waits on another workgroup: a greedy team is
+// decided by whichever workgroup completes it, so the loop never depends on
+// which workgroups are resident. Nothing the data waves do waits on a
+// decision.
 template <typename E, bool kGreedy, bool kVec>
 __device__ __forceinline__ void control_loop(const Params& P, Shared& sh, const int* off) {
     const int U = off[P.B];
@@ -931,7 +901,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Shared& sh, const 
     auto settle = [&]() __attribute__((always_inline)) {
         if (pend.valid &&
             (unsigned)__builtin_amdgcn_readfirstlane((int)pend.old) == (unsigned)(P.C - 1)) {
-            decide_team<E, kGreedy>(P, pend.o);
+            decide_team(P, pend.u);
         }
         pend.valid = false;
     };
@@ -956,9 +926,8 @@ __device__ __forceinline__ void control_loop(const Params& P, Shared& sh, const 
         // 2.
         settle();
         // 3.
-        if (kGreedy || cur.has_d) {
-            pend.o.u = cur;
-            pend.o.x = kGreedy ? 0 : P.tokens[(size_t)cur.b * P.K + cur.i];
+        if (kGreedy) {
+            pend.u = cur;
             drain();                                   // the record is visible first
             pend.old = 0;
             if (lane == 0) pend.old = add32(team_count(P, cur.tr), 1u);
@@ -1195,10 +1164,12 @@ __device__ void p_chunk(const Params& P, const TeamPoll& pl, const TeamStats& ts
 }
 
 // Sampled mode, second pass: one workgroup per request, launched after the
-// streaming pass on the same stream, so every decision word and record is
-// final. Wave 0 finds the request's deciding position j (the first rejected
-// drafted position, k if all k were accepted), merges team j's records into
-// its normalisers and takes the sampling uniform u. The draw is an inverse
+// streaming pass on the same stream, so every record is final. Wave w
+// decides drafted positions w, w + 8, ...: it merges the position's target
+// and drafter records into their normalisers, reads the drafted token's two
+// logits from the record of the chunk holding it and takes the accept test.
+// The deciding position j is the first rejected one (k if all k were
+// accepted); wave 0 takes its normalisers and the sampling uniform u. The draw is an inverse
 // CDF in vocabulary order over blocks of 64 groups (512 bf16 or 256 fp32
 // elements, one 16-byte load per lane): the data waves stream the blocks of
 // a range, wave d taking every (kDrawDataWaves)-th block with kDrawSlots
@@ -1206,8 +1177,8 @@ __device__ void p_chunk(const Params& P, const TeamPoll& pl, const TeamStats& ts
 // block where the running mass first exceeds the threshold, and one data
 // wave scans that block's elements again (cache-resident).
 //  * First rejection (j < k): the residual max(0, p_j - q_j) over the whole
-//    row pair, threshold u R. The first blocks' loads go out while wave 0
-//    merges the records.
+//    row pair, threshold u R. The first blocks' loads go out as soon as the
+//    decisions name j.
 //  * Bonus position (j == k), or a residual without mass (rounding only):
 //    p_j. Its chunk masses follow from the records; the blocks of the chunk
 //    holding u times the total are streamed.
@@ -1219,9 +1190,9 @@ constexpr int kDrawDataWaves = kDrawWaves - 1;
 constexpr int kDrawSlots = 5;                  // blocks in flight per data wave
 constexpr int kDrawNone = 0, kDrawResidual = 1, kDrawP = 2;
 
-// Draw pass state, written by wave 0 between barriers.
+// Draw pass state, written between barriers: the decisions by the waves
+// that take them, the rest by wave 0.
 struct DrawShared {
-    int j, k;
     int mode;          // kDrawNone, kDrawResidual or kDrawP
     int x0, x1;        // block range streamed
     int star;          // block holding the threshold, from x0 (-1: none)
@@ -1231,7 +1202,13 @@ struct DrawShared {
     double u;          // sampling uniform of position j
     double thr;        // threshold, as mass from block x0's start (then from block star's)
     float mt, md, ist, isd;
+    // The decisions: drafted position t's accept bit and its rows' normalisers.
+    int acc[SV_MAX_K];
+    float tmt[SV_MAX_K], tmd[SV_MAX_K];
+    double tst[SV_MAX_K], tsd[SV_MAX_K];
 };
+
+constexpr int kDecPer = (SV_MAX_K + kDrawWaves - 1) / kDrawWaves;   // positions per wave
 
 template <typename E, bool kVec>
 __global__ __launch_bounds__(kDrawThreads) __attribute__((amdgpu_waves_per_eu(4)))
@@ -1252,32 +1229,95 @@ void draw_kernel(Params P) {
     const int K = P.K, V = P.V;
     const int NB = (V + BE - 1) / BE;                    // blocks per row
     const unsigned ep = P.epoch;
-    TeamPoll pl;                                         // wave 0: team j's records
-    if (wave == 0) {
-        // One round of loads: lane t < K the decision of position t, lane 63
-        // the budget.
-        unsigned long long d = 0ull;
-        int kb = 0;
-        if (lane < K) d = ld64(dec_word(P, b * (K + 1) + lane));
-        if (lane == 63) kb = P.budgets[b];
-        int k = __shfl(kb, 63, 64);
-        k = k < 0 ? 0 : (k > K ? K : k);
-        const bool known = lane >= k || (unsigned)(d >> 32) == ep;
-        if (__ballot(!known) != 0 && lane == 0) atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);
-        const unsigned long long rej = __ballot(lane < k && (!known || (d & 1ull) == 0));
-        const int j = rej ? __ffsll((long long)rej) - 1 : k;
-        poll_issue<false>(P, b * (K + 1) + j, pl);
-        if (lane == 0) {
-            dsh.j = j;
-            dsh.k = k;
-            dsh.mode = j < k ? kDrawResidual : kDrawP;
-            dsh.done = 0;
-            dsh.last = 0;
-            dsh.y = 0;
+    // The decisions. Wave w takes drafted positions w, w + 8, ... below the
+    // budget: one round of loads brings the budget, each position's drafted
+    // token and the records of its target and drafter rows (their maxima,
+    // sums and the token's logits, which the chunk holding the token
+    // recorded); then p(x), q(x) and the accept test, as the pages' rule has
+    // them, with the Philox uniform of (b, t).
+    const int C = P.C;
+    int k = P.budgets[b];
+    TeamPoll dpl[kDecPer];
+    unsigned long long dzt[kDecPer], dzd[kDecPer];
+    int dx[kDecPer];
+    #pragma unroll
+    for (int u = 0; u < kDecPer; ++u) {
+        const int t = wave + u * kDrawWaves;
+        dzt[u] = dzd[u] = 0ull;
+        dx[u] = -1;
+        if (t < K) {
+            poll_issue<false>(P, b * (K + 1) + t, dpl[u]);
+            unsigned long long* rec = team_rec(P, b * (K + 1) + t);
+            if (lane < C) {
+                dzt[u] = ld64(rec + lane * kRecWords + R_ZT);
+                dzd[u] = ld64(rec + lane * kRecWords + R_ZD);
+            }
+            dx[u] = P.tokens[(size_t)b * K + t];
         }
     }
+    k = k < 0 ? 0 : (k > K ? K : k);
+    #pragma unroll
+    for (int u = 0; u < kDecPer; ++u) {
+        const int t = wave + u * kDrawWaves;
+        if (t < k) {
+            const int tr = b * (K + 1) + t;
+            if (!poll_complete<false>(P, dpl[u]) && lane == 0) atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);
+            const TeamStats ts = team_stats(P, dpl[u]);
+            const int x = dx[u];
+            const bool valid = x >= 0 && x < V;
+            double px = 0.0, qx = 0.0;
+            if (valid) {
+                const int cx = x / P.CE;
+                unsigned long long wt, wd;
+                if (cx < 64) {
+                    wt = (unsigned long long)__shfl((long long)dzt[u], cx, 64);
+                    wd = (unsigned long long)__shfl((long long)dzd[u], cx, 64);
+                } else {
+                    unsigned long long* rec = team_rec(P, tr);
+                    wt = ld64(rec + cx * kRecWords + R_ZT);
+                    wd = ld64(rec + cx * kRecWords + R_ZD);
+                }
+                if ((!tag_ok(wt, ep) || !tag_ok(wd, ep)) && lane == 0) {
+                    atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);
+                }
+                // z c exactly (a product of two fp32 values fits fp64), minus
+                // the scaled maximum the row's sum was taken under.
+                px = exp2((double)tag_val(wt) * (double)P.c32 - (double)ts.mt) / ts.st;
+                qx = exp2((double)tag_val(wd) * (double)P.c32 - (double)ts.md) / ts.sd;
+            }
+            const uint4 rw = philox4x32_10(P.bbase + (uint32_t)b, (uint32_t)t, 0u, 0u, P.key0, P.key1);
+            const bool accept = word_to_uniform(rw.x) * qx < px;
+            if (lane == 0) {
+                if (!valid) atomicOr(P.status, SV_FLAG_BAD_TOKEN);
+                if (sl == 0) {
+                    if (P.out_p) P.out_p[(size_t)b * K + t] = (float)px;
+                    if (P.out_q) P.out_q[(size_t)b * K + t] = (float)qx;
+                }
+                dsh.acc[t] = accept ? 1 : 0;
+                dsh.tmt[t] = ts.mt;
+                dsh.tmd[t] = ts.md;
+                dsh.tst[t] = ts.st;
+                dsh.tsd[t] = ts.sd;
+            }
+        }
+    }
+    if (tid == 0) {
+        dsh.done = 0;
+        dsh.last = 0;
+        dsh.y = 0;
+    }
     __syncthreads();
-    const int j = dsh.j, k = dsh.k;
+    // The first rejected drafted position (k if none): the residual's, or
+    // the bonus position.
+    int j = k;
+    for (int t = 0; t < k; ++t) {
+        if (dsh.acc[t] == 0) {
+            j = t;
+            break;
+        }
+    }
+    TeamPoll pl;                                         // wave 0, bonus: team k's records
+    if (wave == 0 && j == k) poll_issue<false>(P, b * (K + 1) + j, pl);
     const E* rt = static_cast<const E*>(P.target) + ((size_t)b * (K + 1) + j) * (size_t)V;
     const E* rd = j < k ? static_cast<const E*>(P.draft) + ((size_t)b * K + j) * (size_t)V : nullptr;
     const bool vt = aligned16(rt), vd = rd != nullptr && aligned16(rd);
@@ -1306,18 +1346,28 @@ void draw_kernel(Params P) {
         a1 = x0 + (int)(((long long)(sl + 1) * n) / S);
     };
     bool pre = false;
-    if (dsh.mode == kDrawResidual && wave > 0) {
+    if (j < k && wave > 0) {
         int a0, a1;
         slice(0, NB, a0, a1);
         preload(a0, a1, true);
         pre = true;
     }
     if (wave == 0) {
-        if (!poll_complete<false>(P, pl) && lane == 0) atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);
-        const TeamStats ts = team_stats(P, pl);
+        // The drawn row's normalisers: the residual's from the decisions,
+        // the bonus row's from its records.
+        TeamStats ts;
+        if (j < k) {
+            ts.mt = dsh.tmt[j];
+            ts.md = dsh.tmd[j];
+            ts.st = dsh.tst[j];
+            ts.sd = dsh.tsd[j];
+        } else {
+            if (!poll_complete<false>(P, pl) && lane == 0) atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);
+            ts = team_stats(P, pl);
+        }
         const uint4 rw = philox4x32_10(P.bbase + (uint32_t)b, (uint32_t)j, 0u, 0u, P.key0, P.key1);
         const double u = word_to_uniform(rw.y);
-        int x0 = 0, x1 = NB, mode = dsh.mode;
+        int x0 = 0, x1 = NB, mode = j < k ? kDrawResidual : kDrawP;
         double thr = 0.0;
         if (mode == kDrawP) {
             int chunk = -1;
