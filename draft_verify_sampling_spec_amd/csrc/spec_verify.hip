@@ -46,8 +46,8 @@
 //    request's outputs. Nothing in it waits on another workgroup.
 //  * No wave of either pass waits on another workgroup, so neither pass
 //    depends on which of its workgroups are resident at a time: a greedy
-//    team is decided by whichever workgroup completes it, and the last
-//    workgroup to finish resets the schedule counter for the next call.
+//    team is decided by whichever workgroup completes it, and each launch
+//    clears the schedule counter of the launch after it.
 //  * Synchronisation uses device-scope relaxed atomics (plus s_waitcnt where
 //    a counter orders earlier stores), never release/acquire fences: those
 //    write back and invalidate the whole L2.
@@ -91,9 +91,13 @@ constexpr unsigned kLdsSpinLimit = 1u << 26;   // bounded LDS mailbox wait (~3 s
 constexpr int TW_CNT = 0;       // arrivals of the team's units (reset by the unit that completes it)
 constexpr int TW_DEC = 2;       // greedy 64-bit decision: (epoch << 32) | accepted (words 2-3)
 
-// Scheduling words (Params::sched, 64 bytes apart): the next unit to hand
-// out, and the workgroups that finished the streaming loop.
-constexpr int SC_NEXT = 0, SC_DONE = 16;
+// Scheduling words (Params::sched, 64 bytes apart): two counters of the next
+// unit to hand out. A launch uses the one its epoch's parity names, and
+// clears the other, which the launch before it used (launches on one
+// workspace are stream-ordered and their epochs alternate in parity), for
+// the launch after it. So no workgroup has to find out that it finished
+// last in order to reset the schedule.
+constexpr int SC_NEXT0 = 0, SC_NEXT1 = 16;
 
 // Unit record: 6 64-bit words.
 //   sampled: word f = (value bits << 32) | epoch for the fp32 values
@@ -124,7 +128,7 @@ struct Params {
     unsigned* team;                // [B*(K+1)][kTeamWords]
     unsigned* result;              // [B*(K+1)]: greedy: argmax of the team's row
     unsigned* req_count;           // [B][kReqStride]: greedy: teams completed
-    unsigned* sched;               // scheduling words SC_NEXT, SC_DONE
+    unsigned* sched;               // scheduling words SC_NEXT0, SC_NEXT1
     unsigned* status;              // 1 word
     double* dmass;                 // draw pass split over workgroups: block masses [requests][C * kBlocks]
     unsigned* dcnt;                // draw pass split: slices finished per request, kReqStride apart
@@ -138,6 +142,11 @@ struct Params {
     uint32_t key0, key1;
     unsigned epoch;                // call number (never 0): tags record and decision words
 };
+
+// The schedule counter of this launch.
+__device__ __forceinline__ unsigned* sched_next(const Params& P) {
+    return P.sched + ((P.epoch & 1u) ? SC_NEXT1 : SC_NEXT0);
+}
 
 // ------------------------------------------------------------- atomics --
 
@@ -895,7 +904,11 @@ __device__ __forceinline__ void control_loop(const Params& P, Shared& sh, const 
     // uniform where it is used (the wait for the atomic falls there).
     const int lane = threadIdx.x & 63;
     unsigned fetched = 0;
-    if (end_round == INT_MAX && lane == 0) fetched = add32(P.sched + SC_NEXT, 1u);
+    if (lane == 0) {
+        // Clear the counter the previous launch used, for the next one.
+        if (blockIdx.x == 0) st32(P.sched + ((P.epoch & 1u) ? SC_NEXT0 : SC_NEXT1), 0u);
+        if (end_round == INT_MAX) fetched = add32(sched_next(P), 1u);
+    }
     Pending pend;
     pend.valid = false;
     auto settle = [&]() __attribute__((always_inline)) {
@@ -915,7 +928,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Shared& sh, const 
             if (u >= U) {
                 end_round = planned;
             } else if (lane == 0) {
-                fetched = add32(P.sched + SC_NEXT, 1u);
+                fetched = add32(sched_next(P), 1u);
             }
             ++planned;
         }
@@ -935,16 +948,6 @@ __device__ __forceinline__ void control_loop(const Params& P, Shared& sh, const 
         }
     }
     settle();
-    // The last workgroup to finish resets the schedule for the next call
-    // (every fetch of every workgroup precedes its count here).
-    drain();
-    if (lane == 0) {
-        const unsigned done = add32(P.sched + SC_DONE, 1u);
-        if (done == (unsigned)(G - 1)) {
-            st32(P.sched + SC_NEXT, 0u);
-            st32(P.sched + SC_DONE, 0u);
-        }
-    }
 }
 
 // The data waves' loop: each round reads its plan, reduces the unit in
@@ -1581,10 +1584,11 @@ size_t draw_smem_bytes(int C) { return (size_t)C * kBlocks * sizeof(double); }
 // max_batch requests with up to max_k drafted positions and C chunks per row.
 // The draw pass splits a request over several workgroups only for batches of
 // at most split_reqs requests. The counters must read zero when a call
-// starts: the team arrival counters (word TW_CNT of each team record), the
-// words in [req, req_end) and [dcnt, dcnt_end), and the scheduling words at
-// status + 64; every kernel that raises one leaves it at zero when it
-// completes. The status word at `status` accumulates device-side flags.
+// starts: the team arrival counters (word TW_CNT of each team record) and
+// the words in [req, req_end) and [dcnt, dcnt_end), which every kernel that
+// raises one leaves at zero when it completes, and the scheduling word of
+// the call's epoch parity at status + 64, which the launch before it clears.
+// The status word at `status` accumulates device-side flags.
 struct WsLayout {
     size_t rec, team, result, req, req_end, dmass, dcnt, dcnt_end, status, total;
     size_t teams;
@@ -1709,7 +1713,8 @@ void timed_end(spec_verify_ctx* ctx, int idx, hipStream_t stream) {
 // occupancy); the schedule needs at least as many workgroups as a team has
 // members. Sampled mode then runs the draw pass, one workgroup per request.
 template <typename E, bool G, bool Vv>
-int launch(DeviceInfo& di, spec_verify_ctx* tctx, int split_reqs, Params& p, hipStream_t stream) {
+int launch(DeviceInfo& di, spec_verify_ctx* tctx, int split_reqs, Params& p, hipStream_t stream,
+           unsigned& calls) {
     const int slot = (std::is_same<E, uint16_t>::value ? 4 : 0) + (G ? 2 : 0) + (Vv ? 1 : 0);
     const size_t smem = dyn_smem_bytes(p.B);
     const int occ = occupancy_of<E, G, Vv>(di, slot, smem);
@@ -1719,6 +1724,7 @@ int launch(DeviceInfo& di, spec_verify_ctx* tctx, int split_reqs, Params& p, hip
     hipLaunchKernelGGL((verify_kernel<E, G, Vv>), dim3((unsigned)grid), dim3(kThreads), smem, stream,
                        p);
     if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+    calls = p.epoch;                                // the epoch is spent once the pass is enqueued
     timed_end(tctx, t, stream);
     if (!G) {
         // Two draw workgroups fit a CU. A batch of fewer requests than that
@@ -1806,24 +1812,25 @@ int run_batches(DeviceInfo& di, spec_verify_ctx* tctx, int vocab, int dtype, uns
         q.out_nacc = a.out_nacc + b0;
         q.out_p = a.out_p ? a.out_p + (size_t)b0 * K : nullptr;
         q.out_q = a.out_q ? a.out_q + (size_t)b0 * K : nullptr;
-        calls = calls % 0xFFFFFFFFu + 1u;      // 1 .. 2^32 - 1, never 0
-        q.epoch = calls;
+        // 1 .. 2^32 - 2, never 0; an even cycle, so consecutive launches
+        // alternate in parity, across the wrap too.
+        q.epoch = calls % 0xFFFFFFFEu + 1u;
         const int sr = L.split_reqs;
         if (dtype == SV_DTYPE_BF16) {
             if (vec) {
-                r = greedy ? launch<uint16_t, true, true>(di, tctx, sr, q, s)
-                           : launch<uint16_t, false, true>(di, tctx, sr, q, s);
+                r = greedy ? launch<uint16_t, true, true>(di, tctx, sr, q, s, calls)
+                           : launch<uint16_t, false, true>(di, tctx, sr, q, s, calls);
             } else {
-                r = greedy ? launch<uint16_t, true, false>(di, tctx, sr, q, s)
-                           : launch<uint16_t, false, false>(di, tctx, sr, q, s);
+                r = greedy ? launch<uint16_t, true, false>(di, tctx, sr, q, s, calls)
+                           : launch<uint16_t, false, false>(di, tctx, sr, q, s, calls);
             }
         } else {
             if (vec) {
-                r = greedy ? launch<float, true, true>(di, tctx, sr, q, s)
-                           : launch<float, false, true>(di, tctx, sr, q, s);
+                r = greedy ? launch<float, true, true>(di, tctx, sr, q, s, calls)
+                           : launch<float, false, true>(di, tctx, sr, q, s, calls);
             } else {
-                r = greedy ? launch<float, true, false>(di, tctx, sr, q, s)
-                           : launch<float, false, false>(di, tctx, sr, q, s);
+                r = greedy ? launch<float, true, false>(di, tctx, sr, q, s, calls)
+                           : launch<float, false, false>(di, tctx, sr, q, s, calls);
             }
         }
     }
@@ -1863,8 +1870,8 @@ __global__ void clear_words_kernel(unsigned* team, int nteam, unsigned* a, int n
     for (int i = t; i < na; i += stride) a[i] = 0u;
     for (int i = t; i < nb; i += stride) b[i] = 0u;
     if (t == 0) {
-        sched[SC_NEXT] = 0u;
-        sched[SC_DONE] = 0u;
+        sched[SC_NEXT0] = 0u;
+        sched[SC_NEXT1] = 0u;
         if (status) *status = 0u;
     }
 }
