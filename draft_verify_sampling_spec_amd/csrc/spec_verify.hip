@@ -30,12 +30,13 @@
 //    few rounds ahead, merges the waves' statistics and publishes the chunk's
 //    record; the two kinds of waves exchange tagged LDS messages, with no
 //    workgroup barrier in the loop.
-//  * Every record word carries the call's epoch. Greedy: after publishing a
-//    record the control wave adds one to its team's arrival counter; the
-//    workgroup whose addition completes the team reads the C records and
-//    decides the row's first argmax (the team completing last for a request
-//    writes its outputs). Sampled: the chunk of a drafted position that
-//    holds the drafted token adds that token's two logits to its record.
+//  * Greedy: the control wave posts the chunk's (max, first index) as a
+//    64-bit key to its team's atomic maximum, then counts the unit on its
+//    request's counter; the workgroup that counts a request's last unit
+//    reads the request's team keys (each a row's first argmax), decides and
+//    writes the outputs. Sampled: every record word carries the call's
+//    epoch, and the chunk of a drafted position that holds the drafted
+//    token adds that token's two logits to its record.
 //  * Draw pass (draw_kernel, sampled): one 8-wave workgroup per request, two
 //    per CU. Its waves decide the request's drafted positions side by side
 //    (p(x) and q(x) from each team's records, the accept test), then it
@@ -87,9 +88,9 @@ constexpr int kTeamWords = 32;                 // words per team record (128 byt
 constexpr int kReqStride = 16;                 // words between request counters (64 bytes)
 constexpr unsigned kLdsSpinLimit = 1u << 26;   // bounded LDS mailbox wait (~3 s)
 
-// Team record words.
-constexpr int TW_CNT = 0;       // arrivals of the team's units (reset by the unit that completes it)
-constexpr int TW_DEC = 2;       // greedy 64-bit decision: (epoch << 32) | accepted (words 2-3)
+// Team record words (greedy): a 64-bit argmax key, the atomic maximum of the
+// team's chunk keys (arg_key), zero when no chunk has posted one.
+constexpr int TW_KEY = 0;
 
 // Scheduling words (Params::sched, 64 bytes apart): two counters of the next
 // unit to hand out. A launch uses the one its epoch's parity names, and
@@ -125,9 +126,8 @@ struct Params {
     float* out_p;                  // [B, K] or null
     float* out_q;                  // [B, K] or null
     unsigned long long* rec;       // [B*(K+1)*C][kRecWords]
-    unsigned* team;                // [B*(K+1)][kTeamWords]
-    unsigned* result;              // [B*(K+1)]: greedy: argmax of the team's row
-    unsigned* req_count;           // [B][kReqStride]: greedy: teams completed
+    unsigned* team;                // [B*(K+1)][kTeamWords]: greedy argmax keys
+    unsigned* req_count;           // [B][kReqStride]: greedy: units counted
     unsigned* sched;               // scheduling words SC_NEXT0, SC_NEXT1
     unsigned* status;              // 1 word
     double* dmass;                 // draw pass split over workgroups: block masses [requests][C * kBlocks]
@@ -153,9 +153,6 @@ __device__ __forceinline__ unsigned* sched_next(const Params& P) {
 __device__ __forceinline__ void st32(unsigned* p, unsigned v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ unsigned ld32(unsigned* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ void st64(unsigned long long* p, unsigned long long v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -164,6 +161,9 @@ __device__ __forceinline__ unsigned long long ld64(unsigned long long* p) {
 }
 __device__ __forceinline__ unsigned add32(unsigned* p, unsigned v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void max64(unsigned long long* p, unsigned long long v) {
+    (void)__hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Wait until every memory operation this wave issued has completed, so that
 // device-scope stores above are visible before the counter update below.
@@ -497,8 +497,19 @@ __device__ void chunk_crossing(int C, double thr, F mass, int& chunk, double& ba
 
 // ------------------------------------------------------ request outputs --
 
-__device__ __forceinline__ unsigned long long* dec_word(const Params& P, int tr) {
-    return reinterpret_cast<unsigned long long*>(P.team + (size_t)tr * kTeamWords + TW_DEC);
+// Greedy: the argmax key of (value v, index i). Larger keys have larger
+// values, or equal values and lower indices, the order better_arg gives
+// (-0 counts as +0; the merges never hand on a NaN); 0 is no key.
+__device__ __forceinline__ unsigned long long arg_key(float v, int i) {
+    const unsigned bits = __float_as_uint(v + 0.0f);
+    const unsigned ord = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+    return ((unsigned long long)ord << 32) | (unsigned long long)(0xFFFFFFFFu - (unsigned)i);
+}
+__device__ __forceinline__ int key_index(unsigned long long key) {
+    return key == 0ull ? 0 : (int)(0xFFFFFFFFu - (unsigned)key);   // no key: an all-NaN row, index 0
+}
+__device__ __forceinline__ unsigned long long* team_key(const Params& P, int tr) {
+    return reinterpret_cast<unsigned long long*>(P.team + (size_t)tr * kTeamWords + TW_KEY);
 }
 
 // One lane: request b (budget k) ends at position j (the first rejection,
@@ -521,33 +532,31 @@ __device__ void request_outputs(const Params& P, int b, int k, int j, int y) {
     }
 }
 
-// Control lane, greedy: team tr = (b, i) of a request with budget k is
-// decided (its decision word and argmax are stored). The team completing
-// last for request b writes the request's outputs.
-__device__ void team_complete(const Params& P, int b, int k) {
-    drain();
-    const unsigned old = add32(&P.req_count[b * kReqStride], 1u);
-    if (old != (unsigned)k) return;
+// Control wave, greedy: every unit of request b (budget k) has posted its
+// chunk key and been counted. Read the k + 1 team keys (lane t: position t),
+// take the decisions, write the outputs, and clear the keys and the counter
+// for the next call.
+__device__ void request_complete(const Params& P, int b, int k) {
+    const int lane = threadIdx.x & 63;
     const int tr0 = b * (P.K + 1);
-    int j = k;
-    for (int t = 0; t < k; ++t) {
-        if ((ld64(dec_word(P, tr0 + t)) & 1ull) == 0) {
-            j = t;
-            break;
-        }
+    unsigned long long key = 0ull;
+    int x = -1;
+    if (lane <= k) key = ld64(team_key(P, tr0 + lane));
+    if (lane < k) x = P.tokens[(size_t)b * P.K + lane];
+    const int best = key_index(key);
+    const bool valid = x >= 0 && x < P.V;
+    if (__ballot(lane < k && !valid) != 0ull && lane == 0) atomicOr(P.status, SV_FLAG_BAD_TOKEN);
+    const unsigned long long rej = __ballot(lane < k && !(valid && x == best));
+    const int j = rej != 0ull ? __builtin_ctzll(rej) : k;
+    const int y = __shfl(best, j, 64);
+    if (lane <= k) st64(team_key(P, tr0 + lane), 0ull);
+    if (lane == 0) {
+        request_outputs<true>(P, b, k, j, y);
+        st32(&P.req_count[b * kReqStride], 0u);
     }
-    request_outputs<true>(P, b, k, j, (int)ld32(&P.result[tr0 + j]));
-    // Every team of the request has been counted: reset the counter for the
-    // next call (tagged words carry the call epoch and need no reset).
-    st32(&P.req_count[b * kReqStride], 0u);
 }
 
 // ----------------------------------------------------------- team records --
-
-// Record words a team's decision needs per chunk: sampled R_MT..R_SD,
-// greedy R_MT (max) and R_MD (index).
-template <bool kGreedy>
-__device__ __forceinline__ constexpr int rec_words() { return kGreedy ? 2 : kStatWords; }
 
 // A team's C records as one control-wave load: lane l holds chunk l in
 // registers; chunks 64 and up (vocabularies of more than 64 chunks) are read
@@ -561,28 +570,26 @@ __device__ __forceinline__ unsigned long long* team_rec(const Params& P, int tr)
     return P.rec + (size_t)tr * P.C * kRecWords;
 }
 
-template <bool kGreedy>
 __device__ __forceinline__ void poll_issue(const Params& P, int tr, TeamPoll& pl) {
     const int lane = threadIdx.x & 63;
     unsigned long long* rec = team_rec(P, tr);
     pl.tr = tr;
     #pragma unroll
-    for (int f = 0; f < rec_words<kGreedy>(); ++f) {
+    for (int f = 0; f < kStatWords; ++f) {
         pl.w[f] = lane < P.C ? ld64(rec + lane * kRecWords + f) : (unsigned long long)P.epoch;
     }
 }
 
 // True when every record word of the team carries this call's epoch.
-template <bool kGreedy>
 __device__ __forceinline__ bool poll_complete(const Params& P, const TeamPoll& pl) {
     const int lane = threadIdx.x & 63;
     bool ok = true;
     #pragma unroll
-    for (int f = 0; f < rec_words<kGreedy>(); ++f) ok = ok && tag_ok(pl.w[f], P.epoch);
+    for (int f = 0; f < kStatWords; ++f) ok = ok && tag_ok(pl.w[f], P.epoch);
     if (P.C > 64) {
         unsigned long long* rec = team_rec(P, pl.tr);
         for (int cc = lane + 64; cc < P.C; cc += 64) {
-            for (int f = 0; f < rec_words<kGreedy>(); ++f) ok = ok && tag_ok(ld64(rec + cc * kRecWords + f), P.epoch);
+            for (int f = 0; f < kStatWords; ++f) ok = ok && tag_ok(ld64(rec + cc * kRecWords + f), P.epoch);
         }
     }
     return __ballot(!ok) == 0;
@@ -628,42 +635,6 @@ __device__ TeamStats team_stats(const Params& P, const TeamPoll& pl) {
     t.st = wave_sum(st);
     t.sd = wave_sum(sd);
     return t;
-}
-
-// Control wave, greedy: complete records of team tr (position i of request
-// b with budget k): the row's first argmax; the decision; complete the team.
-__device__ void decide_greedy(const Params& P, const TeamPoll& pl, int b, int i, int k, int tr) {
-    const int lane = threadIdx.x & 63;
-    const int C = P.C;
-    unsigned long long* rec = team_rec(P, tr);
-    float bv = -INFINITY;
-    int bi = INT_MAX;
-    auto take = [&](unsigned long long wm, unsigned long long wi) {
-        const float v = tag_val(wm);
-        const int idx = (int)(unsigned)(wi >> 32);
-        if (better_arg(v, idx, bv, bi)) {
-            bv = v;
-            bi = idx;
-        }
-    };
-    if (lane < C) take(pl.w[R_MT], pl.w[R_MD]);
-    for (int cc = lane + 64; cc < C; cc += 64) {
-        take(ld64(rec + cc * kRecWords + R_MT), ld64(rec + cc * kRecWords + R_MD));
-    }
-    wave_argmax(bv, bi);
-    if (lane == 0) {
-        const int best = bi == INT_MAX ? 0 : bi;      // an all -inf row: index 0
-        bool accept = true;
-        if (i < k) {
-            const int x = P.tokens[(size_t)b * P.K + i];
-            const bool valid = x >= 0 && x < P.V;
-            if (!valid) atomicOr(P.status, SV_FLAG_BAD_TOKEN);
-            accept = valid && x == best;
-        }
-        st32(&P.result[tr], (unsigned)best);
-        st64(dec_word(P, tr), ((unsigned long long)P.epoch << 32) | (accept ? 1u : 0u));
-        team_complete(P, b, k);
-    }
 }
 
 // ---------------------------------------------------------- main kernel --
@@ -740,7 +711,8 @@ __device__ __forceinline__ void issue_loads(const Params& P, const Unit& d, int 
 }
 
 // Control wave: collect the data waves' statistics of the unit of round r,
-// merge them and publish the unit's record (epoch-tagged words, no wait).
+// merge them and publish them (no wait): sampled, the unit's record
+// (epoch-tagged words); greedy, the chunk's argmax key to its team's key.
 template <typename E, bool kGreedy>
 __device__ __forceinline__ void control_unit(const Params& P, Shared& sh, const Unit& cur, int r) {
     const int lane = threadIdx.x & 63;
@@ -773,10 +745,7 @@ __device__ __forceinline__ void control_unit(const Params& P, Shared& sh, const 
         order();
         if (lane == 0) lds_put(&sh.st_done[slot], r + 1);
         wave_argmax(bv, bi);
-        if (lane == 0) {
-            st64(rec + R_MT, tagged(bv, ep));
-            st64(rec + R_MD, ((unsigned long long)(unsigned)bi << 32) | ep);
-        }
+        if (lane == 0 && bi != INT_MAX) max64(team_key(P, cur.tr), arg_key(bv, bi));
     } else {
         float mt = -INFINITY, md = -INFINITY;
         double a = 0.0, d = 0.0;
@@ -842,34 +811,14 @@ __device__ __forceinline__ void plan_round(const Params& P, Shared& sh, const in
     }
 }
 
-// A team's arrival counter: every unit of a team that needs a decision adds
-// one after its record is visible; the unit whose addition completes the
-// team decides it and resets the counter.
-__device__ __forceinline__ unsigned* team_count(const Params& P, int tr) {
-    return P.team + (size_t)tr * kTeamWords + TW_CNT;
-}
-
-// Greedy: a unit whose team decision may fall to this workgroup. Its
-// arrival was counted (old = the counter's value before); the team is
-// decided here once old shows that this arrival completed it.
+// Greedy: a unit that was counted on its request's counter (old = the
+// counter's value before). Its workgroup completes the request once old
+// shows that this unit was the request's last.
 struct Pending {
-    Unit u;
+    int b, k, n;        // request, budget, units of the request
     unsigned old;
     bool valid;
 };
-
-// Control wave, greedy: decide team u (its C records are complete: this
-// workgroup's arrival completed the team): argmax, decision, request
-// completion; then reset the team's counter.
-__device__ void decide_team(const Params& P, const Unit& u) {
-    TeamPoll pl;
-    poll_issue<true>(P, u.tr, pl);
-    if (!poll_complete<true>(P, pl) && (threadIdx.x & 63) == 0) {
-        atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);       // cannot happen: records precede arrivals
-    }
-    decide_greedy(P, pl, u.b, u.i, u.k, u.tr);
-    if ((threadIdx.x & 63) == 0) st32(team_count(P, u.tr), 0u);
-}
 
 // The control wave's loop. Units are handed out dynamically: the first
 // kPlanLead rounds of workgroup w take units w, w + G, w + 2G, ...; later
@@ -879,16 +828,16 @@ __device__ void decide_team(const Params& P, const Unit& u) {
 // time. Every round:
 //  P. plan round r + kPlanLead from the fetched value, and fetch the next;
 //  1. the data waves' results of round r: the unit's statistics are merged
-//     and published;
-//  2. greedy: the arrival counted last round: if it completed its team,
-//     decide it;
-//  3. greedy: count this unit's arrival in its team (after its record is
-//     visible); the returned count is read next round.
+//     and published (greedy: posted to the team's key);
+//  2. greedy: the unit counted last round: if it was its request's last,
+//     complete the request;
+//  3. greedy: count this unit on its request's counter (after its key is
+//     posted); the returned count is read next round.
 // Sampled, the records are all the pass leaves: the draw pass decides the
-// drafted positions. No step waits on another workgroup: a greedy team is
-// decided by whichever workgroup completes it, so the loop never depends on
-// which workgroups are resident. Nothing the data waves do waits on a
-// decision.
+// drafted positions. No step waits on another workgroup: a greedy request
+// is decided by whichever workgroup counts its last unit, so the loop never
+// depends on which workgroups are resident. Nothing the data waves do waits
+// on a decision.
 template <typename E, bool kGreedy, bool kVec>
 __device__ __forceinline__ void control_loop(const Params& P, Shared& sh, const int* off) {
     const int U = off[P.B];
@@ -913,8 +862,8 @@ __device__ __forceinline__ void control_loop(const Params& P, Shared& sh, const 
     pend.valid = false;
     auto settle = [&]() __attribute__((always_inline)) {
         if (pend.valid &&
-            (unsigned)__builtin_amdgcn_readfirstlane((int)pend.old) == (unsigned)(P.C - 1)) {
-            decide_team(P, pend.u);
+            (unsigned)__builtin_amdgcn_readfirstlane((int)pend.old) == (unsigned)(pend.n - 1)) {
+            request_complete(P, pend.b, pend.k);
         }
         pend.valid = false;
     };
@@ -940,10 +889,12 @@ __device__ __forceinline__ void control_loop(const Params& P, Shared& sh, const 
         settle();
         // 3.
         if (kGreedy) {
-            pend.u = cur;
-            drain();                                   // the record is visible first
+            pend.b = cur.b;
+            pend.k = cur.k;
+            pend.n = (cur.k + 1) * P.C;
+            drain();                                   // the key's maximum is performed first
             pend.old = 0;
-            if (lane == 0) pend.old = add32(team_count(P, cur.tr), 1u);
+            if (lane == 0) pend.old = add32(&P.req_count[cur.b * kReqStride], 1u);
             pend.valid = true;
         }
     }
@@ -1249,7 +1200,7 @@ void draw_kernel(Params P) {
         dzt[u] = dzd[u] = 0ull;
         dx[u] = -1;
         if (t < K) {
-            poll_issue<false>(P, b * (K + 1) + t, dpl[u]);
+            poll_issue(P, b * (K + 1) + t, dpl[u]);
             unsigned long long* rec = team_rec(P, b * (K + 1) + t);
             if (lane < C) {
                 dzt[u] = ld64(rec + lane * kRecWords + R_ZT);
@@ -1264,7 +1215,7 @@ void draw_kernel(Params P) {
         const int t = wave + u * kDrawWaves;
         if (t < k) {
             const int tr = b * (K + 1) + t;
-            if (!poll_complete<false>(P, dpl[u]) && lane == 0) atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);
+            if (!poll_complete(P, dpl[u]) && lane == 0) atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);
             const TeamStats ts = team_stats(P, dpl[u]);
             const int x = dx[u];
             const bool valid = x >= 0 && x < V;
@@ -1320,7 +1271,7 @@ void draw_kernel(Params P) {
         }
     }
     TeamPoll pl;                                         // wave 0, bonus: team k's records
-    if (wave == 0 && j == k) poll_issue<false>(P, b * (K + 1) + j, pl);
+    if (wave == 0 && j == k) poll_issue(P, b * (K + 1) + j, pl);
     const E* rt = static_cast<const E*>(P.target) + ((size_t)b * (K + 1) + j) * (size_t)V;
     const E* rd = j < k ? static_cast<const E*>(P.draft) + ((size_t)b * K + j) * (size_t)V : nullptr;
     const bool vt = aligned16(rt), vd = rd != nullptr && aligned16(rd);
@@ -1365,7 +1316,7 @@ void draw_kernel(Params P) {
             ts.st = dsh.tst[j];
             ts.sd = dsh.tsd[j];
         } else {
-            if (!poll_complete<false>(P, pl) && lane == 0) atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);
+            if (!poll_complete(P, pl) && lane == 0) atomicOr(P.status, SV_FLAG_SYNC_TIMEOUT);
             ts = team_stats(P, pl);
         }
         const uint4 rw = philox4x32_10(P.bbase + (uint32_t)b, (uint32_t)j, 0u, 0u, P.key0, P.key1);
@@ -1481,7 +1432,7 @@ void draw_kernel(Params P) {
                     // No residual mass (rounding only): from p_j, whose
                     // records are read again.
                     TeamPoll pr;
-                    poll_issue<false>(P, b * (K + 1) + j, pr);
+                    poll_issue(P, b * (K + 1) + j, pr);
                     const TeamStats tr = team_stats(P, pr);
                     int chunk = -1;
                     p_chunk(P, pr, tr, dsh.u, chunk, nthr);
@@ -1584,13 +1535,13 @@ size_t draw_smem_bytes(int C) { return (size_t)C * kBlocks * sizeof(double); }
 // max_batch requests with up to max_k drafted positions and C chunks per row.
 // The draw pass splits a request over several workgroups only for batches of
 // at most split_reqs requests. The counters must read zero when a call
-// starts: the team arrival counters (word TW_CNT of each team record) and
-// the words in [req, req_end) and [dcnt, dcnt_end), which every kernel that
-// raises one leaves at zero when it completes, and the scheduling word of
+// starts: the greedy team keys (words TW_KEY, TW_KEY + 1 of each team
+// record) and the words in [req, req_end) and [dcnt, dcnt_end), which every
+// kernel that raises one leaves at zero when it completes, and the scheduling word of
 // the call's epoch parity at status + 64, which the launch before it clears.
 // The status word at `status` accumulates device-side flags.
 struct WsLayout {
-    size_t rec, team, result, req, req_end, dmass, dcnt, dcnt_end, status, total;
+    size_t rec, team, req, req_end, dmass, dcnt, dcnt_end, status, total;
     size_t teams;
     int split_reqs;
 };
@@ -1604,8 +1555,6 @@ WsLayout ws_layout(int max_batch, int max_k, int C, int split_reqs) {
     o += round256(teams * C * kRecWords * 8);
     L.team = o;
     o += round256(teams * kTeamWords * 4);
-    L.result = o;
-    o += round256(teams * 4);
     L.req = o;
     o += round256((size_t)max_batch * kReqStride * 4);
     L.req_end = o;
@@ -1779,7 +1728,6 @@ int run_batches(DeviceInfo& di, spec_verify_ctx* tctx, int vocab, int dtype, uns
     std::memset(&p, 0, sizeof(p));
     p.rec = reinterpret_cast<unsigned long long*>(ws + L.rec);
     p.team = reinterpret_cast<unsigned*>(ws + L.team);
-    p.result = reinterpret_cast<unsigned*>(ws + L.result);
     p.req_count = reinterpret_cast<unsigned*>(ws + L.req);
     p.sched = reinterpret_cast<unsigned*>(ws + L.status + 64);
     p.status = status;
@@ -1859,14 +1807,17 @@ std::mutex g_noalloc_mu;
 NoallocDevice g_noalloc[kMaxDevices];
 
 // Zero the call-start counters of the scratch (a fill kernel rather than a
-// memset, so the call can be captured in a HIP graph): the team arrival
-// counters (one word every kTeamWords), the request and draw-split counters,
+// memset, so the call can be captured in a HIP graph): the greedy team keys
+// (two words every kTeamWords), the request and draw-split counters,
 // the scheduling words, and the caller's status word.
 __global__ void clear_words_kernel(unsigned* team, int nteam, unsigned* a, int na, unsigned* b,
                                    int nb, unsigned* sched, uint32_t* status) {
     const int t = blockIdx.x * blockDim.x + threadIdx.x;
     const int stride = gridDim.x * blockDim.x;
-    for (int i = t; i < nteam; i += stride) team[(size_t)i * kTeamWords + TW_CNT] = 0u;
+    for (int i = t; i < nteam; i += stride) {
+        team[(size_t)i * kTeamWords + TW_KEY] = 0u;
+        team[(size_t)i * kTeamWords + TW_KEY + 1] = 0u;
+    }
     for (int i = t; i < na; i += stride) a[i] = 0u;
     for (int i = t; i < nb; i += stride) b[i] = 0u;
     if (t == 0) {

@@ -110,7 +110,7 @@ enum sv_status {
  *   vocab      V, the vocabulary size of every run, 1..SV_MAX_VOCAB.
  *   dtype      sv_dtype of the logits of every run.
  * Allocates and zeroes the device workspace (per-chunk partial statistics,
- * per-row decision words and per-request counters of greedy mode, status
+ * per-row argmax keys and per-request counters of greedy mode, status
  * word). The context owns it until spec_verify_free. Synchronous.
  * Errors: SV_ERR_NULL, SV_ERR_ARG, SV_ERR_DTYPE, SV_ERR_HIP, SV_ERR_NOMEM.
  */

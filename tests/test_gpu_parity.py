@@ -272,6 +272,47 @@ def test_edge_shapes(B, K, V, dtype, budgets, T, masks):
                    tag=f"edge-{B}-{K}-{V}")
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_greedy_argmax_ties_signed_zeros_and_masked_rows(dtype):
+    """The greedy rule's first argmax where it is easiest to get wrong across
+    vocabulary chunks: a -0 and a +0 maximum in different chunks (equal, so
+    the lower index), equal positive maxima in different chunks, rows that
+    are -inf everywhere (the first index) and a maximum in the last,
+    ragged element. Drafted tokens are set to accept or reject on purpose."""
+    B, K, V = 6, 3, 40003                      # 2 (bf16) or 3 (fp32) chunks, ragged tail
+    g = torch.Generator().manual_seed(4242)
+    zt = -1.0 - torch.rand(B, K + 1, V, generator=g)
+    x = torch.zeros(B, K, dtype=torch.int32)
+    lo, hi = 100, 35000                        # first and last chunk
+    zt[0, :, lo] = -0.0
+    zt[0, :, hi] = 0.0
+    x[0, :] = lo                               # all accepted; bonus = lo
+    zt[1, :, lo] = 0.0
+    zt[1, :, hi] = -0.0
+    x[1, :] = hi                               # rejected at 0; y = lo
+    zt[2] = -float("inf")
+    x[2, :] = 0                                # -inf rows: argmax 0, all accepted
+    zt[3, :, V - 1] = 3.0
+    x[3, 0] = V - 1
+    x[3, 1] = V - 2                            # rejected at 1; y = V - 1
+    zt[4, :, 20] = 5.0
+    zt[4, :, 30000] = 5.0
+    x[4, :] = 20
+    x[4, 2] = 30000                            # rejected at 2; y = 20
+    budgets = torch.tensor([3, 3, 3, 2, 3, 0], dtype=torch.int32)
+    # The planted values (0, -0, 3, 5, -inf) are exact in bf16 as well.
+    inp = {"target": zt.to(dtype), "draft": zt[:, :K].to(dtype).contiguous(), "tokens": x,
+           "budgets": budgets, "temperature": 0.0}
+    seed = 0x51A0
+    gpu = _run(inp, seed, temperature=0.0)
+    _assert_parity(inp, seed, gpu, _oracle(inp, seed, temperature=0.0), temperature=0.0,
+                   tag=f"greedy-keys-{dtype}")
+    n = gpu[1]
+    assert list(n) == [3, 0, 3, 1, 2, 0]
+    y = [int(gpu[0][b][int(n[b])]) for b in range(B)]
+    assert y[:5] == [lo, lo, 0, V - 1, 20]
+
+
 MAXIMA = [
     # B, K, V, dtype, budgets: the header's largest K, vocabulary and batch
     (3, 32, 4099, torch.bfloat16, [32, 17, 0]),
