@@ -13,9 +13,11 @@
 // draw.
 //  * Work unit = vocabulary chunk c of position i of request b: the chunk of
 //    target row i and, for a drafted position, the same chunk of drafter row
-//    i. Every chunk has the same size (960 data lanes x 4 sixteen-byte loads
-//    per row). Units are numbered request-major, position-major, chunk-minor,
-//    so the C chunks of one position (a "team") are consecutive.
+//    i. Every chunk of a call has the same size: 960 data lanes x 4
+//    sixteen-byte loads per row when sampled, x 8 when greedy (one row per
+//    unit, so the same bytes in flight). Units are numbered request-major,
+//    position-major, chunk-minor, so the C chunks of one position (a "team")
+//    are consecutive.
 //  * Streaming pass (verify_kernel): one workgroup of 16 waves per CU, grid =
 //    the resident workgroups. Units are handed out dynamically: the first
 //    rounds of workgroup w take units w, w + G, ..., later ones the values of
@@ -76,7 +78,7 @@ constexpr int kWaves = 16;                     // wave 0: control; waves 1-15: d
 constexpr int kThreads = kWaves * 64;
 constexpr int kDataWaves = kWaves - 1;
 constexpr int kDataThreads = kDataWaves * 64;
-constexpr int kG = 4;                          // 16-byte groups per data lane per row of a unit
+constexpr int kG = 4;                          // 16-byte groups per data lane per row of a sampled unit
 constexpr int kLaunchBatch = 8192;             // requests per launch (unit offsets live in LDS)
 constexpr int kMbox = 2;                       // result mailbox slots (rounds the data waves may lead)
 constexpr int kPlanLead = 4;                   // rounds the control wave plans ahead (>= kMbox)
@@ -84,6 +86,10 @@ constexpr int kPlanSlots = 8;                  // plan ring (> kPlanLead + 1)
 static_assert(kPlanLead >= kMbox && kPlanSlots > kPlanLead + 1, "plan ring too short");
 constexpr int PL_END = 0, PL_UNIT = 1;
 constexpr int kBlocks = kG * kDataWaves;       // 64-group blocks (one 16-byte load per lane) in a chunk
+// A greedy unit reads one row, so it takes twice the groups per lane: the
+// same bytes in flight as a sampled unit of a drafted position.
+template <bool kGreedy>
+__host__ __device__ constexpr int groups_of() { return kGreedy ? 2 * kG : kG; }
 constexpr int kTeamWords = 32;                 // words per team record (128 bytes)
 constexpr int kReqStride = 16;                 // words between request counters (64 bytes)
 constexpr unsigned kLdsSpinLimit = 1u << 26;   // bounded LDS mailbox wait (~3 s)
@@ -702,12 +708,12 @@ __device__ __forceinline__ void load_pair(const UnitRows<E>& w, int dt, int j, u
 }
 
 // Data waves: issue the 16-byte loads of a unit into registers (no wait).
-template <typename E, bool kVec>
+template <typename E, bool kVec, int NG>
 __device__ __forceinline__ void issue_loads(const Params& P, const Unit& d, int dt,
-                                            uint4 (&gt)[kG], uint4 (&gd)[kG]) {
+                                            uint4 (&gt)[NG], uint4 (&gd)[NG]) {
     const UnitRows<E> w = unit_rows<E>(P, d);
     #pragma unroll
-    for (int j = 0; j < kG; ++j) load_pair<E, kVec>(w, dt, j, gt[j], gd[j]);
+    for (int j = 0; j < NG; ++j) load_pair<E, kVec>(w, dt, j, gt[j], gd[j]);
 }
 
 // Control wave: collect the data waves' statistics of the unit of round r,
@@ -920,12 +926,13 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
         u = unit_from(P, off, kind == PL_END ? -1 : sh.pl_u[slot], sh.pl_b[slot], kGreedy);
     };
 
-    uint4 gt[kG], gd[kG];
+    constexpr int NG = groups_of<kGreedy>();
+    uint4 gt[NG], gd[NG];
     Unit cur;
     int kind;
     read_plan(0, cur, kind);
     if (kind == PL_END) return;
-    issue_loads<E, kVec>(P, cur, dt, gt, gd);
+    issue_loads<E, kVec, NG>(P, cur, dt, gt, gd);
     for (int r = 0;; ++r) {
         const int slot = r % kMbox;
         Unit nxt;
@@ -943,7 +950,7 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
             UnitRows<E> nw;
             if (more) nw = unit_rows<E>(P, nxt);
             #pragma unroll
-            for (int j = 0; j < kG; ++j) {
+            for (int j = 0; j < NG; ++j) {
                 #pragma unroll
                 for (int kk = 0; kk < W; ++kk) {
                     const float v = Elem<E>::at(gt[j], kk);
@@ -960,7 +967,7 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
         } else {
             float mt = -INFINITY, md = -INFINITY;
             #pragma unroll
-            for (int j = 0; j < kG; ++j) {
+            for (int j = 0; j < NG; ++j) {
                 #pragma unroll
                 for (int kk = 0; kk < W; ++kk) {
                     mt = fmaxf(mt, Elem<E>::at(gt[j], kk));
@@ -970,7 +977,7 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
             // Opaque raw registers: the exp pass converts them again rather
             // than keeping every converted float alive across the reduction.
             #pragma unroll
-            for (int j = 0; j < kG; ++j) {
+            for (int j = 0; j < NG; ++j) {
                 asm volatile("" : "+v"(gt[j].x), "+v"(gt[j].y), "+v"(gt[j].z), "+v"(gt[j].w));
                 asm volatile("" : "+v"(gd[j].x), "+v"(gd[j].y), "+v"(gd[j].z), "+v"(gd[j].w));
             }
@@ -989,7 +996,7 @@ __device__ __forceinline__ void data_loop(const Params& P, Shared& sh, const int
             const float smt = mt * cs, smd = md * cs;
             float lt = 0.0f, ld = 0.0f;
             #pragma unroll
-            for (int j = 0; j < kG; ++j) {
+            for (int j = 0; j < NG; ++j) {
                 float e[W], f[W];
                 #pragma unroll
                 for (int kk = 0; kk < W; ++kk) {
@@ -1518,10 +1525,14 @@ constexpr uint32_t kMagic = 0x53505643u;   // live context marker
 
 int elems_per_group(int dtype) { return dtype == SV_DTYPE_BF16 ? 8 : 4; }
 
-int chunk_elems(int dtype) { return kDataThreads * kG * elems_per_group(dtype); }
+// Elements per chunk, and chunks per row: sampled (the records and the draw
+// pass's blocks are laid out by these), or greedy.
+int chunk_elems(int dtype, bool greedy = false) {
+    return kDataThreads * (greedy ? groups_of<true>() : groups_of<false>()) * elems_per_group(dtype);
+}
 
-int chunks_for(int vocab, int dtype) {
-    const int ce = chunk_elems(dtype);
+int chunks_for(int vocab, int dtype, bool greedy = false) {
+    const int ce = chunk_elems(dtype, greedy);
     return (vocab + ce - 1) / ce;
 }
 
@@ -1735,8 +1746,8 @@ int run_batches(DeviceInfo& di, spec_verify_ctx* tctx, int vocab, int dtype, uns
     p.dcnt = reinterpret_cast<unsigned*>(ws + L.dcnt);
     p.K = K;
     p.V = vocab;
-    p.C = chunks_for(vocab, dtype);
-    p.CE = chunk_elems(dtype);
+    p.C = chunks_for(vocab, dtype, greedy);
+    p.CE = chunk_elems(dtype, greedy);
     p.c64 = greedy ? 0.0 : kLog2e / (double)a.temperature;
     p.c32 = (float)p.c64;
     p.key0 = (uint32_t)(a.seed & 0xFFFFFFFFu);

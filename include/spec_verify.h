@@ -437,7 +437,9 @@ void spec_verify_free(spec_verify_ctx* ctx);
 const char* spec_verify_strerror(int code);
 
 /* spec_verify_chunks -- number of vocabulary chunks a row is split into for
- * (vocab, dtype), or a negative sv_status on bad arguments. Host only. */
+ * (vocab, dtype) in sampled mode (the unit of the workspace's per-chunk
+ * records; greedy calls use chunks twice as long), or a negative sv_status
+ * on bad arguments. Host only. */
 int spec_verify_chunks(int vocab, int dtype);
 
 #ifdef __cplusplus
