@@ -651,27 +651,50 @@ struct Unit {
     int b, i, k, c;
     int tr;        // team record index b * (K + 1) + i
     int e0, n;     // chunk start and length (elements)
-    bool has_d;    // drafted position in sampled mode: the drafter row is read too
+    int n2;        // pair: length of chunk c + 1
+    bool drafted;  // sampled, a drafted position: the drafter row's chunk c is read too
+    bool pair;     // sampled, the bonus position: chunk c + 1 of the target row is read too
+    bool has_d;    // drafted or pair: the second registers hold data
 };
+
+// Units of a request with budget k: greedy, C per position; sampled, C per
+// drafted position and ceil(C / 2) for the bonus position, whose units take
+// two consecutive chunks of its one row (the bytes in flight of a drafted
+// unit).
+__host__ __device__ __forceinline__ int bonus_units(int C, bool greedy) {
+    return greedy ? C : (C + 1) >> 1;
+}
+__host__ __device__ __forceinline__ int request_units(int k, int C, bool greedy) {
+    return k * C + bonus_units(C, greedy);
+}
 
 // The coordinates of unit u of request b (two independent LDS reads; no
 // search). u < 0 gives the empty unit.
 __device__ __forceinline__ Unit unit_from(const Params& P, const int* off, int u, int b, bool greedy) {
     Unit d;
     d.u = u;
-    d.b = d.i = d.k = d.c = d.tr = d.e0 = d.n = 0;
-    d.has_d = false;
+    d.b = d.i = d.k = d.c = d.tr = d.e0 = d.n = d.n2 = 0;
+    d.drafted = d.pair = d.has_d = false;
     if (u < 0) return d;
     d.b = b;
+    const int C = P.C;
     const int o0 = off[b], o1 = off[b + 1];
     const int local = u - o0;
-    d.k = (o1 - o0) / P.C - 1;
-    d.i = local / P.C;
-    d.c = local - d.i * P.C;
+    d.k = (o1 - o0 - bonus_units(C, greedy)) / C;
+    if (local < d.k * C) {
+        d.i = local / C;
+        d.c = local - d.i * C;
+    } else {
+        d.i = d.k;
+        d.c = greedy ? local - d.k * C : 2 * (local - d.k * C);
+    }
     d.tr = b * (P.K + 1) + d.i;
     d.e0 = d.c * P.CE;
     d.n = min(P.CE, P.V - d.e0);
-    d.has_d = !greedy && d.i < d.k;
+    d.drafted = !greedy && d.i < d.k;
+    d.pair = !greedy && d.i == d.k && d.c + 1 < C;
+    d.has_d = d.drafted || d.pair;
+    d.n2 = d.pair ? min(P.CE, P.V - d.e0 - P.CE) : d.n;
     return d;
 }
 
@@ -680,8 +703,8 @@ __device__ __forceinline__ Unit unit_from(const Params& P, const int* off, int u
 template <typename E>
 struct UnitRows {
     const E* bt;       // target row segment
-    const E* bd;       // drafter row segment (null: not read)
-    int n;             // segment length
+    const E* bd;       // drafter row segment, or a pair's next target chunk (null: not read)
+    int n, nd;         // segment lengths
     bool vt, vd;       // 16-byte loads are legal
 };
 
@@ -691,8 +714,11 @@ __device__ __forceinline__ UnitRows<E> unit_rows(const Params& P, const Unit& d)
     const E* draft = static_cast<const E*>(P.draft);
     UnitRows<E> w;
     w.bt = target + ((size_t)d.b * (P.K + 1) + d.i) * (size_t)P.V + d.e0;
-    w.bd = d.has_d ? draft + ((size_t)d.b * P.K + d.i) * (size_t)P.V + d.e0 : nullptr;
+    w.bd = d.drafted ? draft + ((size_t)d.b * P.K + d.i) * (size_t)P.V + d.e0
+         : d.pair    ? w.bt + P.CE
+                     : nullptr;
     w.n = d.n;
+    w.nd = d.n2;
     w.vt = aligned16(w.bt);
     w.vd = d.has_d && aligned16(w.bd);
     return w;
@@ -704,7 +730,7 @@ __device__ __forceinline__ void load_pair(const UnitRows<E>& w, int dt, int j, u
     constexpr int W = Elem<E>::W;
     const int e = (dt + j * kDataThreads) * W;
     t = e < w.n ? load_group<E, kVec>(w.bt, e, w.n, w.vt) : neg_group<E>();
-    q = (w.bd != nullptr && e < w.n) ? load_group<E, kVec>(w.bd, e, w.n, w.vd) : neg_group<E>();
+    q = (w.bd != nullptr && e < w.nd) ? load_group<E, kVec>(w.bd, e, w.nd, w.vd) : neg_group<E>();
 }
 
 // Data waves: issue the 16-byte loads of a unit into registers (no wait).
@@ -729,7 +755,7 @@ __device__ __forceinline__ void control_unit(const Params& P, Shared& sh, const 
     // chunk holds it (the loads go out before the wait below).
     bool has_x = false;
     float zt = 0.0f, zd = 0.0f;
-    if (!kGreedy && cur.has_d) {
+    if (!kGreedy && cur.drafted) {
         const int x = P.tokens[(size_t)cur.b * P.K + cur.i];
         has_x = x >= cur.e0 && x < cur.e0 + cur.n;
         if (has_x) {
@@ -769,7 +795,18 @@ __device__ __forceinline__ void control_unit(const Params& P, Shared& sh, const 
         if (a > 0.0) a *= (double)fast_exp2(mt - Mt);
         if (d > 0.0) d *= (double)fast_exp2(md - Md);
         const double St = wave_sum(a), Sd = wave_sum(d);
-        if (lane == 0) {
+        if (lane == 0 && cur.pair) {
+            // Two chunks of the bonus row: chunk c's statistics, then chunk
+            // c + 1's from the second registers (no drafter row).
+            st64(rec + R_MT, tagged(Mt, ep));
+            st64(rec + R_MD, tagged(-INFINITY, ep));
+            st64(rec + R_ST, tagged((float)St, ep));
+            st64(rec + R_SD, tagged(0.0f, ep));
+            st64(rec + kRecWords + R_MT, tagged(Md, ep));
+            st64(rec + kRecWords + R_MD, tagged(-INFINITY, ep));
+            st64(rec + kRecWords + R_ST, tagged((float)Sd, ep));
+            st64(rec + kRecWords + R_SD, tagged(0.0f, ep));
+        } else if (lane == 0) {
             st64(rec + R_MT, tagged(Mt, ep));
             st64(rec + R_MD, tagged(Md, ep));
             st64(rec + R_ST, tagged((float)St, ep));
@@ -785,7 +822,7 @@ __device__ __forceinline__ void control_unit(const Params& P, Shared& sh, const 
 // -------------------------------------------------------------- planning --
 
 // The request of unit u (off[b] <= u < off[b + 1]; every request has at
-// least C units, so the offsets increase strictly) by a 64-ary search over
+// least one unit, so the offsets increase strictly) by a 64-ary search over
 // the offsets in LDS. Control wave; uniform result.
 __device__ int request_of(const Params& P, const int* off, int u) {
     const int lane = threadIdx.x & 63;
@@ -897,7 +934,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Shared& sh, const 
         if (kGreedy) {
             pend.b = cur.b;
             pend.k = cur.k;
-            pend.n = (cur.k + 1) * P.C;
+            pend.n = request_units(cur.k, P.C, true);
             drain();                                   // the key's maximum is performed first
             pend.old = 0;
             if (lane == 0) pend.old = add32(&P.req_count[cur.b * kReqStride], 1u);
@@ -1059,7 +1096,7 @@ void verify_kernel(Params P) {
                 bad = true;
                 k = k < 0 ? 0 : K;
             }
-            local += (k + 1) * C;
+            local += request_units(k, C, kGreedy);
         }
         if (bad && blockIdx.x == 0) atomicOr(P.status, SV_FLAG_BAD_BUDGET);
         int incl = local;
@@ -1080,7 +1117,7 @@ void verify_kernel(Params P) {
             off[b] = run;
             int k = P.budgets[b];
             k = k < 0 ? 0 : (k > K ? K : k);
-            run += (k + 1) * C;
+            run += request_units(k, C, kGreedy);
         }
         if (tid == kThreads - 1) off[B] = run;
         __syncthreads();
