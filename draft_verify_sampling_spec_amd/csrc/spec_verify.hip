@@ -146,7 +146,7 @@ struct Params {
     float c32;                     // log2(e) / T
     double c64;
     uint32_t key0, key1;
-    unsigned epoch;                // call number (never 0): tags record and decision words
+    unsigned epoch;                // call number (never 0): tags the sampled records
 };
 
 // The schedule counter of this launch.
@@ -1645,7 +1645,7 @@ struct spec_verify_ctx {
     DeviceInfo info;
     WsLayout lay;
     unsigned char* ws;
-    unsigned calls;                // calls made so far (record and decision word epochs)
+    unsigned calls;                // calls made so far (the epochs of its launches)
     // Per-pass timing (off unless enabled): recorded event pairs of later
     // runs, and a pool of events to reuse.
     bool timing;
