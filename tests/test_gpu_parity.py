@@ -313,6 +313,28 @@ def test_greedy_argmax_ties_signed_zeros_and_masked_rows(dtype):
     assert y[:5] == [lo, lo, 0, V - 1, 20]
 
 
+@pytest.mark.parametrize("V,dtype", [(40003, torch.float32), (151936, torch.bfloat16),
+                                     (92161, torch.bfloat16)])
+def test_bonus_draws_over_multi_chunk_rows(V, dtype):
+    """q = p: every drafted token is accepted, so every request draws its
+    bonus token from p_k, whose chunk masses come from the records the
+    streaming pass writes for the bonus row (two chunks per unit, the last
+    one alone when the chunk count is odd). Rows of 3 (fp32), 5 and 4 (bf16)
+    chunks, budgets 0..K."""
+    B, K = 48, 3
+    budgets = [b % (K + 1) for b in range(B)]
+    inp = _edge_inputs(B, K, V, dtype, budgets, seed=V + B)
+    inp["draft"] = inp["target"][:, :K].contiguous()
+    inp["tokens"] = torch.argmax(inp["draft"].float(), dim=-1).to(torch.int32)
+    inp["temperature"] = 1.0
+    seed = philox_seed(3, V)
+    _log(f"bonus-only B={B} K={K} V={V} {dtype}")
+    gpu = _run(inp, seed, temperature=1.0)
+    assert list(gpu[1]) == budgets
+    _assert_parity(inp, seed, gpu, _oracle(inp, seed, temperature=1.0), temperature=1.0,
+                   tag=f"bonus-{V}")
+
+
 MAXIMA = [
     # B, K, V, dtype, budgets: the header's largest K, vocabulary and batch
     (3, 32, 4099, torch.bfloat16, [32, 17, 0]),
