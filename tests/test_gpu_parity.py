@@ -430,6 +430,42 @@ def test_repeat_calls_reuse_workspace_and_are_deterministic():
     sv.close()
 
 
+def test_interleaved_modes_and_sizes_on_one_context():
+    """Greedy and sampled calls of different batch sizes, with a rejected
+    call among them, in turn on one context: every call's outputs equal the
+    same call's on a fresh context. The launches alternate between the two
+    schedule counters, and the greedy keys and counters must be clear again
+    after each call that raised them."""
+    inp = make_inputs("ragged", device=DEV)
+    t, d, x, k = (inp[n].to(DEV) for n in ("target", "draft", "tokens", "budgets"))
+    B, K1, V = t.shape
+    sv = SpecVerify(DEV, max_batch=B, max_k=K1 - 1, vocab=V, dtype=t.dtype)
+
+    def call(ctx, n, T, seed):
+        dd = d[:n].contiguous() if T > 0 else None
+        out = ctx.run(t[:n].contiguous(), dd, x[:n].contiguous(), k[:n].contiguous(), T, seed)
+        return tuple(o.clone() for o in out)
+
+    plan = [(B, 0.8, 11), (B, 0.0, 0), (23, 0.0, 0), (B, 0.8, 12), (5, 0.8, 13), None,
+            (B, 0.0, 0), (1, 0.8, 14), (B, 0.8, 11)]
+    for step in plan:
+        if step is None:
+            with pytest.raises(ValueError):
+                sv.run(t, d, x, k, -1.0, 0)
+            continue
+        n, T, seed = step
+        got = call(sv, n, T, seed)
+        fresh = SpecVerify(DEV, max_batch=n, max_k=K1 - 1, vocab=V, dtype=t.dtype)
+        want = call(fresh, n, T, seed)
+        torch.cuda.synchronize()
+        assert fresh.status() == 0
+        fresh.close()
+        for a, b in zip(got, want):
+            assert torch.equal(a.nan_to_num(-7.0), b.nan_to_num(-7.0)), step
+    assert sv.status() == 0
+    sv.close()
+
+
 def test_runs_on_a_non_default_stream():
     inp = make_inputs("tiny", B=256, variant="sampled")
     s = torch.cuda.Stream(DEV)
