@@ -238,8 +238,9 @@ int spec_verify_philox_words(uint64_t seed, int B, int P, uint32_t* out_words,
  * spec_verify_timing -- per-pass device timing of later runs (off by
  * default). enable != 0: every later spec_verify_run on this context records
  * a HIP event pair on its stream around each pass it launches -- pass 0 the
- * streaming pass (row statistics and decisions), pass 1 the draw pass of
- * sampled mode (first rejection, residual or bonus draw, outputs) -- up to
+ * streaming pass (row statistics; the greedy decisions and outputs), pass 1
+ * the draw pass of sampled mode (accept decisions, first rejection,
+ * residual or bonus draw, outputs) -- up to
  * 65536 passes, then recording stops. enable == 0 waits for and discards
  * what is recorded. The events are the context's; recording adds event
  * markers between the launches and nothing else.
