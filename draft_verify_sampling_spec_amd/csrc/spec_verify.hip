@@ -80,7 +80,7 @@ constexpr int kDataWaves = kWaves - 1;
 constexpr int kDataThreads = kDataWaves * 64;
 constexpr int kG = 4;                          // 16-byte groups per data lane per row of a sampled unit
 constexpr int kLaunchBatch = 8192;             // requests per launch (unit offsets live in LDS)
-constexpr int kMbox = 2;                       // result mailbox slots (rounds the data waves may lead)
+constexpr int kMbox = 1;                       // result mailbox slots (rounds the data waves may lead)
 constexpr int kPlanLead = 4;                   // rounds the control wave plans ahead (>= kMbox)
 constexpr int kPlanSlots = 8;                  // plan ring (> kPlanLead + 1)
 static_assert(kPlanLead >= kMbox && kPlanSlots > kPlanLead + 1, "plan ring too short");
